@@ -1,0 +1,297 @@
+"""CPU oracle for the CubicQuant weight-only dequant-GEMM, in numpy float64.
+
+TEST INFRASTRUCTURE. This module is the plain, slow definition that the HIP
+library is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. The product path never
+imports, links or calls it, and the two share no code, tables or helpers.
+
+Source pages (cited by title and section, never quoted):
+
+* CubicQuant article on ModelScope, "CubicQuant：用三次曲线重塑低比特量化，Kimi K3
+  2.5Bit 模型首发实践" (below: *the CubicQuant article*).
+  - section "CubicQuant 核心：把直线网格掰弯" (*Core*): the positive-side maximum
+    code, the normalised magnitude t of a code, the cubic q(t) with c = 1 - a - b,
+    the reconstructed weight, and the three properties (q(0) = 0, q(1) = 1,
+    q'(t) > 0; a = 1, b = 0 is symmetric uniform INT). The display equations of
+    this section did not survive text extraction; the readings used here are
+    listed under "Readings" below.
+  - section "存储开销是透明的：B+64/G bit" (*Storage*): per group of G weights the
+    format holds G B-bit integer codes, one FP32 scale and two FP16 shape
+    parameters, so B + 64/G bits per weight; first table (bits per weight for
+    G = 128, 256, 512) and second table (bytes per weight and ratio to BF16 at
+    G512).
+  - section "一份 checkpoint，同时服务 A16 与 Dynamic A8" (*A16/A8*): A16 consumes
+    the continuous levels with FP16/BF16 activations; Dynamic A8 quantises each
+    activation row to INT8 at run time, maps the weight levels to a deterministic
+    INT8 carrier, takes integer dot products and scales per group in FP32. The
+    carrier equation did not survive extraction.
+  - section "Kimi-K3-Cubic-2.5Bit 是怎样得到 2.4986 bit 的？" (*Mix*): the per-layer
+    format plan and the payload / metadata arithmetic.
+* msModelSlim article on ai6s.net (Kimi K3 INT quantisation), section
+  "具体量化策略", sub-section on routed experts (W4A8): activations are quantised
+  dynamically per token.
+
+Readings (where the pages are silent or their equations were stripped):
+
+* Kmax = 2^(B-1) - 1; t = |k| / Kmax; q(t) = a t + b t^2 + (1 - a - b) t^3;
+  w = s * sign(k) * q(t). Supported widths B in [2, 8].
+* Codes are B-bit two's complement fields in one LSB-first bitstream over the
+  row-major [N][K] matrix (little-endian bytes).
+* Groups are G consecutive weights along K within a row; scales are a float32
+  array [N][K/G]; shapes are float16 bit patterns [N][K/G][2] (a, then b).
+* The code -2^(B-1) (outside the symmetric range) decodes by the same formula
+  (t > 1); the carrier clamps it.
+* A8 carrier: C_j = clamp(RNE(127 * q_j), -127, 127) and the group scale is
+  s / 127. Activation scale: sx = fp32(amax / 127), xq = clamp(RNE(fp32(x / sx)),
+  -127, 127); an all-zero row gives sx = 0 and xq = 0.
+
+Exactness: a and b are fp16, hence integer multiples of 2^-24. For |a|, |b| <= 16
+every term of Q_j = a j K^2 + b j^2 K + c j^3 (with K = Kmax) is a multiple of
+2^-24 below 2^28, so Q_j is exact in float64 (at most 52 significant bits);
+q_j = Q_j / K^3 and s * q_j each round once in float64.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "kmax", "bits_per_weight", "code_bytes", "storage_bytes",
+    "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
+    "level_numerators", "levels", "dequant", "gemm_a16",
+    "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
+]
+
+# Domain in which the float64 evaluation of Q_j is exact (see module docstring).
+_SHAPE_ABS_MAX = 16.0
+
+
+def kmax(bits: int) -> int:
+    """Positive-side maximum code, 2^(B-1) - 1 (CubicQuant article, Core)."""
+    if not 2 <= bits <= 8:
+        raise ValueError(f"bits must be in [2, 8], got {bits}")
+    return (1 << (bits - 1)) - 1
+
+
+# ----------------------------------------------------------------------------
+# Storage (CubicQuant article, Storage section and its two tables)
+# ----------------------------------------------------------------------------
+def bits_per_weight(bits: int, group: int) -> Fraction:
+    """B payload bits plus 32 (fp32 scale) + 2 * 16 (fp16 a, b) bits per group."""
+    return Fraction(bits) + Fraction(32 + 2 * 16, group)
+
+
+def code_bytes(N: int, K: int, bits: int) -> int:
+    """Bytes of the packed code stream of an N x K matrix."""
+    total_bits = N * K * bits
+    if total_bits % 8:
+        raise ValueError("N*K*bits must be a multiple of 8")
+    return total_bits // 8
+
+
+def storage_bytes(N: int, K: int, bits: int, group: int) -> int:
+    """Code stream plus 8 bytes of metadata per group."""
+    if K % group:
+        raise ValueError("K must be a multiple of group")
+    return code_bytes(N, K, bits) + 8 * N * (K // group)
+
+
+# ----------------------------------------------------------------------------
+# Code stream (reading: B-bit two's complement, LSB-first, row-major [N][K])
+# ----------------------------------------------------------------------------
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """int codes [N][K] -> packed uint8 [N][K*bits/8]. Rejects |k| > Kmax."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    km = kmax(bits)
+    if codes.size and (codes.min() < -km or codes.max() > km):
+        raise ValueError("code outside [-Kmax, Kmax]")
+    if (K * bits) % 8:
+        raise ValueError("K*bits must be a multiple of 8")
+    field = codes.astype(np.int64) & ((1 << bits) - 1)          # two's complement
+    bitplanes = (field[..., None] >> np.arange(bits)) & 1        # [N][K][bits], LSB first
+    stream = bitplanes.reshape(N, K * bits).astype(np.uint8)
+    return np.packbits(stream, axis=1, bitorder="little")
+
+
+def unpack(packed: np.ndarray, N: int, K: int, bits: int) -> np.ndarray:
+    """packed uint8 [N][K*bits/8] (or flat) -> int8 codes [N][K]."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(N, (K * bits) // 8)
+    stream = np.unpackbits(packed, axis=1, bitorder="little").astype(np.int64)
+    bitplanes = stream.reshape(N, K, bits)
+    field = (bitplanes << np.arange(bits)).sum(axis=2)
+    signed = np.where(field >= (1 << (bits - 1)), field - (1 << bits), field)
+    return signed.astype(np.int8)
+
+
+# ----------------------------------------------------------------------------
+# Scalar decodings of the stored floating-point formats
+# ----------------------------------------------------------------------------
+def f16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    return np.asarray(u16, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    u32 = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16
+    return u32.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Levels (CubicQuant article, Core)
+# ----------------------------------------------------------------------------
+def level_numerators(a: np.ndarray, b: np.ndarray, bits: int) -> np.ndarray:
+    """Q_j = Kmax^3 * q(j / Kmax) for j = 0 .. 2^(B-1), exact in float64.
+
+    a, b: float64 arrays (values of fp16 numbers), any shape S. Returns S + (2^(B-1)+1,).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size and (np.abs(a).max() > _SHAPE_ABS_MAX or np.abs(b).max() > _SHAPE_ABS_MAX):
+        raise ValueError("shape parameters outside the exactly evaluated domain |a|,|b| <= 16")
+    km = float(kmax(bits))
+    j = np.arange((1 << (bits - 1)) + 1, dtype=np.float64)
+    c = 1.0 - a - b
+    return (a[..., None] * (j * km * km)
+            + b[..., None] * (j * j * km)
+            + c[..., None] * (j * j * j))
+
+
+def levels(a: np.ndarray, b: np.ndarray, bits: int) -> np.ndarray:
+    """q_j = q(j / Kmax) for j = 0 .. 2^(B-1) (j = 2^(B-1) is the extra negative code)."""
+    km = float(kmax(bits))
+    return level_numerators(a, b, bits) / (km * km * km)
+
+
+def _group_params(scales, shapes, N, K, group):
+    G = K // group
+    s = np.asarray(scales, dtype=np.float32).reshape(N, G).astype(np.float64)
+    ab = np.asarray(shapes, dtype=np.uint16).reshape(N, G, 2)
+    return s, f16_bits_to_f64(ab[..., 0]), f16_bits_to_f64(ab[..., 1])
+
+
+def dequant(codes: np.ndarray, scales: np.ndarray, shapes: np.ndarray,
+            bits: int, group: int) -> np.ndarray:
+    """W[n,k] = s * sign(k) * q(|k| / Kmax) in float64; code 0 gives +0.0."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    if K % group:
+        raise ValueError("K must be a multiple of group")
+    s, a, b = _group_params(scales, shapes, N, K, group)
+    w_level = s[..., None] * levels(a, b, bits)                  # [N][G][2^(B-1)+1]
+    mag = np.abs(codes.astype(np.int64)).reshape(N, K // group, group)
+    w = np.take_along_axis(w_level, mag, axis=2).reshape(N, K)
+    sign = np.sign(codes.astype(np.int64))
+    return np.where(codes == 0, 0.0, sign * w)
+
+
+# ----------------------------------------------------------------------------
+# A16 (CubicQuant article, A16/A8 section): activations consume continuous levels
+# ----------------------------------------------------------------------------
+def gemm_a16(x_bf16: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Y[m,n] = sum_k x[m,k] * W[n,k] in float64 (x given as bf16 bit patterns)."""
+    X = bf16_bits_to_f64(x_bf16)
+    return X @ np.asarray(W, dtype=np.float64).T
+
+
+# ----------------------------------------------------------------------------
+# Dynamic A8 (CubicQuant article, A16/A8 section; msModelSlim article, per-token
+# dynamic activation quantisation)
+# ----------------------------------------------------------------------------
+def act_quant(x_bf16: np.ndarray):
+    """Per-row INT8 quantisation: returns (xq int8 [M][K], sx float32 [M]).
+
+    sx = fp32(amax / 127); xq = clamp(RNE(fp32(x / sx)), -127, 127). Each fp32
+    division is a float64 division rounded to float32, which equals the IEEE
+    fp32 quotient (53 >= 2*24 + 2, so the double rounding is innocuous).
+    """
+    X = bf16_bits_to_f64(x_bf16)
+    M = X.shape[0]
+    amax = np.abs(X).max(axis=1) if X.shape[1] else np.zeros(M)
+    sx = (amax / 127.0).astype(np.float32)
+    xq = np.zeros(X.shape, dtype=np.int8)
+    nz = sx != 0
+    if nz.any():
+        r = (X[nz] / sx[nz].astype(np.float64)[:, None]).astype(np.float32)
+        xq[nz] = np.clip(np.rint(r.astype(np.float64)), -127, 127).astype(np.int8)
+    return xq, sx
+
+
+def _rne_div(num: np.ndarray, den: int) -> np.ndarray:
+    """Round-to-nearest-even of num / den for int64 num and a positive int den."""
+    q = np.floor_divide(num, den)
+    r = num - q * den                       # 0 <= r < den
+    up = (2 * r > den) | ((2 * r == den) & (q % 2 != 0))
+    return q + up.astype(np.int64)
+
+
+def carrier_table(a: np.ndarray, b: np.ndarray, bits: int) -> np.ndarray:
+    """C_j = clamp(RNE(127 * q_j), -127, 127) for j = 0 .. 2^(B-1), exactly.
+
+    Uses integers: with A = a * 2^24 (exact for fp16), Q_j * 2^24 is an integer,
+    so 127 * q_j = 127 * (Q_j * 2^24) / (Kmax^3 * 2^24) is a ratio of int64s.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size and (np.abs(a).max() > _SHAPE_ABS_MAX or np.abs(b).max() > _SHAPE_ABS_MAX):
+        raise ValueError("shape parameters outside the exactly evaluated domain |a|,|b| <= 16")
+    km = kmax(bits)
+    A = (a * 2.0 ** 24).astype(np.int64)
+    B = (b * 2.0 ** 24).astype(np.int64)
+    C = (1 << 24) - A - B
+    j = np.arange((1 << (bits - 1)) + 1, dtype=np.int64)
+    Q = A[..., None] * (j * km * km) + B[..., None] * (j * j * km) + C[..., None] * (j * j * j)
+    return np.clip(_rne_div(127 * Q, km ** 3 << 24), -127, 127)
+
+
+def carrier_codes(codes: np.ndarray, shapes: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Per-weight INT8 carrier sign(k) * C_|k| as int64 [N][K]."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    ab = np.asarray(shapes, dtype=np.uint16).reshape(N, K // group, 2)
+    tab = carrier_table(f16_bits_to_f64(ab[..., 0]), f16_bits_to_f64(ab[..., 1]), bits)
+    mag = np.abs(codes.astype(np.int64)).reshape(N, K // group, group)
+    c = np.take_along_axis(tab, mag, axis=2).reshape(N, K)
+    return np.sign(codes.astype(np.int64)) * c
+
+
+def gemm_a8(xq: np.ndarray, sx: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+            shapes: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Y[m,n] = sx_m * sum_g (s_{n,g} / 127) * I[m,n,g], I = exact integer group dot."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    G = K // group
+    Cw = carrier_codes(codes, shapes, bits, group).astype(np.float64)
+    Xq = np.asarray(xq, dtype=np.float64)
+    s = np.asarray(scales, dtype=np.float32).reshape(N, G).astype(np.float64)
+    Y = np.zeros((Xq.shape[0], N), dtype=np.float64)
+    for g in range(G):
+        sl = slice(g * group, (g + 1) * group)
+        I = Xq[:, sl] @ Cw[:, sl].T        # integers below 2^53: exact in float64
+        Y += I * (s[:, g] / 127.0)[None, :]
+    return np.asarray(sx, dtype=np.float32).astype(np.float64)[:, None] * Y
+
+
+# ----------------------------------------------------------------------------
+# Routed experts: each (token, slot) pair is an A16 product with its expert
+# ----------------------------------------------------------------------------
+def moe_a16(x_bf16: np.ndarray, topk_ids: np.ndarray, num_experts: int, N: int,
+            expert_weight) -> np.ndarray:
+    """Y[t, j, :] = W_e @ x[t] with e = topk_ids[t, j]; ids outside [0, E) give zeros.
+
+    expert_weight(e) -> float64 W_e [N][K] (the caller dequantises its experts).
+    """
+    ids = np.asarray(topk_ids)
+    T, topk = ids.shape
+    X = bf16_bits_to_f64(x_bf16)
+    Y = np.zeros((T, topk, N), dtype=np.float64)
+    cache = {}
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if not 0 <= e < num_experts:
+                continue
+            if e not in cache:
+                cache[e] = np.asarray(expert_weight(e), dtype=np.float64)
+            Y[t, j] = cache[e] @ X[t]
+    return Y

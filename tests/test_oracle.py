@@ -1,0 +1,381 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU. Sources:
+* storage numbers and the 2.4986-bit arithmetic: printed tables of the CubicQuant
+  article (ModelScope), sections on storage cost and on the K3 layer plan;
+* level endpoints, order and the uniform-INT special case: properties stated in
+  the CubicQuant article's core section;
+* everything else: exact rational brute force on tiny inputs (tests/_exact.py),
+  written from the definitions with loops and independent of the oracle's code.
+"""
+import json
+import os
+import random
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import _exact as ex
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16bits(v):
+    return int(np.array(v, dtype=np.float16).view(np.uint16))
+
+
+def _random_shapes(n, seed):
+    import synth
+    g = synth.make_generator(seed)
+    ab = synth.sample_shapes(g, n).numpy().view(np.uint16)
+    return ab
+
+
+# ----------------------------------------------------------------------------- storage
+def test_storage_table_matches_printed_values():
+    t = _load("storage_tables.json")
+    for g, row in t["bits_per_weight"].items():
+        g = int(g)
+        assert float(oracle.bits_per_weight(2, g) - 2) == row["meta"]
+        for w in (2, 3, 4):
+            assert float(oracle.bits_per_weight(w, g)) == row[f"W{w}"]
+    for w in (2, 3, 4):
+        bpw = oracle.storage_bytes(1, 512, w, 512) / 512
+        assert bpw == t["g512_bytes_per_weight"][f"W{w}"]
+        assert round(2.0 / bpw, 2) == t["g512_ratio_vs_bf16_2dp"][f"W{w}"]
+
+
+def test_k3_effective_bits_arithmetic():
+    t = _load("storage_tables.json")
+    plan = t["k3_layer_plan"]
+    layers = sum(p["layers"] for p in plan)
+    payload = sum(F(p["layers"] * p["bits"]) for p in plan) / layers
+    total = sum(p["layers"] * oracle.bits_per_weight(p["bits"], p["group"]) for p in plan) / layers
+    assert round(float(payload), 4) == t["k3_payload_bits_4dp"]
+    assert round(float(total - payload), 4) == t["k3_metadata_bits_4dp"]
+    assert round(float(total), 4) == t["k3_effective_bits_4dp"]
+
+
+def test_storage_bytes_counts_codes_and_metadata():
+    assert oracle.code_bytes(6144, 7168, 2) == 11_010_048
+    assert oracle.storage_bytes(6144, 7168, 2, 512) == 11_010_048 + 8 * 6144 * 14
+    with pytest.raises(ValueError):
+        oracle.storage_bytes(4, 100, 2, 64)
+
+
+# ----------------------------------------------------------------------------- code stream
+def test_pack_vectors():
+    for v in _load("pack_vectors.json")["vectors"]:
+        codes = np.array([v["codes"]], dtype=np.int8)
+        packed = oracle.pack(codes, v["bits"])
+        assert packed.tobytes().hex() == v["hex"]
+        assert np.array_equal(oracle.unpack(packed, 1, codes.shape[1], v["bits"]), codes)
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_pack_matches_bitwise_reading(bits):
+    rng = np.random.default_rng(bits)
+    km = (1 << (bits - 1)) - 1
+    N, K = 3, 16
+    codes = rng.integers(-km, km + 1, size=(N, K)).astype(np.int8)
+    packed = oracle.pack(codes, bits)
+    stream = packed.tobytes()
+    for n in range(N):
+        for k in range(K):
+            field = ex.read_field(stream, (n * K + k) * bits, bits)
+            assert ex.signed_code(field, bits) == codes[n, k]
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_unpack_full_field_range(bits):
+    # every field value, including the extra negative code -2^(B-1)
+    vals = np.arange(-(1 << (bits - 1)), 1 << (bits - 1))
+    K = ((len(vals) + 7) // 8) * 8
+    row = np.resize(vals, K).astype(np.int64)
+    field = row & ((1 << bits) - 1)
+    stream = 0
+    for i, f in enumerate(field):
+        stream |= int(f) << (i * bits)
+    packed = np.frombuffer(stream.to_bytes(K * bits // 8, "little"), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack(packed, 1, K, bits)[0], row.astype(np.int8))
+
+
+def test_pack_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        oracle.pack(np.array([[-2, 0, 0, 0]], dtype=np.int8), 2)
+    with pytest.raises(ValueError):
+        oracle.pack(np.array([[4, 0, 0, 0, 0, 0, 0, 0]], dtype=np.int8), 3)
+
+
+# ----------------------------------------------------------------------------- levels
+def test_level_golden_cases():
+    for c in _load("levels_and_carriers.json")["cases"]:
+        a = np.float64(c["a"])
+        b = np.float64(c["b"])
+        q = oracle.levels(np.array([a]), np.array([b]), c["bits"])[0]
+        exact = [F(s) for s in c["levels"]]
+        assert len(q) == len(exact)
+        for got, want in zip(q, exact):
+            assert abs(F(float(got)) - want) <= abs(want) * F(1, 2 ** 52)
+        assert list(oracle.carrier_table(np.array([a]), np.array([b]), c["bits"])[0]) == c["carrier"]
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_endpoints_exact_and_levels_increasing(bits):
+    ab = _random_shapes(200, seed=10 + bits)
+    a = oracle.f16_bits_to_f64(ab[:, 0])
+    b = oracle.f16_bits_to_f64(ab[:, 1])
+    q = oracle.levels(a, b, bits)
+    km = (1 << (bits - 1)) - 1
+    assert np.all(q[:, 0] == 0.0)
+    assert np.all(q[:, km] == 1.0)                      # extreme codes give +-s exactly
+    assert np.all(np.diff(q[:, : km + 1], axis=1) > 0)  # ordered levels on [0, 1]
+    # exact check of the order on a few groups with rationals
+    for i in range(5):
+        A, B = ex.f16_value(int(ab[i, 0])), ex.f16_value(int(ab[i, 1]))
+        lv = [ex.cubic_q(A, B, F(j, km)) for j in range(km + 1)]
+        assert all(lv[j] < lv[j + 1] for j in range(km))
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_uniform_int_special_case(bits):
+    """a = 1, b = 0 gives the symmetric uniform INT grid s * k / Kmax."""
+    km = (1 << (bits - 1)) - 1
+    rng = np.random.default_rng(100 + bits)
+    N, K, G = 4, 256, 128
+    codes = rng.integers(-km, km + 1, size=(N, K)).astype(np.int8)
+    scales = rng.lognormal(np.log(0.02), 0.3, size=(N, K // G)).astype(np.float32)
+    shapes = np.zeros((N, K // G, 2), dtype=np.uint16)
+    shapes[..., 0] = _f16bits(1.0)
+    shapes[..., 1] = _f16bits(0.0)
+    W = oracle.dequant(codes, scales, shapes, bits, G)
+    for n in range(N):
+        for k in range(0, K, 7):
+            s = F(float(scales[n, k // G]))
+            want = s * codes[n, k] / km
+            assert abs(F(float(W[n, k])) - want) <= abs(want) * F(1, 2 ** 51)
+            # correctly rounded fp32 of the exact value equals fp32 of the oracle value
+            assert float(ex.rn32(want)) == float(np.float32(W[n, k]))
+
+
+def test_dequant_sign_symmetry_and_zero():
+    rng = np.random.default_rng(7)
+    N, K, G, bits = 5, 256, 128, 4
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    scales = rng.lognormal(np.log(0.02), 0.3, size=(N, K // G)).astype(np.float32)
+    shapes = _random_shapes(N * K // G, 3).reshape(N, K // G, 2)
+    W = oracle.dequant(codes, scales, shapes, bits, G)
+    Wn = oracle.dequant(-codes, scales, shapes, bits, G)
+    assert np.all(W == -Wn)
+    z = codes == 0
+    assert np.all(W[z] == 0.0) and not np.any(np.signbit(W[z]))
+    ext = np.abs(codes) == 7
+    s_full = np.repeat(scales, G, axis=1).astype(np.float64)
+    assert np.array_equal(np.abs(W[ext]), s_full[ext])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6])
+def test_dequant_brute_force_from_bytes(bits):
+    rng = np.random.default_rng(200 + bits)
+    N, K, G = 3, 256, 128
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    codes = rng.integers(lo, hi + 1, size=(N, K)).astype(np.int8)   # includes -2^(B-1)
+    field = codes.astype(np.int64) & ((1 << bits) - 1)
+    stream = 0
+    for i, f in enumerate(field.reshape(-1)):
+        stream |= int(f) << (i * bits)
+    raw = stream.to_bytes(N * K * bits // 8, "little")
+    packed = np.frombuffer(raw, dtype=np.uint8)
+    scales = rng.lognormal(np.log(0.02), 0.3, size=(N, K // G)).astype(np.float32)
+    shapes = _random_shapes(N * K // G, 40 + bits).reshape(N, K // G, 2)
+    W = oracle.dequant(oracle.unpack(packed, N, K, bits), scales, shapes, bits, G)
+    for n in range(N):
+        for k in range(K):
+            g = k // G
+            kk = ex.signed_code(ex.read_field(raw, (n * K + k) * bits, bits), bits)
+            want = ex.weight_value(kk, ex.f32_value(float(scales[n, g])),
+                                   ex.f16_value(int(shapes[n, g, 0])), ex.f16_value(int(shapes[n, g, 1])), bits)
+            assert abs(F(float(W[n, k])) - want) <= abs(want) * F(1, 2 ** 51)
+
+
+# ----------------------------------------------------------------------------- A16
+def test_gemm_a16_brute_force_nonsquare():
+    rng = np.random.default_rng(5)
+    M, N, K, G, bits = 3, 5, 256, 128, 3
+    codes = rng.integers(-3, 4, size=(N, K)).astype(np.int8)
+    scales = rng.lognormal(np.log(0.02), 0.3, size=(N, K // G)).astype(np.float32)
+    shapes = _random_shapes(N * K // G, 77).reshape(N, K // G, 2)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xb = (xf.view(np.uint32) >> 16).astype(np.uint16)    # any bf16 patterns will do
+    Y = oracle.gemm_a16(xb, oracle.dequant(codes, scales, shapes, bits, G))
+    assert Y.shape == (M, N)
+    for m in range(M):
+        for n in range(N):
+            acc = F(0)
+            for k in range(K):
+                g = k // G
+                w = ex.weight_value(int(codes[n, k]), ex.f32_value(float(scales[n, g])),
+                                    ex.f16_value(int(shapes[n, g, 0])), ex.f16_value(int(shapes[n, g, 1])), bits)
+                acc += ex.bf16_value(int(xb[m, k])) * w
+            assert abs(F(float(Y[m, n])) - acc) <= F(1, 10 ** 12) * (1 + abs(acc))
+
+
+# ----------------------------------------------------------------------------- act quant
+def _bf16(vals):
+    return (np.asarray(vals, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_act_quant_golden_row():
+    g = _load("levels_and_carriers.json")["act_quant"]
+    xq, sx = oracle.act_quant(_bf16([g["row"]]))
+    assert format(int(sx.view(np.uint32)[0]), "08x") == g["sx_hex_fp32"]
+    assert xq[0].tolist() == g["xq"]
+
+
+def test_act_quant_brute_force_and_invariants():
+    rng = np.random.default_rng(11)
+    M, K = 6, 40
+    x = rng.standard_normal((M, K)).astype(np.float32) * rng.lognormal(0, 3, size=(M, 1)).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xb[3] = 0                                      # zero row
+    xq, sx = oracle.act_quant(xb)
+    for m in range(M):
+        row = [ex.bf16_value(int(v)) for v in xb[m]]
+        amax = max(abs(v) for v in row)
+        if amax == 0:
+            assert sx[m] == 0 and not xq[m].any()
+            continue
+        s = ex.rn32(amax / 127)
+        assert F(float(sx[m])) == s
+        for k in range(K):
+            want = max(-127, min(127, ex.rne_int(ex.rn32(row[k] / s))))
+            assert xq[m, k] == want
+    # sign symmetry and power-of-two scale invariance
+    xq2, sx2 = oracle.act_quant(xb ^ np.uint16(0x8000))
+    assert np.array_equal(xq2, -xq) and np.array_equal(sx2, sx)
+    x4 = (x * 4.0).astype(np.float32)
+    xq4, sx4 = oracle.act_quant((x4.view(np.uint32) >> 16).astype(np.uint16))
+    nz = sx != 0
+    assert np.array_equal(xq4[nz], xq[nz]) and np.array_equal(sx4[nz], sx[nz] * 4)
+    assert np.all(np.abs(xq).max(axis=1)[nz] == 127)
+
+
+# ----------------------------------------------------------------------------- carrier / A8
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_carrier_brute_force(bits):
+    km = (1 << (bits - 1)) - 1
+    ab = _random_shapes(60, seed=300 + bits)
+    tab = oracle.carrier_table(oracle.f16_bits_to_f64(ab[:, 0]), oracle.f16_bits_to_f64(ab[:, 1]), bits)
+    for i in range(ab.shape[0]):
+        A, B = ex.f16_value(int(ab[i, 0])), ex.f16_value(int(ab[i, 1]))
+        for j in range(km + 2):
+            want = max(-127, min(127, ex.rne_int(127 * ex.cubic_q(A, B, F(j, km)))))
+            assert tab[i, j] == want
+
+
+def test_carrier_uniform_int():
+    for bits in range(2, 9):
+        km = (1 << (bits - 1)) - 1
+        tab = oracle.carrier_table(np.array([1.0]), np.array([0.0]), bits)[0]
+        assert [int(v) for v in tab[: km + 1]] == [ex.rne_int(F(127 * j, km)) for j in range(km + 1)]
+
+
+def test_gemm_a8_ternary_special_case():
+    """W2 with a = 1, b = 0: the carrier is 127 k, so each group dot is 127 * sum(xq * k)."""
+    rng = np.random.default_rng(21)
+    M, N, K, G = 4, 6, 512, 128
+    codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    scales = rng.lognormal(np.log(0.015), 0.3, size=(N, K // G)).astype(np.float32)
+    shapes = np.zeros((N, K // G, 2), dtype=np.uint16)
+    shapes[..., 0] = _f16bits(1.0)
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    sx = rng.lognormal(np.log(0.01), 0.5, size=M).astype(np.float32)
+    Y = oracle.gemm_a8(xq, sx, codes, scales, shapes, 2, G)
+    for m in range(M):
+        for n in range(N):
+            acc = F(0)
+            for g in range(K // G):
+                dot = sum(int(xq[m, k]) * int(codes[n, k]) for k in range(g * G, (g + 1) * G))
+                acc += ex.f32_value(float(scales[n, g])) * dot
+            want = ex.f32_value(float(sx[m])) * acc
+            assert abs(F(float(Y[m, n])) - want) <= F(1, 10 ** 12) * (1 + abs(want))
+
+
+def test_gemm_a8_brute_force():
+    rng = np.random.default_rng(22)
+    M, N, K, G, bits = 2, 3, 256, 128, 4
+    codes = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    scales = rng.lognormal(np.log(0.02), 0.3, size=(N, K // G)).astype(np.float32)
+    shapes = _random_shapes(N * K // G, 55).reshape(N, K // G, 2)
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    sx = rng.lognormal(np.log(0.01), 0.5, size=M).astype(np.float32)
+    Y = oracle.gemm_a8(xq, sx, codes, scales, shapes, bits, G)
+    km = 7
+    for m in range(M):
+        for n in range(N):
+            acc = F(0)
+            for g in range(K // G):
+                A, B = ex.f16_value(int(shapes[n, g, 0])), ex.f16_value(int(shapes[n, g, 1]))
+                dot = 0
+                for k in range(g * G, (g + 1) * G):
+                    c = int(codes[n, k])
+                    car = max(-127, min(127, ex.rne_int(127 * ex.cubic_q(A, B, F(abs(c), km)))))
+                    dot += int(xq[m, k]) * (car if c >= 0 else -car)
+                acc += ex.f32_value(float(scales[n, g])) / 127 * dot
+            want = ex.f32_value(float(sx[m])) * acc
+            assert abs(F(float(Y[m, n])) - want) <= F(1, 10 ** 12) * (1 + abs(want))
+
+
+# ----------------------------------------------------------------------------- MoE
+def test_moe_pairs_equal_single_expert_products():
+    rng = np.random.default_rng(31)
+    E, T, topk, N, K, G, bits = 5, 4, 2, 6, 256, 128, 2
+    experts = []
+    for e in range(E):
+        codes = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        scales = rng.lognormal(np.log(0.015), 0.3, size=(N, K // G)).astype(np.float32)
+        shapes = _random_shapes(N * K // G, 500 + e).reshape(N, K // G, 2)
+        experts.append(oracle.dequant(codes, scales, shapes, bits, G))
+    xb = _bf16(rng.standard_normal((T, K)))
+    ids = np.array([[0, 3], [3, 3], [4, -1], [7, 1]], dtype=np.int32)
+    Y = oracle.moe_a16(xb, ids, E, N, lambda e: experts[e])
+    X = oracle.bf16_bits_to_f64(xb)
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            if 0 <= e < E:
+                assert np.array_equal(Y[t, j], experts[e] @ X[t])
+            else:
+                assert not Y[t, j].any()
+
+
+# ----------------------------------------------------------------------------- generators
+def test_generator_shapes_in_increasing_region():
+    ab = _random_shapes(2000, seed=9)
+    a = oracle.f16_bits_to_f64(ab[:, 0])
+    b = oracle.f16_bits_to_f64(ab[:, 1])
+    t = np.linspace(0, 1, 401)
+    qp = a[:, None] + 2 * b[:, None] * t + 3 * (1 - a - b)[:, None] * t * t
+    assert qp.min() > 0
+    assert a.min() >= 0 and a.max() <= 4 and b.min() >= -6.5 and b.max() <= 3
+
+
+def test_generator_determinism_and_distributions():
+    import synth
+    w1, x1 = synth.single_config(seed=1)
+    w2, x2 = synth.single_config(seed=1)
+    assert np.array_equal(w1.codes.numpy(), w2.codes.numpy())
+    assert np.array_equal(x1.float().numpy(), x2.float().numpy())
+    assert int(w1.shapes[0, 0, 0]) & 0xFFFF == _f16bits(1.0) and int(w1.shapes[0, 0, 1]) == 0
+    g = synth.make_generator(3)
+    c = synth.codes_ternary(g, 256, 1024).numpy()
+    assert abs((c == 0).mean() - 0.5) < 0.01 and abs((c == 1).mean() - 0.25) < 0.01
+    c = synth.codes_laplace(g, 64, 1024).numpy()
+    assert c.min() >= -7 and c.max() <= 7 and abs((c == 0).mean() - (1 - np.exp(-(0.5 / 7) / 0.25))) < 0.02
