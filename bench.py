@@ -1,0 +1,244 @@
+"""Benchmark of the CubicQuant dequant-GEMM hot path on one MI355X.
+
+Default workload (one "step"): the Kimi-K3-shaped routed-expert decode at M = 1,
+W2 G512: the fused gate_up product (6144 x 7168) then the down product
+(7168 x 3072), A16 (bf16 activations, fp32 out). Each step reads a different
+copy of the two weights from a rotation pool larger than twice the Infinity
+Cache plus L2, so every launch streams its weights from HBM.
+
+Prints ONE JSON line: metric/value (whole-step HBM GB/s of algorithmic bytes),
+roofline of the dominant kernel (gate_up launch; average duration from HIP
+events recorded on the launch stream around each timed launch), and the oracle
+CPU baseline on a bounded sample. `--extra` adds the prefill (M = 4096) A16 and
+A8 products and the small-M W4 products as extra fields.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, published
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published
+
+
+def algorithmic_bytes(N, K, bits, group, M, a8=False):
+    w = N * K * bits // 8 + 8 * N * (K // group)
+    x = M * K * (1 if a8 else 2) + (4 * M if a8 else 0)
+    y = 4 * M * N
+    return w + x + y
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=40, help="rotating weight copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extra", action="store_true", help="also time prefill and small-M products")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def cpu_baseline(seconds: float):
+    """The oracle (numpy float64, one BLAS thread) on a sample of the decode
+    workload: gate_up rows 0..511 (all K), decode + GEMV, repeated for ~seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+    g = synth.make_generator(2)
+    w = synth.make_weight(g, 512, 7168, 2, 512, "ternary", 0.015)
+    x = synth.activations(g, 1, 7168)
+    codes = w.codes.numpy()
+    scales = w.scales.numpy()
+    shapes = w.shapes.numpy().view(np.uint16)
+    xb = x.view(__import__("torch").int16).numpy().view(np.uint16)
+    packed = oracle.pack(codes, 2)
+    nbytes = algorithmic_bytes(512, 7168, 2, 512, 1)
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            c = oracle.unpack(packed, 512, 7168, 2)
+            W = oracle.dequant(c, scales, shapes, 2, 512)
+            oracle.gemm_a16(xb, W)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"decode gate_up rows 0..511 x K=7168 (W2 G512, M=1): unpack+dequant+GEMV, "
+                      f"{reps} reps in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    import dequant_gemm_amd as cq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    (w_up, x_up), (w_dn, x_dn) = synth.decode_config(seed=2, device=dev)
+
+    def to_cw(w):
+        packed = cq.cubic_pack(w.codes, w.bits).reshape(-1)
+        return cq.CubicWeight(packed, w.scales.contiguous(), w.shapes.contiguous(), w.N, w.K,
+                              w.bits, w.group)
+
+    base_up, base_dn = to_cw(w_up), to_cw(w_dn)
+    del w_up.codes, w_dn.codes
+
+    def clone(cw):
+        return cq.CubicWeight(cw.codes.clone(), cw.scales.clone(), cw.shapes.clone(), cw.N, cw.K,
+                              cw.bits, cw.group)
+
+    R = max(2, args.copies)
+    ups = [base_up] + [clone(base_up) for _ in range(R - 1)]
+    dns = [base_dn] + [clone(base_dn) for _ in range(R - 1)]
+    y_up = torch.empty((1, 6144), dtype=torch.float32, device=dev)
+    y_dn = torch.empty((1, 7168), dtype=torch.float32, device=dev)
+    bytes_up = algorithmic_bytes(6144, 7168, 2, 512, 1)
+    bytes_dn = algorithmic_bytes(7168, 3072, 2, 512, 1)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        cq.cubic_gemm_a16(x_up, ups[i % R], out=y_up)
+        if ev is not None:
+            ev[1].record(stream)
+        cq.cubic_gemm_a16(x_dn, dns[(i + R // 2) % R], out=y_dn)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+
+    # dominant kernel (gate_up launch): events around each launch, same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    up_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    up_avg_ms = sum(up_ms) / len(up_ms)
+    up_med_ms = up_ms[len(up_ms) // 2]
+
+    gbs = (bytes_up + bytes_dn) / (ms_per_step * 1e-3) / 1e9
+    achieved = bytes_up / (up_avg_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            traffic = json.load(open(args.traffic_json)).get("decode_gate_up_bytes_per_launch")
+        except Exception:
+            traffic = None
+    out = {
+        "metric": "Cubic dequant-GEMM HBM GB/s (M=1 decode) and TFLOP/s (M=4096), % of roofline",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "K3 routed-expert decode, W2 G512, M=1, A16: gate_up 6144x7168 + "
+                               "down 7168x3072 per step", "rotating_weight_copies": R,
+                   "algorithmic_bytes_per_step": bytes_up + bytes_dn},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_gemv<DecodeW2> (gate_up 6144x7168, M=1)",
+                     "avg_launch_us": round(up_avg_ms * 1e3, 3),
+                     "median_launch_us": round(up_med_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": bytes_up},
+    }
+    if args.extra:
+        out["extra"] = extra_workloads(cq, synth, dev, stream)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _time(fn, reps, stream):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def extra_workloads(cq, synth, dev, stream):
+    import torch
+    res = {}
+    w, x = synth.prefill_config(seed=5, device=dev)
+    cw = cq.CubicWeight(cq.cubic_pack(w.codes, 3).reshape(-1), w.scales, w.shapes, w.N, w.K, 3, 256)
+    del w.codes
+    flops = 2.0 * 4096 * 6144 * 7168
+    ws = torch.empty(cq.cubic_gemm_a16_workspace_bytes(4096, 7168), dtype=torch.uint8, device=dev)
+    y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
+    ms = _time(lambda: cq.cubic_gemm_a16(x, cw, out=y, workspace=ws), 10, stream)
+    res["prefill_a16"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
+                          "frac_of_f16_peak": round(flops / ms / 1e9 / MFMA_F16_PEAK_TFS, 4)}
+    xq = torch.empty((4096, 7168), dtype=torch.int8, device=dev)
+    sx = torch.empty((4096,), dtype=torch.float32, device=dev)
+    ms_q = _time(lambda: cq.act_quant_int8_per_token(x, xq, sx), 10, stream)
+    ms8 = _time(lambda: cq.cubic_gemm_a8(xq, sx, cw, out=y), 10, stream)
+    res["prefill_a8"] = {"act_quant_ms": round(ms_q, 4), "gemm_ms": round(ms8, 4),
+                         "TOP/s": round(flops / ms8 / 1e9, 2),
+                         "frac_of_i8_peak": round(flops / ms8 / 1e9 / MFMA_I8_PEAK_TOPS, 4),
+                         "act_quant_GB/s": round((4096 * 7168 * 3 + 4096 * 4) / ms_q / 1e6, 1)}
+    del x, xq, y, ws
+    for M in (8, 64):
+        (wu, xu), (wd, xd) = synth.smallm_config(M, seed=3, device=dev)
+        for name, ww, xx in (("gate_up", wu, xu), ("down", wd, xd)):
+            c = cq.CubicWeight(cq.cubic_pack(ww.codes, 4).reshape(-1), ww.scales, ww.shapes, ww.N,
+                               ww.K, 4, 128)
+            wsp = torch.empty(max(1, cq.cubic_gemm_a16_workspace_bytes(M, ww.K)), dtype=torch.uint8,
+                              device=dev)
+            yy = torch.empty((M, ww.N), dtype=torch.float32, device=dev)
+            ms = _time(lambda: cq.cubic_gemm_a16(xx, c, out=yy, workspace=wsp), 50, stream)
+            nb = algorithmic_bytes(ww.N, ww.K, 4, 128, M)
+            res[f"smallm_w4_M{M}_{name}"] = {"us": round(ms * 1e3, 2),
+                                              "GB/s": round(nb / ms / 1e6, 1),
+                                              "note": "L2/MALL-warm (one weight copy)"}
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+"""Thin Python binding of libcubic.so (the CubicQuant dequant-GEMM for gfx950).
+
+Argument marshalling only: every function takes torch tensors, checks their
+dtype, device and contiguity, allocates outputs (and workspaces) with torch, and
+calls the C function of the same name on torch's current HIP stream. All the
+arithmetic runs in the library's HIP kernels; there is no CPU fallback, and a
+missing library raises immediately.
+
+Weight layout (see include/cubic.h): ``codes`` uint8 [N][K*bits/8] bit stream,
+``scales`` float32 [N][K/group], ``shapes`` int16 [N][K/group][2] holding the
+fp16 bit patterns of (a, b).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "CubicError", "CubicWeight", "library_path", "load_library",
+    "cubic_code_bytes", "cubic_storage_bytes", "cubic_pack", "cubic_unpack",
+    "cubic_dequant", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
+    "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_moe_workspace_bytes",
+    "cubic_moe_grouped_gemm", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+EXPORTED_SYMBOLS = [
+    "cubic_code_bytes", "cubic_storage_bytes", "cubic_status_string", "cubic_version",
+    "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_gemm_a16_workspace_bytes",
+    "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8",
+    "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
+]
+
+
+class CubicError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_status_string(status)} ({status})")
+        self.status = status
+
+
+class _CWeight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("shapes", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.environ.get("CUBIC_LIBRARY", os.path.join(_PKG, "lib", "libcubic.so"))
+
+
+_lib = None
+
+
+def load_library():
+    """Load libcubic.so (built by dequant_gemm_amd.build); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libcubic.so not found at {path}; run `python -m dequant_gemm_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    wp = ctypes.POINTER(_CWeight)
+    sigs = {
+        "cubic_code_bytes": (sz, [i64, i64, i32]),
+        "cubic_storage_bytes": (sz, [i64, i64, i32, i32]),
+        "cubic_status_string": (ctypes.c_char_p, [i32]),
+        "cubic_version": (ctypes.c_char_p, []),
+        "cubic_pack": (i32, [vp, i64, i64, i32, vp, vp]),
+        "cubic_unpack": (i32, [vp, i64, i64, i32, vp, vp]),
+        "cubic_dequant": (i32, [wp, vp, vp]),
+        "cubic_gemm_a16_workspace_bytes": (sz, [i64, i64]),
+        "cubic_gemm_a16": (i32, [vp, i64, wp, vp, vp, sz, vp]),
+        "act_quant_int8_per_token": (i32, [vp, i64, i64, vp, vp, vp]),
+        "cubic_gemm_a8": (i32, [vp, vp, i64, wp, vp, vp]),
+        "cubic_moe_workspace_bytes": (sz, [i64, i32, i32, i64]),
+        "cubic_moe_grouped_gemm": (i32, [vp, i64, vp, i32, wp, i32, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().cubic_status_string(status).decode()
+    except Exception:  # pragma: no cover
+        return "status"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise CubicError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+@dataclass
+class CubicWeight:
+    """Device buffers of one Cubic weight (or of E experts back to back)."""
+    codes: torch.Tensor     # uint8, N*K*bits/8 bytes per matrix
+    scales: torch.Tensor    # float32, N*K/group per matrix
+    shapes: torch.Tensor    # int16 (fp16 bit patterns), 2*N*K/group per matrix
+    N: int
+    K: int
+    bits: int
+    group: int
+
+    def c_struct(self) -> _CWeight:
+        _need(self.codes, torch.uint8, "codes")
+        _need(self.scales, torch.float32, "scales")
+        _need(self.shapes, torch.int16, "shapes")
+        return _CWeight(self.codes.data_ptr(), self.scales.data_ptr(), self.shapes.data_ptr(),
+                        self.N, self.K, self.bits, self.group)
+
+
+def cubic_code_bytes(N: int, K: int, bits: int) -> int:
+    return int(load_library().cubic_code_bytes(N, K, bits))
+
+
+def cubic_storage_bytes(N: int, K: int, bits: int, group: int) -> int:
+    return int(load_library().cubic_storage_bytes(N, K, bits, group))
+
+
+def cubic_pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 codes [N][K] -> uint8 bit stream [N][K*bits/8]."""
+    _need(codes, torch.int8, "codes")
+    N, K = codes.shape
+    if out is None:
+        out = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=codes.device)
+    _check(load_library().cubic_pack(_ptr(codes), N, K, bits, _ptr(out), _stream(codes)), "cubic_pack")
+    return out
+
+
+def cubic_unpack(packed: torch.Tensor, N: int, K: int, bits: int,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(packed, torch.uint8, "packed")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _check(load_library().cubic_unpack(_ptr(packed), N, K, bits, _ptr(out), _stream(packed)),
+           "cubic_unpack")
+    return out
+
+
+def cubic_dequant(w: CubicWeight, out: torch.Tensor | None = None) -> torch.Tensor:
+    cw = w.c_struct()
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.codes.device)
+    _check(load_library().cubic_dequant(ctypes.byref(cw), _ptr(out), _stream(w.codes)),
+           "cubic_dequant")
+    return out
+
+
+def cubic_gemm_a16_workspace_bytes(M: int, K: int) -> int:
+    return int(load_library().cubic_gemm_a16_workspace_bytes(M, K))
+
+
+def cubic_gemm_a16(x: torch.Tensor, w: CubicWeight, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M][N] (fp32) = x[M][K] (bf16) * W^T."""
+    _need(x, torch.bfloat16, "x")
+    M = x.shape[0]
+    cw = w.c_struct()
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    need = cubic_gemm_a16_workspace_bytes(M, w.K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(load_library().cubic_gemm_a16(_ptr(x), M, ctypes.byref(cw), _ptr(out), _ptr(workspace),
+                                          ws_bytes, _stream(x)), "cubic_gemm_a16")
+    return out
+
+
+def act_quant_int8_per_token(x: torch.Tensor, xq: torch.Tensor | None = None,
+                             x_scale: torch.Tensor | None = None):
+    """bf16 [M][K] -> (int8 [M][K], fp32 [M])."""
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(load_library().act_quant_int8_per_token(_ptr(x), M, K, _ptr(xq), _ptr(x_scale), _stream(x)),
+           "act_quant_int8_per_token")
+    return xq, x_scale
+
+
+def cubic_gemm_a8(xq: torch.Tensor, x_scale: torch.Tensor, w: CubicWeight,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(xq, torch.int8, "xq")
+    _need(x_scale, torch.float32, "x_scale")
+    M = xq.shape[0]
+    cw = w.c_struct()
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float32, device=xq.device)
+    _check(load_library().cubic_gemm_a8(_ptr(xq), _ptr(x_scale), M, ctypes.byref(cw), _ptr(out),
+                                        _stream(xq)), "cubic_gemm_a8")
+    return out
+
+
+def cubic_moe_workspace_bytes(T: int, topk: int, E: int, K: int) -> int:
+    return int(load_library().cubic_moe_workspace_bytes(T, topk, E, K))
+
+
+def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: CubicWeight, E: int,
+                           out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[T][topk][N] (fp32): each (token, slot) pair times its expert's weights."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, topk = topk_ids.shape
+    cw = experts.c_struct()
+    if out is None:
+        out = torch.empty((T, topk, experts.N), dtype=torch.float32, device=x.device)
+    need = cubic_moe_workspace_bytes(T, topk, E, experts.K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(load_library().cubic_moe_grouped_gemm(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw),
+                                                 E, _ptr(out), _ptr(workspace), workspace.numel(),
+                                                 _stream(x)), "cubic_moe_grouped_gemm")
+    return out

@@ -1,0 +1,244 @@
+// api.cpp -- the C ABI of libcubic.so (declared in include/cubic.h): argument
+// validation on the host, shape dispatch, kernel launches on the caller's
+// stream. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/cubic.h"
+#include "launch.h"
+
+#define CUBIC_API extern "C" __attribute__((visibility("default")))
+
+
+using namespace cubic;
+
+namespace {
+
+constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
+constexpr int64_t kGemvMaxM = 16;          // one MFMA activation tile
+constexpr int64_t kInkMaxM = 4;            // single-kernel A16 path
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+int check_weight(const cubic_weight* w) {
+  if (!w) return CUBIC_ERR_NULL;
+  if (w->N < 0 || w->K < 0) return CUBIC_ERR_SHAPE;
+  if (w->bits < 2 || w->bits > 8) return CUBIC_ERR_BITS;
+  if (w->group <= 0 || w->group % 128 != 0 || w->K % w->group != 0) return CUBIC_ERR_GROUP;
+  if (w->N > 0 && w->K > 0) {
+    if (!w->codes || !w->scales || !w->shapes) return CUBIC_ERR_NULL;
+    if (!aligned16(w->codes) || !aligned16(w->scales) || !aligned16(w->shapes)) return CUBIC_ERR_ALIGN;
+  }
+  return CUBIC_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CUBIC_OK : CUBIC_ERR_HIP; }
+
+// Single-kernel A16 path: M <= 4 and the per-wave activation slices (plus the
+// largest level tables) fit in LDS.
+bool a16_inkernel(int64_t M, int64_t K) {
+  return M <= kInkMaxM && gemv_ink_lds_bytes(M, K, 8) <= kLdsLimit;
+}
+
+std::mutex g_pack_mutex[64];
+
+}  // namespace
+
+CUBIC_API size_t cubic_code_bytes(int64_t N, int64_t K, int bits) {
+  if (N < 0 || K < 0 || bits < 2 || bits > 8) return 0;
+  const int64_t b = N * K * bits;
+  if (b % 8) return 0;
+  return static_cast<size_t>(b / 8);
+}
+
+CUBIC_API size_t cubic_storage_bytes(int64_t N, int64_t K, int bits, int group) {
+  if (group <= 0 || K % group != 0) return 0;
+  const size_t c = cubic_code_bytes(N, K, bits);
+  if (c == 0 && N * K != 0) return 0;
+  return c + static_cast<size_t>(8) * N * (K / group);
+}
+
+CUBIC_API const char* cubic_status_string(int status) {
+  switch (status) {
+    case CUBIC_OK: return "ok";
+    case CUBIC_ERR_NULL: return "null pointer";
+    case CUBIC_ERR_SHAPE: return "invalid shape";
+    case CUBIC_ERR_BITS: return "bits outside [2, 8]";
+    case CUBIC_ERR_GROUP: return "group must be a multiple of 128 dividing K";
+    case CUBIC_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case CUBIC_ERR_CODE_RANGE: return "code outside [-Kmax, Kmax]";
+    case CUBIC_ERR_WORKSPACE: return "workspace missing or too small";
+    case CUBIC_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+CUBIC_API const char* cubic_version(void) { return "cubic 0.1 gfx950"; }
+
+CUBIC_API int cubic_pack(const int8_t* codes, int64_t N, int64_t K, int bits, uint8_t* packed,
+                         cubic_stream_t stream) {
+  if (N < 0 || K < 0 || K % 32 != 0) return CUBIC_ERR_SHAPE;
+  if (bits < 2 || bits > 8) return CUBIC_ERR_BITS;
+  if (N == 0 || K == 0) return CUBIC_OK;
+  if (!codes || !packed) return CUBIC_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(packed)) return CUBIC_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CUBIC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_pack_mutex[dev & 63]);
+  unsigned int bad = 0;
+  const hipError_t e = launch_pack(codes, packed, N, K, bits, static_cast<hipStream_t>(stream), &bad);
+  if (e != hipSuccess) return CUBIC_ERR_HIP;
+  return bad ? CUBIC_ERR_CODE_RANGE : CUBIC_OK;
+}
+
+CUBIC_API int cubic_unpack(const uint8_t* packed, int64_t N, int64_t K, int bits, int8_t* codes,
+                           cubic_stream_t stream) {
+  if (N < 0 || K < 0 || K % 32 != 0) return CUBIC_ERR_SHAPE;
+  if (bits < 2 || bits > 8) return CUBIC_ERR_BITS;
+  if (N == 0 || K == 0) return CUBIC_OK;
+  if (!codes || !packed) return CUBIC_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(packed)) return CUBIC_ERR_ALIGN;
+  return hip_status(launch_unpack(packed, codes, N, K, bits, static_cast<hipStream_t>(stream)));
+}
+
+CUBIC_API int cubic_dequant(const cubic_weight* w, float* out, cubic_stream_t stream) {
+  const int st = check_weight(w);
+  if (st != CUBIC_OK) return st;
+  if (w->N == 0 || w->K == 0) return CUBIC_OK;
+  if (!out) return CUBIC_ERR_NULL;
+  if (!aligned16(out)) return CUBIC_ERR_ALIGN;
+  return hip_status(launch_dequant(w->codes, w->scales, w->shapes, out, w->N, w->K, w->bits,
+                                   w->group, static_cast<hipStream_t>(stream)));
+}
+
+CUBIC_API size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K < 0) return 0;
+  if (a16_inkernel(M, K)) return 0;
+  return align256(static_cast<size_t>(M) * K * 2) + align256(static_cast<size_t>(M) * 4);
+}
+
+CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float* y,
+                             void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  const int st = check_weight(w);
+  if (st != CUBIC_OK) return st;
+  if (M < 0) return CUBIC_ERR_SHAPE;
+  if (M == 0 || w->N == 0) return CUBIC_OK;
+  if (!x_bf16 || !y) return CUBIC_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(y)) return CUBIC_ERR_ALIGN;
+  if (M > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
+  const size_t need = cubic_gemm_a16_workspace_bytes(M, w->K);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need) return CUBIC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CUBIC_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need == 0) {
+    GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
+                 x_bf16, nullptr, nullptr, y};
+    return hip_status(launch_gemv(p, w->bits, true, s));
+  }
+  uint16_t* xp = static_cast<uint16_t*>(workspace);
+  float* xback = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align256(static_cast<size_t>(M) * w->K * 2));
+  const bool use_gemv = M <= kGemvMaxM;
+  hipError_t e = launch_xprep(x_bf16, M, w->K, use_gemv && w->bits == 2, xp, xback, s);
+  if (e != hipSuccess) return CUBIC_ERR_HIP;
+  if (use_gemv) {
+    GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
+                 nullptr, xp, xback, y};
+    return hip_status(launch_gemv(p, w->bits, false, s));
+  }
+  TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xp, xback, y};
+  return hip_status(launch_tiled_a16(p, w->bits, s));
+}
+
+CUBIC_API int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, int8_t* xq,
+                                       float* x_scale, cubic_stream_t stream) {
+  if (M < 0 || K < 0 || K % 8 != 0) return CUBIC_ERR_SHAPE;
+  if (M == 0) return CUBIC_OK;
+  if (!x_bf16 || !xq || !x_scale) return CUBIC_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(xq) || !aligned16(x_scale)) return CUBIC_ERR_ALIGN;
+  if (M > INT32_MAX) return CUBIC_ERR_SHAPE;
+  return hip_status(launch_act_quant(x_bf16, M, K, xq, x_scale, static_cast<hipStream_t>(stream)));
+}
+
+CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
+                            const cubic_weight* w, float* y, cubic_stream_t stream) {
+  const int st = check_weight(w);
+  if (st != CUBIC_OK) return st;
+  if (w->group > 1024) return CUBIC_ERR_GROUP;
+  if (M < 0) return CUBIC_ERR_SHAPE;
+  if (M == 0 || w->N == 0) return CUBIC_OK;
+  if (!xq || !x_scale || !y) return CUBIC_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(y)) return CUBIC_ERR_ALIGN;
+  if ((M + 127) / 128 > 65535) return CUBIC_ERR_SHAPE;
+  TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xq, x_scale, y};
+  return hip_status(launch_tiled_a8(p, w->bits, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+struct MoeLayout {
+  size_t hdr, counts, offsets, active, sorted, xp, xback, total;
+};
+MoeLayout moe_layout(int64_t T, int topk, int E, int64_t K) {
+  MoeLayout L;
+  const size_t P = static_cast<size_t>(T) * topk;
+  size_t o = 0;
+  L.hdr = o;     o += align256(16);
+  L.counts = o;  o += align256(4 * static_cast<size_t>(E));
+  L.offsets = o; o += align256(4 * (static_cast<size_t>(E) + 1));
+  L.active = o;  o += align256(4 * static_cast<size_t>(E));
+  L.sorted = o;  o += align256(4 * P);
+  L.xp = o;      o += align256(static_cast<size_t>(T) * K * 2);
+  L.xback = o;   o += align256(4 * static_cast<size_t>(T));
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K) {
+  if (T < 0 || topk <= 0 || E <= 0 || K < 0) return 0;
+  return moe_layout(T, topk, E, K).total;
+}
+
+CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                                     int topk, const cubic_weight* expert0, int E, float* y,
+                                     void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  const int st = check_weight(expert0);
+  if (st != CUBIC_OK) return st;
+  if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
+  if (T == 0 || expert0->N == 0) return CUBIC_OK;
+  if (T * topk > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
+  if (!x_bf16 || !topk_ids || !y || !workspace) return CUBIC_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(y) || !aligned16(workspace))
+    return CUBIC_ERR_ALIGN;
+  const MoeLayout L = moe_layout(T, topk, E, expert0->K);
+  if (ws_bytes < L.total) return CUBIC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws + L.xp);
+  float* xback = reinterpret_cast<float*>(ws + L.xback);
+  hipError_t e = launch_xprep(x_bf16, T, expert0->K, expert0->bits == 2, xp, xback, s);
+  if (e != hipSuccess) return CUBIC_ERR_HIP;
+  MoeGemvParams p{};
+  p.codes = expert0->codes;
+  p.scales = expert0->scales;
+  p.shapes = expert0->shapes;
+  p.N = expert0->N;
+  p.K = expert0->K;
+  p.group = expert0->group;
+  p.topk = topk;
+  p.code_bytes = static_cast<int64_t>(cubic_code_bytes(expert0->N, expert0->K, expert0->bits));
+  p.xp = xp;
+  p.xback = xback;
+  p.y = y;
+  e = launch_moe(topk_ids, static_cast<int>(T * topk), E, topk, p,
+                 reinterpret_cast<int32_t*>(ws + L.hdr), reinterpret_cast<int32_t*>(ws + L.counts),
+                 reinterpret_cast<int32_t*>(ws + L.offsets), reinterpret_cast<int32_t*>(ws + L.active),
+                 reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s);
+  return hip_status(e);
+}

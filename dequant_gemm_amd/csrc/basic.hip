@@ -1,0 +1,235 @@
+// basic.hip -- code-stream pack/unpack, fp32 dequant and per-row INT8
+// activation quantisation (HBM-bound elementwise kernels).
+//
+// Stream layout: one LSB-first bit stream over the row-major [N][K] code matrix,
+// each code a `bits`-wide two's complement field (the CubicQuant article on
+// ModelScope only says the codes are plain 1-8 bit integers packed densely; the
+// bit order is this library's reading). With K a multiple of 32 each block of 32
+// consecutive codes of a row occupies exactly `bits` dwords, so one thread owns
+// one block and no two threads touch the same dword.
+#include "common.h"
+#include "launch.h"
+
+namespace cubic {
+
+__device__ unsigned int g_pack_range_error;   // set by k_pack, read by the host
+
+__global__ void k_clear_pack_flag() {
+  if (threadIdx.x == 0 && blockIdx.x == 0) g_pack_range_error = 0u;
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ codes,
+                                              uint32_t* __restrict__ out, int64_t nblocks) {
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blk >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(codes + blk * 32);
+  const u32x4 lo = src[0], hi = src[1];
+  const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  constexpr int km = kmax_of(BITS);
+  uint32_t w[BITS];
+#pragma unroll
+  for (int d = 0; d < BITS; ++d) w[d] = 0u;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int k = static_cast<int8_t>((words[i >> 2] >> (8 * (i & 3))) & 0xffu);
+    bad |= (k > km) | (k < -km);
+    const uint32_t f = static_cast<uint32_t>(k) & ((1u << BITS) - 1u);
+    const int bit = i * BITS, d = bit >> 5, off = bit & 31;
+    w[d] |= f << off;
+    if (off + BITS > 32) w[d + 1] |= f >> (32 - off);
+  }
+  uint32_t* dst = out + blk * BITS;
+#pragma unroll
+  for (int d = 0; d < BITS; ++d) dst[d] = w[d];
+  if (bad) atomicOr(&g_pack_range_error, 1u);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ in,
+                                                int8_t* __restrict__ codes, int64_t nblocks) {
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blk >= nblocks) return;
+  uint32_t w[BITS];
+  const uint32_t* src = in + blk * BITS;
+#pragma unroll
+  for (int d = 0; d < BITS; ++d) w[d] = src[d];
+  uint32_t words[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) words[q] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int k = sign_extend(chunk_field<BITS>(w, i), BITS);
+    words[i >> 2] |= (static_cast<uint32_t>(k) & 0xffu) << (8 * (i & 3));
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(codes + blk * 32);
+  dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+  dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+}
+
+// One thread per 32-code block: fp64 level evaluation, one rounding to fp32.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ stream,
+                                                 const float* __restrict__ scales,
+                                                 const uint16_t* __restrict__ shapes,
+                                                 float* __restrict__ out, int64_t nblocks,
+                                                 int64_t K, int group) {
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blk >= nblocks) return;
+  const int64_t k0 = blk * 32;                  // flat index of the first code
+  const int64_t n = k0 / K, kk = k0 - n * K;
+  const int64_t g = n * (K / group) + kk / group;
+  const double s = static_cast<double>(scales[g]);
+  const double a = f16_bits_to_f64(shapes[2 * g]);
+  const double b = f16_bits_to_f64(shapes[2 * g + 1]);
+  constexpr int km = kmax_of(BITS);
+  uint32_t w[BITS];
+  const uint32_t* src = stream + blk * BITS;
+#pragma unroll
+  for (int d = 0; d < BITS; ++d) w[d] = src[d];
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int k = sign_extend(chunk_field<BITS>(w, i), BITS);
+    const int j = k < 0 ? -k : k;
+    const float mag = static_cast<float>(s * level_q(a, b, j, km));
+    v[i] = (k == 0) ? 0.0f : (k < 0 ? -mag : mag);
+  }
+  f32x4* dst = reinterpret_cast<f32x4*>(out + k0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+
+// Per-row INT8 quantisation, one 256-thread block per row (two passes over the
+// row; the second pass hits L2). Division is IEEE fp32 (__fdiv_rn), rounding is
+// rintf (ties to even), as the msModelSlim article's per-token dynamic scheme
+// and this library's reading of the A8 scale (amax / 127) prescribe.
+__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ x, int64_t K,
+                                                   int8_t* __restrict__ xq,
+                                                   float* __restrict__ xs) {
+  const int64_t m = blockIdx.x;
+  const uint16_t* row = x + m * K;
+  int8_t* qrow = xq + m * K;
+  const int tid = threadIdx.x;
+  const int64_t nvec = K / 8;                   // K is a multiple of 8 (checked on the host)
+  const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+  float amax = 0.0f;
+  for (int64_t i = tid; i < nvec; i += 256) {
+    const u32x4 v = rv[i];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(u[q] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
+    }
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sx = __fdiv_rn(amax, 127.0f);
+  if (tid == 0) xs[m] = sx;
+  uint2* qv = reinterpret_cast<uint2*>(qrow);
+  for (int64_t i = tid; i < nvec; i += 256) {
+    const u32x4 v = rv[i];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float xv = __uint_as_float(h ? (u[q] & 0xffff0000u) : (u[q] << 16));
+        int qi = 0;
+        if (sx != 0.0f) {
+          float r = rintf(__fdiv_rn(xv, sx));
+          r = fminf(fmaxf(r, -127.0f), 127.0f);
+          qi = static_cast<int>(r);
+        }
+        const int e = 2 * q + h;                // element 0..7 of the vector
+        o[e >> 2] |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * (e & 3));
+      }
+    }
+    qv[i] = make_uint2(o[0], o[1]);
+  }
+}
+
+}  // namespace cubic
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (called from api.cpp after validation).
+// ---------------------------------------------------------------------------
+namespace cubic {
+
+#define CUBIC_DISPATCH_BITS(bits, FN, ...)              \
+  switch (bits) {                                       \
+    case 2: FN<2>(__VA_ARGS__); break;                  \
+    case 3: FN<3>(__VA_ARGS__); break;                  \
+    case 4: FN<4>(__VA_ARGS__); break;                  \
+    case 5: FN<5>(__VA_ARGS__); break;                  \
+    case 6: FN<6>(__VA_ARGS__); break;                  \
+    case 7: FN<7>(__VA_ARGS__); break;                  \
+    default: FN<8>(__VA_ARGS__); break;                 \
+  }
+
+template <int B>
+static void launch_pack_b(const int8_t* codes, uint8_t* packed, int64_t nblocks, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>((nblocks + 255) / 256);
+  hipLaunchKernelGGL(k_pack<B>, dim3(grid), dim3(256), 0, st, codes,
+                     reinterpret_cast<uint32_t*>(packed), nblocks);
+}
+
+template <int B>
+static void launch_unpack_b(const uint8_t* packed, int8_t* codes, int64_t nblocks, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>((nblocks + 255) / 256);
+  hipLaunchKernelGGL(k_unpack<B>, dim3(grid), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(packed), codes, nblocks);
+}
+
+template <int B>
+static void launch_dequant_b(const uint8_t* stream, const float* scales, const uint16_t* shapes,
+                             float* out, int64_t nblocks, int64_t K, int group, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>((nblocks + 255) / 256);
+  hipLaunchKernelGGL(k_dequant<B>, dim3(grid), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(stream), scales, shapes, out, nblocks, K,
+                     group);
+}
+
+hipError_t launch_pack(const int8_t* codes, uint8_t* packed, int64_t N, int64_t K, int bits,
+                       hipStream_t st, unsigned int* range_error) {
+  hipLaunchKernelGGL(k_clear_pack_flag, dim3(1), dim3(64), 0, st);
+  const int64_t nblocks = N * K / 32;
+  CUBIC_DISPATCH_BITS(bits, launch_pack_b, codes, packed, nblocks, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  unsigned int flag = 0;
+  e = hipMemcpyFromSymbolAsync(&flag, HIP_SYMBOL(g_pack_range_error), sizeof(flag), 0,
+                               hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return e;
+  e = hipStreamSynchronize(st);
+  *range_error = flag;
+  return e;
+}
+
+hipError_t launch_unpack(const uint8_t* packed, int8_t* codes, int64_t N, int64_t K, int bits,
+                         hipStream_t st) {
+  const int64_t nblocks = N * K / 32;
+  CUBIC_DISPATCH_BITS(bits, launch_unpack_b, packed, codes, nblocks, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint16_t* shapes,
+                          float* out, int64_t N, int64_t K, int bits, int group, hipStream_t st) {
+  const int64_t nblocks = N * K / 32;
+  CUBIC_DISPATCH_BITS(bits, launch_dequant_b, stream, scales, shapes, out, nblocks, K, group, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_act_quant, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xq, xs);
+  return hipGetLastError();
+}
+
+}  // namespace cubic

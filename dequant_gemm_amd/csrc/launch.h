@@ -1,0 +1,68 @@
+// launch.h -- parameter blocks and host launchers shared by the kernel files
+// and the C ABI layer (api.cpp). Host-visible only; no device code here.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cubic {
+
+struct GemvParams {
+  const uint8_t* codes;
+  const float* scales;
+  const uint16_t* shapes;
+  int64_t N, K;
+  int group;
+  int M;
+  const uint16_t* x;      // bf16 [M][K] (in-kernel conversion)
+  const uint16_t* xp;     // fp16 [M][K] prepared, chunk-permuted (prepared variant)
+  const float* xback;     // per-row back multiplier of xp
+  float* y;               // [M][N]
+};
+
+struct TiledParams {
+  const uint8_t* codes;
+  const float* scales;
+  const uint16_t* shapes;
+  int64_t M, N, K;
+  int group;
+  const void* xa;         // A16: fp16 [M][K] prepared; A8: int8 [M][K]
+  const float* xs;        // A16: per-row back multiplier; A8: per-row scale
+  float* y;
+};
+
+struct MoeGemvParams {
+  const uint8_t* codes;   // expert 0
+  const float* scales;
+  const uint16_t* shapes;
+  int64_t N, K;
+  int group, topk;
+  int64_t code_bytes;     // per expert
+  const int32_t* hdr;
+  const int32_t* offsets;
+  const int32_t* active;
+  const int32_t* sorted;
+  const uint16_t* xp;     // prepared activations [T][K]
+  const float* xback;     // [T]
+  float* y;               // [T*topk][N]
+};
+
+hipError_t launch_pack(const int8_t* codes, uint8_t* packed, int64_t N, int64_t K, int bits,
+                       hipStream_t st, unsigned int* range_error);
+hipError_t launch_unpack(const uint8_t* packed, int8_t* codes, int64_t N, int64_t K, int bits,
+                         hipStream_t st);
+hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint16_t* shapes,
+                          float* out, int64_t N, int64_t K, int bits, int group, hipStream_t st);
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
+                            hipStream_t st);
+hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st);
+size_t gemv_ink_lds_bytes(int64_t M, int64_t K, int bits);
+hipError_t launch_xprep(const uint16_t* x, int64_t M, int64_t K, bool w2_order, uint16_t* xp,
+                        float* xback, hipStream_t st);
+hipError_t launch_tiled_a16(const TiledParams& p, int bits, hipStream_t st);
+hipError_t launch_tiled_a8(const TiledParams& p, int bits, hipStream_t st);
+hipError_t launch_moe(const int32_t* ids, int P, int E, int topk, const MoeGemvParams& base,
+                      int32_t* hdr, int32_t* counts, int32_t* offsets, int32_t* active,
+                      int32_t* sorted, int bits, hipStream_t st);
+
+}  // namespace cubic

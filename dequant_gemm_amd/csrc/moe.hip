@@ -1,0 +1,177 @@
+// moe.hip -- routed-expert A16 products grouped by expert on the device.
+//
+// The K3 expert layer (Kimi K3 guide, model-card table: 896 experts, 16 active
+// per token) runs every (token, slot) pair against its expert's Cubic weights.
+// The CubicQuant article (section on the A16/A8 crossover) notes that routing
+// density changes which kernel wins; here the pairs are grouped per expert so
+// that every touched expert's weights stream from HBM once per launch, whatever
+// the number of tokens that picked it.
+//
+// k_moe_route (one block): per-expert counts, exclusive scan into offsets,
+// the compacted list of touched experts, and the pair ids sorted by expert.
+// Invalid ids are counted in hdr[0] and their output rows zeroed. No host sync.
+// k_moe_gemv (persistent): work item = (touched expert, 16-row tile); the
+// expert's pairs form the activation rows of the MFMA tile (16 per pass).
+#include "gemv_core.h"
+#include "launch.h"
+
+namespace cubic {
+
+__global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ ids, int P, int E,
+                                                    int64_t N, float* __restrict__ y,
+                                                    int32_t* __restrict__ hdr,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ sorted) {
+  __shared__ int32_t s_sum[1024];
+  __shared__ int32_t s_act[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) counts[e] = 0;
+  if (tid == 0) hdr[0] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) {
+      atomicAdd(&counts[e], 1);
+    } else {
+      atomicAdd(&hdr[0], 1);
+    }
+  }
+  // zero the output rows of invalid pairs (rare)
+  for (int p = 0; p < P; ++p) {
+    const int e = ids[p];
+    if (e < 0 || e >= E) {
+      for (int64_t n = tid; n < N; n += 1024) y[static_cast<int64_t>(p) * N + n] = 0.0f;
+    }
+  }
+  __syncthreads();
+  // each thread scans a contiguous segment of experts
+  const int seg = (E + 1023) / 1024;
+  const int e0 = tid * seg, e1 = min(E, e0 + seg);
+  int sum = 0, act = 0;
+  for (int e = e0; e < e1; ++e) {
+    sum += counts[e];
+    act += counts[e] > 0;
+  }
+  s_sum[tid] = sum;
+  s_act[tid] = act;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 per-thread totals
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int a = tid >= o ? s_sum[tid - o] : 0;
+    const int b = tid >= o ? s_act[tid - o] : 0;
+    __syncthreads();
+    s_sum[tid] += a;
+    s_act[tid] += b;
+    __syncthreads();
+  }
+  int run = s_sum[tid] - sum, arun = s_act[tid] - act;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = run;
+    const int c = counts[e];
+    if (c > 0) active[arun++] = e;
+    run += c;
+  }
+  if (tid == 1023) {
+    offsets[E] = s_sum[1023];
+    hdr[1] = s_act[1023];
+  }
+  __syncthreads();
+  // counts become write cursors
+  for (int e = e0; e < e1; ++e) counts[e] = offsets[e];
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) sorted[atomicAdd(&counts[e], 1)] = p;
+  }
+}
+
+template <class Dec, int P>
+__global__ __launch_bounds__(256) void k_moe_gemv(MoeGemvParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int B = Dec::kBits;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15, kb = lane >> 4;
+  float* red = reinterpret_cast<float*>(smem);
+  uint16_t* tab_wave = reinterpret_cast<uint16_t*>(smem + 4 * 16 * 16 * 4) +
+                       wave * (tab_bytes_per_wave<Dec>() / 2);
+  const int nsteps = static_cast<int>(p.K / kStep);
+  const int sb = wave * nsteps / 4, se = (wave + 1) * nsteps / 4;
+  const int64_t tiles = (p.N + 15) / 16;
+  const int64_t gpr = p.K / p.group;
+  const int64_t items = static_cast<int64_t>(p.hdr[1]) * tiles;
+
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int a = static_cast<int>(it / tiles);
+    const int64_t n0 = (it - static_cast<int64_t>(a) * tiles) * 16;
+    const int e = p.active[a];
+    const int beg = p.offsets[e], cnt = p.offsets[e + 1] - beg;
+    const int64_t nrow = (n0 + nl < p.N) ? (n0 + nl) : (p.N - 1);
+    CoreArgs c;
+    c.crow = reinterpret_cast<const uint32_t*>(p.codes + e * p.code_bytes + nrow * (p.K * B / 8));
+    c.srow = p.scales + (static_cast<int64_t>(e) * p.N + nrow) * gpr;
+    c.abrow = reinterpret_cast<const uint32_t*>(p.shapes + ((static_cast<int64_t>(e) * p.N + nrow) * gpr) * 2);
+    c.group = p.group;
+    c.sb = sb; c.se = se; c.nl = nl; c.kb = kb; c.K = p.K;
+    c.xs_wave = nullptr; c.spw = 0; c.tab_wave = tab_wave;
+    for (int mt = 0; mt < cnt; mt += 16) {
+      const int Mt = min(16, cnt - mt);
+      const int pair = p.sorted[beg + mt + (nl < Mt ? nl : 0)];
+      const int tok = pair / p.topk;
+      c.M = Mt;
+      c.xrow = p.xp + static_cast<int64_t>(tok) * p.K;
+      const f32x4 acc = gemv_core<Dec, false, P>(c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kb + r) * 16 + nl] = acc[r];
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < Mt * 16) {
+        const int m = t >> 4, cc = t & 15;
+        if (n0 + cc < p.N) {
+          const int pr = p.sorted[beg + mt + m];
+          float v = red[(0 * 16 + m) * 16 + cc];
+          v += red[(1 * 16 + m) * 16 + cc];
+          v += red[(2 * 16 + m) * 16 + cc];
+          v += red[(3 * 16 + m) * 16 + cc];
+          p.y[static_cast<int64_t>(pr) * p.N + n0 + cc] = v * p.xback[pr / p.topk];
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <class Dec, int P>
+static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, unsigned grid, hipStream_t st) {
+  const size_t lds = 4 * 16 * 16 * 4 + 4 * tab_bytes_per_wave<Dec>();
+  hipLaunchKernelGGL((k_moe_gemv<Dec, P>), dim3(grid), dim3(256), lds, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe(const int32_t* ids, int P, int E, int topk, const MoeGemvParams& base,
+                      int32_t* hdr, int32_t* counts, int32_t* offsets, int32_t* active,
+                      int32_t* sorted, int bits, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, hdr,
+                     counts, offsets, active, sorted);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  MoeGemvParams p = base;
+  p.topk = topk;
+  p.hdr = hdr; p.offsets = offsets; p.active = active; p.sorted = sorted;
+  const int64_t tiles = (p.N + 15) / 16;
+  const int64_t max_items = static_cast<int64_t>(min(E, P)) * tiles;
+  const unsigned grid = static_cast<unsigned>(max_items < 4096 ? max_items : 4096);
+  if (grid == 0) return hipSuccess;
+  switch (bits) {
+    case 2: return launch_moe_gemv_t<DecodeW2, 4>(p, grid, st);
+    case 3: return launch_moe_gemv_t<DecodeTable<3>, 4>(p, grid, st);
+    case 4: return launch_moe_gemv_t<DecodeTable<4>, 4>(p, grid, st);
+    case 5: return launch_moe_gemv_t<DecodeTable<5>, 2>(p, grid, st);
+    case 6: return launch_moe_gemv_t<DecodeTable<6>, 2>(p, grid, st);
+    case 7: return launch_moe_gemv_t<DecodeTable<7>, 2>(p, grid, st);
+    default: return launch_moe_gemv_t<DecodeTable<8>, 2>(p, grid, st);
+  }
+}
+
+}  // namespace cubic

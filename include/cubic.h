@@ -1,0 +1,146 @@
+/* cubic.h -- C ABI of libcubic.so: CubicQuant weight-only dequant-GEMM for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: the CubicQuant article on ModelScope ("CubicQuant：用三次曲线重塑低比特量化，
+ * Kimi K3 2.5Bit 模型首发实践"). Each weight is a B-bit signed integer code k; per
+ * group of G weights the format stores one fp32 scale s and two fp16 shape
+ * parameters a, b (section "存储开销是透明的：B+64/G bit", so B + 64/G bits per
+ * weight). With Kmax = 2^(B-1) - 1 and t = |k| / Kmax the weight is
+ *     w = s * sign(k) * q(t),   q(t) = a t + b t^2 + (1 - a - b) t^3
+ * (section "CubicQuant 核心：把直线网格掰弯"; its equations did not survive text
+ * extraction and this is the reading the library implements). A16 multiplies
+ * bf16 activations with these continuous levels; Dynamic A8 quantises each
+ * activation row to INT8 at run time and multiplies it with an INT8 carrier of
+ * the levels, scaling each group in fp32 (section "一份 checkpoint，同时服务 A16 与
+ * Dynamic A8"). Decoding happens tile-locally inside the product kernels and no
+ * full-precision weight matrix is ever written (section "压缩权重必须边解码、边计算").
+ *
+ * General contract
+ *  - Every array argument is a DEVICE pointer owned by the caller. The library
+ *    never allocates or frees device memory; scratch space is passed in as
+ *    `workspace` where a call needs it.
+ *  - Calls validate all arguments on the host first. On a validation error
+ *    nothing is enqueued and nothing is written; the error code is returned.
+ *  - Valid calls enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return without waiting, except cubic_pack (see there).
+ *  - Launch failures are reported as CUBIC_ERR_HIP.
+ *  - Outputs must not alias inputs. Non-finite inputs propagate unchecked.
+ *  - Every pointer must be 16-byte aligned.
+ *
+ * Weight layout (struct cubic_weight)
+ *  - codes : uint8 [N][K*bits/8]. One LSB-first bit stream over the row-major
+ *            [N][K] code matrix; each code is a `bits`-wide two's complement
+ *            field. Rows are byte-aligned (K*bits is a multiple of 8).
+ *  - scales: fp32 [N][K/group]: s of group g = k / group of row n.
+ *  - shapes: fp16 bit patterns [N][K/group][2]: a, then b.
+ *  - bits in [2, 8]; group a multiple of 128; K a multiple of group.
+ *    Codes are expected in [-Kmax, Kmax]; the extra field value -2^(B-1)
+ *    decodes by the same formula (t > 1).
+ */
+#ifndef CUBIC_H
+#define CUBIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* cubic_stream_t;
+
+enum {
+  CUBIC_OK = 0,
+  CUBIC_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  CUBIC_ERR_SHAPE = -2,       /* negative size, or K/N/M not as required       */
+  CUBIC_ERR_BITS = -3,        /* bits outside [2, 8]                           */
+  CUBIC_ERR_GROUP = -4,       /* group not a multiple of 128, or K % group     */
+  CUBIC_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned              */
+  CUBIC_ERR_CODE_RANGE = -6,  /* cubic_pack found a code with |k| > Kmax       */
+  CUBIC_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required    */
+  CUBIC_ERR_HIP = -8          /* a HIP runtime call or a launch failed         */
+};
+
+typedef struct cubic_weight {
+  const uint8_t* codes;
+  const float* scales;
+  const uint16_t* shapes;
+  int64_t N, K;
+  int32_t bits, group;
+} cubic_weight;
+
+/* Size helpers (host only, no GPU needed). Storage section of the CubicQuant
+ * article: B bits per weight plus 64 bits per group. Return 0 for invalid args. */
+size_t cubic_code_bytes(int64_t N, int64_t K, int bits);
+size_t cubic_storage_bytes(int64_t N, int64_t K, int bits, int group);
+const char* cubic_status_string(int status);
+/* Library version string, e.g. "cubic 0.1 gfx950". */
+const char* cubic_version(void);
+
+/* Pack int8 codes [N][K] into the bit stream packed[N][K*bits/8].
+ * K must be a multiple of 32. Codes with |k| > Kmax are written as their
+ * low `bits` bits AND make the call return CUBIC_ERR_CODE_RANGE: to report
+ * that, this call waits for its own kernel (one stream synchronisation).
+ * Calls on one device are serialised by a host lock around that check. */
+int cubic_pack(const int8_t* codes, int64_t N, int64_t K, int bits,
+               uint8_t* packed, cubic_stream_t stream);
+
+/* Unpack the bit stream into int8 codes [N][K] (sign-extended fields, including
+ * -2^(B-1)). K must be a multiple of 32. Bit-exact inverse of cubic_pack. */
+int cubic_unpack(const uint8_t* packed, int64_t N, int64_t K, int bits,
+                 int8_t* codes, cubic_stream_t stream);
+
+/* Materialise the decoded weights out[N][K] in fp32 (a test and inspection
+ * utility; the GEMMs never call it). Each value is s * q_j evaluated in fp64
+ * with the numerator a*j*Kmax^2 + b*j^2*Kmax + (1-a-b)*j^3 exact, one division
+ * by Kmax^3, one product with s and one rounding to fp32 (<= 1 fp32 ulp from the
+ * exact value). Code 0 gives +0.0; codes +-Kmax give +-s exactly. */
+int cubic_dequant(const cubic_weight* w, float* out, cubic_stream_t stream);
+
+/* A16 product y[M][N] = x[M][K] * W^T, x in bf16 (bit patterns), y in fp32.
+ * Internally x is converted to fp16 after scaling each row by a power of two
+ * (exact) so that its largest magnitude sits just below 2^15; levels are fp16,
+ * accumulation fp32. Rows with M <= 4 take a single-kernel path that needs no
+ * workspace; larger M first writes the converted activations into `workspace`.
+ * cubic_gemm_a16_workspace_bytes(M, K) gives the required size (0 when none is
+ * needed); `workspace` may be NULL when that size is 0. M == 0 is a no-op. */
+size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K);
+int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w,
+                   float* y, void* workspace, size_t ws_bytes, cubic_stream_t stream);
+
+/* Dynamic per-token INT8 quantisation (msModelSlim article on Kimi K3 INT
+ * quantisation, routed-expert W4A8 scheme; CubicQuant article, A16/A8 section):
+ * for each row m, amax = max |x[m][:]|, x_scale[m] = fp32(amax / 127) (IEEE
+ * division), xq[m][k] = clamp(rint(fp32(x[m][k] / x_scale[m])), -127, 127) with
+ * ties to even. An all-zero row gives x_scale = 0 and xq = 0. Bit-exact. */
+int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K,
+                             int8_t* xq, float* x_scale, cubic_stream_t stream);
+
+/* Dynamic A8 product y[M][N] (fp32) from xq/x_scale of act_quant_int8_per_token.
+ * Each code maps to the INT8 carrier C = sign(k) * clamp(rne(127 * q(|k|/Kmax)),
+ * -127, 127) (computed exactly with integer arithmetic); per group the exact
+ * int32 dot I = sum xq * C is scaled by fp32(s / 127) and accumulated in fp32;
+ * the row result is multiplied by x_scale[m]. group must be <= 1024 so that I
+ * stays below 2^24. M == 0 is a no-op. */
+int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
+                  const cubic_weight* w, float* y, cubic_stream_t stream);
+
+/* Routed-expert A16 products. E experts with identical (N, K, bits, group) lie
+ * back to back: expert e's codes start at expert0->codes + e*code_bytes, its
+ * scales at expert0->scales + e*N*(K/group), its shapes at expert0->shapes +
+ * 2*e*N*(K/group). For every pair (t, j): y[t][j][:] = x[t][:] * W_{topk_ids[t][j]}^T
+ * (fp32 out, layout [T][topk][N]). Ids outside [0, E) produce zero rows and are
+ * counted; the count is left in the first 4 bytes of the workspace (int32).
+ * Grouping by expert happens on the device (no host synchronisation); each
+ * touched expert's weights are read once per launch. */
+size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K);
+int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
+                           const int32_t* topk_ids, int topk,
+                           const cubic_weight* expert0, int E,
+                           float* y, void* workspace, size_t ws_bytes,
+                           cubic_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CUBIC_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every symbol include/cubic.h declares, and
+rejects invalid arguments on the host before any GPU call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_gemm_amd as cq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cubic.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_BITS, ERR_GROUP, ERR_ALIGN, ERR_RANGE, ERR_WS, ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_matches_binding_list():
+    assert _declared() == sorted(cq.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cq.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_size_helpers_match_storage_formula():
+    # B + 64/G bits per weight (CubicQuant article, storage section)
+    assert cq.cubic_code_bytes(6144, 7168, 2) == 11_010_048
+    assert cq.cubic_storage_bytes(6144, 7168, 2, 512) == 11_010_048 + 8 * 6144 * 14
+    assert cq.cubic_storage_bytes(1, 512, 3, 512) / 512 == 0.390625
+    assert cq.cubic_code_bytes(3, 5, 3) == 0          # not a whole number of bytes
+    assert cq.cubic_code_bytes(4, 64, 9) == 0
+    assert cq.cubic_storage_bytes(4, 300, 2, 128) == 0
+
+
+def test_workspace_sizes():
+    assert cq.cubic_gemm_a16_workspace_bytes(1, 7168) == 0
+    assert cq.cubic_gemm_a16_workspace_bytes(4, 7168) == 0
+    assert cq.cubic_gemm_a16_workspace_bytes(8, 7168) >= 8 * 7168 * 2 + 8 * 4
+    assert cq.cubic_moe_workspace_bytes(64, 16, 896, 7168) >= 64 * 7168 * 2 + 4 * (3 * 896 + 1024)
+    lib = cq.load_library()
+    assert lib.cubic_status_string(ERR_WS) == b"workspace missing or too small"
+    assert lib.cubic_version().startswith(b"cubic")
+
+
+def _w(N=256, K=512, bits=3, group=128, codes=16, scales=16, shapes=16):
+    return cq._CWeight(codes, scales, shapes, N, K, bits, group)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=1), ERR_BITS), (dict(bits=9), ERR_BITS),
+    (dict(group=64), ERR_GROUP), (dict(group=256, K=384), ERR_GROUP), (dict(group=0), ERR_GROUP),
+    (dict(N=-1), ERR_SHAPE), (dict(codes=0), ERR_NULL), (dict(scales=8), ERR_ALIGN),
+])
+def test_weight_validation_before_launch(kw, status):
+    lib = cq.load_library()
+    w = _w(**kw)
+    p16 = ctypes.c_void_p(16)
+    assert lib.cubic_gemm_a16(p16, 4, ctypes.byref(w), p16, None, 0, None) == status
+    assert lib.cubic_dequant(ctypes.byref(w), p16, None) == status
+    assert lib.cubic_gemm_a8(p16, p16, 4, ctypes.byref(w), p16, None) == status
+
+
+def test_call_argument_validation_before_launch():
+    lib = cq.load_library()
+    w = _w()
+    p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
+    assert lib.cubic_gemm_a16(None, 4, ctypes.byref(w), p16, None, 0, None) == ERR_NULL
+    assert lib.cubic_gemm_a16(p8, 4, ctypes.byref(w), p16, None, 0, None) == ERR_ALIGN
+    assert lib.cubic_gemm_a16(p16, -1, ctypes.byref(w), p16, None, 0, None) == ERR_SHAPE
+    assert lib.cubic_gemm_a16(p16, 0, ctypes.byref(w), p16, None, 0, None) == OK   # no-op
+    assert lib.cubic_gemm_a16(p16, 8, ctypes.byref(w), p16, None, 0, None) == ERR_WS
+    assert lib.cubic_gemm_a16(p16, 8, ctypes.byref(w), p16, p16, 10, None) == ERR_WS
+    assert lib.cubic_gemm_a16(None, 4, None, p16, None, 0, None) == ERR_NULL
+    w_big_group = _w(group=2048, K=4096)
+    assert lib.cubic_gemm_a8(p16, p16, 4, ctypes.byref(w_big_group), p16, None) == ERR_GROUP
+    assert lib.act_quant_int8_per_token(p16, 4, 100, p16, p16, None) == ERR_SHAPE
+    assert lib.act_quant_int8_per_token(None, 4, 128, p16, p16, None) == ERR_NULL
+    assert lib.act_quant_int8_per_token(p16, 0, 128, p16, p16, None) == OK
+    assert lib.cubic_pack(p16, 4, 48, 3, p16, None) == ERR_SHAPE
+    assert lib.cubic_pack(p16, 4, 64, 9, p16, None) == ERR_BITS
+    assert lib.cubic_unpack(None, 4, 64, 3, p16, None) == ERR_NULL
+    assert lib.cubic_unpack(p16, 4, 64, 3, p8, None) == ERR_ALIGN
+    need = lib.cubic_moe_workspace_bytes(4, 2, 8, 512)
+    assert lib.cubic_moe_grouped_gemm(p16, 4, p16, 2, ctypes.byref(w), 8, p16, p16, need - 1, None) == ERR_WS
+    assert lib.cubic_moe_grouped_gemm(p16, 4, p16, 0, ctypes.byref(w), 8, p16, p16, need, None) == ERR_SHAPE
+    assert lib.cubic_moe_grouped_gemm(p16, 4, None, 2, ctypes.byref(w), 8, p16, p16, need, None) == ERR_NULL
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports the oracle; the library is the only compute."""
+    pkg = os.path.join(ROOT, "dequant_gemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f

@@ -1,0 +1,151 @@
+"""GPU parity of the A16 product (cubic_gemm_a16) against the float64 oracle.
+
+Bar: per-row infinity-norm relative error <= 2e-3 (an all-zero reference row must
+come back exactly zero), on every workload at full size, on small shapes that
+span several tiles with ragged tails, and on the edge cases of the format."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemm_amd as cq
+import oracle
+import synth
+from tests._gpu import DEV, np_weight, row_rel_err, say, upload, x_bits
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _check(w: synth.Weight, x: torch.Tensor, rows=None, tol=TOL):
+    cw = upload(w)
+    y = cq.cubic_gemm_a16(x.to(DEV), cw)
+    y2 = cq.cubic_gemm_a16(x.to(DEV), cw)
+    assert torch.equal(y, y2), "repeat call not bitwise identical"
+    yn = y.cpu().numpy()
+    codes, scales, shapes = np_weight(w)
+    xb = x_bits(x)
+    if rows is not None:
+        xb, yn = xb[rows], yn[rows]
+    ref = oracle.gemm_a16(xb, oracle.dequant(codes, scales, shapes, w.bits, w.group))
+    err = row_rel_err(yn, ref)
+    assert err <= tol, err
+    return err
+
+
+def test_single_workload_w3g128():
+    say("A16 single W3 G128 256x512 M=4")
+    w, x = synth.single_config(seed=1)
+    _check(w, x)
+
+
+def test_decode_workload_full():
+    for (w, x), name in zip(synth.decode_config(seed=2, device=DEV), ("gate_up", "down")):
+        say(f"A16 decode W2 G512 {name} {w.N}x{w.K} M=1")
+        _check(w, x)
+
+
+@pytest.mark.parametrize("M", [8, 64])
+def test_smallm_workload_full(M):
+    for (w, x), name in zip(synth.smallm_config(M, seed=3, device=DEV), ("gate_up", "down")):
+        say(f"A16 small-M W4 G128 {name} {w.N}x{w.K} M={M}")
+        _check(w, x)
+
+
+def test_prefill_workload_full_sampled_rows():
+    say("A16 prefill W3 G256 6144x7168 M=4096 (sampled rows)")
+    w, x = synth.prefill_config(seed=5, device=DEV)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 4095], rng.choice(4096, 45, replace=False)]))
+    _check(w, x, rows=rows)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 512), (2, 128), (3, 128), (3, 256), (4, 128),
+                                        (5, 256), (6, 128), (7, 128), (8, 256)])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 16, 17, 100])
+def test_small_shapes_ragged(bits, group, M):
+    # N not a multiple of 16 or of 128, K spanning several groups and waves
+    say(f"A16 ragged bits={bits} G={group} M={M}")
+    g = synth.make_generator(1000 + 10 * bits + M)
+    kind = "ternary" if bits == 2 else "uniform"
+    w = synth.make_weight(g, 203, 1536, bits, group, kind, 0.02)
+    x = synth.activations(g, M, 1536, 0.01, 50.0)
+    _check(w, x)
+
+
+def test_extra_negative_code_w2_and_w4():
+    # codes -2^(B-1) decode by the formula (t > 1); W2 exercises the slow path
+    for bits in (2, 4):
+        say(f"A16 extra code bits={bits}")
+        g = torch.Generator().manual_seed(bits)
+        N, K, G = 64, 1024, 512 if bits == 2 else 128
+        raw = torch.randint(0, 256, (N * K * bits // 8,), generator=g).to(torch.uint8)
+        codes = oracle.unpack(raw.numpy(), N, K, bits)
+        sg = synth.make_generator(bits + 10)
+        scales = synth.lognormal_scales(sg, N * K // G, 0.02).reshape(N, K // G)
+        shapes = synth.sample_shapes(sg, N * K // G).reshape(N, K // G, 2)
+        cw = cq.CubicWeight(raw.to(DEV), scales.to(DEV), shapes.to(DEV), N, K, bits, G)
+        for M in (1, 8, 40):
+            x = synth.activations(sg, M, K)
+            y = cq.cubic_gemm_a16(x.to(DEV), cw).cpu().numpy()
+            W = oracle.dequant(codes, scales.numpy(), shapes.numpy().view(np.uint16), bits, G)
+            assert row_rel_err(y, oracle.gemm_a16(x_bits(x), W)) <= TOL
+
+
+def test_uniform_int_special_case_matches_integer_matmul():
+    say("A16 a=1 b=0 vs integer matmul")
+    g = synth.make_generator(77)
+    w = synth.make_weight(g, 130, 1024, 3, 128, "uniform", 0.02)
+    w.shapes[..., 0] = int(np.float16(1.0).view(np.int16))
+    w.shapes[..., 1] = 0
+    x = synth.activations(g, 3, 1024)
+    y = cq.cubic_gemm_a16(x.to(DEV), upload(w)).cpu().numpy()
+    codes, scales, _ = np_weight(w)
+    X = oracle.bf16_bits_to_f64(x_bits(x))
+    ref = np.zeros((3, 130))
+    for gi in range(1024 // 128):
+        sl = slice(gi * 128, (gi + 1) * 128)
+        ref += (X[:, sl] @ codes[:, sl].T.astype(np.float64)) * (scales[:, gi] / 3.0)[None, :]
+    assert row_rel_err(y, ref) <= TOL
+
+
+def test_activation_range_extremes_and_zero_rows():
+    # rows far outside the fp16 range, tiny rows, an all-zero row
+    say("A16 activation range extremes")
+    g = synth.make_generator(88)
+    w = synth.make_weight(g, 96, 1024, 2, 512, "ternary", 0.015)
+    cw = upload(w)
+    for M in (4, 12, 130):
+        x = torch.randn((M, 1024), generator=g).float()
+        x[0] *= 1e6
+        x[1] *= 1e-30
+        x[2] = 0.0
+        xb = x.to(torch.bfloat16)
+        y = cq.cubic_gemm_a16(xb.to(DEV), cw).cpu().numpy()
+        codes, scales, shapes = np_weight(w)
+        ref = oracle.gemm_a16(x_bits(xb), oracle.dequant(codes, scales, shapes, 2, 512))
+        assert np.all(y[2] == 0.0)
+        assert row_rel_err(y, ref) <= TOL
+
+
+def test_empty_and_degenerate():
+    say("A16 M=0 and N=1")
+    g = synth.make_generator(99)
+    w = synth.make_weight(g, 1, 512, 3, 128, "uniform", 0.02)
+    cw = upload(w)
+    y = cq.cubic_gemm_a16(torch.zeros((0, 512), dtype=torch.bfloat16, device=DEV), cw)
+    assert y.shape == (0, 1)
+    x = synth.activations(g, 2, 512)
+    y = cq.cubic_gemm_a16(x.to(DEV), cw).cpu().numpy()
+    codes, scales, shapes = np_weight(w)
+    assert row_rel_err(y, oracle.gemm_a16(x_bits(x), oracle.dequant(codes, scales, shapes, 3, 128))) <= TOL
+
+
+def test_workspace_too_small_is_rejected():
+    say("A16 workspace check")
+    g = synth.make_generator(5)
+    w = synth.make_weight(g, 64, 512, 3, 128, "uniform", 0.02)
+    cw = upload(w)
+    x = synth.activations(g, 20, 512).to(DEV)
+    with pytest.raises(cq.CubicError) as e:
+        cq.cubic_gemm_a16(x, cw, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == -7

@@ -1,0 +1,115 @@
+"""GPU parity of the Dynamic A8 path: act_quant_int8_per_token bit-exact against
+the oracle, cubic_gemm_a8 within 2e-3 (per-row infinity norm)."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemm_amd as cq
+import oracle
+import synth
+from tests._gpu import DEV, np_weight, row_rel_err, say, upload, x_bits
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _bf16(t):
+    return t.to(torch.bfloat16)
+
+
+def test_act_quant_golden_row_and_ties():
+    say("act_quant golden row")
+    row = torch.tensor([[2.0, -1.0, 0.5, 0.0, 1.5, 0.0, 0.0, 0.0]])
+    xq, sx = cq.act_quant_int8_per_token(_bf16(row).to(DEV))
+    assert xq.cpu().tolist()[0][:5] == [127, -64, 32, 0, 95]
+    assert format(int(sx.cpu().view(torch.int32)[0]) & 0xFFFFFFFF, "08x") == "3c810204"
+
+
+@pytest.mark.parametrize("M,K", [(1, 8), (5, 520), (64, 7168), (4096, 7168)])
+def test_act_quant_bit_exact(M, K):
+    say(f"act_quant M={M} K={K}")
+    g = torch.Generator().manual_seed(M + K)
+    x = torch.randn((M, K), generator=g) * torch.exp(torch.randn((M, 1), generator=g) * 3)
+    if M > 3:
+        x[1] = 0.0
+        x[2, : K // 2] *= 1e30
+        x[3] *= 1e-35
+    xb = _bf16(x)
+    xq, sx = cq.act_quant_int8_per_token(xb.to(DEV))
+    xq_ref, sx_ref = oracle.act_quant(x_bits(xb))
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+def _check_a8(w, x, rows=None):
+    cw = upload(w)
+    xq, sx = cq.act_quant_int8_per_token(x.to(DEV))
+    y = cq.cubic_gemm_a8(xq, sx, cw)
+    y2 = cq.cubic_gemm_a8(xq, sx, cw)
+    assert torch.equal(y, y2)
+    codes, scales, shapes = np_weight(w)
+    xb = x_bits(x)
+    yn = y.cpu().numpy()
+    if rows is not None:
+        xb, yn = xb[rows], yn[rows]
+    xq_ref, sx_ref = oracle.act_quant(xb)
+    if rows is not None:
+        assert np.array_equal(xq.cpu().numpy()[rows], xq_ref)
+    ref = oracle.gemm_a8(xq_ref, sx_ref, codes, scales, shapes, w.bits, w.group)
+    err = row_rel_err(yn, ref)
+    assert err <= TOL, err
+
+
+def test_prefill_a8_full_sampled_rows():
+    say("A8 prefill W3 G256 6144x7168 M=4096 (sampled rows)")
+    w, x = synth.prefill_config(seed=5, device=DEV)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 46, replace=False)]))
+    _check_a8(w, x, rows=rows)
+
+
+def test_single_workload_a8():
+    say("A8 single W3 G128")
+    w, x = synth.single_config(seed=1)
+    _check_a8(w, x)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 512), (3, 256), (4, 128), (5, 128), (8, 1024)])
+@pytest.mark.parametrize("M", [1, 7, 130])
+def test_a8_ragged(bits, group, M):
+    say(f"A8 ragged bits={bits} G={group} M={M}")
+    g = synth.make_generator(2000 + 10 * bits + M)
+    kind = "ternary" if bits == 2 else "uniform"
+    w = synth.make_weight(g, 203, 2048, bits, group, kind, 0.02)
+    x = synth.activations(g, M, 2048, 0.005, 30.0)
+    _check_a8(w, x)
+
+
+def test_a8_carrier_ties_both_directions():
+    """a=2, b=-1.75 (W3): q(1/3) = 1/2 gives carrier 64 (a tie); a=3.625, b=-1.5:
+    code -4 has q(4/3) = -1/2, carrier -(-64) = 64. Half-up rounding would move
+    either by one unit (1.6 %), far beyond the 2e-3 bar."""
+    for a, b, kset in ((2.0, -1.75, (-1, 1)), (3.625, -1.5, (-4,))):
+        say(f"A8 carrier tie a={a} b={b}")
+        N, K, G = 32, 256, 128
+        g = torch.Generator().manual_seed(3)
+        codes = torch.tensor(kset, dtype=torch.int64)[torch.randint(0, len(kset), (N, K), generator=g)]
+        field = (codes & 7).numpy().astype(np.int64)
+        stream = np.zeros(N * K * 3 // 8, dtype=np.uint8)
+        bitpos = np.arange(N * K) * 3
+        for i in range(3):
+            bit = (field.reshape(-1) >> i) & 1
+            p = bitpos + i
+            np.add.at(stream, p // 8, (bit << (p % 8)).astype(np.uint8))
+        shapes = torch.zeros((N, K // G, 2), dtype=torch.int16)
+        shapes[..., 0] = int(np.float16(a).view(np.int16))
+        shapes[..., 1] = int(np.float16(b).view(np.int16))
+        scales = torch.full((N, K // G), 0.02, dtype=torch.float32)
+        cw = cq.CubicWeight(torch.from_numpy(stream).to(DEV), scales.to(DEV), shapes.to(DEV), N, K, 3, G)
+        x = synth.activations(synth.make_generator(4), 4, K)
+        xq, sx = cq.act_quant_int8_per_token(x.to(DEV))
+        y = cq.cubic_gemm_a8(xq, sx, cw).cpu().numpy()
+        cn = oracle.unpack(stream, N, K, 3)
+        xq_ref, sx_ref = oracle.act_quant(x_bits(x))
+        ref = oracle.gemm_a8(xq_ref, sx_ref, cn, scales.numpy(), shapes.numpy().view(np.uint16), 3, G)
+        assert row_rel_err(y, ref) <= 1e-5

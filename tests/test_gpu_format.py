@@ -1,0 +1,110 @@
+"""GPU parity of the code stream and of the fp32 dequant against the oracle.
+
+Bars: pack / unpack bit-exact; dequant within 1 fp32 ulp of the float64 oracle,
+exact for code 0 (+0.0), codes +-Kmax (+-s) and the uniform-INT case a=1, b=0."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemm_amd as cq
+import oracle
+import synth
+from tests._gpu import DEV, np_weight, say, ulp32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 96), (33, 512), (300, 1024)])
+def test_pack_unpack_bit_exact(bits, N, K):
+    say(f"pack/unpack bits={bits} N={N} K={K}")
+    km = (1 << (bits - 1)) - 1
+    g = torch.Generator().manual_seed(1000 * bits + N + K)
+    codes = torch.randint(-km, km + 1, (N, K), generator=g).to(torch.int8)
+    packed = cq.cubic_pack(codes.to(DEV), bits)
+    ref = oracle.pack(codes.numpy(), bits)
+    assert np.array_equal(packed.cpu().numpy(), ref)
+    # unpack of an arbitrary stream, including the extra field value -2^(B-1)
+    raw = torch.randint(0, 256, (N * K * bits // 8,), generator=g).to(torch.uint8)
+    out = cq.cubic_unpack(raw.to(DEV), N, K, bits)
+    assert np.array_equal(out.cpu().numpy(), oracle.unpack(raw.numpy(), N, K, bits))
+
+
+def test_pack_range_error_reported():
+    say("pack range error")
+    codes = torch.zeros((4, 64), dtype=torch.int8)
+    codes[2, 5] = -2                                  # outside [-1, 1] for 2 bits
+    with pytest.raises(cq.CubicError) as e:
+        cq.cubic_pack(codes.to(DEV), 2)
+    assert e.value.status == -6
+    # the next valid call is clean again
+    cq.cubic_pack(torch.zeros((4, 64), dtype=torch.int8, device=DEV), 2)
+
+
+def test_pack_full_decode_weight():
+    say("pack decode gate_up 6144x7168 W2")
+    (w, _), _ = synth.decode_config(seed=2, device=DEV)
+    packed = cq.cubic_pack(w.codes, 2)
+    ref = oracle.pack(w.codes.cpu().numpy(), 2)
+    assert np.array_equal(packed.cpu().numpy(), ref)
+
+
+def _dequant_check(w: synth.Weight):
+    codes, scales, shapes = np_weight(w)
+    packed = cq.cubic_pack(w.codes.to(DEV), w.bits)
+    cw = cq.CubicWeight(packed.reshape(-1), w.scales.to(DEV), w.shapes.to(DEV), w.N, w.K, w.bits, w.group)
+    got = cq.cubic_dequant(cw).cpu().numpy().astype(np.float64)
+    ref = oracle.dequant(codes, scales, shapes, w.bits, w.group)
+    assert np.all(np.abs(got - ref) <= ulp32(ref)), float((np.abs(got - ref) / ulp32(ref)).max())
+    z = codes == 0
+    assert np.all(got[z] == 0.0) and not np.signbit(got[z]).any()
+    km = (1 << (w.bits - 1)) - 1
+    s_full = np.repeat(scales, w.group, axis=1).astype(np.float64)
+    ext = np.abs(codes.astype(np.int64)) == km
+    assert np.array_equal(np.abs(got[ext]), s_full[ext])
+    return got, ref
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_dequant_within_one_ulp(bits):
+    say(f"dequant bits={bits}")
+    g = synth.make_generator(50 + bits)
+    w = synth.make_weight(g, 40, 1024, bits, 256 if bits % 2 else 128, "uniform", 0.02)
+    _dequant_check(w)
+
+
+def test_dequant_uniform_int_bit_exact():
+    say("dequant a=1 b=0")
+    for bits in (2, 3, 4, 8):
+        g = synth.make_generator(70 + bits)
+        w = synth.make_weight(g, 16, 512, bits, 128, "uniform", 0.02)
+        w.shapes[..., 0] = int(np.float16(1.0).view(np.int16))
+        w.shapes[..., 1] = 0
+        got, _ = _dequant_check(w)
+        km = (1 << (bits - 1)) - 1
+        codes, scales, _ = np_weight(w)
+        s_full = np.repeat(scales, w.group, axis=1).astype(np.float64)
+        want = (s_full * codes / km).astype(np.float32)       # RN32 of s*k/Kmax (see oracle pins)
+        assert np.array_equal(got.astype(np.float32), want)
+
+
+def test_dequant_single_workload_and_extra_code():
+    say("dequant single workload W3 G128")
+    w, _ = synth.single_config(seed=1)
+    _dequant_check(w)
+
+
+def test_dequant_extra_negative_code():
+    say("dequant extra code -2^(B-1)")
+    for bits in (2, 3, 4):
+        g = torch.Generator().manual_seed(bits)
+        N, K, G = 8, 256, 128
+        raw = torch.randint(0, 256, (N * K * bits // 8,), generator=g).to(torch.uint8)
+        codes = oracle.unpack(raw.numpy(), N, K, bits)
+        sg = synth.make_generator(bits)
+        scales = synth.lognormal_scales(sg, N * K // G, 0.02).reshape(N, K // G)
+        shapes = synth.sample_shapes(sg, N * K // G).reshape(N, K // G, 2)
+        cw = cq.CubicWeight(raw.to(DEV), scales.to(DEV), shapes.to(DEV), N, K, bits, G)
+        got = cq.cubic_dequant(cw).cpu().numpy().astype(np.float64)
+        ref = oracle.dequant(codes, scales.numpy(), shapes.numpy().view(np.uint16), bits, G)
+        assert np.all(np.abs(got - ref) <= ulp32(ref))
