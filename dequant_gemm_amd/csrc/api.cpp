@@ -38,10 +38,13 @@ int check_weight(const cubic_weight* w) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CUBIC_OK : CUBIC_ERR_HIP; }
 
-// Single-kernel A16 path: M <= 4 and the per-wave activation slices (plus the
-// largest level tables) fit in LDS.
+// Single-kernel A16 path: M <= 4, and for every width and group size (the worst
+// case is 8 bits, group 128) the per-wave activation slices, level tables and
+// group parameters fit in LDS and a wave spans few enough groups. Depends on
+// (M, K) only, so the workspace size needs no weight description.
 bool a16_inkernel(int64_t M, int64_t K) {
-  return M <= kInkMaxM && gemv_ink_lds_bytes(M, K, 8) <= kLdsLimit;
+  return M <= kInkMaxM && K >= 128 && gemv_ink_lds_bytes(M, K, 8, 128) <= kLdsLimit &&
+         gemv_supported(K, 8, 128) && gemv_supported(K, 3, 128);
 }
 
 std::mutex g_pack_mutex[64];
@@ -136,6 +139,7 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
     if (!aligned16(workspace)) return CUBIC_ERR_ALIGN;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, s));
   if (need == 0) {
     GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
                  x_bf16, nullptr, nullptr, y};
@@ -144,7 +148,7 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
   uint16_t* xp = static_cast<uint16_t*>(workspace);
   float* xback = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           align256(static_cast<size_t>(M) * w->K * 2));
-  const bool use_gemv = M <= kGemvMaxM;
+  const bool use_gemv = M <= kGemvMaxM && gemv_supported(w->K, w->bits, w->group);
   hipError_t e = launch_xprep(x_bf16, M, w->K, use_gemv && w->bits == 2, xp, xback, s);
   if (e != hipSuccess) return CUBIC_ERR_HIP;
   if (use_gemv) {
@@ -176,6 +180,7 @@ CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
   if (!xq || !x_scale || !y) return CUBIC_ERR_NULL;
   if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(y)) return CUBIC_ERR_ALIGN;
   if ((M + 127) / 128 > 65535) return CUBIC_ERR_SHAPE;
+  if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, static_cast<hipStream_t>(stream)));
   TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xq, x_scale, y};
   return hip_status(launch_tiled_a8(p, w->bits, static_cast<hipStream_t>(stream)));
 }
@@ -213,6 +218,8 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
   if (T == 0 || expert0->N == 0) return CUBIC_OK;
   if (T * topk > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
+  if (expert0->K > 0 && !gemv_supported(expert0->K, expert0->bits, expert0->group))
+    return CUBIC_ERR_SHAPE;
   if (!x_bf16 || !topk_ids || !y || !workspace) return CUBIC_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(y) || !aligned16(workspace))
     return CUBIC_ERR_ALIGN;
@@ -222,6 +229,7 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws + L.xp);
   float* xback = reinterpret_cast<float*>(ws + L.xback);
+  if (expert0->K == 0) return hip_status(launch_fill_zero(y, T * topk * expert0->N, s));
   hipError_t e = launch_xprep(x_bf16, T, expert0->K, expert0->bits == 2, xp, xback, s);
   if (e != hipSuccess) return CUBIC_ERR_HIP;
   MoeGemvParams p{};

@@ -155,6 +155,12 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ y, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    y[i] = 0.0f;
+}
+
 }  // namespace cubic
 
 // ---------------------------------------------------------------------------
@@ -229,6 +235,14 @@ hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                             hipStream_t st) {
   hipLaunchKernelGGL(k_act_quant, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xq, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256),
+                     0, st, y, n);
   return hipGetLastError();
 }
 

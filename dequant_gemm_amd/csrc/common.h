@@ -12,6 +12,7 @@
 namespace cubic {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -111,6 +112,15 @@ __device__ __forceinline__ int row_prescale(float amax, float* back) {
   const int e = ilogbf(amax);                   // floor(log2(amax)), exact
   *back = ldexpf(1.0f, e - 14);                 // >= 2^-147: representable
   return 14 - e;
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads. The LDS
+// executes one wave's instructions in order, so only the compiler must not
+// move memory accesses across this point; unlike a release fence it does not
+// wait for outstanding global loads.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Wave-wide max via xor shuffles.

@@ -20,75 +20,153 @@
 
 namespace cubic {
 
-// P = steps kept in flight per lane; INK = activations converted in-kernel.
-template <class Dec, bool INK, int P>
-__global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
+constexpr int kInkWaves = 4;   // waves per workgroup of the single-kernel (in-kernel x) path
+
+// SPL = steps per load, P = macro steps in flight per lane, INK = activations
+// converted in-kernel (M <= 4).
+// MT: compile-time bound on M for the in-kernel activation path (1 or 4).
+// W: waves per workgroup, each streaming 1/W of the K range of the 16 rows.
+template <class Dec, bool INK, int SPL, int P, bool ALLIN, int MT, int W>
+__global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int B = Dec::kBits;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t nrow = (n0 + nl < p.N) ? (n0 + nl) : (p.N - 1);
-  const int nsteps = static_cast<int>(p.K / kStep);
-  const int sb = wave * nsteps / 4, se = (wave + 1) * nsteps / 4;
-  const int spw = (nsteps + 3) / 4;               // LDS steps reserved per wave
+  const GemvGeom geo = gemv_geom(p.K, p.group, SPL, W);
+  const int tb = wave * geo.nmacro / W, te = (wave + 1) * geo.nmacro / W;
   const int M = p.M;
 
-  // LDS carve-up: [red 4x16x16 f32][tables][xs (INK only)]
+  // LDS: [red 4x16x16 f32][tables per wave][group params per wave][xs per wave]
   float* red = reinterpret_cast<float*>(smem);
-  uint16_t* tab_wave = reinterpret_cast<uint16_t*>(smem + 4 * 16 * 16 * 4) +
-                       wave * (tab_bytes_per_wave<Dec>() / 2);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem + 4 * 16 * 16 * 4 + 4 * tab_bytes_per_wave<Dec>());
-  uint16_t* xs_wave = xs + static_cast<int64_t>(wave) * M * spw * kStep;
+  unsigned char* q = smem + W * 16 * 16 * 4;
+  uint16_t* tab_wave = reinterpret_cast<uint16_t*>(q + wave * tab_bytes_per_wave<Dec>());
+  q += W * tab_bytes_per_wave<Dec>();
+  uint32_t* gp_wave = reinterpret_cast<uint32_t*>(q) + wave * 16 * geo.gmax * 2;
+  q += static_cast<size_t>(W) * 16 * geo.gmax * 8;
+  uint16_t* xs_wave = reinterpret_cast<uint16_t*>(q) + static_cast<int64_t>(wave) * M * geo.nch_w * 32;
 
   float xb[4] = {1.0f, 1.0f, 1.0f, 1.0f};        // per-row back multipliers (INK)
-  if constexpr (INK) {
-    const int64_t k0 = static_cast<int64_t>(sb) * kStep;
-    const int nvec = (se - sb) * (kStep / 8);
+  // In-kernel activation staging: each wave copies its own K slice of x into
+  // its own LDS region, chunk-major and in the decoder's slot order.
+  //  - bf16 decoders (2-bit): raw bf16, only permuted (v_perm), no scaling.
+  //  - fp16 decoders: per-row power-of-two prescale over the slice (undone on
+  //    the wave's partial), then fp16.
+  // The first XB 16-element blocks per lane and row are loaded into registers
+  // by issue_x() (before the weight loads; indices clamped so the loads are
+  // unconditional); finish_x() writes them and handles any longer tail.
+  constexpr int XB = 2;
+  const int64_t k0 = static_cast<int64_t>(tb) * kStep * SPL;
+  const int nblk = (te - tb) * kStep * SPL / 16;       // 16-element blocks in the slice
+  u32x4 xreg[INK ? MT : 1][XB][2];
+  auto issue_x = [&]() {
+    if constexpr (INK) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m >= M) break;
-      const u32x4* xv = reinterpret_cast<const u32x4*>(p.x + m * p.K + k0);
-      float amax = 0.0f;
-      for (int i = lane; i < nvec; i += 64) {
-        const u32x4 v = xv[i];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      for (int m = 0; m < MT; ++m) {
+        const u32x4* xv = reinterpret_cast<const u32x4*>(p.x + (m < M ? m : 0) * p.K + k0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          amax = fmaxf(amax, fabsf(__uint_as_float(u[q] << 16)));
-          amax = fmaxf(amax, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
-        }
-      }
-      amax = wave_max(amax);
-      float back;
-      const int sh = row_prescale(amax, &back);
-      xb[m] = back;
-      for (int i = lane; i < nvec; i += 64) {
-        const u32x4 v = xv[i];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (e & 1) ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16);
-          const int kl = 8 * i + e;                         // index within the slice
-          const int ls = kl >> 7, kc = (kl >> 5) & 3, cc = kl & 31;
-          xs_wave[((m * spw + ls) * 4 + kc) * 32 + Dec::code_to_slot(cc)] =
-              f16_bits(ldexpf(__uint_as_float(bits), sh));
+        for (int q = 0; q < XB; ++q) {
+          int i = lane + 64 * q;
+          i = i < nblk ? i : 0;
+          xreg[m][q][0] = xv[2 * i];
+          xreg[m][q][1] = xv[2 * i + 1];
         }
       }
     }
-    __syncthreads();
-  }
+  };
+  auto finish_x = [&]() {
+    if constexpr (INK) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m >= M) break;
+        const u32x4* xv = reinterpret_cast<const u32x4*>(p.x + m * p.K + k0);
+        uint16_t* xo = xs_wave + m * geo.nch_w * 32;
+        if constexpr (Dec::kBf16) {
+          // 16 consecutive codes 16d..16d+15 fill slots 16d..16d+15 as pairs
+          // (code i, code i+8): out[2k] / out[2k+1] take the low / high halves
+          // of input registers k and 4+k.
+          auto put = [&](int i, const u32x4& lo, const u32x4& hi) {
+            const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            uint32_t o[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              o[2 * k] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x05040100u);
+              o[2 * k + 1] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x07060302u);
+            }
+            u32x4* dst = reinterpret_cast<u32x4*>(xo + 16 * i);
+            dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+            dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+          };
+          // unconditional: lanes past the slice rewrite block 0 with block 0's data
+          // (a conditional use would let the compiler sink the loads behind the
+          // weight stream)
+#pragma unroll
+          for (int q = 0; q < XB; ++q) {
+            const int i = lane + 64 * q;
+            put(i < nblk ? i : 0, xreg[m][q][0], xreg[m][q][1]);
+          }
+          for (int i = lane + 64 * XB; i < nblk; i += 64) put(i, xv[2 * i], xv[2 * i + 1]);
+        } else {
+          auto absmax8 = [](const u32x4& v, float a) {
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              a = fmaxf(a, fabsf(__uint_as_float(u[h] << 16)));
+              a = fmaxf(a, fabsf(__uint_as_float(u[h] & 0xffff0000u)));
+            }
+            return a;
+          };
+          float amax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < XB; ++q)
+            if (lane + 64 * q < nblk) amax = absmax8(xreg[m][q][1], absmax8(xreg[m][q][0], amax));
+          for (int i = lane + 64 * XB; i < nblk; i += 64)
+            amax = absmax8(xv[2 * i + 1], absmax8(xv[2 * i], amax));
+          amax = wave_max(amax);
+          float back;
+          const int sh = row_prescale(amax, &back);
+          xb[m] = back;
+          auto put8 = [&](int v8, const u32x4& v) {        // natural order: 8 elements -> 16 B
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const uint32_t e0 = f16_bits(ldexpf(__uint_as_float(u[h] << 16), sh));
+              const uint32_t e1 = f16_bits(ldexpf(__uint_as_float(u[h] & 0xffff0000u), sh));
+              o[h] = e0 | (e1 << 16);
+            }
+            *reinterpret_cast<u32x4*>(xo + 8 * v8) = u32x4{o[0], o[1], o[2], o[3]};
+          };
+#pragma unroll
+          for (int q = 0; q < XB; ++q) {
+            const int i = lane + 64 * q;
+            if (i < nblk) {
+              put8(2 * i, xreg[m][q][0]);
+              put8(2 * i + 1, xreg[m][q][1]);
+            }
+          }
+          for (int i = lane + 64 * XB; i < nblk; i += 64) {
+            put8(2 * i, xv[2 * i]);
+            put8(2 * i + 1, xv[2 * i + 1]);
+          }
+        }
+      }
+    }
+  };
 
   CoreArgs c;
   const int64_t gpr = p.K / p.group;
   c.crow = reinterpret_cast<const uint32_t*>(p.codes + nrow * (p.K * B / 8));
   c.srow = p.scales + nrow * gpr;
   c.abrow = reinterpret_cast<const uint32_t*>(p.shapes + nrow * gpr * 2);
-  c.group = p.group;
-  c.sb = sb; c.se = se; c.nl = nl; c.kb = kb; c.M = M; c.K = p.K;
+  c.mpg = geo.mpg;
+  c.tb = tb; c.te = te; c.nl = nl; c.kb = kb; c.M = M;
   c.xrow = INK ? nullptr : p.xp + static_cast<int64_t>(nl < M ? nl : 0) * p.K;
-  c.xs_wave = xs_wave; c.spw = spw; c.tab_wave = tab_wave;
-  f32x4 acc = gemv_core<Dec, INK, P>(c);
+  c.xs_wave = xs_wave; c.nch_w = geo.nch_w; c.tab_wave = tab_wave;
+  c.gp_wave = gp_wave; c.gmax = geo.gmax;
+  f32x4 acc = gemv_core<Dec, INK, SPL, P, ALLIN>(c, issue_x, finish_x);
 
   // D layout of the 16x16 MFMA: lane holds rows 4*(lane/16) + r of column lane%16.
 #pragma unroll
@@ -103,73 +181,92 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams p) {
   if (t < M * 16) {
     const int m = t >> 4, cc = t & 15;
     if (n0 + cc < p.N) {
-      float v = red[(0 * 16 + m) * 16 + cc];
-      v += red[(1 * 16 + m) * 16 + cc];
-      v += red[(2 * 16 + m) * 16 + cc];
-      v += red[(3 * 16 + m) * 16 + cc];
+      float v = red[m * 16 + cc];
+#pragma unroll
+      for (int w = 1; w < W; ++w) v += red[(w * 16 + m) * 16 + cc];
       if constexpr (!INK) v *= p.xback[m];
       p.y[static_cast<int64_t>(m) * p.N + n0 + cc] = v;
     }
   }
 }
 
-// One 256-thread block per row: per-row prescale, fp16 conversion and the
-// decoder's chunk permutation; writes xp[m][K] and xback[m].
-template <class Dec>
+// Activations for the prepared (multi-kernel) paths, one 256-thread block per
+// row. W2 order: raw bf16 in the 2-bit decoder's slot order, xback = 1.
+// Otherwise: per-row power-of-two prescale and fp16 in natural order.
+template <bool W2ORDER>
 __global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, int64_t K,
                                                uint16_t* __restrict__ xp,
                                                float* __restrict__ xback) {
   const int64_t m = blockIdx.x;
   const uint16_t* row = x + m * K;
-  const int tid = threadIdx.x;
-  const int64_t nvec = K / 8;
-  const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-  float amax = 0.0f;
-  for (int64_t i = tid; i < nvec; i += 256) {
-    const u32x4 v = rv[i];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(u[q] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
-    }
-  }
-  __shared__ float red[4];
-  amax = wave_max(amax);
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float back;
-  const int sh = row_prescale(amax, &back);
-  if (tid == 0) xback[m] = back;
   uint16_t* out = xp + m * K;
-  const int64_t nchunk = K / 32;
-  for (int64_t c = tid; c < nchunk; c += 256) {
-    uint32_t o[16];
+  const int tid = threadIdx.x;
+  if constexpr (W2ORDER) {
+    for (int64_t i = tid; i < K / 16; i += 256) {
+      const u32x4 lo = reinterpret_cast<const u32x4*>(row)[2 * i];
+      const u32x4 hi = reinterpret_cast<const u32x4*>(row)[2 * i + 1];
+      const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      uint32_t o[8];
 #pragma unroll
-    for (int sl = 0; sl < 32; sl += 2) {
-      const uint32_t b0 = row[c * 32 + Dec::slot_to_code(sl)];
-      const uint32_t b1 = row[c * 32 + Dec::slot_to_code(sl + 1)];
-      const uint32_t h0 = f16_bits(ldexpf(__uint_as_float(b0 << 16), sh));
-      const uint32_t h1 = f16_bits(ldexpf(__uint_as_float(b1 << 16), sh));
-      o[sl >> 1] = h0 | (h1 << 16);
+      for (int k = 0; k < 4; ++k) {
+        o[2 * k] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x05040100u);
+        o[2 * k + 1] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x07060302u);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(out + 16 * i);
+      dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+      dst[1] = u32x4{o[4], o[5], o[6], o[7]};
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(out + c * 32);
+    if (tid == 0) xback[m] = 1.0f;
+    return;
+  } else {
+    const int64_t nvec = K / 8;
+    const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+    float amax = 0.0f;
+    for (int64_t i = tid; i < nvec; i += 256) {
+      const u32x4 v = rv[i];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+      for (int q = 0; q < 4; ++q) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(u[q] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
+      }
+    }
+    __shared__ float red[4];
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float back;
+    const int sh = row_prescale(amax, &back);
+    if (tid == 0) xback[m] = back;
+    for (int64_t i = tid; i < nvec; i += 256) {
+      const u32x4 v = rv[i];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t e0 = f16_bits(ldexpf(__uint_as_float(u[h] << 16), sh));
+        const uint32_t e1 = f16_bits(ldexpf(__uint_as_float(u[h] & 0xffff0000u), sh));
+        o[h] = e0 | (e1 << 16);
+      }
+      reinterpret_cast<u32x4*>(out)[i] = u32x4{o[0], o[1], o[2], o[3]};
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <class Dec, bool INK, int P>
+template <class Dec, bool INK, int SPL, int P>
 static hipError_t launch_gemv_t(const GemvParams& p, hipStream_t st) {
-  const int nsteps = static_cast<int>(p.K / kStep);
-  const int spw = (nsteps + 3) / 4;
-  size_t lds = 4 * 16 * 16 * 4 + 4 * tab_bytes_per_wave<Dec>();
-  if (INK) lds += static_cast<size_t>(4) * p.M * spw * kStep * 2;
-  auto kern = k_gemv<Dec, INK, P>;
+  constexpr int W = INK ? kInkWaves : 4;
+  constexpr int MTB = INK ? 4 : 1;                  // MT only matters in-kernel
+  const GemvGeom geo = gemv_geom(p.K, p.group, SPL, W);
+  size_t lds = gemv_lds_fixed<Dec>(geo.gmax, W);
+  if (INK) lds += static_cast<size_t>(W) * p.M * geo.nch_w * 32 * 2;
+  auto kern = geo.mpw <= P
+                  ? (p.M == 1 ? k_gemv<Dec, INK, SPL, P, true, 1, W> : k_gemv<Dec, INK, SPL, P, true, MTB, W>)
+                  : (p.M == 1 ? k_gemv<Dec, INK, SPL, P, false, 1, W> : k_gemv<Dec, INK, SPL, P, false, MTB, W>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -177,46 +274,57 @@ static hipError_t launch_gemv_t(const GemvParams& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const unsigned grid = static_cast<unsigned>((p.N + 15) / 16);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
-// LDS bytes the in-kernel path needs (the dispatcher falls back to the prepared
-// path when this exceeds the 160 KiB of a gfx950 CU).
-size_t gemv_ink_lds_bytes(int64_t M, int64_t K, int bits) {
-  const int64_t nsteps = K / kStep;
-  const int64_t spw = (nsteps + 3) / 4;
+static int gemv_spl(int bits, int group) { return (bits == 2 && group % 256 == 0) ? 2 : 1; }
+
+// LDS bytes and group span of the GEMV paths (the dispatcher uses the tiled
+// kernel when a wave would span more groups than it stages, or LDS overflows).
+size_t gemv_ink_lds_bytes(int64_t M, int64_t K, int bits, int group) {
+  const GemvGeom geo = gemv_geom(K, group, gemv_spl(bits, group), kInkWaves);
   const size_t tab = bits == 2 ? 0 : static_cast<size_t>(16) * (1 << bits) * 2;
-  return 4 * 16 * 16 * 4 + 4 * tab + static_cast<size_t>(4) * M * spw * kStep * 2;
+  return static_cast<size_t>(kInkWaves) * (16 * 16 * 4 + tab + 16 * geo.gmax * 8) +
+         static_cast<size_t>(kInkWaves) * M * geo.nch_w * 32 * 2;
+}
+
+bool gemv_supported(int64_t K, int bits, int group) {
+  const GemvGeom geo = gemv_geom(K, group, gemv_spl(bits, group));
+  return geo.gmax <= 4 * kGpRegs;
 }
 
 hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st) {
+  const bool spl2 = gemv_spl(bits, p.group) == 2;
   switch (bits) {
-    case 2: return ink ? launch_gemv_t<DecodeW2, true, 8>(p, st)
-                       : launch_gemv_t<DecodeW2, false, 4>(p, st);
-    case 3: return ink ? launch_gemv_t<DecodeTable<3>, true, 8>(p, st)
-                       : launch_gemv_t<DecodeTable<3>, false, 4>(p, st);
-    case 4: return ink ? launch_gemv_t<DecodeTable<4>, true, 6>(p, st)
-                       : launch_gemv_t<DecodeTable<4>, false, 4>(p, st);
-    case 5: return ink ? launch_gemv_t<DecodeTable<5>, true, 4>(p, st)
-                       : launch_gemv_t<DecodeTable<5>, false, 2>(p, st);
-    case 6: return ink ? launch_gemv_t<DecodeTable<6>, true, 4>(p, st)
-                       : launch_gemv_t<DecodeTable<6>, false, 2>(p, st);
-    case 7: return ink ? launch_gemv_t<DecodeTable<7>, true, 4>(p, st)
-                       : launch_gemv_t<DecodeTable<7>, false, 2>(p, st);
-    default: return ink ? launch_gemv_t<DecodeTable<8>, true, 4>(p, st)
-                        : launch_gemv_t<DecodeTable<8>, false, 2>(p, st);
+    case 2:
+      if (spl2) return ink ? launch_gemv_t<DecodeW2, true, 2, 8>(p, st)
+                           : launch_gemv_t<DecodeW2, false, 2, 4>(p, st);
+      return ink ? launch_gemv_t<DecodeW2, true, 1, 8>(p, st)
+                 : launch_gemv_t<DecodeW2, false, 1, 4>(p, st);
+    case 3: return ink ? launch_gemv_t<DecodeTable<3>, true, 1, 8>(p, st)
+                       : launch_gemv_t<DecodeTable<3>, false, 1, 4>(p, st);
+    case 4: return ink ? launch_gemv_t<DecodeTable<4>, true, 1, 6>(p, st)
+                       : launch_gemv_t<DecodeTable<4>, false, 1, 4>(p, st);
+    case 5: return ink ? launch_gemv_t<DecodeTable<5>, true, 1, 4>(p, st)
+                       : launch_gemv_t<DecodeTable<5>, false, 1, 2>(p, st);
+    case 6: return ink ? launch_gemv_t<DecodeTable<6>, true, 1, 4>(p, st)
+                       : launch_gemv_t<DecodeTable<6>, false, 1, 2>(p, st);
+    case 7: return ink ? launch_gemv_t<DecodeTable<7>, true, 1, 4>(p, st)
+                       : launch_gemv_t<DecodeTable<7>, false, 1, 2>(p, st);
+    default: return ink ? launch_gemv_t<DecodeTable<8>, true, 1, 4>(p, st)
+                        : launch_gemv_t<DecodeTable<8>, false, 1, 2>(p, st);
   }
 }
 
 hipError_t launch_xprep(const uint16_t* x, int64_t M, int64_t K, bool w2_order, uint16_t* xp,
                         float* xback, hipStream_t st) {
   if (w2_order)
-    hipLaunchKernelGGL(k_xprep<DecodeW2>, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K,
-                       xp, xback);
+    hipLaunchKernelGGL(k_xprep<true>, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xp,
+                       xback);
   else
-    hipLaunchKernelGGL(k_xprep<DecodeTable<3>>, dim3(static_cast<unsigned>(M)), dim3(256), 0, st,
-                       x, K, xp, xback);
+    hipLaunchKernelGGL(k_xprep<false>, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xp,
+                       xback);
   return hipGetLastError();
 }
 

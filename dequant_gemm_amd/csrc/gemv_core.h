@@ -29,24 +29,6 @@ __device__ __forceinline__ void load_chunk(const uint32_t* src, uint32_t* w) {
 template <class Dec> struct IsW2 { static constexpr bool value = false; };
 template <> struct IsW2<DecodeW2> { static constexpr bool value = true; };
 
-// Decode this lane's chunk into 16 packed fp16 pairs.
-template <class Dec>
-__device__ __forceinline__ void decode_chunk(const uint32_t* w, uint32_t gab,
-                                             const uint16_t* tab, uint32_t* r) {
-  if constexpr (IsW2<Dec>::value) {
-    if (__any(DecodeW2::has_extra(w))) {          // wave-uniform slow path
-      const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
-      const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
-      const float q2 = static_cast<float>(level_numerator(a, b, 2, 1));
-      DecodeW2::full(w, q2, r);
-    } else {
-      DecodeW2::fast(w, r);
-    }
-  } else {
-    Dec::decode(w, tab, r);
-  }
-}
-
 template <class Dec>
 __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, uint32_t gab) {
   if constexpr (!IsW2<Dec>::value) {
@@ -56,9 +38,7 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
     uint16_t* t = tab_wave + nl * (1 << B);
 #pragma unroll
     for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry(a, b, static_cast<uint32_t>(v), B);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
   }
 }
 
@@ -69,95 +49,235 @@ __host__ __device__ constexpr int tab_bytes_per_wave() {
 }
 
 // Per-wave state of the streaming loop.
+//
+// Work unit: a "macro step" of SPL x 128 codes per row. Lane (n, kb) owns the
+// SPL consecutive 32-code chunks kb*SPL .. kb*SPL+SPL-1 of each macro step of
+// row n, fetched with one load of SPL*bits dwords; sub-step h feeds MFMAs with
+// chunk kb*SPL + h from every kb lane, so a sub-step spans 4 chunks spread over
+// the macro step, which must lie in one group (group % (128*SPL) == 0).
+// 16x16x32 MFMA with bf16 or fp16 operands (8 per lane), fp32 accumulation.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+constexpr int kGpRegs = 8;     // group-parameter registers per lane: <= 32 groups per wave
+
 struct CoreArgs {
   const uint32_t* crow;     // this lane's weight row (code stream)
-  const float* srow;        // its scales
-  const uint32_t* abrow;    // its (a, b) pairs
-  int group;
-  int sb, se;               // K steps of this wave
-  int nl, kb;               // lane coordinates (row in tile, chunk in step)
+  const float* srow;        // its scales [groups]
+  const uint32_t* abrow;    // its (a, b) pairs [groups]
+  int mpg;                  // macro steps per group
+  int tb, te;               // macro steps of this wave
+  int nl, kb;               // lane coordinates (row in tile, chunk slot)
   int M;                    // valid activation rows in the MFMA tile (<= 16)
-  int64_t K;
-  const uint16_t* xrow;     // prepared activation row of A-lane nl (global variant)
-  const uint16_t* xs_wave;  // LDS activations of this wave (in-kernel variant)
-  int spw;
+  const uint16_t* xrow;     // prepared activation row of A-lane nl (global variant), chunk-major
+  const uint16_t* xs_wave;  // LDS activations of this wave (in-kernel variant), chunk-major
+  int nch_w;                // chunks per row reserved in xs_wave
   uint16_t* tab_wave;       // LDS level tables of this wave (table decoders)
+  uint32_t* gp_wave;        // LDS group parameters of this wave: [16 rows][gmax][2]
+  int gmax;
 };
 
-// Streams this lane's chunks for steps [sb, se), P steps in flight, and returns
-// the group-scaled 16x16 partial of this wave (rows: activations, cols: weights).
-template <class Dec, bool INK, int P>
-__device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c) {
-  constexpr int B = Dec::kBits;
-  const int kb = c.kb, nl = c.nl, sb = c.sb, se = c.se;
-  uint32_t cb[P][B];
-  float sbuf[P];
-  uint32_t abuf[P];
-  u32x4 xa[INK ? 1 : P][4];
+template <int N>
+__device__ __forceinline__ void load_dwords(const uint32_t* src, uint32_t* w) {
+  if constexpr (N == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(src)[q];
+      w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < N; ++d) w[d] = src[d];
+  }
+}
 
-  auto load_step = [&](auto u_c, int s) {
+// Streams this lane's chunks for macro steps [tb, te), P macro steps in flight,
+// and returns the group-scaled 16x16 partial of this wave (rows: activations,
+// cols: weights). issue_x() runs before the weight loads are issued and
+// finish_x() after them, so that waiting for the activations never waits for
+// the weight stream; each macro step then waits only for its own load. ALLIN:
+// the caller guarantees te - tb <= P, so every load is issued up front and
+// nothing is refilled.
+template <class Dec, bool INK, int SPL, int P, bool ALLIN, class IssueX, class FinishX>
+__device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c, IssueX&& issue_x, FinishX&& finish_x) {
+  constexpr int B = Dec::kBits;
+  constexpr int DW = B * SPL;                  // dwords per lane per macro step
+  const int kb = c.kb, nl = c.nl, tb = c.tb, te = c.te, mpg = c.mpg;
+  uint32_t cb[P][DW];
+  u32x4 xa[INK ? 1 : P][SPL][4];
+
+  // Group parameters of the wave's range: entry (row, g - g0) of gp_wave holds
+  // (scale bits, a|b); 16 rows x gn groups, four lanes per row, loaded into
+  // registers now (with the code loads) and written to LDS after the prologue.
+  const int g0 = tb / mpg;
+  const int gn = te > tb ? (te - 1) / mpg - g0 + 1 : 0;
+  uint32_t gsc[kGpRegs], gabr[kGpRegs];
+  // Only the groups the wave spans (uniform bound; all of these loads are waited
+  // for before the main loop, so a variable count costs no pipelining).
+#pragma unroll
+  for (int q = 0; q < kGpRegs; ++q) {
+    if (4 * q < gn) {
+      const int gi = kb + 4 * q;
+      const int g = g0 + (gi < gn ? gi : 0);
+      gsc[q] = __float_as_uint(c.srow[g]);
+      gabr[q] = c.abrow[g];
+    }
+  }
+
+  // Every global load below is unconditional (macro steps past the wave's range
+  // are clamped to its last one; lanes past the activation rows read row 0 and
+  // their MFMA output rows are never stored), so the compiler can count the
+  // outstanding loads and wait only for the oldest.
+  auto load_step = [&](auto u_c, int t_req) {
     constexpr int u = decltype(u_c)::value;
-    load_chunk<B>(c.crow + static_cast<int64_t>(s * 4 + kb) * B, cb[u]);
-    const int g = static_cast<int>((static_cast<int64_t>(s) * kStep) / c.group);
-    sbuf[u] = c.srow[g];
-    abuf[u] = c.abrow[g];
+    int t = t_req < te ? t_req : te - 1;
+    t = t < 0 ? 0 : t;
+    load_dwords<DW>(c.crow + (t * 4 * SPL + kb * SPL) * B, cb[u]);
     if constexpr (!INK) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xa[u][j] = u32x4{0u, 0u, 0u, 0u};
-        if (nl < c.M)
-          xa[u][j] = *reinterpret_cast<const u32x4*>(c.xrow + (s * 4 + kb) * 32 + 8 * j);
-      }
+      for (int h = 0; h < SPL; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xa[u][h][j] = *reinterpret_cast<const u32x4*>(
+              c.xrow + (t * 4 * SPL + kb * SPL + h) * 32 + 8 * j);
     }
   };
 
+  issue_x();
+  __builtin_amdgcn_sched_barrier(0);             // activation loads stay ahead of the weights
   [&]<int... U>(std::integer_sequence<int, U...>) {
-    ((sb + U < se ? load_step(std::integral_constant<int, U>{}, sb + U) : void()), ...);
+    (load_step(std::integral_constant<int, U>{}, tb + U), ...);
   }(std::make_integer_sequence<int, P>{});
+  __builtin_amdgcn_sched_barrier(0);
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
-  int gcur = -1;
+  finish_x();
+#pragma unroll
+  for (int q = 0; q < kGpRegs; ++q) {
+    const int gi = kb + 4 * q;
+    if (4 * q < gn && gi < gn) {
+      c.gp_wave[(nl * c.gmax + gi) * 2] = gsc[q];
+      c.gp_wave[(nl * c.gmax + gi) * 2 + 1] = gabr[q];
+    }
+  }
+  wave_lds_order();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 part[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float gscale = 0.0f;
-  for (int s0 = sb; s0 < se; s0 += P) {
+  uint32_t gab = 0u;
+  int gcur = -1;
+  const int ml = nl < c.M ? nl : 0;
+  for (int t0 = tb; t0 < te; t0 += P) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
       (([&] {
          constexpr int u = U;
-         const int s = s0 + u;
-         if (s < se) {
-           const int g = static_cast<int>((static_cast<int64_t>(s) * kStep) / c.group);
-           if (g != gcur) {
-             acc += gscale * part;
-             part = f32x4{0.f, 0.f, 0.f, 0.f};
-             gcur = g;
-             gscale = sbuf[u] * Dec::kLevelUnit;
-             build_table<Dec>(c.tab_wave, nl, kb, abuf[u]);
-           }
-           uint32_t r[16];
-           decode_chunk<Dec>(cb[u], abuf[u], c.tab_wave + nl * (1 << B), r);
+         const int t = t0 + u;
+         if (t < te) {
+           // operand barrier: decode this slot here, not hoisted ahead of the loop
 #pragma unroll
-           for (int j = 0; j < 4; ++j) {
-             u32x4 av;
-             if constexpr (INK) {
-               av = u32x4{0u, 0u, 0u, 0u};
-               if (nl < c.M)
-                 av = *reinterpret_cast<const u32x4*>(
-                     c.xs_wave + ((nl * c.spw + (s - sb)) * 4 + kb) * 32 + 8 * j);
-             } else {
-               av = xa[u][j];
-             }
-             const u32x4 bv = {r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]};
-             part = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
-                                                           __builtin_bit_cast(f16x8, bv), part,
-                                                           0, 0, 0);
+           for (int d = 0; d < DW; ++d) asm volatile("" : "+v"(cb[u][d]));
+           const int g = t / mpg;
+           if (g != gcur) {                    // wave-uniform
+             acc += gscale * ((part[0] + part[1]) + (part[2] + part[3]));
+#pragma unroll
+             for (int j = 0; j < 4; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+             const uint32_t* gp = c.gp_wave + (nl * c.gmax + (g - g0)) * 2;
+             gscale = __uint_as_float(gp[0]) * Dec::kLevelUnit;
+             gab = gp[1];
+             gcur = g;
+             build_table<Dec>(c.tab_wave, nl, kb, gab);
            }
-           if (s + P < se) load_step(std::integral_constant<int, u>{}, s + P);
+#pragma unroll
+           for (int h = 0; h < SPL; ++h) {
+             u32x4 av[4];
+#pragma unroll
+             for (int j = 0; j < 4; ++j) {
+               if constexpr (INK) {
+                 av[j] = *reinterpret_cast<const u32x4*>(
+                     c.xs_wave + (ml * c.nch_w + (t - tb) * 4 * SPL + kb * SPL + h) * 32 + 8 * j);
+               } else {
+                 av[j] = xa[u][h][j];
+               }
+             }
+             uint32_t r[16];
+             if constexpr (IsW2<Dec>::value) {
+               DecodeW2::fast(&cb[u][h * B], r);
+             } else {
+               Dec::decode(&cb[u][h * B], c.tab_wave + nl * (1 << B), r);
+             }
+#pragma unroll
+             for (int j = 0; j < 4; ++j)
+               part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, part[j]);
+             if constexpr (IsW2<Dec>::value) {
+               const uint32_t* wv = &cb[u][h * B];
+               if (__any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {
+                 // rare (wave-uniform): code -2 present; correct r and add the lo part
+                 const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
+                 const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
+                 const float v = static_cast<float>(-2.0 * level_numerator(a, b, 2, 1));
+                 const uint32_t hi = bf16_rne_bits(v);
+                 const uint32_t lo = bf16_rne_bits(v - __uint_as_float(hi << 16));
+                 // The operand barrier keeps this rare path's arithmetic inside
+                 // the branch (otherwise it is speculated into the hot path).
+                 uint32_t wl[2] = {wv[0], wv[1]};
+                 asm volatile("" : "+v"(wl[0]), "+v"(wl[1]));
+                 uint32_t rhi[16], rlo[16];
+                 DecodeW2::extra(wl, hi, lo, rhi, rlo);
+#pragma unroll
+                 for (int j = 0; j < 4; ++j) {
+                   part[j] = mfma16<true>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]}, part[j]);
+                   part[j] = mfma16<true>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]}, part[j]);
+                 }
+               }
+             }
+           }
          }
+         if constexpr (!ALLIN)
+           load_step(std::integral_constant<int, u>{}, t + P);   // unconditional (clamped)
+         __builtin_amdgcn_sched_barrier(0);       // keep each slot's decode next to its MFMAs
        }()),
        ...);
     }(std::make_integer_sequence<int, P>{});
   }
-  acc += gscale * part;
+  acc += gscale * ((part[0] + part[1]) + (part[2] + part[3]));
   return acc;
+}
+
+// Launch geometry shared by the host launcher and the kernel.
+struct GemvGeom {
+  int nmacro;     // macro steps per row
+  int mpw;        // macro steps reserved per wave (LDS sizing)
+  int nch_w;      // activation chunks reserved per wave and row
+  int mpg;        // macro steps per group
+  int gmax;       // groups a wave can span
+};
+
+__host__ __device__ inline GemvGeom gemv_geom(int64_t K, int group, int spl, int waves = 4) {
+  GemvGeom g;
+  g.nmacro = static_cast<int>(K / (kStep * spl));
+  g.mpw = (g.nmacro + waves - 1) / waves;
+  g.nch_w = g.mpw * 4 * spl;
+  g.mpg = group / (kStep * spl);
+  g.gmax = (g.mpw + g.mpg - 1) / g.mpg + 1;
+  return g;
+}
+
+template <class Dec>
+__host__ __device__ constexpr size_t gemv_lds_fixed(int gmax, int waves = 4) {
+  return static_cast<size_t>(waves) * (16 * 16 * 4 + tab_bytes_per_wave<Dec>() + 16 * gmax * 8);
 }
 
 }  // namespace cubic

@@ -87,17 +87,20 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   }
 }
 
-template <class Dec, int P>
-__global__ __launch_bounds__(256) void k_moe_gemv(MoeGemvParams p) {
+template <class Dec, int SPL, int P>
+__global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int B = Dec::kBits;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
+  const GemvGeom geo = gemv_geom(p.K, p.group, SPL);
   float* red = reinterpret_cast<float*>(smem);
-  uint16_t* tab_wave = reinterpret_cast<uint16_t*>(smem + 4 * 16 * 16 * 4) +
-                       wave * (tab_bytes_per_wave<Dec>() / 2);
-  const int nsteps = static_cast<int>(p.K / kStep);
-  const int sb = wave * nsteps / 4, se = (wave + 1) * nsteps / 4;
+  unsigned char* q = smem + 4 * 16 * 16 * 4;
+  uint16_t* tab_wave = reinterpret_cast<uint16_t*>(q + wave * tab_bytes_per_wave<Dec>());
+  q += 4 * tab_bytes_per_wave<Dec>();
+  uint32_t* gp_wave = reinterpret_cast<uint32_t*>(q) + wave * 16 * geo.gmax * 2;
+  const int tb = wave * geo.nmacro / 4, te = (wave + 1) * geo.nmacro / 4;
   const int64_t tiles = (p.N + 15) / 16;
   const int64_t gpr = p.K / p.group;
   const int64_t items = static_cast<int64_t>(p.hdr[1]) * tiles;
@@ -112,16 +115,17 @@ __global__ __launch_bounds__(256) void k_moe_gemv(MoeGemvParams p) {
     c.crow = reinterpret_cast<const uint32_t*>(p.codes + e * p.code_bytes + nrow * (p.K * B / 8));
     c.srow = p.scales + (static_cast<int64_t>(e) * p.N + nrow) * gpr;
     c.abrow = reinterpret_cast<const uint32_t*>(p.shapes + ((static_cast<int64_t>(e) * p.N + nrow) * gpr) * 2);
-    c.group = p.group;
-    c.sb = sb; c.se = se; c.nl = nl; c.kb = kb; c.K = p.K;
-    c.xs_wave = nullptr; c.spw = 0; c.tab_wave = tab_wave;
+    c.mpg = geo.mpg;
+    c.tb = tb; c.te = te; c.nl = nl; c.kb = kb;
+    c.xs_wave = nullptr; c.nch_w = 0; c.tab_wave = tab_wave;
+    c.gp_wave = gp_wave; c.gmax = geo.gmax;
     for (int mt = 0; mt < cnt; mt += 16) {
       const int Mt = min(16, cnt - mt);
       const int pair = p.sorted[beg + mt + (nl < Mt ? nl : 0)];
       const int tok = pair / p.topk;
       c.M = Mt;
       c.xrow = p.xp + static_cast<int64_t>(tok) * p.K;
-      const f32x4 acc = gemv_core<Dec, false, P>(c);
+      const f32x4 acc = gemv_core<Dec, false, SPL, P, false>(c, [] {}, [] {});
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kb + r) * 16 + nl] = acc[r];
       __syncthreads();
@@ -142,10 +146,11 @@ __global__ __launch_bounds__(256) void k_moe_gemv(MoeGemvParams p) {
   }
 }
 
-template <class Dec, int P>
+template <class Dec, int SPL, int P>
 static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, unsigned grid, hipStream_t st) {
-  const size_t lds = 4 * 16 * 16 * 4 + 4 * tab_bytes_per_wave<Dec>();
-  hipLaunchKernelGGL((k_moe_gemv<Dec, P>), dim3(grid), dim3(256), lds, st, p);
+  const GemvGeom geo = gemv_geom(p.K, p.group, SPL);
+  const size_t lds = gemv_lds_fixed<Dec>(geo.gmax);
+  hipLaunchKernelGGL((k_moe_gemv<Dec, SPL, P>), dim3(grid), dim3(256), lds, st, p);
   return hipGetLastError();
 }
 
@@ -164,13 +169,15 @@ hipError_t launch_moe(const int32_t* ids, int P, int E, int topk, const MoeGemvP
   const unsigned grid = static_cast<unsigned>(max_items < 4096 ? max_items : 4096);
   if (grid == 0) return hipSuccess;
   switch (bits) {
-    case 2: return launch_moe_gemv_t<DecodeW2, 4>(p, grid, st);
-    case 3: return launch_moe_gemv_t<DecodeTable<3>, 4>(p, grid, st);
-    case 4: return launch_moe_gemv_t<DecodeTable<4>, 4>(p, grid, st);
-    case 5: return launch_moe_gemv_t<DecodeTable<5>, 2>(p, grid, st);
-    case 6: return launch_moe_gemv_t<DecodeTable<6>, 2>(p, grid, st);
-    case 7: return launch_moe_gemv_t<DecodeTable<7>, 2>(p, grid, st);
-    default: return launch_moe_gemv_t<DecodeTable<8>, 2>(p, grid, st);
+    case 2:
+      if (p.group % 256 == 0) return launch_moe_gemv_t<DecodeW2, 2, 4>(p, grid, st);
+      return launch_moe_gemv_t<DecodeW2, 1, 4>(p, grid, st);
+    case 3: return launch_moe_gemv_t<DecodeTable<3>, 1, 4>(p, grid, st);
+    case 4: return launch_moe_gemv_t<DecodeTable<4>, 1, 4>(p, grid, st);
+    case 5: return launch_moe_gemv_t<DecodeTable<5>, 1, 2>(p, grid, st);
+    case 6: return launch_moe_gemv_t<DecodeTable<6>, 1, 2>(p, grid, st);
+    case 7: return launch_moe_gemv_t<DecodeTable<7>, 1, 2>(p, grid, st);
+    default: return launch_moe_gemv_t<DecodeTable<8>, 1, 2>(p, grid, st);
   }
 }
 
