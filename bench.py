@@ -15,6 +15,7 @@ A8 products and the small-M W4 products as extra fields.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,7 +46,49 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true", help="also time prefill and small-M products")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 20 plain device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
+
+
+# Sources of the GEMV kernel the roofline line describes; the stored HBM traffic
+# figure is only reported while their hash matches the one it was measured on.
+GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "gemv.hip", "launch.h")
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "dequant_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(path):
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter runs,
+    or None when absent or measured on other kernel sources."""
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemv_source_hash") != gemv_source_hash():
+        return None
+    return t.get("decode_gate_up_bytes_per_launch")
+
+
+def calibrate_copy(mib):
+    """A plain copy kernel of known size: each launch reads and writes exactly
+    mib MiB, so FETCH_SIZE / WRITE_SIZE per dispatch give the counters' scale."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 20}), flush=True)
 
 
 def cpu_baseline(seconds: float):
@@ -86,6 +129,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import torch
 
     import dequant_gemm_amd as cq
@@ -162,12 +208,7 @@ def main():
 
     gbs = (bytes_up + bytes_dn) / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_up / (up_avg_ms * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            traffic = json.load(open(args.traffic_json)).get("decode_gate_up_bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = stored_traffic(args.traffic_json)
     out = {
         "metric": "Cubic dequant-GEMM HBM GB/s (M=1 decode) and TFLOP/s (M=4096), % of roofline",
         "value": round(gbs, 2),
