@@ -53,7 +53,7 @@ def parse():
 
 # Sources of the GEMV kernel the roofline line describes; the stored HBM traffic
 # figure is only reported while their hash matches the one it was measured on.
-GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "gemv.hip", "launch.h")
+GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "gemv.hip")
 
 
 def gemv_source_hash():

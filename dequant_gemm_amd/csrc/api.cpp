@@ -19,6 +19,7 @@ namespace {
 constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
 constexpr int64_t kGemvMaxM = 16;          // one MFMA activation tile
 constexpr int64_t kInkMaxM = 4;            // single-kernel A16 path
+constexpr int64_t kPrefillMinM = 256;      // 256 x 256 tile kernel (2-/3-bit codes)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -157,6 +158,8 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
     return hip_status(launch_gemv(p, w->bits, false, s));
   }
   TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xp, xback, y};
+  if (M >= kPrefillMinM && prefill_supported(M, w->N, w->K, w->bits, w->group))
+    return hip_status(launch_prefill_a16(p, w->bits, s));
   return hip_status(launch_tiled_a16(p, w->bits, s));
 }
 
