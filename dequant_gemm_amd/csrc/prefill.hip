@@ -91,35 +91,112 @@ __device__ __forceinline__ uint32_t table_level(float a, float b, float sk, int 
 
 // fp16 levels of field values 0..2^B-1 (two's complement codes) of one row and
 // group, scaled by s * 2^-e_n, as lo and hi bytes: code +-j share the lo byte,
-// the negative one flips the sign bit of the hi byte.
+// the negative one flips the sign bit of the hi byte. Built in four stages so
+// that the work can be spread between MFMAs.
+// Empty asm that takes and returns a register: pure arithmetic cannot be moved
+// past it, so work written between two MFMAs is also emitted there.
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+struct TableBuild {
+  float a, b, sc, sk;
+  uint32_t L1, L2, P, Q;
+};
+
 template <int B>
-__device__ __forceinline__ PermTable make_perm_table(float s, uint32_t ab, float inv_rowscale) {
+__device__ __forceinline__ void table_stage(TableBuild& tb, PermTable& t, int stage, float s,
+                                            uint32_t ab, float inv_rowscale) {
   static_assert(B == 2 || B == 3, "perm tables hold at most 8 levels");
   constexpr int K = kmax_of(B);
-  const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
-  const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
-  const float sc = s * inv_rowscale;                     // exact (power of two)
-  const float sk = sc * (1.0f / static_cast<float>(K * K * K));
-  PermTable t;
-  if constexpr (B == 3) {
-    // field values 0..7 -> codes 0, 1, 2, 3, -4, -3, -2, -1
-    const uint32_t L1 = table_level<3>(a, b, sk, 1), L2 = table_level<3>(a, b, sk, 2);
-    const uint32_t L3 = f16_bits(sc), L4 = table_level<3>(a, b, sk, 4);
-    const uint32_t P = L1 | (L2 << 16), Q = L3 | (L4 << 16);
-    t.lo0 = __builtin_amdgcn_perm(Q, P, 0x0402000Cu);    // 0, L1, L2, L3
-    t.lo1 = __builtin_amdgcn_perm(Q, P, 0x00020406u);    // L4, L3, L2, L1
-    t.hi0 = __builtin_amdgcn_perm(Q, P, 0x0503010Cu);
-    t.hi1 = __builtin_amdgcn_perm(Q, P, 0x01030507u) ^ 0x80808080u;
+  if (stage == 0) {
+    tb.a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+    tb.b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+    tb.sc = s * inv_rowscale;                              // exact (power of two)
+    tb.sk = tb.sc * (1.0f / static_cast<float>(K * K * K));
+    pin(tb.a);
+    pin(tb.b);
+    pin(tb.sc);
+    pin(tb.sk);
+  } else if (stage == 1) {
+    if constexpr (B == 3) {
+      tb.L1 = table_level<3>(tb.a, tb.b, tb.sk, 1);
+      tb.L2 = table_level<3>(tb.a, tb.b, tb.sk, 2);
+    } else {
+      tb.L1 = f16_bits(tb.sc);
+      tb.L2 = table_level<2>(tb.a, tb.b, tb.sk, 2);
+    }
+    pin(tb.L1);
+    pin(tb.L2);
+  } else if (stage == 2) {
+    tb.P = tb.L1 | (tb.L2 << 16);
+    pin(tb.P);
+    if constexpr (B == 3) {
+      tb.Q = f16_bits(tb.sc) | (table_level<3>(tb.a, tb.b, tb.sk, 4) << 16);
+      pin(tb.Q);
+    }
   } else {
-    // field values 0..3 -> codes 0, 1, -2, -1
-    const uint32_t L1 = f16_bits(sc), L2 = table_level<2>(a, b, sk, 2);
-    const uint32_t P = L1 | (L2 << 16);
-    t.lo0 = __builtin_amdgcn_perm(0u, P, 0x0002000Cu);   // 0, L1, L2, L1
-    t.hi0 = __builtin_amdgcn_perm(0u, P, 0x0103010Cu) ^ 0x80800000u;
-    t.lo1 = 0u;
-    t.hi1 = 0u;
+    if constexpr (B == 3) {
+      // field values 0..7 -> codes 0, 1, 2, 3, -4, -3, -2, -1
+      t.lo0 = __builtin_amdgcn_perm(tb.Q, tb.P, 0x0402000Cu);   // 0, L1, L2, L3
+      t.lo1 = __builtin_amdgcn_perm(tb.Q, tb.P, 0x00020406u);   // L4, L3, L2, L1
+      t.hi0 = __builtin_amdgcn_perm(tb.Q, tb.P, 0x0503010Cu);
+      t.hi1 = __builtin_amdgcn_perm(tb.Q, tb.P, 0x01030507u) ^ 0x80808080u;
+    } else {
+      // field values 0..3 -> codes 0, 1, -2, -1
+      t.lo0 = __builtin_amdgcn_perm(0u, tb.P, 0x0002000Cu);     // 0, L1, L2, L1
+      t.hi0 = __builtin_amdgcn_perm(0u, tb.P, 0x0103010Cu) ^ 0x80800000u;
+      t.lo1 = 0u;
+      t.hi1 = 0u;
+    }
+    pin(t.lo0);
+    pin(t.lo1);
+    pin(t.hi0);
+    pin(t.hi1);
   }
+}
+
+template <int B>
+__device__ __forceinline__ PermTable make_perm_table(float s, uint32_t ab, float inv_rowscale) {
+  TableBuild tb;
+  PermTable t;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) table_stage<B>(tb, t, st, s, ab, inv_rowscale);
   return t;
+}
+
+// One code quad (4 codes -> 2 dwords of fp16 pairs) in four pieces.
+struct QuadState {
+  uint32_t e, o, sel, lo, hi;
+};
+
+template <int B>
+__device__ __forceinline__ void quad_piece(QuadState& st, int piece, const uint32_t* w, int qf,
+                                           const PermTable& t, uint32_t* out) {
+  constexpr uint32_t fm = (1u << B) - 1u;
+  constexpr uint32_t me = fm | (fm << (2 * B));
+  constexpr uint32_t mo = (fm << B) | (fm << (3 * B));
+  if (piece == 0) {
+    const uint32_t v = quad_field<B>(w, qf);
+    st.e = v & me;
+    st.o = v & mo;
+    pin(st.e);
+    pin(st.o);
+  } else if (piece == 1) {
+    const uint32_t e = st.e * (1u + (1u << (16 - 2 * B)));
+    const uint32_t o = st.o * ((1u << (8 - B)) + (1u << (24 - 3 * B)));
+    st.sel = ((e & 0x00FF00FFu) | (o & 0xFF00FF00u)) & (fm * 0x01010101u);
+    pin(st.sel);
+  } else if (piece == 2) {
+    st.lo = __builtin_amdgcn_perm(t.lo1, t.lo0, st.sel);
+    st.hi = __builtin_amdgcn_perm(t.hi1, t.hi0, st.sel);
+    pin(st.lo);
+    pin(st.hi);
+  } else {
+    out[0] = __builtin_amdgcn_perm(st.hi, st.lo, 0x05010400u);
+    out[1] = __builtin_amdgcn_perm(st.hi, st.lo, 0x07030602u);
+    pin(out[0]);
+    pin(out[1]);
+  }
 }
 
 template <int B>
@@ -149,9 +226,16 @@ __device__ __forceinline__ f16x8 decode8(const uint32_t* w, const PermTable& t, 
   return __builtin_bit_cast(f16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
 
-template <int B>
-__global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
+// One output tile: 64 NB weight rows n0.. x 256 activation rows m0.. (NB = 2:
+// the full 256 x 256 tile; NB = 1: half a tile, used to even out the last round
+// of workgroups).
+template <int B, int NB>
+__device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, int64_t n0,
+                                             unsigned char* smem) {
+  static_assert(NB == 2 || NB == 1, "2 or 1 weight blocks per wave");
+  constexpr int MB = 8;                       // activation blocks per wave (256 rows)
+  constexpr int Q = MB / 4;                   // activation loads per wave and MFMA block
+  constexpr int NS = NB * MB;                 // MFMA slots per K block
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);                 // [3][PT * PK] swizzled
   float* colmul = reinterpret_cast<float*>(smem + kABufs * kABufBytes);   // [PT] 2^e_n
   float* rowmul = colmul + PT;                                      // [PT] xback
@@ -160,15 +244,6 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, h = lane >> 5;
 
-  // Tile order: consecutive workgroup ids go to different XCDs; give each XCD a
-  // contiguous run of tiles (same activation rows) when the count divides.
-  const int tiles_n = static_cast<int>((p.N + PT - 1) / PT);
-  const int tiles = static_cast<int>(gridDim.x);
-  int t = static_cast<int>(blockIdx.x);
-  if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
-  const int64_t m0 = static_cast<int64_t>(t / tiles_n) * PT;
-  const int64_t n0 = static_cast<int64_t>(t % tiles_n) * PT;
-
   const int gpr = static_cast<int>(p.K / p.group);
   const int nsteps = static_cast<int>(p.K / PK);
   const int spg = p.group / PK;
@@ -176,24 +251,55 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
   // ---- weight rows of this lane: n0 + 64 wave + 32 i + c (i = 0, 1) ----
   const uint32_t row_bytes = static_cast<uint32_t>(p.K * B / 8);
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(p.codes, static_cast<uint32_t>(p.N) * row_bytes);
-  const float* srow[2];
-  const uint32_t* abrow[2];
-  uint32_t coff[2];
-  float inv_rowscale[2];
+  const float* srow[NB];
+  const uint32_t* abrow[NB];
+  uint32_t coff[NB];
+  float inv_rowscale[NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int nl = 64 * wave + 32 * i + c;
+  for (int i = 0; i < NB; ++i) {
+    const int nl = 32 * NB * wave + 32 * i + c;
     const int64_t n = n0 + nl;
     const int64_t nc = n < p.N ? n : p.N - 1;          // parameters of a valid row
     srow[i] = p.scales + nc * gpr;
     abrow[i] = reinterpret_cast<const uint32_t*>(p.shapes) + nc * gpr;
     coff[i] = static_cast<uint32_t>(n) * row_bytes + static_cast<uint32_t>(h * 4 * B);
-    float smax = 0.0f;
-    for (int g = 0; g < gpr; ++g) smax = fmaxf(smax, fabsf(srow[i][g]));
-    int e = 0;                                          // 2^e >= smax
-    if (smax > 0.0f && smax <= 3.4e38f) e = ilogbf(smax) + 1;
-    inv_rowscale[i] = ldexpf(1.0f, -e);
-    if (h == 0) colmul[nl] = ldexpf(1.0f, e);
+  }
+  // Largest |s| of each row: the row's two lanes (h = 0, 1) take alternate
+  // groups, and all loads of a batch of 32 groups are issued before any is
+  // used (a dependent chain of loads here would cost one memory latency per
+  // group). Loads past the row go to an offset outside the buffer and read 0.
+  {
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(p.scales, static_cast<uint32_t>(p.N * gpr * 4));
+    float smax[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) smax[i] = 0.0f;
+    for (int g0 = 0; g0 < gpr; g0 += 32) {
+      float v[NB][16];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int64_t n = n0 + 32 * NB * wave + 32 * i + c;
+        const int64_t nc = n < p.N ? n : p.N - 1;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int g = g0 + 2 * t + h;
+          const uint32_t off = g < gpr ? static_cast<uint32_t>((nc * gpr + g) * 4) : 0xFFFFFFF0u;
+          v[i][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) smax[i] = fmaxf(smax[i], fabsf(v[i][t]));
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float m = fmaxf(smax[i], __shfl_xor(smax[i], 32, 64));
+      int e = 0;                                        // 2^e >= m
+      if (m > 0.0f && m <= 3.4e38f) e = ilogbf(m) + 1;
+      inv_rowscale[i] = ldexpf(1.0f, -e);
+      if (h == 0) colmul[32 * NB * wave + 32 * i + c] = ldexpf(1.0f, e);
+    }
   }
   {
     const int64_t m = m0 + tid;
@@ -202,17 +308,17 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
 
   // ---- activation tile: global -> LDS, 16-byte slots, XOR swizzle ----
   // Slot (row r, chunk q) of a buffer holds the 8 fp16 x[m0 + r][k0 + 8 (q ^ (r & 7))].
-  // Wave w fills slots 512 w + 64 i + lane (i = 0..7): row 64 w + 8 i + lane / 8.
+  // Wave w fills slots 64 MB w + 64 i + lane (i < MB): row 8 MB w + 8 i + lane / 8.
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K * 2));
-  uint32_t aoff[8];
+  uint32_t aoff[MB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < MB; ++i) {
+    const int r = 8 * MB * wave + 8 * i + (lane >> 3);
     const int q = (lane & 7) ^ (r & 7);
     aoff[i] = static_cast<uint32_t>(((m0 + r) * p.K + 8 * q) * 2);
   }
   auto issue_a = [&](int s, int buf, int i0, int i1) {
-    uint16_t* dst = As + buf * (kABufBytes / 2) + wave * 4096;
+    uint16_t* dst = As + buf * (kABufBytes / 2) + wave * (512 * MB);
 #pragma unroll
     for (int i = i0; i < i1; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst + i * 512, 16, aoff[i] + s * (PK * 2), 0,
@@ -220,37 +326,44 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
   };
 
   // ---- codes and group parameters, two steps ahead ----
-  uint32_t cw[3][2][B];     // [step % 3][row i][dword]
-  float gs[3][2];
-  uint32_t gab[3][2];
+  uint32_t cw[3][NB][B];    // [step % 3][row i][dword]
+  float gs[3][NB];
+  uint32_t gab[3][NB];
   // Code words every step; group parameters only for a step that starts a
   // group (the level table changes only there).
-  auto load_codes = [&](int s, int par) {
+  auto load_codes = [&](int s, int par, bool group_start, int g) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NB; ++i)
       load_half_codes<B>(crs, coff[i] + static_cast<uint32_t>(s) * (PK * B / 8), cw[par][i]);
-    if (s % spg == 0) {
-      const int g = (s < nsteps ? s : nsteps - 1) / spg;
+    if (group_start) {
+      const int gc = g < gpr ? g : gpr - 1;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        gs[par][i] = srow[i][g];
-        gab[par][i] = abrow[i][g];
+      for (int i = 0; i < NB; ++i) {
+        gs[par][i] = srow[i][gc];
+        gab[par][i] = abrow[i][gc];
       }
     }
   };
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      gs[t][i] = 0.0f;
+      gab[t][i] = 0u;
+    }
 
-  f32x16 acc[2][8];
+  f32x16 acc[NB][MB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < MB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // Three activation stages in LDS; step s multiplies stage s % 3. Loads are
   // spread over the step so that the four waves never flood the address FIFO
   // of the texture unit (a wave stalls in order behind a VMEM it cannot
-  // issue): the 8 activation loads of a stage go out two per MFMA block.
+  // issue): the MB activation loads of a stage go out MB / 4 per MFMA block.
   // Stage (s + 2) % 3 is filled during blocks 0..2 of step s and block 3 of
   // step s - 1 (it was last read before the barrier of step s - 1), after the
   // code words and group parameters of step s + 2 (block 3 of step s - 1).
@@ -261,99 +374,123 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
   // s + 1 and decodes that step's first weight fragments with its level table.
   // Weight fragments are always decoded one MFMA block ahead, so the decode
   // VALU work runs in the shadow of the MFMAs.
-  load_codes(0, 0);
-  load_codes(1, 1);
-  load_codes(2, 2);
-  issue_a(0, 0, 0, 8);
-  issue_a(1, 1, 0, 8);
-  issue_a(2, 2, 0, 2);
+  load_codes(0, 0, true, 0);
+  load_codes(1, 1, 1 % spg == 0, 1 / spg);
+  load_codes(2, 2, 2 % spg == 0, 2 / spg);
+  issue_a(0, 0, 0, MB);
+  issue_a(1, 1, 0, MB);
+  issue_a(2, 2, 0, Q);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // fragment of activation block j for MFMA block kb: row 32 j + c, chunk 4 h + kb
-  auto read_fa = [&](const uint16_t* Ab, int kb, f16x8* fa) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 32 * j + c;
-      const int q = (4 * h + kb) ^ (r & 7);
-      fa[j] = *reinterpret_cast<const f16x8*>(Ab + (r * 8 + q) * 8);
-    }
+  // one fragment: activation block j for MFMA block kb, row 32 j + c, chunk 4 h + kb
+  auto read_frag = [&](const uint16_t* Ab, int kb, int j) {
+    const int r = 32 * j + c;
+    const int q = (4 * h + kb) ^ (r & 7);
+    return *reinterpret_cast<const f16x8*>(Ab + (r * 8 + q) * 8);
   };
 
-  PermTable tab[2];
-  f16x8 fb[2];
-  f16x8 fa[2][8];
+  PermTable tab[NB];
+  f16x8 fb[NB];
+  f16x8 fa[2][MB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NB; ++i) {
     tab[i] = make_perm_table<B>(gs[0][i], gab[0][i], inv_rowscale[i]);
     fb[i] = decode8<B>(cw[0][i], tab[i], 0);
   }
-  read_fa(As, 0, fa[0]);
+#pragma unroll
+  for (int j = 0; j < MB; ++j) fa[0][j] = read_frag(As, 0, j);
 
+  // Step s multiplies activation stage s % 3; every MFMA block kb is a fixed
+  // schedule of NB * MB slots, each one MFMA followed by its share of the other
+  // work (sched_barrier keeps the compiler from regrouping it):
+  //  - one fragment read for the next MFMA block (slots 0 .. MB - 1);
+  //  - one of the 8 NB pieces that decode the weight fragments of the next
+  //    block (2 NB code quads of 4 pieces);
+  //  - in block 0 the 4 NB stages of the candidate level table of step s + 1;
+  //    it is taken in block 3 when step s + 1 starts a group;
+  //  - the activation loads for the stage two steps ahead (two slots).
+  // Block 3 also issues the code words (and group parameters) of step s + 3
+  // first, then reads and decodes for step s + 1 from the next stage.
+  int m1 = 1 % spg, m3 = 3 % spg, g3 = 3 / spg;   // (s + 1) % spg, (s + 3) % spg, (s + 3) / spg
   auto step = [&](int s, auto ph_c) {
     constexpr int ph = decltype(ph_c)::value;          // s % 3
     constexpr int ph1 = (ph + 1) % 3, ph2 = (ph + 2) % 3;
     const uint16_t* Ab = As + ph * (kABufBytes / 2);
     const uint16_t* An = As + ph1 * (kABufBytes / 2);
+    const bool newg1 = m1 == 0;
+    TableBuild tbs[NB];
+    PermTable tn[NB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int cb = kb & 1;
-      f16x8 fn[2];
-      if (kb < 3) {
-        issue_a(s + 2, ph2, 2 * kb + 2, 2 * kb + 4);
-        read_fa(Ab, kb + 1, fa[cb ^ 1]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) fn[i] = decode8<B>(cw[ph][i], tab[i], kb + 1);
-      } else {
-        load_codes(s + 3, ph);
+      const int kbn = kb < 3 ? kb + 1 : 0;
+      const uint16_t* Ard = kb < 3 ? Ab : An;
+      const int wp = kb < 3 ? ph : ph1;
+      if (kb == 3) {
+        load_codes(s + 3, ph, m3 == 0, g3);
         __builtin_amdgcn_sched_barrier(0);
-        issue_a(s + 3, ph, 0, 2);
-        read_fa(An, 0, fa[0]);
-        // The candidate table is built every step (it stays interleaved with
-        // the MFMAs) and taken only when step s + 1 starts a group; otherwise
-        // its parameters are stale and it is discarded.
-        const bool newg = (s + 1) % spg == 0;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const PermTable nt = make_perm_table<B>(gs[ph1][i], gab[ph1][i], inv_rowscale[i]);
-          tab[i].lo0 = newg ? nt.lo0 : tab[i].lo0;
-          tab[i].lo1 = newg ? nt.lo1 : tab[i].lo1;
-          tab[i].hi0 = newg ? nt.hi0 : tab[i].hi0;
-          tab[i].hi1 = newg ? nt.hi1 : tab[i].hi1;
-          fn[i] = decode8<B>(cw[ph1][i], tab[i], 0);
-        }
       }
+      QuadState qs[2 * NB];
+      uint32_t out[NB][4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int u = 0; u < NS; ++u) {
+        const int i = u / MB, j = u % MB;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[i], fa[cb][j], acc[i][j], 0, 0, 0);
+        if (u < MB) fa[cb ^ 1][u] = read_frag(Ard, kbn, u);
+        if (kb == 3 && u == 0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[i], fa[cb][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (kb < 3) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          for (int r = 0; r < NB; ++r) {
+            tab[r].lo0 = newg1 ? tn[r].lo0 : tab[r].lo0;
+            tab[r].lo1 = newg1 ? tn[r].lo1 : tab[r].lo1;
+            tab[r].hi0 = newg1 ? tn[r].hi0 : tab[r].hi0;
+            tab[r].hi1 = newg1 ? tn[r].hi1 : tab[r].hi1;
+            pin(tab[r].lo0);
+            pin(tab[r].lo1);
+            pin(tab[r].hi0);
+            pin(tab[r].hi1);
+          }
         }
-        if (u < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (u == 4 || u == 12) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        {
+          const int q = u >> 2, iq = q >> 1, t = q & 1;
+          quad_piece<B>(qs[q], u & 3, cw[wp][iq], 2 * kbn + t, tab[iq], &out[iq][2 * t]);
+        }
+        if (kb == 0 && (u & 1)) {
+          // candidate table stages: 4 NB pieces (NB rows x 4 stages)
+          const int tp = u >> 1;
+          table_stage<B>(tbs[tp >> 2], tn[tp >> 2], tp & 3, gs[ph1][tp >> 2], gab[ph1][tp >> 2],
+                         inv_rowscale[tp >> 2]);
+        }
+        if (u % (NS / 2) == NS / 4) {
+          const int k = u / (NS / 2);
+          if (k < Q) {
+            if (kb < 3) {
+              issue_a(s + 2, ph2, Q * (kb + 1) + k, Q * (kb + 1) + k + 1);
+            } else {
+              issue_a(s + 3, ph, k, k + 1);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
       if (kb == 2) {
-        // vmcnt(8), lgkmcnt(0): only the 8 activation loads of stage s + 2
+        // vmcnt(MB), lgkmcnt(0): only the MB activation loads of stage s + 2
         // may still be in flight, so this wave's part of stage s + 1 is in
         // LDS and its reads of stage s are done. A bare s_barrier (a release
         // fence would also drain the loads still in flight) publishes that to
         // the other waves.
-        __builtin_amdgcn_s_waitcnt(0x0078);
+        __builtin_amdgcn_s_waitcnt(0x0070 | MB);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      fb[0] = fn[0];
-      fb[1] = fn[1];
+#pragma unroll
+      for (int r = 0; r < NB; ++r)
+        fb[r] = __builtin_bit_cast(f16x8, u32x4{out[r][0], out[r][1], out[r][2], out[r][3]});
     }
+    m1 = m1 + 1 == spg ? 0 : m1 + 1;
+    m3 = m3 + 1 == spg ? 0 : m3 + 1;
+    g3 += m3 == 0 ? 1 : 0;
   };
   int s = 0;
   for (; s + 2 < nsteps; s += 3) {
@@ -370,17 +507,17 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
   // ---- epilogue: D row = weight row n (8 (r / 4) + 4 h + r % 4), column = m ----
   const bool vec = (p.N & 3) == 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < MB; ++j) {
     const int ml = 32 * j + c;
     const int64_t m = m0 + ml;
     if (m >= p.M) continue;
     const float xm = rowmul[ml];
     float* yrow = p.y + m * p.N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NB; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int nl = 64 * wave + 32 * i + 8 * q + 4 * h;
+        const int nl = 32 * NB * wave + 32 * i + 8 * q + 4 * h;
         const int64_t n = n0 + nl;
         float v[4];
 #pragma unroll
@@ -397,6 +534,29 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
   }
 }
 
+// Workgroups below full_tiles each take one 256 x 256 tile (consecutive ids go
+// to different XCDs, so each XCD gets a contiguous run of tiles that share
+// activation rows, when the count divides); the ones above take half tiles
+// (128 weight rows) of the remaining tiles, two per tile, so that the last
+// round of workgroups keeps every compute unit busy.
+template <int B>
+__global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams p, int full_tiles) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tiles_n = static_cast<int>((p.N + PT - 1) / PT);
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < full_tiles) {
+    int t = b;
+    if (full_tiles % 8 == 0) t = (b % 8) * (full_tiles / 8) + b / 8;
+    prefill_tile<B, 2>(p, static_cast<int64_t>(t / tiles_n) * PT,
+                       static_cast<int64_t>(t % tiles_n) * PT, smem);
+  } else {
+    const int j = b - full_tiles;
+    const int t = full_tiles + j / 2;
+    prefill_tile<B, 1>(p, static_cast<int64_t>(t / tiles_n) * PT,
+                       static_cast<int64_t>(t % tiles_n) * PT + (PT / 2) * (j & 1), smem);
+  }
+}
+
 }  // namespace
 
 // 2- and 3-bit codes, fp16 activations of k_xprep; the byte sizes of the
@@ -410,6 +570,18 @@ bool prefill_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   return tiles <= INT32_MAX;
 }
 
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 template <int B>
 static hipError_t launch_prefill_b(const TiledParams& p, hipStream_t st) {
   auto kern = k_prefill_a16<B>;
@@ -418,8 +590,20 @@ static hipError_t launch_prefill_b(const TiledParams& p, hipStream_t st) {
                                            static_cast<int>(kPrefillLds));
   if (e != hipSuccess) return e;
   const int64_t tiles = ((p.M + PT - 1) / PT) * ((p.N + PT - 1) / PT);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kPrefillThreads), kPrefillLds,
-                     st, p);
+  // One workgroup per compute unit (LDS). When the tiles overflow the last
+  // round by at most half the compute units, the overflow tiles are run as two
+  // half tiles each.
+  const int64_t cus = device_cu_count();
+  int64_t full = tiles, grid = tiles;
+  if (cus > 0 && tiles > cus) {
+    const int64_t rem = tiles % cus;
+    if (rem > 0 && 2 * rem <= cus) {
+      full = tiles - rem;
+      grid = full + 2 * rem;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kPrefillThreads), kPrefillLds,
+                     st, p, static_cast<int>(full));
   return hipGetLastError();
 }
 

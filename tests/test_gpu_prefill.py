@@ -128,3 +128,20 @@ def test_prefill_full_shape_tile_edges():
     codes, scales, shapes = np_weight(w)
     ref = oracle.gemm_a16(x_bits(x)[rows], oracle.dequant(codes, scales, shapes, 3, 256))
     assert row_rel_err(y[rows], ref) <= TOL
+
+
+def test_prefill_half_tiles_of_the_last_round():
+    """4352 x 4096 makes 272 tiles of 256 x 256: on a 256-CU part the last 16
+    run as 32 half tiles of 128 activation rows. Rows on both sides of every
+    half-tile edge of that region, all columns."""
+    say("prefill half tiles 4352x4096 W2 G256 K=512")
+    g = synth.make_generator(4242)
+    M, N, K = 4352, 4096, 512
+    w = synth.make_weight(g, N, K, 2, 256, "ternary", 0.02)
+    x = synth.activations(g, M, K, 0.005, 30.0)
+    cw = upload(w)
+    y = cq.cubic_gemm_a16(x.to(DEV), cw).cpu().numpy()
+    rows = np.array([0, 4095, 4096, 4223, 4224, 4300, 4351])
+    codes, scales, shapes = np_weight(w)
+    ref = oracle.gemm_a16(x_bits(x)[rows], oracle.dequant(codes, scales, shapes, 2, 256))
+    assert row_rel_err(y[rows], ref) <= TOL
