@@ -33,8 +33,11 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t nrow = (n0 + nl < p.N) ? (n0 + nl) : (p.N - 1);
+  // The workgroup owns p.rows (<= 16) weight rows; MFMA columns past them
+  // repeat rows of the same workgroup (cache hits) and are not stored.
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * p.rows;
+  const int64_t nsrc = n0 + (nl < p.rows ? nl : nl - p.rows);
+  const int64_t nrow = nsrc < p.N ? nsrc : p.N - 1;
   const GemvGeom geo = gemv_geom(p.K, p.group, SPL, W);
   const int tb = wave * geo.nmacro / W, te = (wave + 1) * geo.nmacro / W;
   const int M = p.M;
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   const int t = threadIdx.x;
   if (t < M * 16) {
     const int m = t >> 4, cc = t & 15;
-    if (n0 + cc < p.N) {
+    if (cc < p.rows && n0 + cc < p.N) {
       float v = red[m * 16 + cc];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += red[(w * 16 + m) * 16 + cc];
@@ -273,9 +276,32 @@ static hipError_t launch_gemv_t(const GemvParams& p, hipStream_t st) {
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = static_cast<unsigned>((p.N + 15) / 16);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), lds, st, p);
+  // Rows per workgroup: when 16-row workgroups would leave the last round of
+  // compute units partly idle (e.g. 384 on 256 CUs), spread the rows over a
+  // whole number of rounds instead (512 workgroups of 12 rows).
+  GemvParams q = p;
+  const int64_t tiles16 = (p.N + 15) / 16;
+  const int64_t cus = device_cu_count();
+  q.rows = 16;
+  if (cus > 0 && tiles16 > cus) {
+    const int64_t rounds = (tiles16 + cus - 1) / cus;
+    q.rows = static_cast<int>((p.N + rounds * cus - 1) / (rounds * cus));
+  }
+  const unsigned grid = static_cast<unsigned>((p.N + q.rows - 1) / q.rows);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), lds, st, q);
   return hipGetLastError();
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
 }
 
 static int gemv_spl(int bits, int group) { return (bits == 2 && group % 256 == 0) ? 2 : 1; }

@@ -18,6 +18,7 @@ struct GemvParams {
   const uint16_t* xp;     // fp16 [M][K] prepared, chunk-permuted (prepared variant)
   const float* xback;     // per-row back multiplier of xp
   float* y;               // [M][N]
+  int rows;               // weight rows per workgroup (<= 16; the launcher sets it)
 };
 
 struct TiledParams {
@@ -47,6 +48,7 @@ struct MoeGemvParams {
   float* y;               // [T*topk][N]
 };
 
+int device_cu_count();   // compute units of the current device (0 if unknown)
 hipError_t launch_pack(const int8_t* codes, uint8_t* packed, int64_t N, int64_t K, int bits,
                        hipStream_t st, unsigned int* range_error);
 hipError_t launch_unpack(const uint8_t* packed, int8_t* codes, int64_t N, int64_t K, int bits,

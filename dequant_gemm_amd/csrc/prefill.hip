@@ -570,17 +570,6 @@ bool prefill_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   return tiles <= INT32_MAX;
 }
 
-static int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = cus;
-  }
-  return cached[dev];
-}
 
 template <int B>
 static hipError_t launch_prefill_b(const TiledParams& p, hipStream_t st) {

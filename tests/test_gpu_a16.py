@@ -149,3 +149,16 @@ def test_workspace_too_small_is_rejected():
     with pytest.raises(cq.CubicError) as e:
         cq.cubic_gemm_a16(x, cw, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert e.value.status == -7
+
+
+@pytest.mark.parametrize("bits,group", [(2, 512), (3, 128)])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_small_m_rows_per_workgroup_ragged(bits, group, M):
+    """N = 4100 gives 257 tiles of 16 rows; on 256 CUs the small-M product then
+    uses 9-row workgroups (456 of them, the last holding 5 rows)."""
+    say(f"A16 small-M N=4100 bits={bits} G={group} M={M}")
+    g = synth.make_generator(5000 + 10 * bits + M)
+    kind = "ternary" if bits == 2 else "uniform"
+    w = synth.make_weight(g, 4100, 1024, bits, group, kind, 0.02)
+    x = synth.activations(g, M, 1024, 0.01, 50.0)
+    _check(w, x)
