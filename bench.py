@@ -234,27 +234,47 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_up},
     }
     if args.extra:
+        del ups, dns, g_step, g_up
+        torch.cuda.empty_cache()
         out["extra"] = extra_workloads(cq, synth, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def _time(fn, reps, stream):
+def _graph_time(calls, reps, dev):
+    """Average time of one pass over `calls` (a list of no-argument launchers),
+    captured once into a HIP graph and replayed `reps` times; HIP events on the
+    replay stream bracket the replays."""
     import torch
-    fn()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        for c in calls:
+            c()
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(reps):
-        fn()
+        g.replay()
     b.record(stream)
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
+    return a.elapsed_time(b) / reps / len(calls)
 
 
 def extra_workloads(cq, synth, dev, stream):
+    """The other workloads, each timed as graph replays: prefill (M = 4096, W3
+    G256) A16 and Dynamic A8, small-batch W4 G128 (M = 8, 64) over rotating
+    weight copies, and the routed-expert products (one token x 16 experts, the
+    decode step; 64 tokens x 16 over 896 experts)."""
     import torch
     res = {}
     w, x = synth.prefill_config(seed=5, device=dev)
@@ -263,31 +283,93 @@ def extra_workloads(cq, synth, dev, stream):
     flops = 2.0 * 4096 * 6144 * 7168
     ws = torch.empty(cq.cubic_gemm_a16_workspace_bytes(4096, 7168), dtype=torch.uint8, device=dev)
     y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
-    ms = _time(lambda: cq.cubic_gemm_a16(x, cw, out=y, workspace=ws), 10, stream)
+    ms = _graph_time([lambda: cq.cubic_gemm_a16(x, cw, out=y, workspace=ws)] * 4, 5, dev)
     res["prefill_a16"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
-                          "frac_of_f16_peak": round(flops / ms / 1e9 / MFMA_F16_PEAK_TFS, 4)}
+                          "frac_of_f16_peak": round(flops / ms / 1e9 / MFMA_F16_PEAK_TFS, 4),
+                          "includes": "activation prep kernel + product kernel"}
     xq = torch.empty((4096, 7168), dtype=torch.int8, device=dev)
     sx = torch.empty((4096,), dtype=torch.float32, device=dev)
-    ms_q = _time(lambda: cq.act_quant_int8_per_token(x, xq, sx), 10, stream)
-    ms8 = _time(lambda: cq.cubic_gemm_a8(xq, sx, cw, out=y), 10, stream)
+    ms_q = _graph_time([lambda: cq.act_quant_int8_per_token(x, xq, sx)] * 4, 5, dev)
+    ms8 = _graph_time([lambda: cq.cubic_gemm_a8(xq, sx, cw, out=y)] * 2, 3, dev)
     res["prefill_a8"] = {"act_quant_ms": round(ms_q, 4), "gemm_ms": round(ms8, 4),
                          "TOP/s": round(flops / ms8 / 1e9, 2),
                          "frac_of_i8_peak": round(flops / ms8 / 1e9 / MFMA_I8_PEAK_TOPS, 4),
                          "act_quant_GB/s": round((4096 * 7168 * 3 + 4096 * 4) / ms_q / 1e6, 1)}
-    del x, xq, y, ws
+    del x, xq, y, ws, cw
+    torch.cuda.empty_cache()
+    copies = 16
     for M in (8, 64):
         (wu, xu), (wd, xd) = synth.smallm_config(M, seed=3, device=dev)
         for name, ww, xx in (("gate_up", wu, xu), ("down", wd, xd)):
-            c = cq.CubicWeight(cq.cubic_pack(ww.codes, 4).reshape(-1), ww.scales, ww.shapes, ww.N,
-                               ww.K, 4, 128)
+            base = cq.CubicWeight(cq.cubic_pack(ww.codes, 4).reshape(-1), ww.scales, ww.shapes, ww.N,
+                                  ww.K, 4, 128)
+            pool = [base] + [cq.CubicWeight(base.codes.clone(), base.scales.clone(), base.shapes.clone(),
+                                            base.N, base.K, 4, 128) for _ in range(copies - 1)]
             wsp = torch.empty(max(1, cq.cubic_gemm_a16_workspace_bytes(M, ww.K)), dtype=torch.uint8,
                               device=dev)
             yy = torch.empty((M, ww.N), dtype=torch.float32, device=dev)
-            ms = _time(lambda: cq.cubic_gemm_a16(xx, c, out=yy, workspace=wsp), 50, stream)
+            ms = _graph_time([(lambda c=c: cq.cubic_gemm_a16(xx, c, out=yy, workspace=wsp))
+                              for c in pool], 4, dev)
             nb = algorithmic_bytes(ww.N, ww.K, 4, 128, M)
-            res[f"smallm_w4_M{M}_{name}"] = {"us": round(ms * 1e3, 2),
-                                              "GB/s": round(nb / ms / 1e6, 1),
-                                              "note": "L2/MALL-warm (one weight copy)"}
+            res[f"smallm_w4_M{M}_{name}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                                              "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            del pool, base
+        del wu, wd
+        torch.cuda.empty_cache()
+    res.update(moe_workloads(cq, synth, dev))
+    return res
+
+
+def moe_workloads(cq, synth, dev):
+    """Routed experts, gate_up 6144 x 7168 W2 G512 at the decode distributions.
+    Decode step: one token routed to 16 of 64 resident experts, a different set
+    per launch. C4: 64 tokens x top-16 over 896 experts (~620 touched)."""
+    import torch
+    res = {}
+    N, K, bits, group = 6144, 7168, 2, 512
+    cb = N * K * bits // 8
+
+    def pool(E, seed):
+        codes = torch.empty(E * cb, dtype=torch.uint8, device=dev)
+        scales = torch.empty((E, N, K // group), dtype=torch.float32, device=dev)
+        shapes = torch.empty((E, N, K // group, 2), dtype=torch.int16, device=dev)
+        for e in range(E):
+            w = synth.moe_expert(e, seed=seed, N=N, K=K, bits=bits, group=group, device=dev)
+            cq.cubic_pack(w.codes, bits, out=codes[e * cb:(e + 1) * cb].view(N, K * bits // 8))
+            scales[e] = w.scales
+            shapes[e] = w.shapes
+        return cq.CubicWeight(codes, scales.reshape(-1), shapes.reshape(-1), N, K, bits, group)
+
+    expert_bytes = cb + 8 * N * (K // group)
+    E = 64
+    p = pool(E, 4)
+    x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=16, K=K, device=dev)
+    g = torch.Generator().manual_seed(7)
+    ids = [torch.randperm(E, generator=g)[:16].to(torch.int32).view(1, 16).to(dev) for _ in range(8)]
+    wsb = cq.cubic_moe_workspace_bytes(1, 16, E, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    y = torch.empty((1, 16, N), dtype=torch.float32, device=dev)
+    ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm(x, i, p, E, out=y, workspace=ws))
+                      for i in ids], 5, dev)
+    nb = 16 * expert_bytes + K * 2 + 16 * N * 4
+    res["moe_decode_1tok_top16"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                                    "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                    "bytes_per_launch": nb}
+    del p, ws, y
+    torch.cuda.empty_cache()
+    E, T = 896, 64
+    p = pool(E, 4)
+    x, tid = synth.moe_routing(seed=4, T=T, E=E, topk=16, K=K, device=dev)
+    touched = int(torch.unique(tid).numel())
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, 16, E, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, 16, N), dtype=torch.float32, device=dev)
+    ms = _graph_time([lambda: cq.cubic_moe_grouped_gemm(x, tid, p, E, out=y, workspace=ws)], 3, dev)
+    nb = touched * expert_bytes + T * K * 2 + T * 16 * N * 4
+    res["moe_896x64tok_top16"] = {"ms": round(ms, 4), "GB/s": round(nb / ms / 1e6, 1),
+                                  "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                  "touched_experts": touched}
+    del p, ws, y
+    torch.cuda.empty_cache()
     return res
 
 
