@@ -221,7 +221,8 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
   if (T == 0 || expert0->N == 0) return CUBIC_OK;
   if (T * topk > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
-  if (expert0->K > 0 && !gemv_supported(expert0->K, expert0->bits, expert0->group))
+  if (expert0->K > 0 && (!gemv_supported(expert0->K, expert0->bits, expert0->group) ||
+                         moe_lds_min_bytes(expert0->K, expert0->bits, expert0->group) > kLdsLimit))
     return CUBIC_ERR_SHAPE;
   if (!x_bf16 || !topk_ids || !y || !workspace) return CUBIC_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(y) || !aligned16(workspace))
@@ -247,7 +248,7 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   p.xp = xp;
   p.xback = xback;
   p.y = y;
-  e = launch_moe(topk_ids, static_cast<int>(T * topk), E, topk, p,
+  e = launch_moe(topk_ids, static_cast<int>(T), E, topk, p,
                  reinterpret_cast<int32_t*>(ws + L.hdr), reinterpret_cast<int32_t*>(ws + L.counts),
                  reinterpret_cast<int32_t*>(ws + L.offsets), reinterpret_cast<int32_t*>(ws + L.active),
                  reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s);

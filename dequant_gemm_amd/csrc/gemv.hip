@@ -325,7 +325,7 @@ hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st) 
   switch (bits) {
     case 2:
       if (spl2) return ink ? launch_gemv_t<DecodeW2, true, 2, 8>(p, st)
-                           : launch_gemv_t<DecodeW2, false, 2, 4>(p, st);
+                           : launch_gemv_t<DecodeW2, false, 2, 2>(p, st);
       return ink ? launch_gemv_t<DecodeW2, true, 1, 8>(p, st)
                  : launch_gemv_t<DecodeW2, false, 1, 4>(p, st);
     case 3: return ink ? launch_gemv_t<DecodeTable<3>, true, 1, 8>(p, st)

@@ -36,8 +36,14 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
     const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
     const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
     uint16_t* t = tab_wave + nl * (1 << B);
+    if constexpr (B <= 5) {
 #pragma unroll
-    for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry(a, b, static_cast<uint32_t>(v), B);
+      for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry(a, b, static_cast<uint32_t>(v), B);
+    } else {
+      // wide codes: a rolled loop (unrolled, the fp64 level math overflows the registers)
+#pragma unroll 1
+      for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry(a, b, static_cast<uint32_t>(v), B);
+    }
     wave_lds_order();
   }
 }

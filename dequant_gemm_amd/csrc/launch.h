@@ -67,7 +67,9 @@ hipError_t launch_tiled_a16(const TiledParams& p, int bits, hipStream_t st);
 hipError_t launch_tiled_a8(const TiledParams& p, int bits, hipStream_t st);
 bool prefill_supported(int64_t M, int64_t N, int64_t K, int bits, int group);
 hipError_t launch_prefill_a16(const TiledParams& p, int bits, hipStream_t st);
-hipError_t launch_moe(const int32_t* ids, int P, int E, int topk, const MoeGemvParams& base,
+// LDS the grouped kernel needs with one activation row per pass.
+size_t moe_lds_min_bytes(int64_t K, int bits, int group);
+hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
                       int32_t* hdr, int32_t* counts, int32_t* offsets, int32_t* active,
                       int32_t* sorted, int bits, hipStream_t st);
 

@@ -88,3 +88,22 @@ def test_full_pool_sampled_pairs():
         W = _expert_dense(e, N, K, bits, group, 4)
         ref = oracle.gemm_a16(X[t:t + 1], W)
         assert row_rel_err(y[t, j][None, :], ref) <= TOL, (t, j, e)
+
+
+@pytest.mark.parametrize("bits,group,K", [(2, 512, 1024), (3, 128, 1024), (4, 128, 9216), (2, 128, 9216)])
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_routing_and_long_slices(bits, group, K, T):
+    """Decode-sized routing (one activation row per pass for T = 1, two for T = 3,
+    an odd count that leaves a one-row pass), and K = 9216, whose per-wave
+    activation slices are longer than the part staged through registers."""
+    say(f"MoE decode T={T} bits={bits} G={group} K={K}")
+    E, topk, N = 20, 16, 200
+    pool = _pool(E, N, K, bits, group, seed=60 + bits)
+    x, ids = synth.moe_routing(seed=61 + T, T=T, E=E, topk=topk, K=K, device=DEV)
+    if T == 3:
+        ids[1, :3] = ids[0, :3]        # experts picked by several tokens
+        ids[2, :3] = ids[0, :3]
+    y = cq.cubic_moe_grouped_gemm(x, ids, pool, E).cpu().numpy()
+    ref = oracle.moe_a16(x_bits(x), ids.cpu().numpy(), E, N,
+                         lambda e: _expert_dense(e, N, K, bits, group, 60 + bits))
+    assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
