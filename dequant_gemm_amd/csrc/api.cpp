@@ -44,8 +44,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? CUBIC_OK : CUBIC_ERR_HIP
 // group parameters fit in LDS and a wave spans few enough groups. Depends on
 // (M, K) only, so the workspace size needs no weight description.
 bool a16_inkernel(int64_t M, int64_t K) {
-  return M <= kInkMaxM && K >= 128 && gemv_ink_lds_bytes(M, K, 8, 128) <= kLdsLimit &&
-         gemv_supported(K, 8, 128) && gemv_supported(K, 3, 128);
+  return M <= kInkMaxM && K >= 128 && gemv_supported(K, 8, 128) && gemv_supported(K, 3, 128) &&
+         gemv_ink_lds_bytes(M, K, 8, 128) <= kLdsLimit;
 }
 
 std::mutex g_pack_mutex[64];
@@ -190,19 +190,15 @@ CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
 
 namespace {
 struct MoeLayout {
-  size_t hdr, counts, offsets, active, sorted, xp, xback, total;
+  size_t hdr, erec, sorted, total;
 };
-MoeLayout moe_layout(int64_t T, int topk, int E, int64_t K) {
+MoeLayout moe_layout(int64_t T, int topk, int E) {
   MoeLayout L;
   const size_t P = static_cast<size_t>(T) * topk;
   size_t o = 0;
   L.hdr = o;     o += align256(16);
-  L.counts = o;  o += align256(4 * static_cast<size_t>(E));
-  L.offsets = o; o += align256(4 * (static_cast<size_t>(E) + 1));
-  L.active = o;  o += align256(4 * static_cast<size_t>(E));
+  L.erec = o;    o += align256(32 * static_cast<size_t>(E));
   L.sorted = o;  o += align256(4 * P);
-  L.xp = o;      o += align256(static_cast<size_t>(T) * K * 2);
-  L.xback = o;   o += align256(4 * static_cast<size_t>(T));
   L.total = o;
   return L;
 }
@@ -210,7 +206,7 @@ MoeLayout moe_layout(int64_t T, int topk, int E, int64_t K) {
 
 CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K) {
   if (T < 0 || topk <= 0 || E <= 0 || K < 0) return 0;
-  return moe_layout(T, topk, E, K).total;
+  return moe_layout(T, topk, E).total;
 }
 
 CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
@@ -227,15 +223,11 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   if (!x_bf16 || !topk_ids || !y || !workspace) return CUBIC_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(y) || !aligned16(workspace))
     return CUBIC_ERR_ALIGN;
-  const MoeLayout L = moe_layout(T, topk, E, expert0->K);
+  const MoeLayout L = moe_layout(T, topk, E);
   if (ws_bytes < L.total) return CUBIC_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* xp = reinterpret_cast<uint16_t*>(ws + L.xp);
-  float* xback = reinterpret_cast<float*>(ws + L.xback);
   if (expert0->K == 0) return hip_status(launch_fill_zero(y, T * topk * expert0->N, s));
-  hipError_t e = launch_xprep(x_bf16, T, expert0->K, expert0->bits == 2, xp, xback, s);
-  if (e != hipSuccess) return CUBIC_ERR_HIP;
   MoeGemvParams p{};
   p.codes = expert0->codes;
   p.scales = expert0->scales;
@@ -245,12 +237,11 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   p.group = expert0->group;
   p.topk = topk;
   p.code_bytes = static_cast<int64_t>(cubic_code_bytes(expert0->N, expert0->K, expert0->bits));
-  p.xp = xp;
-  p.xback = xback;
+  p.x = x_bf16;
   p.y = y;
-  e = launch_moe(topk_ids, static_cast<int>(T), E, topk, p,
-                 reinterpret_cast<int32_t*>(ws + L.hdr), reinterpret_cast<int32_t*>(ws + L.counts),
-                 reinterpret_cast<int32_t*>(ws + L.offsets), reinterpret_cast<int32_t*>(ws + L.active),
-                 reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s);
+  const hipError_t e = launch_moe(topk_ids, static_cast<int>(T), E, topk, p,
+                                  reinterpret_cast<int32_t*>(ws + L.hdr),
+                                  reinterpret_cast<int32_t*>(ws + L.erec),
+                                  reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s);
   return hip_status(e);
 }

@@ -52,115 +52,27 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   uint16_t* xs_wave = reinterpret_cast<uint16_t*>(q) + static_cast<int64_t>(wave) * M * geo.nch_w * 32;
 
   float xb[4] = {1.0f, 1.0f, 1.0f, 1.0f};        // per-row back multipliers (INK)
-  // In-kernel activation staging: each wave copies its own K slice of x into
-  // its own LDS region, chunk-major and in the decoder's slot order.
-  //  - bf16 decoders (2-bit): raw bf16, only permuted (v_perm), no scaling.
-  //  - fp16 decoders: per-row power-of-two prescale over the slice (undone on
-  //    the wave's partial), then fp16.
-  // The first XB 16-element blocks per lane and row are loaded into registers
-  // by issue_x() (before the weight loads; indices clamped so the loads are
-  // unconditional); finish_x() writes them and handles any longer tail.
+  // In-kernel activation staging (XStage): each wave copies its own K slice of x
+  // into its own LDS region, loads issued before the weight stream.
   constexpr int XB = 2;
   const int64_t k0 = static_cast<int64_t>(tb) * kStep * SPL;
   const int nblk = (te - tb) * kStep * SPL / 16;       // 16-element blocks in the slice
-  u32x4 xreg[INK ? MT : 1][XB][2];
+  XStage<Dec, INK ? MT : 1, XB> xst;
+  const u32x4* xv[INK ? MT : 1] = {};
+  if constexpr (INK) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      xv[m] = reinterpret_cast<const u32x4*>(p.x + (m < M ? m : 0) * p.K + k0);
+  }
   auto issue_x = [&]() {
-    if constexpr (INK) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const u32x4* xv = reinterpret_cast<const u32x4*>(p.x + (m < M ? m : 0) * p.K + k0);
-#pragma unroll
-        for (int q = 0; q < XB; ++q) {
-          int i = lane + 64 * q;
-          i = i < nblk ? i : 0;
-          xreg[m][q][0] = xv[2 * i];
-          xreg[m][q][1] = xv[2 * i + 1];
-        }
-      }
-    }
+    if constexpr (INK) xst.issue(xv, nblk, lane);
   };
   auto finish_x = [&]() {
-    if constexpr (INK) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m >= M) break;
-        const u32x4* xv = reinterpret_cast<const u32x4*>(p.x + m * p.K + k0);
-        uint16_t* xo = xs_wave + m * geo.nch_w * 32;
-        if constexpr (Dec::kBf16) {
-          // 16 consecutive codes 16d..16d+15 fill slots 16d..16d+15 as pairs
-          // (code i, code i+8): out[2k] / out[2k+1] take the low / high halves
-          // of input registers k and 4+k.
-          auto put = [&](int i, const u32x4& lo, const u32x4& hi) {
-            const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            uint32_t o[8];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              o[2 * k] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x05040100u);
-              o[2 * k + 1] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x07060302u);
-            }
-            u32x4* dst = reinterpret_cast<u32x4*>(xo + 16 * i);
-            dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-            dst[1] = u32x4{o[4], o[5], o[6], o[7]};
-          };
-          // unconditional: lanes past the slice rewrite block 0 with block 0's data
-          // (a conditional use would let the compiler sink the loads behind the
-          // weight stream)
-#pragma unroll
-          for (int q = 0; q < XB; ++q) {
-            const int i = lane + 64 * q;
-            put(i < nblk ? i : 0, xreg[m][q][0], xreg[m][q][1]);
-          }
-          for (int i = lane + 64 * XB; i < nblk; i += 64) put(i, xv[2 * i], xv[2 * i + 1]);
-        } else {
-          auto absmax8 = [](const u32x4& v, float a) {
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              a = fmaxf(a, fabsf(__uint_as_float(u[h] << 16)));
-              a = fmaxf(a, fabsf(__uint_as_float(u[h] & 0xffff0000u)));
-            }
-            return a;
-          };
-          float amax = 0.0f;
-#pragma unroll
-          for (int q = 0; q < XB; ++q)
-            if (lane + 64 * q < nblk) amax = absmax8(xreg[m][q][1], absmax8(xreg[m][q][0], amax));
-          for (int i = lane + 64 * XB; i < nblk; i += 64)
-            amax = absmax8(xv[2 * i + 1], absmax8(xv[2 * i], amax));
-          amax = wave_max(amax);
-          float back;
-          const int sh = row_prescale(amax, &back);
-          xb[m] = back;
-          auto put8 = [&](int v8, const u32x4& v) {        // natural order: 8 elements -> 16 B
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const uint32_t e0 = f16_bits(ldexpf(__uint_as_float(u[h] << 16), sh));
-              const uint32_t e1 = f16_bits(ldexpf(__uint_as_float(u[h] & 0xffff0000u), sh));
-              o[h] = e0 | (e1 << 16);
-            }
-            *reinterpret_cast<u32x4*>(xo + 8 * v8) = u32x4{o[0], o[1], o[2], o[3]};
-          };
-#pragma unroll
-          for (int q = 0; q < XB; ++q) {
-            const int i = lane + 64 * q;
-            if (i < nblk) {
-              put8(2 * i, xreg[m][q][0]);
-              put8(2 * i + 1, xreg[m][q][1]);
-            }
-          }
-          for (int i = lane + 64 * XB; i < nblk; i += 64) {
-            put8(2 * i, xv[2 * i]);
-            put8(2 * i + 1, xv[2 * i + 1]);
-          }
-        }
-      }
-    }
+    if constexpr (INK) xst.finish(xv, xs_wave, geo.nch_w, nblk, lane, M, xb);
   };
 
   CoreArgs c;
-  const int64_t gpr = p.K / p.group;
+  const int gpr = static_cast<int>(p.K) / p.group;
   c.crow = reinterpret_cast<const uint32_t*>(p.codes + nrow * (p.K * B / 8));
   c.srow = p.scales + nrow * gpr;
   c.abrow = reinterpret_cast<const uint32_t*>(p.shapes + nrow * gpr * 2);
@@ -316,6 +228,7 @@ size_t gemv_ink_lds_bytes(int64_t M, int64_t K, int bits, int group) {
 }
 
 bool gemv_supported(int64_t K, int bits, int group) {
+  if (K > (int64_t{1} << 28)) return false;
   const GemvGeom geo = gemv_geom(K, group, gemv_spl(bits, group));
   return geo.gmax <= 4 * kGpRegs;
 }

@@ -36,7 +36,7 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
     const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
     const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
     uint16_t* t = tab_wave + nl * (1 << B);
-    if constexpr (B <= 5) {
+    if constexpr (B <= 4) {
 #pragma unroll
       for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry(a, b, static_cast<uint32_t>(v), B);
     } else {
@@ -105,6 +105,94 @@ __device__ __forceinline__ void load_dwords(const uint32_t* src, uint32_t* w) {
   } else {
 #pragma unroll
     for (int d = 0; d < N; ++d) w[d] = src[d];
+  }
+}
+
+// Accumulators of the streaming loop: group partials (part), the group-scaled
+// total (acc) and the current group's parameters.
+struct StreamState {
+  f32x4 acc;
+  f32x4 part[4];
+  float gscale;
+  uint32_t gab;
+  int gcur;
+  __device__ __forceinline__ void reset() {
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gscale = 0.0f;
+    gab = 0u;
+    gcur = -1;
+  }
+  // fold the open group's partials into acc
+  __device__ __forceinline__ f32x4 total() const {
+    return acc + gscale * ((part[0] + part[1]) + (part[2] + part[3]));
+  }
+};
+
+// One macro step t of this lane: w holds its SPL*bits code dwords. At a group
+// boundary the previous group's partials are scaled into acc and the new
+// group's parameters are read from gp_wave (entry g - g0). Activations come
+// from LDS (INK) or from xa[SPL][4] (registers).
+template <class Dec, bool INK, int SPL>
+__device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, const uint32_t* w,
+                                           const u32x4 (*xa)[4], int t, int g0, int ml) {
+  constexpr int B = Dec::kBits;
+  const int kb = c.kb, nl = c.nl;
+  const int g = t / c.mpg;
+  if (g != st.gcur) {                    // wave-uniform
+    st.acc += st.gscale * ((st.part[0] + st.part[1]) + (st.part[2] + st.part[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t* gp = c.gp_wave + (nl * c.gmax + (g - g0)) * 2;
+    st.gscale = __uint_as_float(gp[0]) * Dec::kLevelUnit;
+    st.gab = gp[1];
+    st.gcur = g;
+    build_table<Dec>(c.tab_wave, nl, kb, st.gab);
+  }
+#pragma unroll
+  for (int h = 0; h < SPL; ++h) {
+    u32x4 av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (INK) {
+        av[j] = *reinterpret_cast<const u32x4*>(
+            c.xs_wave + (ml * c.nch_w + (t - c.tb) * 4 * SPL + kb * SPL + h) * 32 + 8 * j);
+      } else {
+        av[j] = xa[h][j];
+      }
+    }
+    uint32_t r[16];
+    if constexpr (IsW2<Dec>::value) {
+      DecodeW2::fast(&w[h * B], r);
+    } else {
+      Dec::decode(&w[h * B], c.tab_wave + nl * (1 << B), r);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+    if constexpr (IsW2<Dec>::value) {
+      const uint32_t* wv = &w[h * B];
+      if (__any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {
+        // rare (wave-uniform): code -2 present; correct r and add the lo part
+        const double a = f16_bits_to_f64(static_cast<uint16_t>(st.gab & 0xffffu));
+        const double b = f16_bits_to_f64(static_cast<uint16_t>(st.gab >> 16));
+        const float v = static_cast<float>(-2.0 * level_numerator(a, b, 2, 1));
+        const uint32_t hi = bf16_rne_bits(v);
+        const uint32_t lo = bf16_rne_bits(v - __uint_as_float(hi << 16));
+        // The operand barrier keeps this rare path's arithmetic inside
+        // the branch (otherwise it is speculated into the hot path).
+        uint32_t wl[2] = {wv[0], wv[1]};
+        asm volatile("" : "+v"(wl[0]), "+v"(wl[1]));
+        uint32_t rhi[16], rlo[16];
+        DecodeW2::extra(wl, hi, lo, rhi, rlo);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          st.part[j] = mfma16<true>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]}, st.part[j]);
+          st.part[j] = mfma16<true>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]}, st.part[j]);
+        }
+      }
+    }
   }
 }
 
@@ -178,13 +266,8 @@ __device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c, IssueX&& issue_x, 
   }
   wave_lds_order();
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 part[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float gscale = 0.0f;
-  uint32_t gab = 0u;
-  int gcur = -1;
+  StreamState st;
+  st.reset();
   const int ml = nl < c.M ? nl : 0;
   for (int t0 = tb; t0 < te; t0 += P) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
@@ -195,61 +278,7 @@ __device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c, IssueX&& issue_x, 
            // operand barrier: decode this slot here, not hoisted ahead of the loop
 #pragma unroll
            for (int d = 0; d < DW; ++d) asm volatile("" : "+v"(cb[u][d]));
-           const int g = t / mpg;
-           if (g != gcur) {                    // wave-uniform
-             acc += gscale * ((part[0] + part[1]) + (part[2] + part[3]));
-#pragma unroll
-             for (int j = 0; j < 4; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-             const uint32_t* gp = c.gp_wave + (nl * c.gmax + (g - g0)) * 2;
-             gscale = __uint_as_float(gp[0]) * Dec::kLevelUnit;
-             gab = gp[1];
-             gcur = g;
-             build_table<Dec>(c.tab_wave, nl, kb, gab);
-           }
-#pragma unroll
-           for (int h = 0; h < SPL; ++h) {
-             u32x4 av[4];
-#pragma unroll
-             for (int j = 0; j < 4; ++j) {
-               if constexpr (INK) {
-                 av[j] = *reinterpret_cast<const u32x4*>(
-                     c.xs_wave + (ml * c.nch_w + (t - tb) * 4 * SPL + kb * SPL + h) * 32 + 8 * j);
-               } else {
-                 av[j] = xa[u][h][j];
-               }
-             }
-             uint32_t r[16];
-             if constexpr (IsW2<Dec>::value) {
-               DecodeW2::fast(&cb[u][h * B], r);
-             } else {
-               Dec::decode(&cb[u][h * B], c.tab_wave + nl * (1 << B), r);
-             }
-#pragma unroll
-             for (int j = 0; j < 4; ++j)
-               part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, part[j]);
-             if constexpr (IsW2<Dec>::value) {
-               const uint32_t* wv = &cb[u][h * B];
-               if (__any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {
-                 // rare (wave-uniform): code -2 present; correct r and add the lo part
-                 const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
-                 const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
-                 const float v = static_cast<float>(-2.0 * level_numerator(a, b, 2, 1));
-                 const uint32_t hi = bf16_rne_bits(v);
-                 const uint32_t lo = bf16_rne_bits(v - __uint_as_float(hi << 16));
-                 // The operand barrier keeps this rare path's arithmetic inside
-                 // the branch (otherwise it is speculated into the hot path).
-                 uint32_t wl[2] = {wv[0], wv[1]};
-                 asm volatile("" : "+v"(wl[0]), "+v"(wl[1]));
-                 uint32_t rhi[16], rlo[16];
-                 DecodeW2::extra(wl, hi, lo, rhi, rlo);
-#pragma unroll
-                 for (int j = 0; j < 4; ++j) {
-                   part[j] = mfma16<true>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]}, part[j]);
-                   part[j] = mfma16<true>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]}, part[j]);
-                 }
-               }
-             }
-           }
+           step_macro<Dec, INK, SPL>(c, st, cb[u], xa[INK ? 0 : u], t, g0, ml);
          }
          if constexpr (!ALLIN)
            load_step(std::integral_constant<int, u>{}, t + P);   // unconditional (clamped)
@@ -258,9 +287,113 @@ __device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c, IssueX&& issue_x, 
        ...);
     }(std::make_integer_sequence<int, P>{});
   }
-  acc += gscale * ((part[0] + part[1]) + (part[2] + part[3]));
-  return acc;
+  return st.total();
 }
+
+// Per-wave staging of bf16 activation rows into LDS for the streaming loop's
+// in-kernel mode: each wave copies its own K slice of up to MT rows, chunk-major
+// and in the decoder's slot order.
+//  - bf16 decoders (2-bit codes): raw bf16, only permuted (v_perm), back = 1.
+//  - fp16 decoders: a power-of-two prescale per (row, slice), then fp16; back
+//    is the factor that undoes it on the wave's partial sums.
+// issue() loads the first XB 16-element blocks per lane and row into registers
+// (indices clamped, so the loads are unconditional) and should run before the
+// weight loads; finish() writes them and copies any longer tail.
+template <class Dec, int MT, int XB>
+struct XStage {
+  u32x4 reg[MT][XB][2];
+
+  __device__ __forceinline__ void issue(const u32x4* const* xv, int nblk, int lane) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < XB; ++q) {
+        int i = lane + 64 * q;
+        i = i < nblk ? i : 0;
+        reg[m][q][0] = xv[m][2 * i];
+        reg[m][q][1] = xv[m][2 * i + 1];
+      }
+  }
+
+  // xs_wave: the wave's LDS rows (nch_w chunks of 32 each); back[m] receives the
+  // back multiplier of row m (rows >= M are left alone).
+  __device__ __forceinline__ void finish(const u32x4* const* xv, uint16_t* xs_wave, int nch_w,
+                                         int nblk, int lane, int M, float* back) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= M) break;
+      uint16_t* xo = xs_wave + m * nch_w * 32;
+      if constexpr (Dec::kBf16) {
+        // 16 consecutive codes 16d..16d+15 fill slots 16d..16d+15 as pairs
+        // (code i, code i+8): out[2k] / out[2k+1] take the low / high halves
+        // of input registers k and 4+k.
+        auto put = [&](int i, const u32x4& lo, const u32x4& hi) {
+          const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          uint32_t o[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            o[2 * k] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x05040100u);
+            o[2 * k + 1] = __builtin_amdgcn_perm(in[4 + k], in[k], 0x07060302u);
+          }
+          u32x4* dst = reinterpret_cast<u32x4*>(xo + 16 * i);
+          dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+          dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+        };
+        // unconditional: lanes past the slice rewrite block 0 with block 0's data
+        // (a conditional use would let the compiler sink the loads behind the
+        // weight stream)
+#pragma unroll
+        for (int q = 0; q < XB; ++q) {
+          const int i = lane + 64 * q;
+          put(i < nblk ? i : 0, reg[m][q][0], reg[m][q][1]);
+        }
+        for (int i = lane + 64 * XB; i < nblk; i += 64) put(i, xv[m][2 * i], xv[m][2 * i + 1]);
+        back[m] = 1.0f;
+      } else {
+        auto absmax8 = [](const u32x4& v, float a) {
+          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            a = fmaxf(a, fabsf(__uint_as_float(u[h] << 16)));
+            a = fmaxf(a, fabsf(__uint_as_float(u[h] & 0xffff0000u)));
+          }
+          return a;
+        };
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < XB; ++q)
+          if (lane + 64 * q < nblk) amax = absmax8(reg[m][q][1], absmax8(reg[m][q][0], amax));
+        for (int i = lane + 64 * XB; i < nblk; i += 64)
+          amax = absmax8(xv[m][2 * i + 1], absmax8(xv[m][2 * i], amax));
+        amax = wave_max(amax);
+        const int sh = row_prescale(amax, &back[m]);
+        auto put8 = [&](int v8, const u32x4& v) {        // natural order: 8 elements -> 16 B
+          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t e0 = f16_bits(ldexpf(__uint_as_float(u[h] << 16), sh));
+            const uint32_t e1 = f16_bits(ldexpf(__uint_as_float(u[h] & 0xffff0000u), sh));
+            o[h] = e0 | (e1 << 16);
+          }
+          *reinterpret_cast<u32x4*>(xo + 8 * v8) = u32x4{o[0], o[1], o[2], o[3]};
+        };
+#pragma unroll
+        for (int q = 0; q < XB; ++q) {
+          const int i = lane + 64 * q;
+          if (i < nblk) {
+            put8(2 * i, reg[m][q][0]);
+            put8(2 * i + 1, reg[m][q][1]);
+          }
+        }
+        for (int i = lane + 64 * XB; i < nblk; i += 64) {
+          put8(2 * i, xv[m][2 * i]);
+          put8(2 * i + 1, xv[m][2 * i + 1]);
+        }
+      }
+    }
+  }
+};
 
 // Launch geometry shared by the host launcher and the kernel.
 struct GemvGeom {
@@ -273,7 +406,7 @@ struct GemvGeom {
 
 __host__ __device__ inline GemvGeom gemv_geom(int64_t K, int group, int spl, int waves = 4) {
   GemvGeom g;
-  g.nmacro = static_cast<int>(K / (kStep * spl));
+  g.nmacro = static_cast<int>(K) / (kStep * spl);     // K <= 2^28 (gemv_supported)
   g.mpw = (g.nmacro + waves - 1) / waves;
   g.nch_w = g.mpw * 4 * spl;
   g.mpg = group / (kStep * spl);

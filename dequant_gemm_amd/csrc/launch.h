@@ -39,12 +39,10 @@ struct MoeGemvParams {
   int64_t N, K;
   int group, topk;
   int64_t code_bytes;     // per expert
-  const int32_t* hdr;
-  const int32_t* offsets;
-  const int32_t* active;
-  const int32_t* sorted;
-  const uint16_t* xp;     // prepared activations [T][K]
-  const float* xback;     // [T]
+  const int32_t* hdr;     // [1]: touched experts
+  const int32_t* erec;    // per touched expert: expert, first pair, pairs, pair ids 0 and 1
+  const int32_t* sorted;  // pair ids grouped by expert
+  const uint16_t* x;      // bf16 activations [T][K]
   float* y;               // [T*topk][N]
 };
 
@@ -70,7 +68,6 @@ hipError_t launch_prefill_a16(const TiledParams& p, int bits, hipStream_t st);
 // LDS the grouped kernel needs with one activation row per pass.
 size_t moe_lds_min_bytes(int64_t K, int bits, int group);
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
-                      int32_t* hdr, int32_t* counts, int32_t* offsets, int32_t* active,
-                      int32_t* sorted, int bits, hipStream_t st);
+                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st);
 
 }  // namespace cubic

@@ -7,8 +7,8 @@
 // that every touched expert's weights stream from HBM once per launch, whatever
 // the number of tokens that picked it.
 //
-// k_moe_route (one block): per-expert counts, exclusive scan into offsets,
-// the compacted list of touched experts, and the pair ids sorted by expert.
+// k_moe_route (one block): per-expert counts and prefix sums in LDS, the pair
+// ids grouped by expert, and a compact record per touched expert.
 // Invalid ids are counted in hdr[0] and their output rows zeroed. No host sync.
 // k_moe_gemv: one workgroup per (touched expert, 16-row tile); the expert's
 // pairs form the activation rows of the MFMA tile (up to two per pass).
@@ -17,74 +17,150 @@
 
 namespace cubic {
 
+constexpr int kRouteExperts = 2048;   // experts per LDS chunk of the routing kernel
+constexpr int kRouteIdRegs = 4;       // pair ids held in registers per thread (4096 pairs)
+
+// Exclusive prefix sums over the 1024 threads of two per-thread values
+// (wave shuffles, then the 16 wave totals); returns the block totals.
+__device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int& ea, int& eb, int& ta,
+                                            int& tb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = a, y = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(x, o), v = __shfl_up(y, o);
+    if (lane >= o) { x += u; y += v; }
+  }
+  if (lane == 63) { s_w[w] = x; s_w[16 + w] = y; }
+  __syncthreads();
+  int pa = 0, pb = 0;
+  ta = 0; tb = 0;
+  for (int k = 0; k < 16; ++k) {
+    const int wa = s_w[k], wb = s_w[16 + k];
+    if (k < w) { pa += wa; pb += wb; }
+    ta += wa; tb += wb;
+  }
+  ea = pa + x - a;
+  eb = pb + y - b;
+  __syncthreads();                             // s_w is reused by the next call
+}
+
+// One block of 1024 threads. Counts, prefix sums and write cursors live in LDS,
+// over experts in chunks of kRouteExperts; pair ids are read once into
+// registers (up to 4096 pairs, beyond that re-read per pass).
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ ids, int P, int E,
                                                     int64_t N, float* __restrict__ y,
                                                     int32_t* __restrict__ hdr,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ erec,
                                                     int32_t* __restrict__ sorted) {
-  __shared__ int32_t s_sum[1024];
-  __shared__ int32_t s_act[1024];
+  constexpr int kBadList = 256;                 // invalid pairs whose rows are cleared cooperatively
+  constexpr int EPT = kRouteExperts / 1024;     // experts per thread in a chunk
+  __shared__ int32_t s_cnt[kRouteExperts];      // counts, then write cursors
+  __shared__ int32_t s_beg[kRouteExperts];      // first position of each expert in sorted
+  __shared__ int32_t s_first[kRouteExperts][2]; // first two pair ids of each expert
+  __shared__ int32_t s_w[32];
+  __shared__ int32_t s_bad[kBadList];
+  __shared__ int32_t s_nbad;
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) counts[e] = 0;
-  if (tid == 0) hdr[0] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += 1024) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) {
-      atomicAdd(&counts[e], 1);
-    } else {
-      atomicAdd(&hdr[0], 1);
-    }
+  int idr[kRouteIdRegs];
+#pragma unroll
+  for (int r = 0; r < kRouteIdRegs; ++r) {
+    const int p = tid + 1024 * r;
+    idr[r] = p < P ? ids[p] : -1;
   }
-  // zero the output rows of invalid pairs (rare)
-  for (int p = 0; p < P; ++p) {
-    const int e = ids[p];
+  // f(e, p) for every pair p of this thread: the first kRouteIdRegs from registers
+  auto each_pair = [&](auto&& f) {
+#pragma unroll
+    for (int r = 0; r < kRouteIdRegs; ++r) {
+      const int p = tid + 1024 * r;
+      if (p < P) f(idr[r], p);
+    }
+    for (int p = tid + 1024 * kRouteIdRegs; p < P; p += 1024) f(ids[p], p);
+  };
+  if (tid == 0) s_nbad = 0;
+  __syncthreads();
+  each_pair([&](int e, int p) {
     if (e < 0 || e >= E) {
-      for (int64_t n = tid; n < N; n += 1024) y[static_cast<int64_t>(p) * N + n] = 0.0f;
+      const int k = atomicAdd(&s_nbad, 1);
+      if (k < kBadList) {
+        s_bad[k] = p;
+      } else {                                  // beyond the list: this thread clears the row
+        for (int64_t n = 0; n < N; ++n) y[static_cast<int64_t>(p) * N + n] = 0.0f;
+      }
     }
-  }
+  });
   __syncthreads();
-  // each thread scans a contiguous segment of experts
-  const int seg = (E + 1023) / 1024;
-  const int e0 = tid * seg, e1 = min(E, e0 + seg);
-  int sum = 0, act = 0;
-  for (int e = e0; e < e1; ++e) {
-    sum += counts[e];
-    act += counts[e] > 0;
+  // output rows of invalid pairs are zero
+  const int nbad = min(s_nbad, kBadList);
+  for (int b = 0; b < nbad; ++b) {
+    const int64_t row = s_bad[b];
+    for (int64_t n = tid; n < N; n += 1024) y[row * N + n] = 0.0f;
   }
-  s_sum[tid] = sum;
-  s_act[tid] = act;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 per-thread totals
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int a = tid >= o ? s_sum[tid - o] : 0;
-    const int b = tid >= o ? s_act[tid - o] : 0;
+  if (tid == 0) hdr[0] = s_nbad;
+
+  int base_pairs = 0, base_act = 0;             // totals of the chunks before (block-uniform)
+  for (int c0 = 0; c0 < E; c0 += kRouteExperts) {
+    const int c1 = min(E, c0 + kRouteExperts);
+    for (int k = tid; k < kRouteExperts; k += 1024) s_cnt[k] = 0;
     __syncthreads();
-    s_sum[tid] += a;
-    s_act[tid] += b;
+    each_pair([&](int e, int) {
+      if (e >= c0 && e < c1) atomicAdd(&s_cnt[e - c0], 1);
+    });
     __syncthreads();
+    // this thread's experts c0 + EPT*tid + i: first pair offsets and record slots
+    int cnt[EPT], sum = 0, act = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      cnt[i] = s_cnt[EPT * tid + i];
+      sum += cnt[i];
+      act += cnt[i] > 0;
+    }
+    int off, slot, tot, tact;
+    block_scan2(sum, act, s_w, off, slot, tot, tact);
+    off += base_pairs;
+    slot += base_act;
+    int beg[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      beg[i] = off;
+      s_beg[EPT * tid + i] = off;
+      s_cnt[EPT * tid + i] = off;              // becomes the write cursor
+      off += cnt[i];
+    }
+    __syncthreads();
+    each_pair([&](int e, int p) {
+      if (e >= c0 && e < c1) {
+        const int pos = atomicAdd(&s_cnt[e - c0], 1);
+        sorted[pos] = p;
+        const int rank = pos - s_beg[e - c0];
+        if (rank < 2) s_first[e - c0][rank] = p;
+      }
+    });
+    __syncthreads();
+    // One record per touched expert, in expert order: what a workgroup of the
+    // product needs before it can issue its loads (expert, first pair, pair
+    // count, the first two pair ids), in one 32-byte read.
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int k = EPT * tid + i;
+      if (cnt[i] > 0) {
+        const int f0 = s_first[k][0];
+        erec[8 * slot] = c0 + k;
+        erec[8 * slot + 1] = beg[i];
+        erec[8 * slot + 2] = cnt[i];
+        erec[8 * slot + 3] = f0;
+        erec[8 * slot + 4] = cnt[i] > 1 ? s_first[k][1] : f0;
+        ++slot;
+      }
+    }
+    base_pairs += tot;
+    base_act += tact;
+    __syncthreads();                           // LDS arrays are reset by the next chunk
   }
-  int run = s_sum[tid] - sum, arun = s_act[tid] - act;
-  for (int e = e0; e < e1; ++e) {
-    offsets[e] = run;
-    const int c = counts[e];
-    if (c > 0) active[arun++] = e;
-    run += c;
-  }
-  if (tid == 1023) {
-    offsets[E] = s_sum[1023];
-    hdr[1] = s_act[1023];
-  }
-  __syncthreads();
-  // counts become write cursors
-  for (int e = e0; e < e1; ++e) counts[e] = offsets[e];
-  __syncthreads();
-  for (int p = tid; p < P; p += 1024) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) sorted[atomicAdd(&counts[e], 1)] = p;
-  }
+  // Record slots up to the grid's bound get a zero pair count: a workgroup of the
+  // product decides from its record alone whether it has work.
+  if (tid == 0) hdr[1] = base_act;
+  for (int a = base_act + tid; a < min(E, P); a += 1024) erec[8 * a + 2] = 0;
 }
 
 // One workgroup per work item (touched expert a, 16-row tile): the grid covers
@@ -96,13 +172,15 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
 // waves' partial sums meet in LDS in a fixed order.
 template <class Dec, int SPL, int P, bool ALLIN, int MT>
 __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
+  static_assert(MT == 1 || MT == 2, "one or two activation rows per pass");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int B = Dec::kBits;
-  constexpr int XB = 4;                         // 16-byte vectors per lane and row issued ahead
-  const int64_t tiles = (p.N + 15) / 16;
-  const int a = static_cast<int>(blockIdx.x / tiles);
-  if (a >= p.hdr[1]) return;                    // fewer experts touched than the grid allows
-  const int64_t n0 = (blockIdx.x - static_cast<int64_t>(a) * tiles) * 16;
+  constexpr int XB = 2;                         // 16-element blocks per lane and row issued ahead
+  const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
+  const unsigned a = blockIdx.x / tiles;
+  const i32x8 rec = *reinterpret_cast<const i32x8*>(p.erec + 8 * a);
+  if (rec[2] == 0) return;                      // fewer experts touched than the grid allows
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x - a * tiles) * 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
@@ -116,11 +194,10 @@ __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
   uint16_t* xs_wave = reinterpret_cast<uint16_t*>(q) + static_cast<int64_t>(wave) * MT * geo.nch_w * 32;
   const int tb = wave * geo.nmacro / 4, te = (wave + 1) * geo.nmacro / 4;
   const int64_t k0 = static_cast<int64_t>(tb) * kStep * SPL;
-  const int nvec = (te - tb) * kStep * SPL / 8;  // 16-byte vectors in the wave's slice of a row
-  const int64_t gpr = p.K / p.group;
+  const int nblk = (te - tb) * kStep * SPL / 16;  // 16-element blocks in the wave's slice of a row
+  const int gpr = static_cast<int>(p.K) / p.group;
 
-  const int e = p.active[a];
-  const int beg = p.offsets[e], cnt = p.offsets[e + 1] - beg;
+  const int e = rec[0], beg = rec[1], cnt = rec[2];
   const int64_t nrow = (n0 + nl < p.N) ? (n0 + nl) : (p.N - 1);
   CoreArgs c;
   c.crow = reinterpret_cast<const uint32_t*>(p.codes + e * p.code_bytes + nrow * (p.K * B / 8));
@@ -134,55 +211,259 @@ __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
   for (int mt = 0; mt < cnt; mt += MT) {
     const int Mt = min(MT, cnt - mt);
     c.M = Mt;
+    int pr[MT];                                 // pair ids of this pass (the first from the record)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      pr[m] = mt == 0 ? (m == 0 ? rec[3] : rec[4]) : p.sorted[beg + mt + (m < Mt ? m : 0)];
     const u32x4* xv[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int tok = p.sorted[beg + mt + (m < Mt ? m : 0)] / p.topk;
-      xv[m] = reinterpret_cast<const u32x4*>(p.xp + static_cast<int64_t>(tok) * p.K + k0);
-    }
-    // The first XB vectors per lane and row are loaded before the weight stream
-    // (indices clamped, so the loads are unconditional) and written to LDS after
-    // it has been issued; longer slices copy the rest there.
-    u32x4 xreg[MT][XB];
-    auto issue_x = [&]() {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int v = 0; v < XB; ++v) {
-          const int i = lane + 64 * v;
-          xreg[m][v] = xv[m][i < nvec ? i : 0];
-        }
-    };
-    auto finish_x = [&]() {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m >= Mt) break;
-        u32x4* dst = reinterpret_cast<u32x4*>(xs_wave + m * geo.nch_w * 32);
-#pragma unroll
-        for (int v = 0; v < XB; ++v) {
-          const int i = lane + 64 * v;
-          if (i < nvec) dst[i] = xreg[m][v];
-        }
-        for (int i = lane + 64 * XB; i < nvec; i += 64) dst[i] = xv[m][i];
-      }
-    };
+    for (int m = 0; m < MT; ++m)
+      xv[m] = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(pr[m] / p.topk) * p.K + k0);
+    XStage<Dec, MT, XB> xst;
+    float xb[MT];
+    auto issue_x = [&]() { xst.issue(xv, nblk, lane); };
+    auto finish_x = [&]() { xst.finish(xv, xs_wave, geo.nch_w, nblk, lane, Mt, xb); };
     const f32x4 acc = gemv_core<Dec, true, SPL, P, ALLIN>(c, issue_x, finish_x);
+    // acc row 4 kb + r is activation row m of this pass; undo the wave's prescale
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kb + r) * 16 + nl] = acc[r];
+    for (int r = 0; r < 4; ++r) {
+      float v = acc[r];
+      if (kb == 0 && r < Mt) v *= xb[r < MT ? r : 0];
+      red[(wave * 16 + 4 * kb + r) * 16 + nl] = v;
+    }
     __syncthreads();
     const int t = threadIdx.x;
     if (t < Mt * 16) {
       const int m = t >> 4, cc = t & 15;
       if (n0 + cc < p.N) {
-        const int pr = p.sorted[beg + mt + m];
+        const int q = MT == 1 || m == 0 ? pr[0] : pr[MT - 1];
         float v = red[(0 * 16 + m) * 16 + cc];
         v += red[(1 * 16 + m) * 16 + cc];
         v += red[(2 * 16 + m) * 16 + cc];
         v += red[(3 * 16 + m) * 16 + cc];
-        p.y[static_cast<int64_t>(pr) * p.N + n0 + cc] = v * p.xback[pr / p.topk];
+        p.y[static_cast<int64_t>(q) * p.N + n0 + cc] = v;
       }
     }
     if (mt + MT < cnt) __syncthreads();   // red and the LDS slices are reused by the next pass
+  }
+}
+
+// Persistent variant: each workgroup walks units (touched expert, 16-row tile,
+// pass of MT pairs) with a grid stride, and while it computes one unit its
+// lanes already have the next unit's loads in flight: every lane refills the
+// code slot of macro step t with the next unit's macro step t right after
+// consuming it, and the next unit's group parameters and activation rows are
+// fetched one unit ahead into registers. So the memory pipe never drains at a
+// unit boundary. Needs te - tb <= PM for every wave (one slot per macro step)
+// and at most 4 * GPR groups per wave. OCC workgroups per compute unit.
+template <class Dec, int SPL, int PM, int MT, int GPR, int OCC>
+__global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
+                                                         const int32_t* __restrict__ erec,
+                                                         const int32_t* __restrict__ sorted,
+                                                         float* __restrict__ y) {
+  static_assert(MT == 1 || MT == 2, "one or two activation rows per pass");
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int B = Dec::kBits;
+  constexpr int DW = B * SPL;
+  constexpr int XB = 2;
+  const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
+  const unsigned items = static_cast<unsigned>(p.hdr[1]) * tiles;
+  if (blockIdx.x >= items) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nl = lane & 15, kb = lane >> 4;
+  const GemvGeom geo = gemv_geom(p.K, p.group, SPL);
+  float* red = reinterpret_cast<float*>(smem);
+  unsigned char* q = smem + 4 * 16 * 16 * 4;
+  uint16_t* tab_wave = reinterpret_cast<uint16_t*>(q + wave * tab_bytes_per_wave<Dec>());
+  q += 4 * tab_bytes_per_wave<Dec>();
+  uint32_t* gp_wave = reinterpret_cast<uint32_t*>(q) + wave * 16 * geo.gmax * 2;
+  q += static_cast<size_t>(4) * 16 * geo.gmax * 8;
+  uint16_t* xs_wave = reinterpret_cast<uint16_t*>(q) + static_cast<int64_t>(wave) * MT * geo.nch_w * 32;
+  const int tb = wave * geo.nmacro / 4, te = (wave + 1) * geo.nmacro / 4;
+  const int64_t k0 = static_cast<int64_t>(tb) * kStep * SPL;
+  const int nblk = (te - tb) * kStep * SPL / 16;
+  const int gpr = static_cast<int>(p.K) / p.group;
+  const int g0 = tb / geo.mpg;
+  const int gn = te > tb ? (te - 1) / geo.mpg - g0 + 1 : 0;
+  const int64_t row_bytes = p.K * B / 8;
+
+  // A unit: item it (expert slot it / tiles, tile it % tiles) and pass mt.
+  struct Unit {
+    unsigned it;
+    int mt, e, beg, cnt, M;
+    int pr[MT];
+    int64_t n0;
+  };
+  auto make_unit = [&](unsigned it, int mt, const i32x8& rec) {
+    Unit u;
+    u.it = it;
+    u.mt = mt;
+    u.e = rec[0]; u.beg = rec[1]; u.cnt = rec[2];
+    u.M = min(MT, u.cnt - mt);
+    u.n0 = static_cast<int64_t>(it % tiles) * 16;
+    // wave-uniform indices (readfirstlane) make these scalar loads, which do
+    // not wait behind the vector loads in flight
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      u.pr[m] = mt == 0 ? (m == 0 ? rec[3] : rec[4])
+                        : sorted[__builtin_amdgcn_readfirstlane(u.beg + mt + (m < u.M ? m : 0))];
+    return u;
+  };
+  auto load_rec = [&](unsigned it) {
+    const int a = __builtin_amdgcn_readfirstlane(static_cast<int>(it / tiles));
+    return *reinterpret_cast<const i32x8*>(erec + 8 * a);
+  };
+  auto row_of = [&](const Unit& u) {
+    const int64_t n = u.n0 + nl;
+    return static_cast<int64_t>(u.e) * p.N + (n < p.N ? n : p.N - 1);
+  };
+
+  uint32_t cb[PM][DW];
+  uint32_t gsc[GPR], gabr[GPR];
+  XStage<Dec, MT, XB> xst;
+  const u32x4* xv[MT];
+  float xb[MT];
+  auto issue_gp = [&](const Unit& u) {
+    const int64_t r = row_of(u);
+    const float* srow = p.scales + r * gpr;
+    const uint32_t* abrow = reinterpret_cast<const uint32_t*>(p.shapes + r * gpr * 2);
+#pragma unroll
+    for (int k = 0; k < GPR; ++k) {
+      const int gi = kb + 4 * k;
+      const int g = g0 + (gi < gn ? gi : 0);
+      gsc[k] = __float_as_uint(srow[g]);
+      gabr[k] = abrow[g];
+    }
+  };
+  auto set_x = [&](const Unit& u) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      xv[m] = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(u.pr[m] / p.topk) * p.K + k0);
+  };
+  auto code_row = [&](const Unit& u) {
+    const int64_t n = u.n0 + nl;
+    return reinterpret_cast<const uint32_t*>(p.codes + u.e * p.code_bytes +
+                                             (n < p.N ? n : p.N - 1) * row_bytes);
+  };
+  auto issue_slot = [&](auto u_c, const uint32_t* crow) {
+    constexpr int u = decltype(u_c)::value;
+    int t = tb + u < te ? tb + u : te - 1;     // slots past the wave's range repeat its last step
+    t = t < 0 ? 0 : t;                         // (a wave without steps reads step 0, unused)
+    load_dwords<DW>(crow + (t * 4 * SPL + kb * SPL) * B, cb[u]);
+  };
+
+  // first unit: everything issued now
+  i32x8 rec = load_rec(blockIdx.x);
+  Unit cur = make_unit(blockIdx.x, 0, rec);
+  issue_gp(cur);
+  set_x(cur);
+  xst.issue(xv, nblk, lane);
+  const u32x4* xv_cur[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xv_cur[m] = xv[m];
+  // parameters and activations stay ahead of the code loads (in the loop too), so
+  // waiting for them never waits for the code stream
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const uint32_t* crow = code_row(cur);
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      (issue_slot(std::integral_constant<int, U>{}, crow), ...);
+    }(std::make_integer_sequence<int, PM>{});
+  }
+  bool xfresh = true;
+
+  CoreArgs c;
+  c.mpg = geo.mpg;
+  c.tb = tb; c.te = te; c.nl = nl; c.kb = kb;
+  c.xrow = nullptr; c.xs_wave = xs_wave; c.nch_w = geo.nch_w; c.tab_wave = tab_wave;
+  c.gp_wave = gp_wave; c.gmax = geo.gmax;
+
+  for (;;) {
+    // the current unit's activations and group parameters into LDS
+    if (xfresh) xst.finish(xv_cur, xs_wave, geo.nch_w, nblk, lane, cur.M, xb);
+#pragma unroll
+    for (int k = 0; k < GPR; ++k) {
+      const int gi = kb + 4 * k;
+      if (gi < gn) {
+        gp_wave[(nl * geo.gmax + gi) * 2] = gsc[k];
+        gp_wave[(nl * geo.gmax + gi) * 2 + 1] = gabr[k];
+      }
+    }
+    wave_lds_order();
+
+    // the next unit (the current one again when there is none: its loads are
+    // then redundant cache hits and never used)
+    bool has_next = true;
+    Unit nxt;
+    if (cur.mt + MT < cur.cnt) {
+      nxt = make_unit(cur.it, cur.mt + MT, rec);
+    } else {
+      const unsigned it_n = __builtin_amdgcn_readfirstlane(cur.it + gridDim.x);
+      has_next = it_n < items;
+      if (has_next) {
+        rec = load_rec(it_n);
+        nxt = make_unit(it_n, 0, rec);
+      } else {
+        nxt = cur;
+      }
+    }
+    issue_gp(nxt);
+    set_x(nxt);
+    bool same_x = nxt.M == cur.M;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      same_x = same_x && (m >= cur.M || nxt.pr[m] / p.topk == cur.pr[m] / p.topk);
+    xst.issue(xv, nblk, lane);               // unconditional (cache hits when unchanged)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stream the current unit; each slot is refilled with the next unit's step
+    StreamState st;
+    st.reset();
+    const int ml = nl < cur.M ? nl : 0;
+    const uint32_t* crow_n = code_row(nxt);
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      (([&] {
+         constexpr int u = U;
+         const int t = tb + u;
+         if (t < te) {
+#pragma unroll
+           for (int d = 0; d < DW; ++d) asm volatile("" : "+v"(cb[u][d]));
+           step_macro<Dec, true, SPL>(c, st, cb[u], nullptr, t, g0, ml);
+         }
+         issue_slot(std::integral_constant<int, u>{}, crow_n);
+         __builtin_amdgcn_sched_barrier(0);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, PM>{});
+    const f32x4 acc = st.total();
+
+    // partial sums of the four waves meet in LDS in a fixed order
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = acc[r];
+      if (kb == 0 && r < cur.M) v *= xb[r < MT ? r : 0];
+      red[(wave * 16 + 4 * kb + r) * 16 + nl] = v;
+    }
+    __syncthreads();
+    const int tt = threadIdx.x;
+    if (tt < cur.M * 16) {
+      const int m = tt >> 4, cc = tt & 15;
+      if (cur.n0 + cc < p.N) {
+        const int qp = MT == 1 || m == 0 ? cur.pr[0] : cur.pr[MT - 1];
+        float v = red[(0 * 16 + m) * 16 + cc];
+        v += red[(1 * 16 + m) * 16 + cc];
+        v += red[(2 * 16 + m) * 16 + cc];
+        v += red[(3 * 16 + m) * 16 + cc];
+        y[static_cast<int64_t>(qp) * p.N + cur.n0 + cc] = v;
+      }
+    }
+    __syncthreads();                          // red is rewritten by the next unit
+    if (!has_next) break;
+    cur = nxt;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xv_cur[m] = xv[m];
+    xfresh = !same_x;
   }
 }
 
@@ -196,17 +477,19 @@ template <class Dec, int SPL, int P>
 static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, int64_t blocks, int tokens,
                                     hipStream_t st) {
   const GemvGeom geo = gemv_geom(p.K, p.group, SPL);
-  // Rows per pass: a single token needs one; otherwise two while two
-  // workgroups still fit in one compute unit's LDS (experts picked by more
-  // tokens take several passes over their codes, which then come from L2).
-  int mt = tokens <= 1 ? 1 : 2;
+  // Rows per pass: two for the 2-bit (bf16) path when several tokens are routed
+  // and two workgroups still fit in one compute unit's LDS, else one (the fp16
+  // staging of two rows does not fit the register budget). Experts picked by
+  // more tokens take several passes over their codes, which then come from L2.
+  int mt = (tokens <= 1 || !Dec::kBf16) ? 1 : 2;
   if (mt == 2 && moe_lds_bytes<Dec>(geo, 2) > 80 * 1024) mt = 1;
   const size_t lds = moe_lds_bytes<Dec>(geo, mt);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const bool allin = geo.mpw <= P;
+  constexpr int MT2 = Dec::kBf16 ? 2 : 1;
   auto pick = [&]() {
-    if (allin) return mt == 1 ? k_moe_gemv<Dec, SPL, P, true, 1> : k_moe_gemv<Dec, SPL, P, true, 2>;
-    return mt == 1 ? k_moe_gemv<Dec, SPL, P, false, 1> : k_moe_gemv<Dec, SPL, P, false, 2>;
+    if (allin) return mt == 1 ? k_moe_gemv<Dec, SPL, P, true, 1> : k_moe_gemv<Dec, SPL, P, true, MT2>;
+    return mt == 1 ? k_moe_gemv<Dec, SPL, P, false, 1> : k_moe_gemv<Dec, SPL, P, false, MT2>;
   };
   auto kern = pick();
   if (lds > 64 * 1024) {
@@ -219,6 +502,32 @@ static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, int64_t blocks, int 
   return hipGetLastError();
 }
 
+// The persistent kernel for 2-bit codes with groups of 256 or more: PM slots
+// cover a wave's macro steps, GPR registers its groups.
+template <int PM, int GPR>
+static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, int tokens,
+                                      hipStream_t st) {
+  const GemvGeom geo = gemv_geom(p.K, p.group, 2);
+  int mt = tokens <= 1 ? 1 : 2;
+  if (mt == 2 && moe_lds_bytes<DecodeW2>(geo, 2) > 80 * 1024) mt = 1;
+  const size_t lds = moe_lds_bytes<DecodeW2>(geo, mt);
+  // two rows per pass need more registers: two workgroups per compute unit
+  auto kern = mt == 1 ? k_moe_stream<DecodeW2, 2, PM, 1, GPR, 3> : k_moe_stream<DecodeW2, 2, PM, 2, GPR, 2>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  // the resident workgroups walk the units
+  const int64_t cus = device_cu_count();
+  const int64_t occ = mt == 1 ? 3 : 2;
+  const int64_t cap = (cus > 0 ? cus : 256) * occ;
+  const unsigned grid = static_cast<unsigned>(blocks < cap ? blocks : cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p, p.erec, p.sorted, p.y);
+  return hipGetLastError();
+}
+
 size_t moe_lds_min_bytes(int64_t K, int bits, int group) {
   const int spl = (bits == 2 && group % 256 == 0) ? 2 : 1;
   const GemvGeom geo = gemv_geom(K, group, spl);
@@ -226,26 +535,31 @@ size_t moe_lds_min_bytes(int64_t K, int bits, int group) {
 }
 
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
-                      int32_t* hdr, int32_t* counts, int32_t* offsets, int32_t* active,
-                      int32_t* sorted, int bits, hipStream_t st) {
+                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st) {
   const int P = T * topk;
   hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, hdr,
-                     counts, offsets, active, sorted);
+                     erec, sorted);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   MoeGemvParams p = base;
   p.topk = topk;
-  p.hdr = hdr; p.offsets = offsets; p.active = active; p.sorted = sorted;
+  p.hdr = hdr; p.erec = erec; p.sorted = sorted;
   const int64_t tiles = (p.N + 15) / 16;
   const int64_t blocks = static_cast<int64_t>(min(E, P)) * tiles;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   switch (bits) {
     case 2:
-      if (p.group % 256 == 0) return launch_moe_gemv_t<DecodeW2, 2, 8>(p, blocks, T, st);
+      if (p.group % 256 == 0) {
+        const GemvGeom geo = gemv_geom(p.K, p.group, 2);
+        if (geo.mpw <= 4 && geo.gmax <= 4) return launch_moe_stream_t<4, 1>(p, blocks, T, st);
+        if (geo.mpw <= 7 && geo.gmax <= 8) return launch_moe_stream_t<7, 2>(p, blocks, T, st);
+        if (geo.mpw <= 8 && geo.gmax <= 8) return launch_moe_stream_t<8, 2>(p, blocks, T, st);
+        return launch_moe_gemv_t<DecodeW2, 2, 8>(p, blocks, T, st);
+      }
       return launch_moe_gemv_t<DecodeW2, 1, 8>(p, blocks, T, st);
-    case 3: return launch_moe_gemv_t<DecodeTable<3>, 1, 8>(p, blocks, T, st);
-    case 4: return launch_moe_gemv_t<DecodeTable<4>, 1, 6>(p, blocks, T, st);
+    case 3: return launch_moe_gemv_t<DecodeTable<3>, 1, 6>(p, blocks, T, st);
+    case 4: return launch_moe_gemv_t<DecodeTable<4>, 1, 4>(p, blocks, T, st);
     case 5: return launch_moe_gemv_t<DecodeTable<5>, 1, 2>(p, blocks, T, st);
     case 6: return launch_moe_gemv_t<DecodeTable<6>, 1, 2>(p, blocks, T, st);
     case 7: return launch_moe_gemv_t<DecodeTable<7>, 1, 2>(p, blocks, T, st);

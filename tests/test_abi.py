@@ -45,7 +45,9 @@ def test_workspace_sizes():
     assert cq.cubic_gemm_a16_workspace_bytes(1, 7168) == 0
     assert cq.cubic_gemm_a16_workspace_bytes(4, 7168) == 0
     assert cq.cubic_gemm_a16_workspace_bytes(8, 7168) >= 8 * 7168 * 2 + 8 * 4
-    assert cq.cubic_moe_workspace_bytes(64, 16, 896, 7168) >= 64 * 7168 * 2 + 4 * (3 * 896 + 1024)
+    # one 32-byte record per expert and the grouped pair ids; no activation copy
+    assert cq.cubic_moe_workspace_bytes(64, 16, 896, 7168) >= 32 * 896 + 4 * 1024
+    assert cq.cubic_moe_workspace_bytes(64, 16, 896, 7168) == cq.cubic_moe_workspace_bytes(64, 16, 896, 1)
     lib = cq.load_library()
     assert lib.cubic_status_string(ERR_WS) == b"workspace missing or too small"
     assert lib.cubic_version().startswith(b"cubic")

@@ -107,3 +107,29 @@ def test_decode_routing_and_long_slices(bits, group, K, T):
     ref = oracle.moe_a16(x_bits(x), ids.cpu().numpy(), E, N,
                          lambda e: _expert_dense(e, N, K, bits, group, 60 + bits))
     assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
+
+
+def test_routing_over_expert_chunks_and_long_pair_lists():
+    """2500 experts (two LDS chunks of the routing kernel) and 300 x 16 = 4800
+    pairs (more than the routing kernel keeps in registers), with invalid ids."""
+    say("MoE routing: 2500 experts, 4800 pairs")
+    E, T, topk, N, K, bits, group = 2500, 300, 16, 16, 128, 2, 128
+    pool = _pool(E, N, K, bits, group, seed=70)
+    x, ids = synth.moe_routing(seed=71, T=T, E=E, topk=topk, K=K, device=DEV)
+    ids[3, 5] = -7
+    ids[299, 15] = E + 3
+    ids[:40, 0] = 2499                  # one expert with many tokens, in the second chunk
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E, K), dtype=torch.uint8, device=DEV)
+    y = cq.cubic_moe_grouped_gemm(x, ids, pool, E, workspace=ws).cpu().numpy()
+    assert int(ws[:4].view(torch.int32).item()) == 2
+    ids_np = ids.cpu().numpy()
+    dense = {}
+
+    def w_of(e):
+        if e not in dense:
+            dense[e] = _expert_dense(e, N, K, bits, group, 70)
+        return dense[e]
+
+    ref = oracle.moe_a16(x_bits(x), ids_np, E, N, w_of)
+    assert not y[3, 5].any() and not y[299, 15].any()
+    assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
