@@ -150,6 +150,14 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
     st.gcur = g;
     build_table<Dec>(c.tab_wave, nl, kb, st.gab);
   }
+  // 2-bit codes: one test per macro step for the field value 10 (code -2)
+  bool extra = false;
+  if constexpr (IsW2<Dec>::value) {
+    uint32_t ex = 0;
+#pragma unroll
+    for (int d = 0; d < B * SPL; ++d) ex |= w[d] & ~(w[d] << 1);
+    extra = __any((ex & 0xAAAAAAAAu) != 0u);
+  }
 #pragma unroll
   for (int h = 0; h < SPL; ++h) {
     u32x4 av[4];
@@ -173,7 +181,7 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
       st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
     if constexpr (IsW2<Dec>::value) {
       const uint32_t* wv = &w[h * B];
-      if (__any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {
+      if (extra && __any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {
         // rare (wave-uniform): code -2 present; correct r and add the lo part
         const double a = f16_bits_to_f64(static_cast<uint16_t>(st.gab & 0xffffu));
         const double b = f16_bits_to_f64(static_cast<uint16_t>(st.gab >> 16));

@@ -52,3 +52,18 @@ def ulp32(v: np.ndarray) -> np.ndarray:
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     e = np.maximum(e, -126)
     return np.where(a > 0, np.exp2(e - 23), 2.0 ** -149)
+
+
+def pack_fields(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Packs any two's-complement field values, including -2^(bits-1), which the
+    format's packer rejects: LSB-first over the row-major [N][K] codes. Lets
+    tests plant codes outside [-Kmax, Kmax]; checked against oracle.pack and
+    oracle.unpack in the CPU tests."""
+    codes = np.asarray(codes)
+    u = (codes.astype(np.int64) & ((1 << bits) - 1)).reshape(-1)
+    pos0 = np.arange(u.size, dtype=np.int64) * bits
+    out = np.zeros(u.size * bits // 8, dtype=np.int64)
+    for b in range(bits):
+        pos = pos0 + b
+        np.add.at(out, pos // 8, ((u >> b) & 1) << (pos % 8))
+    return out.astype(np.uint8).reshape(codes.shape[0], -1)

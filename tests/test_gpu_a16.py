@@ -10,7 +10,7 @@ import torch
 import dequant_gemm_amd as cq
 import oracle
 import synth
-from tests._gpu import DEV, np_weight, row_rel_err, say, upload, x_bits
+from tests._gpu import DEV, np_weight, pack_fields, row_rel_err, say, upload, x_bits
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -162,3 +162,25 @@ def test_small_m_rows_per_workgroup_ragged(bits, group, M):
     w = synth.make_weight(g, 4100, 1024, bits, group, kind, 0.02)
     x = synth.activations(g, M, 1024, 0.01, 50.0)
     _check(w, x)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_sparse_extra_codes_w2(M):
+    """Ternary 2-bit weights with a few codes -2 planted at scattered positions:
+    most 128-code steps have none, some have one in only one of their halves."""
+    say(f"A16 W2 sparse extra codes M={M}")
+    g = synth.make_generator(321)
+    N, K, G = 200, 2048, 512
+    w = synth.make_weight(g, N, K, 2, G, "ternary", 0.02)
+    codes = w.codes.cpu().numpy().copy()
+    rng = np.random.default_rng(5)
+    for n, k in zip(rng.integers(0, N, 40), rng.integers(0, K, 40)):
+        codes[n, k] = -2
+    codes[7, 0] = codes[7, 255] = codes[7, 256] = codes[7, K - 1] = -2
+    raw = torch.from_numpy(pack_fields(codes, 2).reshape(-1))
+    scales, shapes = w.scales.cpu().numpy(), w.shapes.cpu().numpy().view(np.uint16)
+    cw = cq.CubicWeight(raw.to(DEV), w.scales.to(DEV), w.shapes.to(DEV), N, K, 2, G)
+    x = synth.activations(g, M, K)
+    y = cq.cubic_gemm_a16(x.to(DEV), cw).cpu().numpy()
+    ref = oracle.gemm_a16(x_bits(x), oracle.dequant(codes, scales, shapes, 2, G))
+    assert row_rel_err(y, ref) <= TOL

@@ -10,7 +10,7 @@ import torch
 import dequant_gemm_amd as cq
 import oracle
 import synth
-from tests._gpu import DEV, np_weight, row_rel_err, say, x_bits
+from tests._gpu import DEV, np_weight, pack_fields, row_rel_err, say, x_bits
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -132,4 +132,32 @@ def test_routing_over_expert_chunks_and_long_pair_lists():
 
     ref = oracle.moe_a16(x_bits(x), ids_np, E, N, w_of)
     assert not y[3, 5].any() and not y[299, 15].any()
+    assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_sparse_extra_codes_routed(T):
+    """Routed 2-bit experts with a few codes -2 planted (the rare decode path
+    inside the persistent kernel), decode-sized routing."""
+    say(f"MoE W2 sparse extra codes T={T}")
+    E, topk, N, K, bits, group = 12, 6, 144, 1024, 2, 512
+    cb = N * K * bits // 8
+    rng = np.random.default_rng(9)
+    codes_all, dense = [], []
+    packed = torch.empty(E * cb, dtype=torch.uint8)
+    scales = torch.empty((E, N, K // group), dtype=torch.float32)
+    shapes = torch.empty((E, N, K // group, 2), dtype=torch.int16)
+    for e in range(E):
+        w = synth.moe_expert(e, seed=90, N=N, K=K, bits=bits, group=group)
+        c = w.codes.numpy().copy()
+        for n, k in zip(rng.integers(0, N, 6), rng.integers(0, K, 6)):
+            c[n, k] = -2
+        packed[e * cb:(e + 1) * cb] = torch.from_numpy(pack_fields(c, bits).reshape(-1))
+        scales[e], shapes[e] = w.scales, w.shapes
+        dense.append(oracle.dequant(c, w.scales.numpy(), w.shapes.numpy().view(np.uint16), bits, group))
+    pool = cq.CubicWeight(packed.to(DEV), scales.reshape(-1).to(DEV), shapes.reshape(-1).to(DEV),
+                          N, K, bits, group)
+    x, ids = synth.moe_routing(seed=91, T=T, E=E, topk=topk, K=K, device=DEV)
+    y = cq.cubic_moe_grouped_gemm(x, ids, pool, E).cpu().numpy()
+    ref = oracle.moe_a16(x_bits(x), ids.cpu().numpy(), E, N, lambda e: dense[e])
     assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL

@@ -379,3 +379,16 @@ def test_generator_determinism_and_distributions():
     assert abs((c == 0).mean() - 0.5) < 0.01 and abs((c == 1).mean() - 0.25) < 0.01
     c = synth.codes_laplace(g, 64, 1024).numpy()
     assert c.min() >= -7 and c.max() <= 7 and abs((c == 0).mean() - (1 - np.exp(-(0.5 / 7) / 0.25))) < 0.02
+
+
+def test_test_side_field_packer_matches_oracle():
+    """The tests' packer for planted out-of-range codes agrees with oracle.pack on
+    in-range codes and round-trips through oracle.unpack with -2^(B-1) present."""
+    from tests._gpu import pack_fields
+    rng = np.random.default_rng(3)
+    for bits in (2, 3, 4, 5, 8):
+        km = (1 << (bits - 1)) - 1
+        c = rng.integers(-km, km + 1, size=(5, 64)).astype(np.int8)
+        assert np.array_equal(pack_fields(c, bits), oracle.pack(c, bits))
+        c[0, 0] = c[3, 17] = c[4, 63] = -(1 << (bits - 1))
+        assert np.array_equal(oracle.unpack(pack_fields(c, bits), 5, 64, bits), c)
