@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 20 plain device copies of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--counter-run", choices=("gate_up", "down"), default=None,
+                    help="only launch this product --steps times, eagerly on rotating copies "
+                         "(for rocprofv3 --pmc passes)")
     return ap.parse_args()
 
 
@@ -158,6 +161,13 @@ def main():
     dns = [base_dn] + [clone(base_dn) for _ in range(R - 1)]
     y_up = torch.empty((1, 6144), dtype=torch.float32, device=dev)
     y_dn = torch.empty((1, 7168), dtype=torch.float32, device=dev)
+    if args.counter_run:
+        pool, xx, yy = (ups, x_up, y_up) if args.counter_run == "gate_up" else (dns, x_dn, y_dn)
+        for i in range(args.steps):
+            cq.cubic_gemm_a16(xx, pool[i % R], out=yy)
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_run": args.counter_run, "launches": args.steps}), flush=True)
+        return
     bytes_up = algorithmic_bytes(6144, 7168, 2, 512, 1)
     bytes_dn = algorithmic_bytes(7168, 3072, 2, 512, 1)
 

@@ -134,7 +134,12 @@ int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
  * (fp32 out, layout [T][topk][N]). Ids outside [0, E) produce zero rows and are
  * counted; the count is left in the first 4 bytes of the workspace (int32).
  * Grouping by expert happens on the device (no host synchronisation); each
- * touched expert's weights are read once per launch. */
+ * touched expert's codes are read from HBM once per launch (an expert picked by
+ * more than two tokens takes one pass per one or two of them, the later passes
+ * reading its codes from cache). Requires K <= 2^28 and the per-wave activation
+ * slice to fit in LDS (CUBIC_ERR_SHAPE otherwise). x_bf16 [T][K] is read directly.
+ * The workspace size depends on T, topk and E only (K is accepted and ignored):
+ * a header, one 32-byte record per expert and the pair ids grouped by expert. */
 size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K);
 int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
                            const int32_t* topk_ids, int topk,
