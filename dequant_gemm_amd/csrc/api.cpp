@@ -185,6 +185,8 @@ CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
   if ((M + 127) / 128 > 65535) return CUBIC_ERR_SHAPE;
   if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, static_cast<hipStream_t>(stream)));
   TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xq, x_scale, y};
+  if (prefill_a8_supported(M, w->N, w->K, w->bits, w->group))
+    return hip_status(launch_prefill_a8(p, w->bits, static_cast<hipStream_t>(stream)));
   return hip_status(launch_tiled_a8(p, w->bits, static_cast<hipStream_t>(stream)));
 }
 

@@ -82,13 +82,34 @@ struct DecodeTable {
   static constexpr float kLevelUnit = 1.0f;
   __host__ __device__ static int slot_to_code(int slot) { return slot; }
   __host__ __device__ static int code_to_slot(int c) { return c; }
-  // tab: this lane's row table (2^B fp16 entries)
+  // tab: this lane's row table (2^B fp16 entries), aligned to its own size, so
+  // the byte address of entry f is tab | (f << 1): two ALU ops per code (shift,
+  // and-or). The two entries of a pair load straight into the low and high
+  // halves of r[p] (ds_read_u16_d16 / _d16_hi).
   __device__ static void decode(const uint32_t* w, const uint16_t* tab, uint32_t* r) {
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+    typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab));
+    constexpr uint32_t kMask2 = ((1u << BITS) - 1u) << 1;
+    auto addr = [&](int i) {
+      const int bit = i * BITS;
+      const int d = bit >> 5, off = bit & 31;
+      uint32_t v;
+      if (off == 0) {
+        v = w[d] << 1;
+      } else if (off + BITS <= 32) {
+        v = w[d] >> (off - 1);
+      } else {
+        v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 1);
+      }
+      return (v & kMask2) | base;
+    };
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
-      const uint32_t lo = tab[chunk_field<BITS>(w, 2 * p)];
-      const uint32_t hi = tab[chunk_field<BITS>(w, 2 * p + 1)];
-      r[p] = lo | (hi << 16);
+      u16x2v h;
+      h.x = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(addr(2 * p)));
+      h.y = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(addr(2 * p + 1)));
+      r[p] = __builtin_bit_cast(uint32_t, h);
     }
   }
 };
@@ -98,6 +119,22 @@ struct DecodeTable {
 __device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
   const uint32_t u = __float_as_uint(v);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The same level in fp32, for the per-group tables of the products: with
+// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^10 for B <= 4),
+// a X and b Y are exact fp32 products of fp16 values, so
+// Q = j^3 + a X + b Y rounds twice in fp32, then once more by 1/K^3, before the
+// fp16 rounding: a few fp32 ulps, far inside the products' tolerance.
+__device__ __forceinline__ uint16_t table_entry_f32(float a, float b, uint32_t v, int bits) {
+  const int k = sign_extend(v, bits);
+  const int j = k < 0 ? -k : k;
+  const int km = kmax_of(bits);
+  const float X = static_cast<float>(j * km * km - j * j * j);
+  const float Y = static_cast<float>(j * j * km - j * j * j);
+  const float q = fmaf(a, X, fmaf(b, Y, static_cast<float>(j * j * j))) *
+                  (1.0f / static_cast<float>(km * km * km));
+  return f16_bits(k < 0 ? -q : q);
 }
 
 __device__ __forceinline__ uint16_t table_entry(double a, double b, uint32_t v, int bits) {

@@ -28,7 +28,7 @@ constexpr int kInkWaves = 4;   // waves per workgroup of the single-kernel (in-k
 // W: waves per workgroup, each streaming 1/W of the K range of the 16 rows.
 template <class Dec, bool INK, int SPL, int P, bool ALLIN, int MT, int W>
 __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
+  extern __shared__ __align__(1024) unsigned char smem[];   // table rows rely on this alignment
   constexpr int B = Dec::kBits;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

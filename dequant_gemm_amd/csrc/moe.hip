@@ -173,7 +173,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
 template <class Dec, int SPL, int P, bool ALLIN, int MT>
 __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
   static_assert(MT == 1 || MT == 2, "one or two activation rows per pass");
-  extern __shared__ __align__(16) unsigned char smem[];
+  extern __shared__ __align__(1024) unsigned char smem[];   // table rows rely on this alignment
   constexpr int B = Dec::kBits;
   constexpr int XB = 2;                         // 16-element blocks per lane and row issued ahead
   const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
                                                          const int32_t* __restrict__ sorted,
                                                          float* __restrict__ y) {
   static_assert(MT == 1 || MT == 2, "one or two activation rows per pass");
-  extern __shared__ __align__(16) unsigned char smem[];
+  extern __shared__ __align__(1024) unsigned char smem[];   // table rows rely on this alignment
   constexpr int B = Dec::kBits;
   constexpr int DW = B * SPL;
   constexpr int XB = 2;
