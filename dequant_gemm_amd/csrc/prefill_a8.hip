@@ -4,42 +4,56 @@
 // The CubicQuant article (section "一份 checkpoint，同时服务 A16 与 Dynamic A8")
 // runs the A8 path as: per-token INT8 activations, an INT8 carrier of each
 // weight level, an integer dot product per group and an fp32 group scale.
-// Here one 256-thread workgroup owns a 256 (weight rows n) x 128 (activation
+// Here one 256-thread workgroup owns a 128 (weight rows n) x 256 (activation
 // rows m) output tile and walks K in steps of 128:
-//  - wave w owns weight rows 64 w .. 64 w + 63 against all 128 activation rows
-//    (2 x 4 blocks of 32 x 32): int32 accumulators for the open group and fp32
-//    accumulators that take acc_i32 * fp32(s / 127) at every group end;
-//  - each lane decodes its own weight fragments in registers: the int8 carriers
-//    of a row's 2^B field values sit in two registers, and one v_perm turns four
+//  - wave w owns weight rows 32 w .. 32 w + 31 against all 256 activation rows
+//    (8 blocks of 32 x 32): int32 accumulators for the open group and fp32
+//    accumulators that take acc_i32 * fp32(s / 127) at every group end. Each
+//    decoded weight fragment feeds 8 MFMAs;
+//  - each lane decodes its row's codes in registers: the int8 carriers of the
+//    row's 2^B field values sit in two registers, and one v_perm turns four
 //    codes (their fields spread into a byte selector) into four carriers;
-//  - the int8 activation tile goes from global memory straight into a 4-stage
-//    LDS ring (buffer_load ... lds), three steps ahead, in an XOR-swizzled
-//    layout that keeps the 16-byte fragment reads free of bank conflicts;
-//  - within a step, lane half h takes codes 64 h .. 64 h + 63: codes
+//  - every load of the step loop goes from global memory straight into a
+//    4-stage LDS ring (buffer_load ... lds), three steps ahead: the int8
+//    activation tile (XOR-swizzled so that the 16-byte fragment reads are free
+//    of bank conflicts), the tile's code words and its group parameters. With
+//    no vector load writing a register, the loop's only memory wait is the one
+//    before each step's barrier;
+//  - within a step, lane half h takes codes 64 h .. 64 h + 63 of its row: codes
 //    64 h + 16 ks .. + 15 feed MFMA sub-step ks (0..3), and the activation
 //    fragments follow the same K order.
 // Carriers are exact: clamp(rne(127 q), +-127) decided with integer arithmetic
-// (carrier_level); each lane computes one of its two rows' tables and the pair
-// is exchanged across the wave halves (permlane32_swap).
+// (carrier_level), once per row and group in each lane of the row.
 #include "common.h"
 #include "launch.h"
 
 namespace cubic {
 namespace {
 
-constexpr int A8N = 256;             // weight rows per tile
-constexpr int A8M = 128;             // activation rows per tile
+constexpr int A8N = 128;             // weight rows per tile
+constexpr int A8M = 256;             // activation rows per tile
 constexpr int A8K = 128;             // K per step
 constexpr int kA8Threads = 256;
 constexpr int kA8Stages = 4;
-constexpr size_t kA8StageBytes = static_cast<size_t>(A8M) * A8K;     // int8
-constexpr size_t kA8Lds = kA8Stages * kA8StageBytes;
 constexpr uint32_t kA8RsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+// Stage layout: activations [A8M][A8K] int8, then the code words of the tile's
+// A8N rows (A8K B / 8 bytes each, row-major), then the group parameters (per
+// wave 512 bytes: 64 scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
+constexpr size_t kA8XBytes = static_cast<size_t>(A8M) * A8K;
+constexpr size_t a8_code_bytes(int B) { return static_cast<size_t>(A8N) * A8K * B / 8; }
+constexpr size_t kA8ParamBytes = 4 * 512;
+constexpr size_t a8_stage_bytes(int B) { return kA8XBytes + a8_code_bytes(B) + kA8ParamBytes; }
+constexpr size_t a8_lds_bytes(int B) { return kA8Stages * a8_stage_bytes(B); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t a8_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
                                            static_cast<int>(bytes), static_cast<int>(kA8RsrcWord3));
 }
+
+// s_waitcnt immediate: vmcnt(n) (n < 64: low 4 bits in [3:0], high 2 bits in
+// [15:14]), expcnt not waited for, lgkmcnt(0).
+constexpr int a8_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
 // Byte selector for four consecutive B-bit fields in the low 4B bits of v
 // (field i -> byte i), by two multiplies whose terms never overlap.
@@ -90,28 +104,6 @@ __device__ __forceinline__ void carrier_table(uint32_t ab, uint32_t& t0, uint32_
   }
 }
 
-// s_waitcnt immediate: vmcnt(n) (n < 64: low 4 bits in [3:0], high 2 bits in
-// [15:14]), expcnt not waited for, lgkmcnt(0).
-constexpr int a8_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
-
-// A lane's 64 codes of one row and step: 2B dwords, loaded as 16-byte (2-bit)
-// or two 12-byte (3-bit) pieces.
-constexpr int a8_code_loads(int B) { return B == 2 ? 1 : 2; }
-
-template <int B>
-__device__ __forceinline__ void load_codes64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
-  if constexpr (B == 2) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else {
-    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-    const u32x3 v0 = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
-    const u32x3 v1 = __builtin_amdgcn_raw_buffer_load_b96(r, off + 12, 0, 0);
-    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z;
-    w[3] = v1.x; w[4] = v1.y; w[5] = v1.z;
-  }
-}
-
 // Swizzled position of 16-byte chunk q (0..7) of activation row r (128 bytes)
 // in a stage: any 16 consecutive rows read at one chunk hit 16 distinct
 // 16-byte bank groups (row parity and the XOR of the low three row bits and
@@ -122,8 +114,11 @@ __device__ __forceinline__ int a8_slot(int r, int q) {
 
 template <int B>
 __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int8_t* As = reinterpret_cast<int8_t*>(smem);              // [4][A8M * A8K] swizzled
+  extern __shared__ __align__(16) unsigned char smem[];       // kA8Stages stages
+  constexpr int DPR = A8K * B / 32;             // code dwords per row and step
+  constexpr size_t kStage = a8_stage_bytes(B);
+  constexpr size_t kCodeOff = kA8XBytes;
+  constexpr size_t kParamOff = kA8XBytes + a8_code_bytes(B);
 
   const int tiles_n = static_cast<int>((p.N + A8N - 1) / A8N);
   const int ntiles = tiles_n * static_cast<int>((p.M + A8M - 1) / A8M);
@@ -140,169 +135,146 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   const int gpr = static_cast<int>(p.K / p.group);
   const int nsteps = static_cast<int>(p.K / A8K);
   const int spg = p.group / A8K;
-
-  // ---- this lane's weight rows n0 + 64 wave + 32 i + c (i = 0, 1) ----
   const uint32_t row_bytes = static_cast<uint32_t>(p.K * B / 8);
-  const __amdgpu_buffer_rsrc_t crs = a8_rsrc(p.codes, static_cast<uint32_t>(p.N) * row_bytes);
-  uint32_t coff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t n = n0 + 64 * wave + 32 * i + c;
-    coff[i] = static_cast<uint32_t>(n) * row_bytes + static_cast<uint32_t>(h * 8 * B);
-  }
-  // group parameters: this lane fetches those of its row i = h (the other half
-  // of the wave fetches row 1 - h) and the two are exchanged after the decode
-  const int64_t nown = n0 + 64 * wave + 32 * h + c;
-  const int64_t nc = nown < p.N ? nown : p.N - 1;
-  const float* srow = p.scales + nc * gpr;
-  const uint32_t* abrow = reinterpret_cast<const uint32_t*>(p.shapes) + nc * gpr;
+  const int64_t nrow = n0 + 32 * wave + c;      // this lane's weight row
 
-  // ---- activation stages: global -> LDS ----
-  // Wave w fills slots 256 w + 64 i + lane (i = 0..3) of a stage.
+  // ---- the step's loads: global -> LDS stage ----
+  // activations: wave w fills slots 512 w + 64 i + lane (i = 0..7), 16 bytes each
   const __amdgpu_buffer_rsrc_t xrs = a8_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K));
-  uint32_t aoff[4];
+  uint32_t aoff[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = 256 * wave + 64 * i + lane;
+  for (int i = 0; i < 8; ++i) {
+    const int slot = 512 * wave + 64 * i + lane;
     const int r = slot >> 3;
     const int q = (slot & 7) ^ (r & 7) ^ ((r >> 3) & 1);     // inverse of a8_slot
     aoff[i] = static_cast<uint32_t>((m0 + r) * p.K + 16 * q);  // rows past M read 0
   }
-  auto issue_a = [&](int s, int stage) {
-    int8_t* dst = As + stage * kA8StageBytes + wave * 4096;
+  // code words: dword slots of the tile's rows (row-major); wave w fills slots
+  // 64 (NC w + i) + lane (i < NC); rows past N read 0
+  constexpr int NC = A8N * DPR / 256;           // code loads per wave and step
+  const __amdgpu_buffer_rsrc_t crs = a8_rsrc(p.codes, static_cast<uint32_t>(p.N) * row_bytes);
+  uint32_t coff[NC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst + i * 1024, 16,
+  for (int i = 0; i < NC; ++i) {
+    const int slot = 64 * (NC * wave + i) + lane;
+    const int r = slot / DPR, d = slot % DPR;
+    coff[i] = static_cast<uint32_t>(n0 + r) * row_bytes + 4u * static_cast<uint32_t>(d);
+  }
+  // group parameters of the wave's 32 rows (lanes 32..63 repeat them)
+  const int64_t pc = nrow < p.N ? nrow : p.N - 1;
+  const __amdgpu_buffer_rsrc_t srs = a8_rsrc(p.scales, static_cast<uint32_t>(p.N * gpr * 4));
+  const __amdgpu_buffer_rsrc_t brs = a8_rsrc(p.shapes, static_cast<uint32_t>(p.N * gpr * 4));
+  const uint32_t poff = static_cast<uint32_t>(pc * gpr * 4);
+  constexpr int NV = 8 + NC + 2;                // loads per wave and step
+  auto issue_step = [&](int s, int stage) {
+    unsigned char* st = smem + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, st + wave * 8192 + i * 1024, 16,
                                                aoff[i] + static_cast<uint32_t>(s) * A8K, 0, 0, 0);
-  };
-
-  // ---- NV vector loads per step, in this order: 4 activation loads (to LDS)
-  // for step s + 3, then the code words of both rows and the 2 group
-  // parameters for step s + 2 (codes run one step behind the activations, so
-  // three code slots are live instead of four) ----
-  constexpr int CW = 2 * B;                     // code dwords per row and step
-  constexpr int NV = 4 + 2 * a8_code_loads(B) + 2;
-  uint32_t cw[4][2][CW];
-  float gs[4];
-  uint32_t gab[4];
-  auto issue_codes = [&](int sc, int par) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      load_codes64<B>(crs, coff[i] + static_cast<uint32_t>(sc) * (A8K * B / 8), cw[par][i]);
-    int g = sc / spg;
+    for (int i = 0; i < NC; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * (NC * wave + i), 4,
+                                               coff[i] + static_cast<uint32_t>(s) * (4 * DPR), 0, 0, 0);
+    int g = s / spg;
     g = g < gpr ? g : gpr - 1;
-    gs[par] = srow[g];
-    gab[par] = abrow[g];
-  };
-  auto issue_step = [&](int sa, int pa, int sc, int pc) {
-    issue_a(sa, pa);
-    __builtin_amdgcn_sched_barrier(0);          // the activation loads go first
-    issue_codes(sc, pc);
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, st + kParamOff + 512 * wave, 4,
+                                             poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, st + kParamOff + 512 * wave + 256, 4,
+                                             poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
   };
 
-  i32x16 acci[2][4];                           // the open group's sums (set by its first step)
-  f32x16 accf[2][4];
+  i32x16 acci[8];                              // the open group's sums (set by its first step)
+  f32x16 accf[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        acci[i][j][e] = 0;
-        accf[i][j][e] = 0.0f;
-      }
+    for (int e = 0; e < 16; ++e) {
+      acci[j][e] = 0;
+      accf[j][e] = 0.0f;
+    }
 
-  // prologue: activations of steps 0..2 and codes of steps 0..1; after stage
-  // 2 a filler (codes of step 0 into the slot of step 3, overwritten later)
-  // keeps NV - 4 code-side loads behind every stage, so the count below holds
-  // from the first step on
-  issue_step(0, 0, 0, 0);
-  issue_step(1, 1, 1, 1);
-  issue_step(2, 2, 0, 3);
+  issue_step(0, 0);
+  issue_step(1, 1);
+  issue_step(2, 2);
 
-  uint32_t t0[2] = {0u, 0u}, t1[2] = {0u, 0u};
-  float sc[2] = {0.0f, 0.0f};
+  uint32_t t0 = 0u, t1 = 0u;
+  float sc = 0.0f;
   int mg = 0;                                   // s % spg
 
   auto step = [&](int s, auto ph_c) {
     constexpr int ph = decltype(ph_c)::value;  // s % 4
     constexpr int ph3 = (ph + 3) % 4;
-    // Stage s is complete once only the loads issued after it remain: the code
-    // and parameter loads that follow it and the NV loads of each of the next
-    // two stages. The bare barrier then publishes every wave's part of it, and
-    // every wave has finished reading stage s - 1, which the loads of step s + 3
-    // overwrite.
-    static_assert(3 * NV - 4 < 64, "vmcnt holds at most 63");
-    __builtin_amdgcn_s_waitcnt(a8_wait_vm(3 * NV - 4));
+    // Stage s is complete once only the loads of the next two stages remain.
+    // The bare barrier then publishes every wave's part of it, and every wave
+    // has finished reading stage s - 1, which the loads of step s + 3 overwrite.
+    static_assert(2 * NV < 64, "vmcnt holds at most 63");
+    __builtin_amdgcn_s_waitcnt(a8_wait_vm(2 * NV));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // past K: step 0 again into the free stage (never read), so the count holds
+    issue_step(s + 3 < nsteps ? s + 3 : 0, ph3);
+    const unsigned char* st = smem + ph * kStage;
+    uint32_t cw[2 * B];                         // this lane's 64 codes of the step
     {
-      // past K: step 0 again into the free stage / slot (never read), so the
-      // counts still hold
-      const int sa = s + 3 < nsteps ? s + 3 : 0;
-      const int sc = s + 2 < nsteps ? s + 2 : 0;
-      issue_step(sa, ph3, sc, (ph + 2) % 4);
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(st + kCodeOff) + DPR * (32 * wave + c) + 2 * B * h;
+#pragma unroll
+      for (int d = 0; d < 2 * B; ++d) cw[d] = src[d];
     }
-    if (mg == 0) {
-      // new group: carriers and scale of this lane's own row, then the pair
-      uint32_t a0, a1;
-      carrier_table<B>(gab[ph], a0, a1);
-      const float so = __fdiv_rn(gs[ph], 127.0f);
-      const auto x0 = __builtin_amdgcn_permlane32_swap(a0, a0, false, false);
-      const auto x1 = __builtin_amdgcn_permlane32_swap(a1, a1, false, false);
-      const auto xs = __builtin_amdgcn_permlane32_swap(__float_as_uint(so), __float_as_uint(so),
-                                                       false, false);
-      t0[0] = x0[0]; t0[1] = x0[1];
-      t1[0] = x1[0]; t1[1] = x1[1];
-      sc[0] = __uint_as_float(xs[0]);
-      sc[1] = __uint_as_float(xs[1]);
-    }
-    const int8_t* Ab = As + ph * kA8StageBytes;
     const bool fresh = mg == 0;                // the group's first step: int32 sums start at 0
+    if (fresh) {
+      // new group: the row's carriers and scale
+      const uint32_t* par = reinterpret_cast<const uint32_t*>(st + kParamOff + 512 * wave);
+      carrier_table<B>(par[64 + c], t0, t1);
+      sc = __fdiv_rn(__uint_as_float(par[c]), 127.0f);
+    }
+    const int8_t* Ab = reinterpret_cast<const int8_t*>(st);
+    // Activation fragments roll through one set of registers: right after MFMA
+    // j of sub-step ks consumes fragment j, fragment j of sub-step ks + 1 is
+    // read into it. The weight fragment of sub-step ks + 1 is decoded under
+    // sub-step ks's MFMAs.
+    i32x4 fa[8];
+    auto read_a = [&](int ks, int j) {
+      return *reinterpret_cast<const i32x4*>(Ab + 16 * a8_slot(32 * j + c, 4 * h + ks));
+    };
+    auto decode = [&](int ks) {
+      uint32_t o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        o[u] = __builtin_amdgcn_perm(t1, t0, a8_selector<B>(a8_quad<B>(cw, 4 * ks + u)));
+      return i32x4{static_cast<int>(o[0]), static_cast<int>(o[1]), static_cast<int>(o[2]),
+                   static_cast<int>(o[3])};
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fa[j] = read_a(0, j);
+    i32x4 fb = decode(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      i32x4 fa[4], fb[2];
+      const i32x4 fbn = ks < 3 ? decode(ks + 1) : fb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 32 * j + c;
-        fa[j] = *reinterpret_cast<const i32x4*>(Ab + 16 * a8_slot(r, 4 * h + ks));
+      for (int j = 0; j < 8; ++j) {
+        if (ks == 0 && fresh) {
+          acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb, i32x16{}, 0, 0, 0);
+        } else {
+          acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb, acci[j], 0, 0, 0);
+        }
+        if (ks < 3) fa[j] = read_a(ks + 1, j);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint32_t o[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[u] = __builtin_amdgcn_perm(t1[i], t0[i], a8_selector<B>(a8_quad<B>(cw[ph][i], 4 * ks + u)));
-        fb[i] = i32x4{static_cast<int>(o[0]), static_cast<int>(o[1]), static_cast<int>(o[2]),
-                      static_cast<int>(o[3])};
-      }
-      if (ks == 0 && fresh) {
-        const i32x16 zero = {};
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb[i], zero, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acci[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb[i], acci[i][j], 0, 0, 0);
-      }
+      fb = fbn;
+      __builtin_amdgcn_sched_barrier(0);
     }
     mg = mg + 1 == spg ? 0 : mg + 1;
-    if (mg == 0 || s + 1 == nsteps) {
+    if (mg == 0) {
       // group end: fp32 group scale (exact int32 dot, |I| < 2^24)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 8; ++j) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            accf[i][j][e] = fmaf(static_cast<float>(acci[i][j][e]), sc[i], accf[i][j][e]);
+        for (int e = 0; e < 16; ++e)
+          accf[j][e] = fmaf(static_cast<float>(acci[j][e]), sc, accf[j][e]);
+        __builtin_amdgcn_sched_barrier(0);     // one block at a time (few temporaries)
+      }
     }
   };
   int s = 0;
@@ -316,20 +288,23 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
   if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
   __builtin_amdgcn_s_waitcnt(0);               // loads past K target stages nobody reads
+  __syncthreads();
 
-  // ---- epilogue: D row m = 8 (e / 4) + 4 h + e % 4 of block j, column n = c of block i ----
+  // ---- epilogue: the tile's activation scales through LDS (one load per
+  // thread), then D row m = 8 (e / 4) + 4 h + e % 4 of block j, column n = c ----
+  float* sxs = reinterpret_cast<float*>(smem);
+  {
+    const int64_t m = m0 + tid;
+    sxs[tid] = m < p.M ? p.xs[m] : 0.0f;
+  }
+  __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 8; ++j) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t m = m0 + 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (m >= p.M) continue;
-      const float sx = p.xs[m];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t n = n0 + 64 * wave + 32 * i + c;
-        if (n < p.N) p.y[m * p.N + n] = accf[i][j][e] * sx;
-      }
+      const int ml = 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int64_t m = m0 + ml;
+      if (m < p.M && nrow < p.N) p.y[m * p.N + nrow] = accf[j][e] * sxs[ml];
     }
   }
 }
@@ -337,12 +312,14 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
 }  // namespace
 
 // 2- and 3-bit codes, groups a multiple of 128 up to 1024 (exact int32 group
-// dots), and byte sizes of the activation and code buffers below 2^32.
+// dots), and byte sizes of the activation, code and parameter buffers (with a
+// tile's overhang) below 2^32.
 bool prefill_a8_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   if (bits != 2 && bits != 3) return false;
   if (group % A8K != 0 || group > 1024 || K % A8K != 0) return false;
-  if (M * K >= (int64_t{1} << 32)) return false;
-  if (N * K * bits / 8 >= (int64_t{1} << 32)) return false;
+  if ((M + A8M) * K >= (int64_t{1} << 32)) return false;
+  if ((N + A8N) * K * bits / 8 >= (int64_t{1} << 32)) return false;
+  if (N * (K / group) * 4 >= (int64_t{1} << 32)) return false;
   const int64_t tiles = ((M + A8M - 1) / A8M) * ((N + A8N - 1) / A8N);
   return tiles <= INT32_MAX;
 }
@@ -350,12 +327,14 @@ bool prefill_a8_supported(int64_t M, int64_t N, int64_t K, int bits, int group) 
 template <int B>
 static hipError_t launch_prefill_a8_b(const TiledParams& p, hipStream_t st) {
   auto kern = k_prefill_a8<B>;
+  constexpr size_t lds = a8_lds_bytes(B);
+  static_assert(lds <= 160 * 1024, "one compute unit's LDS");
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(kA8Lds));
+                                           static_cast<int>(lds));
   if (e != hipSuccess) return e;
   const int64_t tiles = ((p.M + A8M - 1) / A8M) * ((p.N + A8N - 1) / A8N);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kA8Threads), kA8Lds, st, p);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kA8Threads), lds, st, p);
   return hipGetLastError();
 }
 
