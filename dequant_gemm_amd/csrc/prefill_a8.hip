@@ -7,23 +7,30 @@
 // Here one 256-thread workgroup owns a 128 (weight rows n) x 256 (activation
 // rows m) output tile and walks K in steps of 128:
 //  - wave w owns weight rows 32 w .. 32 w + 31 against all 256 activation rows
-//    (8 blocks of 32 x 32): int32 accumulators for the open group and fp32
-//    accumulators that take acc_i32 * fp32(s / 127) at every group end. Each
-//    decoded weight fragment feeds 8 MFMAs;
+//    (8 blocks of 32 x 32): int32 sums for the open group and fp32 sums that
+//    take int32 sum * fp32(s / 127) once the group is complete. Each decoded
+//    weight fragment feeds 8 MFMAs;
 //  - each lane decodes its row's codes in registers: the int8 carriers of the
 //    row's 2^B field values sit in two registers, and one v_perm turns four
 //    codes (their fields spread into a byte selector) into four carriers;
+//  - a group's int32 sums are scaled into the fp32 sums in the first sub-step
+//    of the next group, block by block: block j is read out right before the
+//    MFMA that restarts it from zero, and its fp32 update runs beside the
+//    following MFMAs;
 //  - every load of the step loop goes from global memory straight into a
-//    4-stage LDS ring (buffer_load ... lds), three steps ahead: the int8
-//    activation tile (XOR-swizzled so that the 16-byte fragment reads are free
-//    of bank conflicts), the tile's code words and its group parameters. With
-//    no vector load writing a register, the loop's only memory wait is the one
-//    before each step's barrier;
+//    4-stage LDS ring (buffer_load ... lds): the int8 activation tile
+//    (XOR-swizzled so that the 16-byte fragment reads are free of bank
+//    conflicts), the tile's code words and the group parameters of the next
+//    group. The one barrier of step s sits after three quarters of its MFMAs:
+//    it waits until stage s + 1 has landed, so the rest of step s reads and
+//    decodes the first fragments of step s + 1 and refills stage s for step
+//    s + 4;
 //  - within a step, lane half h takes codes 64 h .. 64 h + 63 of its row: codes
 //    64 h + 16 ks .. + 15 feed MFMA sub-step ks (0..3), and the activation
 //    fragments follow the same K order.
-// Carriers are exact: clamp(rne(127 q), +-127) decided with integer arithmetic
-// (carrier_level), once per row and group in each lane of the row.
+// Every MFMA slot of a sub-step is followed by a fixed share of the other work
+// (sched_barrier keeps the compiler from regrouping it), so the VALU work runs
+// in the shadow of the MFMAs.
 #include "common.h"
 #include "launch.h"
 
@@ -38,8 +45,8 @@ constexpr int kA8Stages = 4;
 constexpr uint32_t kA8RsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
 // Stage layout: activations [A8M][A8K] int8, then the code words of the tile's
-// A8N rows (A8K B / 8 bytes each, row-major), then the group parameters (per
-// wave 512 bytes: 64 scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
+// A8N rows (A8K B / 8 bytes each, row-major), then group parameters (per wave
+// 512 bytes: 64 scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
 constexpr size_t kA8XBytes = static_cast<size_t>(A8M) * A8K;
 constexpr size_t a8_code_bytes(int B) { return static_cast<size_t>(A8N) * A8K * B / 8; }
 constexpr size_t kA8ParamBytes = 4 * 512;
@@ -55,52 +62,131 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t a8_rsrc(const void* p, uint32_
 // [15:14]), expcnt not waited for, lgkmcnt(0).
 constexpr int a8_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
-// Byte selector for four consecutive B-bit fields in the low 4B bits of v
-// (field i -> byte i), by two multiplies whose terms never overlap.
-template <int B>
-__device__ __forceinline__ uint32_t a8_selector(uint32_t v) {
-  constexpr uint32_t fm = (1u << B) - 1u;
-  constexpr uint32_t me = fm | (fm << (2 * B));
-  constexpr uint32_t mo = (fm << B) | (fm << (3 * B));
-  const uint32_t e = (v & me) * (1u + (1u << (16 - 2 * B)));
-  const uint32_t o = (v & mo) * ((1u << (8 - B)) + (1u << (24 - 3 * B)));
-  return ((e & 0x00FF00FFu) | (o & 0xFF00FF00u)) & (fm * 0x01010101u);
+// Empty asm that takes and returns a register: arithmetic written in one MFMA
+// slot cannot be moved past it into another.
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
+// Orders 16 values before a use of `a`: the MFMA that takes `a` can only issue
+// once the 16 values exist (the read-out of a block's sums before the MFMA
+// that restarts them).
+__device__ __forceinline__ void hold16(float* f, i32x4& a) {
+  asm volatile(""
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                 "+v"(f[6]), "+v"(f[7]), "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]),
+                 "+v"(f[12]), "+v"(f[13]), "+v"(f[14]), "+v"(f[15]), "+v"(a));
 }
 
-// Fields 4q .. 4q + 3 of a lane's 64 codes w[2B].
+// Carrier of level j (|code| = j): clamp(rne(127 q(j / K)), -127, 127), K = Kmax.
+// With S = K^3 q(j / K) = a j K^2 + b j^2 K + (1 - a - b) j^3, exact rounding
+// of 127 S / K^3 is decided in fp64:
+//  - S is exact: a and b are fp16 (multiples of 2^-24 below 2^16), j <= 4 and
+//    K <= 3, so every partial sum is a multiple of 2^-24 below 2^24;
+//  - X = S * fl(127 / K^3) is within 2^-44 of the true quotient when |X| < 128;
+//  - n0 = rint(X) is then the rounded quotient or one off it, and the residual
+//    D = 127 S - K^3 n0 (a multiple of 2^-24 below 2^6) comes out of one fma
+//    exactly, so comparing D with K^3 / 2 settles ties (to even) and the
+//    off-by-one case.
+template <int B>
+__device__ __forceinline__ int a8_carrier(double a, double b, double c, int j) {
+  constexpr int K = kmax_of(B);
+  constexpr double K3 = static_cast<double>(K * K * K);
+  const double S = fma(a, static_cast<double>(j * K * K),
+                       fma(b, static_cast<double>(j * j * K), c * static_cast<double>(j * j * j)));
+  const double X = S * (127.0 / K3);
+  if (X >= 127.75) return 127;                 // rounds to 128 or more: clamped
+  if (X <= -127.75) return -127;
+  const double n0 = rint(X);
+  const double D = fma(127.0, S, -K3 * n0);
+  const bool odd = (static_cast<int>(n0) & 1) != 0;
+  int n = static_cast<int>(n0);
+  n += (D > 0.5 * K3 || (D == 0.5 * K3 && odd)) ? 1 : 0;
+  n -= (D < -0.5 * K3 || (D == -0.5 * K3 && odd)) ? 1 : 0;
+  return n > 127 ? 127 : (n < -127 ? -127 : n);
+}
+
+// int8 carriers of field values 0..2^B-1 (two's complement codes) of one row
+// and group, as bytes of t0 (fields 0..3) and t1 (fields 4..7), built in four
+// pieces so that the work can be spread between MFMAs.
+struct CarrierBuild {
+  int c1, c2, c4;
+};
+
+template <int B>
+__device__ __forceinline__ void carrier_piece(CarrierBuild& cb, int piece, uint32_t ab, uint32_t sbits,
+                                              uint32_t& t0, uint32_t& t1, float& sc) {
+  static_assert(B == 2 || B == 3, "at most 8 carriers per table");
+  auto byte = [](int v) { return static_cast<uint32_t>(v) & 0xffu; };
+  const double a = f16_bits_to_f64(static_cast<uint16_t>(ab & 0xffffu));
+  const double b = f16_bits_to_f64(static_cast<uint16_t>(ab >> 16));
+  const double c = (1.0 - a) - b;               // exact: both are fp16 values
+  if (piece == 0) {
+    cb.c2 = a8_carrier<B>(a, b, c, 2);
+    pin(cb.c2);
+  } else if (piece == 1) {
+    if constexpr (B == 3) {
+      cb.c1 = a8_carrier<B>(a, b, c, 1);
+      pin(cb.c1);
+    }
+  } else if (piece == 2) {
+    if constexpr (B == 3) {
+      cb.c4 = a8_carrier<B>(a, b, c, 4);
+      pin(cb.c4);
+    }
+  } else {
+    sc = __fdiv_rn(__uint_as_float(sbits), 127.0f);
+    if constexpr (B == 3) {
+      // fields 0..7 -> codes 0, 1, 2, 3, -4, -3, -2, -1 (code 3 = Kmax: q = 1 -> 127)
+      t0 = byte(0) | (byte(cb.c1) << 8) | (byte(cb.c2) << 16) | (byte(127) << 24);
+      t1 = byte(-cb.c4) | (byte(-127) << 8) | (byte(-cb.c2) << 16) | (byte(-cb.c1) << 24);
+    } else {
+      // fields 0..3 -> codes 0, 1, -2, -1 (code 1 = Kmax: 127)
+      t0 = byte(0) | (byte(127) << 8) | (byte(-cb.c2) << 16) | (byte(-127) << 24);
+      t1 = 0u;
+    }
+    pin(t0);
+    pin(t1);
+    pin(sc);
+  }
+}
+
+// Fields 4q .. 4q + 3 of a lane's 64 codes w[2B] at bits 0 .. 4B - 1 (higher
+// bits are garbage; the selector masks ignore them).
 template <int B>
 __device__ __forceinline__ uint32_t a8_quad(const uint32_t* w, int q) {
   const int bit = 4 * B * q;
   const int d = bit >> 5, off = bit & 31;
-  uint32_t v;
-  if (off + 4 * B <= 32) {
-    v = w[d] >> off;
-  } else {
-    v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off);
-  }
-  return v & ((1u << (4 * B)) - 1u);
+  if (off == 0) return w[d];
+  if (off + 4 * B <= 32) return w[d] >> off;
+  return __builtin_amdgcn_alignbit(w[d + 1], w[d], off);
 }
 
-// int8 carriers of field values 0..2^B-1 (two's complement codes) of one row
-// and group, bytes of t0 (fields 0..3) and t1 (fields 4..7).
+// One code quad (four codes -> one dword of int8 carriers) in two pieces: the
+// fields of codes 0 and 2 (mask me) and of codes 1 and 3 (mask mo) are moved
+// into bytes 0..3 by two multiplies whose terms never overlap, then v_perm
+// looks the four field values up in the carrier table.
+struct A8Quad {
+  uint32_t e, o;
+};
+
 template <int B>
-__device__ __forceinline__ void carrier_table(uint32_t ab, uint32_t& t0, uint32_t& t1) {
-  static_assert(B == 2 || B == 3, "at most 8 carriers per table");
-  constexpr int K = kmax_of(B);
-  const double a = f16_bits_to_f64(static_cast<uint16_t>(ab & 0xffffu));
-  const double b = f16_bits_to_f64(static_cast<uint16_t>(ab >> 16));
-  auto byte = [](int v) { return static_cast<uint32_t>(v) & 0xffu; };
-  if constexpr (B == 3) {
-    // fields 0..7 -> codes 0, 1, 2, 3, -4, -3, -2, -1 (code 3 = Kmax: q = 1 -> 127)
-    const int c1 = carrier_level(a, b, 1, K), c2 = carrier_level(a, b, 2, K);
-    const int c4 = carrier_level(a, b, 4, K);
-    t0 = byte(0) | (byte(c1) << 8) | (byte(c2) << 16) | (byte(127) << 24);
-    t1 = byte(-c4) | (byte(-127) << 8) | (byte(-c2) << 16) | (byte(-c1) << 24);
+__device__ __forceinline__ void a8_quad_piece(A8Quad& qs, int piece, const uint32_t* w, int q,
+                                              uint32_t t0, uint32_t t1, uint32_t& out) {
+  constexpr uint32_t fm = (1u << B) - 1u;
+  constexpr uint32_t me = fm | (fm << (2 * B));
+  constexpr uint32_t mo = (fm << B) | (fm << (3 * B));
+  if (piece == 0) {
+    const uint32_t v = a8_quad<B>(w, q);
+    qs.e = v & me;
+    qs.o = v & mo;
+    pin(qs.e);
+    pin(qs.o);
   } else {
-    // fields 0..3 -> codes 0, 1, -2, -1 (code 1 = Kmax: 127)
-    const int c2 = carrier_level(a, b, 2, K);
-    t0 = byte(0) | (byte(127) << 8) | (byte(-c2) << 16) | (byte(-127) << 24);
-    t1 = 0u;
+    const uint32_t e = __umul24(qs.e, 1u + (1u << (16 - 2 * B)));     // fields < 2^12
+    const uint32_t o = __umul24(qs.o, (1u << (8 - B)) + (1u << (24 - 3 * B)));
+    const uint32_t sel = (e & (fm * 0x00010001u)) | (o & (fm * 0x01000100u));
+    out = __builtin_amdgcn_perm(t1, t0, sel);
+    pin(out);
   }
 }
 
@@ -112,7 +198,9 @@ __device__ __forceinline__ int a8_slot(int r, int q) {
   return r * 8 + (q ^ (r & 7) ^ ((r >> 3) & 1));
 }
 
-template <int B>
+// SPG: steps per group when it is 1 or 2 (then known for each of the four
+// unrolled steps), or 0 for any group length (decided at run time).
+template <int B, int SPG>
 __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   extern __shared__ __align__(16) unsigned char smem[];       // kA8Stages stages
   constexpr int DPR = A8K * B / 32;             // code dwords per row and step
@@ -134,20 +222,22 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   const int c = lane & 31, h = lane >> 5;
   const int gpr = static_cast<int>(p.K / p.group);
   const int nsteps = static_cast<int>(p.K / A8K);
-  const int spg = p.group / A8K;
+  const int spg = SPG != 0 ? SPG : p.group / A8K;
   const uint32_t row_bytes = static_cast<uint32_t>(p.K * B / 8);
   const int64_t nrow = n0 + 32 * wave + c;      // this lane's weight row
 
   // ---- the step's loads: global -> LDS stage ----
-  // activations: wave w fills slots 512 w + 64 i + lane (i = 0..7), 16 bytes each
+  // activations: wave w fills slots 512 w + 64 i + lane (i = 0..7), 16 bytes
+  // each: row r = 64 w + 8 i + lane / 8, chunk (lane % 8) ^ (r % 8) ^ (i % 2)
+  // (the inverse of a8_slot), so the offset is one of two per-lane bases (by
+  // the parity of i) plus 8 i K. Rows past M read 0.
   const __amdgpu_buffer_rsrc_t xrs = a8_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K));
-  uint32_t aoff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int slot = 512 * wave + 64 * i + lane;
-    const int r = slot >> 3;
-    const int q = (slot & 7) ^ (r & 7) ^ ((r >> 3) & 1);     // inverse of a8_slot
-    aoff[i] = static_cast<uint32_t>((m0 + r) * p.K + 16 * q);  // rows past M read 0
+  uint32_t abase[2];
+  {
+    const int64_t r = m0 + 64 * wave + (lane >> 3);
+    const int q = (lane & 7) ^ ((lane >> 3) & 7);
+    abase[0] = static_cast<uint32_t>(r * p.K + 16 * q);
+    abase[1] = static_cast<uint32_t>(r * p.K + 16 * (q ^ 1));
   }
   // code words: dword slots of the tile's rows (row-major); wave w fills slots
   // 64 (NC w + i) + lane (i < NC); rows past N read 0
@@ -166,116 +256,197 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   const __amdgpu_buffer_rsrc_t brs = a8_rsrc(p.shapes, static_cast<uint32_t>(p.N * gpr * 4));
   const uint32_t poff = static_cast<uint32_t>(pc * gpr * 4);
   constexpr int NV = 8 + NC + 2;                // loads per wave and step
-  auto issue_step = [&](int s, int stage) {
+  static_assert(NV <= 16, "two loads per MFMA slot of the refill sub-step");
+  static_assert(3 * NV < 64, "vmcnt holds at most 63");
+  // Load i (0 .. NV - 1) of step s into a stage. The parameter slots of step
+  // s hold the group after the one step s belongs to (read in that group's
+  // last step to prepare the next carriers). Past K, step 0 is loaded again
+  // into a stage nobody reads, so that the load count per step stays fixed.
+  auto issue_load = [&](int s, int stage, int i) {
     unsigned char* st = smem + stage * kStage;
+    const int sv = s < nsteps ? s : 0;
+    if (i < 8) {
+      const uint32_t ko = static_cast<uint32_t>(8 * i) * static_cast<uint32_t>(p.K) +
+                          static_cast<uint32_t>(sv) * A8K;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, st + wave * 8192 + i * 1024, 16, abase[i & 1] + ko,
+                                               0, 0, 0);
+    } else if (i < 8 + NC) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * (NC * wave + i - 8), 4,
+                                               coff[i - 8] + static_cast<uint32_t>(sv) * (4 * DPR),
+                                               0, 0, 0);
+    } else {
+      int g = sv / spg + 1;
+      g = g < gpr ? g : gpr - 1;
+      const bool ab = i == 8 + NC + 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ab ? brs : srs, st + kParamOff + 512 * wave + (ab ? 256 : 0),
+                                               4, poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
+    }
+  };
+  auto issue_step = [&](int s, int stage) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, st + wave * 8192 + i * 1024, 16,
-                                               aoff[i] + static_cast<uint32_t>(s) * A8K, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < NC; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * (NC * wave + i), 4,
-                                               coff[i] + static_cast<uint32_t>(s) * (4 * DPR), 0, 0, 0);
-    int g = s / spg;
-    g = g < gpr ? g : gpr - 1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, st + kParamOff + 512 * wave, 4,
-                                             poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, st + kParamOff + 512 * wave + 256, 4,
-                                             poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
+    for (int i = 0; i < NV; ++i) issue_load(s, stage, i);
   };
 
-  i32x16 acci[8];                              // the open group's sums (set by its first step)
+  i32x16 acc[8];                                // int32 sums of the open group
   f32x16 accf[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      acci[j][e] = 0;
+      acc[j][e] = 0;
       accf[j][e] = 0.0f;
     }
 
+  // ---- prologue: group 0's carriers, stages 0..2, then stage 3 ----
+  uint32_t t0 = 0u, t1 = 0u;                    // carriers of the group being decoded
+  float sc = 0.0f;                              // s / 127 of the group in the int32 sums
+  {
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b32(srs, poff, 0, 0);
+    const uint32_t ab = __builtin_amdgcn_raw_buffer_load_b32(brs, poff, 0, 0);
+    CarrierBuild cb;
+#pragma unroll
+    for (int piece = 0; piece < 4; ++piece) carrier_piece<B>(cb, piece, ab, sb, t0, t1, sc);
+  }
   issue_step(0, 0);
   issue_step(1, 1);
   issue_step(2, 2);
+  __builtin_amdgcn_s_waitcnt(a8_wait_vm(2 * NV));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  issue_step(3, 3);
 
-  uint32_t t0 = 0u, t1 = 0u;
-  float sc = 0.0f;
+  uint32_t cw[2 * B];                           // this lane's 64 codes of the current step
+  auto read_codes = [&](const unsigned char* st, uint32_t* w) {
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(st + kCodeOff) + DPR * (32 * wave + c) + 2 * B * h;
+#pragma unroll
+    for (int d = 0; d < 2 * B; ++d) w[d] = src[d];
+  };
+  // Activation fragment j (rows 32 j .. 32 j + 31) of sub-step ks sits at byte
+  // 4096 j + 128 c + 16 ((4 h) ^ sw ^ ks) of a stage, sw = (c % 8) ^ (c / 8 % 2)
+  // (a8_slot with row 32 j + c and chunk 4 h + ks).
+  const uint32_t xlane = static_cast<uint32_t>(128 * c + 16 * ((4 * h) ^ (c & 7) ^ ((c >> 3) & 1)));
+  auto read_a = [&](const unsigned char* st, uint32_t xl, int ks, int j) {
+    return *reinterpret_cast<const i32x4*>(st + (xl ^ (16u * ks)) + 4096 * j);
+  };
+  i32x4 fa[8];
+  i32x4 fb;
+  read_codes(smem, cw);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fa[j] = read_a(smem, xlane, 0, j);
+  {
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      A8Quad qs;
+      a8_quad_piece<B>(qs, 0, cw, q, t0, t1, o[q]);
+      a8_quad_piece<B>(qs, 1, cw, q, t0, t1, o[q]);
+    }
+    fb = i32x4{static_cast<int>(o[0]), static_cast<int>(o[1]), static_cast<int>(o[2]),
+               static_cast<int>(o[3])};
+  }
+
+  float sc_prev = 0.0f;                         // s / 127 of the group before (zero sums at first)
   int mg = 0;                                   // s % spg
-
+  // One sub-step: 8 MFMA slots, then the barrier after sub-step 2. FIRST: the
+  // group's first sub-step (the sums restart from zero after their update).
   auto step = [&](int s, auto ph_c) {
     constexpr int ph = decltype(ph_c)::value;  // s % 4
-    constexpr int ph3 = (ph + 3) % 4;
-    // Stage s is complete once only the loads of the next two stages remain.
-    // The bare barrier then publishes every wave's part of it, and every wave
-    // has finished reading stage s - 1, which the loads of step s + 3 overwrite.
-    static_assert(2 * NV < 64, "vmcnt holds at most 63");
-    __builtin_amdgcn_s_waitcnt(a8_wait_vm(2 * NV));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // past K: step 0 again into the free stage (never read), so the count holds
-    issue_step(s + 3 < nsteps ? s + 3 : 0, ph3);
+    constexpr int ph1 = (ph + 1) % 4;
+    const bool first = SPG == 1 ? true : (SPG == 2 ? ph % 2 == 0 : mg == 0);
+    const bool last = SPG == 1 ? true : (SPG == 2 ? ph % 2 == 1 : mg == spg - 1);
     const unsigned char* st = smem + ph * kStage;
-    uint32_t cw[2 * B];                         // this lane's 64 codes of the step
-    {
-      const uint32_t* src =
-          reinterpret_cast<const uint32_t*>(st + kCodeOff) + DPR * (32 * wave + c) + 2 * B * h;
-#pragma unroll
-      for (int d = 0; d < 2 * B; ++d) cw[d] = src[d];
-    }
-    const bool fresh = mg == 0;                // the group's first step: int32 sums start at 0
-    if (fresh) {
-      // new group: the row's carriers and scale
+    const unsigned char* stn = smem + ph1 * kStage;
+    uint32_t xl = xlane;                        // re-derived per step: not kept per stage
+    pin(xl);
+
+    uint32_t cwn[2 * B];
+    uint32_t t0n = t0, t1n = t1;
+    float scn = sc;
+    uint32_t pab = 0u, psb = 0u;
+    CarrierBuild cb;
+    if (last) {
       const uint32_t* par = reinterpret_cast<const uint32_t*>(st + kParamOff + 512 * wave);
-      carrier_table<B>(par[64 + c], t0, t1);
-      sc = __fdiv_rn(__uint_as_float(par[c]), 127.0f);
+      psb = par[c];
+      pab = par[64 + c];
     }
-    const int8_t* Ab = reinterpret_cast<const int8_t*>(st);
-    // Activation fragments roll through one set of registers: right after MFMA
-    // j of sub-step ks consumes fragment j, fragment j of sub-step ks + 1 is
-    // read into it. The weight fragment of sub-step ks + 1 is decoded under
-    // sub-step ks's MFMAs.
-    i32x4 fa[8];
-    auto read_a = [&](int ks, int j) {
-      return *reinterpret_cast<const i32x4*>(Ab + 16 * a8_slot(32 * j + c, 4 * h + ks));
-    };
-    auto decode = [&](int ks) {
+    auto sub_step = [&](int ks, auto first_c) {
+      constexpr bool restart = decltype(first_c)::value;
+      A8Quad qs[4];
       uint32_t o[4];
+      if (ks == 3) {
+        // past the barrier: stage s + 1 is complete; the next step's codes and
+        // the carriers it decodes with
+        read_codes(stn, cwn);
+      }
+      const uint32_t* wsrc = ks < 3 ? cw : cwn;
+      const uint32_t d0 = ks < 3 ? t0 : (last ? t0n : t0);
+      const uint32_t d1 = ks < 3 ? t1 : (last ? t1n : t1);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[u] = __builtin_amdgcn_perm(t1, t0, a8_selector<B>(a8_quad<B>(cw, 4 * ks + u)));
-      return i32x4{static_cast<int>(o[0]), static_cast<int>(o[1]), static_cast<int>(o[2]),
-                   static_cast<int>(o[3])};
-    };
+      for (int u = 0; u < 8; ++u) {
+        if constexpr (restart) {
+          // the finished group's sums of block u: out before the MFMA restarts
+          // them, into fp32 beside it (exact: |sum| < 2^24)
+          float f[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fa[j] = read_a(0, j);
-    i32x4 fb = decode(0);
+          for (int e = 0; e < 16; ++e) f[e] = static_cast<float>(acc[u][e]);
+          hold16(f, fa[u]);
+          acc[u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[u], fb, i32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const i32x4 fbn = ks < 3 ? decode(ks + 1) : fb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (ks == 0 && fresh) {
-          acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb, i32x16{}, 0, 0, 0);
+          for (int e = 0; e < 16; ++e) {
+            float v = fmaf(f[e], sc_prev, accf[u][e]);
+            pin(v);
+            accf[u][e] = v;
+          }
         } else {
-          acci[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb, acci[j], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[u], fb, acc[u], 0, 0, 0);
         }
-        if (ks < 3) fa[j] = read_a(ks + 1, j);
+        fa[u] = ks < 3 ? read_a(st, xl, ks + 1, u) : read_a(stn, xl, 0, u);
+        // decode of the next sub-step's fragment: quad piece u (sub-steps 0..2),
+        // or from slot 1 on once the next step's codes are read (sub-step 3)
+        if (ks < 3) {
+          a8_quad_piece<B>(qs[u >> 1], u & 1, wsrc, 4 * (ks + 1) + (u >> 1), d0, d1, o[u >> 1]);
+        } else if (u >= 1) {
+          if (u == 1) a8_quad_piece<B>(qs[0], 0, wsrc, 0, d0, d1, o[0]);
+          a8_quad_piece<B>(qs[u >> 1], u & 1, wsrc, u >> 1, d0, d1, o[u >> 1]);
+        }
+        if (last && ks == 1 && (u & 1)) carrier_piece<B>(cb, u >> 1, pab, psb, t0n, t1n, scn);
+        if (ks == 3) {
+          if (2 * u < NV) issue_load(s + 4, ph, 2 * u);
+          if (2 * u + 1 < NV) issue_load(s + 4, ph, 2 * u + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      fb = fbn;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mg = mg + 1 == spg ? 0 : mg + 1;
-    if (mg == 0) {
-      // group end: fp32 group scale (exact int32 dot, |I| < 2^24)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          accf[j][e] = fmaf(static_cast<float>(acci[j][e]), sc, accf[j][e]);
-        __builtin_amdgcn_sched_barrier(0);     // one block at a time (few temporaries)
+      if (ks == 2) {
+        // Stage s + 1 is complete once only the loads of stages s + 2 and s + 3
+        // remain; lgkmcnt(0) ends this wave's reads of stage s. The bare barrier
+        // publishes both, so stage s can be refilled for step s + 4.
+        __builtin_amdgcn_s_waitcnt(a8_wait_vm(2 * NV));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
+      fb = i32x4{static_cast<int>(o[0]), static_cast<int>(o[1]), static_cast<int>(o[2]),
+                 static_cast<int>(o[3])};
+    };
+    if (first) {
+      sub_step(0, std::true_type{});
+    } else {
+      sub_step(0, std::false_type{});
     }
+    sub_step(1, std::false_type{});
+    sub_step(2, std::false_type{});
+    sub_step(3, std::false_type{});
+#pragma unroll
+    for (int d = 0; d < 2 * B; ++d) cw[d] = cwn[d];
+    if (last) {
+      t0 = t0n;
+      t1 = t1n;
+      sc_prev = sc;
+      sc = scn;
+    }
+    mg = last ? 0 : mg + 1;
   };
   int s = 0;
   for (; s + 3 < nsteps; s += 4) {
@@ -287,6 +458,11 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   if (s < nsteps) step(s, std::integral_constant<int, 0>{});
   if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
   if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
+  // the last group's sums (its scale moved to sc_prev at its last step)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accf[j][e] = fmaf(static_cast<float>(acc[j][e]), sc_prev, accf[j][e]);
   __builtin_amdgcn_s_waitcnt(0);               // loads past K target stages nobody reads
   __syncthreads();
 
@@ -324,9 +500,9 @@ bool prefill_a8_supported(int64_t M, int64_t N, int64_t K, int bits, int group) 
   return tiles <= INT32_MAX;
 }
 
-template <int B>
-static hipError_t launch_prefill_a8_b(const TiledParams& p, hipStream_t st) {
-  auto kern = k_prefill_a8<B>;
+template <int B, int SPG>
+static hipError_t launch_prefill_a8_k(const TiledParams& p, hipStream_t st) {
+  auto kern = k_prefill_a8<B, SPG>;
   constexpr size_t lds = a8_lds_bytes(B);
   static_assert(lds <= 160 * 1024, "one compute unit's LDS");
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -336,6 +512,14 @@ static hipError_t launch_prefill_a8_b(const TiledParams& p, hipStream_t st) {
   const int64_t tiles = ((p.M + A8M - 1) / A8M) * ((p.N + A8N - 1) / A8N);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kA8Threads), lds, st, p);
   return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_prefill_a8_b(const TiledParams& p, hipStream_t st) {
+  const int spg = p.group / A8K;
+  if (spg == 1) return launch_prefill_a8_k<B, 1>(p, st);
+  if (spg == 2) return launch_prefill_a8_k<B, 2>(p, st);
+  return launch_prefill_a8_k<B, 0>(p, st);
 }
 
 hipError_t launch_prefill_a8(const TiledParams& p, int bits, hipStream_t st) {

@@ -74,8 +74,9 @@ def test_single_workload_a8():
     _check_a8(w, x)
 
 
-@pytest.mark.parametrize("bits,group", [(2, 512), (3, 256), (4, 128), (5, 128), (8, 1024)])
-@pytest.mark.parametrize("M", [1, 7, 130])
+@pytest.mark.parametrize("bits,group", [(2, 128), (2, 256), (2, 512), (3, 128), (3, 256), (3, 512),
+                                        (3, 1024), (4, 128), (5, 128), (8, 1024)])
+@pytest.mark.parametrize("M", [1, 7, 130, 300])
 def test_a8_ragged(bits, group, M):
     say(f"A8 ragged bits={bits} G={group} M={M}")
     g = synth.make_generator(2000 + 10 * bits + M)
