@@ -23,8 +23,10 @@
 //    conflicts), the tile's code words and the group parameters of the next
 //    group. The one barrier of step s sits after three quarters of its MFMAs:
 //    it waits until stage s + 1 has landed, so the rest of step s reads and
-//    decodes the first fragments of step s + 1 and refills stage s for step
-//    s + 4;
+//    decodes the first fragments of step s + 1. The stage it frees is refilled
+//    for step s + 4, one load per MFMA slot: the activations in the last
+//    sub-step of step s, the code words and parameters in the first sub-step
+//    of step s + 1;
 //  - within a step, lane half h takes codes 64 h .. 64 h + 63 of its row: codes
 //    64 h + 16 ks .. + 15 feed MFMA sub-step ks (0..3), and the activation
 //    fragments follow the same K order.
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   const __amdgpu_buffer_rsrc_t brs = a8_rsrc(p.shapes, static_cast<uint32_t>(p.N * gpr * 4));
   const uint32_t poff = static_cast<uint32_t>(pc * gpr * 4);
   constexpr int NV = 8 + NC + 2;                // loads per wave and step
-  static_assert(NV <= 16, "two loads per MFMA slot of the refill sub-step");
+  static_assert(NV <= 16, "one code or parameter load per MFMA slot of a sub-step");
   static_assert(3 * NV < 64, "vmcnt holds at most 63");
   // Load i (0 .. NV - 1) of step s into a stage. The parameter slots of step
   // s hold the group after the one step s belongs to (read in that group's
@@ -314,7 +316,10 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  issue_step(3, 3);
+  // step 3: its activation loads here (they belong to the last sub-step of
+  // step -1), its code and parameter loads in the first sub-step of step 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) issue_load(3, 3, i);
 
   uint32_t cw[2 * B];                           // this lane's 64 codes of the current step
   auto read_codes = [&](const unsigned char* st, uint32_t* w) {
@@ -412,10 +417,11 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
           a8_quad_piece<B>(qs[u >> 1], u & 1, wsrc, u >> 1, d0, d1, o[u >> 1]);
         }
         if (last && ks == 1 && (u & 1)) carrier_piece<B>(cb, u >> 1, pab, psb, t0n, t1n, scn);
-        if (ks == 3) {
-          if (2 * u < NV) issue_load(s + 4, ph, 2 * u);
-          if (2 * u + 1 < NV) issue_load(s + 4, ph, 2 * u + 1);
-        }
+        // refill of the stage freed by the barrier of step s - 1 or s: the
+        // activation loads of step s + 4 in the last sub-step, the code and
+        // parameter loads of step s + 3 in the first (one load per slot)
+        if (ks == 3) issue_load(s + 4, ph, u);
+        if (ks == 0 && 8 + u < NV) issue_load(s + 3, (ph + 3) % 4, 8 + u);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ks == 2) {
