@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--counter-run", choices=("gate_up", "down"), default=None,
                     help="only launch this product --steps times, eagerly on rotating copies "
                          "(for rocprofv3 --pmc passes)")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="only write --traffic-json from rocprofv3 --pmc outputs under DIR "
+                         "(pmc_<COUNTER>_<gate_up|down|copy>/*counter_collection.csv); no GPU")
     return ap.parse_args()
 
 
@@ -78,6 +81,63 @@ def stored_traffic(path):
     if t.get("gemv_source_hash") != gemv_source_hash():
         return None
     return t.get("decode_gate_up_bytes_per_launch")
+
+
+def _pmc_means(path, match):
+    """Mean Counter_Value per dispatch of the kernels whose name contains `match`,
+    from one rocprofv3 --pmc run (one counter) under `path`."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    vals = []
+    for f in files:
+        with open(f, newline="") as fh:
+            vals += [float(r["Counter_Value"]) for r in csv.DictReader(fh) if match in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no dispatch of {match!r} under {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(src, out, copy_mib=256):
+    """HBM bytes per gate_up / down launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the product kernel, each scaled by what the same counter reads
+    for a plain device copy of copy_mib MiB (which reads and writes exactly
+    that many bytes)."""
+    nbytes = copy_mib * (1 << 20)
+    cf, _ = _pmc_means(os.path.join(src, "pmc_FETCH_SIZE_copy"), "copyBuffer")
+    cw, _ = _pmc_means(os.path.join(src, "pmc_WRITE_SIZE_copy"), "copyBuffer")
+    ff, fw = nbytes / 1024.0 / cf, nbytes / 1024.0 / cw
+    res = {"gemv_source_hash": gemv_source_hash(),
+           "copy_calibration": {"bytes_read_and_written": nbytes, "FETCH_SIZE_KiB": cf,
+                                "WRITE_SIZE_KiB": cw, "fetch_factor": round(ff, 6),
+                                "write_factor": round(fw, 6)},
+           "raw_KiB_per_dispatch": {}}
+    n = None
+    for k in ("gate_up", "down"):
+        f, n = _pmc_means(os.path.join(src, f"pmc_FETCH_SIZE_{k}"), "k_gemv")
+        w, _ = _pmc_means(os.path.join(src, f"pmc_WRITE_SIZE_{k}"), "k_gemv")
+        res["raw_KiB_per_dispatch"][k] = {"FETCH_SIZE": f, "WRITE_SIZE": w}
+        res[f"decode_{k}_bytes_per_launch"] = int(round((f * ff + w * fw) * 1024.0))
+    res["dispatches_averaged"] = n
+    res["commands"] = [
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_FETCH_SIZE_gate_up -o run -- "
+        "python3 bench.py --counter-run gate_up --steps 60 --no-cpu-baseline",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_WRITE_SIZE_gate_up -o run -- "
+        "python3 bench.py --counter-run gate_up --steps 60 --no-cpu-baseline",
+        "(the same two with --counter-run down, into pmc_*_down)",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_FETCH_SIZE_copy -o run -- "
+        "python3 bench.py --calibrate-copy 256",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_WRITE_SIZE_copy -o run -- "
+        "python3 bench.py --calibrate-copy 256",
+        "python3 bench.py --write-traffic <dir>",
+    ]
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({"traffic_json": out, "gate_up": res["decode_gate_up_bytes_per_launch"],
+                      "down": res["decode_down_bytes_per_launch"]}))
 
 
 def calibrate_copy(mib):
@@ -132,6 +192,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.traffic_json)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return

@@ -560,12 +560,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void k_prefill_a16(TiledParams 
 }  // namespace
 
 // 2- and 3-bit codes, fp16 activations of k_xprep; the byte sizes of the
-// activation and code buffers must stay below 2^32 (buffer addressing).
+// activation and code buffers (with a tile's overhang past N) must stay below
+// 2^32 (buffer addressing).
 bool prefill_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   if (bits != 2 && bits != 3) return false;
   if (group % PK != 0 || K % PK != 0) return false;
   if (M * K * 2 >= (int64_t{1} << 32)) return false;
-  if (N * K * bits / 8 >= (int64_t{1} << 32)) return false;
+  if ((N + PT) * K * bits / 8 >= (int64_t{1} << 32)) return false;   // rows past N read 0
   const int64_t tiles = ((M + PT - 1) / PT) * ((N + PT - 1) / PT);
   return tiles <= INT32_MAX;
 }

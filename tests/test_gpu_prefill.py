@@ -38,6 +38,21 @@ def test_prefill_tiles_ragged(bits, group, M, N):
     assert row_rel_err(y.cpu().numpy(), _ref(w, x)) <= TOL
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("K", [1664, 1920])
+def test_prefill_step_tails(bits, K):
+    """K / 64 steps not a multiple of the 4-step unroll (groups are multiples
+    of 128, so two steps are left over)."""
+    say(f"prefill tails bits={bits} K={K}")
+    g = synth.make_generator(3500 + 10 * bits + K)
+    kind = "ternary" if bits == 2 else "uniform"
+    w = synth.make_weight(g, 203, K, bits, 128, kind, 0.02)
+    x = synth.activations(g, 300, K, 0.005, 30.0)
+    cw = upload(w)
+    y = cq.cubic_gemm_a16(x.to(DEV), cw)
+    assert row_rel_err(y.cpu().numpy(), _ref(w, x)) <= TOL
+
+
 def _raw_weight(bits, G, N, K, seed):
     gen = torch.Generator().manual_seed(seed)
     raw = torch.randint(0, 256, (N * K * bits // 8,), generator=gen).to(torch.uint8)
