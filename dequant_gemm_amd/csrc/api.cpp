@@ -149,7 +149,10 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
   uint16_t* xp = static_cast<uint16_t*>(workspace);
   float* xback = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           align256(static_cast<size_t>(M) * w->K * 2));
+  // up to 16 activation rows: the GEMV; 3- and 4-bit codes with 17..64 rows:
+  // the small-batch MFMA kernel
   const bool use_gemv = M <= kGemvMaxM && gemv_supported(w->K, w->bits, w->group);
+  const bool use_skinny = !use_gemv && skinny_supported(M, w->N, w->K, w->bits, w->group);
   hipError_t e = launch_xprep(x_bf16, M, w->K, use_gemv && w->bits == 2, xp, xback, s);
   if (e != hipSuccess) return CUBIC_ERR_HIP;
   if (use_gemv) {
@@ -158,6 +161,7 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
     return hip_status(launch_gemv(p, w->bits, false, s));
   }
   TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xp, xback, y};
+  if (use_skinny) return hip_status(launch_skinny_a16(p, w->bits, s));
   if (M >= kPrefillMinM && prefill_supported(M, w->N, w->K, w->bits, w->group))
     return hip_status(launch_prefill_a16(p, w->bits, s));
   return hip_status(launch_tiled_a16(p, w->bits, s));

@@ -66,6 +66,8 @@ hipError_t launch_tiled_a8(const TiledParams& p, int bits, hipStream_t st);
 bool prefill_supported(int64_t M, int64_t N, int64_t K, int bits, int group);
 hipError_t launch_prefill_a16(const TiledParams& p, int bits, hipStream_t st);
 bool prefill_a8_supported(int64_t M, int64_t N, int64_t K, int bits, int group);
+bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group);
+hipError_t launch_skinny_a16(const TiledParams& p, int bits, hipStream_t st);
 hipError_t launch_prefill_a8(const TiledParams& p, int bits, hipStream_t st);
 // LDS the grouped kernel needs with one activation row per pass.
 size_t moe_lds_min_bytes(int64_t K, int bits, int group);

@@ -1,0 +1,269 @@
+// skinny.hip -- A16 product for small batches (17 <= M <= 64; smaller M runs on
+// the GEMV) with 3- and 4-bit codes.
+//
+// The CubicQuant article (section "压缩权重必须边解码、边计算") decodes each
+// weight tile inside the kernel that consumes it and scales group partial sums
+// in fp32. With up to 64 activation rows one decoded weight fragment feeds one
+// or two MFMAs, so the layout is built around the weight stream:
+//  - a 256-thread workgroup owns 32 weight rows; wave w walks a quarter of K
+//    (steps of 64) against all activation rows (one or two 32-row blocks of
+//    v_mfma_f32_32x32x16_f16), and the four partial tiles are summed in LDS in
+//    a fixed order at the end (deterministic, no atomics);
+//  - every load of the step loop goes from global memory straight into the
+//    wave's own LDS ring (buffer_load ... lds): the fp16 activation chunk of the
+//    step (prepared by k_xprep, XOR-swizzled), the 32 rows' code words and
+//    their group parameters. A wave only reads what it loaded itself, so the
+//    loop needs no workgroup barrier, only its own memory counter;
+//  - lane (c, h) decodes row c, codes 32 h .. 32 h + 31 of the step, by lookups
+//    in the row's fp16 table of normalised levels q (2^B entries in LDS, rebuilt
+//    at each group start); the group's MFMA sums are then scaled by the row's
+//    fp32 s, which is this lane's own column of the MFMA output.
+// Within a step, MFMA sub-step kb takes codes 8 kb .. 8 kb + 7 of each 32-code
+// half, and the activation fragments follow the same K order.
+#include "common.h"
+#include "decode.h"
+#include "launch.h"
+
+namespace cubic {
+namespace {
+
+constexpr int SK_ROWS = 32;            // weight rows per workgroup
+constexpr int SK_K = 64;               // K per step
+constexpr int SK_WAVES = 4;
+constexpr uint32_t kSkRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           static_cast<int>(bytes), static_cast<int>(kSkRsrcWord3));
+}
+
+// s_waitcnt immediate: vmcnt(n) (n < 64), expcnt not waited for, lgkmcnt(0).
+constexpr int sk_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
+
+// Per-wave LDS ring stage: activations [32 MB rows][64 k] fp16 (16-byte chunk
+// q of row r at chunk q ^ (r & 7)), then the code words (lane l's 16 bytes:
+// row l / 2, half l % 2), then the group parameters (64 scales, 64 (a, b)
+// words; lanes 32..63 repeat rows 0..31).
+template <int MB> constexpr int sk_stages() { return MB == 2 ? 4 : 6; }
+template <int MB> constexpr size_t sk_x_bytes() { return static_cast<size_t>(32 * MB) * SK_K * 2; }
+template <int MB> constexpr size_t sk_stage_bytes() { return sk_x_bytes<MB>() + 1024 + 512; }
+template <int B> constexpr size_t sk_tab_bytes() { return static_cast<size_t>(SK_ROWS) * (1 << B) * 2; }
+template <int B, int MB>
+constexpr size_t sk_lds_bytes() {
+  return SK_WAVES * (sk_stages<MB>() * sk_stage_bytes<MB>() + sk_tab_bytes<B>());
+}
+
+template <int B, int MB>
+__global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
+  extern __shared__ __align__(1024) unsigned char smem[];   // row tables rely on this alignment
+  static_assert(B == 3 || B == 4, "16-byte code slots per lane and step");
+  constexpr int NST = sk_stages<MB>();
+  constexpr size_t kStage = sk_stage_bytes<MB>();
+  constexpr size_t kCodeOff = sk_x_bytes<MB>();
+  constexpr size_t kParamOff = kCodeOff + 1024;
+  constexpr int NX = 4 * MB;                     // activation loads per step (1 KB each)
+  constexpr int NV = NX + 3;                     // + codes + scales + (a, b)
+  static_assert(NST * NV < 64, "vmcnt holds at most 63");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * SK_ROWS;
+  const int nsteps = static_cast<int>(p.K / SK_K);
+  const int sb = wave * nsteps / SK_WAVES, se = (wave + 1) * nsteps / SK_WAVES;
+  const int gpr = static_cast<int>(p.K / p.group);
+  const uint32_t row_bytes = static_cast<uint32_t>(p.K * B / 8);
+
+  unsigned char* ring = smem + static_cast<size_t>(wave) * NST * kStage;
+  uint16_t* tab_wave =
+      reinterpret_cast<uint16_t*>(smem + SK_WAVES * NST * kStage + wave * sk_tab_bytes<B>());
+
+  // ---- loads of one step into a stage (this wave's own) ----
+  // activations: load i covers rows 8 i .. 8 i + 7; lane l -> row 8 i + l / 8,
+  // physical chunk l % 8 = logical chunk (l % 8) ^ (l / 8 % 8). Rows past M read 0.
+  const __amdgpu_buffer_rsrc_t xrs = sk_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K * 2));
+  const uint32_t xoff = static_cast<uint32_t>(((lane >> 3) * p.K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+  // code words: lane l -> row n0 + l / 2, codes 32 (l % 2) .. + 31 of the step.
+  // Rows past N read 0.
+  const __amdgpu_buffer_rsrc_t crs = sk_rsrc(p.codes, static_cast<uint32_t>(p.N) * row_bytes);
+  const uint32_t coff = static_cast<uint32_t>(n0 + (lane >> 1)) * row_bytes +
+                        static_cast<uint32_t>((lane & 1) * 4 * B);
+  // group parameters of row n0 + l % 32 (clamped to a valid row)
+  const int64_t prow = n0 + c < p.N ? n0 + c : p.N - 1;
+  const __amdgpu_buffer_rsrc_t srs = sk_rsrc(p.scales, static_cast<uint32_t>(p.N * gpr * 4));
+  const __amdgpu_buffer_rsrc_t brs = sk_rsrc(p.shapes, static_cast<uint32_t>(p.N * gpr * 4));
+  const uint32_t poff = static_cast<uint32_t>(prow * gpr * 4);
+  auto issue = [&](int s, int stage) {
+    const int sv = s < se ? s : sb;            // past the wave's range: reload its first step
+    unsigned char* st = ring + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, st + 1024 * i, 16,
+          xoff + static_cast<uint32_t>(8 * i) * static_cast<uint32_t>(p.K) * 2 +
+              static_cast<uint32_t>(sv) * (SK_K * 2),
+          0, 0, 0);
+    if constexpr (B == 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 16,
+                                               coff + static_cast<uint32_t>(sv) * (8 * B), 0, 0, 0);
+    } else {
+      // 12-byte loads land at a 16-byte lane stride
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 12,
+                                               coff + static_cast<uint32_t>(sv) * (8 * B), 0, 0, 0);
+    }
+    const uint32_t g = static_cast<uint32_t>(sv * SK_K / p.group);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, st + kParamOff, 4, poff + 4u * g, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, st + kParamOff + 256, 4, poff + 4u * g, 0, 0, 0);
+  };
+
+  f32x16 acc[MB], accg[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      acc[j][e] = 0.0f;
+      accg[j][e] = 0.0f;
+    }
+
+  // ---- prologue: steps sb .. sb + NST - 2 ----
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) issue(sb + t, t);
+
+  uint16_t* tab = tab_wave + c * (1 << B);      // this lane's row table
+  const uint32_t tbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab));
+  float sc = 0.0f;
+  for (int s = sb; s < se; ++s) {
+    const int stage = (s - sb) % NST;
+    const unsigned char* st = ring + stage * kStage;
+    // Stage s has landed once only the loads of the next NST - 2 steps remain;
+    // lgkmcnt(0) also ends this wave's reads of the stage refilled next.
+    __builtin_amdgcn_s_waitcnt(sk_wait_vm((NST - 2) * NV));
+    asm volatile("" ::: "memory");
+    issue(s + NST - 1, (stage + NST - 1) % NST);
+    const int k0 = s * SK_K;
+    const bool gstart = s == sb || k0 % p.group == 0;
+    if (gstart) {
+      // new group: this lane's half of its row's level table, and the row's scale
+      const uint32_t* par = reinterpret_cast<const uint32_t*>(st + kParamOff);
+      const uint32_t ab = par[64 + c];
+      sc = __uint_as_float(par[c]);
+      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+#pragma unroll
+      for (int v = h; v < (1 << B); v += 2) tab[v] = table_entry_f32(a, b, static_cast<uint32_t>(v), B);
+      wave_lds_order();
+    }
+    uint32_t w[B];
+    {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff) + 4 * (2 * c + h);
+#pragma unroll
+      for (int d = 0; d < B; ++d) w[d] = src[d];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      // weight fragment: codes 8 kb .. 8 kb + 7 of the lane's 32, via the row table
+      u32x4 fbv;
+      {
+        typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+        typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
+        constexpr uint32_t kMask2 = ((1u << B) - 1u) << 1;
+        auto addr = [&](int i) {
+          const int bit = i * B;
+          const int d = bit >> 5, off = bit & 31;
+          uint32_t v;
+          if (off == 0) {
+            v = w[d] << 1;
+          } else if (off + B <= 32) {
+            v = w[d] >> (off - 1);
+          } else {
+            v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 1);
+          }
+          return (v & kMask2) | tbase;
+        };
+        uint32_t r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u16x2v hv;
+          hv.x = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(addr(8 * kb + 2 * q)));
+          hv.y = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(addr(8 * kb + 2 * q + 1)));
+          r[q] = __builtin_bit_cast(uint32_t, hv);
+        }
+        fbv = u32x4{r[0], r[1], r[2], r[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        // activation rows 32 j + c, logical chunk 4 h + kb
+        const int r = 32 * j + c;
+        const f16x8 fa = *reinterpret_cast<const f16x8*>(st + r * 128 + 16 * ((4 * h + kb) ^ (r & 7)));
+        accg[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, __builtin_bit_cast(f16x8, fbv), accg[j], 0, 0, 0);
+      }
+    }
+    if (s + 1 == se || (k0 + SK_K) % p.group == 0) {
+      // group end: scale by the row's s (this lane's output column) into fp32
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          acc[j][e] = fmaf(accg[j][e], sc, acc[j][e]);
+          accg[j][e] = 0.0f;
+        }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);                // loads past the range target stages nobody reads
+  __syncthreads();
+
+  // ---- sum of the four waves' partial tiles, in wave order ----
+  // D element (row m of activation block j, column n): lane n + 32 ((m / 4) % 2),
+  // register 4 (m / 8) + m % 4.
+  float* red = reinterpret_cast<float*>(smem);  // [wave][j][e][lane]
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[((wave * MB + j) * 16 + e) * 64 + lane] = acc[j][e];
+  __syncthreads();
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4 * MB; ++k) {
+    const int o = t + 256 * k;                  // o = 32 m + n over 32 MB activation rows
+    const int n = o & 31, m = o >> 5;
+    const int j = m >> 5, mm = m & 31;
+    const int l = n + 32 * ((mm >> 2) & 1), e = 4 * (mm >> 3) + (mm & 3);
+    float v = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < SK_WAVES; ++wv) v += red[((wv * MB + j) * 16 + e) * 64 + l];
+    if (m < p.M && n0 + n < p.N) p.y[static_cast<int64_t>(m) * p.N + n0 + n] = v * p.xs[m];
+  }
+}
+
+}  // namespace
+
+bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
+  if (bits != 3 && bits != 4) return false;
+  if (M < 1 || M > 64 || K % SK_K != 0 || K / SK_K < SK_WAVES) return false;
+  if (group % SK_K != 0) return false;
+  if (64 * K * 2 >= (int64_t{1} << 32)) return false;   // activation offsets of 64 rows
+  if ((N + SK_ROWS) * K * bits / 8 >= (int64_t{1} << 32)) return false;
+  if (N * (K / group) * 4 >= (int64_t{1} << 32)) return false;
+  return (N + SK_ROWS - 1) / SK_ROWS <= INT32_MAX;
+}
+
+template <int B, int MB>
+static hipError_t launch_skinny_k(const TiledParams& p, hipStream_t st) {
+  auto kern = k_skinny<B, MB>;
+  constexpr size_t lds = sk_lds_bytes<B, MB>();
+  static_assert(lds <= 160 * 1024, "one compute unit's LDS");
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  const unsigned grid = static_cast<unsigned>((p.N + SK_ROWS - 1) / SK_ROWS);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_a16(const TiledParams& p, int bits, hipStream_t st) {
+  if (bits == 3) return p.M <= 32 ? launch_skinny_k<3, 1>(p, st) : launch_skinny_k<3, 2>(p, st);
+  return p.M <= 32 ? launch_skinny_k<4, 1>(p, st) : launch_skinny_k<4, 2>(p, st);
+}
+
+}  // namespace cubic

@@ -164,6 +164,42 @@ def test_small_m_rows_per_workgroup_ragged(bits, group, M):
     _check(w, x)
 
 
+@pytest.mark.parametrize("bits,group", [(3, 128), (3, 512), (4, 128), (4, 256)])
+@pytest.mark.parametrize("M,N,K", [(17, 203, 512), (31, 64, 1536), (32, 4100, 1024), (33, 203, 1536),
+                                   (64, 230, 3072)])
+def test_small_batch_mfma_shapes(bits, group, M, N, K):
+    """The small-batch MFMA kernel (3- and 4-bit codes, 17..64 rows): one and two
+    32-row activation blocks, ragged N, few steps per wave."""
+    say(f"A16 small batch bits={bits} G={group} M={M} N={N} K={K}")
+    g = synth.make_generator(6000 + 10 * bits + M + N)
+    w = synth.make_weight(g, N, K, bits, group, "uniform", 0.02)
+    x = synth.activations(g, M, K, 0.01, 50.0)
+    _check(w, x)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("K", [1664, 1920])
+def test_small_batch_mfma_uneven_waves(bits, K):
+    """K / 64 steps not divisible by the four waves (26 and 30 steps)."""
+    say(f"A16 small batch uneven waves bits={bits} K={K}")
+    g = synth.make_generator(6100 + 10 * bits + K)
+    w = synth.make_weight(g, 96, K, bits, 128, "uniform", 0.02)
+    x = synth.activations(g, 40, K, 0.01, 50.0)
+    _check(w, x)
+
+
+@pytest.mark.parametrize("factor", [5e7, 5e-7])
+def test_small_batch_mfma_scale_range(factor):
+    """Group scales far from 1: the tables hold normalised levels and the scale
+    is applied in fp32, so the fp16 range does not matter."""
+    say(f"A16 small batch scale x{factor}")
+    g = synth.make_generator(6200)
+    w = synth.make_weight(g, 203, 1024, 4, 128, "uniform", 0.02)
+    w.scales = w.scales * factor
+    x = synth.activations(g, 24, 1024, 0.01, 50.0)
+    _check(w, x)
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_sparse_extra_codes_w2(M):
     """Ternary 2-bit weights with a few codes -2 planted at scattered positions:
