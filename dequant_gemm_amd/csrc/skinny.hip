@@ -15,9 +15,14 @@
 //    their group parameters. A wave only reads what it loaded itself, so the
 //    loop needs no workgroup barrier, only its own memory counter;
 //  - lane (c, h) decodes row c, codes 32 h .. 32 h + 31 of the step, by lookups
-//    in the row's fp16 table of normalised levels q (2^B entries in LDS, rebuilt
-//    at each group start); the group's MFMA sums are then scaled by the row's
-//    fp32 s, which is this lane's own column of the MFMA output.
+//    in the row's fp16 table of levels s q 2^-e (2^B entries in LDS; the next
+//    group's table is built one step ahead, in a second buffer, from the
+//    parameters that come with the step's stage). 2^e is a power of two at or
+//    above the row's largest |s| in the wave's K range, so every level fits
+//    fp16 whatever s is, and the MFMA sums need no per-group scaling: the
+//    wave's partial tile is multiplied by 2^e once, at the end;
+//  - a step issues all of its LDS reads (code words, activation fragments,
+//    table lookups) before its MFMAs, so their latencies overlap.
 // Within a step, MFMA sub-step kb takes codes 8 kb .. 8 kb + 7 of each 32-code
 // half, and the activation fragments follow the same K order.
 #include "common.h"
@@ -42,15 +47,31 @@ constexpr int sk_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) <
 
 // Per-wave LDS ring stage: activations [32 MB rows][64 k] fp16 (16-byte chunk
 // q of row r at chunk q ^ (r & 7)), then the code words (lane l's 16 bytes:
-// row l / 2, half l % 2), then the group parameters (64 scales, 64 (a, b)
-// words; lanes 32..63 repeat rows 0..31).
+// row l / 2, half l % 2), then the group parameters of the step after it (64
+// scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
 template <int MB> constexpr int sk_stages() { return MB == 2 ? 4 : 6; }
 template <int MB> constexpr size_t sk_x_bytes() { return static_cast<size_t>(32 * MB) * SK_K * 2; }
 template <int MB> constexpr size_t sk_stage_bytes() { return sk_x_bytes<MB>() + 1024 + 512; }
-template <int B> constexpr size_t sk_tab_bytes() { return static_cast<size_t>(SK_ROWS) * (1 << B) * 2; }
+template <int B> constexpr size_t sk_tab_bytes() { return 2 * static_cast<size_t>(SK_ROWS) * (1 << B) * 2; }
 template <int B, int MB>
 constexpr size_t sk_lds_bytes() {
   return SK_WAVES * (sk_stages<MB>() * sk_stage_bytes<MB>() + sk_tab_bytes<B>());
+}
+
+// Normalised level q of field value v (two's complement, B bits) in fp32: with
+// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^10), a X and b Y are
+// exact products of fp16 values, so Q = j^3 + a X + b Y rounds twice in fp32
+// and once more by 1/K^3 (a few fp32 ulps; one fp16 rounding follows).
+template <int B>
+__device__ __forceinline__ float sk_level(float a, float b, int v) {
+  constexpr int km = kmax_of(B);
+  const int k = v >= (1 << (B - 1)) ? v - (1 << B) : v;
+  const int j = k < 0 ? -k : k;
+  const float X = static_cast<float>(j * km * km - j * j * j);
+  const float Y = static_cast<float>(j * j * km - j * j * j);
+  const float q = fmaf(a, X, fmaf(b, Y, static_cast<float>(j * j * j))) *
+                  (1.0f / static_cast<float>(km * km * km));
+  return k < 0 ? -q : q;
 }
 
 template <int B, int MB>
@@ -111,27 +132,70 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 12,
                                                coff + static_cast<uint32_t>(sv) * (8 * B), 0, 0, 0);
     }
-    const uint32_t g = static_cast<uint32_t>(sv * SK_K / p.group);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, st + kParamOff, 4, poff + 4u * g, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, st + kParamOff + 256, 4, poff + 4u * g, 0, 0, 0);
+    int g = (sv + 1) * SK_K / p.group;         // the group of the step after sv
+    g = g < gpr ? g : gpr - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, st + kParamOff, 4, poff + 4u * static_cast<uint32_t>(g),
+                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, st + kParamOff + 256, 4,
+                                             poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
   };
 
-  f32x16 acc[MB], accg[MB];
+  f32x16 acc[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      acc[j][e] = 0.0f;
-      accg[j][e] = 0.0f;
-    }
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
 
-  // ---- prologue: steps sb .. sb + NST - 2 ----
+  // ---- the row's level scale over this wave's K range: a power of two
+  // 2^e >= max |s| of its groups there, so that fp16(s q 2^-e) fits whatever s
+  // is. The row's two lanes take alternate groups; loads past the range read
+  // an offset outside the buffer (0).
+  float inv_rs = 1.0f, rs = 1.0f;
+  {
+    const int g_lo = sb * SK_K / p.group;
+    const int g_hi = se > sb ? ((se * SK_K - 1) / p.group) : g_lo;   // last group touched
+    float smax = 0.0f;
+    for (int g0 = g_lo; g0 <= g_hi; g0 += 32) {
+      float v[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int g = g0 + 2 * t + h;
+        const uint32_t off = g <= g_hi ? poff + 4u * static_cast<uint32_t>(g) : 0xFFFFFFF0u;
+        v[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) smax = fmaxf(smax, fabsf(v[t]));
+    }
+    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+    int e = 0;
+    if (smax > 0.0f && smax <= 3.4e38f) e = ilogbf(smax) + 1;
+    inv_rs = ldexpf(1.0f, -e);
+    rs = ldexpf(1.0f, e);
+  }
+
+  // Level tables: two per row (the group being decoded and the next one, built
+  // one step ahead from the parameters that came with the step's stage), each
+  // entry fp16(s q 2^-e) for field values 0 .. 2^B - 1.
+  constexpr int TE = 1 << B;                    // entries per row table
+  auto build = [&](int buf, uint32_t sbits, uint32_t ab) {
+    uint16_t* t = tab_wave + (buf * SK_ROWS + c) * TE;
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+    const float sk = __uint_as_float(sbits) * inv_rs;    // exact (power of two)
+#pragma unroll
+    for (int v = h; v < TE; v += 2) t[v] = f16_bits(sk * sk_level<B>(a, b, v));
+  };
+
+  // ---- prologue: the first group's table, steps sb .. sb + NST - 2 ----
+  int cur = 0;                                   // table of the group being decoded
+  {
+    const uint32_t g0 = static_cast<uint32_t>(sb * SK_K / p.group);
+    build(0, __builtin_amdgcn_raw_buffer_load_b32(srs, poff + 4u * g0, 0, 0),
+          __builtin_amdgcn_raw_buffer_load_b32(brs, poff + 4u * g0, 0, 0));
+  }
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t) issue(sb + t, t);
 
-  uint16_t* tab = tab_wave + c * (1 << B);      // this lane's row table
-  const uint32_t tbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab));
-  float sc = 0.0f;
   for (int s = sb; s < se; ++s) {
     const int stage = (s - sb) % NST;
     const unsigned char* st = ring + stage * kStage;
@@ -140,46 +204,52 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
     __builtin_amdgcn_s_waitcnt(sk_wait_vm((NST - 2) * NV));
     asm volatile("" ::: "memory");
     issue(s + NST - 1, (stage + NST - 1) % NST);
-    const int k0 = s * SK_K;
-    const bool gstart = s == sb || k0 % p.group == 0;
-    if (gstart) {
-      // new group: this lane's half of its row's level table, and the row's scale
-      const uint32_t* par = reinterpret_cast<const uint32_t*>(st + kParamOff);
-      const uint32_t ab = par[64 + c];
-      sc = __uint_as_float(par[c]);
-      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
-      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
-#pragma unroll
-      for (int v = h; v < (1 << B); v += 2) tab[v] = table_entry_f32(a, b, static_cast<uint32_t>(v), B);
-      wave_lds_order();
-    }
+    // all of the step's LDS reads first: code words, activation fragments
     uint32_t w[B];
     {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff) + 4 * (2 * c + h);
 #pragma unroll
       for (int d = 0; d < B; ++d) w[d] = src[d];
     }
+    f16x8 fa[4][MB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      // weight fragment: codes 8 kb .. 8 kb + 7 of the lane's 32, via the row table
-      u32x4 fbv;
-      {
-        typedef __attribute__((address_space(3))) const uint16_t lds_u16;
-        typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
-        constexpr uint32_t kMask2 = ((1u << B) - 1u) << 1;
-        auto addr = [&](int i) {
-          const int bit = i * B;
-          const int d = bit >> 5, off = bit & 31;
-          uint32_t v;
-          if (off == 0) {
-            v = w[d] << 1;
-          } else if (off + B <= 32) {
-            v = w[d] >> (off - 1);
-          } else {
-            v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 1);
-          }
-          return (v & kMask2) | tbase;
-        };
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        // activation rows 32 j + c, logical chunk 4 h + kb
+        const int r = 32 * j + c;
+        fa[kb][j] = *reinterpret_cast<const f16x8*>(st + r * 128 + 16 * ((4 * h + kb) ^ (r & 7)));
+      }
+    // the next step starts a group: its table and scale (parameters of the
+    // group of step s + 1 come with stage s)
+    const bool gnext = s + 1 < se && ((s + 1) * SK_K) % p.group == 0;
+    if (gnext) {
+      const uint32_t* par = reinterpret_cast<const uint32_t*>(st + kParamOff);
+      build(cur ^ 1, par[c], par[64 + c]);
+    }
+    // weight fragments: codes 8 kb .. 8 kb + 7 of the lane's 32, via the row table
+    const uint32_t tbase = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>(tab_wave + (cur * SK_ROWS + c) * TE));
+    u32x4 fb[4];
+    {
+      typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+      typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
+      constexpr uint32_t kMask2 = ((1u << B) - 1u) << 1;
+      auto addr = [&](int i) {
+        const int bit = i * B;
+        const int d = bit >> 5, off = bit & 31;
+        uint32_t v;
+        if (off == 0) {
+          v = w[d] << 1;
+        } else if (off + B <= 32) {
+          v = w[d] >> (off - 1);
+        } else {
+          v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 1);
+        }
+        return (v & kMask2) | tbase;
+      };
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
         uint32_t r[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -188,27 +258,22 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
           hv.y = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(addr(8 * kb + 2 * q + 1)));
           r[q] = __builtin_bit_cast(uint32_t, hv);
         }
-        fbv = u32x4{r[0], r[1], r[2], r[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        // activation rows 32 j + c, logical chunk 4 h + kb
-        const int r = 32 * j + c;
-        const f16x8 fa = *reinterpret_cast<const f16x8*>(st + r * 128 + 16 * ((4 * h + kb) ^ (r & 7)));
-        accg[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, __builtin_bit_cast(f16x8, fbv), accg[j], 0, 0, 0);
+        fb[kb] = u32x4{r[0], r[1], r[2], r[3]};
       }
     }
-    if (s + 1 == se || (k0 + SK_K) % p.group == 0) {
-      // group end: scale by the row's s (this lane's output column) into fp32
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < MB; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          acc[j][e] = fmaf(accg[j][e], sc, acc[j][e]);
-          accg[j][e] = 0.0f;
-        }
-    }
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kb][j], __builtin_bit_cast(f16x8, fb[kb]),
+                                                        acc[j], 0, 0, 0);
+    if (gnext) cur ^= 1;
   }
+  // the row's level scale back (this lane's output column)
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] *= rs;
   __builtin_amdgcn_s_waitcnt(0);                // loads past the range target stages nobody reads
   __syncthreads();
 
