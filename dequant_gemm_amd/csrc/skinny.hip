@@ -5,19 +5,20 @@
 // weight tile inside the kernel that consumes it and scales group partial sums
 // in fp32. With up to 64 activation rows one decoded weight fragment feeds one
 // or two MFMAs, so the layout is built around the weight stream:
-//  - a 256-thread workgroup owns 32 weight rows; wave w walks a quarter of K
+//  - a 512-thread workgroup owns 32 weight rows; wave w walks an eighth of K
 //    (steps of 64) against all activation rows (one or two 32-row blocks of
-//    v_mfma_f32_32x32x16_f16), and the four partial tiles are summed in LDS in
-//    a fixed order at the end (deterministic, no atomics);
+//    v_mfma_f32_32x32x16_f16), and the eight partial tiles are summed in LDS
+//    in a fixed order at the end (deterministic, no atomics). Two waves per
+//    SIMD hide each other's memory and LDS latencies;
 //  - every load of the step loop goes from global memory straight into the
 //    wave's own LDS ring (buffer_load ... lds): the fp16 activation chunk of the
 //    step (prepared by k_xprep, XOR-swizzled), the 32 rows' code words and
 //    their group parameters. A wave only reads what it loaded itself, so the
 //    loop needs no workgroup barrier, only its own memory counter;
 //  - lane (c, h) decodes row c, codes 32 h .. 32 h + 31 of the step, by lookups
-//    in the row's fp16 table of levels s q 2^-e (2^B entries in LDS; the next
-//    group's table is built one step ahead, in a second buffer, from the
-//    parameters that come with the step's stage). 2^e is a power of two at or
+//    in the row's fp16 table of levels s q 2^-e (2^B entries in LDS, rebuilt at
+//    each group's first step from parameters that came with the stage of the
+//    step before). 2^e is a power of two at or
 //    above the row's largest |s| in the wave's K range, so every level fits
 //    fp16 whatever s is, and the MFMA sums need no per-group scaling: the
 //    wave's partial tile is multiplied by 2^e once, at the end;
@@ -34,7 +35,6 @@ namespace {
 
 constexpr int SK_ROWS = 32;            // weight rows per workgroup
 constexpr int SK_K = 64;               // K per step
-constexpr int SK_WAVES = 4;
 constexpr uint32_t kSkRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* p, uint32_t bytes) {
@@ -49,13 +49,14 @@ constexpr int sk_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) <
 // q of row r at chunk q ^ (r & 7)), then the code words (lane l's 16 bytes:
 // row l / 2, half l % 2), then the group parameters of the step after it (64
 // scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
-template <int MB> constexpr int sk_stages() { return MB == 2 ? 4 : 6; }
+// Ring depth: what the LDS holds with W waves of one or two 32-row blocks.
+template <int W, int MB> constexpr int sk_stages() { return W == 8 ? (MB == 2 ? 2 : 3) : (MB == 2 ? 4 : 6); }
 template <int MB> constexpr size_t sk_x_bytes() { return static_cast<size_t>(32 * MB) * SK_K * 2; }
 template <int MB> constexpr size_t sk_stage_bytes() { return sk_x_bytes<MB>() + 1024 + 512; }
-template <int B> constexpr size_t sk_tab_bytes() { return 2 * static_cast<size_t>(SK_ROWS) * (1 << B) * 2; }
-template <int B, int MB>
+template <int B> constexpr size_t sk_tab_bytes() { return static_cast<size_t>(SK_ROWS) * (1 << B) * 2; }
+template <int B, int MB, int W>
 constexpr size_t sk_lds_bytes() {
-  return SK_WAVES * (sk_stages<MB>() * sk_stage_bytes<MB>() + sk_tab_bytes<B>());
+  return W * (sk_stages<W, MB>() * sk_stage_bytes<MB>() + sk_tab_bytes<B>());
 }
 
 // Normalised level q of field value v (two's complement, B bits) in fp32: with
@@ -74,11 +75,11 @@ __device__ __forceinline__ float sk_level(float a, float b, int v) {
   return k < 0 ? -q : q;
 }
 
-template <int B, int MB>
-__global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
+template <int B, int MB, int SK_WAVES>
+__global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
   extern __shared__ __align__(1024) unsigned char smem[];   // row tables rely on this alignment
   static_assert(B == 3 || B == 4, "16-byte code slots per lane and step");
-  constexpr int NST = sk_stages<MB>();
+  constexpr int NST = sk_stages<SK_WAVES, MB>();
   constexpr size_t kStage = sk_stage_bytes<MB>();
   constexpr size_t kCodeOff = sk_x_bytes<MB>();
   constexpr size_t kParamOff = kCodeOff + 1024;
@@ -146,11 +147,33 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
 
+  // Level table of each row (entries fp16(s q 2^-e) for field values 0 ..
+  // 2^B - 1), rebuilt at a group's first step from the parameters that came
+  // with the stage of the step before it.
+  constexpr int TE = 1 << B;                    // entries per row table
+  // Entry v of row c sits at v ^ tswz. Row tables are TE / 2 words apart, so
+  // rows c and c + 64 / TE share LDS banks; XOR-ing 2 (c / (64 / TE)) into the
+  // entry index moves them apart, and the 32 rows of a half wave reading the
+  // same field value hit 32 different banks.
+  const int tswz = 2 * (c / (64 / TE));
+  float inv_rs = 1.0f, rs = 1.0f;               // 2^-e and 2^e of the row (set below)
+  auto build = [&](int buf, uint32_t sbits, uint32_t ab) {
+    uint16_t* t = tab_wave + (buf * SK_ROWS + c) * TE;   // buf is 0 (one table per row)
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+    const float sk = __uint_as_float(sbits) * inv_rs;    // exact (power of two)
+#pragma unroll
+    for (int v = h; v < TE; v += 2) t[v ^ tswz] = f16_bits(sk * sk_level<B>(a, b, v));
+  };
+
+  // ---- prologue: steps sb .. sb + NST - 2 in flight first, then the row
+  // scale and the first group's table (their loads overlap the ring's) ----
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t) issue(sb + t, t);
   // ---- the row's level scale over this wave's K range: a power of two
   // 2^e >= max |s| of its groups there, so that fp16(s q 2^-e) fits whatever s
   // is. The row's two lanes take alternate groups; loads past the range read
   // an offset outside the buffer (0).
-  float inv_rs = 1.0f, rs = 1.0f;
   {
     const int g_lo = sb * SK_K / p.group;
     const int g_hi = se > sb ? ((se * SK_K - 1) / p.group) : g_lo;   // last group touched
@@ -173,28 +196,12 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
     rs = ldexpf(1.0f, e);
   }
 
-  // Level tables: two per row (the group being decoded and the next one, built
-  // one step ahead from the parameters that came with the step's stage), each
-  // entry fp16(s q 2^-e) for field values 0 .. 2^B - 1.
-  constexpr int TE = 1 << B;                    // entries per row table
-  auto build = [&](int buf, uint32_t sbits, uint32_t ab) {
-    uint16_t* t = tab_wave + (buf * SK_ROWS + c) * TE;
-    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
-    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
-    const float sk = __uint_as_float(sbits) * inv_rs;    // exact (power of two)
-#pragma unroll
-    for (int v = h; v < TE; v += 2) t[v] = f16_bits(sk * sk_level<B>(a, b, v));
-  };
-
-  // ---- prologue: the first group's table, steps sb .. sb + NST - 2 ----
-  int cur = 0;                                   // table of the group being decoded
+  uint32_t psb = 0u, pab = 0u;                   // parameters of the next group
   {
     const uint32_t g0 = static_cast<uint32_t>(sb * SK_K / p.group);
     build(0, __builtin_amdgcn_raw_buffer_load_b32(srs, poff + 4u * g0, 0, 0),
           __builtin_amdgcn_raw_buffer_load_b32(brs, poff + 4u * g0, 0, 0));
   }
-#pragma unroll
-  for (int t = 0; t < NST - 1; ++t) issue(sb + t, t);
 
   for (int s = sb; s < se; ++s) {
     const int stage = (s - sb) % NST;
@@ -204,6 +211,7 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
     __builtin_amdgcn_s_waitcnt(sk_wait_vm((NST - 2) * NV));
     asm volatile("" ::: "memory");
     issue(s + NST - 1, (stage + NST - 1) % NST);
+    if (s > sb && (s * SK_K) % p.group == 0) build(0, psb, pab);   // a new group's table
     // all of the step's LDS reads first: code words, activation fragments
     uint32_t w[B];
     {
@@ -224,12 +232,14 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
     // group of step s + 1 come with stage s)
     const bool gnext = s + 1 < se && ((s + 1) * SK_K) % p.group == 0;
     if (gnext) {
+      // parameters of the group of step s + 1 (its table is built there)
       const uint32_t* par = reinterpret_cast<const uint32_t*>(st + kParamOff);
-      build(cur ^ 1, par[c], par[64 + c]);
+      psb = par[c];
+      pab = par[64 + c];
     }
     // weight fragments: codes 8 kb .. 8 kb + 7 of the lane's 32, via the row table
-    const uint32_t tbase = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>(tab_wave + (cur * SK_ROWS + c) * TE));
+    const uint32_t tkey = static_cast<uint32_t>(tswz << 1) | static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>(tab_wave + c * TE));
     u32x4 fb[4];
     {
       typedef __attribute__((address_space(3))) const uint16_t lds_u16;
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
         } else {
           v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 1);
         }
-        return (v & kMask2) | tbase;
+        return (v & kMask2) ^ tkey;            // ((field ^ tswz) << 1) | row base
       };
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -267,7 +277,6 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
       for (int j = 0; j < MB; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[kb][j], __builtin_bit_cast(f16x8, fb[kb]),
                                                         acc[j], 0, 0, 0);
-    if (gnext) cur ^= 1;
   }
   // the row's level scale back (this lane's output column)
 #pragma unroll
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
   __builtin_amdgcn_s_waitcnt(0);                // loads past the range target stages nobody reads
   __syncthreads();
 
-  // ---- sum of the four waves' partial tiles, in wave order ----
+  // ---- sum of the eight waves' partial tiles, in wave order ----
   // D element (row m of activation block j, column n): lane n + 32 ((m / 4) % 2),
   // register 4 (m / 8) + m % 4.
   float* red = reinterpret_cast<float*>(smem);  // [wave][j][e][lane]
@@ -288,8 +297,8 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
   __syncthreads();
   const int t = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < 4 * MB; ++k) {
-    const int o = t + 256 * k;                  // o = 32 m + n over 32 MB activation rows
+  for (int k = 0; k < 16 * MB / SK_WAVES; ++k) {
+    const int o = t + 64 * SK_WAVES * k;        // o = 32 m + n over 32 MB activation rows
     const int n = o & 31, m = o >> 5;
     const int j = m >> 5, mm = m & 31;
     const int l = n + 32 * ((mm >> 2) & 1), e = 4 * (mm >> 3) + (mm & 3);
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(256, 1) void k_skinny(TiledParams p) {
 
 bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   if (bits != 3 && bits != 4) return false;
-  if (M < 1 || M > 64 || K % SK_K != 0 || K / SK_K < SK_WAVES) return false;
+  if (M < 1 || M > 64 || K % SK_K != 0 || K / SK_K < 8) return false;   // a step per wave
   if (group % SK_K != 0) return false;
   if (64 * K * 2 >= (int64_t{1} << 32)) return false;   // activation offsets of 64 rows
   if ((N + SK_ROWS) * K * bits / 8 >= (int64_t{1} << 32)) return false;
@@ -312,23 +321,26 @@ bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   return (N + SK_ROWS - 1) / SK_ROWS <= INT32_MAX;
 }
 
-template <int B, int MB>
+template <int B, int MB, int W>
 static hipError_t launch_skinny_k(const TiledParams& p, hipStream_t st) {
-  auto kern = k_skinny<B, MB>;
-  constexpr size_t lds = sk_lds_bytes<B, MB>();
+  auto kern = k_skinny<B, MB, W>;
+  constexpr size_t lds = sk_lds_bytes<B, MB, W>();
   static_assert(lds <= 160 * 1024, "one compute unit's LDS");
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
   if (e != hipSuccess) return e;
   const unsigned grid = static_cast<unsigned>((p.N + SK_ROWS - 1) / SK_ROWS);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
+constexpr int kSkWaves = 8;                     // two waves per SIMD (measured faster than four per workgroup)
+
 hipError_t launch_skinny_a16(const TiledParams& p, int bits, hipStream_t st) {
-  if (bits == 3) return p.M <= 32 ? launch_skinny_k<3, 1>(p, st) : launch_skinny_k<3, 2>(p, st);
-  return p.M <= 32 ? launch_skinny_k<4, 1>(p, st) : launch_skinny_k<4, 2>(p, st);
+  if (bits == 3)
+    return p.M <= 32 ? launch_skinny_k<3, 1, kSkWaves>(p, st) : launch_skinny_k<3, 2, kSkWaves>(p, st);
+  return p.M <= 32 ? launch_skinny_k<4, 1, kSkWaves>(p, st) : launch_skinny_k<4, 2, kSkWaves>(p, st);
 }
 
 }  // namespace cubic
