@@ -82,14 +82,22 @@ struct DecodeTable {
   static constexpr float kLevelUnit = 1.0f;
   __host__ __device__ static int slot_to_code(int slot) { return slot; }
   __host__ __device__ static int code_to_slot(int c) { return c; }
+  // Rows of a wave's tables are 2^B / 2 LDS words apart, so rows n and
+  // n + 64 / 2^B share banks, and skewed code distributions (most fields near
+  // zero) make their lanes collide. Entry f of row n is therefore stored at
+  // f ^ swizzle(n), which spreads those rows over different words.
+  __host__ __device__ static constexpr int swizzle(int n) {
+    return (1 << BITS) > 64 ? 0 : 2 * ((n / (64 >> BITS)) % ((1 << BITS) / 2));
+  }
   // tab: this lane's row table (2^B fp16 entries), aligned to its own size, so
-  // the byte address of entry f is tab | (f << 1): two ALU ops per code (shift,
-  // and-or). The two entries of a pair load straight into the low and high
-  // halves of r[p] (ds_read_u16_d16 / _d16_hi).
-  __device__ static void decode(const uint32_t* w, const uint16_t* tab, uint32_t* r) {
+  // the byte address of entry f is tab | ((f ^ swz) << 1): two ALU ops per code
+  // (shift, and-xor). The two entries of a pair load straight into the low and
+  // high halves of r[p] (ds_read_u16_d16 / _d16_hi).
+  __device__ static void decode(const uint32_t* w, const uint16_t* tab, int swz, uint32_t* r) {
     typedef __attribute__((address_space(3))) const uint16_t lds_u16;
     typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
-    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab));
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab)) |
+                          (static_cast<uint32_t>(swz) << 1);
     constexpr uint32_t kMask2 = ((1u << BITS) - 1u) << 1;
     auto addr = [&](int i) {
       const int bit = i * BITS;
@@ -102,7 +110,7 @@ struct DecodeTable {
       } else {
         v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 1);
       }
-      return (v & kMask2) | base;
+      return (v & kMask2) ^ base;
     };
 #pragma unroll
     for (int p = 0; p < 16; ++p) {

@@ -34,18 +34,19 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
   if constexpr (!IsW2<Dec>::value) {
     constexpr int B = Dec::kBits;
     uint16_t* t = tab_wave + nl * (1 << B);
+    const int swz = Dec::swizzle(nl);           // entry v of row nl sits at v ^ swz
     if constexpr (B <= 4) {
       // fp32 levels (exact products, a few ulps; see table_entry_f32)
       const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab & 0xffffu)));
       const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab >> 16)));
 #pragma unroll
-      for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry_f32(a, b, static_cast<uint32_t>(v), B);
+      for (int v = kb; v < (1 << B); v += 4) t[v ^ swz] = table_entry_f32(a, b, static_cast<uint32_t>(v), B);
     } else {
       // wide codes (integers up to 2^21 in the level terms): fp64, in a rolled loop
       const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
       const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
 #pragma unroll 1
-      for (int v = kb; v < (1 << B); v += 4) t[v] = table_entry(a, b, static_cast<uint32_t>(v), B);
+      for (int v = kb; v < (1 << B); v += 4) t[v ^ swz] = table_entry(a, b, static_cast<uint32_t>(v), B);
     }
     wave_lds_order();
   }
@@ -177,7 +178,7 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
     if constexpr (IsW2<Dec>::value) {
       DecodeW2::fast(&w[h * B], r);
     } else {
-      Dec::decode(&w[h * B], c.tab_wave + nl * (1 << B), r);
+      Dec::decode(&w[h * B], c.tab_wave + nl * (1 << B), Dec::swizzle(nl), r);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
