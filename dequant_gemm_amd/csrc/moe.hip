@@ -12,6 +12,8 @@
 // Invalid ids are counted in hdr[0] and their output rows zeroed. No host sync.
 // k_moe_gemv: one workgroup per (touched expert, 16-row tile); the expert's
 // pairs form the activation rows of the MFMA tile (up to two per pass).
+#include <algorithm>
+
 #include "gemv_core.h"
 #include "launch.h"
 
@@ -248,27 +250,34 @@ __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
   }
 }
 
-// Persistent variant: each workgroup walks units (touched expert, 16-row tile,
-// pass of MT pairs) with a grid stride, and while it computes one unit its
-// lanes already have the next unit's loads in flight: every lane refills the
-// code slot of macro step t with the next unit's macro step t right after
-// consuming it, and the next unit's group parameters and activation rows are
-// fetched one unit ahead into registers. So the memory pipe never drains at a
-// unit boundary. Needs te - tb <= PM for every wave (one slot per macro step)
+// Persistent variant: the items (touched expert, 16-row tile) are dealt to the
+// workgroups in runs of `run` consecutive items, round robin, and each item
+// is taken in passes of MT pairs. Within a run the units mostly share an expert
+// and its token set, so the staged activation rows are reused (their loads are
+// issued only when the token set changes); across the grid the workgroups stay
+// within a window of gridDim.x runs, which keeps the pages and DRAM rows in use
+// at any time few. While it computes
+// one unit its lanes already have the next unit's loads in flight: every lane
+// refills the code slot of macro step t with the next unit's macro step t right
+// after consuming it, and the next unit's group parameters (and activation rows,
+// when they change) are fetched one unit ahead into registers. So the memory
+// pipe never drains at a unit boundary. Needs te - tb <= PM for every wave (one slot per macro step)
 // and at most 4 * GPR groups per wave. OCC workgroups per compute unit.
 template <class Dec, int SPL, int PM, int MT, int GPR, int OCC>
 __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
                                                          const int32_t* __restrict__ erec,
                                                          const int32_t* __restrict__ sorted,
-                                                         float* __restrict__ y) {
-  static_assert(MT == 1 || MT == 2, "one or two activation rows per pass");
+                                                         float* __restrict__ y, unsigned run) {
+  static_assert(MT == 1 || MT == 2 || MT == 4, "one, two or four activation rows per pass");
   extern __shared__ __align__(1024) unsigned char smem[];   // table rows rely on this alignment
   constexpr int B = Dec::kBits;
   constexpr int DW = B * SPL;
   constexpr int XB = 2;
   const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
   const unsigned items = static_cast<unsigned>(p.hdr[1]) * tiles;
-  if (blockIdx.x >= items) return;
+  // this workgroup's runs start at run * (blockIdx.x + j * gridDim.x)
+  unsigned run_beg = run * blockIdx.x;
+  if (run_beg >= items) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
@@ -305,9 +314,12 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
     // wave-uniform indices (readfirstlane) make these scalar loads, which do
     // not wait behind the vector loads in flight
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      u.pr[m] = mt == 0 ? (m == 0 ? rec[3] : rec[4])
-                        : sorted[__builtin_amdgcn_readfirstlane(u.beg + mt + (m < u.M ? m : 0))];
+    for (int m = 0; m < MT; ++m) {
+      // rows past the pass's M repeat its first pair (their loads are cache hits)
+      const int mm = m < u.M ? m : 0;
+      u.pr[m] = mt == 0 && mm < 2 ? (mm == 0 ? rec[3] : rec[4])
+                                  : sorted[__builtin_amdgcn_readfirstlane(u.beg + mt + mm)];
+    }
     return u;
   };
   auto load_rec = [&](unsigned it) {
@@ -354,8 +366,8 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
   };
 
   // first unit: everything issued now
-  i32x8 rec = load_rec(blockIdx.x);
-  Unit cur = make_unit(blockIdx.x, 0, rec);
+  i32x8 rec = load_rec(run_beg);
+  Unit cur = make_unit(run_beg, 0, rec);
   issue_gp(cur);
   set_x(cur);
   xst.issue(xv, nblk, lane);
@@ -399,7 +411,11 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
     if (cur.mt + MT < cur.cnt) {
       nxt = make_unit(cur.it, cur.mt + MT, rec);
     } else {
-      const unsigned it_n = __builtin_amdgcn_readfirstlane(cur.it + gridDim.x);
+      unsigned it_n = cur.it + 1;
+      if (it_n == run_beg + run) {             // wave-uniform: on to the next run
+        run_beg += run * gridDim.x;
+        it_n = run_beg;
+      }
       has_next = it_n < items;
       if (has_next) {
         rec = load_rec(it_n);
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
 #pragma unroll
     for (int m = 0; m < MT; ++m)
       same_x = same_x && (m >= cur.M || nxt.pr[m] / p.topk == cur.pr[m] / p.topk);
-    xst.issue(xv, nblk, lane);               // unconditional (cache hits when unchanged)
+    if (!same_x) xst.issue(xv, nblk, lane);  // wave-uniform
     __builtin_amdgcn_sched_barrier(0);
 
     // stream the current unit; each slot is refilled with the next unit's step
@@ -450,7 +466,9 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
     if (tt < cur.M * 16) {
       const int m = tt >> 4, cc = tt & 15;
       if (cur.n0 + cc < p.N) {
-        const int qp = MT == 1 || m == 0 ? cur.pr[0] : cur.pr[MT - 1];
+        int qp = cur.pr[0];
+#pragma unroll
+        for (int k = 1; k < MT; ++k) qp = m == k ? cur.pr[k] : qp;
         float v = red[(0 * 16 + m) * 16 + cc];
         v += red[(1 * 16 + m) * 16 + cc];
         v += red[(2 * 16 + m) * 16 + cc];
@@ -508,23 +526,33 @@ template <int PM, int GPR>
 static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, int tokens,
                                       hipStream_t st) {
   const GemvGeom geo = gemv_geom(p.K, p.group, 2);
-  int mt = tokens <= 1 ? 1 : 2;
+  // Rows per pass: one token routes one row; with several, four rows per pass
+  // (fewer passes, so fewer decodes and code re-reads, for experts picked by
+  // more tokens), or two when four do not fit two workgroups' LDS.
+  int mt = tokens <= 1 ? 1 : 4;
+  if (mt == 4 && moe_lds_bytes<DecodeW2>(geo, 4) > 80 * 1024) mt = 2;
   if (mt == 2 && moe_lds_bytes<DecodeW2>(geo, 2) > 80 * 1024) mt = 1;
   const size_t lds = moe_lds_bytes<DecodeW2>(geo, mt);
-  // two rows per pass need more registers: two workgroups per compute unit
-  auto kern = mt == 1 ? k_moe_stream<DecodeW2, 2, PM, 1, GPR, 3> : k_moe_stream<DecodeW2, 2, PM, 2, GPR, 2>;
+  // several rows per pass need more registers: two workgroups per compute unit
+  auto kern = mt == 1 ? k_moe_stream<DecodeW2, 2, PM, 1, GPR, 3>
+                      : (mt == 2 ? k_moe_stream<DecodeW2, 2, PM, 2, GPR, 2>
+                                 : k_moe_stream<DecodeW2, 2, PM, 4, GPR, 2>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  // the resident workgroups walk the units
+  // the resident workgroups walk the units, in runs of up to 8 items when there
+  // are enough items for every workgroup
   const int64_t cus = device_cu_count();
   const int64_t occ = mt == 1 ? 3 : 2;
   const int64_t cap = (cus > 0 ? cus : 256) * occ;
-  const unsigned grid = static_cast<unsigned>(blocks < cap ? blocks : cap);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p, p.erec, p.sorted, p.y);
+  const int64_t run = std::max<int64_t>(1, std::min<int64_t>(8, blocks / cap));
+  const int64_t want = (blocks + run - 1) / run;
+  const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p, p.erec, p.sorted, p.y,
+                     static_cast<unsigned>(run));
   return hipGetLastError();
 }
 

@@ -70,6 +70,23 @@ def test_skewed_routing_and_invalid_ids():
     assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
 
 
+@pytest.mark.parametrize("K", [1024, 7168])
+def test_pass_remainders(K):
+    # expert e is picked by e + 1 pairs (1..9): every remainder of the passes
+    # that take an expert's pairs several rows at a time, ragged N
+    say(f"MoE pass remainders W2 G512 K={K}")
+    E, N, bits, group = 9, 130, 2, 512
+    T = E * (E + 1) // 2
+    pool = _pool(E, N, K, bits, group, seed=55)
+    x, _ = synth.moe_routing(seed=56, T=T, E=E, topk=1, K=K, device=DEV)
+    ids = torch.tensor([e for e in range(E) for _ in range(e + 1)], dtype=torch.int32)
+    ids = ids[torch.randperm(T, generator=torch.Generator().manual_seed(57))].reshape(T, 1).to(DEV)
+    y = cq.cubic_moe_grouped_gemm(x, ids, pool, E).cpu().numpy()
+    ref = oracle.moe_a16(x_bits(x), ids.cpu().numpy(), E, N,
+                         lambda e: _expert_dense(e, N, K, bits, group, 55))
+    assert row_rel_err(y.reshape(T, N), ref.reshape(T, N)) <= TOL
+
+
 def test_full_pool_sampled_pairs():
     """896 experts of gate_up 6144 x 7168 W2 G512, 64 tokens x top-16."""
     say("MoE full pool 896 x 6144x7168 W2 G512, T=64 top-16 (sampled pairs)")
