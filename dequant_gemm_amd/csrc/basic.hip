@@ -101,57 +101,116 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ st
   for (int q = 0; q < 8; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
-// Per-row INT8 quantisation, one 256-thread block per row (two passes over the
-// row; the second pass hits L2). Division is IEEE fp32 (__fdiv_rn), rounding is
-// rintf (ties to even), as the msModelSlim article's per-token dynamic scheme
-// and this library's reading of the A8 scale (amax / 127) prescribe.
-__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ x, int64_t K,
-                                                   int8_t* __restrict__ xq,
-                                                   float* __restrict__ xs) {
-  const int64_t m = blockIdx.x;
-  const uint16_t* row = x + m * K;
-  int8_t* qrow = xq + m * K;
-  const int tid = threadIdx.x;
-  const int64_t nvec = K / 8;                   // K is a multiple of 8 (checked on the host)
-  const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-  float amax = 0.0f;
-  for (int64_t i = tid; i < nvec; i += 256) {
-    const u32x4 v = rv[i];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+// Per-row INT8 quantisation (the msModelSlim article's per-token dynamic scheme,
+// with this library's reading of the A8 scale): sx = fp32(amax / 127) and
+// q = clamp(rne(fp32(x / sx)), -127, 127), bit for bit.
+//
+// The quotient is not formed per element. With r = v_rcp_f32(sx) (1 ulp),
+// x * r is within 2^-16 of x / sx for |x| <= amax, and the IEEE quotient within
+// 2^-18, so whenever x * r lies more than 2^-14 from every half-integer both
+// round to the same integer. One fma against 1.5 * 2^23 rounds x * r to the
+// nearest integer n (ties to even) and leaves n in the low byte of its bits;
+// a second fma gives the residual x * r - n. Lanes with a residual within 2^-14
+// of one half, and rows whose scale lies outside [2^-100, 2^100] (tiny or huge
+// rows, where the bound or the reciprocal fails), take the IEEE division.
+constexpr float kRneMagic = 12582912.0f;        // 1.5 * 2^23
+
+// Eight bf16 values (one 16-byte vector) to eight int8 codes.
+__device__ __forceinline__ uint2 quant8(const u32x4& v, float sx, float rcp, bool fast) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  float xv[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(u[q] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
+  for (int q = 0; q < 4; ++q) {
+    xv[2 * q] = __uint_as_float(u[q] << 16);
+    xv[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+  }
+  uint32_t f[8];
+  bool exact = !fast;
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = fmaf(xv[e], rcp, kRneMagic);
+      const float n = y - kRneMagic;                 // exact: the rounded integer
+      const float t = fmaf(xv[e], rcp, -n);          // x * r - n, one rounding
+      exact = exact || fabsf(t) > 0.5f - 0x1p-14f;
+      f[e] = __float_as_uint(y);                     // low byte: n (two's complement)
     }
   }
-  __shared__ float red[4];
+  if (exact) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int qi = 0;
+      if (sx != 0.0f) {
+        float r = rintf(__fdiv_rn(xv[e], sx));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        qi = static_cast<int>(r);
+      }
+      f[e] = static_cast<uint32_t>(qi);
+    }
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(f[1], f[0], 0x0c0c0400u) | __builtin_amdgcn_perm(f[3], f[2], 0x04000c0cu);
+  const uint32_t hi = __builtin_amdgcn_perm(f[5], f[4], 0x0c0c0400u) | __builtin_amdgcn_perm(f[7], f[6], 0x04000c0cu);
+  return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ float absmax8(const u32x4& v, float a) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    a = fmaxf(a, fabsf(__uint_as_float(u[q] << 16)));
+    a = fmaxf(a, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
+  }
+  return a;
+}
+
+// Row maximum over the block's 256 threads; returns sx, written by thread 0.
+__device__ __forceinline__ float row_scale(float amax, float* red, float* xs_m) {
   amax = wave_max(amax);
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sx = __fdiv_rn(amax, 127.0f);
-  if (tid == 0) xs[m] = sx;
-  uint2* qv = reinterpret_cast<uint2*>(qrow);
-  for (int64_t i = tid; i < nvec; i += 256) {
-    const u32x4 v = rv[i];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[2] = {0u, 0u};
+  if (threadIdx.x == 0) *xs_m = sx;
+  return sx;
+}
+
+// One 256-thread block per row. V > 0: the row (at most 256 * V vectors of 8)
+// is read once into registers, all of its loads in flight together. V == 0:
+// rows of any length, two passes (the second hits L2).
+template <int V>
+__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ x, int64_t K,
+                                                   int8_t* __restrict__ xq,
+                                                   float* __restrict__ xs) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nvec = K / 8;                   // K is a multiple of 8 (checked on the host)
+  const u32x4* rv = reinterpret_cast<const u32x4*>(x + m * K);
+  uint2* qv = reinterpret_cast<uint2*>(xq + m * K);
+  float amax = 0.0f;
+  if constexpr (V > 0) {
+    u32x4 v[V];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float xv = __uint_as_float(h ? (u[q] & 0xffff0000u) : (u[q] << 16));
-        int qi = 0;
-        if (sx != 0.0f) {
-          float r = rintf(__fdiv_rn(xv, sx));
-          r = fminf(fmaxf(r, -127.0f), 127.0f);
-          qi = static_cast<int>(r);
-        }
-        const int e = 2 * q + h;                // element 0..7 of the vector
-        o[e >> 2] |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * (e & 3));
-      }
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = tid + 256 * j;
+      v[j] = i < nvec ? rv[i] : u32x4{0u, 0u, 0u, 0u};
     }
-    qv[i] = make_uint2(o[0], o[1]);
+#pragma unroll
+    for (int j = 0; j < V; ++j) amax = absmax8(v[j], amax);
+    const float sx = row_scale(amax, red, xs + m);
+    const bool fast = sx >= 0x1p-100f && sx <= 0x1p100f;
+    const float rcp = __builtin_amdgcn_rcpf(sx);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = tid + 256 * j;
+      if (i < nvec) qv[i] = quant8(v[j], sx, rcp, fast);
+    }
+  } else {
+    for (int64_t i = tid; i < nvec; i += 256) amax = absmax8(rv[i], amax);
+    const float sx = row_scale(amax, red, xs + m);
+    const bool fast = sx >= 0x1p-100f && sx <= 0x1p100f;
+    const float rcp = __builtin_amdgcn_rcpf(sx);
+    for (int64_t i = tid; i < nvec; i += 256) qv[i] = quant8(rv[i], sx, rcp, fast);
   }
 }
 
@@ -234,7 +293,11 @@ hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                             hipStream_t st) {
-  hipLaunchKernelGGL(k_act_quant, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xq, xs);
+  // registers per thread: the row's vectors over 256 threads, in steps of powers of two
+  const int64_t per = (K / 8 + 255) / 256;
+  auto kern = per <= 1 ? k_act_quant<1> : per <= 2 ? k_act_quant<2> : per <= 4 ? k_act_quant<4>
+                                        : per <= 8 ? k_act_quant<8> : k_act_quant<0>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xq, xs);
   return hipGetLastError();
 }
 

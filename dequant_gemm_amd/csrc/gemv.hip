@@ -107,8 +107,10 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
 
 // Activations for the prepared (multi-kernel) paths, one 256-thread block per
 // row. W2 order: raw bf16 in the 2-bit decoder's slot order, xback = 1.
-// Otherwise: per-row power-of-two prescale and fp16 in natural order.
-template <bool W2ORDER>
+// Otherwise: per-row power-of-two prescale and fp16 in natural order; with
+// V > 0 the row (at most 256 * V vectors of 8) is read once into registers,
+// with V == 0 (longer rows) twice, the second pass hitting L2.
+template <bool W2ORDER, int V>
 __global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, int64_t K,
                                                uint16_t* __restrict__ xp,
                                                float* __restrict__ xback) {
@@ -136,26 +138,17 @@ __global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, i
   } else {
     const int64_t nvec = K / 8;
     const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-    float amax = 0.0f;
-    for (int64_t i = tid; i < nvec; i += 256) {
-      const u32x4 v = rv[i];
+    u32x4* ov = reinterpret_cast<u32x4*>(out);
+    auto absmax8 = [](const u32x4& v, float a) {
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        amax = fmaxf(amax, fabsf(__uint_as_float(u[q] << 16)));
-        amax = fmaxf(amax, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
+        a = fmaxf(a, fabsf(__uint_as_float(u[q] << 16)));
+        a = fmaxf(a, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
       }
-    }
-    __shared__ float red[4];
-    amax = wave_max(amax);
-    if ((tid & 63) == 0) red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float back;
-    const int sh = row_prescale(amax, &back);
-    if (tid == 0) xback[m] = back;
-    for (int64_t i = tid; i < nvec; i += 256) {
-      const u32x4 v = rv[i];
+      return a;
+    };
+    auto to_f16 = [](const u32x4& v, int sh) {
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
       uint32_t o[4];
 #pragma unroll
@@ -164,7 +157,39 @@ __global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, i
         const uint32_t e1 = f16_bits(ldexpf(__uint_as_float(u[h] & 0xffff0000u), sh));
         o[h] = e0 | (e1 << 16);
       }
-      reinterpret_cast<u32x4*>(out)[i] = u32x4{o[0], o[1], o[2], o[3]};
+      return u32x4{o[0], o[1], o[2], o[3]};
+    };
+    __shared__ float red[4];
+    auto prescale = [&](float amax) {
+      amax = wave_max(amax);
+      if ((tid & 63) == 0) red[tid >> 6] = amax;
+      __syncthreads();
+      amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      float back;
+      const int sh = row_prescale(amax, &back);
+      if (tid == 0) xback[m] = back;
+      return sh;
+    };
+    float amax = 0.0f;
+    if constexpr (V > 0) {
+      u32x4 v[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int64_t i = tid + 256 * j;
+        v[j] = i < nvec ? rv[i] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) amax = absmax8(v[j], amax);
+      const int sh = prescale(amax);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int64_t i = tid + 256 * j;
+        if (i < nvec) ov[i] = to_f16(v[j], sh);
+      }
+    } else {
+      for (int64_t i = tid; i < nvec; i += 256) amax = absmax8(rv[i], amax);
+      const int sh = prescale(amax);
+      for (int64_t i = tid; i < nvec; i += 256) ov[i] = to_f16(rv[i], sh);
     }
   }
 }
@@ -258,12 +283,13 @@ hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st) 
 
 hipError_t launch_xprep(const uint16_t* x, int64_t M, int64_t K, bool w2_order, uint16_t* xp,
                         float* xback, hipStream_t st) {
-  if (w2_order)
-    hipLaunchKernelGGL(k_xprep<true>, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xp,
-                       xback);
-  else
-    hipLaunchKernelGGL(k_xprep<false>, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xp,
-                       xback);
+  // fp16 prescale: registers per thread, the row's vectors over 256 threads in
+  // steps of powers of two
+  const int64_t per = (K / 8 + 255) / 256;
+  auto kern = w2_order ? k_xprep<true, 0>
+              : per <= 1 ? k_xprep<false, 1> : per <= 2 ? k_xprep<false, 2>
+              : per <= 4 ? k_xprep<false, 4> : per <= 8 ? k_xprep<false, 8> : k_xprep<false, 0>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xp, xback);
   return hipGetLastError();
 }
 

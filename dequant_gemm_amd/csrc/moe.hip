@@ -543,12 +543,19 @@ static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, in
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  // the resident workgroups walk the units, in runs of up to 8 items when there
-  // are enough items for every workgroup
+  // The resident workgroups walk the units in runs of up to 8 items: the
+  // longest run that keeps the busiest workgroup's item count (for the largest
+  // possible item count) lowest.
   const int64_t cus = device_cu_count();
   const int64_t occ = mt == 1 ? 3 : 2;
   const int64_t cap = (cus > 0 ? cus : 256) * occ;
-  const int64_t run = std::max<int64_t>(1, std::min<int64_t>(8, blocks / cap));
+  int64_t run = 1, best = INT64_MAX;
+  for (int64_t r = 8; r >= 1; --r) {
+    const int64_t runs = (blocks + r - 1) / r;
+    const int64_t g = std::min(runs, cap);
+    const int64_t span = (runs + g - 1) / g * r;
+    if (span < best) { best = span; run = r; }
+  }
   const int64_t want = (blocks + run - 1) / run;
   const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p, p.erec, p.sorted, p.y,

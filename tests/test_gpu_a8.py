@@ -41,6 +41,39 @@ def test_act_quant_bit_exact(M, K):
     assert np.array_equal(xq.cpu().numpy(), xq_ref)
 
 
+def _quant_rows(K, seed):
+    """Rows that exercise each rounding path of the quantiser: exact ties (scale
+    1), near-ties at a random scale, scales below 2^-100, above 2^100 and
+    denormal, a zero row and a single nonzero element."""
+    g = torch.Generator().manual_seed(seed)
+    rows = torch.zeros((8, K), dtype=torch.float64)
+    rows[0] = torch.randn(K, generator=g, dtype=torch.float64)
+    k = torch.arange(K, dtype=torch.float64) % 127
+    sign = torch.where(torch.arange(K) % 2 == 0, 1.0, -1.0).to(torch.float64)
+    rows[1] = sign * (k + 0.5)
+    rows[1, 0] = 127.0
+    s = float(torch.exp(torch.randn(1, generator=g, dtype=torch.float64)))
+    delta = (torch.rand(K, generator=g, dtype=torch.float64) - 0.5) * 2e-3
+    rows[2] = sign * (k + 0.5 + delta) * s
+    rows[2, 0] = 127.0 * s
+    rows[3] = torch.randn(K, generator=g, dtype=torch.float64) * 1e-32
+    rows[4] = torch.randn(K, generator=g, dtype=torch.float64) * 1e33
+    rows[5] = torch.randn(K, generator=g, dtype=torch.float64) * 1e-38
+    rows[7, K // 3] = -3.0
+    return rows.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("K", [8, 2048, 2056, 7168, 16384, 16392])
+def test_act_quant_rounding_paths(K):
+    # K spans one to eight 16-byte vectors per thread and the two-pass fallback
+    say(f"act_quant rounding paths K={K}")
+    xb = _quant_rows(K, seed=K)
+    xq, sx = cq.act_quant_int8_per_token(xb.to(DEV))
+    xq_ref, sx_ref = oracle.act_quant(x_bits(xb))
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
 def _check_a8(w, x, rows=None):
     cw = upload(w)
     xq, sx = cq.act_quant_int8_per_token(x.to(DEV))
