@@ -153,7 +153,13 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
   // the small-batch MFMA kernel
   const bool use_gemv = M <= kGemvMaxM && gemv_supported(w->K, w->bits, w->group);
   const bool use_skinny = !use_gemv && skinny_supported(M, w->N, w->K, w->bits, w->group);
-  hipError_t e = launch_xprep(x_bf16, M, w->K, use_gemv && w->bits == 2, xp, xback, s);
+  if (use_gemv && w->bits > 2) {
+    // 3- to 8-bit codes: the GEMV reads the bf16 rows as they are (split bf16 levels)
+    GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
+                 x_bf16, nullptr, nullptr, y};
+    return hip_status(launch_gemv(p, w->bits, false, s));
+  }
+  hipError_t e = launch_xprep(x_bf16, M, w->K, use_gemv, xp, xback, s);
   if (e != hipSuccess) return CUBIC_ERR_HIP;
   if (use_gemv) {
     GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),

@@ -32,6 +32,7 @@ namespace cubic {
 struct DecodeW2 {
   static constexpr int kBits = 2;
   static constexpr bool kBf16 = true;
+  static constexpr bool kSplit = false;
   static constexpr float kLevelUnit = 0.5f;   // decoded value * s * 0.5 = weight
 
   __host__ __device__ static int slot_to_code(int slot) {
@@ -79,6 +80,7 @@ template <int BITS>
 struct DecodeTable {
   static constexpr int kBits = BITS;
   static constexpr bool kBf16 = false;
+  static constexpr bool kSplit = false;
   static constexpr float kLevelUnit = 1.0f;
   __host__ __device__ static int slot_to_code(int slot) { return slot; }
   __host__ __device__ static int code_to_slot(int c) { return c; }
@@ -134,7 +136,7 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
 // a X and b Y are exact fp32 products of fp16 values, so
 // Q = j^3 + a X + b Y rounds twice in fp32, then once more by 1/K^3, before the
 // fp16 rounding: a few fp32 ulps, far inside the products' tolerance.
-__device__ __forceinline__ uint16_t table_entry_f32(float a, float b, uint32_t v, int bits) {
+__device__ __forceinline__ float table_level_f32(float a, float b, uint32_t v, int bits) {
   const int k = sign_extend(v, bits);
   const int j = k < 0 ? -k : k;
   const int km = kmax_of(bits);
@@ -142,16 +144,84 @@ __device__ __forceinline__ uint16_t table_entry_f32(float a, float b, uint32_t v
   const float Y = static_cast<float>(j * j * km - j * j * j);
   const float q = fmaf(a, X, fmaf(b, Y, static_cast<float>(j * j * j))) *
                   (1.0f / static_cast<float>(km * km * km));
-  return f16_bits(k < 0 ? -q : q);
+  return k < 0 ? -q : q;
 }
 
-__device__ __forceinline__ uint16_t table_entry(double a, double b, uint32_t v, int bits) {
+__device__ __forceinline__ uint16_t table_entry_f32(float a, float b, uint32_t v, int bits) {
+  return f16_bits(table_level_f32(a, b, v, bits));
+}
+
+// Wide codes: the level in fp64 (integers up to 2^21 in its terms), as fp32.
+__device__ __forceinline__ float table_level(double a, double b, uint32_t v, int bits) {
   const int k = sign_extend(v, bits);
   const int j = k < 0 ? -k : k;
   const int km = kmax_of(bits);
   const double K = static_cast<double>(km);
   const float q = static_cast<float>(level_numerator(a, b, j, km) * (1.0 / (K * K * K)));
-  return f16_bits(k < 0 ? -q : q);
+  return k < 0 ? -q : q;
 }
+
+__device__ __forceinline__ uint16_t table_entry(double a, double b, uint32_t v, int bits) {
+  return f16_bits(table_level(a, b, v, bits));
+}
+
+// A level as two bf16 halves of one dword: hi = rne(q) in the low half,
+// lo = rne(q - hi) in the high half (hi + lo carries about 16 significant bits).
+__device__ __forceinline__ uint32_t split_bf16_pair(float q) {
+  const uint32_t hi = bf16_rne_bits(q);
+  const uint32_t lo = bf16_rne_bits(q - __uint_as_float(hi << 16));
+  return hi | (lo << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Any width, against raw bf16 activations: the per-row table holds every level
+// as a bf16 (hi, lo) pair in one dword (split_bf16_pair), so the activations
+// need neither a prescale nor a conversion. Natural order, level unit 1. A pair
+// of codes gives one hi fragment dword and one lo fragment dword (two v_perm),
+// and the chunk takes two bf16 MFMAs per fragment: sum x * hi + sum x * lo.
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct DecodeTableSplit {
+  static constexpr int kBits = BITS;
+  static constexpr bool kBf16 = true;
+  static constexpr bool kSplit = true;
+  static constexpr float kLevelUnit = 1.0f;
+  __host__ __device__ static int slot_to_code(int slot) { return slot; }
+  __host__ __device__ static int code_to_slot(int c) { return c; }
+  // Rows are 2^B LDS words apart; entry f of row n sits at f ^ swizzle(n) so
+  // that rows n and n + 32 / 2^B, which share banks, use different words.
+  __host__ __device__ static constexpr int swizzle(int n) {
+    return (1 << BITS) >= 32 ? 0 : (n / (32 >> BITS)) % (1 << BITS);
+  }
+  // tab: this lane's row table (2^B dwords), aligned to its own size: entry f
+  // is at byte tab | ((f ^ swz) << 2).
+  __device__ static void decode(const uint32_t* w, const uint32_t* tab, int swz, uint32_t* rhi,
+                                uint32_t* rlo) {
+    typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tab)) |
+                          (static_cast<uint32_t>(swz) << 2);
+    constexpr uint32_t kMask4 = ((1u << BITS) - 1u) << 2;
+    auto addr = [&](int i) {
+      const int bit = i * BITS;
+      const int d = bit >> 5, off = bit & 31;
+      uint32_t v;
+      if (off < 2) {
+        v = w[d] << (2 - off);
+      } else if (off + BITS <= 32) {
+        v = w[d] >> (off - 2);
+      } else {
+        v = __builtin_amdgcn_alignbit(w[d + 1], w[d], off - 2);
+      }
+      return (v & kMask4) ^ base;
+    };
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const uint32_t d0 = *reinterpret_cast<const lds_u32*>(static_cast<uintptr_t>(addr(2 * p)));
+      const uint32_t d1 = *reinterpret_cast<const lds_u32*>(static_cast<uintptr_t>(addr(2 * p + 1)));
+      rhi[p] = __builtin_amdgcn_perm(d1, d0, 0x05040100u);
+      rlo[p] = __builtin_amdgcn_perm(d1, d0, 0x07060302u);
+    }
+  }
+};
 
 }  // namespace cubic

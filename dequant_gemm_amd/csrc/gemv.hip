@@ -10,11 +10,14 @@
 // accumulation after the tile-local dot product). The waves' partial outputs
 // are summed in LDS in a fixed order, so results are deterministic.
 //
-// Activations: fp16 after a per-row power-of-two prescale (exact for bf16 in
-// range). With M <= 4 each wave prescales and converts its own K slice into
-// LDS (the prescale is per (row, wave) and is undone on the wave's partial
-// before the sum), so the whole product is one kernel. Larger M use x
-// prepared once by k_xprep (per-row prescale) and read from global memory.
+// Activations, M <= 4: each wave copies its own K slice into LDS (2-bit codes:
+// raw bf16; wider codes: fp16 after a power-of-two prescale per (row, wave),
+// exact for bf16 in range and undone on the wave's partial before the sum), so
+// the whole product is one kernel. 5 <= M <= 16, wider codes: the caller's bf16
+// rows are read from global memory as they are, against per-row tables of
+// split bf16 levels (hi + lo, two MFMAs per fragment; DecodeTableSplit), again
+// one kernel. 5 <= M <= 16, 2-bit codes: k_xprep reorders x once into the
+// decoder's slot order.
 #include "gemv_core.h"
 #include "launch.h"
 
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   c.abrow = reinterpret_cast<const uint32_t*>(p.shapes + nrow * gpr * 2);
   c.mpg = geo.mpg;
   c.tb = tb; c.te = te; c.nl = nl; c.kb = kb; c.M = M;
-  c.xrow = INK ? nullptr : p.xp + static_cast<int64_t>(nl < M ? nl : 0) * p.K;
+  c.xrow = INK ? nullptr : (Dec::kSplit ? p.x : p.xp) + static_cast<int64_t>(nl < M ? nl : 0) * p.K;
   c.xs_wave = xs_wave; c.nch_w = geo.nch_w; c.tab_wave = tab_wave;
   c.gp_wave = gp_wave; c.gmax = geo.gmax;
   f32x4 acc = gemv_core<Dec, INK, SPL, P, ALLIN>(c, issue_x, finish_x);
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
       float v = red[m * 16 + cc];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += red[(w * 16 + m) * 16 + cc];
-      if constexpr (!INK) v *= p.xback[m];
+      if constexpr (!INK && !Dec::kSplit) v *= p.xback[m];
       p.y[static_cast<int64_t>(m) * p.N + n0 + cc] = v;
     }
   }
@@ -266,18 +269,20 @@ hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st) 
                            : launch_gemv_t<DecodeW2, false, 2, 2>(p, st);
       return ink ? launch_gemv_t<DecodeW2, true, 1, 8>(p, st)
                  : launch_gemv_t<DecodeW2, false, 1, 4>(p, st);
+    // wider codes without in-kernel staging read the caller's bf16 rows
+    // directly against split bf16 levels (no preparation kernel)
     case 3: return ink ? launch_gemv_t<DecodeTable<3>, true, 1, 8>(p, st)
-                       : launch_gemv_t<DecodeTable<3>, false, 1, 4>(p, st);
+                       : launch_gemv_t<DecodeTableSplit<3>, false, 1, 4>(p, st);
     case 4: return ink ? launch_gemv_t<DecodeTable<4>, true, 1, 6>(p, st)
-                       : launch_gemv_t<DecodeTable<4>, false, 1, 4>(p, st);
+                       : launch_gemv_t<DecodeTableSplit<4>, false, 1, 4>(p, st);
     case 5: return ink ? launch_gemv_t<DecodeTable<5>, true, 1, 4>(p, st)
-                       : launch_gemv_t<DecodeTable<5>, false, 1, 2>(p, st);
+                       : launch_gemv_t<DecodeTableSplit<5>, false, 1, 2>(p, st);
     case 6: return ink ? launch_gemv_t<DecodeTable<6>, true, 1, 4>(p, st)
-                       : launch_gemv_t<DecodeTable<6>, false, 1, 2>(p, st);
+                       : launch_gemv_t<DecodeTableSplit<6>, false, 1, 2>(p, st);
     case 7: return ink ? launch_gemv_t<DecodeTable<7>, true, 1, 4>(p, st)
-                       : launch_gemv_t<DecodeTable<7>, false, 1, 2>(p, st);
+                       : launch_gemv_t<DecodeTableSplit<7>, false, 1, 2>(p, st);
     default: return ink ? launch_gemv_t<DecodeTable<8>, true, 1, 4>(p, st)
-                        : launch_gemv_t<DecodeTable<8>, false, 1, 2>(p, st);
+                        : launch_gemv_t<DecodeTableSplit<8>, false, 1, 2>(p, st);
   }
 }
 

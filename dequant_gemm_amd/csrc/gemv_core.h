@@ -31,7 +31,26 @@ template <> struct IsW2<DecodeW2> { static constexpr bool value = true; };
 
 template <class Dec>
 __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, uint32_t gab) {
-  if constexpr (!IsW2<Dec>::value) {
+  if constexpr (Dec::kSplit) {
+    // bf16 (hi, lo) pairs, one dword per entry
+    constexpr int B = Dec::kBits;
+    uint32_t* t = reinterpret_cast<uint32_t*>(tab_wave) + nl * (1 << B);
+    const int swz = Dec::swizzle(nl);
+    if constexpr (B <= 4) {
+      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab & 0xffffu)));
+      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab >> 16)));
+#pragma unroll
+      for (int v = kb; v < (1 << B); v += 4)
+        t[v ^ swz] = split_bf16_pair(table_level_f32(a, b, static_cast<uint32_t>(v), B));
+    } else {
+      const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
+      const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
+#pragma unroll 1
+      for (int v = kb; v < (1 << B); v += 4)
+        t[v ^ swz] = split_bf16_pair(table_level(a, b, static_cast<uint32_t>(v), B));
+    }
+    wave_lds_order();
+  } else if constexpr (!IsW2<Dec>::value) {
     constexpr int B = Dec::kBits;
     uint16_t* t = tab_wave + nl * (1 << B);
     const int swz = Dec::swizzle(nl);           // entry v of row nl sits at v ^ swz
@@ -55,7 +74,7 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
 // LDS bytes of the per-wave level tables.
 template <class Dec>
 __host__ __device__ constexpr int tab_bytes_per_wave() {
-  return IsW2<Dec>::value ? 0 : 16 * (1 << Dec::kBits) * 2;
+  return IsW2<Dec>::value ? 0 : 16 * (1 << Dec::kBits) * (Dec::kSplit ? 4 : 2);
 }
 
 // Per-wave state of the streaming loop.
@@ -87,7 +106,8 @@ struct CoreArgs {
   int tb, te;               // macro steps of this wave
   int nl, kb;               // lane coordinates (row in tile, chunk slot)
   int M;                    // valid activation rows in the MFMA tile (<= 16)
-  const uint16_t* xrow;     // prepared activation row of A-lane nl (global variant), chunk-major
+  const uint16_t* xrow;     // activation row of A-lane nl (global variant): prepared fp16, or
+                            // the caller's bf16 for split-level decoders
   const uint16_t* xs_wave;  // LDS activations of this wave (in-kernel variant), chunk-major
   int nch_w;                // chunks per row reserved in xs_wave
   uint16_t* tab_wave;       // LDS level tables of this wave (table decoders)
@@ -175,14 +195,25 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
       }
     }
     uint32_t r[16];
-    if constexpr (IsW2<Dec>::value) {
-      DecodeW2::fast(&w[h * B], r);
-    } else {
-      Dec::decode(&w[h * B], c.tab_wave + nl * (1 << B), Dec::swizzle(nl), r);
-    }
+    if constexpr (Dec::kSplit) {
+      uint32_t rl[16];
+      Dec::decode(&w[h * B], reinterpret_cast<const uint32_t*>(c.tab_wave) + nl * (1 << B),
+                  Dec::swizzle(nl), r, rl);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+      for (int j = 0; j < 4; ++j) {
+        st.part[j] = mfma16<true>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+        st.part[j] = mfma16<true>(av[j], u32x4{rl[4 * j], rl[4 * j + 1], rl[4 * j + 2], rl[4 * j + 3]}, st.part[j]);
+      }
+    } else {
+      if constexpr (IsW2<Dec>::value) {
+        DecodeW2::fast(&w[h * B], r);
+      } else {
+        Dec::decode(&w[h * B], c.tab_wave + nl * (1 << B), Dec::swizzle(nl), r);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+    }
     if constexpr (IsW2<Dec>::value) {
       const uint32_t* wv = &w[h * B];
       if (extra && __any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {

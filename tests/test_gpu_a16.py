@@ -108,11 +108,13 @@ def test_uniform_int_special_case_matches_integer_matmul():
     assert row_rel_err(y, ref) <= TOL
 
 
-def test_activation_range_extremes_and_zero_rows():
-    # rows far outside the fp16 range, tiny rows, an all-zero row
-    say("A16 activation range extremes")
+@pytest.mark.parametrize("bits,group", [(2, 512), (4, 128)])
+def test_activation_range_extremes_and_zero_rows(bits, group):
+    # rows far outside the fp16 range, tiny rows, an all-zero row (M = 12 takes
+    # the raw-bf16 GEMV for 4-bit codes)
+    say(f"A16 activation range extremes bits={bits}")
     g = synth.make_generator(88)
-    w = synth.make_weight(g, 96, 1024, 2, 512, "ternary", 0.015)
+    w = synth.make_weight(g, 96, 1024, bits, group, "ternary" if bits == 2 else "uniform", 0.015)
     cw = upload(w)
     for M in (4, 12, 130):
         x = torch.randn((M, 1024), generator=g).float()
@@ -122,7 +124,7 @@ def test_activation_range_extremes_and_zero_rows():
         xb = x.to(torch.bfloat16)
         y = cq.cubic_gemm_a16(xb.to(DEV), cw).cpu().numpy()
         codes, scales, shapes = np_weight(w)
-        ref = oracle.gemm_a16(x_bits(xb), oracle.dequant(codes, scales, shapes, 2, 512))
+        ref = oracle.gemm_a16(x_bits(xb), oracle.dequant(codes, scales, shapes, bits, group))
         assert np.all(y[2] == 0.0)
         assert row_rel_err(y, ref) <= TOL
 
