@@ -99,11 +99,15 @@ int cubic_dequant(const cubic_weight* w, float* out, cubic_stream_t stream);
 
 /* A16 product y[M][N] = x[M][K] * W^T, x in bf16 (bit patterns), y in fp32.
  * For 2-bit weights x is used in bf16 as is (the valid levels are -s, 0, s, so
- * every product is exact before the fp32 group scaling). For wider codes x is
+ * every product is exact before the fp32 group scaling). For wider codes and
+ * 5 <= M <= 16, x is also used as is, against levels held as two bf16 halves
+ * (hi + lo, about 16 significant bits). Otherwise, for wider codes, x is
  * converted to fp16 after scaling each row by a power of two so that its
  * largest magnitude sits just below 2^15 (exact unless elements drop below
- * fp16's normal range); levels are fp16, accumulation fp32. Rows with M <= 4 take a single-kernel path that needs no
- * workspace; larger M first writes the converted activations into `workspace`.
+ * fp16's normal range), and levels are fp16. Accumulation is fp32 throughout.
+ * Rows with M <= 4 take a single-kernel path that needs no workspace; larger M
+ * may first write reordered or converted activations into `workspace` (the
+ * 5..16-row paths of wider codes do not touch it).
  * cubic_gemm_a16_workspace_bytes(M, K) gives the required size (0 when none is
  * needed); `workspace` may be NULL when that size is 0. M == 0 is a no-op. */
 size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K);
