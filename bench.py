@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true", help="also time prefill and small-M products")
+    ap.add_argument("--crossover", type=int, default=0, metavar="REPS",
+                    help="only time A16 against A8 over M, widths and the two expert shapes")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 20 plain device copies of MIB MiB (HBM counter calibration)")
@@ -187,6 +189,52 @@ def cpu_baseline(seconds: float):
                       f"{reps} reps in {dt:.1f} s"}
 
 
+def crossover(steps):
+    """A16 against Dynamic A8 on the routed-expert shapes: gate_up 6144 x 7168 and
+    down 7168 x 3072, 2-bit (G512), 5- and 8-bit (G128) codes, M in {1, 16, 64,
+    256}. A8 is timed as the quantiser plus the product. Each product rotates
+    over enough weight copies (at least 640 MB) that every launch reads its
+    weight from HBM; graph replays, HIP events on the replay stream."""
+    import torch
+
+    import dequant_gemm_amd as cq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for name, N, K in (("gate_up", 6144, 7168), ("down", 7168, 3072)):
+        for bits, group in ((2, 512), (5, 128), (8, 128)):
+            g = synth.make_generator(7000 + 10 * bits + (N > K), dev)
+            w = synth.make_weight(g, N, K, bits, group, "ternary" if bits == 2 else "uniform", 0.02, dev)
+            base = cq.CubicWeight(cq.cubic_pack(w.codes, bits).reshape(-1), w.scales.contiguous(),
+                                  w.shapes.contiguous(), N, K, bits, group)
+            del w
+            nb = algorithmic_bytes(N, K, bits, group, 0)
+            copies = max(4, -(-640_000_000 // nb))
+            pool = [base] + [cq.CubicWeight(base.codes.clone(), base.scales.clone(), base.shapes.clone(),
+                                            N, K, bits, group) for _ in range(copies - 1)]
+            for M in (1, 16, 64, 256):
+                x = synth.activations(g, M, K, device=dev)
+                y = torch.empty((M, N), dtype=torch.float32, device=dev)
+                ws = torch.empty(max(1, cq.cubic_gemm_a16_workspace_bytes(M, K)), dtype=torch.uint8,
+                                 device=dev)
+                xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+                sx = torch.empty((M,), dtype=torch.float32, device=dev)
+                t16 = _graph_time([(lambda c=c: cq.cubic_gemm_a16(x, c, out=y, workspace=ws)) for c in pool],
+                                  steps, dev)
+                tq = _graph_time([lambda: cq.act_quant_int8_per_token(x, xq, sx)] * 8, steps, dev)
+                t8 = _graph_time([(lambda c=c: cq.cubic_gemm_a8(xq, sx, c, out=y)) for c in pool], steps, dev)
+                rows.append({"shape": name, "bits": bits, "group": group, "M": M,
+                             "a16_us": round(t16 * 1e3, 2), "a8_us": round((tq + t8) * 1e3, 2),
+                             "a8_quant_us": round(tq * 1e3, 2), "a8_gemm_us": round(t8 * 1e3, 2),
+                             "faster": "a16" if t16 <= tq + t8 else "a8", "copies": copies})
+                print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            del pool, base
+            torch.cuda.empty_cache()
+    print(json.dumps({"crossover": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -197,6 +245,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.crossover:
+        crossover(args.crossover)
         return
     import torch
 

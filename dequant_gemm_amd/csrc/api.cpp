@@ -18,6 +18,7 @@ namespace {
 
 constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
 constexpr int64_t kGemvMaxM = 16;          // one MFMA activation tile
+constexpr int64_t kGemvMaxMW2 = 8;         // 2-bit codes: the small-batch kernel is faster above
 constexpr int64_t kInkMaxM = 4;            // single-kernel A16 path
 constexpr int64_t kPrefillMinM = 256;      // 256 x 256 tile kernel (2-/3-bit codes)
 
@@ -149,9 +150,10 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
   uint16_t* xp = static_cast<uint16_t*>(workspace);
   float* xback = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           align256(static_cast<size_t>(M) * w->K * 2));
-  // up to 16 activation rows: the GEMV; 3- and 4-bit codes with 17..64 rows:
-  // the small-batch MFMA kernel
-  const bool use_gemv = M <= kGemvMaxM && gemv_supported(w->K, w->bits, w->group);
+  // up to 16 activation rows (2-bit codes: 8): the GEMV; 2- to 4-bit codes
+  // with up to 64 rows: the small-batch MFMA kernel
+  const bool use_gemv = M <= (w->bits == 2 ? kGemvMaxMW2 : kGemvMaxM) &&
+                        gemv_supported(w->K, w->bits, w->group);
   const bool use_skinny = !use_gemv && skinny_supported(M, w->N, w->K, w->bits, w->group);
   if (use_gemv && w->bits > 2) {
     // 3- to 8-bit codes: the GEMV reads the bf16 rows as they are (split bf16 levels)

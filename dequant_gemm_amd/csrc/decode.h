@@ -132,10 +132,11 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
 }
 
 // The same level in fp32, for the per-group tables of the products: with
-// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^10 for B <= 4),
-// a X and b Y are exact fp32 products of fp16 values, so
-// Q = j^3 + a X + b Y rounds twice in fp32, then once more by 1/K^3, before the
-// fp16 rounding: a few fp32 ulps, far inside the products' tolerance.
+// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers, exact in fp32), a X and b Y
+// are exact fp32 products of fp16 values while X, Y stay below 2^13 (B <= 5)
+// and round once otherwise, so Q = j^3 + a X + b Y carries a few roundings in
+// fp32, then one more by 1/K^3, before the 16-bit rounding of the entry: a few
+// fp32 ulps, far inside the products' tolerance.
 __device__ __forceinline__ float table_level_f32(float a, float b, uint32_t v, int bits) {
   const int k = sign_extend(v, bits);
   const int j = k < 0 ? -k : k;
@@ -149,20 +150,6 @@ __device__ __forceinline__ float table_level_f32(float a, float b, uint32_t v, i
 
 __device__ __forceinline__ uint16_t table_entry_f32(float a, float b, uint32_t v, int bits) {
   return f16_bits(table_level_f32(a, b, v, bits));
-}
-
-// Wide codes: the level in fp64 (integers up to 2^21 in its terms), as fp32.
-__device__ __forceinline__ float table_level(double a, double b, uint32_t v, int bits) {
-  const int k = sign_extend(v, bits);
-  const int j = k < 0 ? -k : k;
-  const int km = kmax_of(bits);
-  const double K = static_cast<double>(km);
-  const float q = static_cast<float>(level_numerator(a, b, j, km) * (1.0 / (K * K * K)));
-  return k < 0 ? -q : q;
-}
-
-__device__ __forceinline__ uint16_t table_entry(double a, double b, uint32_t v, int bits) {
-  return f16_bits(table_level(a, b, v, bits));
 }
 
 // A level as two bf16 halves of one dword: hi = rne(q) in the low half,

@@ -31,42 +31,28 @@ template <> struct IsW2<DecodeW2> { static constexpr bool value = true; };
 
 template <class Dec>
 __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, uint32_t gab) {
+  // Levels in fp32 (table_level_f32: a few fp32 ulps for every width, far
+  // below the 16-bit entries), each of the four lanes of a row taking every
+  // fourth entry.
+  constexpr int B = Dec::kBits;
+  constexpr int kUnroll = B <= 4 ? 4 : 8;
   if constexpr (Dec::kSplit) {
     // bf16 (hi, lo) pairs, one dword per entry
-    constexpr int B = Dec::kBits;
     uint32_t* t = reinterpret_cast<uint32_t*>(tab_wave) + nl * (1 << B);
     const int swz = Dec::swizzle(nl);
-    if constexpr (B <= 4) {
-      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab & 0xffffu)));
-      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab >> 16)));
-#pragma unroll
-      for (int v = kb; v < (1 << B); v += 4)
-        t[v ^ swz] = split_bf16_pair(table_level_f32(a, b, static_cast<uint32_t>(v), B));
-    } else {
-      const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
-      const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
-#pragma unroll 1
-      for (int v = kb; v < (1 << B); v += 4)
-        t[v ^ swz] = split_bf16_pair(table_level(a, b, static_cast<uint32_t>(v), B));
-    }
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab & 0xffffu)));
+    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab >> 16)));
+#pragma unroll kUnroll
+    for (int v = kb; v < (1 << B); v += 4)
+      t[v ^ swz] = split_bf16_pair(table_level_f32(a, b, static_cast<uint32_t>(v), B));
     wave_lds_order();
   } else if constexpr (!IsW2<Dec>::value) {
-    constexpr int B = Dec::kBits;
     uint16_t* t = tab_wave + nl * (1 << B);
     const int swz = Dec::swizzle(nl);           // entry v of row nl sits at v ^ swz
-    if constexpr (B <= 4) {
-      // fp32 levels (exact products, a few ulps; see table_entry_f32)
-      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab & 0xffffu)));
-      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab >> 16)));
-#pragma unroll
-      for (int v = kb; v < (1 << B); v += 4) t[v ^ swz] = table_entry_f32(a, b, static_cast<uint32_t>(v), B);
-    } else {
-      // wide codes (integers up to 2^21 in the level terms): fp64, in a rolled loop
-      const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
-      const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
-#pragma unroll 1
-      for (int v = kb; v < (1 << B); v += 4) t[v ^ swz] = table_entry(a, b, static_cast<uint32_t>(v), B);
-    }
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab & 0xffffu)));
+    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(gab >> 16)));
+#pragma unroll kUnroll
+    for (int v = kb; v < (1 << B); v += 4) t[v ^ swz] = table_entry_f32(a, b, static_cast<uint32_t>(v), B);
     wave_lds_order();
   }
 }

@@ -1,5 +1,5 @@
 // skinny.hip -- A16 product for small batches (17 <= M <= 64; smaller M runs on
-// the GEMV) with 3- and 4-bit codes.
+// the GEMV) with 2-, 3- and 4-bit codes.
 //
 // The CubicQuant article (section "压缩权重必须边解码、边计算") decodes each
 // weight tile inside the kernel that consumes it and scales group partial sums
@@ -47,7 +47,7 @@ constexpr int sk_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) <
 
 // Per-wave LDS ring stage: activations [32 MB rows][64 k] fp16 (16-byte chunk
 // q of row r at chunk q ^ (r & 7)), then the code words (lane l's 16 bytes:
-// row l / 2, half l % 2), then the group parameters of the step after it (64
+// row l / 2, half l % 2; 2-bit codes: dword d of lane l at 256 d + 4 l), then the group parameters of the step after it (64
 // scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
 // Ring depth: what the LDS holds with W waves of one or two 32-row blocks.
 template <int W, int MB> constexpr int sk_stages() { return W == 8 ? (MB == 2 ? 2 : 3) : (MB == 2 ? 4 : 6); }
@@ -78,13 +78,14 @@ __device__ __forceinline__ float sk_level(float a, float b, int v) {
 template <int B, int MB, int SK_WAVES>
 __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
   extern __shared__ __align__(1024) unsigned char smem[];   // row tables rely on this alignment
-  static_assert(B == 3 || B == 4, "16-byte code slots per lane and step");
+  static_assert(B >= 2 && B <= 4, "code slots of at most 16 bytes per lane and step");
   constexpr int NST = sk_stages<SK_WAVES, MB>();
   constexpr size_t kStage = sk_stage_bytes<MB>();
   constexpr size_t kCodeOff = sk_x_bytes<MB>();
   constexpr size_t kParamOff = kCodeOff + 1024;
   constexpr int NX = 4 * MB;                     // activation loads per step (1 KB each)
-  constexpr int NV = NX + 3;                     // + codes + scales + (a, b)
+  constexpr int NC = B == 2 ? 2 : 1;             // code loads per step
+  constexpr int NV = NX + NC + 2;                // + codes + scales + (a, b)
   static_assert(NST * NV < 64, "vmcnt holds at most 63");
 
   const int lane = threadIdx.x & 63;
@@ -128,6 +129,14 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
     if constexpr (B == 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 16,
                                                coff + static_cast<uint32_t>(sv) * (8 * B), 0, 0, 0);
+    } else if constexpr (B == 2) {
+      // the lane's two dwords as two 4-byte loads (4-byte lane stride): dword d
+      // of every lane lands in its own 256-byte area
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * d, 4,
+                                                 coff + static_cast<uint32_t>(sv) * (8 * B) + 4 * d, 0, 0,
+                                                 0);
     } else {
       // 12-byte loads land at a 16-byte lane stride
       __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 12,
@@ -214,7 +223,11 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
     if (s > sb && (s * SK_K) % p.group == 0) build(0, psb, pab);   // a new group's table
     // all of the step's LDS reads first: code words, activation fragments
     uint32_t w[B];
-    {
+    if constexpr (B == 2) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff) + (2 * c + h);
+      w[0] = src[0];
+      w[1] = src[64];
+    } else {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff) + 4 * (2 * c + h);
 #pragma unroll
       for (int d = 0; d < B; ++d) w[d] = src[d];
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
 }  // namespace
 
 bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
-  if (bits != 3 && bits != 4) return false;
+  if (bits < 2 || bits > 4) return false;
   if (M < 1 || M > 64 || K % SK_K != 0 || K / SK_K < 8) return false;   // a step per wave
   if (group % SK_K != 0) return false;
   if (64 * K * 2 >= (int64_t{1} << 32)) return false;   // activation offsets of 64 rows
@@ -338,6 +351,8 @@ static hipError_t launch_skinny_k(const TiledParams& p, hipStream_t st) {
 constexpr int kSkWaves = 8;                     // two waves per SIMD (measured faster than four per workgroup)
 
 hipError_t launch_skinny_a16(const TiledParams& p, int bits, hipStream_t st) {
+  if (bits == 2)
+    return p.M <= 32 ? launch_skinny_k<2, 1, kSkWaves>(p, st) : launch_skinny_k<2, 2, kSkWaves>(p, st);
   if (bits == 3)
     return p.M <= 32 ? launch_skinny_k<3, 1, kSkWaves>(p, st) : launch_skinny_k<3, 2, kSkWaves>(p, st);
   return p.M <= 32 ? launch_skinny_k<4, 1, kSkWaves>(p, st) : launch_skinny_k<4, 2, kSkWaves>(p, st);

@@ -61,7 +61,7 @@ def test_prefill_workload_full_sampled_rows():
 
 @pytest.mark.parametrize("bits,group", [(2, 512), (2, 128), (3, 128), (3, 256), (4, 128),
                                         (5, 256), (6, 128), (7, 128), (8, 256)])
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 16, 17, 100])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 9, 16, 17, 100])
 def test_small_shapes_ragged(bits, group, M):
     # N not a multiple of 16 or of 128, K spanning several groups and waves
     say(f"A16 ragged bits={bits} G={group} M={M}")
@@ -166,11 +166,11 @@ def test_small_m_rows_per_workgroup_ragged(bits, group, M):
     _check(w, x)
 
 
-@pytest.mark.parametrize("bits,group", [(3, 128), (3, 512), (4, 128), (4, 256)])
+@pytest.mark.parametrize("bits,group", [(2, 128), (2, 512), (3, 128), (3, 512), (4, 128), (4, 256)])
 @pytest.mark.parametrize("M,N,K", [(17, 203, 512), (31, 64, 1536), (32, 4100, 1024), (33, 203, 1536),
                                    (64, 230, 3072)])
 def test_small_batch_mfma_shapes(bits, group, M, N, K):
-    """The small-batch MFMA kernel (3- and 4-bit codes, 17..64 rows): one and two
+    """The small-batch MFMA kernel (2- to 4-bit codes, 17..64 rows): one and two
     32-row activation blocks, ragged N, few steps per wave."""
     say(f"A16 small batch bits={bits} G={group} M={M} N={N} K={K}")
     g = synth.make_generator(6000 + 10 * bits + M + N)
@@ -179,7 +179,7 @@ def test_small_batch_mfma_shapes(bits, group, M, N, K):
     _check(w, x)
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("K", [1664, 1920])
 def test_small_batch_mfma_uneven_waves(bits, K):
     """K / 64 steps not divisible by the four waves (26 and 30 steps)."""
