@@ -22,17 +22,20 @@ __all__ = [
     "CubicError", "CubicWeight", "library_path", "load_library",
     "cubic_code_bytes", "cubic_storage_bytes", "cubic_pack", "cubic_unpack",
     "cubic_dequant", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
-    "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_moe_workspace_bytes",
-    "cubic_moe_grouped_gemm", "EXPORTED_SYMBOLS",
+    "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode", "cubic_linear_workspace_bytes",
+    "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = [
     "cubic_code_bytes", "cubic_storage_bytes", "cubic_status_string", "cubic_version",
     "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_gemm_a16_workspace_bytes",
-    "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8",
-    "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
+    "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode",
+    "cubic_linear_workspace_bytes", "cubic_linear", "cubic_moe_workspace_bytes",
+    "cubic_moe_grouped_gemm",
 ]
+MODE_A16, MODE_A8 = 0, 1          # cubic_linear_mode results
 
 
 class CubicError(RuntimeError):
@@ -77,6 +80,9 @@ def load_library():
         "cubic_gemm_a16": (i32, [vp, i64, wp, vp, vp, sz, vp]),
         "act_quant_int8_per_token": (i32, [vp, i64, i64, vp, vp, vp]),
         "cubic_gemm_a8": (i32, [vp, vp, i64, wp, vp, vp]),
+        "cubic_linear_mode": (i32, [i64, i64, i64, i32, i32]),
+        "cubic_linear_workspace_bytes": (sz, [i64, i64]),
+        "cubic_linear": (i32, [vp, i64, wp, vp, vp, sz, vp]),
         "cubic_moe_workspace_bytes": (sz, [i64, i32, i32, i64]),
         "cubic_moe_grouped_gemm": (i32, [vp, i64, vp, i32, wp, i32, vp, vp, sz, vp]),
     }
@@ -218,6 +224,33 @@ def cubic_gemm_a8(xq: torch.Tensor, x_scale: torch.Tensor, w: CubicWeight,
         out = torch.empty((M, w.N), dtype=torch.float32, device=xq.device)
     _check(load_library().cubic_gemm_a8(_ptr(xq), _ptr(x_scale), M, ctypes.byref(cw), _ptr(out),
                                         _stream(xq)), "cubic_gemm_a8")
+    return out
+
+
+def cubic_linear_mode(M: int, N: int, K: int, bits: int, group: int) -> int:
+    """MODE_A16 or MODE_A8: the activation mode cubic_linear takes for this shape."""
+    return int(load_library().cubic_linear_mode(M, N, K, bits, group))
+
+
+def cubic_linear_workspace_bytes(M: int, K: int) -> int:
+    return int(load_library().cubic_linear_workspace_bytes(M, K))
+
+
+def cubic_linear(x: torch.Tensor, w: CubicWeight, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M][N] (fp32) from bf16 x[M][K] in the mode of cubic_linear_mode (A16, or
+    the per-token INT8 quantiser followed by the A8 product)."""
+    _need(x, torch.bfloat16, "x")
+    M = x.shape[0]
+    cw = w.c_struct()
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    need = cubic_linear_workspace_bytes(M, w.K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(load_library().cubic_linear(_ptr(x), M, ctypes.byref(cw), _ptr(out), _ptr(workspace),
+                                        ws_bytes, _stream(x)), "cubic_linear")
     return out
 
 

@@ -202,6 +202,41 @@ CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
   return hip_status(launch_tiled_a8(p, w->bits, static_cast<hipStream_t>(stream)));
 }
 
+constexpr int64_t kLinearA8MinM = 256;     // the measured crossover of 2- and 3-bit codes
+
+CUBIC_API int cubic_linear_mode(int64_t M, int64_t N, int64_t K, int bits, int group) {
+  if ((bits == 2 || bits == 3) && M >= kLinearA8MinM && N > 0 && K > 0 && group > 0 &&
+      prefill_a8_supported(M, N, K, bits, group))
+    return CUBIC_MODE_A8;
+  return CUBIC_MODE_A16;
+}
+
+CUBIC_API size_t cubic_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K < 0) return 0;
+  const size_t a8 = align256(static_cast<size_t>(M) * K) + align256(static_cast<size_t>(M) * 4);
+  const size_t a16 = cubic_gemm_a16_workspace_bytes(M, K);
+  return a8 > a16 ? a8 : a16;
+}
+
+CUBIC_API int cubic_linear(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float* y,
+                           void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  const int st = check_weight(w);
+  if (st != CUBIC_OK) return st;
+  if (M < 0) return CUBIC_ERR_SHAPE;
+  if (cubic_linear_mode(M, w->N, w->K, w->bits, w->group) == CUBIC_MODE_A16)
+    return cubic_gemm_a16(x_bf16, M, w, y, workspace, ws_bytes, stream);
+  if (!x_bf16 || !y) return CUBIC_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(y)) return CUBIC_ERR_ALIGN;
+  const size_t xq_bytes = align256(static_cast<size_t>(M) * w->K);
+  if (!workspace || ws_bytes < xq_bytes + align256(static_cast<size_t>(M) * 4)) return CUBIC_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return CUBIC_ERR_ALIGN;
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + xq_bytes);
+  const int q = act_quant_int8_per_token(x_bf16, M, w->K, xq, xs, stream);
+  if (q != CUBIC_OK) return q;
+  return cubic_gemm_a8(xq, xs, M, w, y, stream);
+}
+
 namespace {
 struct MoeLayout {
   size_t hdr, erec, sorted, total;

@@ -131,6 +131,29 @@ int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K,
 int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
                   const cubic_weight* w, float* y, cubic_stream_t stream);
 
+/* Shape dispatcher between the two activation modes (CubicQuant article, A16/A8
+ * section and its kernel comparison: A16 serves decode-sized batches best, the
+ * integer path once each decoded weight serves enough rows). The rule is
+ * static and comes from the A16-vs-A8 sweep of this library on MI355X:
+ * Dynamic A8 for 2- and 3-bit codes with M >= 256 (where its prefill kernel
+ * runs), A16 otherwise. The modes differ in numerics (A8 quantises the
+ * activations); cubic_linear_mode tells which one a shape takes. It is a host
+ * function and needs no device. */
+enum { CUBIC_MODE_A16 = 0, CUBIC_MODE_A8 = 1 };
+int cubic_linear_mode(int64_t M, int64_t N, int64_t K, int bits, int group);
+/* Workspace that cubic_linear needs for any weight with this K: the larger of
+ * the A16 workspace and the A8 staging (xq: M*K bytes, then x_scale: 4*M bytes,
+ * each rounded up to 256). */
+size_t cubic_linear_workspace_bytes(int64_t M, int64_t K);
+/* y[M][N] (fp32) by the mode of cubic_linear_mode: cubic_gemm_a16, or
+ * act_quant_int8_per_token into the workspace followed by cubic_gemm_a8. The
+ * results equal those calls' results bit for bit. Arguments and errors as for
+ * cubic_gemm_a16. A workspace of cubic_linear_workspace_bytes(M, K) always
+ * suffices; each route checks only what it uses (the A16 route the A16
+ * workspace, the A8 route its staging) and returns CUBIC_ERR_WORKSPACE below. */
+int cubic_linear(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float* y,
+                 void* workspace, size_t ws_bytes, cubic_stream_t stream);
+
 /* Routed-expert A16 products. E experts with identical (N, K, bits, group) lie
  * back to back: expert e's codes start at expert0->codes + e*code_bytes, its
  * scales at expert0->scales + e*N*(K/group), its shapes at expert0->shapes +
@@ -139,7 +162,7 @@ int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
  * counted; the count is left in the first 4 bytes of the workspace (int32).
  * Grouping by expert happens on the device (no host synchronisation); each
  * touched expert's codes are read from HBM once per launch (an expert picked by
- * more than two tokens takes one pass per one or two of them, the later passes
+ * more than four tokens takes one pass per up to four of them, the later passes
  * reading its codes from cache). Requires K <= 2^28 and the per-wave activation
  * slice to fit in LDS (CUBIC_ERR_SHAPE otherwise). x_bf16 [T][K] is read directly.
  * The workspace size depends on T, topk and E only (K is accepted and ignored):

@@ -53,6 +53,42 @@ def test_workspace_sizes():
     assert lib.cubic_version().startswith(b"cubic")
 
 
+def test_linear_mode_rule_and_workspace():
+    # Dynamic A8 for 2- and 3-bit codes from 256 rows on (the measured crossover), A16 otherwise
+    A16, A8 = cq.MODE_A16, cq.MODE_A8
+    assert cq.cubic_linear_mode(1, 6144, 7168, 2, 512) == A16
+    assert cq.cubic_linear_mode(255, 6144, 7168, 2, 512) == A16
+    assert cq.cubic_linear_mode(256, 6144, 7168, 2, 512) == A8
+    assert cq.cubic_linear_mode(4096, 6144, 7168, 3, 256) == A8
+    assert cq.cubic_linear_mode(4096, 6144, 7168, 4, 128) == A16
+    assert cq.cubic_linear_mode(256, 7168, 3072, 5, 128) == A16
+    assert cq.cubic_linear_mode(4096, 256, 4096, 2, 2048) == A16     # group beyond the A8 kernel
+    assert cq.cubic_linear_mode(0, 6144, 7168, 2, 512) == A16
+    # the larger of the A16 workspace and the A8 staging (xq, then x_scale, 256-aligned)
+    assert cq.cubic_linear_workspace_bytes(1, 7168) == 7168 + 256
+    assert cq.cubic_linear_workspace_bytes(4096, 7168) == max(
+        cq.cubic_gemm_a16_workspace_bytes(4096, 7168), 4096 * 7168 + 4096 * 4)
+    assert cq.cubic_linear_workspace_bytes(0, 7168) == 0
+
+
+def test_linear_validation_before_launch():
+    lib = cq.load_library()
+    p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
+    w8 = _w(N=256, K=512, bits=3, group=128)           # M = 256 takes the A8 route
+    need = lib.cubic_linear_workspace_bytes(256, 512)
+    a8_need = 256 * 512 + 256 * 4                      # the A8 staging this route checks
+    assert lib.cubic_linear(p16, 256, ctypes.byref(w8), p16, p16, a8_need - 1, None) == ERR_WS
+    assert lib.cubic_linear(p16, 256, ctypes.byref(w8), p16, None, 0, None) == ERR_WS
+    assert lib.cubic_linear(None, 256, ctypes.byref(w8), p16, p16, need, None) == ERR_NULL
+    assert lib.cubic_linear(p8, 256, ctypes.byref(w8), p16, p16, need, None) == ERR_ALIGN
+    assert lib.cubic_linear(p16, 256, ctypes.byref(w8), p16, p8, need, None) == ERR_ALIGN
+    assert lib.cubic_linear(p16, -1, ctypes.byref(w8), p16, p16, need, None) == ERR_SHAPE
+    assert lib.cubic_linear(p16, 256, ctypes.byref(_w(bits=1)), p16, p16, need, None) == ERR_BITS
+    assert lib.cubic_linear(p16, 0, ctypes.byref(w8), p16, None, 0, None) == OK   # no-op
+    # the A16 route validates as cubic_gemm_a16 does
+    assert lib.cubic_linear(p16, 8, ctypes.byref(w8), p16, None, 0, None) == ERR_WS
+
+
 def _w(N=256, K=512, bits=3, group=128, codes=16, scales=16, shapes=16):
     return cq._CWeight(codes, scales, shapes, N, K, bits, group)
 
