@@ -33,6 +33,7 @@ struct DecodeW2 {
   static constexpr int kBits = 2;
   static constexpr bool kBf16 = true;
   static constexpr bool kSplit = false;
+  static constexpr bool kDirect = false;
   static constexpr float kLevelUnit = 0.5f;   // decoded value * s * 0.5 = weight
 
   __host__ __device__ static int slot_to_code(int slot) {
@@ -81,6 +82,7 @@ struct DecodeTable {
   static constexpr int kBits = BITS;
   static constexpr bool kBf16 = false;
   static constexpr bool kSplit = false;
+  static constexpr bool kDirect = false;
   static constexpr float kLevelUnit = 1.0f;
   __host__ __device__ static int slot_to_code(int slot) { return slot; }
   __host__ __device__ static int code_to_slot(int c) { return c; }
@@ -172,6 +174,7 @@ struct DecodeTableSplit {
   static constexpr int kBits = BITS;
   static constexpr bool kBf16 = true;
   static constexpr bool kSplit = true;
+  static constexpr bool kDirect = false;
   static constexpr float kLevelUnit = 1.0f;
   __host__ __device__ static int slot_to_code(int slot) { return slot; }
   __host__ __device__ static int code_to_slot(int c) { return c; }
@@ -207,6 +210,72 @@ struct DecodeTableSplit {
       const uint32_t d1 = *reinterpret_cast<const lds_u32*>(static_cast<uintptr_t>(addr(2 * p + 1)));
       rhi[p] = __builtin_amdgcn_perm(d1, d0, 0x05040100u);
       rlo[p] = __builtin_amdgcn_perm(d1, d0, 0x07060302u);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Wide codes (7 and 8 bits), levels computed per code: a row's 2^B-entry table
+// would be rebuilt for every group (128 codes per row at G = 128) and cost more
+// than the codes it serves. With t = |k| / Kmax the level is
+// q = t (a + t (b + t c)), c = 1 - a - b, in fp32 (a few ulps), signed like k,
+// then rounded to the operand type. SPLIT: bf16 hi = rne(q) and lo = rne(q - hi)
+// against raw bf16 activations (two MFMAs per fragment); otherwise fp16 against
+// prescaled fp16 activations. Natural order, level unit 1.
+// ---------------------------------------------------------------------------
+template <int BITS, bool SPLIT>
+struct DecodeDirect {
+  static constexpr int kBits = BITS;
+  static constexpr bool kBf16 = SPLIT;
+  static constexpr bool kSplit = SPLIT;
+  static constexpr bool kDirect = true;
+  static constexpr float kLevelUnit = 1.0f;
+  __host__ __device__ static int slot_to_code(int slot) { return slot; }
+  __host__ __device__ static int code_to_slot(int c) { return c; }
+  __host__ __device__ static constexpr int swizzle(int) { return 0; }
+
+  // Per-group constants of the Horner form, from the (a, b) word.
+  struct Coef {
+    float a, b, c;
+  };
+  __device__ static Coef coef(uint32_t ab) {
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+    return Coef{a, b, (1.0f - a) - b};
+  }
+
+  // q of the chunk's 32 codes (w: BITS dwords), as 16 fp16 pairs (r) or 16 bf16
+  // hi pairs (r) and 16 bf16 lo pairs (rl).
+  __device__ static void decode(const uint32_t* w, const Coef& k, uint32_t* r, uint32_t* rl) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    constexpr float kInv = 1.0f / static_cast<float>((1 << (BITS - 1)) - 1);
+    auto level = [&](int i) {
+      const int bit = i * BITS;
+      const int d = bit >> 5, off = bit & 31;
+      int v;
+      if (off + BITS <= 32) {
+        v = __builtin_amdgcn_sbfe(w[d], off, BITS);
+      } else {
+        v = __builtin_amdgcn_sbfe(__builtin_amdgcn_alignbit(w[d + 1], w[d], off), 0, BITS);
+      }
+      const float kf = static_cast<float>(v);
+      const float t = fabsf(kf) * kInv;
+      const float q = t * fmaf(t, fmaf(t, k.c, k.b), k.a);
+      return copysignf(q, kf);
+    };
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const f2 q = {level(2 * p), level(2 * p + 1)};
+      if constexpr (SPLIT) {
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, b2));
+        const f2 h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+        r[p] = hi;
+        rl[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q - h, b2));
+      } else {
+        r[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, h2));
+      }
     }
   }
 };

@@ -279,10 +279,12 @@ hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st) 
                        : launch_gemv_t<DecodeTableSplit<5>, false, 1, 2>(p, st);
     case 6: return ink ? launch_gemv_t<DecodeTable<6>, true, 1, 4>(p, st)
                        : launch_gemv_t<DecodeTableSplit<6>, false, 1, 2>(p, st);
-    case 7: return ink ? launch_gemv_t<DecodeTable<7>, true, 1, 4>(p, st)
-                       : launch_gemv_t<DecodeTableSplit<7>, false, 1, 2>(p, st);
-    default: return ink ? launch_gemv_t<DecodeTable<8>, true, 1, 4>(p, st)
-                        : launch_gemv_t<DecodeTableSplit<8>, false, 1, 2>(p, st);
+    // 7- and 8-bit codes: levels computed per code (a table per 128-code group
+    // would cost more than the codes; measured for 5-bit codes, tables win)
+    case 7: return ink ? launch_gemv_t<DecodeDirect<7, false>, true, 1, 4>(p, st)
+                       : launch_gemv_t<DecodeDirect<7, true>, false, 1, 4>(p, st);
+    default: return ink ? launch_gemv_t<DecodeDirect<8, false>, true, 1, 4>(p, st)
+                        : launch_gemv_t<DecodeDirect<8, true>, false, 1, 4>(p, st);
   }
 }
 

@@ -36,7 +36,9 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
   // fourth entry.
   constexpr int B = Dec::kBits;
   constexpr int kUnroll = B <= 4 ? 4 : 8;
-  if constexpr (Dec::kSplit) {
+  if constexpr (Dec::kDirect) {
+    // no table: the levels are computed per code
+  } else if constexpr (Dec::kSplit) {
     // bf16 (hi, lo) pairs, one dword per entry
     uint32_t* t = reinterpret_cast<uint32_t*>(tab_wave) + nl * (1 << B);
     const int swz = Dec::swizzle(nl);
@@ -60,7 +62,7 @@ __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, 
 // LDS bytes of the per-wave level tables.
 template <class Dec>
 __host__ __device__ constexpr int tab_bytes_per_wave() {
-  return IsW2<Dec>::value ? 0 : 16 * (1 << Dec::kBits) * (Dec::kSplit ? 4 : 2);
+  return (IsW2<Dec>::value || Dec::kDirect) ? 0 : 16 * (1 << Dec::kBits) * (Dec::kSplit ? 4 : 2);
 }
 
 // Per-wave state of the streaming loop.
@@ -126,6 +128,7 @@ struct StreamState {
   float gscale;
   uint32_t gab;
   int gcur;
+  float ca, cb, cc;          // Horner coefficients of the group (direct-level decoders)
   __device__ __forceinline__ void reset() {
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -158,6 +161,12 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
     st.gscale = __uint_as_float(gp[0]) * Dec::kLevelUnit;
     st.gab = gp[1];
     st.gcur = g;
+    if constexpr (Dec::kDirect) {
+      const auto k = Dec::coef(st.gab);
+      st.ca = k.a;
+      st.cb = k.b;
+      st.cc = k.c;
+    }
     build_table<Dec>(c.tab_wave, nl, kb, st.gab);
   }
   // 2-bit codes: one test per macro step for the field value 10 (code -2)
@@ -181,7 +190,16 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
       }
     }
     uint32_t r[16];
-    if constexpr (Dec::kSplit) {
+    if constexpr (Dec::kDirect) {
+      uint32_t rl[16];
+      Dec::decode(&w[h * B], typename Dec::Coef{st.ca, st.cb, st.cc}, r, rl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+        if constexpr (Dec::kSplit)
+          st.part[j] = mfma16<true>(av[j], u32x4{rl[4 * j], rl[4 * j + 1], rl[4 * j + 2], rl[4 * j + 3]}, st.part[j]);
+      }
+    } else if constexpr (Dec::kSplit) {
       uint32_t rl[16];
       Dec::decode(&w[h * B], reinterpret_cast<const uint32_t*>(c.tab_wave) + nl * (1 << B),
                   Dec::swizzle(nl), r, rl);

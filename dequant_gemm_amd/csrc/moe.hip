@@ -597,8 +597,8 @@ hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvP
     case 4: return launch_moe_gemv_t<DecodeTable<4>, 1, 4>(p, blocks, T, st);
     case 5: return launch_moe_gemv_t<DecodeTable<5>, 1, 2>(p, blocks, T, st);
     case 6: return launch_moe_gemv_t<DecodeTable<6>, 1, 2>(p, blocks, T, st);
-    case 7: return launch_moe_gemv_t<DecodeTable<7>, 1, 2>(p, blocks, T, st);
-    default: return launch_moe_gemv_t<DecodeTable<8>, 1, 2>(p, blocks, T, st);
+    case 7: return launch_moe_gemv_t<DecodeDirect<7, false>, 1, 2>(p, blocks, T, st);
+    default: return launch_moe_gemv_t<DecodeDirect<8, false>, 1, 2>(p, blocks, T, st);
   }
 }
 

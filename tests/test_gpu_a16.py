@@ -72,9 +72,10 @@ def test_small_shapes_ragged(bits, group, M):
     _check(w, x)
 
 
-def test_extra_negative_code_w2_and_w4():
-    # codes -2^(B-1) decode by the formula (t > 1); W2 exercises the slow path
-    for bits in (2, 4):
+def test_extra_negative_code_w2_w4_w8():
+    # codes -2^(B-1) decode by the formula (t > 1); W2 exercises the slow path,
+    # W8 the levels computed per code
+    for bits in (2, 4, 8):
         say(f"A16 extra code bits={bits}")
         g = torch.Generator().manual_seed(bits)
         N, K, G = 64, 1024, 512 if bits == 2 else 128

@@ -36,7 +36,7 @@ def _expert_dense(e, N, K, bits, group, seed):
     return oracle.dequant(codes, scales, shapes, bits, group)
 
 
-@pytest.mark.parametrize("bits,group", [(2, 512), (3, 128), (4, 256)])
+@pytest.mark.parametrize("bits,group", [(2, 512), (3, 128), (4, 256), (7, 128), (8, 256)])
 def test_mini_k3_all_pairs(bits, group):
     # K3 mini shapes (hidden 512, expert intermediate 256, 8 experts, top-2)
     say(f"MoE mini bits={bits}")
