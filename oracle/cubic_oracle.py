@@ -61,6 +61,7 @@ __all__ = [
     "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
     "level_numerators", "levels", "dequant", "gemm_a16",
     "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
+    "encode_levels_f32", "encode",
 ]
 
 # Domain in which the float64 evaluation of Q_j is exact (see module docstring).
@@ -295,3 +296,59 @@ def moe_a16(x_bf16: np.ndarray, topk_ids: np.ndarray, num_experts: int, N: int,
                 cache[e] = np.asarray(expert_weight(e), dtype=np.float64)
             Y[t, j] = cache[e] @ X[t]
     return Y
+
+
+# ----------------------------------------------------------------------------
+# Nearest-level encoding (CubicQuant article, Core: each weight takes the code of
+# the nearest level of its group, given the group's s, a, b). The pages fix no
+# arithmetic for the choice; this library's reading decides it in fp32, so that
+# the device encoder and this definition agree code for code:
+#   q_j = fl32( fl32(a X_j + fl32(b Y_j + j^3)) * fl32(1 / Kmax^3) ),
+#         X_j = j Kmax^2 - j^3, Y_j = j^2 Kmax - j^3 (each fl32 a single rounding
+#         of the exact value, i.e. two fused multiply-adds and one product),
+#   v_j = fl32(|s| q_j),  d_j = |fl32(|w| - v_j)|   for j = 0 .. Kmax,
+#   k = j* with the sign of w * s, j* the first j of smallest d_j (ties go to
+#   the smaller |k|). The extra code -2^(B-1) is never chosen.
+# ----------------------------------------------------------------------------
+def encode_levels_f32(a: np.ndarray, b: np.ndarray, bits: int) -> np.ndarray:
+    """q_j (float32) for j = 0 .. Kmax of fp16 shape values a, b (float64 arrays).
+
+    Each fused multiply-add is evaluated exactly in float64 and rounded once:
+    a and b are multiples of 2^-24 and |X|, |Y|, j^3 < 2^22, so every
+    intermediate is a multiple of 2^-24 below 2^26 (at most 50 bits)."""
+    km = kmax(bits)
+    a = np.asarray(a, dtype=np.float64)[..., None]
+    b = np.asarray(b, dtype=np.float64)[..., None]
+    j = np.arange(km + 1, dtype=np.int64)
+    X = (j * km * km - j ** 3).astype(np.float64)
+    Y = (j * j * km - j ** 3).astype(np.float64)
+    t1 = (b * Y + (j ** 3).astype(np.float64)).astype(np.float32)
+    t2 = (a * X + t1.astype(np.float64)).astype(np.float32)
+    inv = np.float32(1.0) / np.float32(km * km * km)
+    return t2 * inv
+
+
+def encode(w: np.ndarray, scales: np.ndarray, shapes: np.ndarray, bits: int,
+           group: int) -> np.ndarray:
+    """int8 codes [N][K] of float32 weights w [N][K] by the rule above."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of group")
+    G = K // group
+    s = np.asarray(scales, dtype=np.float32).reshape(N, G)
+    ab = np.asarray(shapes, dtype=np.uint16).reshape(N, G, 2)
+    q = encode_levels_f32(f16_bits_to_f64(ab[..., 0]), f16_bits_to_f64(ab[..., 1]), bits)  # [N][G][Kmax+1]
+    aw = np.abs(w).reshape(N, G, group)
+    sa = np.abs(s)
+    best_d = np.full(aw.shape, np.inf, dtype=np.float32)
+    best_j = np.zeros(aw.shape, dtype=np.int64)
+    for jj in range(kmax(bits) + 1):
+        v = sa * q[..., jj]                                  # float32 product
+        d = np.abs(aw - v[..., None])                        # float32 difference
+        better = d < best_d
+        best_d = np.where(better, d, best_d)
+        best_j = np.where(better, jj, best_j)
+    neg = np.signbit(w.reshape(N, G, group)) != np.signbit(s)[..., None]
+    k = np.where(neg, -best_j, best_j)
+    return k.reshape(N, K).astype(np.int8)

@@ -392,3 +392,92 @@ def test_test_side_field_packer_matches_oracle():
         assert np.array_equal(pack_fields(c, bits), oracle.pack(c, bits))
         c[0, 0] = c[3, 17] = c[4, 63] = -(1 << (bits - 1))
         assert np.array_equal(oracle.unpack(pack_fields(c, bits), 5, 64, bits), c)
+
+
+# ----------------------------------------------------------------------------
+# Nearest-level encoding (CubicQuant article, Core)
+# ----------------------------------------------------------------------------
+def _enc_params(N, G, bits, seed, uniform=False):
+    rng = np.random.default_rng(seed)
+    s = np.exp(np.log(0.02) + 0.3 * rng.standard_normal((N, G))).astype(np.float32)
+    if uniform:
+        sh = np.zeros((N, G, 2), np.uint16)
+        sh[..., 0] = _f16bits(1.0)
+    else:
+        sh = _random_shapes(N * G, seed).reshape(N, G, 2)
+    return s, sh
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_encode_uniform_int_closed_form(bits):
+    # a = 1, b = 0 is symmetric uniform INT: k = round(w / s * Kmax) clamped,
+    # checked away from the midpoints where fp32 rounding of the levels decides
+    km = oracle.kmax(bits)
+    N, K, G = 6, 512, 128
+    s, sh = _enc_params(N, K // G, bits, 11 + bits, uniform=True)
+    rng = np.random.default_rng(bits)
+    w = (rng.standard_normal((N, K)) * 0.03).astype(np.float32)
+    u = np.abs(w.astype(np.float64)) / np.repeat(s.astype(np.float64), G, axis=1) * km
+    ref = np.minimum(np.floor(u + 0.5), km) * np.sign(w)
+    away = np.abs(u - np.floor(u) - 0.5) > 1e-4
+    codes = oracle.encode(w, s, sh, bits, G)
+    assert np.array_equal(codes[away], ref[away].astype(np.int8))
+    assert away.mean() > 0.99
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_encode_round_trip_of_levels(bits):
+    # every representable weight encodes to its own code
+    km = oracle.kmax(bits)
+    N, K, G = 8, 256, 128
+    s, sh = _enc_params(N, K // G, bits, 21 + bits)
+    codes = np.random.default_rng(bits).integers(-km, km + 1, (N, K)).astype(np.int8)
+    w = oracle.dequant(codes, s, sh, bits, G).astype(np.float32)
+    assert np.array_equal(oracle.encode(w, s, sh, bits, G), codes)
+
+
+def test_encode_monotone_signs_and_degenerate_scales():
+    bits, G = 4, 128
+    s, sh = _enc_params(3, 1, bits, 31)
+    w = np.sort(np.random.default_rng(3).standard_normal((3, G)) * 0.04).astype(np.float32)
+    c = oracle.encode(w, s, sh, bits, G)
+    assert np.all(np.diff(c.astype(np.int64), axis=1) >= 0)
+    # a negative scale flips every code; zero scale and zero weights give 0
+    assert np.array_equal(oracle.encode(w, -s, sh, bits, G), -c)
+    assert not oracle.encode(w, np.zeros_like(s), sh, bits, G).any()
+    z = np.zeros((3, G), np.float32)
+    z[0, 0] = -0.0
+    assert not oracle.encode(z, s, sh, bits, G).any()
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6])
+def test_encode_is_nearest_within_fp32_rounding(bits):
+    # against every level in float64 (the exact levels of dequant): the chosen
+    # level is the nearest up to the fp32 rounding of levels and distances
+    km = oracle.kmax(bits)
+    N, K, G = 4, 384, 128
+    s, sh = _enc_params(N, K // G, bits, 41 + bits)
+    w = (np.random.default_rng(bits).standard_normal((N, K)) * 0.03).astype(np.float32)
+    codes = oracle.encode(w, s, sh, bits, G)
+    allk = np.arange(-km, km + 1)
+    for n in range(N):
+        for g in range(K // G):
+            q = oracle.levels(oracle.f16_bits_to_f64(sh[n, g, 0]), oracle.f16_bits_to_f64(sh[n, g, 1]), bits)
+            vals = float(s[n, g]) * np.sign(allk) * q[np.abs(allk)]
+            ww = w[n, g * G:(g + 1) * G].astype(np.float64)
+            d = np.abs(ww[:, None] - vals[None, :])
+            chosen = d[np.arange(G), codes[n, g * G:(g + 1) * G].astype(np.int64) + km]
+            assert np.all(chosen <= d.min(axis=1) + 8 * np.spacing(np.float32(np.abs(ww).max() + s[n, g])))
+
+
+def test_encode_exact_tie_goes_to_the_smaller_code():
+    bits, G = 3, 128
+    s, sh = _enc_params(1, 1, bits, 51)
+    q = oracle.encode_levels_f32(oracle.f16_bits_to_f64(sh[0, 0, 0]), oracle.f16_bits_to_f64(sh[0, 0, 1]), bits)
+    v1 = np.float32(abs(s[0, 0])) * q.reshape(-1)[1]
+    w = np.zeros((1, G), np.float32)
+    w[0, 0] = v1 / np.float32(2)          # exactly between level 0 and level 1
+    w[0, 1] = -(v1 / np.float32(2))
+    w[0, 2] = v1
+    c = oracle.encode(w, s, sh, bits, G)
+    assert c[0, 0] == 0 and c[0, 1] == 0 and c[0, 2] == 1
