@@ -445,7 +445,30 @@ def extra_workloads(cq, synth, dev, stream):
             del pool, base
         del wu, wd
         torch.cuda.empty_cache()
+    res.update(encode_workloads(cq, synth, dev))
     res.update(moe_workloads(cq, synth, dev))
+    return res
+
+
+def encode_workloads(cq, synth, dev):
+    """cubic_encode of fp32 gate_up 6144 x 7168 weights (W2 G512 and W4 G128):
+    three rotating weight copies (528 MB), graph replays. Algorithmic bytes:
+    4 per weight in, 1 per weight out, 8 per group of parameters."""
+    import torch
+    res = {}
+    N, K = 6144, 7168
+    for bits, group in ((2, 512), (4, 128)):
+        g = synth.make_generator(9500 + bits, dev)
+        w = synth.make_weight(g, N, K, bits, group, "ternary" if bits == 2 else "uniform", 0.02, dev)
+        xs = [torch.randn((N, K), generator=g, device=dev) * 0.03 for _ in range(3)]
+        out = torch.empty((N, K), dtype=torch.int8, device=dev)
+        ms = _graph_time([(lambda x=x: cq.cubic_encode(x, w.scales, w.shapes, bits, group, out=out)) for x in xs],
+                         5, dev)
+        nb = N * K * 5 + 8 * N * (K // group)
+        res[f"encode_w{bits}g{group}_gate_up"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
+                                                   "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del xs, w
+        torch.cuda.empty_cache()
     return res
 
 

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "CubicError", "CubicWeight", "library_path", "load_library",
     "cubic_code_bytes", "cubic_storage_bytes", "cubic_pack", "cubic_unpack",
-    "cubic_dequant", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
+    "cubic_dequant", "cubic_encode", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
     "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode", "cubic_linear_workspace_bytes",
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
     "EXPORTED_SYMBOLS",
@@ -30,7 +30,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = [
     "cubic_code_bytes", "cubic_storage_bytes", "cubic_status_string", "cubic_version",
-    "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_gemm_a16_workspace_bytes",
+    "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_encode", "cubic_gemm_a16_workspace_bytes",
     "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode",
     "cubic_linear_workspace_bytes", "cubic_linear", "cubic_moe_workspace_bytes",
     "cubic_moe_grouped_gemm",
@@ -76,6 +76,7 @@ def load_library():
         "cubic_pack": (i32, [vp, i64, i64, i32, vp, vp]),
         "cubic_unpack": (i32, [vp, i64, i64, i32, vp, vp]),
         "cubic_dequant": (i32, [wp, vp, vp]),
+        "cubic_encode": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp]),
         "cubic_gemm_a16_workspace_bytes": (sz, [i64, i64]),
         "cubic_gemm_a16": (i32, [vp, i64, wp, vp, vp, sz, vp]),
         "act_quant_int8_per_token": (i32, [vp, i64, i64, vp, vp, vp]),
@@ -176,6 +177,18 @@ def cubic_dequant(w: CubicWeight, out: torch.Tensor | None = None) -> torch.Tens
         out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.codes.device)
     _check(load_library().cubic_dequant(ctypes.byref(cw), _ptr(out), _stream(w.codes)),
            "cubic_dequant")
+    return out
+
+
+def cubic_encode(w: torch.Tensor, scales: torch.Tensor, shapes: torch.Tensor, bits: int, group: int,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 weights [N][K] -> int8 codes [N][K] of the nearest levels (pack with cubic_pack)."""
+    _need(w, torch.float32, "w")
+    N, K = w.shape
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    _check(load_library().cubic_encode(_ptr(w), N, K, bits, group, _ptr(scales), _ptr(shapes), _ptr(out),
+                                        _stream(w)), "cubic_encode")
     return out
 
 

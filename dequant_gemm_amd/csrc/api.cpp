@@ -120,6 +120,20 @@ CUBIC_API int cubic_dequant(const cubic_weight* w, float* out, cubic_stream_t st
                                    w->group, static_cast<hipStream_t>(stream)));
 }
 
+CUBIC_API int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int group,
+                           const float* scales, const uint16_t* shapes, int8_t* codes,
+                           cubic_stream_t stream) {
+  if (N < 0 || K < 0) return CUBIC_ERR_SHAPE;
+  if (bits < 2 || bits > 8) return CUBIC_ERR_BITS;
+  if (group <= 0 || group % 128 != 0 || K % group != 0) return CUBIC_ERR_GROUP;
+  if (N == 0 || K == 0) return CUBIC_OK;
+  if (!w || !scales || !shapes || !codes) return CUBIC_ERR_NULL;
+  if (!aligned16(w) || !aligned16(scales) || !aligned16(shapes) || !aligned16(codes)) return CUBIC_ERR_ALIGN;
+  if ((N * K / 8 + 255) / 256 > INT32_MAX) return CUBIC_ERR_SHAPE;
+  return hip_status(launch_encode(w, N, K, bits, group, scales, shapes, codes,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 CUBIC_API size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K < 0) return 0;
   if (a16_inkernel(M, K)) return 0;

@@ -8,6 +8,7 @@
 // consecutive codes of a row occupies exactly `bits` dwords, so one thread owns
 // one block and no two threads touch the same dword.
 #include "common.h"
+#include "decode.h"
 #include "launch.h"
 
 namespace cubic {
@@ -214,6 +215,63 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
   }
 }
 
+// Nearest-level encoding (CubicQuant article, Core: each weight takes the code
+// of its group's nearest level). The choice is made in fp32 exactly as follows,
+// so that every code is determined by IEEE operations: q_j is the fp32 level of
+// table_level_f32 (two fused multiply-adds and one product), v_j = |s| q_j,
+// d_j = | |w| - v_j |, each rounded once; the first j of smallest d_j wins (ties
+// to the smaller |k|) and k takes the sign of w * s. One thread encodes 8
+// consecutive weights of a row (one group); j runs over 0 .. Kmax.
+template <int B>
+__global__ __launch_bounds__(256) void k_encode(const float* __restrict__ w, int64_t nvec, int64_t K,
+                                                int group, const float* __restrict__ scales,
+                                                const uint32_t* __restrict__ shapes,
+                                                int8_t* __restrict__ codes) {
+#pragma clang fp contract(off)
+  constexpr int KM = (1 << (B - 1)) - 1;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= nvec) return;
+  const int64_t e0 = i * 8;                     // first weight (row-major [N][K])
+  const int64_t n = e0 / K, k0 = e0 - n * K;
+  const int64_t gi = n * (K / group) + k0 / group;
+  const float s = scales[gi];
+  const uint32_t ab = shapes[gi];
+  const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+  const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+  const float sa = fabsf(s);
+  const f32x4 lo = reinterpret_cast<const f32x4*>(w + e0)[0];
+  const f32x4 hi = reinterpret_cast<const f32x4*>(w + e0)[1];
+  const float wv[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  float aw[8], bd[8];
+  int bj[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    aw[e] = fabsf(wv[e]);
+    bd[e] = aw[e];                              // j = 0: v_0 = 0
+    bj[e] = 0;
+  }
+#pragma unroll 4
+  for (int j = 1; j <= KM; ++j) {
+    const float v = sa * table_level_f32(a, b, static_cast<uint32_t>(j), B);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = fabsf(aw[e] - v);
+      if (d < bd[e]) {
+        bd[e] = d;
+        bj[e] = j;
+      }
+    }
+  }
+  const bool sneg = __builtin_signbit(s);
+  uint32_t o[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = (__builtin_signbit(wv[e]) != sneg) ? -bj[e] : bj[e];
+    o[e >> 2] |= (static_cast<uint32_t>(k) & 0xffu) << (8 * (e & 3));
+  }
+  reinterpret_cast<uint2*>(codes + e0)[0] = make_uint2(o[0], o[1]);
+}
+
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ y, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * 256)
@@ -298,6 +356,27 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
   auto kern = per <= 1 ? k_act_quant<1> : per <= 2 ? k_act_quant<2> : per <= 4 ? k_act_quant<4>
                                         : per <= 8 ? k_act_quant<8> : k_act_quant<0>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xq, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const float* w, int64_t N, int64_t K, int bits, int group, const float* scales,
+                         const uint16_t* shapes, int8_t* codes, hipStream_t st) {
+  const int64_t nvec = N * K / 8;
+  if (nvec == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>((nvec + 255) / 256);
+  const uint32_t* ab = reinterpret_cast<const uint32_t*>(shapes);
+#define CUBIC_ENCODE(BB)                                                                            \
+  hipLaunchKernelGGL(k_encode<BB>, dim3(grid), dim3(256), 0, st, w, nvec, K, group, scales, ab, codes)
+  switch (bits) {
+    case 2: CUBIC_ENCODE(2); break;
+    case 3: CUBIC_ENCODE(3); break;
+    case 4: CUBIC_ENCODE(4); break;
+    case 5: CUBIC_ENCODE(5); break;
+    case 6: CUBIC_ENCODE(6); break;
+    case 7: CUBIC_ENCODE(7); break;
+    default: CUBIC_ENCODE(8); break;
+  }
+#undef CUBIC_ENCODE
   return hipGetLastError();
 }
 

@@ -97,6 +97,20 @@ int cubic_unpack(const uint8_t* packed, int64_t N, int64_t K, int bits,
  * exact value). Code 0 gives +0.0; codes +-Kmax give +-s exactly. */
 int cubic_dequant(const cubic_weight* w, float* out, cubic_stream_t stream);
 
+/* Nearest-level encoding (CubicQuant article, Core section: each weight takes
+ * the code of its group's nearest level), for given scales and shapes (the
+ * fitting of s, a, b is not part of this library). w: fp32 [N][K]; scales,
+ * shapes as in cubic_weight; codes: int8 [N][K] out, in [-Kmax, Kmax] (pack
+ * them with cubic_pack). The choice is made in fp32, bit for bit: with the fp32
+ * level q_j = fl(fl(a*(j*Kmax^2 - j^3) + fl(b*(j^2*Kmax - j^3) + j^3)) *
+ * fl(1/Kmax^3)) (two fused multiply-adds, one product), v_j = fl(|s| * q_j) and
+ * d_j = |fl(|w| - v_j)| for j = 0 .. Kmax, the first j of smallest d_j wins (ties
+ * go to the smaller |k|) and k takes the sign of w * s. Errors as for the other
+ * calls (bits, group, alignment, NULL); N == 0 or K == 0 is a no-op. */
+int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int group,
+                 const float* scales, const uint16_t* shapes, int8_t* codes,
+                 cubic_stream_t stream);
+
 /* A16 product y[M][N] = x[M][K] * W^T, x in bf16 (bit patterns), y in fp32.
  * For 2-bit weights x is used in bf16 as is (the valid levels are -s, 0, s, so
  * every product is exact before the fp32 group scaling). For wider codes and

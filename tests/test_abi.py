@@ -89,6 +89,19 @@ def test_linear_validation_before_launch():
     assert lib.cubic_linear(p16, 8, ctypes.byref(w8), p16, None, 0, None) == ERR_WS
 
 
+def test_encode_validation_before_launch():
+    lib = cq.load_library()
+    p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
+    assert lib.cubic_encode(p16, 4, 512, 1, 128, p16, p16, p16, None) == ERR_BITS
+    assert lib.cubic_encode(p16, 4, 512, 3, 64, p16, p16, p16, None) == ERR_GROUP
+    assert lib.cubic_encode(p16, 4, 384, 3, 256, p16, p16, p16, None) == ERR_GROUP
+    assert lib.cubic_encode(p16, -1, 512, 3, 128, p16, p16, p16, None) == ERR_SHAPE
+    assert lib.cubic_encode(None, 4, 512, 3, 128, p16, p16, p16, None) == ERR_NULL
+    assert lib.cubic_encode(p16, 4, 512, 3, 128, p16, p16, None, None) == ERR_NULL
+    assert lib.cubic_encode(p8, 4, 512, 3, 128, p16, p16, p16, None) == ERR_ALIGN
+    assert lib.cubic_encode(p16, 0, 512, 3, 128, None, None, None, None) == OK    # no-op
+
+
 def _w(N=256, K=512, bits=3, group=128, codes=16, scales=16, shapes=16):
     return cq._CWeight(codes, scales, shapes, N, K, bits, group)
 

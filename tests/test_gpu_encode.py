@@ -1,0 +1,84 @@
+"""GPU parity of cubic_encode: the device encoder gives the oracle's codes bit
+for bit (its decision rule is fixed in fp32 on both sides)."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemm_amd as cq
+import oracle
+import synth
+from tests._gpu import DEV, np_weight, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _params(N, K, bits, group, seed):
+    g = synth.make_generator(seed)
+    w = synth.make_weight(g, N, K, bits, group, "uniform", 0.02)
+    return w.scales, w.shapes
+
+
+def _encode_both(x, scales, shapes, bits, group):
+    codes = cq.cubic_encode(x.to(DEV), scales.to(DEV), shapes.to(DEV), bits, group).cpu().numpy()
+    ref = oracle.encode(x.numpy(), scales.numpy(), shapes.numpy().view(np.uint16), bits, group)
+    return codes, ref
+
+
+@pytest.mark.parametrize("bits,group", [(2, 512), (3, 128), (3, 256), (4, 128), (5, 256), (6, 128), (8, 128)])
+def test_encode_matches_oracle(bits, group):
+    say(f"encode bits={bits} G={group}")
+    N, K = 203, 1024
+    scales, shapes = _params(N, K, bits, group, 9000 + bits)
+    g = torch.Generator().manual_seed(bits)
+    x = torch.randn((N, K), generator=g) * 0.03
+    x[:, ::97] *= 20.0                               # outliers beyond the largest level
+    x[0, :64] = 0.0
+    x[1, :64] = -0.0
+    codes, ref = _encode_both(x, scales, shapes, bits, group)
+    assert np.array_equal(codes, ref)
+
+
+def test_encode_ties_signs_and_degenerate_scales():
+    say("encode ties, signs, degenerate scales")
+    bits, group, N, K = 3, 128, 4, 256
+    scales, shapes = _params(N, K, bits, group, 9100)
+    scales[1] = -scales[1]                            # negative scales flip the codes
+    scales[2, 0] = 0.0                                # all levels zero
+    ab = shapes.numpy().view(np.uint16)
+    q = oracle.encode_levels_f32(oracle.f16_bits_to_f64(ab[0, 0, 0]), oracle.f16_bits_to_f64(ab[0, 0, 1]), bits)
+    v = np.abs(scales.numpy()[0, 0]) * q.reshape(-1)
+    x = torch.randn((N, K), generator=torch.Generator().manual_seed(7)) * 0.03
+    for j in range(1, oracle.kmax(bits) + 1):           # exact midpoints 0|1 and the levels themselves
+        x[0, 2 * j] = float(v[j])
+        x[0, 2 * j + 1] = -float(v[j])
+    x[0, 0] = float(v[1] / np.float32(2))
+    x[0, 1] = -float(v[1] / np.float32(2))
+    codes, ref = _encode_both(x, scales, shapes, bits, group)
+    assert np.array_equal(codes, ref)
+    assert codes[0, 0] == 0 and codes[0, 1] == 0
+    assert not codes[2, :group].any()
+
+
+@pytest.mark.parametrize("bits,group", [(2, 512), (4, 128), (8, 256)])
+def test_encode_round_trip_through_device_dequant(bits, group):
+    say(f"encode round trip bits={bits}")
+    N, K = 96, 1536
+    g = synth.make_generator(9200 + bits)
+    w = synth.make_weight(g, N, K, bits, group, "ternary" if bits == 2 else "uniform", 0.02)
+    cw = cq.CubicWeight(cq.cubic_pack(w.codes.to(DEV), bits).reshape(-1), w.scales.to(DEV), w.shapes.to(DEV),
+                        N, K, bits, group)
+    W = cq.cubic_dequant(cw)
+    codes = cq.cubic_encode(W, w.scales.to(DEV), w.shapes.to(DEV), bits, group)
+    assert torch.equal(codes.cpu(), w.codes)
+
+
+def test_encode_full_shape_sampled_rows():
+    """gate_up 6144 x 7168, W4 G128 (the small-batch weight shape)."""
+    say("encode 6144x7168 W4 G128 (sampled rows)")
+    N, K, bits, group = 6144, 7168, 4, 128
+    scales, shapes = _params(N, K, bits, group, 9300)
+    x = torch.randn((N, K), generator=torch.Generator().manual_seed(3)) * 0.03
+    codes = cq.cubic_encode(x.to(DEV), scales.to(DEV), shapes.to(DEV), bits, group).cpu().numpy()
+    rows = np.array([0, 1, 2047, 4096, 6143])
+    ref = oracle.encode(x.numpy()[rows], scales.numpy()[rows], shapes.numpy().view(np.uint16)[rows], bits, group)
+    assert np.array_equal(codes[rows], ref)
