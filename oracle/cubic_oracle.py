@@ -61,7 +61,7 @@ __all__ = [
     "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
     "level_numerators", "levels", "dequant", "gemm_a16",
     "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
-    "encode_levels_f32", "encode",
+    "encode_levels_f32", "encode", "bf16_rne", "moe_mlp",
 ]
 
 # Domain in which the float64 evaluation of Q_j is exact (see module docstring).
@@ -352,3 +352,53 @@ def encode(w: np.ndarray, scales: np.ndarray, shapes: np.ndarray, bits: int,
     neg = np.signbit(w.reshape(N, G, group)) != np.signbit(s)[..., None]
     k = np.where(neg, -best_j, best_j)
     return k.reshape(N, K).astype(np.int8)
+
+
+# ----------------------------------------------------------------------------
+# Routed-expert MLP step (Kimi K3 guide, model card: routed experts with a fused
+# gate_up and a down projection). The pages give the expert layout, not the
+# arithmetic between the products; this library's reading: h = SiLU(gate) * up
+# rounded to bf16 (the down projection's activations), outputs weighted by the
+# router's weights and summed over the token's slots.
+# ----------------------------------------------------------------------------
+def bf16_rne(v: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bf16 value (ties to even), as float64, by exact rational
+    steps: the bf16 spacing around v is a power of two, so v / spacing is rounded
+    to an even integer on ties with np.rint and scaled back. Finite inputs."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros_like(v)
+    nz = v != 0
+    e = np.floor(np.log2(np.abs(v[nz])))
+    # fix the exponent where log2 rounded across a power of two
+    e = np.where(np.abs(v[nz]) >= 2.0 ** (e + 1), e + 1, e)
+    e = np.where(np.abs(v[nz]) < 2.0 ** e, e - 1, e)
+    e = np.maximum(e, -126.0)                          # bf16 subnormals share the smallest spacing
+    spacing = 2.0 ** (e - 7)                           # 8 significant bits
+    out[nz] = np.rint(v[nz] / spacing) * spacing
+    return out
+
+
+def moe_mlp(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, num_experts: int,
+            gate_up_weight, down_weight) -> np.ndarray:
+    """y[t] = sum_j w[t, j] * D_e @ bf16(SiLU(g) * u), [g | u] = GU_e @ x[t], e = ids[t, j]
+    (float64; ids outside [0, E) add nothing). gate_up_weight(e): [2I][H]; down_weight(e): [H][I]."""
+    ids = np.asarray(topk_ids)
+    T, topk = ids.shape
+    X = bf16_bits_to_f64(x_bf16)
+    Y = np.zeros((T, X.shape[1]), dtype=np.float64)      # H = K of gate_up = N of down
+    cache = {}
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if not 0 <= e < num_experts:
+                continue
+            if e not in cache:
+                cache[e] = (np.asarray(gate_up_weight(e), dtype=np.float64),
+                            np.asarray(down_weight(e), dtype=np.float64))
+            GU, D = cache[e]
+            I = D.shape[1]
+            gu = GU @ X[t]
+            g, u = gu[:I], gu[I:]
+            h = bf16_rne(g / (1.0 + np.exp(-g)) * u)
+            Y[t] += float(topk_w[t, j]) * (D @ h)
+    return Y

@@ -481,3 +481,78 @@ def test_encode_exact_tie_goes_to_the_smaller_code():
     w[0, 2] = v1
     c = oracle.encode(w, s, sh, bits, G)
     assert c[0, 0] == 0 and c[0, 1] == 0 and c[0, 2] == 1
+
+
+# ----------------------------------------------------------------------------
+# Routed-expert MLP step (Kimi K3 guide, model card)
+# ----------------------------------------------------------------------------
+def test_bf16_rne_nearest_and_ties_to_even():
+    import torch
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(2000) * np.exp(rng.standard_normal(2000) * 5)
+    r = oracle.bf16_rne(v)
+    # representable: float32 with the low 16 bits clear
+    bits = r.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0) and np.array_equal(r.astype(np.float32).astype(np.float64), r)
+    # the nearer neighbour: no bf16 value (r +- one spacing) is closer
+    up = (bits + 0x10000).view(np.float32).astype(np.float64)
+    dn = (bits - 0x10000).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(v - r) <= np.abs(v - up)) and np.all(np.abs(v - r) <= np.abs(v - dn))
+    # exact midpoints go to the even neighbour
+    lo = np.float32(1.0) + np.float32(2.0 ** -7) * np.arange(8, dtype=np.float32)
+    mid = lo.astype(np.float64) + 2.0 ** -8
+    got = oracle.bf16_rne(mid).astype(np.float32).view(np.uint32) >> 16
+    assert np.all(got % 2 == 0)
+    # agrees with torch's conversion of float32 inputs (single rounding there)
+    f = rng.standard_normal(500).astype(np.float32)
+    assert np.array_equal(oracle.bf16_rne(f.astype(np.float64)),
+                          torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy())
+
+
+def _mlp_expert(scale_up, scale_dn):
+    # H = 2, I = 1: gate row picks x[0], up row picks scale_up * x[1]; down = [[1], [scale_dn]]
+    GU = np.array([[1.0, 0.0], [0.0, scale_up]])
+    D = np.array([[1.0], [scale_dn]])
+    return GU, D
+
+
+def test_moe_mlp_closed_form_silu_times_up():
+    import math
+    import torch
+    s_vals = [1.7, -0.9, 3.3]
+    X = np.array([[s, 1.0] for s in s_vals], dtype=np.float32)
+    xb = (torch.from_numpy(X).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    xs = oracle.bf16_bits_to_f64(xb)[:, 0]
+    experts = {0: _mlp_expert(3.0, 2.0), 1: _mlp_expert(5.0, -1.0)}
+    ids = np.array([[0, 1], [1, 7], [0, 0]], dtype=np.int32)      # 7 is invalid
+    w = np.array([[0.25, 0.75], [2.0, 9.0], [0.5, 0.5]], dtype=np.float32)
+    y = oracle.moe_mlp(xb, ids, w, 2, lambda e: experts[e][0], lambda e: experts[e][1])
+    for t in range(3):
+        ref = np.zeros(2)
+        for j in range(2):
+            e = int(ids[t, j])
+            if e not in experts:
+                continue
+            su, sd = (3.0, 2.0) if e == 0 else (5.0, -1.0)
+            g = xs[t]
+            h = g / (1.0 + math.exp(-g)) * su
+            hb = torch.tensor(h, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).item()
+            assert hb == oracle.bf16_rne(np.array([h]))[0]
+            ref += float(w[t, j]) * np.array([hb, sd * hb])
+        assert np.allclose(y[t], ref, rtol=0, atol=1e-12), (t, y[t], ref)
+
+
+def test_moe_mlp_zero_cases():
+    xb = np.full((2, 2), 0x3F80, dtype=np.uint16)                   # x = 1
+    GU = np.array([[0.0, 0.0], [1.0, 1.0]])                         # gate 0 -> SiLU(0) = 0
+    D = np.array([[1.0], [1.0]])
+    y = oracle.moe_mlp(xb, np.array([[0], [0]], np.int32), np.ones((2, 1), np.float32), 1,
+                       lambda e: GU, lambda e: D)
+    assert not y.any()
+    GU2 = np.array([[1.0, 1.0], [1.0, 1.0]])
+    y2 = oracle.moe_mlp(xb, np.array([[0], [5]], np.int32), np.zeros((2, 1), np.float32), 1,
+                        lambda e: GU2, lambda e: D)
+    assert not y2.any()
+    y3 = oracle.moe_mlp(xb, np.array([[3], [4]], np.int32), np.ones((2, 1), np.float32), 1,
+                        lambda e: GU2, lambda e: D)
+    assert y3.shape == (2, 2) and not y3.any()                      # every id invalid
