@@ -24,7 +24,7 @@ __all__ = [
     "cubic_dequant", "cubic_encode", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
     "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode", "cubic_linear_workspace_bytes",
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
-    "EXPORTED_SYMBOLS",
+    "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = [
     "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_encode", "cubic_gemm_a16_workspace_bytes",
     "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode",
     "cubic_linear_workspace_bytes", "cubic_linear", "cubic_moe_workspace_bytes",
-    "cubic_moe_grouped_gemm",
+    "cubic_moe_grouped_gemm", "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
 ]
 MODE_A16, MODE_A8 = 0, 1          # cubic_linear_mode results
 
@@ -86,6 +86,8 @@ def load_library():
         "cubic_linear": (i32, [vp, i64, wp, vp, vp, sz, vp]),
         "cubic_moe_workspace_bytes": (sz, [i64, i32, i32, i64]),
         "cubic_moe_grouped_gemm": (i32, [vp, i64, vp, i32, wp, i32, vp, vp, sz, vp]),
+        "cubic_moe_mlp_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
+        "cubic_moe_mlp": (i32, [vp, i64, vp, vp, i32, wp, wp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -287,4 +289,29 @@ def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: Cub
     _check(load_library().cubic_moe_grouped_gemm(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw),
                                                  E, _ptr(out), _ptr(workspace), workspace.numel(),
                                                  _stream(x)), "cubic_moe_grouped_gemm")
+    return out
+
+
+def cubic_moe_mlp_workspace_bytes(T: int, topk: int, E: int, H: int, I: int) -> int:
+    return int(load_library().cubic_moe_mlp_workspace_bytes(T, topk, E, H, I))
+
+
+def cubic_moe_mlp(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                  gate_up: CubicWeight, down: CubicWeight, E: int, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[T][H] (fp32): sum_j w[t][j] * (bf16(SiLU(gate) * up) of token t through expert
+    topk_ids[t][j]'s gate_up) through that expert's down projection."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_weights, torch.float32, "topk_weights")
+    T, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((T, down.N), dtype=torch.float32, device=x.device)
+    need = cubic_moe_mlp_workspace_bytes(T, topk, E, gate_up.K, down.K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    gu, dn = gate_up.c_struct(), down.c_struct()
+    _check(load_library().cubic_moe_mlp(_ptr(x), T, _ptr(topk_ids), _ptr(topk_weights), topk,
+                                        ctypes.byref(gu), ctypes.byref(dn), E, _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(x)), "cubic_moe_mlp")
     return out

@@ -267,6 +267,82 @@ MoeLayout moe_layout(int64_t T, int topk, int E) {
 }
 }  // namespace
 
+namespace {
+struct MlpLayout {
+  MoeLayout route;
+  size_t y1, h, y2, total;
+};
+MlpLayout mlp_layout(int64_t T, int topk, int E, int64_t H, int64_t I) {
+  MlpLayout L;
+  L.route = moe_layout(T, topk, E);
+  const size_t P = static_cast<size_t>(T) * topk;
+  size_t o = L.route.total;
+  L.y1 = o;  o += align256(P * static_cast<size_t>(2 * I) * 4);
+  L.h = o;   o += align256(P * static_cast<size_t>(I) * 2);
+  L.y2 = o;  o += align256(P * static_cast<size_t>(H) * 4);
+  L.total = o;
+  return L;
+}
+
+int moe_weight_fits(const cubic_weight* w) {
+  if (w->K > 0 && (!gemv_supported(w->K, w->bits, w->group) ||
+                   moe_lds_min_bytes(w->K, w->bits, w->group) > kLdsLimit))
+    return CUBIC_ERR_SHAPE;
+  return CUBIC_OK;
+}
+}  // namespace
+
+CUBIC_API size_t cubic_moe_mlp_workspace_bytes(int64_t T, int topk, int E, int64_t H, int64_t I) {
+  if (T < 0 || topk <= 0 || E <= 0 || H < 0 || I < 0) return 0;
+  return mlp_layout(T, topk, E, H, I).total;
+}
+
+CUBIC_API int cubic_moe_mlp(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                            const float* topk_weights, int topk, const cubic_weight* gate_up0,
+                            const cubic_weight* down0, int E, float* y, void* workspace, size_t ws_bytes,
+                            cubic_stream_t stream) {
+  int st = check_weight(gate_up0);
+  if (st != CUBIC_OK) return st;
+  st = check_weight(down0);
+  if (st != CUBIC_OK) return st;
+  if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
+  const int64_t H = gate_up0->K, I = down0->K;
+  if (gate_up0->N != 2 * I || down0->N != H || H == 0 || I == 0) return CUBIC_ERR_SHAPE;
+  if (T == 0) return CUBIC_OK;
+  if (T * topk > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
+  if ((st = moe_weight_fits(gate_up0)) != CUBIC_OK || (st = moe_weight_fits(down0)) != CUBIC_OK) return st;
+  if (!x_bf16 || !topk_ids || !topk_weights || !y || !workspace) return CUBIC_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(topk_weights) || !aligned16(y) ||
+      !aligned16(workspace))
+    return CUBIC_ERR_ALIGN;
+  const MlpLayout L = mlp_layout(T, topk, E, H, I);
+  if (ws_bytes < L.total) return CUBIC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  auto params = [&](const cubic_weight* w, const uint16_t* x, float* out) {
+    MoeGemvParams p{};
+    p.codes = w->codes;
+    p.scales = w->scales;
+    p.shapes = w->shapes;
+    p.N = w->N;
+    p.K = w->K;
+    p.group = w->group;
+    p.topk = topk;
+    p.code_bytes = static_cast<int64_t>(cubic_code_bytes(w->N, w->K, w->bits));
+    p.x = x;
+    p.y = out;
+    return p;
+  };
+  float* y1 = reinterpret_cast<float*>(ws + L.y1);
+  float* y2 = reinterpret_cast<float*>(ws + L.y2);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  const hipError_t e = launch_moe_mlp(
+      topk_ids, topk_weights, static_cast<int>(T), E, topk, params(gate_up0, x_bf16, y1), gate_up0->bits,
+      params(down0, h, y2), down0->bits, reinterpret_cast<int32_t*>(ws + L.route.hdr),
+      reinterpret_cast<int32_t*>(ws + L.route.erec), reinterpret_cast<int32_t*>(ws + L.route.sorted), h, y,
+      static_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
 CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K) {
   if (T < 0 || topk <= 0 || E <= 0 || K < 0) return 0;
   return moe_layout(T, topk, E).total;

@@ -569,16 +569,10 @@ size_t moe_lds_min_bytes(int64_t K, int bits, int group) {
   return bits == 2 ? moe_lds_bytes<DecodeW2>(geo, 1) : moe_lds_bytes<DecodeTable<8>>(geo, 1);
 }
 
-hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
-                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st) {
-  const int P = T * topk;
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, hdr,
-                     erec, sorted);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  MoeGemvParams p = base;
-  p.topk = topk;
-  p.hdr = hdr; p.erec = erec; p.sorted = sorted;
+// The grouped product over a routing already in hdr / erec / sorted (p holds
+// them): P pairs, activation row of pair q = q / p.topk, output row q.
+static hipError_t launch_moe_product(const MoeGemvParams& p, int P, int E, int T, int bits,
+                                     hipStream_t st) {
   const int64_t tiles = (p.N + 15) / 16;
   const int64_t blocks = static_cast<int64_t>(min(E, P)) * tiles;
   if (blocks == 0) return hipSuccess;
@@ -600,6 +594,93 @@ hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvP
     case 7: return launch_moe_gemv_t<DecodeDirect<7, false>, 1, 2>(p, blocks, T, st);
     default: return launch_moe_gemv_t<DecodeDirect<8, false>, 1, 2>(p, blocks, T, st);
   }
+}
+
+hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
+                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st) {
+  const int P = T * topk;
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, hdr,
+                     erec, sorted);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  MoeGemvParams p = base;
+  p.topk = topk;
+  p.hdr = hdr; p.erec = erec; p.sorted = sorted;
+  return launch_moe_product(p, P, E, T, bits, st);
+}
+
+// ---------------------------------------------------------------------------
+// The routed-expert MLP step around the two grouped products: h = SiLU(gate) *
+// up in fp32, rounded to bf16 (the down product's activation rows, one per
+// pair), and the router-weighted sum of each token's pair outputs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_moe_act(const float* __restrict__ y1, int64_t P, int64_t I,
+                                                 uint16_t* __restrict__ h) {
+  const int64_t nvec = P * I / 4;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+       v += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t q = v / (I / 4), i = (v - q * (I / 4)) * 4;
+    const f32x4 g = *reinterpret_cast<const f32x4*>(y1 + q * 2 * I + i);
+    const f32x4 u = *reinterpret_cast<const f32x4*>(y1 + q * 2 * I + I + i);
+    uint32_t o[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float h0 = g[2 * e] / (1.0f + expf(-g[2 * e])) * u[2 * e];
+      const float h1 = g[2 * e + 1] / (1.0f + expf(-g[2 * e + 1])) * u[2 * e + 1];
+      o[e] = bf16_rne_bits(h0) | (bf16_rne_bits(h1) << 16);
+    }
+    *reinterpret_cast<uint2*>(h + q * I + i) = make_uint2(o[0], o[1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y2,
+                                                     const int32_t* __restrict__ ids,
+                                                     const float* __restrict__ w, int64_t T, int topk,
+                                                     int E, int64_t H, float* __restrict__ out) {
+  const int64_t nvec = T * H / 4;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; v < nvec;
+       v += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = v / (H / 4), n = (v - t * (H / 4)) * 4;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < topk; ++j) {           // slot order: deterministic
+      const int64_t q = t * topk + j;
+      const int id = ids[q];
+      if (id < 0 || id >= E) continue;         // invalid ids add nothing
+      const float wj = w[q];
+      const f32x4 r = *reinterpret_cast<const f32x4*>(y2 + q * H + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wj, r[e], acc[e]);
+    }
+    *reinterpret_cast<f32x4*>(out + t * H + n) = acc;
+  }
+}
+
+static unsigned elementwise_grid(int64_t nvec) {
+  const int64_t b = (nvec + 255) / 256;
+  return static_cast<unsigned>(b < 8192 ? (b > 0 ? b : 1) : 8192);
+}
+
+hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E, int topk,
+                          const MoeGemvParams& up, int up_bits, const MoeGemvParams& dn, int dn_bits,
+                          int32_t* hdr, int32_t* erec, int32_t* sorted, uint16_t* h, float* out,
+                          hipStream_t st) {
+  const int P = T * topk;
+  const int64_t I = dn.K, H = dn.N;
+  hipError_t err = launch_moe(ids, T, E, topk, up, hdr, erec, sorted, up_bits, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_moe_act, dim3(elementwise_grid(P * I / 4)), dim3(256), 0, st, up.y,
+                     static_cast<int64_t>(P), I, h);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  MoeGemvParams p = dn;
+  p.topk = 1;                                  // one activation row per pair
+  p.x = h;
+  p.hdr = hdr; p.erec = erec; p.sorted = sorted;
+  err = launch_moe_product(p, P, E, T, dn_bits, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_moe_combine, dim3(elementwise_grid(static_cast<int64_t>(T) * H / 4)), dim3(256), 0,
+                     st, dn.y, ids, topk_w, static_cast<int64_t>(T), topk, E, H, out);
+  return hipGetLastError();
 }
 
 }  // namespace cubic

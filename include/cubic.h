@@ -188,6 +188,28 @@ int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
                            float* y, void* workspace, size_t ws_bytes,
                            cubic_stream_t stream);
 
+/* The routed-expert MLP step of a Kimi-K3-style layer (Kimi K3 guide, model
+ * card: routed experts with a fused gate_up and a down projection; CubicQuant
+ * article, A16/A8 section: the expert weights are Cubic-coded):
+ *   [g | u] = x_t * GU_e^T    (gate_up expert e: N = 2I rows, K = H; gate rows
+ *                              0 .. I-1, up rows I .. 2I-1), for every pair (t, j)
+ *   h       = bf16(SiLU(g) * u)          (fp32, rounded to bf16, nearest even)
+ *   o_tj    = h * D_e^T       (down expert e: N = H rows, K = I)
+ *   y[t]    = sum_j topk_weights[t][j] * o_tj   (fp32, slots in order)
+ * e = topk_ids[t][j]; pairs with ids outside [0, E) add nothing. Experts of each
+ * kind lie back to back as in cubic_moe_grouped_gemm (gate_up0, down0: expert 0).
+ * x_bf16 [T][H], topk_ids int32 [T][topk], topk_weights fp32 [T][topk], y fp32
+ * [T][H]. One routing feeds both grouped products; the intermediates live in
+ * the workspace (routing records, then [T*topk][2I] fp32, [T*topk][I] bf16 and
+ * [T*topk][H] fp32), whose size cubic_moe_mlp_workspace_bytes gives. Errors as
+ * for cubic_moe_grouped_gemm; CUBIC_ERR_SHAPE when the two weights disagree
+ * (gate_up N != 2 * down K or down N != gate_up K). */
+size_t cubic_moe_mlp_workspace_bytes(int64_t T, int topk, int E, int64_t H, int64_t I);
+int cubic_moe_mlp(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                  const float* topk_weights, int topk, const cubic_weight* gate_up0,
+                  const cubic_weight* down0, int E, float* y, void* workspace, size_t ws_bytes,
+                  cubic_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,6 +102,26 @@ def test_encode_validation_before_launch():
     assert lib.cubic_encode(p16, 0, 512, 3, 128, None, None, None, None) == OK    # no-op
 
 
+def test_moe_mlp_validation_before_launch():
+    lib = cq.load_library()
+    p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
+    gu = _w(N=1024, K=512, bits=2, group=256)         # H = 512, I = 512
+    dn = _w(N=512, K=512, bits=2, group=256)
+    need = lib.cubic_moe_mlp_workspace_bytes(4, 2, 8, 512, 512)
+    assert need >= 4 * 2 * (1024 * 4 + 512 * 2 + 512 * 4)
+    assert lib.cubic_moe_mlp(p16, 4, p16, p16, 2, ctypes.byref(gu), ctypes.byref(dn), 8, p16, p16, need - 1,
+                             None) == ERR_WS
+    bad = _w(N=500, K=512, bits=2, group=256)         # gate_up rows != 2 x down K
+    assert lib.cubic_moe_mlp(p16, 4, p16, p16, 2, ctypes.byref(bad), ctypes.byref(dn), 8, p16, p16, need,
+                             None) == ERR_SHAPE
+    assert lib.cubic_moe_mlp(p16, 4, None, p16, 2, ctypes.byref(gu), ctypes.byref(dn), 8, p16, p16, need,
+                             None) == ERR_NULL
+    assert lib.cubic_moe_mlp(p16, 4, p16, p8, 2, ctypes.byref(gu), ctypes.byref(dn), 8, p16, p16, need,
+                             None) == ERR_ALIGN
+    assert lib.cubic_moe_mlp(p16, 0, p16, p16, 2, ctypes.byref(gu), ctypes.byref(dn), 8, p16, p16, need,
+                             None) == OK                                       # no-op
+
+
 def _w(N=256, K=512, bits=3, group=128, codes=16, scales=16, shapes=16):
     return cq._CWeight(codes, scales, shapes, N, K, bits, group)
 

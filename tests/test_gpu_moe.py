@@ -178,3 +178,48 @@ def test_sparse_extra_codes_routed(T):
     y = cq.cubic_moe_grouped_gemm(x, ids, pool, E).cpu().numpy()
     ref = oracle.moe_a16(x_bits(x), ids.cpu().numpy(), E, N, lambda e: dense[e])
     assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
+
+
+# The MLP step composes two products through h = SiLU(g) * u ~ g u sigma(g): an
+# error of eps (relative to a row's largest value) in g and u becomes about
+# 2 eps (max / typical) in h, the bf16 rounding of h adds 2^-9, and the down
+# product adds eps again. With the products' bar eps = 2e-3 and max / typical
+# about 2 for these rows, the step's bar is 1e-2. Swapped halves, a wrong
+# router weight or a lost term give errors of order one.
+TOL_MLP = 1e-2
+
+
+@pytest.mark.parametrize("bits,group,T,topk,E", [(2, 256, 20, 2, 6), (4, 128, 20, 2, 6), (2, 512, 1, 4, 16)])
+def test_moe_mlp_step(bits, group, T, topk, E):
+    """cubic_moe_mlp: gate_up and down experts, SiLU * up in bf16, router-weighted sum."""
+    say(f"MoE MLP step bits={bits} G={group} T={T} topk={topk} E={E}")
+    H, I = 1024, 512
+    gu = _pool(E, 2 * I, H, bits, group, seed=80 + bits)
+    dn = _pool(E, H, I, bits, group, seed=90 + bits)
+    x, ids = synth.moe_routing(seed=81, T=T, E=E, topk=topk, K=H, device=DEV)
+    if T > 1:
+        ids[3, 1] = -1                                   # invalid ids add nothing
+        ids[5, 0] = E
+    w = torch.rand((T, topk), generator=torch.Generator().manual_seed(82)).to(DEV)
+    y = cq.cubic_moe_mlp(x, ids, w, gu, dn, E)
+    y2 = cq.cubic_moe_mlp(x, ids, w, gu, dn, E)
+    assert torch.equal(y, y2)
+    ref = oracle.moe_mlp(x_bits(x), ids.cpu().numpy(), w.cpu().numpy(), E,
+                         lambda e: _expert_dense(e, 2 * I, H, bits, group, 80 + bits),
+                         lambda e: _expert_dense(e, H, I, bits, group, 90 + bits))
+    assert row_rel_err(y.cpu().numpy(), ref) <= TOL_MLP
+
+
+def test_moe_mlp_k3_dims_few_tokens():
+    """Kimi K3 expert dims (hidden 7168, intermediate 3072), W2 G512, 2 tokens x top-2."""
+    say("MoE MLP step K3 dims, 2 tokens x top-2 of 4 experts")
+    E, T, topk, H, I, bits, group = 4, 2, 2, 7168, 3072, 2, 512
+    gu = _pool(E, 2 * I, H, bits, group, seed=84)
+    dn = _pool(E, H, I, bits, group, seed=85)
+    x, ids = synth.moe_routing(seed=86, T=T, E=E, topk=topk, K=H, device=DEV)
+    w = torch.tensor([[0.6, 0.4], [0.3, 0.7]], dtype=torch.float32, device=DEV)
+    y = cq.cubic_moe_mlp(x, ids, w, gu, dn, E).cpu().numpy()
+    ref = oracle.moe_mlp(x_bits(x), ids.cpu().numpy(), w.cpu().numpy(), E,
+                         lambda e: _expert_dense(e, 2 * I, H, bits, group, 84),
+                         lambda e: _expert_dense(e, H, I, bits, group, 85))
+    assert row_rel_err(y, ref) <= TOL_MLP
