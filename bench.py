@@ -394,6 +394,19 @@ def _graph_time(calls, reps, dev):
     return a.elapsed_time(b) / reps / len(calls)
 
 
+def _leg(res, key, val):
+    """Store one extra leg's result and report it on stderr as it finishes."""
+    import sys
+    res[key] = val
+    print(json.dumps({key: val}), file=sys.stderr, flush=True)
+
+
+def _report(res, key):
+    """One extra leg done: its result on stderr, as progress."""
+    import sys
+    print(json.dumps({key: res[key]}), file=sys.stderr, flush=True)
+
+
 def extra_workloads(cq, synth, dev, stream):
     """The other workloads, each timed as graph replays: prefill (M = 4096, W3
     G256) A16 and Dynamic A8, small-batch W4 G128 (M = 8, 64) over rotating
@@ -411,6 +424,7 @@ def extra_workloads(cq, synth, dev, stream):
     res["prefill_a16"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
                           "frac_of_f16_peak": round(flops / ms / 1e9 / MFMA_F16_PEAK_TFS, 4),
                           "includes": "activation prep kernel + product kernel"}
+    _report(res, "prefill_a16")
     xq = torch.empty((4096, 7168), dtype=torch.int8, device=dev)
     sx = torch.empty((4096,), dtype=torch.float32, device=dev)
     # the quantiser is HBM-bound: six input/output sets (528 MB) rotate, more
@@ -424,6 +438,7 @@ def extra_workloads(cq, synth, dev, stream):
                          "TOP/s": round(flops / ms8 / 1e9, 2),
                          "frac_of_i8_peak": round(flops / ms8 / 1e9 / MFMA_I8_PEAK_TOPS, 4),
                          "act_quant_GB/s": round((4096 * 7168 * 3 + 4096 * 4) / ms_q / 1e6, 1)}
+    _report(res, "prefill_a8")
     del x, xq, y, ws, cw
     torch.cuda.empty_cache()
     copies = 16
@@ -442,6 +457,7 @@ def extra_workloads(cq, synth, dev, stream):
             nb = algorithmic_bytes(ww.N, ww.K, 4, 128, M)
             res[f"smallm_w4_M{M}_{name}"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
                                               "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+            _report(res, f"smallm_w4_M{M}_{name}")
             del pool, base
         del wu, wd
         torch.cuda.empty_cache()
@@ -467,21 +483,27 @@ def encode_workloads(cq, synth, dev):
         nb = N * K * 5 + 8 * N * (K // group)
         res[f"encode_w{bits}g{group}_gate_up"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
                                                    "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        _report(res, f"encode_w{bits}g{group}_gate_up")
         del xs, w
         torch.cuda.empty_cache()
     return res
 
 
 def moe_workloads(cq, synth, dev):
-    """Routed experts, gate_up 6144 x 7168 W2 G512 at the decode distributions.
-    Decode step: one token routed to 16 of 64 resident experts, a different set
-    per launch. C4: 64 tokens x top-16 over 896 experts (~620 touched)."""
+    """Routed experts at the decode distributions, W2 G512: gate_up 6144 x 7168
+    (the grouped product) and the whole MLP step (gate_up, SiLU * up in bf16,
+    down 7168 x 3072, router-weighted sum). Decode step: one token routed to 16
+    of 64 resident experts, a different set per launch. Batch: 64 tokens x top-16
+    over 896 experts (~600 touched). Algorithmic bytes: the touched experts'
+    codes and group parameters plus activations in and outputs out; the step's
+    intermediates ([P][2I] fp32, [P][I] bf16, [P][H] fp32 for P routed pairs)
+    are not counted."""
     import torch
     res = {}
-    N, K, bits, group = 6144, 7168, 2, 512
-    cb = N * K * bits // 8
+    H, I, bits, group = 7168, 3072, 2, 512
 
-    def pool(E, seed):
+    def pool(E, seed, N, K):
+        cb = N * K * bits // 8
         codes = torch.empty(E * cb, dtype=torch.uint8, device=dev)
         scales = torch.empty((E, N, K // group), dtype=torch.float32, device=dev)
         shapes = torch.empty((E, N, K // group, 2), dtype=torch.int16, device=dev)
@@ -492,35 +514,57 @@ def moe_workloads(cq, synth, dev):
             shapes[e] = w.shapes
         return cq.CubicWeight(codes, scales.reshape(-1), shapes.reshape(-1), N, K, bits, group)
 
-    expert_bytes = cb + 8 * N * (K // group)
-    E = 64
-    p = pool(E, 4)
-    x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=16, K=K, device=dev)
+    def expert_bytes(N, K):
+        return N * K * bits // 8 + 8 * N * (K // group)
+
+    def row(ms, nb, **kw):
+        r = {"us": round(ms * 1e3, 2)} if ms < 1 else {"ms": round(ms, 4)}
+        r.update({"GB/s": round(nb / ms / 1e6, 1), "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4)})
+        r.update(kw)
+        return r
+
+    gu_b, dn_b = expert_bytes(2 * I, H), expert_bytes(H, I)
+    E, topk = 64, 16
+    gu, dn = pool(E, 4, 2 * I, H), pool(E, 6, H, I)
+    x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=topk, K=H, device=dev)
     g = torch.Generator().manual_seed(7)
-    ids = [torch.randperm(E, generator=g)[:16].to(torch.int32).view(1, 16).to(dev) for _ in range(8)]
-    wsb = cq.cubic_moe_workspace_bytes(1, 16, E, K)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    y = torch.empty((1, 16, N), dtype=torch.float32, device=dev)
-    ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm(x, i, p, E, out=y, workspace=ws))
+    ids = [torch.randperm(E, generator=g)[:topk].to(torch.int32).view(1, topk).to(dev) for _ in range(8)]
+    tw = torch.softmax(torch.rand((1, topk), generator=g), dim=1).to(dev)
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E, H), dtype=torch.uint8, device=dev)
+    y = torch.empty((1, topk, 2 * I), dtype=torch.float32, device=dev)
+    ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm(x, i, gu, E, out=y, workspace=ws))
                       for i in ids], 5, dev)
-    nb = 16 * expert_bytes + K * 2 + 16 * N * 4
-    res["moe_decode_1tok_top16"] = {"us": round(ms * 1e3, 2), "GB/s": round(nb / ms / 1e6, 1),
-                                    "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4),
-                                    "bytes_per_launch": nb}
-    del p, ws, y
+    nb = topk * gu_b + H * 2 + topk * 2 * I * 4
+    res["moe_decode_1tok_top16"] = row(ms, nb, bytes_per_launch=nb)
+    _report(res, "moe_decode_1tok_top16")
+    wsm = torch.empty(cq.cubic_moe_mlp_workspace_bytes(1, topk, E, H, I), dtype=torch.uint8, device=dev)
+    ym = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ms = _graph_time([(lambda i=i: cq.cubic_moe_mlp(x, i, tw, gu, dn, E, out=ym, workspace=wsm))
+                      for i in ids], 5, dev)
+    nb = topk * (gu_b + dn_b) + H * 2 + H * 4
+    res["moe_mlp_decode_1tok_top16"] = row(ms, nb, bytes_per_launch=nb)
+    _report(res, "moe_mlp_decode_1tok_top16")
+    del gu, dn, ws, wsm, y
     torch.cuda.empty_cache()
     E, T = 896, 64
-    p = pool(E, 4)
-    x, tid = synth.moe_routing(seed=4, T=T, E=E, topk=16, K=K, device=dev)
+    gu, dn = pool(E, 4, 2 * I, H), pool(E, 6, H, I)
+    x, tid = synth.moe_routing(seed=4, T=T, E=E, topk=topk, K=H, device=dev)
+    tw = torch.softmax(torch.rand((T, topk), generator=torch.Generator().manual_seed(8)), dim=1).to(dev)
     touched = int(torch.unique(tid).numel())
-    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, 16, E, K), dtype=torch.uint8, device=dev)
-    y = torch.empty((T, 16, N), dtype=torch.float32, device=dev)
-    ms = _graph_time([lambda: cq.cubic_moe_grouped_gemm(x, tid, p, E, out=y, workspace=ws)], 3, dev)
-    nb = touched * expert_bytes + T * K * 2 + T * 16 * N * 4
-    res["moe_896x64tok_top16"] = {"ms": round(ms, 4), "GB/s": round(nb / ms / 1e6, 1),
-                                  "frac_of_hbm_peak": round(nb / ms / 1e6 / HBM_PEAK_GBS, 4),
-                                  "touched_experts": touched}
-    del p, ws, y
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E, H), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, topk, 2 * I), dtype=torch.float32, device=dev)
+    ms = _graph_time([lambda: cq.cubic_moe_grouped_gemm(x, tid, gu, E, out=y, workspace=ws)], 3, dev)
+    nb = touched * gu_b + T * H * 2 + T * topk * 2 * I * 4
+    res["moe_896x64tok_top16"] = row(ms, nb, touched_experts=touched)
+    _report(res, "moe_896x64tok_top16")
+    del ws, y
+    wsm = torch.empty(cq.cubic_moe_mlp_workspace_bytes(T, topk, E, H, I), dtype=torch.uint8, device=dev)
+    ym = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ms = _graph_time([lambda: cq.cubic_moe_mlp(x, tid, tw, gu, dn, E, out=ym, workspace=wsm)], 3, dev)
+    nb = touched * (gu_b + dn_b) + T * H * 2 + T * H * 4
+    res["moe_mlp_896x64tok_top16"] = row(ms, nb, touched_experts=touched)
+    _report(res, "moe_mlp_896x64tok_top16")
+    del gu, dn, wsm, ym
     torch.cuda.empty_cache()
     return res
 

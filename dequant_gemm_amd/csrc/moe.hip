@@ -642,14 +642,29 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y
        v += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t t = v / (H / 4), n = (v - t * (H / 4)) * 4;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < topk; ++j) {           // slot order: deterministic
-      const int64_t q = t * topk + j;
-      const int id = ids[q];
-      if (id < 0 || id >= E) continue;         // invalid ids add nothing
-      const float wj = w[q];
-      const f32x4 r = *reinterpret_cast<const f32x4*>(y2 + q * H + n);
+    // Eight slots at a time: every load of a chunk is issued before the first
+    // sum (rows q < T * topk all lie inside y2, so a slot past topk or with an
+    // invalid id loads a row in bounds and is then left out); the sums still
+    // run in slot order, so the result does not depend on the chunking.
+    for (int j0 = 0; j0 < topk; j0 += 8) {
+      bool ok[8];
+      float wj[8];
+      f32x4 r[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wj, r[e], acc[e]);
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u < topk ? j0 + u : topk - 1;
+        const int64_t q = t * topk + j;
+        const int id = ids[q];
+        ok[u] = j0 + u < topk && id >= 0 && id < E;    // invalid ids add nothing
+        wj[u] = w[q];
+        r[u] = *reinterpret_cast<const f32x4*>(y2 + q * H + n);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!ok[u]) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wj[u], r[u][e], acc[e]);
+      }
     }
     *reinterpret_cast<f32x4*>(out + t * H + n) = acc;
   }
