@@ -62,6 +62,7 @@ __all__ = [
     "level_numerators", "levels", "dequant", "gemm_a16",
     "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
     "encode_levels_f32", "encode", "bf16_rne", "moe_mlp",
+    "FIT_CLIP_STEPS", "fit_is_monotone", "fit_shape_candidates", "f64_to_f16_bits", "fit_group_sse", "fit",
 ]
 
 # Domain in which the float64 evaluation of Q_j is exact (see module docstring).
@@ -352,6 +353,107 @@ def encode(w: np.ndarray, scales: np.ndarray, shapes: np.ndarray, bits: int,
     neg = np.signbit(w.reshape(N, G, group)) != np.signbit(s)[..., None]
     k = np.where(neg, -best_j, best_j)
     return k.reshape(N, K).astype(np.int8)
+
+
+# ----------------------------------------------------------------------------
+# Data-free group fitting (CubicQuant article, the section on data-free in-group
+# fitting: per group, search monotone (a, b) candidates, choose the scale together
+# with a soft-clip threshold, give every weight its nearest level, store a, b as
+# fp16 and s as fp32). The pages fix neither the search grid nor the loss; this
+# library's reading: the loss is the group's sum of squared weight errors, a and b
+# run over multiples of 1/8 (a in [0, 3], b in [-3, 3], exact in fp16, so the fp16
+# step changes nothing), and the clip threshold is the scale itself,
+# s = fl32(rho * max|w|) with rho = 1 - r/32, r = 0 .. 15: weights beyond s take
+# the top level. Codes follow the nearest-level rule of `encode`.
+# ----------------------------------------------------------------------------
+FIT_CLIP_STEPS = 16
+
+
+def fit_is_monotone(a: Fraction, b: Fraction) -> bool:
+    """True when q(t) = a t + b t^2 + (1-a-b) t^3 is non-decreasing on [0, 1]:
+    q'(t) = a + 2 b t + 3 c t^2 >= 0 at both ends and at an interior stationary point."""
+    c = 1 - a - b
+
+    def dq(t):
+        return a + 2 * b * t + 3 * c * t * t
+
+    if dq(Fraction(0)) < 0 or dq(Fraction(1)) < 0:
+        return False
+    if c != 0:
+        t = -b / (3 * c)
+        if 0 < t < 1 and dq(t) < 0:
+            return False
+    return True
+
+
+def fit_shape_candidates() -> np.ndarray:
+    """(a, b) pairs of the search in search order, float64 [n][2]: a = i/8 for
+    i = 0 .. 24 (outer), b = j/8 for j = -24 .. 24 (inner), monotone pairs only."""
+    out = []
+    for i in range(0, 25):
+        for j in range(-24, 25):
+            a, b = Fraction(i, 8), Fraction(j, 8)
+            if fit_is_monotone(a, b):
+                out.append((float(a), float(b)))
+    return np.array(out, dtype=np.float64)
+
+
+def f64_to_f16_bits(v: np.ndarray) -> np.ndarray:
+    """Exact fp16 bit patterns of float64 values that fp16 represents."""
+    h = np.asarray(v, dtype=np.float64).astype(np.float16)
+    if not np.array_equal(h.astype(np.float64), np.asarray(v, dtype=np.float64)):
+        raise ValueError("value not representable in fp16")
+    return h.view(np.uint16)
+
+
+def fit_group_sse(wg: np.ndarray, bits: int, ab: np.ndarray):
+    """Losses of every candidate for one group of float32 weights wg [G]:
+    float64 [n_ab][FIT_CLIP_STEPS], the exact squared distance of each weight to
+    the fp32 level that `encode`'s rule picks, summed over the group."""
+    wg = np.asarray(wg, dtype=np.float32)
+    aw = np.abs(wg)
+    amax = aw.max() if aw.size else np.float32(0.0)
+    rho = (np.float32(1.0) - np.arange(FIT_CLIP_STEPS, dtype=np.float32) / np.float32(32.0)).astype(np.float32)
+    s = (rho * amax).astype(np.float32)                         # [R], one fp32 rounding each
+    q = encode_levels_f32(ab[:, 0], ab[:, 1], bits)            # [n][L] float32
+    out = np.empty((len(ab), FIT_CLIP_STEPS), dtype=np.float64)
+    step = max(1, (1 << 23) // (FIT_CLIP_STEPS * q.shape[1] * max(1, aw.size)))
+    for c0 in range(0, len(ab), step):                         # chunks of pairs bound the memory
+        v = (s[None, :, None] * q[c0:c0 + step, None, :]).astype(np.float32)  # [n][R][L] fp32 levels
+        d = np.abs(aw[None, None, None, :] - v[..., None])     # [n][R][L][G] fp32 differences
+        j = np.argmin(d, axis=2)                               # first nearest level
+        vj = np.take_along_axis(v, j, axis=2).astype(np.float64)  # [n][R][G]
+        e = aw.astype(np.float64)[None, None, :] - vj
+        out[c0:c0 + step] = (e * e).sum(axis=2)
+    return out, s
+
+
+def fit(w: np.ndarray, bits: int, group: int):
+    """Fit every group of float32 weights w [N][K]: returns (codes int8 [N][K],
+    scales float32 [N][K/group], shapes fp16 bits [N][K/group][2], loss float64
+    [N][K/group], candidate index int64 [N][K/group] = shape index * 16 + r).
+    The first candidate of smallest loss wins."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of group")
+    G = K // group
+    ab = fit_shape_candidates()
+    scales = np.zeros((N, G), dtype=np.float32)
+    shapes = np.zeros((N, G, 2), dtype=np.uint16)
+    loss = np.zeros((N, G), dtype=np.float64)
+    index = np.zeros((N, G), dtype=np.int64)
+    for n in range(N):
+        for g in range(G):
+            sse, s = fit_group_sse(w[n, g * group:(g + 1) * group], bits, ab)
+            k = int(np.argmin(sse.reshape(-1)))
+            i, r = divmod(k, FIT_CLIP_STEPS)
+            scales[n, g] = s[r]
+            shapes[n, g] = f64_to_f16_bits(ab[i])
+            loss[n, g] = sse.reshape(-1)[k]
+            index[n, g] = k
+    codes = encode(w, scales, shapes, bits, group)
+    return codes, scales, shapes, loss, index
 
 
 # ----------------------------------------------------------------------------

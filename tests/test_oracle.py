@@ -556,3 +556,142 @@ def test_moe_mlp_zero_cases():
     y3 = oracle.moe_mlp(xb, np.array([[3], [4]], np.int32), np.ones((2, 1), np.float32), 1,
                         lambda e: GU2, lambda e: D)
     assert y3.shape == (2, 2) and not y3.any()                      # every id invalid
+
+
+# ---------------------------------------------------------------------------
+# Data-free group fitting (CubicQuant article, data-free in-group fitting; the
+# W4 G128 reconstruction table of its results section)
+# ---------------------------------------------------------------------------
+def test_fit_candidates_are_the_monotone_grid_pairs():
+    """Membership decided by sampling q' densely on [0, 1] (independent of the
+    exact rational test): every kept pair is non-decreasing, every dropped one dips."""
+    ab = {tuple(p) for p in oracle.fit_shape_candidates()}
+    t = np.linspace(0.0, 1.0, 20001)
+    kept = 0
+    for i in range(25):
+        for j in range(-24, 25):
+            a, b = i / 8, j / 8
+            c = 1 - a - b
+            dq = a + 2 * b * t + 3 * c * t * t
+            mono = dq.min() >= -1e-12
+            assert ((a, b) in ab) == mono, (a, b, dq.min())
+            kept += mono
+    assert kept == len(ab) == 532
+    order = oracle.fit_shape_candidates()
+    assert tuple(order[0]) == (0.0, 0.0) and tuple(order[-1]) == (3.0, -3.0)
+    assert (1.0, 0.0) in ab                                  # the uniform INT grid is a candidate
+
+
+def test_fit_matches_per_candidate_brute_force():
+    """A tiny group: every candidate's loss recomputed one by one through `encode`
+    and the fp32 levels, then the first minimum; fit's vectorised search agrees."""
+    rng = np.random.default_rng(11)
+    bits, G = 3, 128
+    w = (rng.standard_normal((1, G)) * 0.05).astype(np.float32)
+    ab = oracle.fit_shape_candidates()
+    amax = np.abs(w).max()
+    best, best_k = np.inf, -1
+    for i in range(0, len(ab), 7):                           # a spread of pairs, all 16 clips each
+        sh = oracle.f64_to_f16_bits(ab[i]).reshape(1, 1, 2)
+        q = oracle.encode_levels_f32(ab[i, 0], ab[i, 1], bits)
+        for r in range(16):
+            s = np.float32(np.float32(1 - r / 32) * amax)
+            k = oracle.encode(w, np.array([[s]], dtype=np.float32), sh, bits, G)[0]
+            lv = (s * q[np.abs(k).astype(int)]).astype(np.float64)
+            e = np.abs(w[0].astype(np.float64)) - lv
+            L = float((e * e).sum())
+            if L < best:
+                best, best_k = L, i * 16 + r
+    sse, _ = oracle.fit_group_sse(w[0], bits, ab[::7])
+    flat = sse.reshape(-1)
+    k = int(np.argmin(flat))
+    assert flat[k] == best and (k // 16) * 7 * 16 + k % 16 == best_k
+
+
+def test_fit_recovers_planted_levels_exactly():
+    """Weights placed exactly on the fp32 levels of a grid candidate with rho = 1
+    (some weight at the top level): the fit's loss is 0 and it returns those codes."""
+    rng = np.random.default_rng(12)
+    bits, G = 4, 128
+    a, b = 0.375, 1.25                                       # monotone: q' = .375 + 2.5t - 1.875t^2
+    assert oracle.fit_is_monotone(F(3, 8), F(5, 4))
+    q = oracle.encode_levels_f32(a, b, bits)
+    assert np.all(np.diff(q) > 0)
+    s = np.float32(0.0625)
+    k = rng.integers(-7, 8, size=(2, G))
+    k[:, 0] = 7
+    w = (np.sign(k) * (s * q[np.abs(k)]).astype(np.float32)).astype(np.float32)
+    codes, scales, shapes, loss, _ = oracle.fit(w, bits, G)
+    assert np.all(loss == 0.0)
+    assert np.array_equal(codes, k.astype(np.int8))
+    assert np.all(scales == s)
+
+
+def test_fit_linear_candidate_is_symmetric_int():
+    """The (a, b) = (1, 0) candidate is the symmetric INT grid: its loss for each
+    clip equals that of rounding |w| / s * Kmax to the nearest integer (clipped),
+    computed here in float64 on data with no ties."""
+    rng = np.random.default_rng(13)
+    bits, G = 4, 128
+    w = rng.laplace(0, 0.02, G).astype(np.float32)
+    ab = np.array([[1.0, 0.0]])
+    sse, s = oracle.fit_group_sse(w, bits, ab)
+    km = 7
+    for r in range(16):
+        sv = float(s[r])
+        k = np.minimum(np.rint(np.abs(w.astype(np.float64)) / sv * km), km)
+        e = np.abs(w.astype(np.float64)) - sv * k / km
+        np.testing.assert_allclose(sse[0, r], (e * e).sum(), rtol=1e-6)
+
+
+def test_fit_scale_invariant_under_powers_of_two():
+    rng = np.random.default_rng(14)
+    w = rng.standard_normal((1, 256)).astype(np.float32)
+    c1, s1, h1, l1, i1 = oracle.fit(w, 3, 128)
+    c2, s2, h2, l2, i2 = oracle.fit(w * np.float32(8.0), 3, 128)
+    assert np.array_equal(c1, c2) and np.array_equal(h1, h2) and np.array_equal(i1, i2)
+    assert np.array_equal(s2, s1 * np.float32(8.0))
+    np.testing.assert_allclose(l2, l1 * 64.0, rtol=1e-12)
+
+
+def test_fit_zero_group():
+    codes, scales, shapes, loss, index = oracle.fit(np.zeros((1, 128), np.float32), 4, 128)
+    assert not codes.any() and scales[0, 0] == 0 and not shapes.any() and loss[0, 0] == 0 and index[0, 0] == 0
+
+
+# W4 G128 NRMSE on 15,360 zero-mean samples per distribution (CubicQuant article,
+# results: finite-group reconstruction table). The article's grid and loss are
+# not given, so the fit lands near, not on, its numbers: within 3 %. Its INT4
+# column is the symmetric 15-level grid with the best clip per group, which a
+# fine clip search here reproduces to within 3 % as well.
+PAGES_W4G128 = {"uniform": (0.062979, 0.065536), "gaussian": (0.092396, 0.106803),
+                "laplace": (0.106764, 0.148571)}
+
+
+def _nrmse_samples(name):
+    rng = np.random.default_rng({"uniform": 31, "gaussian": 32, "laplace": 33}[name])
+    x = {"uniform": lambda: rng.uniform(-1, 1, 15360), "gaussian": lambda: rng.standard_normal(15360),
+         "laplace": lambda: rng.laplace(0, 1, 15360)}[name]()
+    return x.astype(np.float32).reshape(-1, 128)
+
+
+@pytest.mark.parametrize("name", ["uniform", "gaussian", "laplace"])
+def test_fit_reproduces_w4g128_nrmse_table(name):
+    w = _nrmse_samples(name)
+    codes, scales, shapes, loss, _ = oracle.fit(w, 4, 128)
+    w64 = w.astype(np.float64)
+    err = w64 - oracle.dequant(codes, scales, shapes, 4, 128)
+    den = (w64 ** 2).sum()
+    cubic = np.sqrt((err ** 2).sum() / den)
+    int4 = 0.0
+    for g in w64:
+        am = np.abs(g).max()
+        int4 += min(((g - np.clip(np.rint(g / (r * am / 7)), -7, 7) * (r * am / 7)) ** 2).sum()
+                    for r in np.linspace(0.3, 1.0, 351))
+    int4 = np.sqrt(int4 / den)
+    pc, pi = PAGES_W4G128[name]
+    assert abs(cubic / pc - 1) < 0.03, (cubic, pc)
+    assert abs(int4 / pi - 1) < 0.03, (int4, pi)
+    assert cubic < int4
+    # the stored losses are the squared errors of the dequantised weights
+    np.testing.assert_allclose(loss.sum(), (err ** 2).sum(), rtol=1e-6)
