@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "CubicError", "CubicWeight", "library_path", "load_library",
     "cubic_code_bytes", "cubic_storage_bytes", "cubic_pack", "cubic_unpack",
-    "cubic_dequant", "cubic_encode", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
+    "cubic_dequant", "cubic_encode", "cubic_fit", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
     "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode", "cubic_linear_workspace_bytes",
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS",
@@ -30,7 +30,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = [
     "cubic_code_bytes", "cubic_storage_bytes", "cubic_status_string", "cubic_version",
-    "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_encode", "cubic_gemm_a16_workspace_bytes",
+    "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_encode", "cubic_fit", "cubic_gemm_a16_workspace_bytes",
     "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode",
     "cubic_linear_workspace_bytes", "cubic_linear", "cubic_moe_workspace_bytes",
     "cubic_moe_grouped_gemm", "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
@@ -77,6 +77,7 @@ def load_library():
         "cubic_unpack": (i32, [vp, i64, i64, i32, vp, vp]),
         "cubic_dequant": (i32, [wp, vp, vp]),
         "cubic_encode": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp]),
+        "cubic_fit": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "cubic_gemm_a16_workspace_bytes": (sz, [i64, i64]),
         "cubic_gemm_a16": (i32, [vp, i64, wp, vp, vp, sz, vp]),
         "act_quant_int8_per_token": (i32, [vp, i64, i64, vp, vp, vp]),
@@ -192,6 +193,22 @@ def cubic_encode(w: torch.Tensor, scales: torch.Tensor, shapes: torch.Tensor, bi
     _check(load_library().cubic_encode(_ptr(w), N, K, bits, group, _ptr(scales), _ptr(shapes), _ptr(out),
                                         _stream(w)), "cubic_encode")
     return out
+
+
+def cubic_fit(w: torch.Tensor, bits: int, group: int, with_loss: bool = False):
+    """Fit every group of fp32 weights w [N][K]: returns (codes int8 [N][K], scales
+    fp32 [N][K/group], shapes int16 [N][K/group][2] holding fp16 a, b bits), plus the
+    per-group loss (fp32) when with_loss."""
+    _need(w, torch.float32, "w")
+    N, K = w.shape
+    G = K // group if group > 0 else 0
+    codes = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    scales = torch.empty((N, G), dtype=torch.float32, device=w.device)
+    shapes = torch.empty((N, G, 2), dtype=torch.int16, device=w.device)
+    loss = torch.empty((N, G), dtype=torch.float32, device=w.device) if with_loss else None
+    _check(load_library().cubic_fit(_ptr(w), N, K, bits, group, _ptr(codes), _ptr(scales), _ptr(shapes),
+                                    _ptr(loss) if loss is not None else None, _stream(w)), "cubic_fit")
+    return (codes, scales, shapes, loss) if with_loss else (codes, scales, shapes)
 
 
 def cubic_gemm_a16_workspace_bytes(M: int, K: int) -> int:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libcubic.so")
-SOURCES = ["basic.hip", "gemv.hip", "moe.hip", "tiled.hip", "prefill.hip", "prefill_a8.hip", "skinny.hip", "api.cpp"]
+SOURCES = ["basic.hip", "fit.hip", "gemv.hip", "moe.hip", "tiled.hip", "prefill.hip", "prefill_a8.hip", "skinny.hip", "api.cpp"]
 ARCH = os.environ.get("CUBIC_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -134,6 +134,20 @@ CUBIC_API int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int g
                                   static_cast<hipStream_t>(stream)));
 }
 
+CUBIC_API int cubic_fit(const float* w, int64_t N, int64_t K, int bits, int group, int8_t* codes,
+                        float* scales, uint16_t* shapes, float* loss, cubic_stream_t stream) {
+  if (N < 0 || K < 0) return CUBIC_ERR_SHAPE;
+  if (bits < 2 || bits > 8) return CUBIC_ERR_BITS;
+  if (group <= 0 || group % 128 != 0 || group > fit_max_group() || K % group != 0) return CUBIC_ERR_GROUP;
+  if (N == 0 || K == 0) return CUBIC_OK;
+  if (!w || !codes || !scales || !shapes) return CUBIC_ERR_NULL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned16(shapes)) return CUBIC_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(loss) & 3u) != 0) return CUBIC_ERR_ALIGN;
+  if (N * (K / group) > INT32_MAX) return CUBIC_ERR_SHAPE;
+  return hip_status(launch_fit(w, N, K, bits, group, codes, scales, shapes, loss,
+                               static_cast<hipStream_t>(stream)));
+}
+
 CUBIC_API size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K < 0) return 0;
   if (a16_inkernel(M, K)) return 0;

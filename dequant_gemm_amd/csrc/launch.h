@@ -56,6 +56,9 @@ hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t st);
 hipError_t launch_encode(const float* w, int64_t N, int64_t K, int bits, int group, const float* scales,
                          const uint16_t* shapes, int8_t* codes, hipStream_t st);
+int fit_max_group();
+hipError_t launch_fit(const float* w, int64_t N, int64_t K, int bits, int group, int8_t* codes,
+                      float* scales, uint16_t* shapes, float* loss, hipStream_t st);
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                             hipStream_t st);
 hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st);

@@ -111,6 +111,25 @@ int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int group,
                  const float* scales, const uint16_t* shapes, int8_t* codes,
                  cubic_stream_t stream);
 
+/* Data-free group fitting (CubicQuant article, data-free in-group fitting: per
+ * group a search over monotone (a, b), the scale chosen with its soft-clip
+ * threshold, nearest-level codes, a and b kept in fp16 and s in fp32). The
+ * article leaves the grid and the loss open; this call searches
+ *   a = i/8 (i = 0..24) x b = j/8 (j = -24..24), pairs for which
+ *       q(t) = a t + b t^2 + (1-a-b) t^3 is non-decreasing on [0, 1] (532 pairs),
+ *   s = fl32(rho * max|w|) with rho = 1 - r/32, r = 0..15 (weights beyond s take
+ *       the top level),
+ * minimising the group's sum of squared distances from |w| to its nearest fp32
+ * level s * q_j (fp32 sums in weight order). Candidate index = pair * 16 + r, pairs
+ * in the order above; the first smallest loss wins. codes follow cubic_encode's
+ * rule for the chosen s, a, b, so cubic_pack of them with scales/shapes is the
+ * fitted weight. w fp32 [N][K] (finite), codes int8 [N][K], scales fp32 [N][K/group],
+ * shapes fp16 pairs [N][K/group][2], loss fp32 [N][K/group] or NULL. group a
+ * multiple of 128 up to 2048. A group of zeros gets s = 0, (a, b) = (0, 0), codes 0.
+ * Asynchronous on `stream`. */
+int cubic_fit(const float* w, int64_t N, int64_t K, int bits, int group, int8_t* codes,
+              float* scales, uint16_t* shapes, float* loss, cubic_stream_t stream);
+
 /* A16 product y[M][N] = x[M][K] * W^T, x in bf16 (bit patterns), y in fp32.
  * For 2-bit weights x is used in bf16 as is (the valid levels are -s, 0, s, so
  * every product is exact before the fp32 group scaling). For wider codes and

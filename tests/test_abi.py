@@ -102,6 +102,21 @@ def test_encode_validation_before_launch():
     assert lib.cubic_encode(p16, 0, 512, 3, 128, None, None, None, None) == OK    # no-op
 
 
+def test_fit_validation_before_launch():
+    lib = cq.load_library()
+    p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
+    assert lib.cubic_fit(p16, 4, 512, 9, 128, p16, p16, p16, None, None) == ERR_BITS
+    assert lib.cubic_fit(p16, 4, 512, 3, 64, p16, p16, p16, None, None) == ERR_GROUP
+    assert lib.cubic_fit(p16, 4, 4096, 3, 4096, p16, p16, p16, None, None) == ERR_GROUP   # above 2048
+    assert lib.cubic_fit(p16, 4, 384, 3, 256, p16, p16, p16, None, None) == ERR_GROUP
+    assert lib.cubic_fit(p16, -1, 512, 3, 128, p16, p16, p16, None, None) == ERR_SHAPE
+    assert lib.cubic_fit(None, 4, 512, 3, 128, p16, p16, p16, None, None) == ERR_NULL
+    assert lib.cubic_fit(p16, 4, 512, 3, 128, p16, None, p16, None, None) == ERR_NULL
+    assert lib.cubic_fit(p8, 4, 512, 3, 128, p16, p16, p16, None, None) == ERR_ALIGN
+    assert lib.cubic_fit(p16, 4, 512, 3, 128, p16, p16, p16, ctypes.c_void_p(18), None) == ERR_ALIGN
+    assert lib.cubic_fit(p16, 0, 512, 3, 128, None, None, None, None, None) == OK        # no-op
+
+
 def test_moe_mlp_validation_before_launch():
     lib = cq.load_library()
     p16, p8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
