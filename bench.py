@@ -462,6 +462,7 @@ def extra_workloads(cq, synth, dev, stream):
         del wu, wd
         torch.cuda.empty_cache()
     res.update(encode_workloads(cq, synth, dev))
+    res.update(fit_workloads(cq, synth, dev))
     res.update(moe_workloads(cq, synth, dev))
     return res
 
@@ -486,6 +487,41 @@ def encode_workloads(cq, synth, dev):
         _report(res, f"encode_w{bits}g{group}_gate_up")
         del xs, w
         torch.cuda.empty_cache()
+    return res
+
+
+# fp32 VALU issue: 256 compute units x 4 SIMDs x 32 lanes per clock at 2.4 GHz =
+# 78.6 T lane-instructions/s (the 157.3 TFLOP/s vector figure counts an fma as two)
+VALU_PEAK_TINSTR = 256 * 4 * 32 * 2.4e9 / 1e12
+
+
+def fit_workloads(cq, synth, dev):
+    """cubic_fit (data-free group fitting, 8512 candidates per group): gate_up
+    6144 x 7168 at W4 G128 (344,064 groups) and the 3 x 15,360-sample W4 G128
+    reconstruction workload. VALU work per (weight, candidate) at W4: 13
+    instructions (7 differences, 1 min and 3 three-way mins over |d|, the
+    canonicalising max of the first operand, 1 fma), the k_fit<4> inner loop."""
+    import torch
+    res = {}
+    cands = 532 * 16
+    g = synth.make_generator(9600, dev)
+    w = torch.randn((6144, 7168), generator=g, device=dev) * 0.02
+    ms = _graph_time([lambda: cq.cubic_fit(w, 4, 128)], 2, dev)
+    instr = 6144 * 7168 * cands * 13
+    res["fit_w4g128_gate_up"] = {"ms": round(ms, 3), "groups/s": round(6144 * 56 / ms * 1e3, 1),
+                                 "valu_T_lane_instr/s": round(instr / ms / 1e9, 2),
+                                 "frac_of_valu_issue_peak": round(instr / ms / 1e9 / VALU_PEAK_TINSTR, 4)}
+    _report(res, "fit_w4g128_gate_up")
+    gen = torch.Generator().manual_seed(9601)
+    xs = [torch.rand(15360, generator=gen) * 2 - 1, torch.randn(15360, generator=gen),
+          torch.distributions.Laplace(0.0, 1.0).sample((15360,))]
+    ws = [x.to(torch.float32).reshape(-1, 128).to(dev) for x in xs]
+    ms = _graph_time([(lambda x=x: cq.cubic_fit(x, 4, 128)) for x in ws], 5, dev)
+    res["fit_w4g128_nrmse_15360x3"] = {"us_per_distribution": round(ms * 1e3, 2),
+                                       "note": "120 groups per launch: fewer workgroups than compute units"}
+    _report(res, "fit_w4g128_nrmse_15360x3")
+    del w, ws
+    torch.cuda.empty_cache()
     return res
 
 
