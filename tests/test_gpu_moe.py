@@ -223,3 +223,25 @@ def test_moe_mlp_k3_dims_few_tokens():
                          lambda e: _expert_dense(e, 2 * I, H, bits, group, 84),
                          lambda e: _expert_dense(e, H, I, bits, group, 85))
     assert row_rel_err(y, ref) <= TOL_MLP
+
+
+@pytest.mark.parametrize("E,T", [(64, 1), (896, 64)])
+def test_moe_mlp_full_size_sampled_tokens(E, T):
+    """The MLP step at hidden 7168 / intermediate 3072, W2 G512, top-16, in the two
+    launch configurations the bench times (one token over 64 experts; 64 tokens over
+    896), with softmax router weights; sampled tokens against the oracle."""
+    say(f"MoE MLP step full size E={E} T={T} top-16 (sampled tokens)")
+    H, I, topk, bits, group = 7168, 3072, 16, 2, 512
+    gu = _pool(E, 2 * I, H, bits, group, seed=4)
+    dn = _pool(E, H, I, bits, group, seed=6)
+    x, ids = synth.moe_routing(seed=4, T=T, E=E, topk=topk, K=H, device=DEV)
+    w = torch.softmax(torch.rand((T, topk), generator=torch.Generator().manual_seed(8)), dim=1).to(DEV)
+    y = cq.cubic_moe_mlp(x, ids, w, gu, dn, E)
+    assert torch.equal(y, cq.cubic_moe_mlp(x, ids, w, gu, dn, E))
+    y = y.cpu().numpy()
+    X, ids_np, w_np = x_bits(x), ids.cpu().numpy(), w.cpu().numpy()
+    for t in ([0] if T == 1 else [5, 63]):
+        ref = oracle.moe_mlp(X[t:t + 1], ids_np[t:t + 1], w_np[t:t + 1], E,
+                             lambda e: _expert_dense(e, 2 * I, H, bits, group, 4),
+                             lambda e: _expert_dense(e, H, I, bits, group, 6))
+        assert row_rel_err(y[t:t + 1], ref) <= TOL_MLP, t
