@@ -18,6 +18,7 @@ import torch
 
 import dequant_gemm_amd as cq
 import oracle
+import synth
 from tests._gpu import DEV, say
 
 pytestmark = pytest.mark.gpu
@@ -128,14 +129,15 @@ def test_fit_nrmse_workload(name):
 
 
 def test_fit_large_sampled():
-    """512 x 7168 W4 G128 (28,672 groups): every code against the oracle's rule for
-    the device's parameters, the search checked on sampled groups."""
-    say("fit 512x7168 W4 G128, sampled groups")
-    g = torch.Generator().manual_seed(740)
-    x = torch.randn((512, 7168), generator=g) * 0.02
-    w = x.numpy()
+    """gate_up 6144 x 7168 W4 G128 (344,064 groups), drawn as the bench draws it:
+    every code against the oracle's rule for the device's parameters, the search
+    checked on sampled groups."""
+    say("fit 6144x7168 W4 G128, sampled groups")
+    g = synth.make_generator(9600, DEV)
+    x = torch.randn((6144, 7168), generator=g, device=DEV) * 0.02
     out = _fit(x, 4, 128)
+    w = x.cpu().numpy()
     rng = np.random.default_rng(741)
-    sample = [(0, 0), (511, 55)] + [(int(n), int(c)) for n, c in zip(rng.integers(0, 512, 10),
-                                                                    rng.integers(0, 56, 10))]
+    sample = [(0, 0), (6143, 55)] + [(int(n), int(c)) for n, c in zip(rng.integers(0, 6144, 10),
+                                                                     rng.integers(0, 56, 10))]
     _check(w, 4, 128, out, sample=sample)
