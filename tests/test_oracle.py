@@ -662,10 +662,27 @@ def test_fit_zero_group():
 # W4 G128 NRMSE on 15,360 zero-mean samples per distribution (CubicQuant article,
 # results: finite-group reconstruction table). The article's grid and loss are
 # not given, so the fit lands near, not on, its numbers: within 3 %. Its INT4
-# column is the symmetric 15-level grid with the best clip per group, which a
-# fine clip search here reproduces to within 3 % as well.
-PAGES_W4G128 = {"uniform": (0.062979, 0.065536), "gaussian": (0.092396, 0.106803),
-                "laplace": (0.106764, 0.148571)}
+# column is the symmetric 15-level grid with the best clip per group, and its
+# FP4 column the best of the finite 4-bit float grids (sign plus E0M3 / E1M2,
+# both uniform, E2M1 or E3M0 magnitudes; with a per-group scale the exponent
+# bias drops out), each with the best clip per group: a fine clip search here
+# reproduces both to within 3 % as well.
+PAGES_W4G128 = {"uniform": (0.062979, 0.065536, 0.065536), "gaussian": (0.092396, 0.106803, 0.102027),
+                "laplace": (0.106764, 0.148571, 0.113906)}
+FP4_MAGNITUDES = {"e2m1": np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6.0]),
+                  "e3m0": np.array([0, 1, 2, 4, 8, 16, 32, 64.0])}
+
+
+def _grid_sse(g, mags, ratios):
+    """Smallest squared error of one group on the symmetric grid s * (+-mags) over
+    clip ratios (s = ratio * max|g| / largest magnitude), nearest magnitude."""
+    am = np.abs(g).max()
+    best = np.inf
+    for r in ratios:
+        s = r * am / mags[-1]
+        q = mags[np.argmin(np.abs(np.abs(g)[:, None] / s - mags[None, :]), axis=1)] * s
+        best = min(best, ((np.abs(g) - q) ** 2).sum())
+    return best
 
 
 def _nrmse_samples(name):
@@ -689,9 +706,13 @@ def test_fit_reproduces_w4g128_nrmse_table(name):
         int4 += min(((g - np.clip(np.rint(g / (r * am / 7)), -7, 7) * (r * am / 7)) ** 2).sum()
                     for r in np.linspace(0.3, 1.0, 351))
     int4 = np.sqrt(int4 / den)
-    pc, pi = PAGES_W4G128[name]
+    ratios = np.linspace(0.3, 1.0, 351)
+    fp4 = min([int4] + [np.sqrt(sum(_grid_sse(g, m, ratios) for g in w64) / den)
+                        for m in FP4_MAGNITUDES.values()])
+    pc, pi, pf = PAGES_W4G128[name]
     assert abs(cubic / pc - 1) < 0.03, (cubic, pc)
     assert abs(int4 / pi - 1) < 0.03, (int4, pi)
-    assert cubic < int4
+    assert abs(fp4 / pf - 1) < 0.03, (fp4, pf)
+    assert cubic < fp4 <= int4
     # the stored losses are the squared errors of the dequantised weights
     np.testing.assert_allclose(loss.sum(), (err ** 2).sum(), rtol=1e-6)
