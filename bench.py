@@ -9,8 +9,10 @@ Cache plus L2, so every launch streams its weights from HBM.
 Prints ONE JSON line: metric/value (whole-step HBM GB/s of algorithmic bytes),
 roofline of the dominant kernel (gate_up launch; average duration from HIP
 events on the launch stream around graph replays of gate_up launches), and the oracle
-CPU baseline on a bounded sample. `--extra` adds the prefill (M = 4096) A16 and
-A8 products and the small-M W4 products as extra fields.
+CPU baseline on a bounded sample. `--extra` adds, as extra fields (each also
+reported on stderr as it finishes): the prefill (M = 4096) A16 and A8 products,
+the small-M W4 products, nearest-level encoding, data-free group fitting, the
+routed-expert grouped products and the whole routed-expert MLP step.
 """
 from __future__ import annotations
 
