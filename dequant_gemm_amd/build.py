@@ -32,9 +32,15 @@ FLAGS = [
 ]
 
 
+# The group fitter takes finite weights only (its C-ABI says so): without NaN
+# semantics the first operand of its running minimum needs no canonicalising
+# max, one VALU instruction in thirteen of its inner loop.
+SOURCE_FLAGS = {"fit.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
