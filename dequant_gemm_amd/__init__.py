@@ -24,6 +24,7 @@ __all__ = [
     "cubic_dequant", "cubic_encode", "cubic_fit", "cubic_gemm_a16", "cubic_gemm_a16_workspace_bytes",
     "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode", "cubic_linear_workspace_bytes",
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
+    "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +34,8 @@ EXPORTED_SYMBOLS = [
     "cubic_pack", "cubic_unpack", "cubic_dequant", "cubic_encode", "cubic_fit", "cubic_gemm_a16_workspace_bytes",
     "cubic_gemm_a16", "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode",
     "cubic_linear_workspace_bytes", "cubic_linear", "cubic_moe_workspace_bytes",
-    "cubic_moe_grouped_gemm", "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
+    "cubic_moe_grouped_gemm", "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
+    "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
 ]
 MODE_A16, MODE_A8 = 0, 1          # cubic_linear_mode results
 
@@ -87,6 +89,8 @@ def load_library():
         "cubic_linear": (i32, [vp, i64, wp, vp, vp, sz, vp]),
         "cubic_moe_workspace_bytes": (sz, [i64, i32, i32, i64]),
         "cubic_moe_grouped_gemm": (i32, [vp, i64, vp, i32, wp, i32, vp, vp, sz, vp]),
+        "cubic_moe_grouped_gemm_static_max_bytes": (sz, []),
+        "cubic_moe_grouped_gemm_static": (i32, [vp, i64, vp, i32, wp, i32, vp, vp]),
         "cubic_moe_mlp_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
         "cubic_moe_mlp": (i32, [vp, i64, vp, vp, i32, wp, wp, i32, vp, vp, sz, vp]),
     }
@@ -306,6 +310,25 @@ def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: Cub
     _check(load_library().cubic_moe_grouped_gemm(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw),
                                                  E, _ptr(out), _ptr(workspace), workspace.numel(),
                                                  _stream(x)), "cubic_moe_grouped_gemm")
+    return out
+
+
+def cubic_moe_grouped_gemm_static_max_bytes() -> int:
+    return int(load_library().cubic_moe_grouped_gemm_static_max_bytes())
+
+
+def cubic_moe_grouped_gemm_static(x: torch.Tensor, topk_ids: torch.Tensor, experts: CubicWeight, E: int,
+                                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """cubic_moe_grouped_gemm with the library's per-device routing scratch (no workspace)."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, topk = topk_ids.shape
+    cw = experts.c_struct()
+    if out is None:
+        out = torch.empty((T, topk, experts.N), dtype=torch.float32, device=x.device)
+    _check(load_library().cubic_moe_grouped_gemm_static(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw),
+                                                        E, _ptr(out), _stream(x)),
+           "cubic_moe_grouped_gemm_static")
     return out
 
 

@@ -362,9 +362,13 @@ CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K
   return moe_layout(T, topk, E).total;
 }
 
-CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
-                                     int topk, const cubic_weight* expert0, int E, float* y,
-                                     void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+namespace {
+// The grouped product behind both routed-expert entry points; `workspace` is
+// the caller's buffer or the library's routing scratch (nullptr: look it up
+// after validation, so a rejected call touches no device state).
+int moe_grouped(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids, int topk,
+                const cubic_weight* expert0, int E, float* y, void* workspace, size_t ws_bytes,
+                bool library_scratch, cubic_stream_t stream) {
   const int st = check_weight(expert0);
   if (st != CUBIC_OK) return st;
   if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
@@ -373,11 +377,15 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
   if (expert0->K > 0 && (!gemv_supported(expert0->K, expert0->bits, expert0->group) ||
                          moe_lds_min_bytes(expert0->K, expert0->bits, expert0->group) > kLdsLimit))
     return CUBIC_ERR_SHAPE;
-  if (!x_bf16 || !topk_ids || !y || !workspace) return CUBIC_ERR_NULL;
+  if (!x_bf16 || !topk_ids || !y || (!workspace && !library_scratch)) return CUBIC_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(y) || !aligned16(workspace))
     return CUBIC_ERR_ALIGN;
   const MoeLayout L = moe_layout(T, topk, E);
   if (ws_bytes < L.total) return CUBIC_ERR_WORKSPACE;
+  if (library_scratch) {
+    const hipError_t a = moe_scratch_address(&workspace);
+    if (a != hipSuccess) return CUBIC_ERR_HIP;
+  }
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (expert0->K == 0) return hip_status(launch_fill_zero(y, T * topk * expert0->N, s));
@@ -397,4 +405,20 @@ CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const in
                                   reinterpret_cast<int32_t*>(ws + L.erec),
                                   reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s);
   return hip_status(e);
+}
+}  // namespace
+
+CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                                     int topk, const cubic_weight* expert0, int E, float* y,
+                                     void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  return moe_grouped(x_bf16, T, topk_ids, topk, expert0, E, y, workspace, ws_bytes, false, stream);
+}
+
+CUBIC_API size_t cubic_moe_grouped_gemm_static_max_bytes(void) { return moe_scratch_bytes(); }
+
+CUBIC_API int cubic_moe_grouped_gemm_static(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                                            int topk, const cubic_weight* expert0, int E, float* y,
+                                            cubic_stream_t stream) {
+  return moe_grouped(x_bf16, T, topk_ids, topk, expert0, E, y, nullptr, moe_scratch_bytes(), true,
+                     stream);
 }

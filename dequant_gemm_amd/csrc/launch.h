@@ -78,6 +78,10 @@ hipError_t launch_prefill_a8(const TiledParams& p, int bits, hipStream_t st);
 size_t moe_lds_min_bytes(int64_t K, int bits, int group);
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
                       int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st);
+// Library-owned routing scratch (one per device): its size, and its device
+// address on the current device (looked up on first use per device).
+size_t moe_scratch_bytes();
+hipError_t moe_scratch_address(void** out);
 // up.y: [T*topk][2I] fp32 scratch; dn.y: [T*topk][H] fp32 scratch; h: [T*topk][I] bf16 scratch.
 hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E, int topk,
                           const MoeGemvParams& up, int up_bits, const MoeGemvParams& dn, int dn_bits,

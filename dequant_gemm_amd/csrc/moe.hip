@@ -13,6 +13,7 @@
 // k_moe_gemv: one workgroup per (touched expert, 16-row tile); the expert's
 // pairs form the activation rows of the MFMA tile (up to two per pass).
 #include <algorithm>
+#include <mutex>
 
 #include "gemv_core.h"
 #include "launch.h"
@@ -696,6 +697,41 @@ hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E,
   hipLaunchKernelGGL(k_moe_combine, dim3(elementwise_grid(static_cast<int64_t>(T) * H / 4)), dim3(256), 0,
                      st, dn.y, ids, topk_w, static_cast<int64_t>(T), topk, E, H, out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned routing scratch for callers that cannot allocate device memory.
+// The routing header, the per-expert records and the pair lists of one grouped
+// product live here instead of in a caller's workspace. Each device holds its
+// own copy for the life of the process; host code never passes `scratch` itself
+// to a kernel, only the device address looked up once per device below.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kMoeScratchBytes = size_t{2} << 20;
+constexpr int kMoeScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kMoeScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMoeScratchDevices] = {};
+}  // namespace
+
+size_t moe_scratch_bytes() { return kMoeScratchBytes; }
+
+hipError_t moe_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMoeScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // this device is current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace cubic

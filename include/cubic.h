@@ -18,7 +18,9 @@
  * General contract
  *  - Every array argument is a DEVICE pointer owned by the caller. The library
  *    never allocates or frees device memory; scratch space is passed in as
- *    `workspace` where a call needs it.
+ *    `workspace` where a call needs it. The one exception is the routing
+ *    scratch of cubic_moe_grouped_gemm_static: a fixed 2 MiB buffer that the
+ *    library holds on each device it runs on, for callers that cannot allocate.
  *  - Calls validate all arguments on the host first. On a validation error
  *    nothing is enqueued and nothing is written; the error code is returned.
  *  - Valid calls enqueue kernels on `stream` (a hipStream_t; NULL = the null
@@ -206,6 +208,25 @@ int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
                            const cubic_weight* expert0, int E,
                            float* y, void* workspace, size_t ws_bytes,
                            cubic_stream_t stream);
+
+/* cubic_moe_grouped_gemm for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results (bit for bit) as cubic_moe_grouped_gemm,
+ * but the routing scratch (header, per-expert records, pair ids) is a buffer of
+ * cubic_moe_grouped_gemm_static_max_bytes() = 2 MiB that the library holds on
+ * each device for the life of the process, instead of a workspace argument.
+ * The call allocates and frees nothing. Returns CUBIC_ERR_WORKSPACE when
+ * cubic_moe_workspace_bytes(T, topk, E, K) exceeds that maximum (nothing is
+ * enqueued then). The routing kernel rewrites everything the product reads, so
+ * the buffer needs no clearing between calls. All calls on one device share the
+ * buffer: calls that overlap on that device (other streams, or other host
+ * threads) race and must be serialised by the caller. The invalid-id count is
+ * kept in the library's buffer and is not reported. */
+size_t cubic_moe_grouped_gemm_static_max_bytes(void);
+int cubic_moe_grouped_gemm_static(const uint16_t* x_bf16, int64_t T,
+                                  const int32_t* topk_ids, int topk,
+                                  const cubic_weight* expert0, int E,
+                                  float* y, cubic_stream_t stream);
 
 /* The routed-expert MLP step of a Kimi-K3-style layer (Kimi K3 guide, model
  * card: routed experts with a fused gate_up and a down projection; CubicQuant
