@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void k_unpack(const uint32_t* __restrict__ in,
   dst[1] = u32x4{words[4], words[5], words[6], words[7]};
 }
 
-// One thread per 32-code block: fp64 level evaluation, one rounding to fp32.
+// One thread per 32-code block: each weight is the format's fp32 value
+// RN32(s * sign(k) * q(|k| / Kmax)) (level_rn32); a zero weight is +0.0.
 template <int BITS>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ stream,
                                                  const float* __restrict__ scales,
@@ -81,9 +82,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ st
   const int64_t k0 = blk * 32;                  // flat index of the first code
   const int64_t n = k0 / K, kk = k0 - n * K;
   const int64_t g = n * (K / group) + kk / group;
-  const double s = static_cast<double>(scales[g]);
-  const double a = f16_bits_to_f64(shapes[2 * g]);
-  const double b = f16_bits_to_f64(shapes[2 * g + 1]);
+  const float s = scales[g];
+  const float a = static_cast<float>(f16_bits_to_f64(shapes[2 * g]));
+  const float b = static_cast<float>(f16_bits_to_f64(shapes[2 * g + 1]));
   constexpr int km = kmax_of(BITS);
   uint32_t w[BITS];
   const uint32_t* src = stream + blk * BITS;
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ st
   for (int i = 0; i < 32; ++i) {
     const int k = sign_extend(chunk_field<BITS>(w, i), BITS);
     const int j = k < 0 ? -k : k;
-    const float mag = static_cast<float>(s * level_q(a, b, j, km));
-    v[i] = (k == 0) ? 0.0f : (k < 0 ? -mag : mag);
+    const float mag = level_rn32(s, a, b, j, km);
+    v[i] = (mag == 0.0f) ? 0.0f : (k < 0 ? -mag : mag);
   }
   f32x4* dst = reinterpret_cast<f32x4*>(out + k0);
 #pragma unroll
@@ -216,12 +217,31 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
 }
 
 // Nearest-level encoding (CubicQuant article, Core: each weight takes the code
-// of its group's nearest level). The choice is made in fp32 exactly as follows,
-// so that every code is determined by IEEE operations: q_j is the fp32 level of
-// table_level_f32 (two fused multiply-adds and one product), v_j = |s| q_j,
-// d_j = | |w| - v_j |, each rounded once; the first j of smallest d_j wins (ties
-// to the smaller |k|) and k takes the sign of w * s. One thread encodes 8
-// consecutive weights of a row (one group); j runs over 0 .. Kmax.
+// of its group's nearest reconstruction level). The levels are the format's
+// fp32 values L_{+-j} = +-v_j, v_j = level_rn32(s, a, b, j) for j = 0 .. Kmax;
+// the code is the first j (smallest |k|) of smallest exact distance
+// | |w| - |v_j| |, with k = j * sign(w) * sign(v_j).
+//
+// A workgroup covers 2048 consecutive weights (whole groups, since K is a
+// multiple of the group): its threads first build the |v_j| and signs of every
+// group it touches in LDS, then each thread encodes 8 weights. Distances are
+// compared in fp32 first: rounding is monotone, so a smaller rounded distance
+// means a smaller exact one and a larger means larger. Only equal rounded
+// distances are decided exactly, in fp64, where x = |w| and y = |v_j| are exact
+// and Fast2Sum gives hi = fl(max - min), lo = (max - hi) - min with hi + lo =
+// |x - y|, compared lexicographically. NaN distances never win (a NaN weight
+// takes code 0).
+constexpr int kEncodeWeights = 2048;            // per workgroup: 256 threads x 8
+
+__device__ __forceinline__ bool exact_closer(float x, float y, float yb) {
+  const double xd = x, a = y, b = yb;
+  const bool ga = xd >= a, gb = xd >= b;
+  const double pa = ga ? xd : a, ma = ga ? a : xd, pb = gb ? xd : b, mb = gb ? b : xd;
+  const double ha = pa - ma, la = (pa - ha) - ma;
+  const double hb = pb - mb, lb = (pb - hb) - mb;
+  return ha < hb || (ha == hb && la < lb);
+}
+
 template <int B>
 __global__ __launch_bounds__(256) void k_encode(const float* __restrict__ w, int64_t nvec, int64_t K,
                                                 int group, const float* __restrict__ scales,
@@ -229,44 +249,61 @@ __global__ __launch_bounds__(256) void k_encode(const float* __restrict__ w, int
                                                 int8_t* __restrict__ codes) {
 #pragma clang fp contract(off)
   constexpr int KM = (1 << (B - 1)) - 1;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int L = KM + 1;
+  constexpr int kMaxGroups = kEncodeWeights / 128 + 1;
+  __shared__ float s_lv[kMaxGroups * L];        // |v_j| of each group the workgroup touches
+  __shared__ uint32_t s_neg[kMaxGroups * L];    // 1 where v_j is negative
+  const int tid = threadIdx.x;
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kEncodeWeights;
+  const int64_t total = nvec * 8;
+  const int64_t g0 = w0 / group;
+  const int64_t wlast = min(w0 + kEncodeWeights, total) - 1;
+  const int ng = static_cast<int>(wlast / group - g0) + 1;
+  for (int t = tid; t < ng * L; t += 256) {
+    const int gl = t / L, j = t - gl * L;
+    const int64_t gi = g0 + gl;
+    const uint32_t ab = shapes[gi];
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+    const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+    const float lv = level_rn32(scales[gi], a, b, j, KM);
+    s_lv[t] = fabsf(lv);
+    s_neg[t] = __builtin_signbit(lv) ? 1u : 0u;
+  }
+  __syncthreads();
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid;
   if (i >= nvec) return;
   const int64_t e0 = i * 8;                     // first weight (row-major [N][K])
-  const int64_t n = e0 / K, k0 = e0 - n * K;
-  const int64_t gi = n * (K / group) + k0 / group;
-  const float s = scales[gi];
-  const uint32_t ab = shapes[gi];
-  const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
-  const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
-  const float sa = fabsf(s);
-  const f32x4 lo = reinterpret_cast<const f32x4*>(w + e0)[0];
-  const f32x4 hi = reinterpret_cast<const f32x4*>(w + e0)[1];
-  const float wv[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  float aw[8], bd[8];
+  const int gl = static_cast<int>(e0 / group - g0);
+  const float* lv = s_lv + gl * L;
+  const f32x4 lo4 = reinterpret_cast<const f32x4*>(w + e0)[0];
+  const f32x4 hi4 = reinterpret_cast<const f32x4*>(w + e0)[1];
+  const float wv[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  float x[8], bd[8], by[8];
   int bj[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    aw[e] = fabsf(wv[e]);
-    bd[e] = aw[e];                              // j = 0: v_0 = 0
+    x[e] = fabsf(wv[e]);
+    bd[e] = x[e];                               // j = 0: v_0 = +0, distance |w| exactly
+    by[e] = 0.0f;
     bj[e] = 0;
   }
-#pragma unroll 4
   for (int j = 1; j <= KM; ++j) {
-    const float v = sa * table_level_f32(a, b, static_cast<uint32_t>(j), B);
+    const float y = lv[j];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float d = fabsf(aw[e] - v);
-      if (d < bd[e]) {
-        bd[e] = d;
-        bj[e] = j;
-      }
+      const float d = fabsf(x[e] - y);
+      bool better = d < bd[e];
+      if (d == bd[e]) better = exact_closer(x[e], y, by[e]);
+      bd[e] = better ? d : bd[e];
+      by[e] = better ? y : by[e];
+      bj[e] = better ? j : bj[e];
     }
   }
-  const bool sneg = __builtin_signbit(s);
   uint32_t o[2] = {0u, 0u};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int k = (__builtin_signbit(wv[e]) != sneg) ? -bj[e] : bj[e];
+    const bool neg = s_neg[gl * L + bj[e]] != 0u;
+    const int k = (__builtin_signbit(wv[e]) != neg) ? -bj[e] : bj[e];
     o[e >> 2] |= (static_cast<uint32_t>(k) & 0xffu) << (8 * (e & 3));
   }
   reinterpret_cast<uint2*>(codes + e0)[0] = make_uint2(o[0], o[1]);
@@ -363,7 +400,7 @@ hipError_t launch_encode(const float* w, int64_t N, int64_t K, int bits, int gro
                          const uint16_t* shapes, int8_t* codes, hipStream_t st) {
   const int64_t nvec = N * K / 8;
   if (nvec == 0) return hipSuccess;
-  const unsigned grid = static_cast<unsigned>((nvec + 255) / 256);
+  const unsigned grid = static_cast<unsigned>((nvec * 8 + kEncodeWeights - 1) / kEncodeWeights);
   const uint32_t* ab = reinterpret_cast<const uint32_t*>(shapes);
 #define CUBIC_ENCODE(BB)                                                                            \
   hipLaunchKernelGGL(k_encode<BB>, dim3(grid), dim3(256), 0, st, w, nvec, K, group, scales, ab, codes)

@@ -49,10 +49,127 @@ __device__ __forceinline__ double level_numerator(double a, double b, int j, int
   return a * (J * K * K) + b * (J * J * K) + c * (J * J * J);
 }
 
-// q(j / Kmax) in fp64 with a single rounding (IEEE division).
-__device__ __forceinline__ double level_q(double a, double b, int j, int km) {
-  const double K = static_cast<double>(km);
-  return level_numerator(a, b, j, km) / (K * K * K);
+
+// The format's fp32 value of a level: RN32(s * q(j / Kmax)), the exact product
+// s * Q_j / Kmax^3 rounded once to the nearest fp32 value (ties to even), an
+// exact zero as +0.0 (core section of the CubicQuant article gives q; the storage
+// section stores s in fp32 and a, b in fp16). Exact for every finite fp32 s and
+// every finite fp16 a, b; a non-finite s gives the fp64 product's rounding.
+//
+// Fast path: R = Q_j * 2^24 is an integer (a, b are multiples of 2^-24). When
+// |R| < 2^53, y = fl(s * fl(R * fl(2^-24 / Kmax^3))) carries three roundings and
+// lies within 2^-51 |V| of V = s * Q_j / Kmax^3; if no fp32 rounding boundary
+// (the midpoint between two neighbouring fp32 values) lies within 2^-51 |y| of
+// y, RN32(V) = RN32(y). Otherwise the exact path decides with 128-bit integers:
+// |V| = P * 2^(es - 24) / D with P = |S * R|, s = S * 2^es and D = Kmax^3, its
+// binade E found exactly, and the significand n = |V| / 2^(E - 23) rounded
+// half to even from the integer remainder.
+namespace level_detail {
+typedef __int128 i128;
+typedef unsigned __int128 u128;
+
+__host__ __device__ inline double u128_to_f64(u128 v) {
+  return static_cast<double>(static_cast<uint64_t>(v >> 64)) * 0x1p64 +
+         static_cast<double>(static_cast<uint64_t>(v));
+}
+
+// P >= D * 2^t, exactly (P < 2^90, D < 2^21).
+__host__ __device__ inline bool ge_pow2(u128 P, u128 D, int t) {
+  if (t >= 0) return t < 100 && P >= (D << t);
+  const int u = -t;
+  if (u >= 64) return true;                       // P >= 1 > D * 2^-64
+  return P >= ((D + ((static_cast<u128>(1) << u) - 1)) >> u);
+}
+
+__host__ __device__ __attribute__((noinline)) inline float exact(float s, i128 R, int64_t km) {
+  const uint32_t sb = __builtin_bit_cast(uint32_t, s);
+  const int ex = static_cast<int>((sb >> 23) & 0xffu);
+  uint64_t S = sb & 0x7fffffu;
+  int es;
+  if (ex == 0) {
+    es = -149;
+  } else {
+    S |= 0x800000u;
+    es = ex - 150;
+  }
+  const bool neg = ((sb >> 31) != 0) != (R < 0);
+  const u128 P = static_cast<u128>(R < 0 ? -R : R) * S;
+  if (P == 0) return 0.0f;
+  const u128 D = static_cast<u128>(km * km * km);
+  int xe = 0;
+  frexp(ldexp(u128_to_f64(P) / u128_to_f64(D), es - 24), &xe);
+  int E = xe - 1;                                 // estimate of floor(log2 |V|)
+  for (int it = 0; it < 4 && !ge_pow2(P, D, E + 24 - es); ++it) --E;
+  for (int it = 0; it < 4 && ge_pow2(P, D, E + 25 - es); ++it) ++E;
+  if (E >= 128) return neg ? -__builtin_inff() : __builtin_inff();
+  const int u = (E < -126 ? -126 : E) - 23;       // exponent of the fp32 ulp at |V|
+  const int sh = es - 24 - u;                     // n = P * 2^sh / D
+  const u128 num = sh >= 0 ? (P << sh) : P;
+  const u128 den = sh >= 0 ? D : (D << (-sh));
+  uint64_t n = static_cast<uint64_t>(u128_to_f64(num) / u128_to_f64(den));
+  i128 r = static_cast<i128>(num) - static_cast<i128>(n) * static_cast<i128>(den);
+  for (int it = 0; it < 4 && r < 0; ++it) { --n; r += static_cast<i128>(den); }
+  for (int it = 0; it < 4 && r >= static_cast<i128>(den); ++it) { ++n; r -= static_cast<i128>(den); }
+  const i128 r2 = 2 * r;
+  if (r2 > static_cast<i128>(den) || (r2 == static_cast<i128>(den) && (n & 1u))) ++n;
+  const float v = ldexpf(static_cast<float>(n), u);   // n <= 2^24: exact
+  return neg ? -v : v;
+}
+}  // namespace level_detail
+
+// RN32(y) when y (within 2^-51 |V| of V) decides RN32(V); false otherwise.
+// In the normal fp32 range, rounding y to fp32 drops the low 29 bits of its
+// fp64 significand, and the fp32 rounding boundaries (midpoints) are where
+// those bits equal 2^28. |V - y| < 2^-51 |y| < 4 fp64 ulps of y, so when the
+// dropped bits lie more than 8 ulps from 2^28, V rounds like y (near the
+// representable points at 0 and 2^29 both round to the same fp32 number, also
+// across a power of two). Outside the normal range the caller decides exactly.
+__host__ __device__ inline bool level_fast(double y, float* out) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, y);
+  const uint32_t ex = static_cast<uint32_t>(u >> 52) & 0x7ffu;
+  if (ex < 1023u - 126u || ex > 1023u + 127u) return false;
+  const uint32_t low = static_cast<uint32_t>(u) & ((1u << 29) - 1u);
+  const uint32_t dist = low > (1u << 28) ? low - (1u << 28) : (1u << 28) - low;
+  if (dist <= 8u) return false;
+  *out = static_cast<float>(y);
+  return true;
+}
+
+// Kmax^3 * q(j / Kmax) * 2^24 as an exact integer, for fp16 values a, b.
+__host__ __device__ inline level_detail::i128 level_numerator_i(float a, float b, int j, int km) {
+  using level_detail::i128;
+  const int64_t A = static_cast<int64_t>(static_cast<double>(a) * 16777216.0);
+  const int64_t Bq = static_cast<int64_t>(static_cast<double>(b) * 16777216.0);
+  const int64_t C = 16777216 - A - Bq;
+  const int64_t J = j, K = km;
+  return static_cast<i128>(A) * (J * K * K) + static_cast<i128>(Bq) * (J * J * K) +
+         static_cast<i128>(C) * (J * J * J);
+}
+
+// level_rn32 for a numerator R = Kmax^3 q_j 2^24 given as an integer-valued
+// double with |R| < 2^53 (exact), and a finite s.
+__host__ __device__ inline float level_rn32_r(float s, double R, int km) {
+  if (R == 0.0 || s == 0.0f) return 0.0f;
+  const double inv = 0x1p-24 / static_cast<double>(static_cast<int64_t>(km) * km * km);
+  float v;
+  if (level_fast(static_cast<double>(s) * (R * inv), &v)) return v;
+  return level_detail::exact(s, static_cast<level_detail::i128>(static_cast<int64_t>(R)), km);
+}
+
+__host__ __device__ inline float level_rn32(float s, float a, float b, int j, int km) {
+  using level_detail::i128;
+  const i128 R = level_numerator_i(a, b, j, km);
+  if (R == 0 || s == 0.0f) return 0.0f;
+  const double inv = 0x1p-24 / static_cast<double>(static_cast<int64_t>(km) * km * km);
+  if (!(fabsf(s) <= 3.4028234663852886e38f))
+    return static_cast<float>(static_cast<double>(s) * (level_detail::u128_to_f64(R < 0 ? -R : R) * inv) *
+                              (R < 0 ? -1.0 : 1.0));
+  const i128 lim = static_cast<i128>(1) << 53;
+  if (R < lim && R > -lim) {
+    float v;
+    if (level_fast(static_cast<double>(s) * (static_cast<double>(static_cast<int64_t>(R)) * inv), &v)) return v;
+  }
+  return level_detail::exact(s, R, km);
 }
 
 // Two's complement value of a `bits`-wide field.

@@ -6,9 +6,11 @@
 //   a = i/8 (i = 0 .. 24), b = j/8 (j = -24 .. 24), monotone pairs only,
 //   s = fl32(rho * max|w|), rho = 1 - r/32 (r = 0 .. 15): the clip threshold is s,
 //       weights beyond it take the top level,
-// and minimises the group's sum of squared errors to the chosen fp32 levels.
-// Candidate c = pair * 16 + r; the first candidate of smallest loss wins. Codes
-// follow the nearest-level rule of cubic_encode (fp32, ties to the smaller |k|).
+// and minimises the group's sum of squared errors to the candidate's fp32 levels
+// (the format's values RN32(s q_j), level_rn32). Candidate c = pair * 16 + r; the
+// first candidate of smallest loss wins. The codes of the chosen (s, a, b) are
+// written by cubic_encode's kernel right after (exact nearest level, ties to the
+// smaller |k|).
 // Multiples of 1/8 in [-3, 3] are exact in fp16, so storing a, b changes nothing.
 #include "common.h"
 #include "decode.h"
@@ -65,7 +67,7 @@ __device__ __forceinline__ uint16_t f16_of(float v) {
 // level. The group's |w| sit in LDS and every lane reads the same word (broadcast).
 template <int B>
 __global__ __launch_bounds__(256) void k_fit(const float* __restrict__ w, int64_t K, int group,
-                                             int8_t* __restrict__ codes, float* __restrict__ scales,
+                                             float* __restrict__ scales,
                                              uint32_t* __restrict__ shapes, float* __restrict__ loss) {
 #pragma clang fp contract(off)
   constexpr int KM = (1 << (B - 1)) - 1;
@@ -97,10 +99,17 @@ __global__ __launch_bounds__(256) void k_fit(const float* __restrict__ w, int64_
     const float a = 0.125f * static_cast<float>(g_fit_pairs.p[p][0]);
     const float b = 0.125f * static_cast<float>(g_fit_pairs.p[p][1]);
     const float s = (1.0f - static_cast<float>(r) * (1.0f / 32.0f)) * amax;
+    // R_j = Kmax^3 q_j 2^24 = (A j K^2 + Bq j^2 K + C j^3) 2^21 with A = 8a,
+    // Bq = 8b, C = 8 - A - Bq: small integers, exact in fp64
+    const double A = static_cast<double>(g_fit_pairs.p[p][0]), Bq = static_cast<double>(g_fit_pairs.p[p][1]);
+    const double C = 8.0 - A - Bq;
     float v[KM + 1];
     v[0] = 0.0f;
 #pragma unroll
-    for (int j = 1; j <= KM; ++j) v[j] = s * table_level_f32(a, b, static_cast<uint32_t>(j), B);
+    for (int j = 1; j <= KM; ++j) {
+      const double J = j, Kd = KM;
+      v[j] = level_rn32_r(s, (A * (J * Kd * Kd) + Bq * (J * J * Kd) + C * (J * J * J)) * 0x1p21, KM);
+    }
     float sse = 0.0f;
     for (int i = 0; i < group; i += 4) {
       const f32x4 x4 = *reinterpret_cast<const f32x4*>(aw + i);
@@ -151,26 +160,6 @@ __global__ __launch_bounds__(256) void k_fit(const float* __restrict__ w, int64_
     shapes[gi] = static_cast<uint32_t>(f16_of(a)) | (static_cast<uint32_t>(f16_of(b)) << 16);
     if (loss) loss[gi] = best;
   }
-  // codes of the chosen candidate by the nearest-level rule (s >= 0)
-  float v[KM + 1];
-  v[0] = 0.0f;
-#pragma unroll
-  for (int j = 1; j <= KM; ++j) v[j] = s * table_level_f32(a, b, static_cast<uint32_t>(j), B);
-  for (int i = tid; i < group; i += 256) {
-    const float x = aw[i];
-    float bd = x;
-    int bj = 0;
-#pragma unroll
-    for (int j = 1; j <= KM; ++j) {
-      const float d = fabsf(x - v[j]);
-      if (d < bd) {
-        bd = d;
-        bj = j;
-      }
-    }
-    const bool neg = __builtin_signbit(wg[i]) != __builtin_signbit(s);
-    codes[n * K + k0 + i] = static_cast<int8_t>(neg ? -bj : bj);
-  }
 }
 
 }  // namespace
@@ -184,7 +173,7 @@ hipError_t launch_fit(const float* w, int64_t N, int64_t K, int bits, int group,
   uint32_t* ab = reinterpret_cast<uint32_t*>(shapes);
 #define CUBIC_FIT(BB)                                                                              \
   hipLaunchKernelGGL(k_fit<BB>, dim3(static_cast<unsigned>(groups)), dim3(256), 0, st, w, K, group, \
-                     codes, scales, ab, loss)
+                     scales, ab, loss)
   switch (bits) {
     case 2: CUBIC_FIT(2); break;
     case 3: CUBIC_FIT(3); break;
@@ -195,7 +184,10 @@ hipError_t launch_fit(const float* w, int64_t N, int64_t K, int bits, int group,
     default: CUBIC_FIT(8); break;
   }
 #undef CUBIC_FIT
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the codes of the chosen (s, a, b) by the nearest-level rule of cubic_encode
+  return launch_encode(w, N, K, bits, group, scales, shapes, codes, st);
 }
 
 }  // namespace cubic

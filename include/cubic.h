@@ -93,22 +93,23 @@ int cubic_unpack(const uint8_t* packed, int64_t N, int64_t K, int bits,
                  int8_t* codes, cubic_stream_t stream);
 
 /* Materialise the decoded weights out[N][K] in fp32 (a test and inspection
- * utility; the GEMMs never call it). Each value is s * q_j evaluated in fp64
- * with the numerator a*j*Kmax^2 + b*j^2*Kmax + (1-a-b)*j^3 exact, one division
- * by Kmax^3, one product with s and one rounding to fp32 (<= 1 fp32 ulp from the
- * exact value). Code 0 gives +0.0; codes +-Kmax give +-s exactly. */
+ * utility; the GEMMs never call it). CubicQuant article, Core section (the
+ * reconstructed weight) and Storage section (s kept in fp32): each value is
+ * RN32(s * sign(k) * q(|k| / Kmax)), the exact real value rounded once to the
+ * nearest fp32 number, ties to even, for every finite s and fp16 a, b. A zero
+ * weight is +0.0 (code 0 always); codes +-Kmax give +-s exactly. */
 int cubic_dequant(const cubic_weight* w, float* out, cubic_stream_t stream);
 
 /* Nearest-level encoding (CubicQuant article, Core section: each weight takes
- * the code of its group's nearest level), for given scales and shapes (the
- * fitting of s, a, b is not part of this library). w: fp32 [N][K]; scales,
- * shapes as in cubic_weight; codes: int8 [N][K] out, in [-Kmax, Kmax] (pack
- * them with cubic_pack). The choice is made in fp32, bit for bit: with the fp32
- * level q_j = fl(fl(a*(j*Kmax^2 - j^3) + fl(b*(j^2*Kmax - j^3) + j^3)) *
- * fl(1/Kmax^3)) (two fused multiply-adds, one product), v_j = fl(|s| * q_j) and
- * d_j = |fl(|w| - v_j)| for j = 0 .. Kmax, the first j of smallest d_j wins (ties
- * go to the smaller |k|) and k takes the sign of w * s. Errors as for the other
- * calls (bits, group, alignment, NULL); N == 0 or K == 0 is a no-op. */
+ * the code of its group's nearest reconstruction level), for given scales and
+ * shapes. w: fp32 [N][K]; scales, shapes as in cubic_weight; codes: int8 [N][K]
+ * out, in [-Kmax, Kmax] (pack them with cubic_pack). The levels are the
+ * format's fp32 values L_k = RN32(s * sign(k) * q(|k| / Kmax)), exactly those
+ * cubic_dequant returns, and distances |w - L_k| are compared exactly: the code
+ * is the k of smallest distance, the smaller |k| on ties (so 0 for a zero
+ * weight of either sign); the code -2^(B-1) is never chosen. NaN weights take
+ * code 0. Codes are bit-exact whatever the arithmetic order. Errors as for the
+ * other calls (bits, group, alignment, NULL); N == 0 or K == 0 is a no-op. */
 int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int group,
                  const float* scales, const uint16_t* shapes, int8_t* codes,
                  cubic_stream_t stream);
@@ -122,7 +123,7 @@ int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int group,
  *   s = fl32(rho * max|w|) with rho = 1 - r/32, r = 0..15 (weights beyond s take
  *       the top level),
  * minimising the group's sum of squared distances from |w| to its nearest fp32
- * level s * q_j (fp32 sums in weight order). Candidate index = pair * 16 + r, pairs
+ * level RN32(s * q_j) (the levels of cubic_dequant; fp32 sums in weight order). Candidate index = pair * 16 + r, pairs
  * in the order above; the first smallest loss wins. codes follow cubic_encode's
  * rule for the chosen s, a, b, so cubic_pack of them with scales/shapes is the
  * fitted weight. w fp32 [N][K] (finite), codes int8 [N][K], scales fp32 [N][K/group],

@@ -61,7 +61,7 @@ __all__ = [
     "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
     "level_numerators", "levels", "dequant", "gemm_a16",
     "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
-    "encode_levels_f32", "encode", "bf16_rne", "moe_mlp",
+    "format_levels", "dequant_f32", "encode", "bf16_rne", "moe_mlp",
     "FIT_CLIP_STEPS", "fit_is_monotone", "fit_shape_candidates", "f64_to_f16_bits", "fit_group_sse", "fit",
 ]
 
@@ -300,59 +300,170 @@ def moe_a16(x_bf16: np.ndarray, topk_ids: np.ndarray, num_experts: int, N: int,
 
 
 # ----------------------------------------------------------------------------
-# Nearest-level encoding (CubicQuant article, Core: each weight takes the code of
-# the nearest level of its group, given the group's s, a, b). The pages fix no
-# arithmetic for the choice; this library's reading decides it in fp32, so that
-# the device encoder and this definition agree code for code:
-#   q_j = fl32( fl32(a X_j + fl32(b Y_j + j^3)) * fl32(1 / Kmax^3) ),
-#         X_j = j Kmax^2 - j^3, Y_j = j^2 Kmax - j^3 (each fl32 a single rounding
-#         of the exact value, i.e. two fused multiply-adds and one product),
-#   v_j = fl32(|s| q_j),  d_j = |fl32(|w| - v_j)|   for j = 0 .. Kmax,
-#   k = j* with the sign of w * s, j* the first j of smallest d_j (ties go to
-#   the smaller |k|). The extra code -2^(B-1) is never chosen.
+# The format's fp32 levels. A stored group reconstructs each weight as the real
+# number s * sign(k) * q(|k| / Kmax) (CubicQuant article, Core); written out in
+# fp32 (the storage section keeps s in fp32) it is that number rounded once to
+# the nearest fp32 value, ties to even. An exact zero is +0.0; a nonzero value
+# too small for fp32 rounds to a zero of its own sign, and one beyond the fp32
+# range to an infinity.
 # ----------------------------------------------------------------------------
-def encode_levels_f32(a: np.ndarray, b: np.ndarray, bits: int) -> np.ndarray:
-    """q_j (float32) for j = 0 .. Kmax of fp16 shape values a, b (float64 arrays).
+def _rn32_rational(v: Fraction) -> np.float32:
+    """Nearest fp32 value of an exact rational (ties to even)."""
+    if v == 0:
+        return np.float32(0.0)
+    m = abs(v)
+    e = m.numerator.bit_length() - m.denominator.bit_length()   # floor(log2 m) is e or e - 1
+    if m < Fraction(2) ** e:
+        e -= 1
+    e = max(e, -126)                                            # subnormals share the smallest spacing
+    ulp = Fraction(2) ** (e - 23)
+    n = round(m / ulp)                                          # Fraction rounding: half to even
+    mag = np.float32(np.inf) if n * ulp >= 2 ** 128 else np.float32(float(n * ulp))
+    return -mag if v < 0 else mag
 
-    Each fused multiply-add is evaluated exactly in float64 and rounded once:
-    a and b are multiples of 2^-24 and |X|, |Y|, j^3 < 2^22, so every
-    intermediate is a multiple of 2^-24 below 2^26 (at most 50 bits)."""
+
+def _level_exact(s: float, a: float, b: float, j: int, bits: int) -> Fraction:
+    """s * q(j / Kmax) as an exact rational from the stored fp32 s and fp16 a, b."""
     km = kmax(bits)
-    a = np.asarray(a, dtype=np.float64)[..., None]
-    b = np.asarray(b, dtype=np.float64)[..., None]
-    j = np.arange(km + 1, dtype=np.int64)
-    X = (j * km * km - j ** 3).astype(np.float64)
-    Y = (j * j * km - j ** 3).astype(np.float64)
-    t1 = (b * Y + (j ** 3).astype(np.float64)).astype(np.float32)
-    t2 = (a * X + t1.astype(np.float64)).astype(np.float32)
-    inv = np.float32(1.0) / np.float32(km * km * km)
-    return t2 * inv
+    a, b = Fraction(a), Fraction(b)
+    t = Fraction(j, km)
+    return Fraction(float(s)) * (a * t + b * t * t + (1 - a - b) * t * t * t)
 
 
-def encode(w: np.ndarray, scales: np.ndarray, shapes: np.ndarray, bits: int,
-           group: int) -> np.ndarray:
-    """int8 codes [N][K] of float32 weights w [N][K] by the rule above."""
-    w = np.asarray(w, dtype=np.float32)
-    N, K = w.shape
+def format_levels(scales: np.ndarray, a: np.ndarray, b: np.ndarray, bits: int) -> np.ndarray:
+    """fp32 levels RN32(s * q_j) for j = 0 .. 2^(B-1) (float32, shape S + (2^(B-1)+1,)).
+
+    scales float32, a and b float64 values of fp16 numbers, all of one shape S.
+    The float64 product y = s * q_j (q_j from `levels`) carries two roundings, so
+    it lies within 2^-52 |V| of the exact value V; wherever y is further than
+    2^-51 |y| from every fp32 rounding boundary, V rounds like y. The remaining
+    entries, shapes outside the exactly evaluated domain, and non-finite scales
+    are computed with exact rationals instead."""
+    s32 = np.asarray(scales, dtype=np.float32)
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    L = (1 << (bits - 1)) + 1
+    out = np.zeros(s32.shape + (L,), dtype=np.float32)
+    inside = (np.abs(a) <= _SHAPE_ABS_MAX) & (np.abs(b) <= _SHAPE_ABS_MAX)
+    y = np.zeros(out.shape, dtype=np.float64)
+    if inside.any():
+        y[inside] = s32[inside].astype(np.float64)[..., None] * levels(a[inside], b[inside], bits)
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = y.astype(np.float32)
+        mag = np.abs(v)
+        down = np.nextafter(mag, np.float32(0)).astype(np.float64)
+        down = np.where(mag > 0, down, -(2.0 ** -149))
+        up = np.nextafter(mag, np.float32(np.inf)).astype(np.float64)
+        lo = (mag.astype(np.float64) + down) / 2
+        hi = (mag.astype(np.float64) + up) / 2
+        ay = np.abs(y)
+        tol = ay * 2.0 ** -51
+        safe = (ay - tol > lo) & (ay + tol < hi) & np.isfinite(mag) & (mag < np.float32(3.4028235e38))
+    safe &= inside[..., None] & np.isfinite(s32)[..., None]
+    # exact zeros (s = 0 or Q_j = 0) are +0.0, whatever the other factor is
+    q_zero = level_numerators(np.where(inside, a, 0), np.where(inside, b, 0), bits) == 0
+    zero = inside[..., None] & ((s32[..., None] == 0) | q_zero)
+    out[safe] = v[safe]
+    out[zero] = np.float32(0.0)
+    for idx in zip(*np.nonzero(~(safe | zero))):
+        g, j = idx[:-1], int(idx[-1])
+        s = float(s32[g])
+        exact = _level_exact(1.0, float(a[g]), float(b[g]), j, bits)      # q_j
+        if s == 0 or exact == 0:
+            out[idx] = np.float32(0.0)
+        elif not np.isfinite(s):
+            out[idx] = np.float32(s * float(exact))                         # +-inf or NaN
+        else:
+            out[idx] = _rn32_rational(Fraction(s) * exact)
+    return out
+
+
+def dequant_f32(codes: np.ndarray, scales: np.ndarray, shapes: np.ndarray,
+                bits: int, group: int) -> np.ndarray:
+    """W[n,k] in fp32 as the format stores it: RN32(s * sign(k) * q(|k| / Kmax))."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
     if K % group:
         raise ValueError("K must be a multiple of group")
     G = K // group
     s = np.asarray(scales, dtype=np.float32).reshape(N, G)
     ab = np.asarray(shapes, dtype=np.uint16).reshape(N, G, 2)
-    q = encode_levels_f32(f16_bits_to_f64(ab[..., 0]), f16_bits_to_f64(ab[..., 1]), bits)  # [N][G][Kmax+1]
-    aw = np.abs(w).reshape(N, G, group)
-    sa = np.abs(s)
-    best_d = np.full(aw.shape, np.inf, dtype=np.float32)
-    best_j = np.zeros(aw.shape, dtype=np.int64)
-    for jj in range(kmax(bits) + 1):
-        v = sa * q[..., jj]                                  # float32 product
-        d = np.abs(aw - v[..., None])                        # float32 difference
-        better = d < best_d
-        best_d = np.where(better, d, best_d)
-        best_j = np.where(better, jj, best_j)
-    neg = np.signbit(w.reshape(N, G, group)) != np.signbit(s)[..., None]
-    k = np.where(neg, -best_j, best_j)
-    return k.reshape(N, K).astype(np.int8)
+    lv = format_levels(s, f16_bits_to_f64(ab[..., 0]), f16_bits_to_f64(ab[..., 1]), bits)
+    mag = np.abs(codes.astype(np.int64)).reshape(N, G, group)
+    w = np.take_along_axis(lv, mag, axis=2).reshape(N, K)
+    out = np.where(codes < 0, -w, w)
+    return np.where(out == 0, np.float32(0.0), out).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Nearest-level encoding (CubicQuant article, Core: each weight takes the code of
+# its group's nearest reconstruction level, given the group's s, a, b). The
+# levels are the format's fp32 values L_k = RN32(s * sign(k) * q(|k| / Kmax)) for
+# k in [-Kmax, Kmax] (the extra code -2^(B-1) is never chosen), and distances
+# are exact. With v_j = RN32(s q_j), L_{+-j} = +-v_j, so |w - L_k| is smallest
+# over the two signs at | |w| - |v_j| |: the code is j* sign(w) sign(v_j*) for
+# the first j (smallest |k|) of smallest exact | |w| - |v_j| |. A weight of
+# either zero sign takes code 0, and so does a NaN weight (no distance is smaller
+# than another's).
+# ----------------------------------------------------------------------------
+def _nearest_j(aw: np.ndarray, av: np.ndarray):
+    """First index j of the smallest exact | aw - av[j] | for non-negative float32
+    aw [...][n] against av [...][L]: int64 [...][n]. A NaN distance counts as
+    larger than every other, so NaN levels never win and a NaN weight takes 0.
+
+    The difference of two non-negative fp32 values x >= y is exact in float64
+    when y = 0 or x < 2^28 y (it then spans at most 53 bits); weights with a
+    level outside that ratio are decided with exact rationals."""
+    x = aw.astype(np.float64)
+    y = av.astype(np.float64)
+    best = np.full(x.shape, np.inf)
+    bj = np.zeros(x.shape, dtype=np.int64)
+    for j in range(y.shape[-1]):                     # the first strictly smaller distance wins
+        with np.errstate(invalid="ignore"):
+            dj = np.abs(x - y[..., j:j + 1])
+            better = dj < best                       # False for NaN
+        best = np.where(better, dj, best)
+        bj[better] = j
+    # the largest and the smallest positive finite level of each set decide the ratio test
+    fin = np.isfinite(y)
+    ymax = np.where(fin, y, 0.0).max(axis=-1)[..., None]
+    ymin = np.where(fin & (y > 0), y, np.inf).min(axis=-1)[..., None]
+    with np.errstate(over="ignore", invalid="ignore"):
+        loose = (x > 0) & np.isfinite(x) & ((x >= ymin * 2.0 ** 28) | (ymax >= x * 2.0 ** 28))
+    for idx in zip(*np.nonzero(loose)):
+        xv = Fraction(float(x[idx]))
+        best_f, jj = None, 0
+        for j in range(y.shape[-1]):
+            yv = float(y[idx[:-1]][j])
+            if not np.isfinite(yv):
+                continue
+            dj = abs(xv - Fraction(yv))
+            if best_f is None or dj < best_f:
+                best_f, jj = dj, j
+        bj[idx] = jj
+    return bj
+
+
+def encode(w: np.ndarray, scales: np.ndarray, shapes: np.ndarray, bits: int,
+           group: int) -> np.ndarray:
+    """int8 codes [N][K] of float32 weights w [N][K] by the nearest-level rule above."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of group")
+    G = K // group
+    km = kmax(bits)
+    s = np.asarray(scales, dtype=np.float32).reshape(N, G)
+    ab = np.asarray(shapes, dtype=np.uint16).reshape(N, G, 2)
+    v = format_levels(s, f16_bits_to_f64(ab[..., 0]), f16_bits_to_f64(ab[..., 1]), bits)[..., :km + 1]
+    wg = w.reshape(N, G, group)
+    out = np.empty((N, G, group), dtype=np.int64)
+    for n in range(N):                                     # one row at a time bounds the memory
+        j = _nearest_j(np.abs(wg[n]), np.abs(v[n]))        # [G][group]
+        vj = np.take_along_axis(v[n], j, axis=1)
+        flip = np.signbit(wg[n]) != np.signbit(vj)
+        out[n] = np.where(flip, -j, j)
+    return out.reshape(N, K).astype(np.int8)
 
 
 # ----------------------------------------------------------------------------
@@ -408,21 +519,28 @@ def f64_to_f16_bits(v: np.ndarray) -> np.ndarray:
 
 def fit_group_sse(wg: np.ndarray, bits: int, ab: np.ndarray):
     """Losses of every candidate for one group of float32 weights wg [G]:
-    float64 [n_ab][FIT_CLIP_STEPS], the exact squared distance of each weight to
-    the fp32 level that `encode`'s rule picks, summed over the group."""
+    float64 [n_ab][FIT_CLIP_STEPS], the sum over the group of the squared
+    distance from each |w| to its nearest fp32 level of the candidate (the
+    format's levels RN32(s q_j), the nearest by exact distance, as `encode`
+    chooses), each distance exact and squared and summed in float64."""
     wg = np.asarray(wg, dtype=np.float32)
     aw = np.abs(wg)
     amax = aw.max() if aw.size else np.float32(0.0)
+    km = kmax(bits)
     rho = (np.float32(1.0) - np.arange(FIT_CLIP_STEPS, dtype=np.float32) / np.float32(32.0)).astype(np.float32)
     s = (rho * amax).astype(np.float32)                         # [R], one fp32 rounding each
-    q = encode_levels_f32(ab[:, 0], ab[:, 1], bits)            # [n][L] float32
     out = np.empty((len(ab), FIT_CLIP_STEPS), dtype=np.float64)
-    step = max(1, (1 << 23) // (FIT_CLIP_STEPS * q.shape[1] * max(1, aw.size)))
+    step = max(1, (1 << 22) // (FIT_CLIP_STEPS * (km + 1) * max(1, aw.size)))
+    R = FIT_CLIP_STEPS
     for c0 in range(0, len(ab), step):                         # chunks of pairs bound the memory
-        v = (s[None, :, None] * q[c0:c0 + step, None, :]).astype(np.float32)  # [n][R][L] fp32 levels
-        d = np.abs(aw[None, None, None, :] - v[..., None])     # [n][R][L][G] fp32 differences
-        j = np.argmin(d, axis=2)                               # first nearest level
-        vj = np.take_along_axis(v, j, axis=2).astype(np.float64)  # [n][R][G]
+        abc = ab[c0:c0 + step]
+        n = len(abc)
+        sc = np.broadcast_to(s[None, :], (n, R))
+        a = np.broadcast_to(abc[:, 0:1], (n, R))
+        b = np.broadcast_to(abc[:, 1:2], (n, R))
+        v = np.abs(format_levels(sc, a, b, bits)[..., :km + 1])          # [n][R][L] fp32
+        j = _nearest_j(np.broadcast_to(aw, (n, R, aw.size)), v)         # [n][R][G]
+        vj = np.take_along_axis(v, j, axis=2).astype(np.float64)
         e = aw.astype(np.float64)[None, None, :] - vj
         out[c0:c0 + step] = (e * e).sum(axis=2)
     return out, s

@@ -88,3 +88,33 @@ def rne_int(x: F) -> int:
     if r > F(1, 2) or (r == F(1, 2) and fl % 2):
         fl += 1
     return fl
+
+
+def rn32_float32(x: F):
+    """rn32 as a numpy float32: an exact zero is +0.0, a nonzero value that rounds
+    to zero keeps its sign, a rounded magnitude of 2^128 or more is an infinity."""
+    import numpy as np
+    if x == 0:
+        return np.float32(0.0)
+    r = rn32(x)
+    if abs(r) >= F(2) ** 128:
+        return np.float32(np.inf) if x > 0 else np.float32(-np.inf)
+    if r == 0:
+        return np.float32(-0.0) if x < 0 else np.float32(0.0)
+    return np.float32(float(r))
+
+
+def nearest_code(w: F, s: F, a: F, b: F, bits: int) -> int:
+    """Code k in [-Kmax, Kmax] whose fp32 level rn32(s sign(k) q(|k|/Kmax)) is
+    nearest to w by exact distance; among equal distances the smaller |k|, then
+    the first of k = +j, -j (equal distances at +j and -j need w = 0 or a zero
+    level, and then k = 0 is at least as near)."""
+    km = (1 << (bits - 1)) - 1
+    best, best_k = None, 0
+    for j in range(km + 1):
+        for k in ((j, -j) if j else (0,)):
+            lv = rn32(weight_value(k, s, a, b, bits))
+            d = abs(w - lv)
+            if best is None or d < best:
+                best, best_k = d, k
+    return best_k

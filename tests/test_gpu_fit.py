@@ -1,6 +1,8 @@
 """GPU parity of cubic_fit (CubicQuant article, data-free in-group fitting).
 
-The device sums each candidate's loss in fp32, the oracle in float64. Two
+Both score a candidate against its fp32 levels (the format's values, the
+levels cubic_dequant returns). The device sums each candidate's loss in fp32,
+the oracle in float64. Two
 candidates whose losses lie within the fp32 summation error of each other may
 therefore be picked differently, and the minimum loss is what is unique. So the
 tests check that:
@@ -90,11 +92,11 @@ def test_fit_edges():
     w[1, 7] = -0.25
     rng = np.random.default_rng(730)
     w[2] = -np.abs(rng.standard_normal(256)).astype(np.float32)
-    q = oracle.encode_levels_f32(0.375, 1.25, bits)
+    s = np.float32(0.0625)
+    q = oracle.format_levels(np.array([s]), np.array([0.375]), np.array([1.25]), bits)[0, :8]
     k = rng.integers(-7, 8, size=256)
     k[0] = k[128] = 7
-    s = np.float32(0.0625)
-    w[3] = np.sign(k) * (s * q[np.abs(k)]).astype(np.float32)
+    w[3] = np.sign(k) * q[np.abs(k)]
     w[4] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-30)   # tiny magnitudes
     codes, scales, shapes, loss = out = _fit(torch.from_numpy(w), bits, group)
     _check(w, bits, group, out)

@@ -1,6 +1,7 @@
 """GPU parity of the code stream and of the fp32 dequant against the oracle.
 
-Bars: pack / unpack bit-exact; dequant within 1 fp32 ulp of the float64 oracle,
+Bars: pack / unpack bit-exact; dequant bit-exact against the correctly rounded
+fp32 levels of the oracle (and within 1 fp32 ulp of its float64 values),
 exact for code 0 (+0.0), codes +-Kmax (+-s) and the uniform-INT case a=1, b=0."""
 import numpy as np
 import pytest
@@ -53,7 +54,10 @@ def _dequant_check(w: synth.Weight):
     codes, scales, shapes = np_weight(w)
     packed = cq.cubic_pack(w.codes.to(DEV), w.bits)
     cw = cq.CubicWeight(packed.reshape(-1), w.scales.to(DEV), w.shapes.to(DEV), w.N, w.K, w.bits, w.group)
-    got = cq.cubic_dequant(cw).cpu().numpy().astype(np.float64)
+    got32 = cq.cubic_dequant(cw).cpu().numpy()
+    exact = oracle.dequant_f32(codes, scales, shapes, w.bits, w.group)
+    assert np.array_equal(got32.view(np.uint32), exact.view(np.uint32))
+    got = got32.astype(np.float64)
     ref = oracle.dequant(codes, scales, shapes, w.bits, w.group)
     assert np.all(np.abs(got - ref) <= ulp32(ref)), float((np.abs(got - ref) / ulp32(ref)).max())
     z = codes == 0
@@ -105,6 +109,70 @@ def test_dequant_extra_negative_code():
         scales = synth.lognormal_scales(sg, N * K // G, 0.02).reshape(N, K // G)
         shapes = synth.sample_shapes(sg, N * K // G).reshape(N, K // G, 2)
         cw = cq.CubicWeight(raw.to(DEV), scales.to(DEV), shapes.to(DEV), N, K, bits, G)
-        got = cq.cubic_dequant(cw).cpu().numpy().astype(np.float64)
+        got32 = cq.cubic_dequant(cw).cpu().numpy()
+        exact = oracle.dequant_f32(codes, scales.numpy(), shapes.numpy().view(np.uint16), bits, G)
+        assert np.array_equal(got32.view(np.uint32), exact.view(np.uint32))
+        got = got32.astype(np.float64)
         ref = oracle.dequant(codes, scales.numpy(), shapes.numpy().view(np.uint16), bits, G)
         assert np.all(np.abs(got - ref) <= ulp32(ref))
+
+
+def _midpoint_groups(bits, n, seed):
+    """(s, a, b) for n groups, each with a level s * q_j that lies exactly on the
+    midpoint between two neighbouring fp32 numbers, so that only the tie rule
+    decides its rounding. With s = Kmax^3 * m * 2^e (m odd) the level is the dyadic
+    number m * R_j * 2^(e - 24), R_j = Kmax^3 * q_j * 2^24 an integer; it is a
+    midpoint when that product has exactly 25 significant bits."""
+    rng = np.random.default_rng(seed)
+    km = oracle.kmax(bits)
+    D = km ** 3
+    mmax = (1 << 24) // D                            # s = D * m stays exact in fp32
+    s = np.empty(n, np.float32)
+    ab = np.empty((n, 2), np.float16)
+    i = 0
+    while i < n:
+        a, b = np.float16(rng.uniform(0, 4)), np.float16(rng.uniform(-6.5, 3))
+        j = int(rng.integers(1, km))
+        A, B = int(float(a) * 2 ** 24), int(float(b) * 2 ** 24)
+        R = abs(A * j * km * km + B * j * j * km + ((1 << 24) - A - B) * j ** 3)
+        if R == 0:
+            continue
+        Rodd = R >> ((R & -R).bit_length() - 1)
+        want = 25 - Rodd.bit_length()                # bits of m for a 25-bit product
+        if want < 1 or (1 << (want - 1)) > mmax:
+            continue
+        for _ in range(64):
+            m = int(rng.integers(1 << (want - 1), min(1 << want, mmax + 1))) | 1
+            if (m * Rodd).bit_length() == 25:
+                break
+        else:
+            continue
+        s[i] = np.float32(D * m * 2.0 ** int(rng.integers(-50, -20)))
+        ab[i] = [a, b]
+        i += 1
+    return s, ab
+
+
+@pytest.mark.parametrize("bits", [3, 4, 5, 8])
+def test_dequant_exact_rounding_near_fp32_midpoints(bits):
+    """Scales that put levels on or next to fp32 rounding midpoints, and shape
+    values outside the monotone box (|a|, |b| up to the fp16 range), subnormal
+    and huge scales: every value equals the correctly rounded level."""
+    say(f"dequant rounding edge cases bits={bits}")
+    km = oracle.kmax(bits)
+    N, G = 16, 128
+    K = G * 8
+    s, ab = _midpoint_groups(bits, N * 8, 500 + bits)
+    rng = np.random.default_rng(600 + bits)
+    ab[:8] = rng.uniform(-3e4, 3e4, (8, 2)).astype(np.float16)          # wide shapes: the integer path
+    s[8:12] = np.array([1e-45, 3e-42, 2.5e-39, 1.2e-38], np.float32)    # subnormal and tiny scales
+    s[12:14] = np.array([3.0e38, -2.0e38], np.float32)                   # levels beyond fp32 overflow
+    codes = rng.integers(-km, km + 1, (N, K)).astype(np.int8)
+    scales = s.reshape(N, 8)
+    shapes = ab.view(np.uint16).reshape(N, 8, 2)
+    cw = cq.CubicWeight(cq.cubic_pack(torch.from_numpy(codes).to(DEV), bits).reshape(-1),
+                        torch.from_numpy(scales).to(DEV), torch.from_numpy(shapes.view(np.int16)).to(DEV),
+                        N, K, bits, G)
+    got = cq.cubic_dequant(cw).cpu().numpy()
+    exact = oracle.dequant_f32(codes, scales, shapes, bits, G)
+    assert np.array_equal(got.view(np.uint32), exact.view(np.uint32))

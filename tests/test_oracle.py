@@ -408,6 +408,183 @@ def _enc_params(N, G, bits, seed, uniform=False):
     return s, sh
 
 
+@pytest.mark.parametrize("bits", range(2, 9))
+def test_format_levels_are_correctly_rounded(bits):
+    """The fp32 level RN32(s * q_j) against exact rationals (tests/_exact.py), on
+    generated groups, wide fp16 shapes, subnormal, tiny and huge scales (fp32
+    overflow) and zero scales."""
+    km = oracle.kmax(bits)
+    rng = np.random.default_rng(300 + bits)
+    n = 60
+    s = np.exp(np.log(0.02) + 0.3 * rng.standard_normal(n)).astype(np.float32)
+    ab = _random_shapes(n, 60 + bits).astype(np.uint16)
+    ab[:10] = rng.uniform(-6e4, 6e4, (10, 2)).astype(np.float16).view(np.uint16)
+    s[10:14] = np.array([1e-45, -3e-41, 1.1e-38, 0.0], np.float32)
+    s[14:17] = np.array([3.4e38, -1e38, 2.0 ** 100], np.float32)
+    a, b = oracle.f16_bits_to_f64(ab[:, 0]), oracle.f16_bits_to_f64(ab[:, 1])
+    lv = oracle.format_levels(s, a, b, bits)
+    for i in range(n):
+        A, B = ex.f16_value(int(ab[i, 0])), ex.f16_value(int(ab[i, 1]))
+        for j in range(km + 2):
+            want = ex.rn32_float32(ex.f32_value(float(s[i])) * ex.cubic_q(A, B, F(j, km)))
+            assert np.array([lv[i, j]]).view(np.uint32)[0] == np.array([want]).view(np.uint32)[0], (i, j)
+
+
+def _tie_groups(bits, n, seed):
+    """(s, a, b) with a level exactly on an fp32 rounding midpoint: s = Kmax^3 m 2^e
+    (m odd) makes the level the dyadic m * R_j * 2^(e - 24), a midpoint when that
+    product has 25 significant bits."""
+    rng = np.random.default_rng(seed)
+    km = oracle.kmax(bits)
+    D = km ** 3
+    out = []
+    while len(out) < n:
+        a, b = np.float16(rng.uniform(0, 4)), np.float16(rng.uniform(-6.5, 3))
+        j = int(rng.integers(1, km)) if km > 1 else 1
+        A, B = int(float(a) * 2 ** 24), int(float(b) * 2 ** 24)
+        R = abs(A * j * km * km + B * j * j * km + ((1 << 24) - A - B) * j ** 3)
+        if R == 0:
+            continue
+        Ro = R >> ((R & -R).bit_length() - 1)
+        want = 25 - Ro.bit_length()
+        if want < 1 or (1 << (want - 1)) > (1 << 24) // D:
+            continue
+        m = int(rng.integers(1 << (want - 1), min(1 << want, (1 << 24) // D + 1))) | 1
+        if (m * Ro).bit_length() != 25:
+            continue
+        out.append((np.float32(D * m * 2.0 ** int(rng.integers(-40, -10))), a, b, j))
+    return out
+
+
+@pytest.mark.parametrize("bits", [3, 4, 5, 8])
+def test_format_levels_ties_to_even(bits):
+    """Levels exactly halfway between two fp32 numbers round to the even one: the
+    float64 product is not exact there, so this exercises the exact path."""
+    km = oracle.kmax(bits)
+    for s, a, b, j in _tie_groups(bits, 40, 320 + bits):
+        lv = oracle.format_levels(np.array([s]), np.array([float(a)]), np.array([float(b)]), bits)[0, j]
+        V = ex.f32_value(float(s)) * ex.cubic_q(F(float(a)), F(float(b)), F(j, km))
+        up, dn = ex.rn32(V + V / 2 ** 40), ex.rn32(V - V / 2 ** 40)
+        assert up != dn and (up + dn) / 2 == V                 # V is an exact midpoint
+        assert F(float(lv)) == ex.rn32(V)
+        assert (int(np.array([lv]).view(np.uint32)[0]) & 1) == 0
+
+
+def test_format_levels_hand_worked_tie():
+    """W3, a = 7/8, b = 2^-9: Q_1 = 8a + 2b + 1 = 2049/256. With s = 27 * 8193 * 2^-24
+    the level is s Q_1 / 27 = 8193 * 2049 * 2^-32 = 16787457 * 2^-32, halfway
+    between the fp32 numbers 16787456 * 2^-32 (even significand) and
+    16787458 * 2^-32: it rounds to the first."""
+    s = np.float32(27 * 8193 * 2.0 ** -24)
+    lv = oracle.format_levels(np.array([s]), np.array([0.875]), np.array([2.0 ** -9]), 3)
+    assert lv[0, 1] == np.float32(16787456 * 2.0 ** -32)
+    assert lv[0, 3] == s and lv[0, 0] == 0 and not np.signbit(lv[0, 0])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_dequant_f32_brute_force_from_bytes(bits):
+    rng = np.random.default_rng(210 + bits)
+    N, K, G = 2, 256, 128
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    codes = rng.integers(lo, hi + 1, size=(N, K)).astype(np.int8)   # includes -2^(B-1)
+    field = codes.astype(np.int64) & ((1 << bits) - 1)
+    stream = 0
+    for i, f in enumerate(field.reshape(-1)):
+        stream |= int(f) << (i * bits)
+    raw = stream.to_bytes(N * K * bits // 8, "little")
+    scales = rng.lognormal(np.log(0.02), 0.3, size=(N, K // G)).astype(np.float32)
+    scales[1, 1] = 0.0
+    shapes = _random_shapes(N * K // G, 80 + bits).reshape(N, K // G, 2)
+    W = oracle.dequant_f32(oracle.unpack(np.frombuffer(raw, np.uint8), N, K, bits), scales, shapes, bits, G)
+    for n in range(N):
+        for k in range(K):
+            g = k // G
+            kk = ex.signed_code(ex.read_field(raw, (n * K + k) * bits, bits), bits)
+            want = ex.rn32_float32(ex.weight_value(kk, ex.f32_value(float(scales[n, g])),
+                                                   ex.f16_value(int(shapes[n, g, 0])),
+                                                   ex.f16_value(int(shapes[n, g, 1])), bits))
+            want = np.float32(0.0) if want == 0 else want               # a zero weight is +0.0
+            assert np.array([W[n, k]]).view(np.uint32)[0] == np.array([want]).view(np.uint32)[0]
+
+
+def _enc_params(N, G, bits, seed, uniform=False):
+    rng = np.random.default_rng(seed)
+    s = np.exp(np.log(0.02) + 0.3 * rng.standard_normal((N, G))).astype(np.float32)
+    if uniform:
+        sh = np.zeros((N, G, 2), np.uint16)
+        sh[..., 0] = _f16bits(1.0)
+    else:
+        sh = _random_shapes(N * G, seed).reshape(N, G, 2)
+    return s, sh
+
+
+def _brute_encode(w, s, sh, bits, G):
+    N, K = w.shape
+    out = np.zeros((N, K), np.int8)
+    for n in range(N):
+        for k in range(K):
+            g = k // G
+            out[n, k] = ex.nearest_code(ex.f32_value(float(w[n, k])), ex.f32_value(float(s[n, g])),
+                                        ex.f16_value(int(sh[n, g, 0])), ex.f16_value(int(sh[n, g, 1])), bits)
+    return out
+
+
+def _hard_weights(s, sh, bits, G, rng):
+    """Weights on each level, one fp32 step either side, and on the exact midpoint
+    of neighbouring levels when that is an fp32 number (a tie), with random signs."""
+    N, Gn = s.shape
+    km = oracle.kmax(bits)
+    lv = oracle.format_levels(s, oracle.f16_bits_to_f64(sh[..., 0]), oracle.f16_bits_to_f64(sh[..., 1]), bits)
+    w = (rng.standard_normal((N, Gn * G)) * 0.02).astype(np.float32)
+    for n in range(N):
+        for g in range(Gn):
+            c = []
+            for j in range(1, km + 1):
+                for v in (np.float32(lv[n, g, j]), np.float32((float(lv[n, g, j - 1]) + float(lv[n, g, j])) / 2)):
+                    if j > 1 or v != lv[n, g, j] or True:
+                        c += [np.nextafter(v, np.float32(-1)), v, np.nextafter(v, np.float32(1))]
+            c = c[:G]
+            w[n, g * G:g * G + len(c)] = np.array(c, np.float32) * np.where(rng.random(len(c)) < 0.5, 1, -1)
+    return w
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encode_brute_force_exact(bits):
+    """Every code against an exact-rational search over all codes (tests/_exact.py),
+    with weights on, next to and exactly between levels, huge weights against
+    tiny levels (where a float64 difference rounds), zeros of both signs and a
+    negative and a zero scale."""
+    rng = np.random.default_rng(400 + bits)
+    G = 128
+    s, sh = _enc_params(3, 2, bits, 410 + bits)
+    s[1, 0] = -s[1, 0]
+    s[2, 1] = np.float32(2.0 ** -110)
+    w = _hard_weights(s, sh, bits, G, rng)
+    w[2, 128:136] = np.array([1.0, -2.0 ** 30, 0.0, -0.0, 2.0 ** -100, 3e38, -1e-45, 0.5], np.float32)
+    s[0, 1] = 0.0
+    assert np.array_equal(oracle.encode(w, s, sh, bits, G), _brute_encode(w, s, sh, bits, G))
+
+
+def test_encode_brute_force_wide_codes():
+    rng = np.random.default_rng(420)
+    s, sh = _enc_params(1, 1, 8, 421)
+    w = _hard_weights(s, sh, 8, 128, rng)
+    assert np.array_equal(oracle.encode(w, s, sh, 8, 128), _brute_encode(w, s, sh, 8, 128))
+
+
+@pytest.mark.parametrize("bits", [3, 5])
+def test_encode_at_fp32_tie_levels(bits):
+    """Groups whose levels sit on fp32 rounding midpoints (their fp32 values come
+    from the tie rule), weights placed on and around them."""
+    rng = np.random.default_rng(430 + bits)
+    groups = _tie_groups(bits, 4, 440 + bits)
+    s = np.array([[g[0]] for g in groups], np.float32)
+    sh = np.array([[[int(np.array(g[1]).view(np.uint16)), int(np.array(g[2]).view(np.uint16))]] for g in groups],
+                  np.uint16)
+    w = _hard_weights(s, sh, bits, 128, rng)
+    assert np.array_equal(oracle.encode(w, s, sh, bits, 128), _brute_encode(w, s, sh, bits, 128))
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_encode_uniform_int_closed_form(bits):
     # a = 1, b = 0 is symmetric uniform INT: k = round(w / s * Kmax) clamped,
@@ -427,12 +604,12 @@ def test_encode_uniform_int_closed_form(bits):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
 def test_encode_round_trip_of_levels(bits):
-    # every representable weight encodes to its own code
+    # every weight stored by the format (dequant_f32) encodes to its own code
     km = oracle.kmax(bits)
     N, K, G = 8, 256, 128
     s, sh = _enc_params(N, K // G, bits, 21 + bits)
     codes = np.random.default_rng(bits).integers(-km, km + 1, (N, K)).astype(np.int8)
-    w = oracle.dequant(codes, s, sh, bits, G).astype(np.float32)
+    w = oracle.dequant_f32(codes, s, sh, bits, G)
     assert np.array_equal(oracle.encode(w, s, sh, bits, G), codes)
 
 
@@ -442,43 +619,23 @@ def test_encode_monotone_signs_and_degenerate_scales():
     w = np.sort(np.random.default_rng(3).standard_normal((3, G)) * 0.04).astype(np.float32)
     c = oracle.encode(w, s, sh, bits, G)
     assert np.all(np.diff(c.astype(np.int64), axis=1) >= 0)
-    # a negative scale flips every code; zero scale and zero weights give 0
+    # a negative scale flips every code; zero scale, zero and NaN weights give 0
     assert np.array_equal(oracle.encode(w, -s, sh, bits, G), -c)
     assert not oracle.encode(w, np.zeros_like(s), sh, bits, G).any()
     z = np.zeros((3, G), np.float32)
     z[0, 0] = -0.0
+    z[1, 3] = np.nan
     assert not oracle.encode(z, s, sh, bits, G).any()
-
-
-@pytest.mark.parametrize("bits", [3, 4, 6])
-def test_encode_is_nearest_within_fp32_rounding(bits):
-    # against every level in float64 (the exact levels of dequant): the chosen
-    # level is the nearest up to the fp32 rounding of levels and distances
-    km = oracle.kmax(bits)
-    N, K, G = 4, 384, 128
-    s, sh = _enc_params(N, K // G, bits, 41 + bits)
-    w = (np.random.default_rng(bits).standard_normal((N, K)) * 0.03).astype(np.float32)
-    codes = oracle.encode(w, s, sh, bits, G)
-    allk = np.arange(-km, km + 1)
-    for n in range(N):
-        for g in range(K // G):
-            q = oracle.levels(oracle.f16_bits_to_f64(sh[n, g, 0]), oracle.f16_bits_to_f64(sh[n, g, 1]), bits)
-            vals = float(s[n, g]) * np.sign(allk) * q[np.abs(allk)]
-            ww = w[n, g * G:(g + 1) * G].astype(np.float64)
-            d = np.abs(ww[:, None] - vals[None, :])
-            chosen = d[np.arange(G), codes[n, g * G:(g + 1) * G].astype(np.int64) + km]
-            assert np.all(chosen <= d.min(axis=1) + 8 * np.spacing(np.float32(np.abs(ww).max() + s[n, g])))
 
 
 def test_encode_exact_tie_goes_to_the_smaller_code():
     bits, G = 3, 128
     s, sh = _enc_params(1, 1, bits, 51)
-    q = oracle.encode_levels_f32(oracle.f16_bits_to_f64(sh[0, 0, 0]), oracle.f16_bits_to_f64(sh[0, 0, 1]), bits)
-    v1 = np.float32(abs(s[0, 0])) * q.reshape(-1)[1]
+    v = oracle.format_levels(s[0], oracle.f16_bits_to_f64(sh[0, 0, 0]), oracle.f16_bits_to_f64(sh[0, 0, 1]), bits)[0]
     w = np.zeros((1, G), np.float32)
-    w[0, 0] = v1 / np.float32(2)          # exactly between level 0 and level 1
-    w[0, 1] = -(v1 / np.float32(2))
-    w[0, 2] = v1
+    w[0, 0] = v[1] / np.float32(2)          # exactly between level 0 and level 1
+    w[0, 1] = -(v[1] / np.float32(2))
+    w[0, 2] = v[1]
     c = oracle.encode(w, s, sh, bits, G)
     assert c[0, 0] == 0 and c[0, 1] == 0 and c[0, 2] == 1
 
@@ -593,11 +750,11 @@ def test_fit_matches_per_candidate_brute_force():
     best, best_k = np.inf, -1
     for i in range(0, len(ab), 7):                           # a spread of pairs, all 16 clips each
         sh = oracle.f64_to_f16_bits(ab[i]).reshape(1, 1, 2)
-        q = oracle.encode_levels_f32(ab[i, 0], ab[i, 1], bits)
         for r in range(16):
             s = np.float32(np.float32(1 - r / 32) * amax)
             k = oracle.encode(w, np.array([[s]], dtype=np.float32), sh, bits, G)[0]
-            lv = (s * q[np.abs(k).astype(int)]).astype(np.float64)
+            q = oracle.format_levels(np.array([s]), np.array([ab[i, 0]]), np.array([ab[i, 1]]), bits)[0]
+            lv = np.abs(q[np.abs(k).astype(int)]).astype(np.float64)
             e = np.abs(w[0].astype(np.float64)) - lv
             L = float((e * e).sum())
             if L < best:
@@ -615,12 +772,12 @@ def test_fit_recovers_planted_levels_exactly():
     bits, G = 4, 128
     a, b = 0.375, 1.25                                       # monotone: q' = .375 + 2.5t - 1.875t^2
     assert oracle.fit_is_monotone(F(3, 8), F(5, 4))
-    q = oracle.encode_levels_f32(a, b, bits)
-    assert np.all(np.diff(q) > 0)
     s = np.float32(0.0625)
+    q = oracle.format_levels(np.array([s]), np.array([a]), np.array([b]), bits)[0, :8]
+    assert np.all(np.diff(q) > 0)
     k = rng.integers(-7, 8, size=(2, G))
     k[:, 0] = 7
-    w = (np.sign(k) * (s * q[np.abs(k)]).astype(np.float32)).astype(np.float32)
+    w = (np.sign(k) * q[np.abs(k)]).astype(np.float32)
     codes, scales, shapes, loss, _ = oracle.fit(w, bits, G)
     assert np.all(loss == 0.0)
     assert np.array_equal(codes, k.astype(np.int8))
