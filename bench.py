@@ -568,7 +568,7 @@ def moe_workloads(cq, synth, dev):
     g = torch.Generator().manual_seed(7)
     ids = [torch.randperm(E, generator=g)[:topk].to(torch.int32).view(1, topk).to(dev) for _ in range(8)]
     tw = torch.softmax(torch.rand((1, topk), generator=g), dim=1).to(dev)
-    ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E, H), dtype=torch.uint8, device=dev)
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E), dtype=torch.uint8, device=dev)
     y = torch.empty((1, topk, 2 * I), dtype=torch.float32, device=dev)
     ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm(x, i, gu, E, out=y, workspace=ws))
                       for i in ids], 5, dev)
@@ -589,7 +589,7 @@ def moe_workloads(cq, synth, dev):
     x, tid = synth.moe_routing(seed=4, T=T, E=E, topk=topk, K=H, device=dev)
     tw = torch.softmax(torch.rand((T, topk), generator=torch.Generator().manual_seed(8)), dim=1).to(dev)
     touched = int(torch.unique(tid).numel())
-    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E, H), dtype=torch.uint8, device=dev)
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E), dtype=torch.uint8, device=dev)
     y = torch.empty((T, topk, 2 * I), dtype=torch.float32, device=dev)
     ms = _graph_time([lambda: cq.cubic_moe_grouped_gemm(x, tid, gu, E, out=y, workspace=ws)], 3, dev)
     nb = touched * gu_b + T * H * 2 + T * topk * 2 * I * 4

@@ -87,7 +87,7 @@ def load_library():
         "cubic_linear_mode": (i32, [i64, i64, i64, i32, i32]),
         "cubic_linear_workspace_bytes": (sz, [i64, i64]),
         "cubic_linear": (i32, [vp, i64, wp, vp, vp, sz, vp]),
-        "cubic_moe_workspace_bytes": (sz, [i64, i32, i32, i64]),
+        "cubic_moe_workspace_bytes": (sz, [i64, i32, i32]),
         "cubic_moe_grouped_gemm": (i32, [vp, i64, vp, i32, wp, i32, vp, vp, sz, vp]),
         "cubic_moe_grouped_gemm_static_max_bytes": (sz, []),
         "cubic_moe_grouped_gemm_static": (i32, [vp, i64, vp, i32, wp, i32, vp, vp]),
@@ -290,8 +290,8 @@ def cubic_linear(x: torch.Tensor, w: CubicWeight, out: torch.Tensor | None = Non
     return out
 
 
-def cubic_moe_workspace_bytes(T: int, topk: int, E: int, K: int) -> int:
-    return int(load_library().cubic_moe_workspace_bytes(T, topk, E, K))
+def cubic_moe_workspace_bytes(T: int, topk: int, E: int) -> int:
+    return int(load_library().cubic_moe_workspace_bytes(T, topk, E))
 
 
 def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: CubicWeight, E: int,
@@ -304,7 +304,7 @@ def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: Cub
     cw = experts.c_struct()
     if out is None:
         out = torch.empty((T, topk, experts.N), dtype=torch.float32, device=x.device)
-    need = cubic_moe_workspace_bytes(T, topk, E, experts.K)
+    need = cubic_moe_workspace_bytes(T, topk, E)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(load_library().cubic_moe_grouped_gemm(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw),

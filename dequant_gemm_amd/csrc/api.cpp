@@ -357,8 +357,8 @@ CUBIC_API int cubic_moe_mlp(const uint16_t* x_bf16, int64_t T, const int32_t* to
   return hip_status(e);
 }
 
-CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K) {
-  if (T < 0 || topk <= 0 || E <= 0 || K < 0) return 0;
+CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E) {
+  if (T < 0 || topk <= 0 || E <= 0) return 0;
   return moe_layout(T, topk, E).total;
 }
 

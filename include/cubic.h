@@ -79,8 +79,10 @@ const char* cubic_status_string(int status);
 /* Library version string, e.g. "cubic 0.1 gfx950". */
 const char* cubic_version(void);
 
-/* Pack int8 codes [N][K] into the bit stream packed[N][K*bits/8].
- * K must be a multiple of 32. Codes with |k| > Kmax are written as their
+/* Pack int8 codes [N][K] into the bit stream packed[N][K*bits/8] (CubicQuant
+ * article, Storage section: the codes are plain B-bit integers stored densely,
+ * B bits per weight; the LSB-first two's complement layout is this library's
+ * reading). K must be a multiple of 32. Codes with |k| > Kmax are written as their
  * low `bits` bits AND make the call return CUBIC_ERR_CODE_RANGE: to report
  * that, this call waits for its own kernel (one stream synchronisation).
  * Calls on one device are serialised by a host lock around that check. */
@@ -88,7 +90,8 @@ int cubic_pack(const int8_t* codes, int64_t N, int64_t K, int bits,
                uint8_t* packed, cubic_stream_t stream);
 
 /* Unpack the bit stream into int8 codes [N][K] (sign-extended fields, including
- * -2^(B-1)). K must be a multiple of 32. Bit-exact inverse of cubic_pack. */
+ * -2^(B-1)); the inverse of cubic_pack (CubicQuant article, Storage section).
+ * K must be a multiple of 32. Bit-exact. */
 int cubic_unpack(const uint8_t* packed, int64_t N, int64_t K, int bits,
                  int8_t* codes, cubic_stream_t stream);
 
@@ -133,7 +136,11 @@ int cubic_encode(const float* w, int64_t N, int64_t K, int bits, int group,
 int cubic_fit(const float* w, int64_t N, int64_t K, int bits, int group, int8_t* codes,
               float* scales, uint16_t* shapes, float* loss, cubic_stream_t stream);
 
-/* A16 product y[M][N] = x[M][K] * W^T, x in bf16 (bit patterns), y in fp32.
+/* A16 product y[M][N] = x[M][K] * W^T, x in bf16 (bit patterns), y in fp32
+ * (CubicQuant article, section "一份 checkpoint，同时服务 A16 与 Dynamic A8": A16
+ * multiplies FP16/BF16 activations with the continuous levels; section
+ * "压缩权重必须边解码、边计算": the codes are decoded inside the product's tiles,
+ * scaled per group in FP32, and no dequantised matrix is written).
  * For 2-bit weights x is used in bf16 as is (the valid levels are -s, 0, s, so
  * every product is exact before the fp32 group scaling). For wider codes and
  * 5 <= M <= 16, x is also used as is, against levels held as two bf16 halves
@@ -158,8 +165,11 @@ int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w,
 int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K,
                              int8_t* xq, float* x_scale, cubic_stream_t stream);
 
-/* Dynamic A8 product y[M][N] (fp32) from xq/x_scale of act_quant_int8_per_token.
- * Each code maps to the INT8 carrier C = sign(k) * clamp(rne(127 * q(|k|/Kmax)),
+/* Dynamic A8 product y[M][N] (fp32) from xq/x_scale of act_quant_int8_per_token
+ * (CubicQuant article, section "一份 checkpoint，同时服务 A16 与 Dynamic A8": the
+ * levels map to a deterministic INT8 carrier, the product is an integer dot per
+ * group, scaled per group in FP32; the carrier's formula did not survive text
+ * extraction and the one below is this library's reading). Each code maps to the INT8 carrier C = sign(k) * clamp(rne(127 * q(|k|/Kmax)),
  * -127, 127) (computed exactly with integer arithmetic); per group the exact
  * int32 dot I = sum xq * C is scaled by fp32(s / 127) and accumulated in fp32;
  * the row result is multiplied by x_scale[m]. group must be <= 1024 so that I
@@ -190,8 +200,11 @@ size_t cubic_linear_workspace_bytes(int64_t M, int64_t K);
 int cubic_linear(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float* y,
                  void* workspace, size_t ws_bytes, cubic_stream_t stream);
 
-/* Routed-expert A16 products. E experts with identical (N, K, bits, group) lie
- * back to back: expert e's codes start at expert0->codes + e*code_bytes, its
+/* Routed-expert A16 products (Kimi K3 guide, model-card table: a layer routes
+ * each token to 16 of its experts; CubicQuant article, section "Kimi-K3-Cubic-
+ * 2.5Bit 是怎样得到 2.4986 bit 的？": the routed experts carry the Cubic weights,
+ * and the A16/A8 section notes that routing density decides which kernel wins).
+ * E experts with identical (N, K, bits, group) lie back to back: expert e's codes start at expert0->codes + e*code_bytes, its
  * scales at expert0->scales + e*N*(K/group), its shapes at expert0->shapes +
  * 2*e*N*(K/group). For every pair (t, j): y[t][j][:] = x[t][:] * W_{topk_ids[t][j]}^T
  * (fp32 out, layout [T][topk][N]). Ids outside [0, E) produce zero rows and are
@@ -201,9 +214,10 @@ int cubic_linear(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float
  * more than four tokens takes one pass per up to four of them, the later passes
  * reading its codes from cache). Requires K <= 2^28 and the per-wave activation
  * slice to fit in LDS (CUBIC_ERR_SHAPE otherwise). x_bf16 [T][K] is read directly.
- * The workspace size depends on T, topk and E only (K is accepted and ignored):
- * a header, one 32-byte record per expert and the pair ids grouped by expert. */
-size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E, int64_t K);
+ * The workspace holds a 16-byte header, one 32-byte record per expert and the
+ * pair ids grouped by expert (each part 256-byte aligned); its size depends on
+ * T, topk and E only. Returns 0 for invalid arguments. */
+size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E);
 int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
                            const int32_t* topk_ids, int topk,
                            const cubic_weight* expert0, int E,
@@ -217,7 +231,7 @@ int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
  * cubic_moe_grouped_gemm_static_max_bytes() = 2 MiB that the library holds on
  * each device for the life of the process, instead of a workspace argument.
  * The call allocates and frees nothing. Returns CUBIC_ERR_WORKSPACE when
- * cubic_moe_workspace_bytes(T, topk, E, K) exceeds that maximum (nothing is
+ * cubic_moe_workspace_bytes(T, topk, E) exceeds that maximum (nothing is
  * enqueued then). The routing kernel rewrites everything the product reads, so
  * the buffer needs no clearing between calls. All calls on one device share the
  * buffer: calls that overlap on that device (other streams, or other host

@@ -46,8 +46,10 @@ def test_workspace_sizes():
     assert cq.cubic_gemm_a16_workspace_bytes(4, 7168) == 0
     assert cq.cubic_gemm_a16_workspace_bytes(8, 7168) >= 8 * 7168 * 2 + 8 * 4
     # one 32-byte record per expert and the grouped pair ids; no activation copy
-    assert cq.cubic_moe_workspace_bytes(64, 16, 896, 7168) >= 32 * 896 + 4 * 1024
-    assert cq.cubic_moe_workspace_bytes(64, 16, 896, 7168) == cq.cubic_moe_workspace_bytes(64, 16, 896, 1)
+    assert cq.cubic_moe_workspace_bytes(64, 16, 896) >= 32 * 896 + 4 * 1024
+    # 256-byte aligned parts: header, 896 records of 32 bytes, 1024 pair ids
+    assert cq.cubic_moe_workspace_bytes(64, 16, 896) == 256 + 28672 + 4096
+    assert cq.cubic_moe_workspace_bytes(64, 0, 896) == 0
     lib = cq.load_library()
     assert lib.cubic_status_string(ERR_WS) == b"workspace missing or too small"
     assert lib.cubic_version().startswith(b"cubic")
@@ -175,7 +177,7 @@ def test_call_argument_validation_before_launch():
     assert lib.cubic_pack(p16, 4, 64, 9, p16, None) == ERR_BITS
     assert lib.cubic_unpack(None, 4, 64, 3, p16, None) == ERR_NULL
     assert lib.cubic_unpack(p16, 4, 64, 3, p8, None) == ERR_ALIGN
-    need = lib.cubic_moe_workspace_bytes(4, 2, 8, 512)
+    need = lib.cubic_moe_workspace_bytes(4, 2, 8)
     assert lib.cubic_moe_grouped_gemm(p16, 4, p16, 2, ctypes.byref(w), 8, p16, p16, need - 1, None) == ERR_WS
     assert lib.cubic_moe_grouped_gemm(p16, 4, p16, 0, ctypes.byref(w), 8, p16, p16, need, None) == ERR_SHAPE
     assert lib.cubic_moe_grouped_gemm(p16, 4, None, 2, ctypes.byref(w), 8, p16, p16, need, None) == ERR_NULL

@@ -61,7 +61,7 @@ def test_skewed_routing_and_invalid_ids():
     ids[5, 1] = -1
     ids[7, 0] = E
     ids = ids.to(DEV)
-    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E, K), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E), dtype=torch.uint8, device=DEV)
     y = cq.cubic_moe_grouped_gemm(x, ids, pool, E, workspace=ws).cpu().numpy()
     assert int(ws[:4].view(torch.int32).item()) == 2
     ref = oracle.moe_a16(x_bits(x), ids.cpu().numpy(), E, N,
@@ -136,7 +136,7 @@ def test_routing_over_expert_chunks_and_long_pair_lists():
     ids[3, 5] = -7
     ids[299, 15] = E + 3
     ids[:40, 0] = 2499                  # one expert with many tokens, in the second chunk
-    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E, K), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(T, topk, E), dtype=torch.uint8, device=DEV)
     y = cq.cubic_moe_grouped_gemm(x, ids, pool, E, workspace=ws).cpu().numpy()
     assert int(ws[:4].view(torch.int32).item()) == 2
     ids_np = ids.cpu().numpy()

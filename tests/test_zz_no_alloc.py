@@ -55,7 +55,7 @@ def test_static_scratch_rejects_oversized_routing():
     cap = cq.cubic_moe_grouped_gemm_static_max_bytes()
     assert cap == 2 << 20
     E, T, topk = 8, 1 << 17, 8                                # 4 MiB of pair ids
-    assert cq.cubic_moe_workspace_bytes(T, topk, E, 512) > cap
+    assert cq.cubic_moe_workspace_bytes(T, topk, E) > cap
     x = torch.zeros((16, 512), dtype=torch.bfloat16, device=DEV)
     w = cq.CubicWeight(torch.zeros(16, dtype=torch.uint8, device=DEV), torch.zeros(4, device=DEV),
                        torch.zeros(8, dtype=torch.int16, device=DEV), 8, 512, 2, 512)
