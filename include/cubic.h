@@ -255,8 +255,11 @@ int cubic_moe_grouped_gemm_static(const uint16_t* x_bf16, int64_t T,
  * kind lie back to back as in cubic_moe_grouped_gemm (gate_up0, down0: expert 0).
  * x_bf16 [T][H], topk_ids int32 [T][topk], topk_weights fp32 [T][topk], y fp32
  * [T][H]. One routing feeds both grouped products; the intermediates live in
- * the workspace (routing records, then [T*topk][2I] fp32, [T*topk][I] bf16 and
- * [T*topk][H] fp32), whose size cubic_moe_mlp_workspace_bytes gives. Errors as
+ * the workspace, whose size cubic_moe_mlp_workspace_bytes gives: first the
+ * routing part (cubic_moe_workspace_bytes(T, topk, E) bytes), then the gate_up
+ * outputs [T*topk][2I] fp32, h [T*topk][I] bf16 and the down outputs
+ * [T*topk][H] fp32, each starting at the next multiple of 256 bytes; they stay
+ * there after the call (a pair with an invalid id leaves its rows unspecified). Errors as
  * for cubic_moe_grouped_gemm; CUBIC_ERR_SHAPE when the two weights disagree
  * (gate_up N != 2 * down K or down N != gate_up K). */
 size_t cubic_moe_mlp_workspace_bytes(int64_t T, int topk, int E, int64_t H, int64_t I);

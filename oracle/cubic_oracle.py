@@ -61,7 +61,7 @@ __all__ = [
     "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
     "level_numerators", "levels", "dequant", "gemm_a16",
     "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
-    "format_levels", "dequant_f32", "encode", "bf16_rne", "moe_mlp",
+    "format_levels", "dequant_f32", "encode", "bf16_rne", "silu_mul", "moe_mlp_hidden", "moe_mlp",
     "FIT_CLIP_STEPS", "fit_is_monotone", "fit_shape_candidates", "f64_to_f16_bits", "fit_group_sse", "fit",
 ]
 
@@ -596,6 +596,37 @@ def bf16_rne(v: np.ndarray) -> np.ndarray:
     spacing = 2.0 ** (e - 7)                           # 8 significant bits
     out[nz] = np.rint(v[nz] / spacing) * spacing
     return out
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """SiLU(g) * u = g / (1 + exp(-g)) * u in float64 (before the bf16 rounding of h)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g)) * np.asarray(u, dtype=np.float64)
+
+
+def moe_mlp_hidden(x_bf16: np.ndarray, topk_ids: np.ndarray, num_experts: int, gate_up_weight):
+    """The MLP step's intermediate per pair: (v, h) float64 [T][topk][I] with
+    v = SiLU(g) * u and h = bf16(v), [g | u] = GU_e @ x[t]; zeros for invalid ids."""
+    ids = np.asarray(topk_ids)
+    T, topk = ids.shape
+    X = bf16_bits_to_f64(x_bf16)
+    v_out = None
+    cache = {}
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if not 0 <= e < num_experts:
+                continue
+            if e not in cache:
+                cache[e] = np.asarray(gate_up_weight(e), dtype=np.float64)
+            gu = cache[e] @ X[t]
+            I = gu.shape[0] // 2
+            if v_out is None:
+                v_out = np.zeros((T, topk, I), dtype=np.float64)
+            v_out[t, j] = silu_mul(gu[:I], gu[I:])
+    if v_out is None:
+        return None, None
+    return v_out, bf16_rne(v_out)
 
 
 def moe_mlp(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, num_experts: int,
