@@ -8,11 +8,13 @@ Cache plus L2, so every launch streams its weights from HBM.
 
 Prints ONE JSON line: metric/value (whole-step HBM GB/s of algorithmic bytes),
 roofline of the dominant kernel (gate_up launch; average duration from HIP
-events on the launch stream around graph replays of gate_up launches), and the oracle
-CPU baseline on a bounded sample. `--extra` adds, as extra fields (each also
-reported on stderr as it finishes): the prefill (M = 4096) A16 and A8 products,
+events on the launch stream around graph replays of gate_up launches), the
+M = 4096 half of the metric (prefill_a16: TFLOP/s against the bf16 MFMA peak;
+prefill_a8: TOP/s against the int8 peak), the 16-expert decode step of one layer
+(decode_step_16x, HBM GB/s), and the oracle CPU baseline on a bounded sample.
+`--extra` adds, as extra fields (each also reported on stderr as it finishes):
 the small-M W4 products, nearest-level encoding, data-free group fitting, the
-routed-expert grouped products and the whole routed-expert MLP step.
+routed-expert products and the whole routed-expert MLP step.
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--copies", type=int, default=40, help="rotating weight copies")
+    ap.add_argument("--copies", type=int, default=50, help="rotating weight copies (at least 50)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true", help="also time prefill and small-M products")
@@ -158,14 +160,28 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 20}), flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds: float):
-    """The oracle (numpy float64, one BLAS thread) on a sample of the decode
-    workload: gate_up rows 0..511 (all K), decode + GEMV, repeated for ~seconds."""
+    """The oracle (numpy float64) on a sample of the decode workload: gate_up rows
+    0..511 (all K), unpack + dequant + GEMV, repeated for ~seconds, with the BLAS
+    allowed every core this process may run on. The unpack and dequant steps are
+    numpy element-wise code on one thread; only the GEMV goes through BLAS."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     import synth
+    cores = len(os.sched_getaffinity(0))
     g = synth.make_generator(2)
     w = synth.make_weight(g, 512, 7168, 2, 512, "ternary", 0.015)
     x = synth.activations(g, 1, 7168)
@@ -176,7 +192,8 @@ def cpu_baseline(seconds: float):
     packed = oracle.pack(codes, 2)
     nbytes = algorithmic_bytes(512, 7168, 2, 512, 1)
     reps = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores, user_api="blas"):
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         t0 = time.perf_counter()
         while True:
             c = oracle.unpack(packed, 512, 7168, 2)
@@ -186,9 +203,12 @@ def cpu_baseline(seconds: float):
             if time.perf_counter() - t0 >= seconds:
                 break
         dt = time.perf_counter() - t0
-    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    vendor = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                       for i in blas) or "unknown"
+    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu": _cpu_model(), "blas": vendor,
             "sample": f"decode gate_up rows 0..511 x K=7168 (W2 G512, M=1): unpack+dequant+GEMV, "
-                      f"{reps} reps in {dt:.1f} s"}
+                      f"{reps} reps in {dt:.1f} s; BLAS on {cores} threads, unpack and dequant single-threaded numpy"}
 
 
 def crossover(steps):
@@ -237,10 +257,59 @@ def crossover(steps):
     print(json.dumps({"crossover": rows}), flush=True)
 
 
+def _rotation_graphs(launch, R, c, dev):
+    """HIP graphs G_0 .. G_{R/c - 1}: G_k replays steps k*c .. k*c + c - 1 of a
+    rotation over R weight copies (`launch(i)` enqueues step i on copy i % R).
+    Replaying them in order walks the whole pool, so every launch reads weights
+    that no launch of the last R - 1 steps touched."""
+    import torch
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        for i in range(R):
+            launch(i)
+    torch.cuda.synchronize()
+    graphs = []
+    for k in range(R // c):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(k * c, k * c + c):
+                launch(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def _replay_ms(graphs, first, n, stream):
+    """Time n graph replays (graphs[first], graphs[first + 1], ... cyclically)
+    with HIP events on the replay stream; returns (ms, next index)."""
+    import torch
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    k = first
+    for _ in range(n):
+        graphs[k].replay()
+        k = (k + 1) % len(graphs)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), k
+
+
+def _chunk(steps, R):
+    """Steps per graph: the largest c <= 10 that divides both the step count and R."""
+    for c in range(10, 0, -1):
+        if steps % c == 0 and R % c == 0:
+            return c
+    return 1
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only (one process, one device); "
+                                   "--gpus must be 1"}))
         sys.exit(2)
     if args.write_traffic:
         write_traffic(args.write_traffic, args.traffic_json)
@@ -272,7 +341,7 @@ def main():
         return cq.CubicWeight(cw.codes.clone(), cw.scales.clone(), cw.shapes.clone(), cw.N, cw.K,
                               cw.bits, cw.group)
 
-    R = max(2, args.copies)
+    R = max(50, args.copies)
     ups = [base_up] + [clone(base_up) for _ in range(R - 1)]
     dns = [base_dn] + [clone(base_dn) for _ in range(R - 1)]
     y_up = torch.empty((1, 6144), dtype=torch.float32, device=dev)
@@ -287,50 +356,31 @@ def main():
     bytes_up = algorithmic_bytes(6144, 7168, 2, 512, 1)
     bytes_dn = algorithmic_bytes(7168, 3072, 2, 512, 1)
 
-    def step(i, only_up=False):
+    # One step = the gate_up product on copy i % R, then the down product on copy
+    # (i + R / 2) % R. The launches are captured into HIP graphs of c steps that
+    # together walk the whole pool (R copies, 880 MB at R = 50: over three times
+    # the 256 MB Infinity Cache), so the timed region measures the GPU, not
+    # Python's per-call cost, and every launch streams its weights from HBM
+    # whatever the step count.
+    def step(i):
         cq.cubic_gemm_a16(x_up, ups[i % R], out=y_up)
-        if not only_up:
-            cq.cubic_gemm_a16(x_dn, dns[(i + R // 2) % R], out=y_dn)
+        cq.cubic_gemm_a16(x_dn, dns[(i + R // 2) % R], out=y_dn)
 
-    # The launch sequence is captured once into HIP graphs (one graph = `chunk`
-    # steps over the rotating copies) so that the timed region measures the GPU,
-    # not Python's per-call submission cost.
-    chunk = min(args.steps, 2 * R)
-    reps = max(1, args.steps // chunk)
-    steps_timed = chunk * reps
-    cap = torch.cuda.Stream(dev)
-    cap.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(cap):
-        for i in range(2):
-            step(i)
-    torch.cuda.synchronize()
-    g_step, g_up = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step, stream=cap):
-        for i in range(chunk):
-            step(i)
-    with torch.cuda.graph(g_up, stream=cap):
-        for i in range(chunk):
-            step(i, only_up=True)
+    def up_only(i):
+        cq.cubic_gemm_a16(x_up, ups[i % R], out=y_up)
+
+    c = _chunk(args.steps, R)
+    g_step = _rotation_graphs(step, R, c, dev)
+    g_up = _rotation_graphs(up_only, R, c, dev)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(max(1, args.warmup // chunk + 1)):
-        g_step.replay()
-        g_up.replay()
-    torch.cuda.synchronize()
-
-    def timed(graph):
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for _ in range(reps):
-            graph.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
-
-    ms_per_step = timed(g_step) / steps_timed
-    up_avg_ms = timed(g_up) / steps_timed
-    up_med_ms = up_avg_ms
+    for i in range(args.warmup):                                    # W warmup steps, eager
+        step(i)
+    k_step = (-(-args.warmup // c)) % len(g_step)                   # the pool continues after them
+    ms, _ = _replay_ms(g_step, k_step, args.steps // c, stream)     # exactly K steps
+    ms_per_step = ms / args.steps
+    _, k_up = _replay_ms(g_up, 0, len(g_up), stream)
+    ms, _ = _replay_ms(g_up, k_up, 2 * len(g_up), stream)           # two passes over the pool
+    up_avg_ms = ms / (2 * R)
 
     gbs = (bytes_up + bytes_dn) / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_up / (up_avg_ms * 1e-3) / 1e9
@@ -340,7 +390,7 @@ def main():
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps_timed,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
@@ -350,22 +400,113 @@ def main():
         "data": "synthetic",
         "config": {"workload": "K3 routed-expert decode, W2 G512, M=1, A16: gate_up 6144x7168 + "
                                "down 7168x3072 per step", "rotating_weight_copies": R,
-                   "algorithmic_bytes_per_step": bytes_up + bytes_dn},
+                   "steps_per_graph": c, "algorithmic_bytes_per_step": bytes_up + bytes_dn},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "k_gemv<DecodeW2> (gate_up 6144x7168, M=1)",
                      "avg_launch_us": round(up_avg_ms * 1e3, 3),
-                     "timing": "HIP events on the launch stream around graph replays of "
-                               "back-to-back gate_up launches (rotating copies)",
+                     "timing": f"HIP events on the launch stream around graph replays of {2 * R} "
+                               f"back-to-back gate_up launches over {R} rotating copies",
                      "algorithmic_bytes_per_launch": bytes_up},
     }
+    del ups, dns, g_step, g_up
+    torch.cuda.empty_cache()
+    out.update(prefill_blocks(cq, synth, dev, stream))
+    out["decode_step_16x"] = decode_step_block(cq, synth, dev)
     if args.extra:
-        del ups, dns, g_step, g_up
-        torch.cuda.empty_cache()
         out["extra"] = extra_workloads(cq, synth, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def prefill_blocks(cq, synth, dev, stream):
+    """The M = 4096 half of the metric: W3 G256 weight 6144 x 7168, activations
+    4096 x 7168 bf16 with 36 outlier columns. prefill_a16: one cubic_gemm_a16 call
+    (activation preparation + k_prefill_a16). prefill_a8: act_quant_int8_per_token
+    then cubic_gemm_a8 (k_prefill_a8), the roofline for the product kernel alone.
+    MFMA-bound, so the weight is not rotated; graph replays, HIP events on the
+    replay stream."""
+    import torch
+    res = {}
+    w, x = synth.prefill_config(seed=5, device=dev)
+    cw = cq.CubicWeight(cq.cubic_pack(w.codes, 3).reshape(-1), w.scales, w.shapes, w.N, w.K, 3, 256)
+    del w.codes
+    flops = 2.0 * 4096 * 6144 * 7168
+    ws = torch.empty(cq.cubic_gemm_a16_workspace_bytes(4096, 7168), dtype=torch.uint8, device=dev)
+    y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
+    ms = _graph_time([lambda: cq.cubic_gemm_a16(x, cw, out=y, workspace=ws)] * 4, 5, dev)
+    tf = flops / ms / 1e9
+    res["prefill_a16"] = {
+        "TFLOP/s": round(tf, 2), "ms": round(ms, 4),
+        "workload": "W3 G256 6144x7168, M=4096 bf16, A16 (fp32 out)",
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_F16_PEAK_TFS, 4), "traffic": None,
+                     "kernel": "cubic_gemm_a16 call: k_xprep + k_prefill_a16",
+                     "avg_launch_us": round(ms * 1e3, 2),
+                     "algorithmic_flops_per_launch": flops,
+                     "timing": "HIP events around graph replays of 20 back-to-back calls"}}
+    print(json.dumps({"prefill_a16": res["prefill_a16"]}), file=sys.stderr, flush=True)
+    xq = torch.empty((4096, 7168), dtype=torch.int8, device=dev)
+    sx = torch.empty((4096,), dtype=torch.float32, device=dev)
+    ms_q = _graph_time([lambda: cq.act_quant_int8_per_token(x, xq, sx)] * 4, 5, dev)
+    ms8 = _graph_time([lambda: cq.cubic_gemm_a8(xq, sx, cw, out=y)] * 4, 5, dev)
+    t8 = flops / ms8 / 1e9
+    res["prefill_a8"] = {
+        "TOP/s": round(t8, 2), "gemm_ms": round(ms8, 4), "act_quant_ms": round(ms_q, 4),
+        "TOP/s_with_act_quant": round(flops / (ms8 + ms_q) / 1e9, 2),
+        "workload": "W3 G256 6144x7168, M=4096, Dynamic A8 (per-token int8)",
+        "roofline": {"bound": "mfma", "achieved": round(t8, 2), "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(t8 / MFMA_I8_PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "k_prefill_a8", "avg_launch_us": round(ms8 * 1e3, 2),
+                     "algorithmic_ops_per_launch": flops,
+                     "timing": "HIP events around graph replays of 20 back-to-back launches"}}
+    print(json.dumps({"prefill_a8": res["prefill_a8"]}), file=sys.stderr, flush=True)
+    del x, xq, y, ws, cw
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_step_block(cq, synth, dev):
+    """The Kimi K3 decode step of one layer's routed experts: one token, top-16,
+    as one grouped launch (routing + k_moe_stream) over gate_up 6144 x 7168 W2
+    G512 experts. 128 experts are resident (1.5 GB); launch i takes the i-th of
+    eight disjoint sets of 16, so consecutive launches share no expert and a set
+    recurs only after 1.3 GB of other experts. Algorithmic bytes: 16 experts'
+    codes and group parameters, the token row in, the 16 output rows out."""
+    import torch
+    H, I, bits, group, E, topk = 7168, 3072, 2, 512, 128, 16
+    N, cb = 2 * I, 2 * I * H * bits // 8
+    codes = torch.empty(E * cb, dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N, H // group), dtype=torch.float32, device=dev)
+    shapes = torch.empty((E, N, H // group, 2), dtype=torch.int16, device=dev)
+    for e in range(E):
+        w = synth.moe_expert(e, seed=4, N=N, K=H, bits=bits, group=group, device=dev)
+        cq.cubic_pack(w.codes, bits, out=codes[e * cb:(e + 1) * cb].view(N, H * bits // 8))
+        scales[e] = w.scales
+        shapes[e] = w.shapes
+    pool = cq.CubicWeight(codes, scales.reshape(-1), shapes.reshape(-1), N, H, bits, group)
+    x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=topk, K=H, device=dev)
+    perm = torch.randperm(E, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    ids = [perm[16 * k:16 * k + 16].view(1, topk).to(dev) for k in range(E // topk)]
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E), dtype=torch.uint8, device=dev)
+    y = torch.empty((1, topk, N), dtype=torch.float32, device=dev)
+    ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm(x, i, pool, E, out=y, workspace=ws)) for i in ids],
+                     5, dev)
+    nb = topk * (N * H * bits // 8 + 8 * N * (H // group)) + H * 2 + topk * N * 4
+    gbs = nb / ms / 1e6
+    res = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 2), "bytes_per_launch": nb,
+           "workload": "1 token x top-16 of 128 resident experts, gate_up 6144x7168 W2 G512, A16",
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "cubic_moe_grouped_gemm call: k_moe_route + k_moe_stream<DecodeW2>",
+                        "avg_launch_us": round(ms * 1e3, 2),
+                        "timing": "HIP events around graph replays of 40 launches over 8 disjoint "
+                                  "expert sets"}}
+    print(json.dumps({"decode_step_16x": res}), file=sys.stderr, flush=True)
+    del codes, scales, shapes, pool
+    torch.cuda.empty_cache()
+    return res
 
 
 def _graph_time(calls, reps, dev):
@@ -410,39 +551,12 @@ def _report(res, key):
 
 
 def extra_workloads(cq, synth, dev, stream):
-    """The other workloads, each timed as graph replays: prefill (M = 4096, W3
-    G256) A16 and Dynamic A8, small-batch W4 G128 (M = 8, 64) over rotating
-    weight copies, and the routed-expert products (one token x 16 experts, the
-    decode step; 64 tokens x 16 over 896 experts)."""
+    """The other workloads, each timed as graph replays: small-batch W4 G128
+    (M = 8, 64) over rotating weight copies, nearest-level encoding, group
+    fitting, and the routed-expert products and MLP step (one token x 16
+    experts; 64 tokens x 16 over 896 experts)."""
     import torch
     res = {}
-    w, x = synth.prefill_config(seed=5, device=dev)
-    cw = cq.CubicWeight(cq.cubic_pack(w.codes, 3).reshape(-1), w.scales, w.shapes, w.N, w.K, 3, 256)
-    del w.codes
-    flops = 2.0 * 4096 * 6144 * 7168
-    ws = torch.empty(cq.cubic_gemm_a16_workspace_bytes(4096, 7168), dtype=torch.uint8, device=dev)
-    y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
-    ms = _graph_time([lambda: cq.cubic_gemm_a16(x, cw, out=y, workspace=ws)] * 4, 5, dev)
-    res["prefill_a16"] = {"ms": round(ms, 4), "TFLOP/s": round(flops / ms / 1e9, 2),
-                          "frac_of_f16_peak": round(flops / ms / 1e9 / MFMA_F16_PEAK_TFS, 4),
-                          "includes": "activation prep kernel + product kernel"}
-    _report(res, "prefill_a16")
-    xq = torch.empty((4096, 7168), dtype=torch.int8, device=dev)
-    sx = torch.empty((4096,), dtype=torch.float32, device=dev)
-    # the quantiser is HBM-bound: six input/output sets (528 MB) rotate, more
-    # than the last-level cache holds
-    qsets = [(x.clone(), torch.empty_like(xq), torch.empty_like(sx)) for _ in range(6)]
-    ms_q = _graph_time([(lambda q=q: cq.act_quant_int8_per_token(*q)) for q in qsets], 5, dev)
-    del qsets
-    cq.act_quant_int8_per_token(x, xq, sx)
-    ms8 = _graph_time([lambda: cq.cubic_gemm_a8(xq, sx, cw, out=y)] * 2, 3, dev)
-    res["prefill_a8"] = {"act_quant_ms": round(ms_q, 4), "gemm_ms": round(ms8, 4),
-                         "TOP/s": round(flops / ms8 / 1e9, 2),
-                         "frac_of_i8_peak": round(flops / ms8 / 1e9 / MFMA_I8_PEAK_TOPS, 4),
-                         "act_quant_GB/s": round((4096 * 7168 * 3 + 4096 * 4) / ms_q / 1e6, 1)}
-    _report(res, "prefill_a8")
-    del x, xq, y, ws, cw
-    torch.cuda.empty_cache()
     copies = 16
     for M in (8, 64):
         (wu, xu), (wd, xd) = synth.smallm_config(M, seed=3, device=dev)
@@ -531,7 +645,8 @@ def moe_workloads(cq, synth, dev):
     """Routed experts at the decode distributions, W2 G512: gate_up 6144 x 7168
     (the grouped product) and the whole MLP step (gate_up, SiLU * up in bf16,
     down 7168 x 3072, router-weighted sum). Decode step: one token routed to 16
-    of 64 resident experts, a different set per launch. Batch: 64 tokens x top-16
+    of 64 resident experts, four disjoint sets in turn (consecutive launches share
+    no expert). Batch: 64 tokens x top-16
     over 896 experts (~600 touched). Algorithmic bytes: the touched experts'
     codes and group parameters plus activations in and outputs out; the step's
     intermediates ([P][2I] fp32, [P][I] bf16, [P][H] fp32 for P routed pairs)
@@ -566,7 +681,8 @@ def moe_workloads(cq, synth, dev):
     gu, dn = pool(E, 4, 2 * I, H), pool(E, 6, H, I)
     x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=topk, K=H, device=dev)
     g = torch.Generator().manual_seed(7)
-    ids = [torch.randperm(E, generator=g)[:topk].to(torch.int32).view(1, topk).to(dev) for _ in range(8)]
+    perm = torch.randperm(E, generator=g).to(torch.int32)          # 4 disjoint sets of 16
+    ids = [perm[topk * k:topk * k + topk].view(1, topk).to(dev) for k in range(E // topk)]
     tw = torch.softmax(torch.rand((1, topk), generator=g), dim=1).to(dev)
     ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E), dtype=torch.uint8, device=dev)
     y = torch.empty((1, topk, 2 * I), dtype=torch.float32, device=dev)
