@@ -120,26 +120,35 @@ __device__ __forceinline__ void load_dwords(const uint32_t* src, uint32_t* w) {
   }
 }
 
-// Accumulators of the streaming loop: group partials (part), the group-scaled
-// total (acc) and the current group's parameters.
+// Accumulators of the streaming loop: the open group's MFMA partial (part, one
+// chain of MFMAs; several waves per SIMD hide their latency), the group-scaled
+// total (acc) and the current group's parameters. At a group boundary the
+// partial is scaled into acc and the group's first MFMA starts from zero
+// instead of a cleared register.
 struct StreamState {
   f32x4 acc;
-  f32x4 part[4];
+  f32x4 part;
+  bool fresh;                // the next MFMA opens a group: its C input is zero
   float gscale;
   uint32_t gab;
   int gcur;
   float ca, cb, cc;          // Horner coefficients of the group (direct-level decoders)
   __device__ __forceinline__ void reset() {
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    part = f32x4{0.f, 0.f, 0.f, 0.f};
+    fresh = true;
     gscale = 0.0f;
     gab = 0u;
     gcur = -1;
   }
-  // fold the open group's partials into acc
+  template <bool BF16>
+  __device__ __forceinline__ void mac(const u32x4& a, const u32x4& b) {
+    part = mfma16<BF16>(a, b, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : part);
+    fresh = false;
+  }
+  // fold the open group's partial into acc
   __device__ __forceinline__ f32x4 total() const {
-    return acc + gscale * ((part[0] + part[1]) + (part[2] + part[3]));
+    return fresh ? acc : acc + gscale * part;
   }
 };
 
@@ -154,9 +163,8 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
   const int kb = c.kb, nl = c.nl;
   const int g = t / c.mpg;
   if (g != st.gcur) {                    // wave-uniform
-    st.acc += st.gscale * ((st.part[0] + st.part[1]) + (st.part[2] + st.part[3]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) st.part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!st.fresh) st.acc += st.gscale * st.part;
+    st.fresh = true;
     const uint32_t* gp = c.gp_wave + (nl * c.gmax + (g - g0)) * 2;
     st.gscale = __uint_as_float(gp[0]) * Dec::kLevelUnit;
     st.gab = gp[1];
@@ -195,9 +203,9 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
       Dec::decode(&w[h * B], typename Dec::Coef{st.ca, st.cb, st.cc}, r, rl);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+        st.template mac<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]});
         if constexpr (Dec::kSplit)
-          st.part[j] = mfma16<true>(av[j], u32x4{rl[4 * j], rl[4 * j + 1], rl[4 * j + 2], rl[4 * j + 3]}, st.part[j]);
+          st.template mac<true>(av[j], u32x4{rl[4 * j], rl[4 * j + 1], rl[4 * j + 2], rl[4 * j + 3]});
       }
     } else if constexpr (Dec::kSplit) {
       uint32_t rl[16];
@@ -205,8 +213,8 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
                   Dec::swizzle(nl), r, rl);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        st.part[j] = mfma16<true>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
-        st.part[j] = mfma16<true>(av[j], u32x4{rl[4 * j], rl[4 * j + 1], rl[4 * j + 2], rl[4 * j + 3]}, st.part[j]);
+        st.template mac<true>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]});
+        st.template mac<true>(av[j], u32x4{rl[4 * j], rl[4 * j + 1], rl[4 * j + 2], rl[4 * j + 3]});
       }
     } else {
       if constexpr (IsW2<Dec>::value) {
@@ -216,7 +224,7 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        st.part[j] = mfma16<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, st.part[j]);
+        st.template mac<Dec::kBf16>(av[j], u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]});
     }
     if constexpr (IsW2<Dec>::value) {
       const uint32_t* wv = &w[h * B];
@@ -235,8 +243,8 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
         DecodeW2::extra(wl, hi, lo, rhi, rlo);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          st.part[j] = mfma16<true>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]}, st.part[j]);
-          st.part[j] = mfma16<true>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]}, st.part[j]);
+          st.template mac<true>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]});
+          st.template mac<true>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]});
         }
       }
     }
