@@ -26,6 +26,7 @@ __all__ = [
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
     "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS",
+    "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = [
     "cubic_linear_workspace_bytes", "cubic_linear", "cubic_moe_workspace_bytes",
     "cubic_moe_grouped_gemm", "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
+    "cubic_gemm_a16_ex", "act_quant_int8_per_token_ex", "cubic_gemm_a8_ex", "cubic_moe_grouped_gemm_ex",
 ]
 MODE_A16, MODE_A8 = 0, 1          # cubic_linear_mode results
 
@@ -90,6 +92,10 @@ def load_library():
         "cubic_moe_workspace_bytes": (sz, [i64, i32, i32]),
         "cubic_moe_grouped_gemm": (i32, [vp, i64, vp, i32, wp, i32, vp, vp, sz, vp]),
         "cubic_moe_grouped_gemm_static_max_bytes": (sz, []),
+        "cubic_gemm_a16_ex": (i32, [vp, i32, i64, wp, vp, i32, vp, sz, vp]),
+        "act_quant_int8_per_token_ex": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+        "cubic_gemm_a8_ex": (i32, [vp, vp, i64, wp, vp, i32, vp]),
+        "cubic_moe_grouped_gemm_ex": (i32, [vp, i32, i64, vp, i32, wp, i32, vp, i32, vp, sz, vp]),
         "cubic_moe_grouped_gemm_static": (i32, [vp, i64, vp, i32, wp, i32, vp, vp]),
         "cubic_moe_mlp_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
         "cubic_moe_mlp": (i32, [vp, i64, vp, vp, i32, wp, wp, i32, vp, vp, sz, vp]),
@@ -219,47 +225,84 @@ def cubic_gemm_a16_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().cubic_gemm_a16_workspace_bytes(M, K))
 
 
+DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2          # element types of the _ex entry points
+_DT_IN = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+_DT_OUT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+
+def _in_dtype(x: torch.Tensor, name: str) -> int:
+    if x.dtype not in _DT_IN:
+        raise TypeError(f"{name}: expected bfloat16 or float16, got {x.dtype}")
+    _need(x, x.dtype, name)
+    return _DT_IN[x.dtype]
+
+
+def _out_dtype(out_dtype) -> int:
+    if out_dtype not in _DT_OUT:
+        raise TypeError(f"out_dtype: expected float32 or bfloat16, got {out_dtype}")
+    return _DT_OUT[out_dtype]
+
+
 def cubic_gemm_a16(x: torch.Tensor, w: CubicWeight, out: torch.Tensor | None = None,
-                   workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y[M][N] (fp32) = x[M][K] (bf16) * W^T."""
-    _need(x, torch.bfloat16, "x")
+                   workspace: torch.Tensor | None = None, out_dtype=torch.float32) -> torch.Tensor:
+    """y[M][N] = x[M][K] * W^T; x bf16 (cubic_gemm_a16) or fp16, y fp32 or bf16
+    (cubic_gemm_a16_ex)."""
+    xd, yd = _in_dtype(x, "x"), _out_dtype(out_dtype)
     M = x.shape[0]
     cw = w.c_struct()
     if out is None:
-        out = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+        out = torch.empty((M, w.N), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype:
+        raise TypeError(f"out: expected {out_dtype}, got {out.dtype}")
     need = cubic_gemm_a16_workspace_bytes(M, w.K)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
-    _check(load_library().cubic_gemm_a16(_ptr(x), M, ctypes.byref(cw), _ptr(out), _ptr(workspace),
-                                          ws_bytes, _stream(x)), "cubic_gemm_a16")
+    lib = load_library()
+    if xd == DTYPE_BF16 and yd == DTYPE_F32:
+        st = lib.cubic_gemm_a16(_ptr(x), M, ctypes.byref(cw), _ptr(out), _ptr(workspace), ws_bytes, _stream(x))
+    else:
+        st = lib.cubic_gemm_a16_ex(_ptr(x), xd, M, ctypes.byref(cw), _ptr(out), yd, _ptr(workspace), ws_bytes,
+                                   _stream(x))
+    _check(st, "cubic_gemm_a16")
     return out
 
 
 def act_quant_int8_per_token(x: torch.Tensor, xq: torch.Tensor | None = None,
                              x_scale: torch.Tensor | None = None):
-    """bf16 [M][K] -> (int8 [M][K], fp32 [M])."""
-    _need(x, torch.bfloat16, "x")
+    """bf16 or fp16 [M][K] -> (int8 [M][K], fp32 [M])."""
+    xd = _in_dtype(x, "x")
     M, K = x.shape
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if x_scale is None:
         x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _check(load_library().act_quant_int8_per_token(_ptr(x), M, K, _ptr(xq), _ptr(x_scale), _stream(x)),
-           "act_quant_int8_per_token")
+    lib = load_library()
+    if xd == DTYPE_BF16:
+        st = lib.act_quant_int8_per_token(_ptr(x), M, K, _ptr(xq), _ptr(x_scale), _stream(x))
+    else:
+        st = lib.act_quant_int8_per_token_ex(_ptr(x), xd, M, K, _ptr(xq), _ptr(x_scale), _stream(x))
+    _check(st, "act_quant_int8_per_token")
     return xq, x_scale
 
 
 def cubic_gemm_a8(xq: torch.Tensor, x_scale: torch.Tensor, w: CubicWeight,
-                  out: torch.Tensor | None = None) -> torch.Tensor:
+                  out: torch.Tensor | None = None, out_dtype=torch.float32) -> torch.Tensor:
     _need(xq, torch.int8, "xq")
     _need(x_scale, torch.float32, "x_scale")
+    yd = _out_dtype(out_dtype)
     M = xq.shape[0]
     cw = w.c_struct()
     if out is None:
-        out = torch.empty((M, w.N), dtype=torch.float32, device=xq.device)
-    _check(load_library().cubic_gemm_a8(_ptr(xq), _ptr(x_scale), M, ctypes.byref(cw), _ptr(out),
-                                        _stream(xq)), "cubic_gemm_a8")
+        out = torch.empty((M, w.N), dtype=out_dtype, device=xq.device)
+    elif out.dtype != out_dtype:
+        raise TypeError(f"out: expected {out_dtype}, got {out.dtype}")
+    lib = load_library()
+    if yd == DTYPE_F32:
+        st = lib.cubic_gemm_a8(_ptr(xq), _ptr(x_scale), M, ctypes.byref(cw), _ptr(out), _stream(xq))
+    else:
+        st = lib.cubic_gemm_a8_ex(_ptr(xq), _ptr(x_scale), M, ctypes.byref(cw), _ptr(out), yd, _stream(xq))
+    _check(st, "cubic_gemm_a8")
     return out
 
 
@@ -296,20 +339,28 @@ def cubic_moe_workspace_bytes(T: int, topk: int, E: int) -> int:
 
 def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: CubicWeight, E: int,
                            out: torch.Tensor | None = None,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y[T][topk][N] (fp32): each (token, slot) pair times its expert's weights."""
-    _need(x, torch.bfloat16, "x")
+                           workspace: torch.Tensor | None = None, out_dtype=torch.float32) -> torch.Tensor:
+    """y[T][topk][N]: each (token, slot) pair times its expert's weights; x bf16 or
+    fp16, y fp32 or bf16."""
+    xd, yd = _in_dtype(x, "x"), _out_dtype(out_dtype)
     _need(topk_ids, torch.int32, "topk_ids")
     T, topk = topk_ids.shape
     cw = experts.c_struct()
     if out is None:
-        out = torch.empty((T, topk, experts.N), dtype=torch.float32, device=x.device)
+        out = torch.empty((T, topk, experts.N), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype:
+        raise TypeError(f"out: expected {out_dtype}, got {out.dtype}")
     need = cubic_moe_workspace_bytes(T, topk, E)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _check(load_library().cubic_moe_grouped_gemm(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw),
-                                                 E, _ptr(out), _ptr(workspace), workspace.numel(),
-                                                 _stream(x)), "cubic_moe_grouped_gemm")
+    lib = load_library()
+    if xd == DTYPE_BF16 and yd == DTYPE_F32:
+        st = lib.cubic_moe_grouped_gemm(_ptr(x), T, _ptr(topk_ids), topk, ctypes.byref(cw), E, _ptr(out),
+                                        _ptr(workspace), workspace.numel(), _stream(x))
+    else:
+        st = lib.cubic_moe_grouped_gemm_ex(_ptr(x), xd, T, _ptr(topk_ids), topk, ctypes.byref(cw), E, _ptr(out),
+                                           yd, _ptr(workspace), workspace.numel(), _stream(x))
+    _check(st, "cubic_moe_grouped_gemm")
     return out
 
 

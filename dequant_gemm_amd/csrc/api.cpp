@@ -78,6 +78,7 @@ CUBIC_API const char* cubic_status_string(int status) {
     case CUBIC_ERR_CODE_RANGE: return "code outside [-Kmax, Kmax]";
     case CUBIC_ERR_WORKSPACE: return "workspace missing or too small";
     case CUBIC_ERR_HIP: return "HIP runtime error";
+    case CUBIC_ERR_DTYPE: return "unsupported activation or output dtype";
     default: return "unknown status";
   }
 }
@@ -154,14 +155,18 @@ CUBIC_API size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K) {
   return align256(static_cast<size_t>(M) * K * 2) + align256(static_cast<size_t>(M) * 4);
 }
 
-CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float* y,
-                             void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+namespace {
+bool dtype_in_ok(int d) { return d == CUBIC_DTYPE_BF16 || d == CUBIC_DTYPE_F16; }
+bool dtype_out_ok(int d) { return d == CUBIC_DTYPE_F32 || d == CUBIC_DTYPE_BF16; }
+
+int gemm_a16_impl(const uint16_t* x, bool xf16, int64_t M, const cubic_weight* w, float* y, bool ybf16,
+                  void* workspace, size_t ws_bytes, cubic_stream_t stream) {
   const int st = check_weight(w);
   if (st != CUBIC_OK) return st;
   if (M < 0) return CUBIC_ERR_SHAPE;
   if (M == 0 || w->N == 0) return CUBIC_OK;
-  if (!x_bf16 || !y) return CUBIC_ERR_NULL;
-  if (!aligned16(x_bf16) || !aligned16(y)) return CUBIC_ERR_ALIGN;
+  if (!x || !y) return CUBIC_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return CUBIC_ERR_ALIGN;
   if (M > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
   const size_t need = cubic_gemm_a16_workspace_bytes(M, w->K);
   if (need > 0) {
@@ -169,11 +174,12 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
     if (!aligned16(workspace)) return CUBIC_ERR_ALIGN;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, s));
+  const int yb = ybf16 ? 1 : 0;
+  if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, ybf16, s));
   if (need == 0) {
     GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
-                 x_bf16, nullptr, nullptr, y};
-    return hip_status(launch_gemv(p, w->bits, true, s));
+                 x, nullptr, nullptr, y, 0, yb};
+    return hip_status(launch_gemv(p, w->bits, true, xf16, s));
   }
   uint16_t* xp = static_cast<uint16_t*>(workspace);
   float* xback = reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -184,37 +190,46 @@ CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weig
                         gemv_supported(w->K, w->bits, w->group);
   const bool use_skinny = !use_gemv && skinny_supported(M, w->N, w->K, w->bits, w->group);
   if (use_gemv && w->bits > 2) {
-    // 3- to 8-bit codes: the GEMV reads the bf16 rows as they are (split bf16 levels)
+    // 3- to 8-bit codes: the GEMV reads the caller's rows as they are (bf16:
+    // against split bf16 levels; fp16: against fp16 levels)
     GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
-                 x_bf16, nullptr, nullptr, y};
-    return hip_status(launch_gemv(p, w->bits, false, s));
+                 xf16 ? nullptr : x, xf16 ? x : nullptr, nullptr, y, 0, yb};
+    return hip_status(launch_gemv(p, w->bits, false, xf16, s));
   }
-  hipError_t e = launch_xprep(x_bf16, M, w->K, use_gemv, xp, xback, s);
-  if (e != hipSuccess) return CUBIC_ERR_HIP;
+  // fp16 rows are already what the multi-row kernels read (fp16, back factor 1);
+  // bf16 rows are converted (or, for the 2-bit GEMV, reordered) first
+  const uint16_t* xa = x;
+  const float* xs = nullptr;
+  if (!xf16 || use_gemv) {
+    hipError_t e = launch_xprep(x, M, w->K, use_gemv, xp, xback, s);
+    if (e != hipSuccess) return CUBIC_ERR_HIP;
+    xa = xp;
+    xs = xback;
+  }
   if (use_gemv) {
     GemvParams p{w->codes, w->scales, w->shapes, w->N, w->K, w->group, static_cast<int>(M),
-                 nullptr, xp, xback, y};
-    return hip_status(launch_gemv(p, w->bits, false, s));
+                 nullptr, xa, xs, y, 0, yb};
+    return hip_status(launch_gemv(p, w->bits, false, xf16, s));
   }
-  TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xp, xback, y};
+  TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xa, xs, y, yb};
   if (use_skinny) return hip_status(launch_skinny_a16(p, w->bits, s));
   if (M >= kPrefillMinM && prefill_supported(M, w->N, w->K, w->bits, w->group))
     return hip_status(launch_prefill_a16(p, w->bits, s));
   return hip_status(launch_tiled_a16(p, w->bits, s));
 }
 
-CUBIC_API int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, int8_t* xq,
-                                       float* x_scale, cubic_stream_t stream) {
+int act_quant_impl(const uint16_t* x, bool xf16, int64_t M, int64_t K, int8_t* xq, float* x_scale,
+                   cubic_stream_t stream) {
   if (M < 0 || K < 0 || K % 8 != 0) return CUBIC_ERR_SHAPE;
   if (M == 0) return CUBIC_OK;
-  if (!x_bf16 || !xq || !x_scale) return CUBIC_ERR_NULL;
-  if (!aligned16(x_bf16) || !aligned16(xq) || !aligned16(x_scale)) return CUBIC_ERR_ALIGN;
+  if (!x || !xq || !x_scale) return CUBIC_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return CUBIC_ERR_ALIGN;
   if (M > INT32_MAX) return CUBIC_ERR_SHAPE;
-  return hip_status(launch_act_quant(x_bf16, M, K, xq, x_scale, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_act_quant(x, xf16, M, K, xq, x_scale, static_cast<hipStream_t>(stream)));
 }
 
-CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
-                            const cubic_weight* w, float* y, cubic_stream_t stream) {
+int gemm_a8_impl(const int8_t* xq, const float* x_scale, int64_t M, const cubic_weight* w, float* y,
+                 bool ybf16, cubic_stream_t stream) {
   const int st = check_weight(w);
   if (st != CUBIC_OK) return st;
   if (w->group > 1024) return CUBIC_ERR_GROUP;
@@ -223,11 +238,46 @@ CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
   if (!xq || !x_scale || !y) return CUBIC_ERR_NULL;
   if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(y)) return CUBIC_ERR_ALIGN;
   if ((M + 127) / 128 > 65535) return CUBIC_ERR_SHAPE;
-  if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, static_cast<hipStream_t>(stream)));
-  TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xq, x_scale, y};
-  if (prefill_a8_supported(M, w->N, w->K, w->bits, w->group))
-    return hip_status(launch_prefill_a8(p, w->bits, static_cast<hipStream_t>(stream)));
-  return hip_status(launch_tiled_a8(p, w->bits, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, ybf16, s));
+  TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xq, x_scale, y, ybf16 ? 1 : 0};
+  if (prefill_a8_supported(M, w->N, w->K, w->bits, w->group)) return hip_status(launch_prefill_a8(p, w->bits, s));
+  return hip_status(launch_tiled_a8(p, w->bits, s));
+}
+}  // namespace
+
+CUBIC_API int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w, float* y,
+                             void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  return gemm_a16_impl(x_bf16, false, M, w, y, false, workspace, ws_bytes, stream);
+}
+
+CUBIC_API int cubic_gemm_a16_ex(const void* x, int x_dtype, int64_t M, const cubic_weight* w, void* y,
+                                int y_dtype, void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  if (!dtype_in_ok(x_dtype) || !dtype_out_ok(y_dtype)) return CUBIC_ERR_DTYPE;
+  return gemm_a16_impl(static_cast<const uint16_t*>(x), x_dtype == CUBIC_DTYPE_F16, M, w, static_cast<float*>(y),
+                       y_dtype == CUBIC_DTYPE_BF16, workspace, ws_bytes, stream);
+}
+
+CUBIC_API int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K, int8_t* xq,
+                                       float* x_scale, cubic_stream_t stream) {
+  return act_quant_impl(x_bf16, false, M, K, xq, x_scale, stream);
+}
+
+CUBIC_API int act_quant_int8_per_token_ex(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
+                                          float* x_scale, cubic_stream_t stream) {
+  if (!dtype_in_ok(x_dtype)) return CUBIC_ERR_DTYPE;
+  return act_quant_impl(static_cast<const uint16_t*>(x), x_dtype == CUBIC_DTYPE_F16, M, K, xq, x_scale, stream);
+}
+
+CUBIC_API int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
+                            const cubic_weight* w, float* y, cubic_stream_t stream) {
+  return gemm_a8_impl(xq, x_scale, M, w, y, false, stream);
+}
+
+CUBIC_API int cubic_gemm_a8_ex(const int8_t* xq, const float* x_scale, int64_t M, const cubic_weight* w,
+                               void* y, int y_dtype, cubic_stream_t stream) {
+  if (!dtype_out_ok(y_dtype)) return CUBIC_ERR_DTYPE;
+  return gemm_a8_impl(xq, x_scale, M, w, static_cast<float*>(y), y_dtype == CUBIC_DTYPE_BF16, stream);
 }
 
 constexpr int64_t kLinearA8MinM = 256;     // the measured crossover of 2- and 3-bit codes
@@ -366,8 +416,8 @@ namespace {
 // The grouped product behind both routed-expert entry points; `workspace` is
 // the caller's buffer or the library's routing scratch (nullptr: look it up
 // after validation, so a rejected call touches no device state).
-int moe_grouped(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids, int topk,
-                const cubic_weight* expert0, int E, float* y, void* workspace, size_t ws_bytes,
+int moe_grouped(const uint16_t* x_bf16, bool xf16, int64_t T, const int32_t* topk_ids, int topk,
+                const cubic_weight* expert0, int E, float* y, bool ybf16, void* workspace, size_t ws_bytes,
                 bool library_scratch, cubic_stream_t stream) {
   const int st = check_weight(expert0);
   if (st != CUBIC_OK) return st;
@@ -388,7 +438,7 @@ int moe_grouped(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids, int 
   }
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (expert0->K == 0) return hip_status(launch_fill_zero(y, T * topk * expert0->N, s));
+  if (expert0->K == 0) return hip_status(launch_fill_zero(y, T * topk * expert0->N, ybf16, s));
   MoeGemvParams p{};
   p.codes = expert0->codes;
   p.scales = expert0->scales;
@@ -400,10 +450,11 @@ int moe_grouped(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids, int 
   p.code_bytes = static_cast<int64_t>(cubic_code_bytes(expert0->N, expert0->K, expert0->bits));
   p.x = x_bf16;
   p.y = y;
+  p.ybf16 = ybf16 ? 1 : 0;
   const hipError_t e = launch_moe(topk_ids, static_cast<int>(T), E, topk, p,
                                   reinterpret_cast<int32_t*>(ws + L.hdr),
                                   reinterpret_cast<int32_t*>(ws + L.erec),
-                                  reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s);
+                                  reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, xf16, s);
   return hip_status(e);
 }
 }  // namespace
@@ -411,7 +462,15 @@ int moe_grouped(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids, int 
 CUBIC_API int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
                                      int topk, const cubic_weight* expert0, int E, float* y,
                                      void* workspace, size_t ws_bytes, cubic_stream_t stream) {
-  return moe_grouped(x_bf16, T, topk_ids, topk, expert0, E, y, workspace, ws_bytes, false, stream);
+  return moe_grouped(x_bf16, false, T, topk_ids, topk, expert0, E, y, false, workspace, ws_bytes, false, stream);
+}
+
+CUBIC_API int cubic_moe_grouped_gemm_ex(const void* x, int x_dtype, int64_t T, const int32_t* topk_ids,
+                                        int topk, const cubic_weight* expert0, int E, void* y, int y_dtype,
+                                        void* workspace, size_t ws_bytes, cubic_stream_t stream) {
+  if (!dtype_in_ok(x_dtype) || !dtype_out_ok(y_dtype)) return CUBIC_ERR_DTYPE;
+  return moe_grouped(static_cast<const uint16_t*>(x), x_dtype == CUBIC_DTYPE_F16, T, topk_ids, topk, expert0, E,
+                     static_cast<float*>(y), y_dtype == CUBIC_DTYPE_BF16, workspace, ws_bytes, false, stream);
 }
 
 CUBIC_API size_t cubic_moe_grouped_gemm_static_max_bytes(void) { return moe_scratch_bytes(); }
@@ -419,6 +478,6 @@ CUBIC_API size_t cubic_moe_grouped_gemm_static_max_bytes(void) { return moe_scra
 CUBIC_API int cubic_moe_grouped_gemm_static(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
                                             int topk, const cubic_weight* expert0, int E, float* y,
                                             cubic_stream_t stream) {
-  return moe_grouped(x_bf16, T, topk_ids, topk, expert0, E, y, nullptr, moe_scratch_bytes(), true,
+  return moe_grouped(x_bf16, false, T, topk_ids, topk, expert0, E, y, false, nullptr, moe_scratch_bytes(), true,
                      stream);
 }

@@ -118,14 +118,26 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ st
 constexpr float kRneMagic = 12582912.0f;        // 1.5 * 2^23
 
 // Eight bf16 values (one 16-byte vector) to eight int8 codes.
-__device__ __forceinline__ uint2 quant8(const u32x4& v, float sx, float rcp, bool fast) {
+// Eight bf16 (or, with XF16, fp16) values of one 16-byte vector as fp32 (exact).
+template <bool XF16>
+__device__ __forceinline__ void unpack8(const u32x4& v, float* xv) {
   const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-  float xv[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    xv[2 * q] = __uint_as_float(u[q] << 16);
-    xv[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+    if constexpr (XF16) {
+      xv[2 * q] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u[q] & 0xffffu)));
+      xv[2 * q + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u[q] >> 16)));
+    } else {
+      xv[2 * q] = __uint_as_float(u[q] << 16);
+      xv[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+    }
   }
+}
+
+template <bool XF16>
+__device__ __forceinline__ uint2 quant8(const u32x4& v, float sx, float rcp, bool fast) {
+  float xv[8];
+  unpack8<XF16>(v, xv);
   uint32_t f[8];
   bool exact = !fast;
   if (fast) {
@@ -155,13 +167,12 @@ __device__ __forceinline__ uint2 quant8(const u32x4& v, float sx, float rcp, boo
   return make_uint2(lo, hi);
 }
 
+template <bool XF16>
 __device__ __forceinline__ float absmax8(const u32x4& v, float a) {
-  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  float xv[8];
+  unpack8<XF16>(v, xv);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    a = fmaxf(a, fabsf(__uint_as_float(u[q] << 16)));
-    a = fmaxf(a, fabsf(__uint_as_float(u[q] & 0xffff0000u)));
-  }
+  for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(xv[e]));
   return a;
 }
 
@@ -179,7 +190,7 @@ __device__ __forceinline__ float row_scale(float amax, float* red, float* xs_m) 
 // One 256-thread block per row. V > 0: the row (at most 256 * V vectors of 8)
 // is read once into registers, all of its loads in flight together. V == 0:
 // rows of any length, two passes (the second hits L2).
-template <int V>
+template <int V, bool XF16>
 __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ x, int64_t K,
                                                    int8_t* __restrict__ xq,
                                                    float* __restrict__ xs) {
@@ -198,21 +209,21 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
       v[j] = i < nvec ? rv[i] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < V; ++j) amax = absmax8(v[j], amax);
+    for (int j = 0; j < V; ++j) amax = absmax8<XF16>(v[j], amax);
     const float sx = row_scale(amax, red, xs + m);
     const bool fast = sx >= 0x1p-100f && sx <= 0x1p100f;
     const float rcp = __builtin_amdgcn_rcpf(sx);
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int64_t i = tid + 256 * j;
-      if (i < nvec) qv[i] = quant8(v[j], sx, rcp, fast);
+      if (i < nvec) qv[i] = quant8<XF16>(v[j], sx, rcp, fast);
     }
   } else {
-    for (int64_t i = tid; i < nvec; i += 256) amax = absmax8(rv[i], amax);
+    for (int64_t i = tid; i < nvec; i += 256) amax = absmax8<XF16>(rv[i], amax);
     const float sx = row_scale(amax, red, xs + m);
     const bool fast = sx >= 0x1p-100f && sx <= 0x1p100f;
     const float rcp = __builtin_amdgcn_rcpf(sx);
-    for (int64_t i = tid; i < nvec; i += 256) qv[i] = quant8(rv[i], sx, rcp, fast);
+    for (int64_t i = tid; i < nvec; i += 256) qv[i] = quant8<XF16>(rv[i], sx, rcp, fast);
   }
 }
 
@@ -309,10 +320,10 @@ __global__ __launch_bounds__(256) void k_encode(const float* __restrict__ w, int
   reinterpret_cast<uint2*>(codes + e0)[0] = make_uint2(o[0], o[1]);
 }
 
-__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ y, int64_t n) {
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ y, int64_t n, int bf16) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * 256)
-    y[i] = 0.0f;
+    store_out(y, bf16 != 0, i, 0.0f);
 }
 
 }  // namespace cubic
@@ -386,12 +397,17 @@ hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint
   return hipGetLastError();
 }
 
-hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
-                            hipStream_t st) {
+template <bool XF16>
+static auto act_quant_kernel(int64_t K) {
   // registers per thread: the row's vectors over 256 threads, in steps of powers of two
   const int64_t per = (K / 8 + 255) / 256;
-  auto kern = per <= 1 ? k_act_quant<1> : per <= 2 ? k_act_quant<2> : per <= 4 ? k_act_quant<4>
-                                        : per <= 8 ? k_act_quant<8> : k_act_quant<0>;
+  return per <= 1 ? k_act_quant<1, XF16> : per <= 2 ? k_act_quant<2, XF16> : per <= 4 ? k_act_quant<4, XF16>
+                  : per <= 8 ? k_act_quant<8, XF16> : k_act_quant<0, XF16>;
+}
+
+hipError_t launch_act_quant(const uint16_t* x, bool xf16, int64_t M, int64_t K, int8_t* xq, float* xs,
+                            hipStream_t st) {
+  auto kern = xf16 ? act_quant_kernel<true>(K) : act_quant_kernel<false>(K);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(M)), dim3(256), 0, st, x, K, xq, xs);
   return hipGetLastError();
 }
@@ -417,11 +433,11 @@ hipError_t launch_encode(const float* w, int64_t N, int64_t K, int bits, int gro
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t st) {
+hipError_t launch_fill_zero(float* y, int64_t n, bool bf16, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256),
-                     0, st, y, n);
+                     0, st, y, n, bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -172,6 +172,36 @@ __host__ __device__ inline float level_rn32(float s, float a, float b, int j, in
   return level_detail::exact(s, R, km);
 }
 
+// bf16 bit pattern of an fp32 value, rounded to nearest even (finite values).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Output element idx of a row-major array of fp32, or of bf16 when bf16 is set
+// (the fp32 value rounded to nearest even; NaN stays a quiet NaN).
+__device__ __forceinline__ void store_out(float* y, bool bf16, int64_t idx, float v) {
+  if (bf16) {
+    const uint32_t h = (v != v) ? ((__float_as_uint(v) >> 16) | 0x40u) : bf16_rne_bits(v);
+    reinterpret_cast<uint16_t*>(y)[idx] = static_cast<uint16_t>(h);
+  } else {
+    y[idx] = v;
+  }
+}
+
+// Four consecutive outputs starting at idx (idx a multiple of 4, the array
+// 16-byte aligned): one 16-byte fp32 or 8-byte bf16 store.
+__device__ __forceinline__ void store_out4(float* y, bool bf16, int64_t idx, const float* v) {
+  if (bf16) {
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = (v[r] != v[r]) ? ((__float_as_uint(v[r]) >> 16) | 0x40u) : bf16_rne_bits(v[r]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  } else {
+    *reinterpret_cast<f32x4*>(y + idx) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 // Two's complement value of a `bits`-wide field.
 __device__ __forceinline__ int sign_extend(uint32_t field, int bits) {
   return static_cast<int>(field << (32 - bits)) >> (32 - bits);

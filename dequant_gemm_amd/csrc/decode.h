@@ -29,9 +29,12 @@ namespace cubic {
 // sees it, two more MFMAs add x * hi and x * lo at those positions, with
 // hi = bf16(-2 q(2)) and lo = bf16(-2 q(2) - hi) (~16 significant bits).
 // ---------------------------------------------------------------------------
-struct DecodeW2 {
+// F16: the same decode against fp16 activations (the values 0, +-2.0 have the
+// same bit patterns in fp16), multiplied on the fp16 MFMA.
+template <bool F16>
+struct DecodeW2T {
   static constexpr int kBits = 2;
-  static constexpr bool kBf16 = true;
+  static constexpr bool kBf16 = !F16;
   static constexpr bool kSplit = false;
   static constexpr bool kDirect = false;
   static constexpr float kLevelUnit = 0.5f;   // decoded value * s * 0.5 = weight
@@ -72,6 +75,8 @@ struct DecodeW2 {
     }
   }
 };
+using DecodeW2 = DecodeW2T<false>;
+using DecodeW2H = DecodeW2T<true>;
 
 // ---------------------------------------------------------------------------
 // Any width: natural order (register r holds codes 2r, 2r+1); each field indexes
@@ -128,11 +133,6 @@ struct DecodeTable {
 
 // Normalised fp16 level of field value v (two's complement, `bits` wide).
 // bf16 bit pattern of v, round to nearest even (finite v).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // The same level in fp32, for the per-group tables of the products: with
 // X = j K^2 - j^3 and Y = j^2 K - j^3 (integers, exact in fp32), a X and b Y
 // are exact fp32 products of fp16 values while X, Y stay below 2^13 (B <= 5)

@@ -29,7 +29,9 @@ constexpr int kInkWaves = 4;   // waves per workgroup of the single-kernel (in-k
 // converted in-kernel (M <= 4).
 // MT: compile-time bound on M for the in-kernel activation path (1 or 4).
 // W: waves per workgroup, each streaming 1/W of the K range of the 16 rows.
-template <class Dec, bool INK, int SPL, int P, bool ALLIN, int MT, int W>
+// XF16: the activations are fp16 (staged as they are; with table decoders the
+// in-kernel staging copies them without a prescale).
+template <class Dec, bool INK, int SPL, int P, bool ALLIN, int MT, int W, bool XF16>
 __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   extern __shared__ __align__(1024) unsigned char smem[];   // table rows rely on this alignment
   constexpr int B = Dec::kBits;
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
   constexpr int XB = 2;
   const int64_t k0 = static_cast<int64_t>(tb) * kStep * SPL;
   const int nblk = (te - tb) * kStep * SPL / 16;       // 16-element blocks in the slice
-  XStage<Dec, INK ? MT : 1, XB> xst;
+  XStage<Dec, INK ? MT : 1, XB, XF16> xst;
   const u32x4* xv[INK ? MT : 1] = {};
   if constexpr (INK) {
 #pragma unroll
@@ -102,8 +104,8 @@ __global__ __launch_bounds__(64 * W, 3) void k_gemv(GemvParams p) {
       float v = red[m * 16 + cc];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += red[(w * 16 + m) * 16 + cc];
-      if constexpr (!INK && !Dec::kSplit) v *= p.xback[m];
-      p.y[static_cast<int64_t>(m) * p.N + n0 + cc] = v;
+      if constexpr (!INK && !Dec::kSplit) v *= p.xback ? p.xback[m] : 1.0f;
+      store_out(p.y, p.ybf16 != 0, static_cast<int64_t>(m) * p.N + n0 + cc, v);
     }
   }
 }
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void k_xprep(const uint16_t* __restrict__ x, i
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <class Dec, bool INK, int SPL, int P>
+template <class Dec, bool INK, int SPL, int P, bool XF16 = false>
 static hipError_t launch_gemv_t(const GemvParams& p, hipStream_t st) {
   constexpr int W = INK ? kInkWaves : 4;
   constexpr int MTB = INK ? 4 : 1;                  // MT only matters in-kernel
@@ -208,8 +210,9 @@ static hipError_t launch_gemv_t(const GemvParams& p, hipStream_t st) {
   size_t lds = gemv_lds_fixed<Dec>(geo.gmax, W);
   if (INK) lds += static_cast<size_t>(W) * p.M * geo.nch_w * 32 * 2;
   auto kern = geo.mpw <= P
-                  ? (p.M == 1 ? k_gemv<Dec, INK, SPL, P, true, 1, W> : k_gemv<Dec, INK, SPL, P, true, MTB, W>)
-                  : (p.M == 1 ? k_gemv<Dec, INK, SPL, P, false, 1, W> : k_gemv<Dec, INK, SPL, P, false, MTB, W>);
+                  ? (p.M == 1 ? k_gemv<Dec, INK, SPL, P, true, 1, W, XF16> : k_gemv<Dec, INK, SPL, P, true, MTB, W, XF16>)
+                  : (p.M == 1 ? k_gemv<Dec, INK, SPL, P, false, 1, W, XF16>
+                              : k_gemv<Dec, INK, SPL, P, false, MTB, W, XF16>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -261,8 +264,32 @@ bool gemv_supported(int64_t K, int bits, int group) {
   return geo.gmax <= 4 * kGpRegs;
 }
 
-hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st) {
+hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, bool xf16, hipStream_t st) {
   const bool spl2 = gemv_spl(bits, p.group) == 2;
+  if (xf16) {
+    // fp16 activations: 2-bit codes on the fp16 MFMA (x only permuted, by k_xprep for
+    // the multi-row path); wider codes against fp16 levels, x staged in-kernel
+    // (M <= 4) or read as the prepared rows (p.xp = the caller's x, p.xback = NULL)
+    switch (bits) {
+      case 2:
+        if (spl2) return ink ? launch_gemv_t<DecodeW2H, true, 2, 8, true>(p, st)
+                             : launch_gemv_t<DecodeW2H, false, 2, 2, true>(p, st);
+        return ink ? launch_gemv_t<DecodeW2H, true, 1, 8, true>(p, st)
+                   : launch_gemv_t<DecodeW2H, false, 1, 4, true>(p, st);
+      case 3: return ink ? launch_gemv_t<DecodeTable<3>, true, 1, 8, true>(p, st)
+                         : launch_gemv_t<DecodeTable<3>, false, 1, 4, true>(p, st);
+      case 4: return ink ? launch_gemv_t<DecodeTable<4>, true, 1, 6, true>(p, st)
+                         : launch_gemv_t<DecodeTable<4>, false, 1, 4, true>(p, st);
+      case 5: return ink ? launch_gemv_t<DecodeTable<5>, true, 1, 4, true>(p, st)
+                         : launch_gemv_t<DecodeTable<5>, false, 1, 2, true>(p, st);
+      case 6: return ink ? launch_gemv_t<DecodeTable<6>, true, 1, 4, true>(p, st)
+                         : launch_gemv_t<DecodeTable<6>, false, 1, 2, true>(p, st);
+      case 7: return ink ? launch_gemv_t<DecodeDirect<7, false>, true, 1, 4, true>(p, st)
+                         : launch_gemv_t<DecodeDirect<7, false>, false, 1, 4, true>(p, st);
+      default: return ink ? launch_gemv_t<DecodeDirect<8, false>, true, 1, 4, true>(p, st)
+                          : launch_gemv_t<DecodeDirect<8, false>, false, 1, 4, true>(p, st);
+    }
+  }
   switch (bits) {
     case 2:
       if (spl2) return ink ? launch_gemv_t<DecodeW2, true, 2, 8>(p, st)

@@ -27,7 +27,7 @@ __device__ __forceinline__ void load_chunk(const uint32_t* src, uint32_t* w) {
 }
 
 template <class Dec> struct IsW2 { static constexpr bool value = false; };
-template <> struct IsW2<DecodeW2> { static constexpr bool value = true; };
+template <bool F16> struct IsW2<DecodeW2T<F16>> { static constexpr bool value = true; };
 
 template <class Dec>
 __device__ __forceinline__ void build_table(uint16_t* tab_wave, int nl, int kb, uint32_t gab) {
@@ -218,7 +218,7 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
       }
     } else {
       if constexpr (IsW2<Dec>::value) {
-        DecodeW2::fast(&w[h * B], r);
+        Dec::fast(&w[h * B], r);
       } else {
         Dec::decode(&w[h * B], c.tab_wave + nl * (1 << B), Dec::swizzle(nl), r);
       }
@@ -228,23 +228,30 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
     }
     if constexpr (IsW2<Dec>::value) {
       const uint32_t* wv = &w[h * B];
-      if (extra && __any((DecodeW2::extra_bits(wv[0]) | DecodeW2::extra_bits(wv[1])) != 0u)) {
+      if (extra && __any((Dec::extra_bits(wv[0]) | Dec::extra_bits(wv[1])) != 0u)) {
         // rare (wave-uniform): code -2 present; correct r and add the lo part
         const double a = f16_bits_to_f64(static_cast<uint16_t>(st.gab & 0xffffu));
         const double b = f16_bits_to_f64(static_cast<uint16_t>(st.gab >> 16));
         const float v = static_cast<float>(-2.0 * level_numerator(a, b, 2, 1));
-        const uint32_t hi = bf16_rne_bits(v);
-        const uint32_t lo = bf16_rne_bits(v - __uint_as_float(hi << 16));
+        // hi + lo in the MFMA's 16-bit type
+        uint32_t hi, lo;
+        if constexpr (Dec::kBf16) {
+          hi = bf16_rne_bits(v);
+          lo = bf16_rne_bits(v - __uint_as_float(hi << 16));
+        } else {
+          hi = f16_bits(v);
+          lo = f16_bits(v - static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi))));
+        }
         // The operand barrier keeps this rare path's arithmetic inside
         // the branch (otherwise it is speculated into the hot path).
         uint32_t wl[2] = {wv[0], wv[1]};
         asm volatile("" : "+v"(wl[0]), "+v"(wl[1]));
         uint32_t rhi[16], rlo[16];
-        DecodeW2::extra(wl, hi, lo, rhi, rlo);
+        Dec::extra(wl, hi, lo, rhi, rlo);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          st.template mac<true>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]});
-          st.template mac<true>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]});
+          st.template mac<Dec::kBf16>(av[j], u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]});
+          st.template mac<Dec::kBf16>(av[j], u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]});
         }
       }
     }
@@ -354,7 +361,7 @@ __device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c, IssueX&& issue_x, 
 // issue() loads the first XB 16-element blocks per lane and row into registers
 // (indices clamped, so the loads are unconditional) and should run before the
 // weight loads; finish() writes them and copies any longer tail.
-template <class Dec, int MT, int XB>
+template <class Dec, int MT, int XB, bool XF16 = false>
 struct XStage {
   u32x4 reg[MT][XB][2];
 
@@ -378,7 +385,8 @@ struct XStage {
     for (int m = 0; m < MT; ++m) {
       if (m >= M) break;
       uint16_t* xo = xs_wave + m * nch_w * 32;
-      if constexpr (Dec::kBf16) {
+      if constexpr (IsW2<Dec>::value) {
+        // x is already in the MFMA's type (bf16, or fp16 for DecodeW2H): only permuted.
         // 16 consecutive codes 16d..16d+15 fill slots 16d..16d+15 as pairs
         // (code i, code i+8): out[2k] / out[2k+1] take the low / high halves
         // of input registers k and 4+k.
@@ -397,6 +405,20 @@ struct XStage {
         // unconditional: lanes past the slice rewrite block 0 with block 0's data
         // (a conditional use would let the compiler sink the loads behind the
         // weight stream)
+#pragma unroll
+        for (int q = 0; q < XB; ++q) {
+          const int i = lane + 64 * q;
+          put(i < nblk ? i : 0, reg[m][q][0], reg[m][q][1]);
+        }
+        for (int i = lane + 64 * XB; i < nblk; i += 64) put(i, xv[m][2 * i], xv[m][2 * i + 1]);
+        back[m] = 1.0f;
+      } else if constexpr (XF16) {
+        // fp16 activations against fp16 levels: copied as they are, back = 1
+        auto put = [&](int i, const u32x4& lo, const u32x4& hi) {
+          u32x4* dst = reinterpret_cast<u32x4*>(xo + 16 * i);
+          dst[0] = lo;
+          dst[1] = hi;
+        };
 #pragma unroll
         for (int q = 0; q < XB; ++q) {
           const int i = lane + 64 * q;

@@ -17,8 +17,9 @@ struct GemvParams {
   const uint16_t* x;      // bf16 [M][K] (in-kernel conversion)
   const uint16_t* xp;     // fp16 [M][K] prepared, chunk-permuted (prepared variant)
   const float* xback;     // per-row back multiplier of xp
-  float* y;               // [M][N]
+  float* y;               // [M][N] fp32, or bf16 when ybf16
   int rows;               // weight rows per workgroup (<= 16; the launcher sets it)
+  int ybf16;              // outputs rounded to bf16 (nearest even) and stored as 16-bit
 };
 
 struct TiledParams {
@@ -29,7 +30,8 @@ struct TiledParams {
   int group;
   const void* xa;         // A16: fp16 [M][K] prepared; A8: int8 [M][K]
   const float* xs;        // A16: per-row back multiplier; A8: per-row scale
-  float* y;
+  float* y;               // [M][N] fp32, or bf16 when ybf16
+  int ybf16;
 };
 
 struct MoeGemvParams {
@@ -43,7 +45,8 @@ struct MoeGemvParams {
   const int32_t* erec;    // per touched expert: expert, first pair, pairs, pair ids 0 and 1
   const int32_t* sorted;  // pair ids grouped by expert
   const uint16_t* x;      // bf16 activations [T][K]
-  float* y;               // [T*topk][N]
+  float* y;               // [T*topk][N] fp32, or bf16 when ybf16
+  int ybf16;
 };
 
 int device_cu_count();   // compute units of the current device (0 if unknown)
@@ -53,15 +56,16 @@ hipError_t launch_unpack(const uint8_t* packed, int8_t* codes, int64_t N, int64_
                          hipStream_t st);
 hipError_t launch_dequant(const uint8_t* stream, const float* scales, const uint16_t* shapes,
                           float* out, int64_t N, int64_t K, int bits, int group, hipStream_t st);
-hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t st);
+hipError_t launch_fill_zero(float* y, int64_t n, bool bf16, hipStream_t st);
 hipError_t launch_encode(const float* w, int64_t N, int64_t K, int bits, int group, const float* scales,
                          const uint16_t* shapes, int8_t* codes, hipStream_t st);
 int fit_max_group();
 hipError_t launch_fit(const float* w, int64_t N, int64_t K, int bits, int group, int8_t* codes,
                       float* scales, uint16_t* shapes, float* loss, hipStream_t st);
-hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
+hipError_t launch_act_quant(const uint16_t* x, bool xf16, int64_t M, int64_t K, int8_t* xq, float* xs,
                             hipStream_t st);
-hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, hipStream_t st);
+// xf16: the activations are fp16 (x, or xp with xback NULL on the multi-row path)
+hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, bool xf16, hipStream_t st);
 size_t gemv_ink_lds_bytes(int64_t M, int64_t K, int bits, int group);
 bool gemv_supported(int64_t K, int bits, int group);
 hipError_t launch_xprep(const uint16_t* x, int64_t M, int64_t K, bool w2_order, uint16_t* xp,
@@ -77,7 +81,7 @@ hipError_t launch_prefill_a8(const TiledParams& p, int bits, hipStream_t st);
 // LDS the grouped kernel needs with one activation row per pass.
 size_t moe_lds_min_bytes(int64_t K, int bits, int group);
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
-                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st);
+                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, bool xf16, hipStream_t st);
 // Library-owned routing scratch (one per device): its size, and its device
 // address on the current device (looked up on first use per device).
 size_t moe_scratch_bytes();

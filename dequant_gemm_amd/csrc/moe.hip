@@ -14,6 +14,7 @@
 // pairs form the activation rows of the MFMA tile (up to two per pass).
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "gemv_core.h"
 #include "launch.h"
@@ -52,7 +53,7 @@ __device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int& ea, int
 // over experts in chunks of kRouteExperts; pair ids are read once into
 // registers (up to 4096 pairs, beyond that re-read per pass).
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ ids, int P, int E,
-                                                    int64_t N, float* __restrict__ y,
+                                                    int64_t N, float* __restrict__ y, int ybf16,
                                                     int32_t* __restrict__ hdr,
                                                     int32_t* __restrict__ erec,
                                                     int32_t* __restrict__ sorted) {
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
       if (k < kBadList) {
         s_bad[k] = p;
       } else {                                  // beyond the list: this thread clears the row
-        for (int64_t n = 0; n < N; ++n) y[static_cast<int64_t>(p) * N + n] = 0.0f;
+        for (int64_t n = 0; n < N; ++n) store_out(y, ybf16 != 0, static_cast<int64_t>(p) * N + n, 0.0f);
       }
     }
   });
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   const int nbad = min(s_nbad, kBadList);
   for (int b = 0; b < nbad; ++b) {
     const int64_t row = s_bad[b];
-    for (int64_t n = tid; n < N; n += 1024) y[row * N + n] = 0.0f;
+    for (int64_t n = tid; n < N; n += 1024) store_out(y, ybf16 != 0, row * N + n, 0.0f);
   }
   if (tid == 0) hdr[0] = s_nbad;
 
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
 // layout the streaming loop reads in its in-kernel mode), so activations are
 // read from LDS by the MFMA lanes instead of from global memory, and the four
 // waves' partial sums meet in LDS in a fixed order.
-template <class Dec, int SPL, int P, bool ALLIN, int MT>
+template <class Dec, int SPL, int P, bool ALLIN, int MT, bool XF16>
 __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
   static_assert(MT == 1 || MT == 2, "one or two activation rows per pass");
   extern __shared__ __align__(1024) unsigned char smem[];   // table rows rely on this alignment
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
       xv[m] = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(pr[m] / p.topk) * p.K + k0);
-    XStage<Dec, MT, XB> xst;
+    XStage<Dec, MT, XB, XF16> xst;
     float xb[MT];
     auto issue_x = [&]() { xst.issue(xv, nblk, lane); };
     auto finish_x = [&]() { xst.finish(xv, xs_wave, geo.nch_w, nblk, lane, Mt, xb); };
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
         v += red[(1 * 16 + m) * 16 + cc];
         v += red[(2 * 16 + m) * 16 + cc];
         v += red[(3 * 16 + m) * 16 + cc];
-        p.y[static_cast<int64_t>(q) * p.N + n0 + cc] = v;
+        store_out(p.y, p.ybf16 != 0, static_cast<int64_t>(q) * p.N + n0 + cc, v);
       }
     }
     if (mt + MT < cnt) __syncthreads();   // red and the LDS slices are reused by the next pass
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(256, 3) void k_moe_gemv(MoeGemvParams p) {
 // when they change) are fetched one unit ahead into registers. So the memory
 // pipe never drains at a unit boundary. Needs te - tb <= PM for every wave (one slot per macro step)
 // and at most 4 * GPR groups per wave. OCC workgroups per compute unit.
-template <class Dec, int SPL, int PM, int MT, int GPR, int OCC>
+template <class Dec, int SPL, int PM, int MT, int GPR, int OCC, bool XF16>
 __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
                                                          const int32_t* __restrict__ erec,
                                                          const int32_t* __restrict__ sorted,
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
 
   uint32_t cb[PM][DW];
   uint32_t gsc[GPR], gabr[GPR];
-  XStage<Dec, MT, XB> xst;
+  XStage<Dec, MT, XB, XF16> xst;
   const u32x4* xv[MT];
   float xb[MT];
   auto issue_gp = [&](const Unit& u) {
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
         v += red[(1 * 16 + m) * 16 + cc];
         v += red[(2 * 16 + m) * 16 + cc];
         v += red[(3 * 16 + m) * 16 + cc];
-        y[static_cast<int64_t>(qp) * p.N + cur.n0 + cc] = v;
+        store_out(y, p.ybf16 != 0, static_cast<int64_t>(qp) * p.N + cur.n0 + cc, v);
       }
     }
     __syncthreads();                          // red is rewritten by the next unit
@@ -492,7 +493,7 @@ static size_t moe_lds_bytes(const GemvGeom& geo, int mt) {
   return gemv_lds_fixed<Dec>(geo.gmax) + static_cast<size_t>(4) * mt * geo.nch_w * 32 * 2;
 }
 
-template <class Dec, int SPL, int P>
+template <class Dec, int SPL, int P, bool XF16>
 static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, int64_t blocks, int tokens,
                                     hipStream_t st) {
   const GemvGeom geo = gemv_geom(p.K, p.group, SPL);
@@ -500,15 +501,15 @@ static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, int64_t blocks, int 
   // and two workgroups still fit in one compute unit's LDS, else one (the fp16
   // staging of two rows does not fit the register budget). Experts picked by
   // more tokens take several passes over their codes, which then come from L2.
-  int mt = (tokens <= 1 || !Dec::kBf16) ? 1 : 2;
+  int mt = (tokens <= 1 || !IsW2<Dec>::value) ? 1 : 2;
   if (mt == 2 && moe_lds_bytes<Dec>(geo, 2) > 80 * 1024) mt = 1;
   const size_t lds = moe_lds_bytes<Dec>(geo, mt);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const bool allin = geo.mpw <= P;
-  constexpr int MT2 = Dec::kBf16 ? 2 : 1;
+  constexpr int MT2 = IsW2<Dec>::value ? 2 : 1;
   auto pick = [&]() {
-    if (allin) return mt == 1 ? k_moe_gemv<Dec, SPL, P, true, 1> : k_moe_gemv<Dec, SPL, P, true, MT2>;
-    return mt == 1 ? k_moe_gemv<Dec, SPL, P, false, 1> : k_moe_gemv<Dec, SPL, P, false, MT2>;
+    if (allin) return mt == 1 ? k_moe_gemv<Dec, SPL, P, true, 1, XF16> : k_moe_gemv<Dec, SPL, P, true, MT2, XF16>;
+    return mt == 1 ? k_moe_gemv<Dec, SPL, P, false, 1, XF16> : k_moe_gemv<Dec, SPL, P, false, MT2, XF16>;
   };
   auto kern = pick();
   if (lds > 64 * 1024) {
@@ -523,9 +524,10 @@ static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, int64_t blocks, int 
 
 // The persistent kernel for 2-bit codes with groups of 256 or more: PM slots
 // cover a wave's macro steps, GPR registers its groups.
-template <int PM, int GPR>
+template <int PM, int GPR, bool XF16>
 static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, int tokens,
                                       hipStream_t st) {
+  using Dec = typename std::conditional<XF16, DecodeW2H, DecodeW2>::type;
   const GemvGeom geo = gemv_geom(p.K, p.group, 2);
   // Rows per pass: one token routes one row; with several, four rows per pass
   // (fewer passes, so fewer decodes and code re-reads, for experts picked by
@@ -535,9 +537,9 @@ static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, in
   if (mt == 2 && moe_lds_bytes<DecodeW2>(geo, 2) > 80 * 1024) mt = 1;
   const size_t lds = moe_lds_bytes<DecodeW2>(geo, mt);
   // several rows per pass need more registers: two workgroups per compute unit
-  auto kern = mt == 1 ? k_moe_stream<DecodeW2, 2, PM, 1, GPR, 3>
-                      : (mt == 2 ? k_moe_stream<DecodeW2, 2, PM, 2, GPR, 2>
-                                 : k_moe_stream<DecodeW2, 2, PM, 4, GPR, 2>);
+  auto kern = mt == 1 ? k_moe_stream<Dec, 2, PM, 1, GPR, 3, XF16>
+                      : (mt == 2 ? k_moe_stream<Dec, 2, PM, 2, GPR, 2, XF16>
+                                 : k_moe_stream<Dec, 2, PM, 4, GPR, 2, XF16>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -572,42 +574,52 @@ size_t moe_lds_min_bytes(int64_t K, int bits, int group) {
 
 // The grouped product over a routing already in hdr / erec / sorted (p holds
 // them): P pairs, activation row of pair q = q / p.topk, output row q.
-static hipError_t launch_moe_product(const MoeGemvParams& p, int P, int E, int T, int bits,
-                                     hipStream_t st) {
-  const int64_t tiles = (p.N + 15) / 16;
-  const int64_t blocks = static_cast<int64_t>(min(E, P)) * tiles;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+template <bool XF16>
+static hipError_t launch_moe_product_t(const MoeGemvParams& p, int64_t blocks, int T, int bits,
+                                       hipStream_t st) {
+  using W2 = typename std::conditional<XF16, DecodeW2H, DecodeW2>::type;
   switch (bits) {
     case 2:
       if (p.group % 256 == 0) {
         const GemvGeom geo = gemv_geom(p.K, p.group, 2);
-        if (geo.mpw <= 4 && geo.gmax <= 4) return launch_moe_stream_t<4, 1>(p, blocks, T, st);
-        if (geo.mpw <= 7 && geo.gmax <= 8) return launch_moe_stream_t<7, 2>(p, blocks, T, st);
-        if (geo.mpw <= 8 && geo.gmax <= 8) return launch_moe_stream_t<8, 2>(p, blocks, T, st);
-        return launch_moe_gemv_t<DecodeW2, 2, 8>(p, blocks, T, st);
+        if (geo.mpw <= 4 && geo.gmax <= 4) return launch_moe_stream_t<4, 1, XF16>(p, blocks, T, st);
+        if (geo.mpw <= 7 && geo.gmax <= 8) return launch_moe_stream_t<7, 2, XF16>(p, blocks, T, st);
+        if (geo.mpw <= 8 && geo.gmax <= 8) return launch_moe_stream_t<8, 2, XF16>(p, blocks, T, st);
+        return launch_moe_gemv_t<W2, 2, 8, XF16>(p, blocks, T, st);
       }
-      return launch_moe_gemv_t<DecodeW2, 1, 8>(p, blocks, T, st);
-    case 3: return launch_moe_gemv_t<DecodeTable<3>, 1, 6>(p, blocks, T, st);
-    case 4: return launch_moe_gemv_t<DecodeTable<4>, 1, 4>(p, blocks, T, st);
-    case 5: return launch_moe_gemv_t<DecodeTable<5>, 1, 2>(p, blocks, T, st);
-    case 6: return launch_moe_gemv_t<DecodeTable<6>, 1, 2>(p, blocks, T, st);
-    case 7: return launch_moe_gemv_t<DecodeDirect<7, false>, 1, 2>(p, blocks, T, st);
-    default: return launch_moe_gemv_t<DecodeDirect<8, false>, 1, 2>(p, blocks, T, st);
+      return launch_moe_gemv_t<W2, 1, 8, XF16>(p, blocks, T, st);
+    case 3: return launch_moe_gemv_t<DecodeTable<3>, 1, 6, XF16>(p, blocks, T, st);
+    case 4: return launch_moe_gemv_t<DecodeTable<4>, 1, 4, XF16>(p, blocks, T, st);
+    case 5: return launch_moe_gemv_t<DecodeTable<5>, 1, 2, XF16>(p, blocks, T, st);
+    case 6: return launch_moe_gemv_t<DecodeTable<6>, 1, 2, XF16>(p, blocks, T, st);
+    case 7: return launch_moe_gemv_t<DecodeDirect<7, false>, 1, 2, XF16>(p, blocks, T, st);
+    default: return launch_moe_gemv_t<DecodeDirect<8, false>, 1, 2, XF16>(p, blocks, T, st);
   }
 }
 
+// The grouped product over a routing already in hdr / erec / sorted (p holds
+// them): P pairs, activation row of pair q = q / p.topk, output row q.
+static hipError_t launch_moe_product(const MoeGemvParams& p, int P, int E, int T, int bits,
+                                     bool xf16, hipStream_t st) {
+  const int64_t tiles = (p.N + 15) / 16;
+  const int64_t blocks = static_cast<int64_t>(min(E, P)) * tiles;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  return xf16 ? launch_moe_product_t<true>(p, blocks, T, bits, st)
+              : launch_moe_product_t<false>(p, blocks, T, bits, st);
+}
+
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
-                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, hipStream_t st) {
+                      int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, bool xf16, hipStream_t st) {
   const int P = T * topk;
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, hdr,
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, base.ybf16, hdr,
                      erec, sorted);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   MoeGemvParams p = base;
   p.topk = topk;
   p.hdr = hdr; p.erec = erec; p.sorted = sorted;
-  return launch_moe_product(p, P, E, T, bits, st);
+  return launch_moe_product(p, P, E, T, bits, xf16, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -682,7 +694,7 @@ hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E,
                           hipStream_t st) {
   const int P = T * topk;
   const int64_t I = dn.K, H = dn.N;
-  hipError_t err = launch_moe(ids, T, E, topk, up, hdr, erec, sorted, up_bits, st);
+  hipError_t err = launch_moe(ids, T, E, topk, up, hdr, erec, sorted, up_bits, false, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_moe_act, dim3(elementwise_grid(P * I / 4)), dim3(256), 0, st, up.y,
                      static_cast<int64_t>(P), I, h);
@@ -692,7 +704,7 @@ hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E,
   p.topk = 1;                                  // one activation row per pair
   p.x = h;
   p.hdr = hdr; p.erec = erec; p.sorted = sorted;
-  err = launch_moe_product(p, P, E, T, dn_bits, st);
+  err = launch_moe_product(p, P, E, T, dn_bits, false, st);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_moe_combine, dim3(elementwise_grid(static_cast<int64_t>(T) * H / 4)), dim3(256), 0,
                      st, dn.y, ids, topk_w, static_cast<int64_t>(T), topk, E, H, out);

@@ -303,7 +303,7 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
   }
   {
     const int64_t m = m0 + tid;
-    rowmul[tid] = m < p.M ? p.xs[m] : 0.0f;
+    rowmul[tid] = m < p.M ? (p.xs ? p.xs[m] : 1.0f) : 0.0f;
   }
 
   // ---- activation tile: global -> LDS, 16-byte slots, XOR swizzle ----
@@ -512,7 +512,7 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
     const int64_t m = m0 + ml;
     if (m >= p.M) continue;
     const float xm = rowmul[ml];
-    float* yrow = p.y + m * p.N;
+    const int64_t yrow = m * p.N;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
 #pragma unroll
@@ -523,11 +523,11 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * xm * colmul[nl + r];
         if (vec && n + 3 < p.N) {
-          *reinterpret_cast<f32x4*>(yrow + n) = f32x4{v[0], v[1], v[2], v[3]};
+          store_out4(p.y, p.ybf16 != 0, yrow + n, v);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (n + r < p.N) yrow[n + r] = v[r];
+            if (n + r < p.N) store_out(p.y, p.ybf16 != 0, yrow + n + r, v[r]);
         }
       }
     }

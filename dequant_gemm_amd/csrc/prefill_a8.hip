@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
     for (int e = 0; e < 16; ++e) {
       const int ml = 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
       const int64_t m = m0 + ml;
-      if (m < p.M && nrow < p.N) p.y[m * p.N + nrow] = accf[j][e] * sxs[ml];
+      if (m < p.M && nrow < p.N) store_out(p.y, p.ybf16 != 0, m * p.N + nrow, accf[j][e] * sxs[ml]);
     }
   }
 }

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
     float v = 0.0f;
 #pragma unroll
     for (int wv = 0; wv < SK_WAVES; ++wv) v += red[((wv * MB + j) * 16 + e) * 64 + l];
-    if (m < p.M && n0 + n < p.N) p.y[static_cast<int64_t>(m) * p.N + n0 + n] = v * p.xs[m];
+    if (m < p.M && n0 + n < p.N) store_out(p.y, p.ybf16 != 0, static_cast<int64_t>(m) * p.N + n0 + n, v * (p.xs ? p.xs[m] : 1.0f));
   }
 }
 

@@ -139,11 +139,11 @@ __global__ __launch_bounds__(256) void k_tiled_a16(TiledParams p) {
     for (int e = 0; e < 16; ++e) {
       const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (m >= p.M) continue;
-      const float back = p.xs[m];
+      const float back = p.xs ? p.xs[m] : 1.0f;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (n < p.N) p.y[m * p.N + n] = acc[i][j][e] * back;
+        if (n < p.N) store_out(p.y, p.ybf16 != 0, m * p.N + n, acc[i][j][e] * back);
       }
     }
   }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void k_tiled_a8(TiledParams p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (n < p.N) p.y[m * p.N + n] = accf[i][j][e] * sx;
+        if (n < p.N) store_out(p.y, p.ybf16 != 0, m * p.N + n, accf[i][j][e] * sx);
       }
     }
   }

@@ -60,7 +60,18 @@ enum {
   CUBIC_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned              */
   CUBIC_ERR_CODE_RANGE = -6,  /* cubic_pack found a code with |k| > Kmax       */
   CUBIC_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required    */
-  CUBIC_ERR_HIP = -8          /* a HIP runtime call or a launch failed         */
+  CUBIC_ERR_HIP = -8,         /* a HIP runtime call or a launch failed         */
+  CUBIC_ERR_DTYPE = -9        /* an activation or output dtype not supported   */
+};
+
+/* Element types of the _ex entry points' activations and outputs (CubicQuant
+ * article, section "一份 checkpoint，同时服务 A16 与 Dynamic A8": activations in
+ * FP16 or BF16; flow figure of section "压缩权重必须边解码、边计算": results
+ * leave the kernel in the model's dtype). */
+enum {
+  CUBIC_DTYPE_F32 = 0,        /* fp32 (outputs)                                */
+  CUBIC_DTYPE_BF16 = 1,       /* bf16 bit patterns (activations, outputs)      */
+  CUBIC_DTYPE_F16 = 2         /* fp16 bit patterns (activations)               */
 };
 
 typedef struct cubic_weight {
@@ -157,6 +168,18 @@ size_t cubic_gemm_a16_workspace_bytes(int64_t M, int64_t K);
 int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w,
                    float* y, void* workspace, size_t ws_bytes, cubic_stream_t stream);
 
+/* cubic_gemm_a16 with the activation and output types chosen: x_dtype
+ * CUBIC_DTYPE_BF16 or CUBIC_DTYPE_F16 (bit patterns [M][K]); y_dtype
+ * CUBIC_DTYPE_F32 or CUBIC_DTYPE_BF16 ([M][N]). fp16 activations are used as
+ * they are: 2-bit codes multiply them on the fp16 MFMA (every product exact),
+ * wider codes against fp16 levels, with no prescale (an fp16 row already fits).
+ * A bf16 output is the fp32 result rounded to nearest even in the kernel's
+ * epilogue (NaN stays NaN). Other arguments, workspace sizes and errors as for
+ * cubic_gemm_a16; CUBIC_ERR_DTYPE for other dtypes. */
+int cubic_gemm_a16_ex(const void* x, int x_dtype, int64_t M, const cubic_weight* w,
+                      void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                      cubic_stream_t stream);
+
 /* Dynamic per-token INT8 quantisation (msModelSlim article on Kimi K3 INT
  * quantisation, routed-expert W4A8 scheme; CubicQuant article, A16/A8 section):
  * for each row m, amax = max |x[m][:]|, x_scale[m] = fp32(amax / 127) (IEEE
@@ -164,6 +187,10 @@ int cubic_gemm_a16(const uint16_t* x_bf16, int64_t M, const cubic_weight* w,
  * ties to even. An all-zero row gives x_scale = 0 and xq = 0. Bit-exact. */
 int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K,
                              int8_t* xq, float* x_scale, cubic_stream_t stream);
+/* The same for x_dtype CUBIC_DTYPE_BF16 or CUBIC_DTYPE_F16 (every fp16 value is
+ * exact in fp32, so the rule above applies unchanged). */
+int act_quant_int8_per_token_ex(const void* x, int x_dtype, int64_t M, int64_t K,
+                                int8_t* xq, float* x_scale, cubic_stream_t stream);
 
 /* Dynamic A8 product y[M][N] (fp32) from xq/x_scale of act_quant_int8_per_token
  * (CubicQuant article, section "一份 checkpoint，同时服务 A16 与 Dynamic A8": the
@@ -176,6 +203,10 @@ int act_quant_int8_per_token(const uint16_t* x_bf16, int64_t M, int64_t K,
  * stays below 2^24. M == 0 is a no-op. */
 int cubic_gemm_a8(const int8_t* xq, const float* x_scale, int64_t M,
                   const cubic_weight* w, float* y, cubic_stream_t stream);
+/* cubic_gemm_a8 with y_dtype CUBIC_DTYPE_F32 or CUBIC_DTYPE_BF16 (the fp32
+ * result rounded to nearest even in the epilogue). */
+int cubic_gemm_a8_ex(const int8_t* xq, const float* x_scale, int64_t M,
+                     const cubic_weight* w, void* y, int y_dtype, cubic_stream_t stream);
 
 /* Shape dispatcher between the two activation modes (CubicQuant article, A16/A8
  * section and its kernel comparison: A16 serves decode-sized batches best, the
@@ -223,6 +254,14 @@ int cubic_moe_grouped_gemm(const uint16_t* x_bf16, int64_t T,
                            const cubic_weight* expert0, int E,
                            float* y, void* workspace, size_t ws_bytes,
                            cubic_stream_t stream);
+/* cubic_moe_grouped_gemm with x_dtype CUBIC_DTYPE_BF16 or CUBIC_DTYPE_F16 and
+ * y_dtype CUBIC_DTYPE_F32 or CUBIC_DTYPE_BF16 (as in cubic_gemm_a16_ex; rows of
+ * invalid ids are zero in either output type). */
+int cubic_moe_grouped_gemm_ex(const void* x, int x_dtype, int64_t T,
+                              const int32_t* topk_ids, int topk,
+                              const cubic_weight* expert0, int E,
+                              void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                              cubic_stream_t stream);
 
 /* cubic_moe_grouped_gemm for callers that cannot allocate device memory: code
  * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.

@@ -190,9 +190,19 @@ def dequant(codes: np.ndarray, scales: np.ndarray, shapes: np.ndarray,
 # ----------------------------------------------------------------------------
 # A16 (CubicQuant article, A16/A8 section): activations consume continuous levels
 # ----------------------------------------------------------------------------
-def gemm_a16(x_bf16: np.ndarray, W: np.ndarray) -> np.ndarray:
-    """Y[m,n] = sum_k x[m,k] * W[n,k] in float64 (x given as bf16 bit patterns)."""
-    X = bf16_bits_to_f64(x_bf16)
+def _act_values(x_bits: np.ndarray, fmt: str) -> np.ndarray:
+    """Exact values of 16-bit activations: bf16 or fp16 bit patterns."""
+    if fmt == "bf16":
+        return bf16_bits_to_f64(x_bits)
+    if fmt == "f16":
+        return f16_bits_to_f64(x_bits)
+    raise ValueError(f"activation format {fmt!r}")
+
+
+def gemm_a16(x_bits: np.ndarray, W: np.ndarray, fmt: str = "bf16") -> np.ndarray:
+    """Y[m,n] = sum_k x[m,k] * W[n,k] in float64 (x given as bf16, or with
+    fmt="f16" fp16, bit patterns: the article's A16 takes FP16 or BF16)."""
+    X = _act_values(x_bits, fmt)
     return X @ np.asarray(W, dtype=np.float64).T
 
 
@@ -200,14 +210,15 @@ def gemm_a16(x_bf16: np.ndarray, W: np.ndarray) -> np.ndarray:
 # Dynamic A8 (CubicQuant article, A16/A8 section; msModelSlim article, per-token
 # dynamic activation quantisation)
 # ----------------------------------------------------------------------------
-def act_quant(x_bf16: np.ndarray):
-    """Per-row INT8 quantisation: returns (xq int8 [M][K], sx float32 [M]).
+def act_quant(x_bf16: np.ndarray, fmt: str = "bf16"):
+    """Per-row INT8 quantisation: returns (xq int8 [M][K], sx float32 [M]); x as
+    bf16 (or, with fmt="f16", fp16) bit patterns.
 
     sx = fp32(amax / 127); xq = clamp(RNE(fp32(x / sx)), -127, 127). Each fp32
     division is a float64 division rounded to float32, which equals the IEEE
     fp32 quotient (53 >= 2*24 + 2, so the double rounding is innocuous).
     """
-    X = bf16_bits_to_f64(x_bf16)
+    X = _act_values(x_bf16, fmt)
     M = X.shape[0]
     amax = np.abs(X).max(axis=1) if X.shape[1] else np.zeros(M)
     sx = (amax / 127.0).astype(np.float32)
@@ -278,14 +289,15 @@ def gemm_a8(xq: np.ndarray, sx: np.ndarray, codes: np.ndarray, scales: np.ndarra
 # Routed experts: each (token, slot) pair is an A16 product with its expert
 # ----------------------------------------------------------------------------
 def moe_a16(x_bf16: np.ndarray, topk_ids: np.ndarray, num_experts: int, N: int,
-            expert_weight) -> np.ndarray:
+            expert_weight, fmt: str = "bf16") -> np.ndarray:
     """Y[t, j, :] = W_e @ x[t] with e = topk_ids[t, j]; ids outside [0, E) give zeros.
 
-    expert_weight(e) -> float64 W_e [N][K] (the caller dequantises its experts).
+    expert_weight(e) -> float64 W_e [N][K] (the caller dequantises its experts);
+    x as bf16 (or, with fmt="f16", fp16) bit patterns.
     """
     ids = np.asarray(topk_ids)
     T, topk = ids.shape
-    X = bf16_bits_to_f64(x_bf16)
+    X = _act_values(x_bf16, fmt)
     Y = np.zeros((T, topk, N), dtype=np.float64)
     cache = {}
     for t in range(T):

@@ -183,6 +183,24 @@ def test_call_argument_validation_before_launch():
     assert lib.cubic_moe_grouped_gemm(p16, 4, None, 2, ctypes.byref(w), 8, p16, p16, need, None) == ERR_NULL
 
 
+def test_dtype_codes_rejected_before_launch():
+    """Element-type codes: inputs bf16 (1) or fp16 (2), outputs fp32 (0) or bf16 (1)."""
+    lib = cq.load_library()
+    w = _w()
+    p16 = ctypes.c_void_p(16)
+    ERR_DTYPE = -9
+    for xd, yd in ((0, 0), (3, 0), (1, 2), (1, -1), (-1, 1)):
+        assert lib.cubic_gemm_a16_ex(p16, xd, 4, ctypes.byref(w), p16, yd, None, 0, None) == ERR_DTYPE
+        assert lib.cubic_moe_grouped_gemm_ex(p16, xd, 4, p16, 2, ctypes.byref(w), 8, p16, yd, p16, 1 << 20,
+                                             None) == ERR_DTYPE
+    for xd in (0, 3):
+        assert lib.act_quant_int8_per_token_ex(p16, xd, 4, 128, p16, p16, None) == ERR_DTYPE
+    for yd in (2, 5):
+        assert lib.cubic_gemm_a8_ex(p16, p16, 4, ctypes.byref(w), p16, yd, None) == ERR_DTYPE
+    assert lib.cubic_gemm_a16_ex(p16, 2, 0, ctypes.byref(w), p16, 1, None, 0, None) == OK   # no-op
+    assert "type" in lib.cubic_status_string(ERR_DTYPE).decode()
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports the oracle; the library is the only compute."""
     pkg = os.path.join(ROOT, "dequant_gemm_amd")

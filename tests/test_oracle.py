@@ -268,6 +268,35 @@ def test_act_quant_brute_force_and_invariants():
 
 
 # ----------------------------------------------------------------------------- carrier / A8
+def test_act_quant_fp16_brute_force():
+    """fp16 activations (the article's A16 allows FP16 or BF16): the same per-row
+    rule on the exact fp16 values, recomputed with rationals."""
+    rng = np.random.default_rng(77)
+    x = (rng.standard_normal((5, 64)) * np.array([1, 300, 1e-3, 60000 / 4, 1])[:, None]).astype(np.float16)
+    x[4] = 0
+    bits = x.view(np.uint16)
+    xq, sx = oracle.act_quant(bits, fmt="f16")
+    for m in range(5):
+        vals = [ex.f16_value(int(b)) for b in bits[m]]
+        amax = max(abs(v) for v in vals)
+        s = ex.rn32(amax / 127)
+        assert F(float(sx[m])) == s
+        for k in range(64):
+            want = 0 if s == 0 else max(-127, min(127, ex.rne_int(ex.rn32(vals[k] / s))))
+            assert xq[m, k] == want
+
+
+def test_gemm_a16_fp16_activations():
+    rng = np.random.default_rng(78)
+    x = (rng.standard_normal((3, 256)) * 100).astype(np.float16)
+    W = rng.standard_normal((5, 256))
+    Y = oracle.gemm_a16(x.view(np.uint16), W, fmt="f16")
+    for m in range(3):
+        for n in range(5):
+            want = sum(ex.f16_value(int(b)) * F(float(w)) for b, w in zip(x.view(np.uint16)[m], W[n]))
+            assert abs(F(float(Y[m, n])) - want) <= abs(want) * F(1, 2 ** 40) + F(1, 2 ** 60)
+
+
 @pytest.mark.parametrize("bits", range(2, 9))
 def test_carrier_brute_force(bits):
     km = (1 << (bits - 1)) - 1
