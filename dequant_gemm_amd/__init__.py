@@ -25,7 +25,7 @@ __all__ = [
     "act_quant_int8_per_token", "cubic_gemm_a8", "cubic_linear_mode", "cubic_linear_workspace_bytes",
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
     "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
-    "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS",
+    "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS", "cubic_moe_grouped_gemm_a8",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
 ]
 
@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = [
     "cubic_moe_grouped_gemm", "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
     "cubic_gemm_a16_ex", "act_quant_int8_per_token_ex", "cubic_gemm_a8_ex", "cubic_moe_grouped_gemm_ex",
+    "cubic_moe_grouped_gemm_a8",
 ]
 MODE_A16, MODE_A8 = 0, 1          # cubic_linear_mode results
 
@@ -97,6 +98,7 @@ def load_library():
         "cubic_gemm_a8_ex": (i32, [vp, vp, i64, wp, vp, i32, vp]),
         "cubic_moe_grouped_gemm_ex": (i32, [vp, i32, i64, vp, i32, wp, i32, vp, i32, vp, sz, vp]),
         "cubic_moe_grouped_gemm_static": (i32, [vp, i64, vp, i32, wp, i32, vp, vp]),
+        "cubic_moe_grouped_gemm_a8": (i32, [vp, vp, i64, vp, i32, wp, i32, vp, i32, vp, sz, vp]),
         "cubic_moe_mlp_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
         "cubic_moe_mlp": (i32, [vp, i64, vp, vp, i32, wp, wp, i32, vp, vp, sz, vp]),
     }
@@ -361,6 +363,30 @@ def cubic_moe_grouped_gemm(x: torch.Tensor, topk_ids: torch.Tensor, experts: Cub
         st = lib.cubic_moe_grouped_gemm_ex(_ptr(x), xd, T, _ptr(topk_ids), topk, ctypes.byref(cw), E, _ptr(out),
                                            yd, _ptr(workspace), workspace.numel(), _stream(x))
     _check(st, "cubic_moe_grouped_gemm")
+    return out
+
+
+def cubic_moe_grouped_gemm_a8(xq: torch.Tensor, x_scale: torch.Tensor, topk_ids: torch.Tensor,
+                              experts: CubicWeight, E: int, out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None, out_dtype=torch.float32) -> torch.Tensor:
+    """y[T][topk][N]: each (token, slot) pair's Dynamic A8 product with its expert;
+    xq int8 [T][K] and x_scale fp32 [T] from act_quant_int8_per_token."""
+    _need(xq, torch.int8, "xq")
+    _need(x_scale, torch.float32, "x_scale")
+    _need(topk_ids, torch.int32, "topk_ids")
+    yd = _out_dtype(out_dtype)
+    T, topk = topk_ids.shape
+    cw = experts.c_struct()
+    if out is None:
+        out = torch.empty((T, topk, experts.N), dtype=out_dtype, device=xq.device)
+    elif out.dtype != out_dtype:
+        raise TypeError(f"out: expected {out_dtype}, got {out.dtype}")
+    if workspace is None:
+        workspace = torch.empty(cubic_moe_workspace_bytes(T, topk, E), dtype=torch.uint8, device=xq.device)
+    _check(load_library().cubic_moe_grouped_gemm_a8(_ptr(xq), _ptr(x_scale), T, _ptr(topk_ids), topk,
+                                                    ctypes.byref(cw), E, _ptr(out), yd, _ptr(workspace),
+                                                    workspace.numel(), _stream(xq)),
+           "cubic_moe_grouped_gemm_a8")
     return out
 
 

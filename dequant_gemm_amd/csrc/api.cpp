@@ -473,6 +473,46 @@ CUBIC_API int cubic_moe_grouped_gemm_ex(const void* x, int x_dtype, int64_t T, c
                      static_cast<float*>(y), y_dtype == CUBIC_DTYPE_BF16, workspace, ws_bytes, false, stream);
 }
 
+CUBIC_API int cubic_moe_grouped_gemm_a8(const int8_t* xq, const float* x_scale, int64_t T,
+                                        const int32_t* topk_ids, int topk, const cubic_weight* expert0, int E,
+                                        void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                                        cubic_stream_t stream) {
+  if (!dtype_out_ok(y_dtype)) return CUBIC_ERR_DTYPE;
+  const int st = check_weight(expert0);
+  if (st != CUBIC_OK) return st;
+  if (expert0->group > 1024) return CUBIC_ERR_GROUP;
+  if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
+  if (T == 0 || expert0->N == 0) return CUBIC_OK;
+  if (T * topk > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
+  if (!moe_a8_supported(expert0->K, expert0->bits, expert0->group)) return CUBIC_ERR_SHAPE;
+  if (cubic_code_bytes(expert0->N, expert0->K, expert0->bits) > UINT32_MAX) return CUBIC_ERR_SHAPE;
+  if (!xq || !x_scale || !topk_ids || !y || !workspace) return CUBIC_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(topk_ids) || !aligned16(y) || !aligned16(workspace))
+    return CUBIC_ERR_ALIGN;
+  const MoeLayout L = moe_layout(T, topk, E);
+  if (ws_bytes < L.total) return CUBIC_ERR_WORKSPACE;
+  const bool ybf16 = y_dtype == CUBIC_DTYPE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (expert0->K == 0) return hip_status(launch_fill_zero(static_cast<float*>(y), T * topk * expert0->N, ybf16, s));
+  char* ws = static_cast<char*>(workspace);
+  MoeA8Params p{};
+  p.codes = expert0->codes;
+  p.scales = expert0->scales;
+  p.shapes = expert0->shapes;
+  p.N = expert0->N;
+  p.K = expert0->K;
+  p.group = expert0->group;
+  p.topk = topk;
+  p.code_bytes = static_cast<int64_t>(cubic_code_bytes(expert0->N, expert0->K, expert0->bits));
+  p.xq = xq;
+  p.xs = x_scale;
+  p.y = static_cast<float*>(y);
+  p.ybf16 = ybf16 ? 1 : 0;
+  return hip_status(launch_moe_a8(topk_ids, static_cast<int>(T), E, topk, p,
+                                  reinterpret_cast<int32_t*>(ws + L.hdr), reinterpret_cast<int32_t*>(ws + L.erec),
+                                  reinterpret_cast<int32_t*>(ws + L.sorted), expert0->bits, s));
+}
+
 CUBIC_API size_t cubic_moe_grouped_gemm_static_max_bytes(void) { return moe_scratch_bytes(); }
 
 CUBIC_API int cubic_moe_grouped_gemm_static(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,

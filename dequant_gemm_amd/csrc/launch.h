@@ -49,6 +49,23 @@ struct MoeGemvParams {
   int ybf16;
 };
 
+// Routed experts in the Dynamic A8 mode: int8 activations with per-token scales.
+struct MoeA8Params {
+  const uint8_t* codes;   // expert 0
+  const float* scales;
+  const uint16_t* shapes;
+  int64_t N, K;
+  int group, topk;
+  int64_t code_bytes;     // per expert
+  const int32_t* hdr;
+  const int32_t* erec;
+  const int32_t* sorted;
+  const int8_t* xq;       // [T][K] int8 activations
+  const float* xs;        // [T] per-token scales
+  float* y;               // [T*topk][N] fp32, or bf16 when ybf16
+  int ybf16;
+};
+
 int device_cu_count();   // compute units of the current device (0 if unknown)
 hipError_t launch_pack(const int8_t* codes, uint8_t* packed, int64_t N, int64_t K, int bits,
                        hipStream_t st, unsigned int* range_error);
@@ -82,6 +99,15 @@ hipError_t launch_prefill_a8(const TiledParams& p, int bits, hipStream_t st);
 size_t moe_lds_min_bytes(int64_t K, int bits, int group);
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
                       int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, bool xf16, hipStream_t st);
+// The routing kernel alone: pair ids grouped by expert into hdr / erec / sorted,
+// output rows of invalid pairs cleared.
+hipError_t launch_moe_route(const int32_t* ids, int P, int E, int64_t N, float* y, int ybf16, int32_t* hdr,
+                            int32_t* erec, int32_t* sorted, hipStream_t st);
+bool moe_a8_supported(int64_t K, int bits, int group);
+hipError_t launch_moe_a8(const int32_t* ids, int T, int E, int topk, const MoeA8Params& base, int32_t* hdr,
+                         int32_t* erec, int32_t* sorted, int bits, hipStream_t st);
+// The A8 grouped product over a routing already in p.hdr / p.erec / p.sorted.
+hipError_t launch_moe_a8_product(const MoeA8Params& p, int P, int E, int T, int bits, hipStream_t st);
 // Library-owned routing scratch (one per device): its size, and its device
 // address on the current device (looked up on first use per device).
 size_t moe_scratch_bytes();

@@ -609,12 +609,16 @@ static hipError_t launch_moe_product(const MoeGemvParams& p, int P, int E, int T
               : launch_moe_product_t<false>(p, blocks, T, bits, st);
 }
 
+hipError_t launch_moe_route(const int32_t* ids, int P, int E, int64_t N, float* y, int ybf16, int32_t* hdr,
+                            int32_t* erec, int32_t* sorted, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, N, y, ybf16, hdr, erec, sorted);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
                       int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, bool xf16, hipStream_t st) {
   const int P = T * topk;
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, st, ids, P, E, base.N, base.y, base.ybf16, hdr,
-                     erec, sorted);
-  const hipError_t err = hipGetLastError();
+  const hipError_t err = launch_moe_route(ids, P, E, base.N, base.y, base.ybf16, hdr, erec, sorted, st);
   if (err != hipSuccess) return err;
   MoeGemvParams p = base;
   p.topk = topk;

@@ -263,6 +263,25 @@ int cubic_moe_grouped_gemm_ex(const void* x, int x_dtype, int64_t T,
                               void* y, int y_dtype, void* workspace, size_t ws_bytes,
                               cubic_stream_t stream);
 
+/* Routed-expert products in the Dynamic A8 mode (CubicQuant article, section
+ * "一份 checkpoint，同时服务 A16 与 Dynamic A8": the same checkpoint serves the
+ * integer path; its deployment section switches the routed experts to it). For
+ * every pair (t, j) with e = topk_ids[t][j] in [0, E): y[t][j][:] is the
+ * cubic_gemm_a8 product of row t of xq [T][K] (int8) and x_scale [T] (fp32),
+ * the output of act_quant_int8_per_token, with expert e (same carriers, exact
+ * int32 group dots, fp32(s / 127) per group, x_scale[t] last). Experts lie back
+ * to back as in cubic_moe_grouped_gemm; invalid ids give zero rows and are
+ * counted in the workspace's first int32; the workspace is the one
+ * cubic_moe_workspace_bytes(T, topk, E) sizes. y_dtype CUBIC_DTYPE_F32 or
+ * CUBIC_DTYPE_BF16, layout [T][topk][N]. group must be <= 1024
+ * (CUBIC_ERR_GROUP); K a multiple of 128 whose per-wave activation slice fits
+ * in LDS (CUBIC_ERR_SHAPE otherwise). */
+int cubic_moe_grouped_gemm_a8(const int8_t* xq, const float* x_scale, int64_t T,
+                              const int32_t* topk_ids, int topk,
+                              const cubic_weight* expert0, int E,
+                              void* y, int y_dtype, void* workspace, size_t ws_bytes,
+                              cubic_stream_t stream);
+
 /* cubic_moe_grouped_gemm for callers that cannot allocate device memory: code
  * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.
  * Same arguments, kernels and results (bit for bit) as cubic_moe_grouped_gemm,

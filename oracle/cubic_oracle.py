@@ -60,7 +60,7 @@ __all__ = [
     "kmax", "bits_per_weight", "code_bytes", "storage_bytes",
     "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
     "level_numerators", "levels", "dequant", "gemm_a16",
-    "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16",
+    "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16", "moe_a8",
     "format_levels", "dequant_f32", "encode", "bf16_rne", "silu_mul", "moe_mlp_hidden", "moe_mlp",
     "FIT_CLIP_STEPS", "fit_is_monotone", "fit_shape_candidates", "f64_to_f16_bits", "fit_group_sse", "fit",
 ]
@@ -308,6 +308,29 @@ def moe_a16(x_bf16: np.ndarray, topk_ids: np.ndarray, num_experts: int, N: int,
             if e not in cache:
                 cache[e] = np.asarray(expert_weight(e), dtype=np.float64)
             Y[t, j] = cache[e] @ X[t]
+    return Y
+
+
+def moe_a8(xq: np.ndarray, sx: np.ndarray, topk_ids: np.ndarray, num_experts: int, N: int,
+           expert_codes, bits: int, group: int) -> np.ndarray:
+    """Dynamic A8 on the routed experts: Y[t, j, :] = gemm_a8 of row t of (xq, sx)
+    with expert e = topk_ids[t, j]; ids outside [0, E) give zeros.
+
+    expert_codes(e) -> (codes [N][K], scales [N][K/G], shapes [N][K/G][2] as fp16 bits).
+    """
+    ids = np.asarray(topk_ids)
+    T, topk = ids.shape
+    Y = np.zeros((T, topk, N), dtype=np.float64)
+    cache = {}
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if not 0 <= e < num_experts:
+                continue
+            if e not in cache:
+                cache[e] = expert_codes(e)
+            codes, scales, shapes = cache[e]
+            Y[t, j] = gemm_a8(xq[t:t + 1], sx[t:t + 1], codes, scales, shapes, bits, group)[0]
     return Y
 
 

@@ -201,6 +201,25 @@ def test_dtype_codes_rejected_before_launch():
     assert "type" in lib.cubic_status_string(ERR_DTYPE).decode()
 
 
+def test_moe_a8_validation_before_launch():
+    lib = cq.load_library()
+    p16 = ctypes.c_void_p(16)
+    need = lib.cubic_moe_workspace_bytes(4, 2, 8)
+    w = _w()
+    call = lambda w, T=4, topk=2, yd=0, ws=need, ids=p16: lib.cubic_moe_grouped_gemm_a8(
+        p16, p16, T, ids, topk, ctypes.byref(w), 8, p16, yd, p16, ws, None)
+    assert call(w, yd=2) == -9                       # fp16 output: unsupported type
+    assert call(_w(group=2048, K=4096)) == ERR_GROUP
+    assert call(w, ws=need - 1) == ERR_WS
+    assert call(w, topk=0) == ERR_SHAPE
+    assert call(w, T=-1) == ERR_SHAPE
+    assert call(w, T=0) == OK                         # no-op
+    assert call(w, ids=None) == ERR_NULL
+    assert call(_w(bits=9)) == ERR_BITS
+    assert lib.cubic_moe_grouped_gemm_a8(ctypes.c_void_p(8), p16, 4, p16, 2, ctypes.byref(w), 8, p16, 0, p16,
+                                         need, None) == ERR_ALIGN
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports the oracle; the library is the only compute."""
     pkg = os.path.join(ROOT, "dequant_gemm_amd")

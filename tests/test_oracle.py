@@ -902,3 +902,39 @@ def test_fit_reproduces_w4g128_nrmse_table(name):
     assert cubic < fp4 <= int4
     # the stored losses are the squared errors of the dequantised weights
     np.testing.assert_allclose(loss.sum(), (err ** 2).sum(), rtol=1e-6)
+
+
+def test_moe_a8_pairs_written_out():
+    """oracle.moe_a8 (Dynamic A8 on the routed experts): every pair equals its
+    token's A8 product with its expert, written out with rationals from the
+    carrier table (pinned above) and the definition: x_scale * sum over groups of
+    (s / 127) * sum xq * carrier; invalid ids give zero rows."""
+    rng = np.random.default_rng(91)
+    bits, G, N, K, E, T = 3, 128, 3, 256, 3, 2
+    codes = rng.integers(-4, 4, size=(E, N, K)).astype(np.int8)
+    scales = rng.uniform(0.01, 0.1, size=(E, N, K // G)).astype(np.float32)
+    ab = np.array([[1.0, 0.0], [2.0, -1.75], [0.5, 0.25]])
+    shp = np.zeros((E, N, K // G, 2), dtype=np.uint16)
+    for e in range(E):
+        pick = ab[(np.arange(N * (K // G)) + e) % 3].reshape(N, K // G, 2)
+        shp[e] = pick.astype(np.float16).view(np.uint16)
+    xq = rng.integers(-127, 128, size=(T, K)).astype(np.int8)
+    sx = np.array([0.0123, 0.5], dtype=np.float32)
+    ids = np.array([[0, 2], [1, 7]])
+    Y = oracle.moe_a8(xq, sx, ids, E, N, lambda e: (codes[e], scales[e], shp[e]), bits, G)
+    assert not Y[1, 1].any()
+    for t in range(T):
+        for j in range(2):
+            e = ids[t, j]
+            if e >= E:
+                continue
+            for n in range(N):
+                tot = F(0)
+                for g in range(K // G):
+                    a, b = oracle.f16_bits_to_f64(shp[e, n, g])
+                    tab = oracle.carrier_table(np.array([a]), np.array([b]), bits)[0]
+                    dot = sum(int(xq[t, k]) * (1 if codes[e, n, k] >= 0 else -1) * int(tab[abs(int(codes[e, n, k]))])
+                              for k in range(g * G, (g + 1) * G))
+                    tot += F(float(scales[e, n, g])) / 127 * dot
+                want = F(float(sx[t])) * tot
+                assert abs(F(float(Y[t, j, n])) - want) <= abs(want) * F(1, 2 ** 45) + F(1, 2 ** 80)
