@@ -26,6 +26,7 @@ __all__ = [
     "cubic_linear", "MODE_A16", "MODE_A8", "cubic_moe_workspace_bytes", "cubic_moe_grouped_gemm",
     "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp", "EXPORTED_SYMBOLS", "cubic_moe_grouped_gemm_a8",
+    "cubic_moe_mlp_a8_workspace_bytes", "cubic_moe_mlp_a8",
     "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
 ]
 
@@ -38,7 +39,7 @@ EXPORTED_SYMBOLS = [
     "cubic_moe_grouped_gemm", "cubic_moe_grouped_gemm_static_max_bytes", "cubic_moe_grouped_gemm_static",
     "cubic_moe_mlp_workspace_bytes", "cubic_moe_mlp",
     "cubic_gemm_a16_ex", "act_quant_int8_per_token_ex", "cubic_gemm_a8_ex", "cubic_moe_grouped_gemm_ex",
-    "cubic_moe_grouped_gemm_a8",
+    "cubic_moe_grouped_gemm_a8", "cubic_moe_mlp_a8_workspace_bytes", "cubic_moe_mlp_a8",
 ]
 MODE_A16, MODE_A8 = 0, 1          # cubic_linear_mode results
 
@@ -101,6 +102,8 @@ def load_library():
         "cubic_moe_grouped_gemm_a8": (i32, [vp, vp, i64, vp, i32, wp, i32, vp, i32, vp, sz, vp]),
         "cubic_moe_mlp_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
         "cubic_moe_mlp": (i32, [vp, i64, vp, vp, i32, wp, wp, i32, vp, vp, sz, vp]),
+        "cubic_moe_mlp_a8_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
+        "cubic_moe_mlp_a8": (i32, [vp, i64, vp, vp, i32, wp, wp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -431,4 +434,29 @@ def cubic_moe_mlp(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.T
     _check(load_library().cubic_moe_mlp(_ptr(x), T, _ptr(topk_ids), _ptr(topk_weights), topk,
                                         ctypes.byref(gu), ctypes.byref(dn), E, _ptr(out), _ptr(workspace),
                                         workspace.numel(), _stream(x)), "cubic_moe_mlp")
+    return out
+
+
+def cubic_moe_mlp_a8_workspace_bytes(T: int, topk: int, E: int, H: int, I: int) -> int:
+    return int(load_library().cubic_moe_mlp_a8_workspace_bytes(T, topk, E, H, I))
+
+
+def cubic_moe_mlp_a8(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                     gate_up: CubicWeight, down: CubicWeight, E: int, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """cubic_moe_mlp in the Dynamic A8 mode: the token rows and the intermediate h
+    rows are quantised per row to int8 before their grouped products."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_weights, torch.float32, "topk_weights")
+    T, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((T, down.N), dtype=torch.float32, device=x.device)
+    need = cubic_moe_mlp_a8_workspace_bytes(T, topk, E, gate_up.K, down.K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    gu, dn = gate_up.c_struct(), down.c_struct()
+    _check(load_library().cubic_moe_mlp_a8(_ptr(x), T, _ptr(topk_ids), _ptr(topk_weights), topk,
+                                           ctypes.byref(gu), ctypes.byref(dn), E, _ptr(out), _ptr(workspace),
+                                           workspace.numel(), _stream(x)), "cubic_moe_mlp_a8")
     return out

@@ -407,6 +407,85 @@ CUBIC_API int cubic_moe_mlp(const uint16_t* x_bf16, int64_t T, const int32_t* to
   return hip_status(e);
 }
 
+namespace {
+struct MlpA8Layout {
+  MoeLayout route;
+  size_t xq, xs, y1, h, hq, hs, y2, total;
+};
+MlpA8Layout mlp_a8_layout(int64_t T, int topk, int E, int64_t H, int64_t I) {
+  MlpA8Layout L;
+  L.route = moe_layout(T, topk, E);
+  const size_t P = static_cast<size_t>(T) * topk;
+  size_t o = L.route.total;
+  L.xq = o;  o += align256(static_cast<size_t>(T) * H);
+  L.xs = o;  o += align256(static_cast<size_t>(T) * 4);
+  L.y1 = o;  o += align256(P * static_cast<size_t>(2 * I) * 4);
+  L.h = o;   o += align256(P * static_cast<size_t>(I) * 2);
+  L.hq = o;  o += align256(P * static_cast<size_t>(I));
+  L.hs = o;  o += align256(P * 4);
+  L.y2 = o;  o += align256(P * static_cast<size_t>(H) * 4);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+CUBIC_API size_t cubic_moe_mlp_a8_workspace_bytes(int64_t T, int topk, int E, int64_t H, int64_t I) {
+  if (T < 0 || topk <= 0 || E <= 0 || H < 0 || I < 0) return 0;
+  return mlp_a8_layout(T, topk, E, H, I).total;
+}
+
+CUBIC_API int cubic_moe_mlp_a8(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                               const float* topk_weights, int topk, const cubic_weight* gate_up0,
+                               const cubic_weight* down0, int E, float* y, void* workspace, size_t ws_bytes,
+                               cubic_stream_t stream) {
+  int st = check_weight(gate_up0);
+  if (st != CUBIC_OK) return st;
+  st = check_weight(down0);
+  if (st != CUBIC_OK) return st;
+  if (gate_up0->group > 1024 || down0->group > 1024) return CUBIC_ERR_GROUP;
+  if (T < 0 || topk <= 0 || E <= 0) return CUBIC_ERR_SHAPE;
+  const int64_t H = gate_up0->K, I = down0->K;
+  if (gate_up0->N != 2 * I || down0->N != H || H == 0 || I == 0) return CUBIC_ERR_SHAPE;
+  if (T == 0) return CUBIC_OK;
+  if (T * topk > INT32_MAX / 2) return CUBIC_ERR_SHAPE;
+  for (const cubic_weight* w : {gate_up0, down0})
+    if (!moe_a8_supported(w->K, w->bits, w->group) || cubic_code_bytes(w->N, w->K, w->bits) > UINT32_MAX)
+      return CUBIC_ERR_SHAPE;
+  if (!x_bf16 || !topk_ids || !topk_weights || !y || !workspace) return CUBIC_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(topk_ids) || !aligned16(topk_weights) || !aligned16(y) ||
+      !aligned16(workspace))
+    return CUBIC_ERR_ALIGN;
+  const MlpA8Layout L = mlp_a8_layout(T, topk, E, H, I);
+  if (ws_bytes < L.total) return CUBIC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  auto params = [&](const cubic_weight* w) {
+    MoeA8Params p{};
+    p.codes = w->codes;
+    p.scales = w->scales;
+    p.shapes = w->shapes;
+    p.N = w->N;
+    p.K = w->K;
+    p.group = w->group;
+    p.topk = topk;
+    p.code_bytes = static_cast<int64_t>(cubic_code_bytes(w->N, w->K, w->bits));
+    return p;
+  };
+  MoeMlpA8Buffers b;
+  b.xq = reinterpret_cast<int8_t*>(ws + L.xq);
+  b.xs = reinterpret_cast<float*>(ws + L.xs);
+  b.y1 = reinterpret_cast<float*>(ws + L.y1);
+  b.h = reinterpret_cast<uint16_t*>(ws + L.h);
+  b.hq = reinterpret_cast<int8_t*>(ws + L.hq);
+  b.hs = reinterpret_cast<float*>(ws + L.hs);
+  b.y2 = reinterpret_cast<float*>(ws + L.y2);
+  const hipError_t e = launch_moe_mlp_a8(
+      x_bf16, topk_ids, topk_weights, static_cast<int>(T), E, topk, params(gate_up0), gate_up0->bits,
+      params(down0), down0->bits, reinterpret_cast<int32_t*>(ws + L.route.hdr),
+      reinterpret_cast<int32_t*>(ws + L.route.erec), reinterpret_cast<int32_t*>(ws + L.route.sorted), b, y,
+      static_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
 CUBIC_API size_t cubic_moe_workspace_bytes(int64_t T, int topk, int E) {
   if (T < 0 || topk <= 0 || E <= 0) return 0;
   return moe_layout(T, topk, E).total;

@@ -108,6 +108,24 @@ hipError_t launch_moe_a8(const int32_t* ids, int T, int E, int topk, const MoeA8
                          int32_t* erec, int32_t* sorted, int bits, hipStream_t st);
 // The A8 grouped product over a routing already in p.hdr / p.erec / p.sorted.
 hipError_t launch_moe_a8_product(const MoeA8Params& p, int P, int E, int T, int bits, hipStream_t st);
+// The MLP step's elementwise kernels: h = bf16(SiLU(gate) * up) from the gate_up
+// outputs y1 [P][2I], and the router-weighted sum of the pair outputs y2 [P][H].
+hipError_t launch_moe_act(const float* y1, int64_t P, int64_t I, uint16_t* h, hipStream_t st);
+hipError_t launch_moe_combine(const float* y2, const int32_t* ids, const float* topk_w, int64_t T, int topk,
+                              int E, int64_t H, float* out, hipStream_t st);
+// The MLP step in the Dynamic A8 mode: the token rows (x bf16 [T][H]) and the
+// intermediate rows h are each quantised per row before their grouped product.
+struct MoeMlpA8Buffers {
+  int8_t* xq; float* xs;       // [T][H], [T]
+  float* y1;                   // [P][2I]
+  uint16_t* h;                 // [P][I] bf16
+  int8_t* hq; float* hs;       // [P][I], [P]
+  float* y2;                   // [P][H]
+};
+hipError_t launch_moe_mlp_a8(const uint16_t* x, const int32_t* ids, const float* topk_w, int T, int E, int topk,
+                             const MoeA8Params& up, int up_bits, const MoeA8Params& dn, int dn_bits,
+                             int32_t* hdr, int32_t* erec, int32_t* sorted, const MoeMlpA8Buffers& b, float* out,
+                             hipStream_t st);
 // Library-owned routing scratch (one per device): its size, and its device
 // address on the current device (looked up on first use per device).
 size_t moe_scratch_bytes();

@@ -692,6 +692,18 @@ static unsigned elementwise_grid(int64_t nvec) {
   return static_cast<unsigned>(b < 8192 ? (b > 0 ? b : 1) : 8192);
 }
 
+hipError_t launch_moe_act(const float* y1, int64_t P, int64_t I, uint16_t* h, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_act, dim3(elementwise_grid(P * I / 4)), dim3(256), 0, st, y1, P, I, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const float* y2, const int32_t* ids, const float* topk_w, int64_t T, int topk,
+                              int E, int64_t H, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_moe_combine, dim3(elementwise_grid(T * H / 4)), dim3(256), 0, st, y2, ids, topk_w, T,
+                     topk, E, H, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E, int topk,
                           const MoeGemvParams& up, int up_bits, const MoeGemvParams& dn, int dn_bits,
                           int32_t* hdr, int32_t* erec, int32_t* sorted, uint16_t* h, float* out,
@@ -700,9 +712,7 @@ hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E,
   const int64_t I = dn.K, H = dn.N;
   hipError_t err = launch_moe(ids, T, E, topk, up, hdr, erec, sorted, up_bits, false, st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_act, dim3(elementwise_grid(P * I / 4)), dim3(256), 0, st, up.y,
-                     static_cast<int64_t>(P), I, h);
-  err = hipGetLastError();
+  err = launch_moe_act(up.y, P, I, h, st);
   if (err != hipSuccess) return err;
   MoeGemvParams p = dn;
   p.topk = 1;                                  // one activation row per pair
@@ -710,9 +720,7 @@ hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E,
   p.hdr = hdr; p.erec = erec; p.sorted = sorted;
   err = launch_moe_product(p, P, E, T, dn_bits, false, st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_combine, dim3(elementwise_grid(static_cast<int64_t>(T) * H / 4)), dim3(256), 0,
-                     st, dn.y, ids, topk_w, static_cast<int64_t>(T), topk, E, H, out);
-  return hipGetLastError();
+  return launch_moe_combine(dn.y, ids, topk_w, T, topk, E, H, out, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -493,4 +493,29 @@ hipError_t launch_moe_a8(const int32_t* ids, int T, int E, int topk, const MoeA8
   return launch_moe_a8_product(p, P, E, T, bits, st);
 }
 
+hipError_t launch_moe_mlp_a8(const uint16_t* x, const int32_t* ids, const float* topk_w, int T, int E, int topk,
+                             const MoeA8Params& up, int up_bits, const MoeA8Params& dn, int dn_bits,
+                             int32_t* hdr, int32_t* erec, int32_t* sorted, const MoeMlpA8Buffers& b, float* out,
+                             hipStream_t st) {
+  const int P = T * topk;
+  const int64_t H = up.K, I = dn.K;
+  hipError_t err = launch_act_quant(x, false, T, H, b.xq, b.xs, st);
+  if (err != hipSuccess) return err;
+  MoeA8Params pu = up;
+  pu.xq = b.xq; pu.xs = b.xs; pu.y = b.y1; pu.ybf16 = 0;
+  err = launch_moe_a8(ids, T, E, topk, pu, hdr, erec, sorted, up_bits, st);
+  if (err != hipSuccess) return err;
+  err = launch_moe_act(b.y1, P, I, b.h, st);
+  if (err != hipSuccess) return err;
+  err = launch_act_quant(b.h, false, P, I, b.hq, b.hs, st);
+  if (err != hipSuccess) return err;
+  MoeA8Params pd = dn;
+  pd.topk = 1;                                 // one activation row per pair
+  pd.xq = b.hq; pd.xs = b.hs; pd.y = b.y2; pd.ybf16 = 0;
+  pd.hdr = hdr; pd.erec = erec; pd.sorted = sorted;
+  err = launch_moe_a8_product(pd, P, E, T, dn_bits, st);
+  if (err != hipSuccess) return err;
+  return launch_moe_combine(b.y2, ids, topk_w, T, topk, E, dn.N, out, st);
+}
+
 }  // namespace cubic

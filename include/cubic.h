@@ -326,6 +326,29 @@ int cubic_moe_mlp(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
                   const cubic_weight* down0, int E, float* y, void* workspace, size_t ws_bytes,
                   cubic_stream_t stream);
 
+/* The routed-expert MLP step in the Dynamic A8 mode (CubicQuant article,
+ * section "一份 checkpoint，同时服务 A16 与 Dynamic A8": one checkpoint serves
+ * both modes; its deployment section switches the routed experts to A8). As
+ * cubic_moe_mlp, with both grouped products on int8 activations:
+ *   (xq, sx) = act_quant_int8_per_token(x)     per token, [T][H]
+ *   [g | u]  = cubic_moe_grouped_gemm_a8 of (xq, sx) with gate_up (fp32)
+ *   h        = bf16(SiLU(g) * u)
+ *   (hq, hs) = act_quant_int8_per_token(h)     per pair, [T*topk][I]
+ *   o_tj     = cubic_moe_grouped_gemm_a8 of (hq, hs) with down (fp32)
+ *   y[t]     = sum_j topk_weights[t][j] * o_tj  (fp32, slots in order)
+ * Same argument layout and validation as cubic_moe_mlp, plus the grouped A8
+ * product's limits (group <= 1024: CUBIC_ERR_GROUP). The workspace
+ * (cubic_moe_mlp_a8_workspace_bytes) holds, each part starting at the next
+ * multiple of 256 bytes: the routing part (cubic_moe_workspace_bytes(T, topk,
+ * E) bytes), xq [T][H] int8, sx [T] fp32, the gate_up outputs [T*topk][2I]
+ * fp32, h [T*topk][I] bf16, hq [T*topk][I] int8, hs [T*topk] fp32 and the down
+ * outputs [T*topk][H] fp32; they stay there after the call. */
+size_t cubic_moe_mlp_a8_workspace_bytes(int64_t T, int topk, int E, int64_t H, int64_t I);
+int cubic_moe_mlp_a8(const uint16_t* x_bf16, int64_t T, const int32_t* topk_ids,
+                     const float* topk_weights, int topk, const cubic_weight* gate_up0,
+                     const cubic_weight* down0, int E, float* y, void* workspace, size_t ws_bytes,
+                     cubic_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,7 +61,7 @@ __all__ = [
     "pack", "unpack", "f16_bits_to_f64", "bf16_bits_to_f64",
     "level_numerators", "levels", "dequant", "gemm_a16",
     "act_quant", "carrier_table", "carrier_codes", "gemm_a8", "moe_a16", "moe_a8",
-    "format_levels", "dequant_f32", "encode", "bf16_rne", "silu_mul", "moe_mlp_hidden", "moe_mlp",
+    "format_levels", "dequant_f32", "encode", "bf16_rne", "silu_mul", "moe_mlp_hidden", "moe_mlp", "moe_mlp_a8",
     "FIT_CLIP_STEPS", "fit_is_monotone", "fit_shape_candidates", "f64_to_f16_bits", "fit_group_sse", "fit",
 ]
 
@@ -688,3 +688,45 @@ def moe_mlp(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, num_ex
             h = bf16_rne(g / (1.0 + np.exp(-g)) * u)
             Y[t] += float(topk_w[t, j]) * (D @ h)
     return Y
+
+
+def _bf16_bits_of(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that are bf16 numbers already (exact)."""
+    return (np.asarray(h, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def moe_mlp_a8(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, num_experts: int,
+               gate_up_codes, down_codes, up_bits: int, up_group: int, dn_bits: int, dn_group: int):
+    """The MLP step with both products in the Dynamic A8 mode (float64 apart from
+    the steps the mode fixes). Per token t: (xq, sx) = act_quant(x[t]); per pair
+    (t, j), e = ids[t, j] in [0, E): [g | u] = gemm_a8(xq, sx, GU_e);
+    h = bf16(SiLU(g) * u); (hq, hs) = act_quant(h); o = gemm_a8(hq, hs, D_e);
+    y[t] += w[t, j] * o. gate_up_codes(e) / down_codes(e) -> (codes, scales, shapes).
+    Returns (y [T][H], v [T][topk][I], h [T][topk][I]); v and h are zero for
+    invalid ids."""
+    ids = np.asarray(topk_ids)
+    T, topk = ids.shape
+    xq, sx = act_quant(x_bf16)
+    y = np.zeros((T, np.asarray(x_bf16).shape[1]))     # H = K of gate_up = N of down
+    v_all = h_all = None
+    cache = {}
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if not 0 <= e < num_experts:
+                continue
+            if e not in cache:
+                cache[e] = (gate_up_codes(e), down_codes(e))
+            (gc, gs, gsh), (dc, ds, dsh) = cache[e]
+            gu = gemm_a8(xq[t:t + 1], sx[t:t + 1], gc, gs, gsh, up_bits, up_group)[0]
+            I = gu.shape[0] // 2
+            v = silu_mul(gu[:I], gu[I:])
+            h = bf16_rne(v)
+            hq, hs = act_quant(_bf16_bits_of(h)[None, :])
+            o = gemm_a8(hq, hs, dc, ds, dsh, dn_bits, dn_group)[0]
+            if v_all is None:
+                v_all = np.zeros((T, topk, I))
+                h_all = np.zeros((T, topk, I))
+            v_all[t, j], h_all[t, j] = v, h
+            y[t] += float(topk_w[t, j]) * o
+    return y, v_all, h_all

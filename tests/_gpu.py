@@ -60,6 +60,13 @@ def pack_fields(codes: np.ndarray, bits: int) -> np.ndarray:
     tests plant codes outside [-Kmax, Kmax]; checked against oracle.pack and
     oracle.unpack in the CPU tests."""
     codes = np.asarray(codes)
+    if bits in (2, 4, 8):                           # whole fields per byte: shift and add
+        per = 8 // bits
+        u = (codes.astype(np.int64) & ((1 << bits) - 1)).reshape(-1, per)
+        out = np.zeros(u.shape[0], dtype=np.int64)
+        for i in range(per):
+            out |= u[:, i] << (bits * i)
+        return out.astype(np.uint8).reshape(codes.shape[0], -1)
     u = (codes.astype(np.int64) & ((1 << bits) - 1)).reshape(-1)
     pos0 = np.arange(u.size, dtype=np.int64) * bits
     out = np.zeros(u.size * bits // 8, dtype=np.int64)

@@ -220,6 +220,23 @@ def test_moe_a8_validation_before_launch():
                                          need, None) == ERR_ALIGN
 
 
+def test_moe_mlp_a8_validation_and_workspace():
+    lib = cq.load_library()
+    p16 = ctypes.c_void_p(16)
+    T, topk, E, H, I = 3, 2, 4, 256, 128
+    need = lib.cubic_moe_mlp_a8_workspace_bytes(T, topk, E, H, I)
+    up = lambda n: -(-n // 256) * 256
+    P = T * topk
+    assert need == (lib.cubic_moe_workspace_bytes(T, topk, E) + up(T * H) + up(T * 4) + up(P * 2 * I * 4)
+                    + up(P * I * 2) + up(P * I) + up(P * 4) + up(P * H * 4))
+    gu, dn = _w(N=2 * I, K=H), _w(N=H, K=I)
+    call = lambda gu, dn, ws=need: lib.cubic_moe_mlp_a8(p16, T, p16, p16, topk, ctypes.byref(gu), ctypes.byref(dn),
+                                                        E, p16, p16, ws, None)
+    assert call(gu, dn, ws=need - 1) == ERR_WS
+    assert call(gu, _w(N=H + 1, K=I)) == ERR_SHAPE
+    assert call(_w(N=2 * I, K=2048, group=2048), _w(N=2048, K=I)) == ERR_GROUP
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports the oracle; the library is the only compute."""
     pkg = os.path.join(ROOT, "dequant_gemm_amd")

@@ -148,3 +148,96 @@ def test_carrier_ties_and_clamps():
     y = _run(xq, sx, ids, pool, E).cpu().numpy()
     ref = _ref(xq, sx, ids, E, N, host, bits, group)
     assert row_rel_err(y.reshape(T * topk, N), ref.reshape(T * topk, N)) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# The MLP step in the A8 mode (cubic_moe_mlp_a8)
+# ---------------------------------------------------------------------------
+TOL_MLP = 5e-3
+
+
+def _hidden_of(ws, T, topk, E, H, I):
+    """Device h [T][topk][I] from the A8 MLP workspace: routing part, xq [T][H],
+    sx [T], gate_up outputs [P][2I] fp32, then h [P][I] bf16 (256-byte aligned)."""
+    P = T * topk
+    up = lambda n: -(-n // 256) * 256
+    off = cq.cubic_moe_workspace_bytes(T, topk, E) + up(T * H) + up(T * 4) + up(P * 2 * I * 4)
+    hb = ws[off:off + P * I * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    return oracle.bf16_bits_to_f64(hb).reshape(T, topk, I)
+
+
+def _check_hidden_a8(h_dev, v, h_ref, xq, sx, ids_np, up_codes, E, bits, group):
+    """h_dev equals the oracle's h, or lies between bf16(v - dv) and bf16(v + dv):
+    dv bounds the device's error in v. The group dots are exact integers on both
+    sides; the device rounds fp32(s / 127), each group's scaled sum, the sum of the
+    four waves' partials and the token scale: fewer than n = K/G + 8 roundings of
+    2^-23 (any rounding mode) of mag = sx * sum_g |s / 127| |I_g|; SiLU and the
+    product in fp32 add 2^-20 |v|."""
+    T, topk, I = h_ref.shape
+    flips = 0
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids_np[t, j])
+            if not 0 <= e < E:
+                continue
+            codes, scales, shapes = up_codes(e)
+            C = oracle.carrier_codes(codes, shapes, bits, group).astype(np.float64)
+            N, K = C.shape
+            Ig = (C.reshape(N, K // group, group) * xq[t].astype(np.float64).reshape(1, K // group, group)).sum(2)
+            mag = float(sx[t]) * (np.abs(Ig) * (scales.astype(np.float64) / 127.0)).sum(1)
+            g = float(sx[t]) * (Ig * (scales.astype(np.float64) / 127.0)).sum(1)
+            n = K // group + 8
+            gamma = n * 2.0 ** -23 / (1 - n * 2.0 ** -23)
+            gg, uu = g[:I], g[I:]
+            sig = 1.0 / (1.0 + np.exp(-gg))
+            dsilu = np.abs(sig * (1.0 + gg * (1.0 - sig)))
+            dv = dsilu * np.abs(uu) * gamma * mag[:I] + np.abs(gg * sig) * gamma * mag[I:] + 2.0 ** -20 * np.abs(v[t, j])
+            same = h_dev[t, j] == h_ref[t, j]
+            lo, hi = oracle.bf16_rne(v[t, j] - dv), oracle.bf16_rne(v[t, j] + dv)
+            ok = same | ((h_dev[t, j] >= lo) & (h_dev[t, j] <= hi))
+            bad = np.nonzero(~ok)[0]
+            assert ok.all(), (t, j, [(int(i), v[t, j, i], h_ref[t, j, i], h_dev[t, j, i], dv[i]) for i in bad[:4]])
+            flips += int((~same).sum())
+    return flips
+
+
+def _mlp_case(E, T, topk, H, I, bits, group, seed, mod_ids=None):
+    gu, gu_host = _pool(E, 2 * I, H, bits, group, seed=seed)
+    dn, dn_host = _pool(E, H, I, bits, group, seed=seed + 1)
+    x, ids = synth.moe_routing(seed=seed + 2, T=T, E=E, topk=topk, K=H)
+    if mod_ids is not None:
+        mod_ids(ids)
+    w = torch.softmax(torch.rand((T, topk), generator=torch.Generator().manual_seed(seed + 3)), dim=1)
+    ws = torch.empty(cq.cubic_moe_mlp_a8_workspace_bytes(T, topk, E, H, I), dtype=torch.uint8, device=DEV)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), w.to(DEV)
+    y = cq.cubic_moe_mlp_a8(xd, idd, wd, gu, dn, E, workspace=ws)
+    h_dev = _hidden_of(ws, T, topk, E, H, I)
+    assert torch.equal(y, cq.cubic_moe_mlp_a8(xd, idd, wd, gu, dn, E))
+    ids_np = ids.numpy()
+    up_codes = lambda e: tuple(a[e] for a in gu_host)
+    dn_codes = lambda e: tuple(a[e] for a in dn_host)
+    ref, v, h_ref = oracle.moe_mlp_a8(x_bits(x), ids_np, w.numpy(), E, up_codes, dn_codes, bits, group,
+                                      bits, group)
+    xq, sx = oracle.act_quant(x_bits(x))
+    flips = _check_hidden_a8(h_dev, v, h_ref, xq, sx, ids_np, up_codes, E, bits, group)
+    assert flips <= 0.002 * h_ref.size, flips
+    assert row_rel_err(y.cpu().numpy(), ref) <= TOL_MLP
+
+
+@pytest.mark.parametrize("bits,group", [(2, 256), (3, 128), (4, 128)])
+def test_mlp_a8_step(bits, group):
+    """gate_up and down in A8, h checked element by element, invalid ids add nothing."""
+    say(f"MoE MLP A8 step bits={bits} G={group}")
+
+    def bad(ids):
+        ids[3, 1] = -1
+        ids[5, 0] = 6
+
+    _mlp_case(6, 20, 2, 1024, 512, bits, group, seed=150 + bits, mod_ids=bad)
+
+
+def test_mlp_a8_k3_dims_one_token():
+    """Kimi K3 expert dims (hidden 7168, intermediate 3072), W2 G512, one token
+    over 16 experts: the decode shape of the A8 step."""
+    say("MoE MLP A8 K3 dims, one token top-16 of 16")
+    _mlp_case(16, 1, 16, 7168, 3072, 2, 512, seed=160)

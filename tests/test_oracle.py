@@ -938,3 +938,89 @@ def test_moe_a8_pairs_written_out():
                     tot += F(float(scales[e, n, g])) / 127 * dot
                 want = F(float(sx[t])) * tot
                 assert abs(F(float(Y[t, j, n])) - want) <= abs(want) * F(1, 2 ** 45) + F(1, 2 ** 80)
+
+
+def _rn_bf16(x):
+    """Nearest bf16 value of a rational (ties to even), 8 significant bits."""
+    if x == 0:
+        return F(0)
+    sgn, m, e = (-1 if x < 0 else 1), abs(x), 0
+    while m >= 2:
+        m /= 2
+        e += 1
+    while m < 1:
+        m *= 2
+        e -= 1
+    return sgn * F(ex.rne_int(m * 128)) * F(2) ** (e - 7)
+
+
+def _a8_row(xq_row, sx, codes, scales, shapes, bits, G):
+    """One output row set of the A8 product, exactly: sx * sum_g (s / 127) * int dot."""
+    N, K = codes.shape
+    out = []
+    for n in range(N):
+        tot = F(0)
+        for g in range(K // G):
+            a, b = ex.f16_value(int(shapes[n, g, 0])), ex.f16_value(int(shapes[n, g, 1]))
+            km = oracle.kmax(bits)
+            dot = 0
+            for k in range(g * G, (g + 1) * G):
+                c = int(codes[n, k])
+                j = abs(c)
+                Q = a * j * km * km + b * j * j * km + (1 - a - b) * j ** 3
+                car = 0 if j == 0 else max(-127, min(127, ex.rne_int(127 * Q / km ** 3)))
+                dot += int(xq_row[k]) * (car if c >= 0 else -car)
+            tot += F(float(scales[n, g])) / 127 * dot
+        out.append(sx * tot)
+    return out
+
+
+def _quant_row(vals):
+    amax = max(abs(v) for v in vals)
+    s = ex.rn32(amax / 127)
+    q = [0 if s == 0 else max(-127, min(127, ex.rne_int(ex.rn32(v / s)))) for v in vals]
+    return q, s
+
+
+def test_moe_mlp_a8_written_out():
+    """oracle.moe_mlp_a8 against the step restated with rationals: per-token int8
+    rows, carriers from the cubic's exact integer numerator, exact group dots,
+    SiLU in float64 (math.exp), h rounded to bf16 by hand, h quantised per pair,
+    the down product, router-weighted sums; invalid ids add nothing."""
+    import math
+    rng = np.random.default_rng(93)
+    bits, G, H, I, E, T, topk = 3, 128, 256, 128, 2, 2, 2
+    gu_c = rng.integers(-4, 4, size=(E, 2 * I, H)).astype(np.int8)
+    dn_c = rng.integers(-4, 4, size=(E, H, I)).astype(np.int8)
+    gu_s = rng.uniform(0.002, 0.02, size=(E, 2 * I, H // G)).astype(np.float32)
+    dn_s = rng.uniform(0.002, 0.02, size=(E, H, I // G)).astype(np.float32)
+    sh = np.array([[1.0, 0.0], [2.0, -1.75], [0.5, 0.25]]).astype(np.float16).view(np.uint16)
+    gu_sh = sh[rng.integers(0, 3, size=(E, 2 * I, H // G))]
+    dn_sh = sh[rng.integers(0, 3, size=(E, H, I // G))]
+    x = (rng.standard_normal((T, H)) * 3).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([[0, 1], [1, 5]])
+    w = np.array([[0.25, 0.75], [0.5, 0.5]], dtype=np.float32)
+    y, v, h = oracle.moe_mlp_a8(xb, ids, w, E, lambda e: (gu_c[e], gu_s[e], gu_sh[e]),
+                                lambda e: (dn_c[e], dn_s[e], dn_sh[e]), bits, G, bits, G)
+    assert not h[1, 1].any()
+    for t in range(T):
+        xq, sx = _quant_row([ex.bf16_value(int(b)) for b in xb[t]])
+        want = [F(0)] * H
+        for j in range(topk):
+            e = int(ids[t, j])
+            if e >= E:
+                continue
+            gu = _a8_row(xq, sx, gu_c[e], gu_s[e], gu_sh[e], bits, G)
+            hh = []
+            for i in range(I):
+                g, u = float(gu[i]), float(gu[I + i])
+                vv = g / (1.0 + math.exp(-g)) * u
+                assert abs(vv - v[t, j, i]) <= 1e-12 * abs(vv) + 1e-300
+                hh.append(_rn_bf16(F(vv)))
+            assert [float(q) for q in hh] == list(h[t, j])
+            hq, hs = _quant_row(hh)
+            o = _a8_row(hq, hs, dn_c[e], dn_s[e], dn_sh[e], bits, G)
+            want = [a + F(float(w[t, j])) * b for a, b in zip(want, o)]
+        for n in range(H):
+            assert abs(F(float(y[t, n])) - want[n]) <= abs(want[n]) * F(1, 2 ** 40) + F(1, 2 ** 60), (t, n)
