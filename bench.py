@@ -503,6 +503,16 @@ def decode_step_block(cq, synth, dev):
                         "avg_launch_us": round(ms * 1e3, 2),
                         "timing": "HIP events around graph replays of 40 launches over 8 disjoint "
                                   "expert sets"}}
+    # the same step in the Dynamic A8 mode: the token's int8 row (quantised once,
+    # outside the timed launches) against the same 16-expert sets
+    xq, sx = cq.act_quant_int8_per_token(x)
+    ms8 = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm_a8(xq, sx, i, pool, E, out=y, workspace=ws))
+                       for i in ids], 5, dev)
+    nb8 = topk * (N * H * bits // 8 + 8 * N * (H // group)) + H + 4 + topk * N * 4
+    g8 = nb8 / ms8 / 1e6
+    res["a8"] = {"GB/s": round(g8, 1), "us": round(ms8 * 1e3, 2), "bytes_per_launch": nb8,
+                 "kernel": "cubic_moe_grouped_gemm_a8 call: k_moe_route + k_moe_a8<2>",
+                 "frac_of_hbm_peak": round(g8 / HBM_PEAK_GBS, 4)}
     print(json.dumps({"decode_step_16x": res}), file=sys.stderr, flush=True)
     del codes, scales, shapes, pool
     torch.cuda.empty_cache()
@@ -698,7 +708,19 @@ def moe_workloads(cq, synth, dev):
     nb = topk * (gu_b + dn_b) + H * 2 + H * 4
     res["moe_mlp_decode_1tok_top16"] = row(ms, nb, bytes_per_launch=nb)
     _report(res, "moe_mlp_decode_1tok_top16")
-    del gu, dn, ws, wsm, y
+    xq, sx = cq.act_quant_int8_per_token(x)
+    ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm_a8(xq, sx, i, gu, E, out=y, workspace=ws))
+                      for i in ids], 5, dev)
+    nb = topk * gu_b + H + 4 + topk * 2 * I * 4
+    res["moe_a8_decode_1tok_top16"] = row(ms, nb, bytes_per_launch=nb)
+    _report(res, "moe_a8_decode_1tok_top16")
+    wsa = torch.empty(cq.cubic_moe_mlp_a8_workspace_bytes(1, topk, E, H, I), dtype=torch.uint8, device=dev)
+    ms = _graph_time([(lambda i=i: cq.cubic_moe_mlp_a8(x, i, tw, gu, dn, E, out=ym, workspace=wsa))
+                      for i in ids], 5, dev)
+    nb = topk * (gu_b + dn_b) + H * 2 + H * 4
+    res["moe_mlp_a8_decode_1tok_top16"] = row(ms, nb, bytes_per_launch=nb)
+    _report(res, "moe_mlp_a8_decode_1tok_top16")
+    del gu, dn, ws, wsm, wsa, y
     torch.cuda.empty_cache()
     E, T = 896, 64
     gu, dn = pool(E, 4, 2 * I, H), pool(E, 6, H, I)
@@ -711,6 +733,11 @@ def moe_workloads(cq, synth, dev):
     nb = touched * gu_b + T * H * 2 + T * topk * 2 * I * 4
     res["moe_896x64tok_top16"] = row(ms, nb, touched_experts=touched)
     _report(res, "moe_896x64tok_top16")
+    xq, sx = cq.act_quant_int8_per_token(x)
+    ms = _graph_time([lambda: cq.cubic_moe_grouped_gemm_a8(xq, sx, tid, gu, E, out=y, workspace=ws)], 3, dev)
+    nb = touched * gu_b + T * (H + 4) + T * topk * 2 * I * 4
+    res["moe_a8_896x64tok_top16"] = row(ms, nb, touched_experts=touched)
+    _report(res, "moe_a8_896x64tok_top16")
     del ws, y
     wsm = torch.empty(cq.cubic_moe_mlp_workspace_bytes(T, topk, E, H, I), dtype=torch.uint8, device=dev)
     ym = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -718,7 +745,12 @@ def moe_workloads(cq, synth, dev):
     nb = touched * (gu_b + dn_b) + T * H * 2 + T * H * 4
     res["moe_mlp_896x64tok_top16"] = row(ms, nb, touched_experts=touched)
     _report(res, "moe_mlp_896x64tok_top16")
-    del gu, dn, wsm, ym
+    del wsm
+    wsa = torch.empty(cq.cubic_moe_mlp_a8_workspace_bytes(T, topk, E, H, I), dtype=torch.uint8, device=dev)
+    ms = _graph_time([lambda: cq.cubic_moe_mlp_a8(x, tid, tw, gu, dn, E, out=ym, workspace=wsa)], 3, dev)
+    res["moe_mlp_a8_896x64tok_top16"] = row(ms, nb, touched_experts=touched)
+    _report(res, "moe_mlp_a8_896x64tok_top16")
+    del gu, dn, wsa, ym
     torch.cuda.empty_cache()
     return res
 
