@@ -1,5 +1,5 @@
 // skinny.hip -- A16 product for small batches (17 <= M <= 64; smaller M runs on
-// the GEMV) with 2-, 3- and 4-bit codes.
+// the GEMV) with 2- to 8-bit codes.
 //
 // The CubicQuant article (section "压缩权重必须边解码、边计算") decodes each
 // weight tile inside the kernel that consumes it and scales group partial sums
@@ -46,23 +46,44 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* p, uint32_
 constexpr int sk_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
 // Per-wave LDS ring stage: activations [32 MB rows][64 k] fp16 (16-byte chunk
-// q of row r at chunk q ^ (r & 7)), then the code words (lane l's 16 bytes:
-// row l / 2, half l % 2; 2-bit codes: dword d of lane l at 256 d + 4 l), then the group parameters of the step after it (64
-// scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
-// Ring depth: what the LDS holds with W waves of one or two 32-row blocks.
-template <int W, int MB> constexpr int sk_stages() { return W == 8 ? (MB == 2 ? 2 : 3) : (MB == 2 ? 4 : 6); }
+// q of row r at chunk q ^ (r & 7)), then the code words, then the group
+// parameters of the step after it (64 scales, 64 (a, b) words; lanes 32..63
+// repeat rows 0..31). Code words of lane l (row l / 2, half l % 2): 2-bit codes,
+// dword d at 256 d + 4 l; 3- and 4-bit codes, 16 l; wider codes, dwords 0..3 at
+// 16 l and the rest at 1024 + 4 l (5-bit), 1024 + 4 l and 1280 + 4 l (6-bit) or
+// 1024 + 16 l (7- and 8-bit).
+template <int B> constexpr size_t sk_code_bytes() {
+  return B <= 4 ? 1024 : (B == 5 ? 1280 : (B == 6 ? 1536 : 2048));
+}
 template <int MB> constexpr size_t sk_x_bytes() { return static_cast<size_t>(32 * MB) * SK_K * 2; }
-template <int MB> constexpr size_t sk_stage_bytes() { return sk_x_bytes<MB>() + 1024 + 512; }
-template <int B> constexpr size_t sk_tab_bytes() { return static_cast<size_t>(SK_ROWS) * (1 << B) * 2; }
+template <int B, int MB> constexpr size_t sk_stage_bytes() { return sk_x_bytes<MB>() + sk_code_bytes<B>() + 512; }
+// 7- and 8-bit codes compute each level (no table); narrower codes look levels
+// up in a per-row table of 2^B fp16 entries.
+template <int B> constexpr bool sk_direct() { return B >= 7; }
+template <int B> constexpr size_t sk_tab_bytes() {
+  return sk_direct<B>() ? 0 : static_cast<size_t>(SK_ROWS) * (1 << B) * 2;
+}
+// Ring depth: the most stages (up to 6) that W waves fit in one compute unit's LDS.
+template <int B, int W, int MB> constexpr int sk_stages() {
+  int n = 6;
+  while (n > 2 && W * (n * sk_stage_bytes<B, MB>() + sk_tab_bytes<B>()) > 160 * 1024) --n;
+  return n;
+}
 template <int B, int MB, int W>
 constexpr size_t sk_lds_bytes() {
-  return W * (sk_stages<W, MB>() * sk_stage_bytes<MB>() + sk_tab_bytes<B>());
+  return W * (sk_stages<B, W, MB>() * sk_stage_bytes<B, MB>() + sk_tab_bytes<B>());
+}
+// Waves per workgroup: two per SIMD where the LDS allows a ring of two stages,
+// else one.
+template <int B, int MB> constexpr int sk_waves() {
+  return 8 * (2 * sk_stage_bytes<B, MB>() + sk_tab_bytes<B>()) <= 160 * 1024 ? 8 : 4;
 }
 
 // Normalised level q of field value v (two's complement, B bits) in fp32: with
-// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^10), a X and b Y are
-// exact products of fp16 values, so Q = j^3 + a X + b Y rounds twice in fp32
-// and once more by 1/K^3 (a few fp32 ulps; one fp16 rounding follows).
+// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers), Q = j^3 + a X + b Y is
+// evaluated with two fmas and scaled by 1/K^3: a few fp32 ulps (for up to 4-bit
+// codes a X and b Y are exact, X and Y being below 2^10), far below the fp16
+// rounding of the table entry that follows.
 template <int B>
 __device__ __forceinline__ float sk_level(float a, float b, int v) {
   constexpr int km = kmax_of(B);
@@ -78,13 +99,13 @@ __device__ __forceinline__ float sk_level(float a, float b, int v) {
 template <int B, int MB, int SK_WAVES>
 __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
   extern __shared__ __align__(1024) unsigned char smem[];   // row tables rely on this alignment
-  static_assert(B >= 2 && B <= 4, "code slots of at most 16 bytes per lane and step");
-  constexpr int NST = sk_stages<SK_WAVES, MB>();
-  constexpr size_t kStage = sk_stage_bytes<MB>();
+  static_assert(B >= 2 && B <= 8, "2- to 8-bit codes");
+  constexpr int NST = sk_stages<B, SK_WAVES, MB>();
+  constexpr size_t kStage = sk_stage_bytes<B, MB>();
   constexpr size_t kCodeOff = sk_x_bytes<MB>();
-  constexpr size_t kParamOff = kCodeOff + 1024;
+  constexpr size_t kParamOff = kCodeOff + sk_code_bytes<B>();
   constexpr int NX = 4 * MB;                     // activation loads per step (1 KB each)
-  constexpr int NC = B == 2 ? 2 : 1;             // code loads per step
+  constexpr int NC = B == 2 ? 2 : (B <= 4 ? 1 : (B == 6 ? 3 : 2));   // code loads per step
   constexpr int NV = NX + NC + 2;                // + codes + scales + (a, b)
   static_assert(NST * NV < 64, "vmcnt holds at most 63");
 
@@ -137,10 +158,25 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * d, 4,
                                                  coff + static_cast<uint32_t>(sv) * (8 * B) + 4 * d, 0, 0,
                                                  0);
-    } else {
+    } else if constexpr (B == 3) {
       // 12-byte loads land at a 16-byte lane stride
       __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 12,
                                                coff + static_cast<uint32_t>(sv) * (8 * B), 0, 0, 0);
+    } else {
+      // dwords 0..3, then the rest (4-byte loads at a 4-byte lane stride, or one
+      // 12- or 16-byte load at a 16-byte stride)
+      const uint32_t o = coff + static_cast<uint32_t>(sv) * (8 * B);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff, 16, o, 0, 0, 0);
+      if constexpr (B == 5 || B == 6) {
+#pragma unroll
+        for (int d = 4; d < B; ++d)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 1024 + 256 * (d - 4), 4, o + 4 * d, 0,
+                                                   0, 0);
+      } else if constexpr (B == 7) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 1024, 12, o + 16, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 1024, 16, o + 16, 0, 0, 0);
+      }
     }
     int g = (sv + 1) * SK_K / p.group;         // the group of the step after sv
     g = g < gpr ? g : gpr - 1;
@@ -164,15 +200,24 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
   // rows c and c + 64 / TE share LDS banks; XOR-ing 2 (c / (64 / TE)) into the
   // entry index moves them apart, and the 32 rows of a half wave reading the
   // same field value hit 32 different banks.
-  const int tswz = 2 * (c / (64 / TE));
+  const int tswz = sk_direct<B>() ? 0 : 2 * (c / (TE >= 64 ? 1 : 64 / TE));
   float inv_rs = 1.0f, rs = 1.0f;               // 2^-e and 2^e of the row (set below)
+  // 7- and 8-bit codes: the level of |k| = t Kmax is t (a' + t (b' + t c')) with
+  // the group's s 2^-e folded into a', b', c' (Horner form in fp32)
+  float ha = 0.0f, hb = 0.0f, hc = 0.0f;
   auto build = [&](int buf, uint32_t sbits, uint32_t ab) {
-    uint16_t* t = tab_wave + (buf * SK_ROWS + c) * TE;   // buf is 0 (one table per row)
     const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
     const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
     const float sk = __uint_as_float(sbits) * inv_rs;    // exact (power of two)
+    if constexpr (sk_direct<B>()) {
+      ha = sk * a;
+      hb = sk * b;
+      hc = sk * ((1.0f - a) - b);
+    } else {
+      uint16_t* t = tab_wave + (buf * SK_ROWS + c) * TE;   // buf is 0 (one table per row)
 #pragma unroll
-    for (int v = h; v < TE; v += 2) t[v ^ tswz] = f16_bits(sk * sk_level<B>(a, b, v));
+      for (int v = h; v < TE; v += 2) t[v ^ tswz] = f16_bits(sk * sk_level<B>(a, b, v));
+    }
   };
 
   // ---- prologue: steps sb .. sb + NST - 2 in flight first, then the row
@@ -227,10 +272,22 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff) + (2 * c + h);
       w[0] = src[0];
       w[1] = src[64];
-    } else {
+    } else if constexpr (B <= 4) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff) + 4 * (2 * c + h);
 #pragma unroll
       for (int d = 0; d < B; ++d) w[d] = src[d];
+    } else {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + kCodeOff + 16 * (2 * c + h));
+      w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+      if constexpr (B == 5 || B == 6) {
+#pragma unroll
+        for (int d = 4; d < B; ++d)
+          w[d] = reinterpret_cast<const uint32_t*>(st + kCodeOff + 1024 + 256 * (d - 4))[2 * c + h];
+      } else {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(st + kCodeOff + 1024) + 4 * (2 * c + h);
+#pragma unroll
+        for (int d = 4; d < B; ++d) w[d] = src[d - 4];
+      }
     }
     f16x8 fa[4][MB];
 #pragma unroll
@@ -250,10 +307,39 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
       psb = par[c];
       pab = par[64 + c];
     }
-    // weight fragments: codes 8 kb .. 8 kb + 7 of the lane's 32, via the row table
+    // weight fragments: codes 8 kb .. 8 kb + 7 of the lane's 32, via the row
+    // table (up to 6-bit codes) or computed per code (7- and 8-bit)
+    u32x4 fb[4];
+    if constexpr (sk_direct<B>()) {
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      constexpr float kInv = 1.0f / static_cast<float>(kmax_of(B));
+      auto level = [&](int i) {
+        const int bit = i * B;
+        const int d = bit >> 5, off = bit & 31;
+        int v;
+        if (off + B <= 32) {
+          v = __builtin_amdgcn_sbfe(w[d], off, B);
+        } else {
+          v = __builtin_amdgcn_sbfe(__builtin_amdgcn_alignbit(w[d + 1], w[d], off), 0, B);
+        }
+        const float kf = static_cast<float>(v);
+        const float t = fabsf(kf) * kInv;
+        return copysignf(t * fmaf(t, fmaf(t, hc, hb), ha), kf);
+      };
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        uint32_t r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f2 lv = {level(8 * kb + 2 * q), level(8 * kb + 2 * q + 1)};
+          r[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lv, h2));
+        }
+        fb[kb] = u32x4{r[0], r[1], r[2], r[3]};
+      }
+    } else {
     const uint32_t tkey = static_cast<uint32_t>(tswz << 1) | static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>(tab_wave + c * TE));
-    u32x4 fb[4];
     {
       typedef __attribute__((address_space(3))) const uint16_t lds_u16;
       typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
@@ -283,6 +369,7 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
         }
         fb[kb] = u32x4{r[0], r[1], r[2], r[3]};
       }
+    }
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -325,7 +412,7 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
 }  // namespace
 
 bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
-  if (bits < 2 || bits > 4) return false;
+  if (bits < 2 || bits > 8) return false;
   if (M < 1 || M > 64 || K % SK_K != 0 || K / SK_K < 8) return false;   // a step per wave
   if (group % SK_K != 0) return false;
   if (64 * K * 2 >= (int64_t{1} << 32)) return false;   // activation offsets of 64 rows
@@ -334,8 +421,9 @@ bool skinny_supported(int64_t M, int64_t N, int64_t K, int bits, int group) {
   return (N + SK_ROWS - 1) / SK_ROWS <= INT32_MAX;
 }
 
-template <int B, int MB, int W>
+template <int B, int MB>
 static hipError_t launch_skinny_k(const TiledParams& p, hipStream_t st) {
+  constexpr int W = sk_waves<B, MB>();
   auto kern = k_skinny<B, MB, W>;
   constexpr size_t lds = sk_lds_bytes<B, MB, W>();
   static_assert(lds <= 160 * 1024, "one compute unit's LDS");
@@ -348,14 +436,21 @@ static hipError_t launch_skinny_k(const TiledParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-constexpr int kSkWaves = 8;                     // two waves per SIMD (measured faster than four per workgroup)
+template <int B>
+static hipError_t launch_skinny_b(const TiledParams& p, hipStream_t st) {
+  return p.M <= 32 ? launch_skinny_k<B, 1>(p, st) : launch_skinny_k<B, 2>(p, st);
+}
 
 hipError_t launch_skinny_a16(const TiledParams& p, int bits, hipStream_t st) {
-  if (bits == 2)
-    return p.M <= 32 ? launch_skinny_k<2, 1, kSkWaves>(p, st) : launch_skinny_k<2, 2, kSkWaves>(p, st);
-  if (bits == 3)
-    return p.M <= 32 ? launch_skinny_k<3, 1, kSkWaves>(p, st) : launch_skinny_k<3, 2, kSkWaves>(p, st);
-  return p.M <= 32 ? launch_skinny_k<4, 1, kSkWaves>(p, st) : launch_skinny_k<4, 2, kSkWaves>(p, st);
+  switch (bits) {
+    case 2: return launch_skinny_b<2>(p, st);
+    case 3: return launch_skinny_b<3>(p, st);
+    case 4: return launch_skinny_b<4>(p, st);
+    case 5: return launch_skinny_b<5>(p, st);
+    case 6: return launch_skinny_b<6>(p, st);
+    case 7: return launch_skinny_b<7>(p, st);
+    default: return launch_skinny_b<8>(p, st);
+  }
 }
 
 }  // namespace cubic

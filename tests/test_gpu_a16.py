@@ -72,6 +72,45 @@ def test_small_shapes_ragged(bits, group, M):
     _check(w, x)
 
 
+@pytest.mark.parametrize("bits,group", [(5, 128), (6, 256), (7, 128), (8, 128), (8, 1024)])
+@pytest.mark.parametrize("M", [17, 32, 33, 64])
+def test_small_batch_wide_codes(bits, group, M):
+    # 5- to 8-bit codes at 17..64 rows (the small-batch kernel: level tables up to
+    # 6 bits, levels computed per code for 7 and 8 bits; one or two 32-row blocks);
+    # N not a multiple of the 32-row tile, K over several groups and waves
+    say(f"A16 small batch wide codes bits={bits} G={group} M={M}")
+    g = synth.make_generator(1500 + 10 * bits + M)
+    w = synth.make_weight(g, 203, 4096, bits, group, "uniform", 0.02)
+    x = synth.activations(g, M, 4096, 0.01, 50.0)
+    _check(w, x)
+
+
+def test_small_batch_wide_codes_full_shape():
+    for bits in (5, 8):
+        for M in (24, 64):
+            say(f"A16 small batch W{bits} G128 gate_up 6144x7168 M={M}")
+            g = synth.make_generator(1600 + bits + M, DEV)
+            w = synth.make_weight(g, 6144, 7168, bits, 128, "uniform", 0.02, DEV)
+            x = synth.activations(g, M, 7168, 0.01, 50.0, DEV)
+            rows = np.unique(np.r_[0:3, M - 1, np.random.default_rng(M).integers(0, M, 4)])
+            _check_rows_cols(w, x, rows)
+
+
+def _check_rows_cols(w, x, rows, cols=None):
+    """Sampled outputs of a large product: rows `rows` against the oracle on
+    weight rows `cols` (default: the first and last 256 and 64 spread rows)."""
+    cw = upload(w)
+    y = cq.cubic_gemm_a16(x.to(DEV), cw).cpu().numpy()
+    N = w.N
+    if cols is None:
+        cols = np.unique(np.r_[0:256, N - 256:N, np.random.default_rng(7).integers(0, N, 64)])
+    codes, scales, shapes = np_weight(w)
+    W = oracle.dequant(codes[cols], scales[cols], shapes[cols], w.bits, w.group)
+    ref = oracle.gemm_a16(x_bits(x)[rows], W)
+    err = row_rel_err(y[rows][:, cols], ref)
+    assert err <= TOL, err
+
+
 def test_extra_negative_code_w2_w4_w8():
     # codes -2^(B-1) decode by the formula (t > 1); W2 exercises the slow path,
     # W8 the levels computed per code
