@@ -249,6 +249,25 @@ __device__ __forceinline__ int carrier_level(double a, double b, int j, int km) 
   return static_cast<int>(n);
 }
 
+// carrier_level for fp16 a and b, decided in fp32 where that is safe: with
+// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^20), y = 127 (j^3 + a X +
+// b Y) / K^3 takes two fmas and one multiply. For |a|, |b| <= 16 and K <= 127 the
+// terms stay below 2^25, so y is within 2e-4 of 127 q_j; when y lies within 1e-3
+// of a half-integer (a possible tie or a rounding the estimate could get wrong),
+// or a or b is outside that range, the exact integer rule decides.
+__device__ __forceinline__ int carrier_fast(float a, float b, int j, int km) {
+  const float j3 = static_cast<float>(j * j * j);
+  const float X = static_cast<float>(j * km * km) - j3;
+  const float Y = static_cast<float>(j * j * km) - j3;
+  const float y = fmaf(a, X, fmaf(b, Y, j3)) * (127.0f / static_cast<float>(km * km * km));
+  const float r = rintf(y);
+  const bool near_tie = fabsf(fabsf(y - r) - 0.5f) < 1e-3f;
+  if (near_tie || !(fabsf(a) <= 16.0f && fabsf(b) <= 16.0f))
+    return carrier_level(static_cast<double>(a), static_cast<double>(b), j, km);
+  const int n = static_cast<int>(r);
+  return n > 127 ? 127 : (n < -127 ? -127 : n);
+}
+
 // Power-of-two prescale of a row before its fp16 conversion: returns the shift
 // n such that ldexpf(amax, n) lies in [2^14, 2^15), and writes 2^-n to *back.
 // Zero, NaN and Inf rows are left unscaled (n = 0).

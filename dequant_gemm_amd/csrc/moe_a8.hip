@@ -29,7 +29,7 @@
 //    never overlap, then v_perm (4-bit: two of them and a bit select) looks
 //    them up. Natural order.
 //  - 5- to 8-bit codes: a table of the row's 2^B carriers in LDS, rebuilt at
-//    each group, one byte read per code. Natural order.
+//    each group (carrier_fast), one byte read per code. Natural order.
 // The per-row carrier registers and the group scale are computed once per
 // workgroup, each lane of a row taking every fourth group of the wave's range,
 // and read from LDS at each group boundary.
@@ -148,12 +148,12 @@ __device__ __forceinline__ void decode_lds(const uint32_t* w, const int8_t* tab_
 template <int B>
 __device__ __forceinline__ void build_lds_table(int8_t* tab_row, int kb, uint32_t ab) {
   constexpr int km = kmax_of(B);
-  const double a = f16_bits_to_f64(static_cast<uint16_t>(ab & 0xffffu));
-  const double b = f16_bits_to_f64(static_cast<uint16_t>(ab >> 16));
+  const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+  const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
   for (int f = kb; f < (1 << B); f += 4) {
     const int k = sign_extend(static_cast<uint32_t>(f), B);
     const int j = k < 0 ? -k : k;
-    const int c = j == 0 ? 0 : (j == km ? 127 : carrier_level(a, b, j, km));
+    const int c = j == 0 ? 0 : (j == km ? 127 : carrier_fast(a, b, j, km));
     tab_row[f] = static_cast<int8_t>(k < 0 ? -c : c);
   }
 }

@@ -3,9 +3,10 @@
 // The CubicQuant article (section "压缩权重必须边解码、边计算") describes a 2-D
 // dense kernel that decodes a weight tile inside the tile and consumes it at
 // once. Here a 256-thread workgroup computes a 128 x 128 output tile; per K step
-// of 64 codes every thread decodes one 32-code chunk of one weight row through a
-// per-(row, group) level table in LDS into an fp16 (A16) or INT8-carrier (A8) tile
-// in LDS, next to the activation tile, and four waves run 32x32 MFMAs on it.
+// of 64 codes every thread decodes one 32-code chunk of one weight row (through
+// a per-(row, group) table in LDS for up to 6-bit codes, computed per code for 7
+// and 8 bits) into an fp16 (A16) or INT8-carrier (A8) tile in LDS, next to the
+// activation tile, and four waves run 32x32 MFMAs on it.
 //  - A16: levels are fp16(s * q) (group scale folded in), activations fp16 after
 //    the per-row power-of-two prescale of k_xprep; fp32 accumulation.
 //  - A8: INT8 carrier clamp(rne(127 q)) (CubicQuant article, A16/A8 section),
@@ -31,9 +32,14 @@ __global__ __launch_bounds__(256) void k_tiled_a16(TiledParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Bs = As + TBM * A16_LDS_STRIDE;
-  uint16_t* tab = Bs + TBN * A16_LDS_STRIDE;               // [TBN][2^B]
+  uint16_t* tab = Bs + TBN * A16_LDS_STRIDE;               // [TBN][2^B] (table widths)
   constexpr int NT = 1 << BITS;
   constexpr int km = kmax_of(BITS);
+  // 7- and 8-bit codes compute each level s q(|k| / Kmax) in fp32 (Horner form,
+  // the scale folded into the coefficients); narrower codes build a per-(row,
+  // group) table of fp16(s q) in fp32.
+  constexpr bool kDirect = BITS >= 7;
+  float ha = 0.0f, hb = 0.0f, hc = 0.0f;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -81,18 +87,19 @@ __global__ __launch_bounds__(256) void k_tiled_a16(TiledParams p) {
     }
     __syncthreads();                                   // previous MFMAs done with LDS
     if (newg) {
-      const double a = f16_bits_to_f64(static_cast<uint16_t>(ab & 0xffffu));
-      const double b = f16_bits_to_f64(static_cast<uint16_t>(ab >> 16));
-      const double K3 = static_cast<double>(km) * km * km;
-      for (int v = h * (NT / 2); v < (h + 1) * (NT / 2); ++v) {
-        const int k = sign_extend(static_cast<uint32_t>(v), BITS);
-        const int j = k < 0 ? -k : k;
-        const float wv = static_cast<float>(static_cast<double>(s) *
-                                            (level_numerator(a, b, j, km) / K3));
-        tab[r * NT + v] = f16_bits(k < 0 ? -wv : wv);
+      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+      if constexpr (kDirect) {
+        ha = s * a;
+        hb = s * b;
+        hc = s * ((1.0f - a) - b);
+      } else {
+#pragma unroll 4
+        for (int v = h * (NT / 2); v < (h + 1) * (NT / 2); ++v)
+          tab[r * NT + v] = f16_bits(s * table_level_f32(a, b, static_cast<uint32_t>(v), BITS));
       }
       gcur = g;
-      __syncthreads();
+      if constexpr (!kDirect) __syncthreads();
     }
     // A tile
 #pragma unroll
@@ -100,12 +107,28 @@ __global__ __launch_bounds__(256) void k_tiled_a16(TiledParams p) {
       *reinterpret_cast<u32x4*>(As + r * A16_LDS_STRIDE + h * 32 + q * 8) = av[q];
     // B tile: decode 32 codes
     {
-      const uint16_t* t = tab + r * NT;
       uint32_t o[16];
+      if constexpr (kDirect) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        constexpr float kInv = 1.0f / static_cast<float>(km);
+        auto level = [&](int i) {
+          const int kf = sign_extend(chunk_field<BITS>(w, i), BITS);
+          const float t = static_cast<float>(kf < 0 ? -kf : kf) * kInv;
+          return copysignf(t * fmaf(t, fmaf(t, hc, hb), ha), static_cast<float>(kf));
+        };
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        o[i] = static_cast<uint32_t>(t[chunk_field<BITS>(w, 2 * i)]) |
-               (static_cast<uint32_t>(t[chunk_field<BITS>(w, 2 * i + 1)]) << 16);
+        for (int i = 0; i < 16; ++i) {
+          const f2 lv = {level(2 * i), level(2 * i + 1)};
+          o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lv, h2));
+        }
+      } else {
+        const uint16_t* t = tab + r * NT;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          o[i] = static_cast<uint32_t>(t[chunk_field<BITS>(w, 2 * i)]) |
+                 (static_cast<uint32_t>(t[chunk_field<BITS>(w, 2 * i + 1)]) << 16);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x4*>(Bs + r * A16_LDS_STRIDE + h * 32 + q * 8) =
@@ -152,12 +175,16 @@ __global__ __launch_bounds__(256) void k_tiled_a16(TiledParams p) {
 template <int BITS>
 __global__ __launch_bounds__(256) void k_tiled_a8(TiledParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int8_t* As = reinterpret_cast<int8_t*>(smem);
-  int8_t* Bs = As + TBM * A8_LDS_STRIDE;
-  int8_t* tab = Bs + TBN * A8_LDS_STRIDE;                   // [TBN][2^B]
-  float* scs = reinterpret_cast<float*>(tab + TBN * (1 << BITS));   // [TBN]
+  // 7- and 8-bit codes compute each carrier (carrier_fast); narrower codes build
+  // a per-(row, group) table of the 2^B carriers.
+  constexpr bool kDirect = BITS >= 7;
   constexpr int NT = 1 << BITS;
   constexpr int km = kmax_of(BITS);
+  int8_t* As = reinterpret_cast<int8_t*>(smem);
+  int8_t* Bs = As + TBM * A8_LDS_STRIDE;
+  int8_t* tab = Bs + TBN * A8_LDS_STRIDE;                   // [TBN][2^B] (table widths)
+  float* scs = reinterpret_cast<float*>(tab + (kDirect ? 0 : TBN * NT));   // [TBN]
+  float ga = 0.0f, gb = 0.0f;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -208,13 +235,18 @@ __global__ __launch_bounds__(256) void k_tiled_a8(TiledParams p) {
     }
     __syncthreads();
     if (newg) {
-      const double a = f16_bits_to_f64(static_cast<uint16_t>(ab & 0xffffu));
-      const double b = f16_bits_to_f64(static_cast<uint16_t>(ab >> 16));
-      for (int v = h * (NT / 2); v < (h + 1) * (NT / 2); ++v) {
-        const int k = sign_extend(static_cast<uint32_t>(v), BITS);
-        const int j = k < 0 ? -k : k;
-        const int cv = carrier_level(a, b, j, km);
-        tab[r * NT + v] = static_cast<int8_t>(k < 0 ? -cv : cv);
+      const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab & 0xffffu)));
+      const float b = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ab >> 16)));
+      if constexpr (kDirect) {
+        ga = a;
+        gb = b;
+      } else {
+        for (int v = h * (NT / 2); v < (h + 1) * (NT / 2); ++v) {
+          const int k = sign_extend(static_cast<uint32_t>(v), BITS);
+          const int j = k < 0 ? -k : k;
+          const int cv = j == 0 ? 0 : (j == km ? 127 : carrier_fast(a, b, j, km));
+          tab[r * NT + v] = static_cast<int8_t>(k < 0 ? -cv : cv);
+        }
       }
       if (h == 0) scs[r] = __fdiv_rn(s, 127.0f);
       __syncthreads();
@@ -231,9 +263,18 @@ __global__ __launch_bounds__(256) void k_tiled_a8(TiledParams p) {
       for (int i = 0; i < 8; ++i) {
         uint32_t v = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v |= (static_cast<uint32_t>(static_cast<uint8_t>(t[chunk_field<BITS>(w, 4 * i + e)])))
-               << (8 * e);
+        for (int e = 0; e < 4; ++e) {
+          int cv;
+          if constexpr (kDirect) {
+            const int k = sign_extend(chunk_field<BITS>(w, 4 * i + e), BITS);
+            const int j = k < 0 ? -k : k;
+            const int c = j == 0 ? 0 : (j == km ? 127 : carrier_fast(ga, gb, j, km));
+            cv = k < 0 ? -c : c;
+          } else {
+            cv = t[chunk_field<BITS>(w, 4 * i + e)];
+          }
+          v |= (static_cast<uint32_t>(cv) & 0xffu) << (8 * e);
+        }
         o[i] = v;
       }
 #pragma unroll
@@ -289,7 +330,7 @@ __global__ __launch_bounds__(256) void k_tiled_a8(TiledParams p) {
 
 template <int B>
 static hipError_t launch_a16_b(const TiledParams& p, hipStream_t st) {
-  const size_t lds = (TBM + TBN) * A16_LDS_STRIDE * 2 + TBN * (1 << B) * 2;
+  const size_t lds = (TBM + TBN) * A16_LDS_STRIDE * 2 + (B >= 7 ? 0 : TBN * (1 << B) * 2);
   auto kern = k_tiled_a16<B>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -304,7 +345,7 @@ static hipError_t launch_a16_b(const TiledParams& p, hipStream_t st) {
 
 template <int B>
 static hipError_t launch_a8_b(const TiledParams& p, hipStream_t st) {
-  const size_t lds = (TBM + TBN) * A8_LDS_STRIDE + TBN * (1 << B) + TBN * 4;
+  const size_t lds = (TBM + TBN) * A8_LDS_STRIDE + (B >= 7 ? 0 : TBN * (1 << B)) + TBN * 4;
   dim3 grid(static_cast<unsigned>((p.N + TBN - 1) / TBN), static_cast<unsigned>((p.M + TBM - 1) / TBM));
   hipLaunchKernelGGL(k_tiled_a8<B>, grid, dim3(256), lds, st, p);
   return hipGetLastError();

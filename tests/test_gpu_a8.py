@@ -147,3 +147,42 @@ def test_a8_carrier_ties_both_directions():
         xq_ref, sx_ref = oracle.act_quant(x_bits(x))
         ref = oracle.gemm_a8(xq_ref, sx_ref, cn, scales.numpy(), shapes.numpy().view(np.uint16), 3, G)
         assert row_rel_err(y, ref) <= 1e-5
+
+
+# fp16 shapes on which a carrier is an exact tie (127 q_j = n + 1/2), found by an
+# exact rational search: (a, b) for 3-, 5-, 7- and 8-bit codes
+TIE_SHAPES = {3: [(2.0, -1.75)], 5: [(1.900390625, 3.97265625)], 7: [(0.57421875, 3.953125)],
+              8: [(1.955078125, 3.26171875), (2.802734375, -1.05859375)]}
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_a8_carriers_exact_through_identity_rows(bits):
+    """Every carrier the device uses, read back exactly: xq = the K x K identity
+    (x_scale 1) gives y[k][n] = fp32(s / 127) * C(n, k), so C is recovered by one
+    division and must equal the oracle's carrier (exact integer rounding, ties to
+    even, clamps, the extra code -2^(B-1)) for every weight. Rows carry planted
+    tie shapes; codes cover every field value."""
+    say(f"A8 carriers exact via identity rows bits={bits}")
+    N, K, G = 48, 256, 128
+    rng = np.random.default_rng(4000 + bits)
+    lo = -(1 << (bits - 1))
+    codes = rng.integers(lo, -lo, size=(N, K)).astype(np.int8)
+    sg = synth.make_generator(4100 + bits)
+    scales = synth.lognormal_scales(sg, N * (K // G), 0.02).reshape(N, K // G)
+    shapes = synth.sample_shapes(sg, N * (K // G)).reshape(N, K // G, 2).numpy().view(np.uint16).copy()
+    for i, (a, b) in enumerate(TIE_SHAPES.get(bits, [])):
+        shapes[4 * i:4 * i + 4, :, 0] = np.float16(a).view(np.uint16)
+        shapes[4 * i:4 * i + 4, :, 1] = np.float16(b).view(np.uint16)
+    from tests._gpu import pack_fields
+    cw = cq.CubicWeight(torch.from_numpy(pack_fields(codes, bits).reshape(-1)).to(DEV), scales.to(DEV),
+                        torch.from_numpy(shapes.view(np.int16)).to(DEV), N, K, bits, G)
+    xq = torch.eye(K, dtype=torch.int8, device=DEV)
+    sx = torch.ones(K, dtype=torch.float32, device=DEV)
+    y = cq.cubic_gemm_a8(xq, sx, cw).cpu().numpy().astype(np.float64)      # [K][N]
+    sc = (scales.numpy() / np.float32(127.0)).astype(np.float32).astype(np.float64)   # fp32(s / 127)
+    unit = np.repeat(sc, G, axis=1).T                                       # [K][N]
+    C = y / unit
+    Ci = np.rint(C)
+    assert np.abs(C - Ci).max() < 1e-3
+    want = oracle.carrier_codes(codes, shapes, bits, G).T
+    assert np.array_equal(Ci.astype(np.int64), want)
