@@ -54,9 +54,14 @@ def parse():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 20 plain device copies of MIB MiB (HBM counter calibration)")
-    ap.add_argument("--counter-run", choices=("gate_up", "down"), default=None,
-                    help="only launch this product --steps times, eagerly on rotating copies "
-                         "(for rocprofv3 --pmc passes)")
+    ap.add_argument("--counter-run", choices=("gate_up", "down", "prefill_a16", "prefill_a8", "decode_step",
+                                              "decode_step_a8", "skinny_w4_m64"), default=None,
+                    help="only launch this product --steps times, eagerly (the GEMVs on rotating "
+                         "copies; for rocprofv3 --pmc passes)")
+    ap.add_argument("--leg", choices=("prefill", "decode_step", "moe", "smallm"), default=None,
+                    help="only run one workload block (prefill A16/A8, the 16-expert decode step, the "
+                         "routed-expert legs of --extra, or the small-batch legs) and print it; for "
+                         "profiler runs")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
                     help="only write --traffic-json from rocprofv3 --pmc outputs under DIR "
                          "(pmc_<COUNTER>_<gate_up|down|copy>/*counter_collection.csv); no GPU")
@@ -327,6 +332,21 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.counter_run and args.counter_run not in ("gate_up", "down"):
+        counter_run_other(cq, synth, dev, args.counter_run, args.steps)
+        return
+    if args.leg:
+        stream = torch.cuda.current_stream(dev)
+        if args.leg == "prefill":
+            res = prefill_blocks(cq, synth, dev, stream)
+        elif args.leg == "decode_step":
+            res = {"decode_step_16x": decode_step_block(cq, synth, dev)}
+        elif args.leg == "moe":
+            res = moe_workloads(cq, synth, dev)
+        else:
+            res = smallm_workloads(cq, synth, dev)
+        print(json.dumps({"leg": args.leg, **res}), flush=True)
+        return
     (w_up, x_up), (w_dn, x_dn) = synth.decode_config(seed=2, device=dev)
 
     def to_cw(w):
@@ -420,6 +440,64 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def counter_run_other(cq, synth, dev, which, steps):
+    """Eager launches of one product (no graphs), for counter passes: the M = 4096
+    prefill products (W3 G256 6144 x 7168), the 16-expert decode step (A16 or A8,
+    eight disjoint expert sets of 128 resident experts) or W4 G128 gate_up at 64 rows."""
+    import torch
+    if which in ("prefill_a16", "prefill_a8"):
+        w, x = synth.prefill_config(seed=5, device=dev)
+        cw = cq.CubicWeight(cq.cubic_pack(w.codes, 3).reshape(-1), w.scales, w.shapes, w.N, w.K, 3, 256)
+        y = torch.empty((4096, 6144), dtype=torch.float32, device=dev)
+        if which == "prefill_a16":
+            ws = torch.empty(cq.cubic_gemm_a16_workspace_bytes(4096, 7168), dtype=torch.uint8, device=dev)
+            run = lambda i: cq.cubic_gemm_a16(x, cw, out=y, workspace=ws)
+        else:
+            xq, sx = cq.act_quant_int8_per_token(x)
+            run = lambda i: cq.cubic_gemm_a8(xq, sx, cw, out=y)
+    elif which in ("decode_step", "decode_step_a8"):
+        pool, x, ids, ws, y = _decode_step_setup(cq, synth, dev)
+        if which == "decode_step":
+            run = lambda i: cq.cubic_moe_grouped_gemm(x, ids[i % len(ids)], pool, 128, out=y, workspace=ws)
+        else:
+            xq, sx = cq.act_quant_int8_per_token(x)
+            run = lambda i: cq.cubic_moe_grouped_gemm_a8(xq, sx, ids[i % len(ids)], pool, 128, out=y,
+                                                         workspace=ws)
+    else:
+        (wu, xu), _ = synth.smallm_config(64, seed=3, device=dev)
+        cw = cq.CubicWeight(cq.cubic_pack(wu.codes, 4).reshape(-1), wu.scales, wu.shapes, wu.N, wu.K, 4, 128)
+        ws = torch.empty(max(1, cq.cubic_gemm_a16_workspace_bytes(64, wu.K)), dtype=torch.uint8, device=dev)
+        y = torch.empty((64, wu.N), dtype=torch.float32, device=dev)
+        run = lambda i: cq.cubic_gemm_a16(xu, cw, out=y, workspace=ws)
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": which, "launches": steps}), flush=True)
+
+
+def _decode_step_setup(cq, synth, dev):
+    """128 resident gate_up experts 6144 x 7168 W2 G512, one token, eight disjoint
+    top-16 sets of them, workspace and output."""
+    import torch
+    H, I, bits, group, E, topk = 7168, 3072, 2, 512, 128, 16
+    N, cb = 2 * I, 2 * I * H * bits // 8
+    codes = torch.empty(E * cb, dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N, H // group), dtype=torch.float32, device=dev)
+    shapes = torch.empty((E, N, H // group, 2), dtype=torch.int16, device=dev)
+    for e in range(E):
+        w = synth.moe_expert(e, seed=4, N=N, K=H, bits=bits, group=group, device=dev)
+        cq.cubic_pack(w.codes, bits, out=codes[e * cb:(e + 1) * cb].view(N, H * bits // 8))
+        scales[e] = w.scales
+        shapes[e] = w.shapes
+    pool = cq.CubicWeight(codes, scales.reshape(-1), shapes.reshape(-1), N, H, bits, group)
+    x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=topk, K=H, device=dev)
+    perm = torch.randperm(E, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    ids = [perm[16 * k:16 * k + 16].view(1, topk).to(dev) for k in range(E // topk)]
+    ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E), dtype=torch.uint8, device=dev)
+    y = torch.empty((1, topk, N), dtype=torch.float32, device=dev)
+    return pool, x, ids, ws, y
+
+
 def prefill_blocks(cq, synth, dev, stream):
     """The M = 4096 half of the metric: W3 G256 weight 6144 x 7168, activations
     4096 x 7168 bf16 with 36 outlier columns. prefill_a16: one cubic_gemm_a16 call
@@ -475,22 +553,9 @@ def decode_step_block(cq, synth, dev):
     recurs only after 1.3 GB of other experts. Algorithmic bytes: 16 experts'
     codes and group parameters, the token row in, the 16 output rows out."""
     import torch
-    H, I, bits, group, E, topk = 7168, 3072, 2, 512, 128, 16
-    N, cb = 2 * I, 2 * I * H * bits // 8
-    codes = torch.empty(E * cb, dtype=torch.uint8, device=dev)
-    scales = torch.empty((E, N, H // group), dtype=torch.float32, device=dev)
-    shapes = torch.empty((E, N, H // group, 2), dtype=torch.int16, device=dev)
-    for e in range(E):
-        w = synth.moe_expert(e, seed=4, N=N, K=H, bits=bits, group=group, device=dev)
-        cq.cubic_pack(w.codes, bits, out=codes[e * cb:(e + 1) * cb].view(N, H * bits // 8))
-        scales[e] = w.scales
-        shapes[e] = w.shapes
-    pool = cq.CubicWeight(codes, scales.reshape(-1), shapes.reshape(-1), N, H, bits, group)
-    x, _ = synth.moe_routing(seed=4, T=1, E=E, topk=topk, K=H, device=dev)
-    perm = torch.randperm(E, generator=torch.Generator().manual_seed(7)).to(torch.int32)
-    ids = [perm[16 * k:16 * k + 16].view(1, topk).to(dev) for k in range(E // topk)]
-    ws = torch.empty(cq.cubic_moe_workspace_bytes(1, topk, E), dtype=torch.uint8, device=dev)
-    y = torch.empty((1, topk, N), dtype=torch.float32, device=dev)
+    H, bits, group, E, topk = 7168, 2, 512, 128, 16
+    N = 6144
+    pool, x, ids, ws, y = _decode_step_setup(cq, synth, dev)
     ms = _graph_time([(lambda i=i: cq.cubic_moe_grouped_gemm(x, i, pool, E, out=y, workspace=ws)) for i in ids],
                      5, dev)
     nb = topk * (N * H * bits // 8 + 8 * N * (H // group)) + H * 2 + topk * N * 4
@@ -514,7 +579,7 @@ def decode_step_block(cq, synth, dev):
                  "kernel": "cubic_moe_grouped_gemm_a8 call: k_moe_route + k_moe_a8<2>",
                  "frac_of_hbm_peak": round(g8 / HBM_PEAK_GBS, 4)}
     print(json.dumps({"decode_step_16x": res}), file=sys.stderr, flush=True)
-    del codes, scales, shapes, pool
+    del pool
     torch.cuda.empty_cache()
     return res
 
@@ -565,6 +630,15 @@ def extra_workloads(cq, synth, dev, stream):
     (M = 8, 64) over rotating weight copies, nearest-level encoding, group
     fitting, and the routed-expert products and MLP step (one token x 16
     experts; 64 tokens x 16 over 896 experts)."""
+    res = smallm_workloads(cq, synth, dev)
+    res.update(encode_workloads(cq, synth, dev))
+    res.update(fit_workloads(cq, synth, dev))
+    res.update(moe_workloads(cq, synth, dev))
+    return res
+
+
+def smallm_workloads(cq, synth, dev):
+    """Small-batch W4 G128 products (M = 8, 64) over 16 rotating weight copies."""
     import torch
     res = {}
     copies = 16
@@ -587,9 +661,6 @@ def extra_workloads(cq, synth, dev, stream):
             del pool, base
         del wu, wd
         torch.cuda.empty_cache()
-    res.update(encode_workloads(cq, synth, dev))
-    res.update(fit_workloads(cq, synth, dev))
-    res.update(moe_workloads(cq, synth, dev))
     return res
 
 

@@ -13,8 +13,9 @@
 //    registers (byte-wise v_perm: lo and hi bytes of 2^B fp16 levels). No weight
 //    value passes through LDS and no row is decoded twice;
 //  - the fp16 activation tile (prepared by k_xprep) goes from global memory
-//    straight into LDS (buffer_load ... lds), double buffered, in an XOR-swizzled
-//    layout that keeps the MFMA fragment reads free of bank conflicts;
+//    straight into LDS (buffer_load ... lds), in three stages, in an XOR-swizzled
+//    layout that keeps the MFMA fragment reads free of bank conflicts (any 16
+//    consecutive rows read at one chunk hit 16 distinct 16-byte bank groups);
 //  - within a step the K order is permuted identically on both operands: MFMA
 //    block kb takes codes 8 kb .. 8 kb + 7 of each 32-code half.
 // Levels are fp16(s * q * 2^-e_n), with 2^e_n a per-row power of two at or above
@@ -307,14 +308,16 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
   }
 
   // ---- activation tile: global -> LDS, 16-byte slots, XOR swizzle ----
-  // Slot (row r, chunk q) of a buffer holds the 8 fp16 x[m0 + r][k0 + 8 (q ^ (r & 7))].
+  // Slot (row r, chunk q) of a buffer holds the 8 fp16 x[m0 + r][k0 + 8 (q ^ sw(r))],
+  // sw(r) = (r & 7) ^ ((r >> 3) & 1): rows are 128 bytes, so rows r and r + 8 of
+  // a 16-lane group would share banks under r & 7 alone.
   // Wave w fills slots 64 MB w + 64 i + lane (i < MB): row 8 MB w + 8 i + lane / 8.
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K * 2));
   uint32_t aoff[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int r = 8 * MB * wave + 8 * i + (lane >> 3);
-    const int q = (lane & 7) ^ (r & 7);
+    const int q = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
     aoff[i] = static_cast<uint32_t>(((m0 + r) * p.K + 8 * q) * 2);
   }
   auto issue_a = [&](int s, int buf, int i0, int i1) {
@@ -386,7 +389,7 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
   // one fragment: activation block j for MFMA block kb, row 32 j + c, chunk 4 h + kb
   auto read_frag = [&](const uint16_t* Ab, int kb, int j) {
     const int r = 32 * j + c;
-    const int q = (4 * h + kb) ^ (r & 7);
+    const int q = (4 * h + kb) ^ (r & 7) ^ ((r >> 3) & 1);
     return *reinterpret_cast<const f16x8*>(Ab + (r * 8 + q) * 8);
   };
 

@@ -46,7 +46,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* p, uint32_
 constexpr int sk_wait_vm(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
 // Per-wave LDS ring stage: activations [32 MB rows][64 k] fp16 (16-byte chunk
-// q of row r at chunk q ^ (r & 7)), then the code words, then the group
+// q of row r at chunk q ^ (r & 7) ^ ((r >> 3) & 1)), then the code words, then the group
 // parameters of the step after it (64 scales, 64 (a, b) words; lanes 32..63
 // repeat rows 0..31). Code words of lane l (row l / 2, half l % 2): 2-bit codes,
 // dword d at 256 d + 4 l; 3- and 4-bit codes, 16 l; wider codes, dwords 0..3 at
@@ -123,10 +123,13 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
       reinterpret_cast<uint16_t*>(smem + SK_WAVES * NST * kStage + wave * sk_tab_bytes<B>());
 
   // ---- loads of one step into a stage (this wave's own) ----
-  // activations: load i covers rows 8 i .. 8 i + 7; lane l -> row 8 i + l / 8,
-  // physical chunk l % 8 = logical chunk (l % 8) ^ (l / 8 % 8). Rows past M read 0.
+  // activations: load i covers rows 8 i .. 8 i + 7; lane l -> row r = 8 i + l / 8,
+  // physical chunk l % 8 = logical chunk (l % 8) ^ sw(r), sw(r) = (r & 7) ^
+  // ((r >> 3) & 1) (rows are 128 bytes: without the second term rows r and r + 8
+  // of a 16-lane group share banks). Rows past M read 0.
   const __amdgpu_buffer_rsrc_t xrs = sk_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K * 2));
-  const uint32_t xoff = static_cast<uint32_t>(((lane >> 3) * p.K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+  const uint32_t xoff0 = static_cast<uint32_t>(((lane >> 3) * p.K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+  const uint32_t xoff1 = static_cast<uint32_t>(((lane >> 3) * p.K + 8 * ((lane & 7) ^ ((lane >> 3) & 7) ^ 1)) * 2);
   // code words: lane l -> row n0 + l / 2, codes 32 (l % 2) .. + 31 of the step.
   // Rows past N read 0.
   const __amdgpu_buffer_rsrc_t crs = sk_rsrc(p.codes, static_cast<uint32_t>(p.N) * row_bytes);
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
     for (int i = 0; i < NX; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrs, st + 1024 * i, 16,
-          xoff + static_cast<uint32_t>(8 * i) * static_cast<uint32_t>(p.K) * 2 +
+          (i & 1 ? xoff1 : xoff0) + static_cast<uint32_t>(8 * i) * static_cast<uint32_t>(p.K) * 2 +
               static_cast<uint32_t>(sv) * (SK_K * 2),
           0, 0, 0);
     if constexpr (B == 4) {
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(64 * SK_WAVES, 1) void k_skinny(TiledParams p) {
       for (int j = 0; j < MB; ++j) {
         // activation rows 32 j + c, logical chunk 4 h + kb
         const int r = 32 * j + c;
-        fa[kb][j] = *reinterpret_cast<const f16x8*>(st + r * 128 + 16 * ((4 * h + kb) ^ (r & 7)));
+        fa[kb][j] = *reinterpret_cast<const f16x8*>(st + r * 128 + 16 * ((4 * h + kb) ^ (r & 7) ^ ((r >> 3) & 1)));
       }
     // the next step starts a group: its table and scale (parameters of the
     // group of step s + 1 come with stage s)
