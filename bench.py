@@ -62,6 +62,9 @@ def parse():
                     help="only run one workload block (prefill A16/A8, the 16-expert decode step, the "
                          "routed-expert legs of --extra, or the small-batch legs) and print it; for "
                          "profiler runs")
+    ap.add_argument("--floors", action="store_true",
+                    help="only time the floor kernels (empty launch, load-only streams of the gate_up "
+                         "codes, dependent-load chase) and print them")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
                     help="only write --traffic-json from rocprofv3 --pmc outputs under DIR "
                          "(pmc_<COUNTER>_<gate_up|down|copy>/*counter_collection.csv); no GPU")
@@ -332,6 +335,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.floors:
+        floors(dev)
+        return
     if args.counter_run and args.counter_run not in ("gate_up", "down"):
         counter_run_other(cq, synth, dev, args.counter_run, args.steps)
         return
@@ -438,6 +444,70 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def floors(dev):
+    """Floors of one launch on this part, from the floor kernels of
+    libcubic_floors.so, each timed as graph replays with HIP events:
+    - empty kernels with the decode GEMV's grid (512 x 256) and with 1 x 64;
+    - load-only streams over the codes of gate_up 6144 x 7168 W2 (11,010,048 bytes)
+      on 50 rotating copies (551 MB, past the 256 MB last-level cache): the GEMV's
+      access pattern (12-row workgroups, 16 rows x 64 bytes per wave load) and
+      contiguous 1 KB wave loads on 512 and on 256 workgroups;
+    - one lane chasing a cyclic permutation of 2^27 uint32 (512 MB): the latency of
+      a dependent load that misses every cache."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "dequant_gemm_amd", "lib", "libcubic_floors.so"))
+    vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint
+    lib.floors_empty.argtypes = [u32, u32, vp, vp]
+    lib.floors_rows.argtypes = [vp, i64, i64, vp, vp]
+    lib.floors_contig.argtypes = [vp, u32, i64, vp, vp]
+    lib.floors_chase.argtypes = [vp, i64, vp, vp]
+    for f in (lib.floors_empty, lib.floors_rows, lib.floors_contig, lib.floors_chase):
+        f.restype = ctypes.c_int
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    out = torch.empty(512 * 256, dtype=torch.int32, device=dev)
+    op = ctypes.c_void_p(out.data_ptr())
+    rows, row_bytes = 6144, 1792
+    nbytes = rows * row_bytes
+    bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device=dev) for i in range(50)]
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"floor kernel launch failed ({rc})")
+
+    res = {}
+    res["empty_512x256_us"] = round(_graph_time([lambda: ok(lib.floors_empty(512, 256, op, st()))] * 50, 5, dev)
+                                    * 1e3, 3)
+    res["empty_1x64_us"] = round(_graph_time([lambda: ok(lib.floors_empty(1, 64, op, st()))] * 50, 5, dev) * 1e3, 3)
+    for name, call in (
+            ("stream_gemv_pattern_512wg", lambda b: ok(lib.floors_rows(b.data_ptr(), rows, row_bytes, op, st()))),
+            ("stream_contig_512wg", lambda b: ok(lib.floors_contig(b.data_ptr(), 512, nbytes // 512, op, st()))),
+            ("stream_contig_256wg", lambda b: ok(lib.floors_contig(b.data_ptr(), 256, nbytes // 256, op, st())))):
+        ms = _graph_time([(lambda b=b: call(b)) for b in bufs], 5, dev)
+        res[name + "_us"] = round(ms * 1e3, 3)
+        res[name + "_GB/s"] = round(nbytes / ms / 1e6, 1)
+    del bufs
+    n = 1 << 27
+    perm = np.random.default_rng(11).permutation(n).astype(np.uint32)
+    nxt = np.empty(n, dtype=np.uint32)
+    nxt[perm] = np.roll(perm, -1)                      # one cycle through every index
+    dn = torch.from_numpy(nxt.view(np.int32)).to(dev)
+    del perm, nxt
+    steps = 20000
+    ok(lib.floors_chase(dn.data_ptr(), 1000, op, st()))
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    ok(lib.floors_chase(dn.data_ptr(), steps, op, st()))
+    b.record()
+    torch.cuda.synchronize()
+    res["chase_ns_per_dependent_load"] = round(a.elapsed_time(b) * 1e6 / steps, 1)
+    res["bytes_per_stream_launch"] = nbytes
+    print(json.dumps({"floors": res}), flush=True)
 
 
 def counter_run_other(cq, synth, dev, which, steps):

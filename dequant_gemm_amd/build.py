@@ -62,7 +62,25 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_floors(verbose)
     return LIB
+
+
+FLOORS_LIB = os.path.join(LIBDIR, "libcubic_floors.so")
+
+
+def build_floors(verbose: bool = True) -> str:
+    """The benchmark's floor kernels (csrc/floors.hip) as a library of their own."""
+    obj = _compile("floors.hip")
+    tmp = FLOORS_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, FLOORS_LIB)
+    if verbose:
+        print(f"built {FLOORS_LIB}")
+    return FLOORS_LIB
 
 
 if __name__ == "__main__":
