@@ -453,7 +453,9 @@ def floors(dev):
     - load-only streams over the codes of gate_up 6144 x 7168 W2 (11,010,048 bytes)
       on 50 rotating copies (551 MB, past the 256 MB last-level cache): the GEMV's
       access pattern (12-row workgroups, 16 rows x 64 bytes per wave load) and
-      contiguous 1 KB wave loads on 512 and on 256 workgroups;
+      contiguous 1 KB wave loads on 512 and on 256 workgroups; the same for the
+      16-expert decode step's 176 MB of codes in one launch (GEMV pattern, and
+      contiguous with eight loads in flight per lane on 2688 and 768 workgroups);
     - one lane chasing a cyclic permutation of 2^27 uint32 (512 MB): the latency of
       a dependent load that misses every cache."""
     import ctypes
@@ -465,11 +467,12 @@ def floors(dev):
     lib.floors_empty.argtypes = [u32, u32, vp, vp]
     lib.floors_rows.argtypes = [vp, i64, i64, vp, vp]
     lib.floors_contig.argtypes = [vp, u32, i64, vp, vp]
+    lib.floors_contig8.argtypes = [vp, u32, i64, vp, vp]
     lib.floors_chase.argtypes = [vp, i64, vp, vp]
-    for f in (lib.floors_empty, lib.floors_rows, lib.floors_contig, lib.floors_chase):
+    for f in (lib.floors_empty, lib.floors_rows, lib.floors_contig, lib.floors_contig8, lib.floors_chase):
         f.restype = ctypes.c_int
     st = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    out = torch.empty(512 * 256, dtype=torch.int32, device=dev)
+    out = torch.empty(8192 * 256, dtype=torch.int32, device=dev)
     op = ctypes.c_void_p(out.data_ptr())
     rows, row_bytes = 6144, 1792
     nbytes = rows * row_bytes
@@ -491,6 +494,20 @@ def floors(dev):
         res[name + "_us"] = round(ms * 1e3, 3)
         res[name + "_GB/s"] = round(nbytes / ms / 1e6, 1)
     del bufs
+    # the 16-expert decode step's code bytes in one launch: 16 x 6144 rows of
+    # 1792 bytes (176 MB), three rotating copies (528 MB)
+    big_rows = 16 * rows
+    big = big_rows * row_bytes
+    bigs = [torch.full((big,), i, dtype=torch.uint8, device=dev) for i in range(3)]
+    for name, call in (
+            ("step16_gemv_pattern", lambda b: ok(lib.floors_rows(b.data_ptr(), big_rows, row_bytes, op, st()))),
+            ("step16_contig8_2688wg", lambda b: ok(lib.floors_contig8(b.data_ptr(), 2688, big // 2688, op, st()))),
+            ("step16_contig8_768wg", lambda b: ok(lib.floors_contig8(b.data_ptr(), 768, big // 768, op, st())))):
+        ms = _graph_time([(lambda b=b: call(b)) for b in bigs], 5, dev)
+        res[name + "_us"] = round(ms * 1e3, 3)
+        res[name + "_GB/s"] = round(big / ms / 1e6, 1)
+    res["step16_bytes"] = big
+    del bigs
     n = 1 << 27
     perm = np.random.default_rng(11).permutation(n).astype(np.uint32)
     nxt = np.empty(n, dtype=np.uint32)

@@ -17,6 +17,7 @@ using namespace cubic;
 namespace {
 
 constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
+constexpr int64_t kGemvA8MaxM = 16;         // A8 rows taken by the routed kernel's organisation (passes of 4)
 constexpr int64_t kGemvMaxM = 16;          // one MFMA activation tile
 constexpr int64_t kGemvMaxMW2 = 8;         // 2-bit codes: the small-batch kernel is faster above
 constexpr int64_t kInkMaxM = 4;            // single-kernel A16 path
@@ -240,6 +241,25 @@ int gemm_a8_impl(const int8_t* xq, const float* x_scale, int64_t M, const cubic_
   if ((M + 127) / 128 > 65535) return CUBIC_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, ybf16, s));
+  if (M <= kGemvA8MaxM && moe_a8_supported(w->K, w->bits, w->group) &&
+      cubic_code_bytes(w->N, w->K, w->bits) <= UINT32_MAX) {
+    // small M: the routed A8 kernel's organisation on one weight, no routing
+    MoeA8Params q{};
+    q.codes = w->codes;
+    q.scales = w->scales;
+    q.shapes = w->shapes;
+    q.N = w->N;
+    q.K = w->K;
+    q.group = w->group;
+    q.topk = 1;
+    q.code_bytes = static_cast<int64_t>(cubic_code_bytes(w->N, w->K, w->bits));
+    q.xq = xq;
+    q.xs = x_scale;
+    q.y = y;
+    q.ybf16 = ybf16 ? 1 : 0;
+    q.dense_m = static_cast<int>(M);
+    return hip_status(launch_gemv_a8(q, w->bits, s));
+  }
   TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xq, x_scale, y, ybf16 ? 1 : 0};
   if (prefill_a8_supported(M, w->N, w->K, w->bits, w->group)) return hip_status(launch_prefill_a8(p, w->bits, s));
   return hip_status(launch_tiled_a8(p, w->bits, s));

@@ -4,7 +4,8 @@
 //  - an empty kernel with a given grid (launch and dispatch cost);
 //  - a load-only stream over a weight-sized buffer, with the decode GEMV's
 //    access pattern (16 rows x 64 bytes per wave load, 12-row workgroups, a
-//    quarter of each row per wave) or with contiguous 1 KB wave loads;
+//    quarter of each row per wave) or with contiguous 1 KB wave loads (one, or
+//    eight, in flight per lane);
 //  - a dependent-load chase through a cyclic permutation (latency of one
 //    access that misses every cache).
 #include <hip/hip_runtime.h>
@@ -56,6 +57,24 @@ __global__ __launch_bounds__(256) void k_floor_contig(const unsigned char* __res
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = z;
 }
 
+// Contiguous with 8 loads in flight per lane: workgroup b reads bytes
+// [b chunk, (b + 1) chunk) (chunk a multiple of 32 KB), each wave 1 KB per load.
+__global__ __launch_bounds__(256) void k_floor_contig8(const unsigned char* __restrict__ w, int64_t chunk,
+                                                       uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned char* base = w + static_cast<int64_t>(blockIdx.x) * chunk;
+  uint32_t z = 0;
+  for (int64_t o = 0; o < chunk; o += 32768) {
+    u32x4f v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const u32x4f*>(base + o + (static_cast<int64_t>(u * 4 + wave) * 64 + lane) * 16);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) z ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = z;
+}
+
 // One lane follows next[] for `steps` dependent loads (next is a cyclic
 // permutation of [0, n), so every index stays in range).
 __global__ void k_floor_chase(const uint32_t* __restrict__ next, int64_t steps, uint32_t* __restrict__ out) {
@@ -90,6 +109,15 @@ __attribute__((visibility("default"))) int floors_contig(const void* w, unsigned
                                                          void* stream) {
   if (grid == 0 || chunk <= 0 || chunk % 16 != 0) return -1;
   hipLaunchKernelGGL(k_floor_contig, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char*>(w), chunk, static_cast<uint32_t*>(out));
+  return static_cast<int>(hipGetLastError());
+}
+
+// out: grid * 256 uint32; bytes = grid * chunk, chunk a multiple of 32768.
+__attribute__((visibility("default"))) int floors_contig8(const void* w, unsigned grid, int64_t chunk, void* out,
+                                                          void* stream) {
+  if (grid == 0 || chunk <= 0 || chunk % 32768 != 0) return -1;
+  hipLaunchKernelGGL(k_floor_contig8, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const unsigned char*>(w), chunk, static_cast<uint32_t*>(out));
   return static_cast<int>(hipGetLastError());
 }

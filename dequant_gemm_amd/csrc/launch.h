@@ -64,6 +64,7 @@ struct MoeA8Params {
   const float* xs;        // [T] per-token scales
   float* y;               // [T*topk][N] fp32, or bf16 when ybf16
   int ybf16;
+  int dense_m;            // launch_gemv_a8: activation rows of a plain product (no routing)
 };
 
 int device_cu_count();   // compute units of the current device (0 if unknown)
@@ -106,6 +107,9 @@ hipError_t launch_moe_route(const int32_t* ids, int P, int E, int64_t N, float* 
 bool moe_a8_supported(int64_t K, int bits, int group);
 hipError_t launch_moe_a8(const int32_t* ids, int T, int E, int topk, const MoeA8Params& base, int32_t* hdr,
                          int32_t* erec, int32_t* sorted, int bits, hipStream_t st);
+// The plain A8 product of p.dense_m rows (small M) on the routed kernel's
+// organisation: one workgroup per 16-row tile, passes of up to four rows.
+hipError_t launch_gemv_a8(const MoeA8Params& p, int bits, hipStream_t st);
 // The A8 grouped product over a routing already in p.hdr / p.erec / p.sorted.
 hipError_t launch_moe_a8_product(const MoeA8Params& p, int P, int E, int T, int bits, hipStream_t st);
 // The MLP step's elementwise kernels: h = bf16(SiLU(gate) * up) from the gate_up

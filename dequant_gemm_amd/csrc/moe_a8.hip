@@ -217,8 +217,10 @@ __host__ __device__ inline size_t a8_lds_bytes(const A8Geom& g, int mt) {
 }
 
 // One workgroup per (touched expert slot, 16-row tile); slots past the touched
-// count exit at once. ALLIN: every step of a wave fits the load slots.
-template <int B, int MT, bool ALLIN>
+// count exit at once. ALLIN: every step of a wave fits the load slots. DENSE:
+// the plain A8 product of p.dense_m activation rows with one weight (expert 0,
+// row m of x and of y for pair m; no routing): one workgroup per 16-row tile.
+template <int B, int MT, bool ALLIN, bool DENSE = false>
 __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
   using Cfg = A8Cfg<B>;
   constexpr int PS = Cfg::kSlots;
@@ -226,7 +228,12 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
   const unsigned a = blockIdx.x / tiles;
-  const i32x8 rec = *reinterpret_cast<const i32x8*>(p.erec + 8 * a);
+  i32x8 rec;
+  if constexpr (DENSE) {
+    rec = i32x8{0, 0, p.dense_m, 0, p.dense_m > 1 ? 1 : 0, 0, 0, 0};
+  } else {
+    rec = *reinterpret_cast<const i32x8*>(p.erec + 8 * a);
+  }
   if (rec[2] == 0) return;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x - a * tiles) * 16;
   const int lane = threadIdx.x & 63;
@@ -278,7 +285,11 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int mm = m < Mt ? m : 0;            // rows past the pass repeat its first pair
-      pr[m] = (mt == 0 && mm < 2) ? rec[3 + mm] : p.sorted[__builtin_amdgcn_readfirstlane(beg + mt + mm)];
+      if constexpr (DENSE) {
+        pr[m] = mt + mm;
+      } else {
+        pr[m] = (mt == 0 && mm < 2) ? rec[3 + mm] : p.sorted[__builtin_amdgcn_readfirstlane(beg + mt + mm)];
+      }
     }
     const u32x4* xv[MT];
 #pragma unroll
@@ -464,6 +475,41 @@ bool moe_a8_supported(int64_t K, int bits, int group) {
     default: lds = a8_lds_bytes<8>(geo, 1); break;
   }
   return lds <= 160 * 1024;
+}
+
+template <int B>
+hipError_t launch_gemv_a8_b(const MoeA8Params& p, hipStream_t st) {
+  const A8Geom geo = a8_geom(p.K, p.group);
+  const bool allin = geo.mpw <= A8Cfg<B>::kSlots;
+  // four rows per pass when the four activation slices fit, else one
+  int mt = p.dense_m <= 1 ? 1 : 4;
+  if (mt == 4 && a8_lds_bytes<B>(geo, 4) > 160 * 1024) mt = 1;
+  const size_t lds = a8_lds_bytes<B>(geo, mt);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  auto kern = mt == 1 ? (allin ? k_moe_a8<B, 1, true, true> : k_moe_a8<B, 1, false, true>)
+                      : (allin ? k_moe_a8<B, 4, true, true> : k_moe_a8<B, 4, false, true>);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  const int64_t tiles = (p.N + 15) / 16;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(256), lds, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_a8(const MoeA8Params& p, int bits, hipStream_t st) {
+  if (p.dense_m <= 0 || p.N <= 0) return hipSuccess;
+  if ((p.N + 15) / 16 > 0x7fffffff) return hipErrorInvalidValue;
+  switch (bits) {
+    case 2: return launch_gemv_a8_b<2>(p, st);
+    case 3: return launch_gemv_a8_b<3>(p, st);
+    case 4: return launch_gemv_a8_b<4>(p, st);
+    case 5: return launch_gemv_a8_b<5>(p, st);
+    case 6: return launch_gemv_a8_b<6>(p, st);
+    case 7: return launch_gemv_a8_b<7>(p, st);
+    default: return launch_gemv_a8_b<8>(p, st);
+  }
 }
 
 hipError_t launch_moe_a8_product(const MoeA8Params& p, int P, int E, int T, int bits, hipStream_t st) {

@@ -108,8 +108,8 @@ def test_single_workload_a8():
 
 
 @pytest.mark.parametrize("bits,group", [(2, 128), (2, 256), (2, 512), (3, 128), (3, 256), (3, 512),
-                                        (3, 1024), (4, 128), (5, 128), (8, 1024)])
-@pytest.mark.parametrize("M", [1, 7, 130, 300])
+                                        (3, 1024), (4, 128), (5, 128), (6, 256), (7, 128), (8, 1024)])
+@pytest.mark.parametrize("M", [1, 4, 7, 16, 130, 300])
 def test_a8_ragged(bits, group, M):
     say(f"A8 ragged bits={bits} G={group} M={M}")
     g = synth.make_generator(2000 + 10 * bits + M)
@@ -186,3 +186,9 @@ def test_a8_carriers_exact_through_identity_rows(bits):
     assert np.abs(C - Ci).max() < 1e-3
     want = oracle.carrier_codes(codes, shapes, bits, G).T
     assert np.array_equal(Ci.astype(np.int64), want)
+    # the same read-back through the small-batch kernel: 16 identity rows a call
+    for k0 in range(0, K, 16):
+        ys = cq.cubic_gemm_a8(xq[k0:k0 + 16].contiguous(), sx[:16].contiguous(), cw).cpu().numpy()
+        Cs = ys.astype(np.float64) / unit[k0:k0 + 16]
+        assert np.abs(Cs - np.rint(Cs)).max() < 1e-3
+        assert np.array_equal(np.rint(Cs).astype(np.int64), want[k0:k0 + 16]), k0
