@@ -249,12 +249,40 @@ __device__ __forceinline__ int carrier_level(double a, double b, int j, int km) 
   return static_cast<int>(n);
 }
 
+// carrier_level for fp16 a and b with |a|, |b| <= 16, in fp64 with no integer
+// products and no division. S = Kmax^3 q(j / Kmax) = a X + b Y + j^3 (X = j Kmax^2
+// - j^3, Y = j^2 Kmax - j^3, integers below 2^21 for j <= 128) is a multiple of
+// 2^-24 below 2^27 in magnitude, so the two fmas that form it are exact. Then
+// Xq = S * fl(127 / Kmax^3) lies within 2^-44 of 127 S / Kmax^3, so n0 = rint(Xq)
+// is the correctly rounded carrier or one off it next to a tie; the residual D =
+// 127 S - Kmax^3 n0 (a multiple of 2^-24 below 2^21) comes out of one fma
+// exactly, and comparing it with Kmax^3 / 2 settles the off-by-one case and ties
+// (to even).
+__device__ __forceinline__ int carrier_exact(double a, double b, int j, int km) {
+  const double j3 = static_cast<double>(j * j * j);
+  const double X = static_cast<double>(j * km * km) - j3;
+  const double Y = static_cast<double>(j * j * km) - j3;
+  const double K3 = static_cast<double>(km * km * km);
+  const double S = fma(a, X, fma(b, Y, j3));
+  const double Xq = S * (127.0 / K3);
+  if (Xq >= 127.75) return 127;                 // rounds to 128 or more: clamped
+  if (Xq <= -127.75) return -127;
+  const double n0 = rint(Xq);
+  const double D = fma(127.0, S, -K3 * n0);
+  const double h = 0.5 * K3;
+  int n = static_cast<int>(n0);
+  const bool odd = (n & 1) != 0;
+  n += (D > h || (D == h && odd)) ? 1 : 0;
+  n -= (D < -h || (D == -h && odd)) ? 1 : 0;
+  return n > 127 ? 127 : (n < -127 ? -127 : n);
+}
+
 // carrier_level for fp16 a and b, decided in fp32 where that is safe: with
-// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^20), y = 127 (j^3 + a X +
+// X = j K^2 - j^3 and Y = j^2 K - j^3 (integers below 2^21), y = 127 (j^3 + a X +
 // b Y) / K^3 takes two fmas and one multiply. For |a|, |b| <= 16 and K <= 127 the
-// terms stay below 2^25, so y is within 2e-4 of 127 q_j; when y lies within 1e-3
-// of a half-integer (a possible tie or a rounding the estimate could get wrong),
-// or a or b is outside that range, the exact integer rule decides.
+// terms stay below 2^26, so y is within 3e-4 of 127 q_j; when y lies within 1e-3
+// of a half-integer (a possible tie or a rounding the estimate could get wrong)
+// carrier_exact decides, and for a or b outside that range the integer rule.
 __device__ __forceinline__ int carrier_fast(float a, float b, int j, int km) {
   const float j3 = static_cast<float>(j * j * j);
   const float X = static_cast<float>(j * km * km) - j3;
@@ -262,8 +290,11 @@ __device__ __forceinline__ int carrier_fast(float a, float b, int j, int km) {
   const float y = fmaf(a, X, fmaf(b, Y, j3)) * (127.0f / static_cast<float>(km * km * km));
   const float r = rintf(y);
   const bool near_tie = fabsf(fabsf(y - r) - 0.5f) < 1e-3f;
-  if (near_tie || !(fabsf(a) <= 16.0f && fabsf(b) <= 16.0f))
-    return carrier_level(static_cast<double>(a), static_cast<double>(b), j, km);
+  const bool small = fabsf(a) <= 16.0f && fabsf(b) <= 16.0f;
+  if (near_tie || !small) {
+    return small ? carrier_exact(static_cast<double>(a), static_cast<double>(b), j, km)
+                 : carrier_level(static_cast<double>(a), static_cast<double>(b), j, km);
+  }
   const int n = static_cast<int>(r);
   return n > 127 ? 127 : (n < -127 ? -127 : n);
 }

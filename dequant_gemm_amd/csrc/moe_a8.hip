@@ -17,7 +17,7 @@
 // sum of the four waves' partials.
 //
 // Carriers (sign(k) * clamp(rne(127 q(|k| / Kmax)), -127, 127), decided exactly
-// with integers by carrier_level):
+// by carrier_exact, or carrier_level for shapes beyond 16 in magnitude):
 //  - 2-bit codes: the row's four carriers sit in one register. For 16 codes
 //    in a dword w, (w >> 2j) & 0x03030303 holds the fields of codes j, 4 + j,
 //    8 + j, 12 + j as byte selectors, and one v_perm per j turns them into
@@ -45,7 +45,9 @@ template <int B>
 struct A8Cfg {
   static constexpr int kSlots = B == 2 ? 16 : (B == 3 ? 10 : (B == 4 ? 8 : 4));   // steps in flight
   static constexpr bool kRegTable = B <= 4;
-  static constexpr int kGpDwords = B <= 3 ? 4 : 8;   // LDS entry per (row, group): scale, carriers
+  static constexpr bool kDirect = B >= 7;            // carriers computed per code, no table
+  // LDS entry per (row, group): scale, then the carriers (up to 4 bits) or (a, b)
+  static constexpr int kGpDwords = B == 2 ? 2 : (B == 3 ? 3 : (B == 4 ? 5 : 2));
 };
 
 constexpr int kA8GpRegs = 8;        // group-parameter registers per lane: <= 32 groups per wave
@@ -64,7 +66,10 @@ __device__ __forceinline__ void carrier_regs(uint32_t ab, uint32_t* T) {
   int C[NF / 2 + 1];
   C[0] = 0;
 #pragma unroll
-  for (int j = 1; j <= NF / 2; ++j) C[j] = j == km ? 127 : carrier_level(a, b, j, km);
+  for (int j = 1; j <= NF / 2; ++j) {
+    C[j] = j == km ? 127 : (fabs(a) <= 16.0 && fabs(b) <= 16.0 ? carrier_exact(a, b, j, km)
+                                                               : carrier_level(a, b, j, km));
+  }
 #pragma unroll
   for (int d = 0; d < NF / 4; ++d) {
     uint32_t v = 0u;
@@ -143,6 +148,25 @@ __device__ __forceinline__ void decode_lds(const uint32_t* w, const int8_t* tab_
   }
 }
 
+// 7- and 8-bit codes: chunk w[B] -> out[8], each carrier computed from the
+// group's (a, b). With a table of 2^B entries per row and group against the 32
+// codes a lane decodes per step, this is the cheaper side at these widths.
+template <int B>
+__device__ __forceinline__ void decode_direct(const uint32_t* w, float a, float b, uint32_t* out) {
+  constexpr int km = kmax_of(B);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = sign_extend(chunk_field<B>(w, 4 * q + i), B);
+      const int c = carrier_fast(a, b, k < 0 ? -k : k, km);
+      v |= carrier_byte(k < 0 ? -c : c) << (8 * i);
+    }
+    out[q] = v;
+  }
+}
+
 // The LDS table of one row and group: the four lanes of the row take every
 // fourth field value.
 template <int B>
@@ -208,25 +232,32 @@ __host__ __device__ inline A8Geom a8_geom(int64_t K, int group) {
   return g;
 }
 
+// nrg: 16-row groups per workgroup (four waves each); the groups share the
+// activation slices.
 template <int B>
-__host__ __device__ inline size_t a8_lds_bytes(const A8Geom& g, int mt) {
-  const size_t tab = A8Cfg<B>::kRegTable ? 0 : static_cast<size_t>(4) * 16 * (1 << B);
-  return static_cast<size_t>(4) * 16 * 16 * 4 +                                        // partials
-         static_cast<size_t>(4) * 16 * g.gmax * A8Cfg<B>::kGpDwords * 4 +              // group entries
-         tab + static_cast<size_t>(4) * mt * g.mpw * 128;                               // activations
+__host__ __device__ inline size_t a8_lds_bytes(const A8Geom& g, int mt, int nrg = 1) {
+  const size_t w = static_cast<size_t>(4) * nrg;
+  const size_t tab = (A8Cfg<B>::kRegTable || A8Cfg<B>::kDirect) ? 0 : w * 16 * (1 << B);
+  return w * 16 * 16 * 4 +                                                      // partials
+         w * 16 * g.gmax * A8Cfg<B>::kGpDwords * 4 +                            // group entries
+         tab + static_cast<size_t>(4) * mt * (g.mpw * 128 + 16);                // activations
 }
 
 // One workgroup per (touched expert slot, 16-row tile); slots past the touched
 // count exit at once. ALLIN: every step of a wave fits the load slots. DENSE:
 // the plain A8 product of p.dense_m activation rows with one weight (expert 0,
-// row m of x and of y for pair m; no routing): one workgroup per 16-row tile.
-template <int B, int MT, bool ALLIN, bool DENSE = false>
-__global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
+// row m of x and of y for pair m; no routing): one workgroup per tile of 16
+// NRG rows. With NRG = 2, waves 4..7 take the second 16 rows against the same
+// activation slices as waves 0..3 (the two groups stage half of the rows each).
+template <int B, int MT, bool ALLIN, bool DENSE = false, int NRG = 1>
+__global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
   using Cfg = A8Cfg<B>;
   constexpr int PS = Cfg::kSlots;
   constexpr int GPD = Cfg::kGpDwords;
+  constexpr int TR = 16 * NRG;                   // weight rows per tile
+  static_assert(NRG == 1 || (NRG == 2 && MT == 16), "two row groups share 16-row passes");
   extern __shared__ __align__(16) unsigned char smem[];
-  const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
+  const unsigned tiles = static_cast<unsigned>((p.N + TR - 1) / TR);
   const unsigned a = blockIdx.x / tiles;
   i32x8 rec;
   if constexpr (DENSE) {
@@ -235,24 +266,28 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
     rec = *reinterpret_cast<const i32x8*>(p.erec + 8 * a);
   }
   if (rec[2] == 0) return;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x - a * tiles) * 16;
+  const int64_t t0n = static_cast<int64_t>(blockIdx.x - a * tiles) * TR;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kq = wave & 3, rg = wave >> 2;       // K quarter, row group
+  const int64_t n0 = t0n + 16 * rg;
   const int nl = lane & 15, kb = lane >> 4;
   const A8Geom geo = a8_geom(p.K, p.group);
-  const int tb = wave * geo.nstep / 4, te = (wave + 1) * geo.nstep / 4;
+  const int tb = kq * geo.nstep / 4, te = (kq + 1) * geo.nstep / 4;
   const int g0 = tb / geo.spg;
   const int gn = te > tb ? (te - 1) / geo.spg - g0 + 1 : 0;
   const int gpr = static_cast<int>(p.K / p.group);
-  const int xrow_bytes = geo.mpw * 128;
+  // activation rows of a wave's slice, 16 bytes apart in bank position: the
+  // fragment reads of 16 different rows then hit different banks
+  const int xrow_bytes = geo.mpw * 128 + 16;
 
   float* red = reinterpret_cast<float*>(smem);
-  unsigned char* q = smem + 4 * 16 * 16 * 4;
+  unsigned char* q = smem + 4 * NRG * 16 * 16 * 4;
   uint32_t* gp_row = reinterpret_cast<uint32_t*>(q) + static_cast<int64_t>(wave * 16 + nl) * geo.gmax * GPD;
-  q += static_cast<size_t>(4) * 16 * geo.gmax * GPD * 4;
+  q += static_cast<size_t>(4) * NRG * 16 * geo.gmax * GPD * 4;
   int8_t* tab_row = reinterpret_cast<int8_t*>(q) + (wave * 16 + nl) * (1 << B);
-  if constexpr (!Cfg::kRegTable) q += static_cast<size_t>(4) * 16 * (1 << B);
-  int8_t* xw = reinterpret_cast<int8_t*>(q) + static_cast<int64_t>(wave) * MT * xrow_bytes;
+  if constexpr (!Cfg::kRegTable && !Cfg::kDirect) q += static_cast<size_t>(4) * NRG * 16 * (1 << B);
+  int8_t* xw = reinterpret_cast<int8_t*>(q) + static_cast<int64_t>(kq) * MT * xrow_bytes;
 
   const int e = rec[0], beg = rec[1], cnt = rec[2];
   const int64_t nrow = n0 + nl < p.N ? n0 + nl : p.N - 1;
@@ -296,12 +331,16 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
     for (int m = 0; m < MT; ++m)
       xv[m] = reinterpret_cast<const u32x4*>(p.xq + static_cast<int64_t>(pr[m] / p.topk) * p.K +
                                              static_cast<int64_t>(tb) * 128);
-    // activations first (unconditional, indices clamped), then the code stream
-    u32x4 xr[MT][2];
+    // Up to four rows a pass: the first activation vectors of each row first
+    // (unconditional, indices clamped), then the code stream. More rows copy
+    // their activations after the code loads are issued.
+    constexpr int XR = MT <= 4 ? 2 : 0;
+    static_assert(XR > 0 || MT % 4 == 0, "wide passes stage four rows at a time");
+    u32x4 xr[MT][XR > 0 ? XR : 1];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < XR; ++r) {
         const int i = lane + 64 * r;
         xr[m][r] = xv[m][i < nv ? i : 0];
       }
@@ -336,25 +375,55 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
       }
     }
     // this pass's activation rows into the wave's LDS slice
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m >= Mt) break;
+    auto put = [&](int m, int i, const u32x4& v) {
       u32x4* xo = reinterpret_cast<u32x4*>(xw + m * xrow_bytes);
-      auto put = [&](int i, const u32x4& v) {
-        if constexpr (B == 2) {
-          xo[i] = transpose16(v);
-        } else {
-          xo[i] = v;
-        }
-      };
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int i = lane + 64 * r;
-        if (i < nv) put(i, xr[m][r]);
+      if constexpr (B == 2) {
+        xo[i] = transpose16(v);
+      } else {
+        xo[i] = v;
       }
-      for (int i = lane + 128; i < nv; i += 64) put(i, xv[m][i]);
+    };
+    if constexpr (XR > 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m >= Mt) break;
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+          const int i = lane + 64 * r;
+          if (i < nv) put(m, i, xr[m][r]);
+        }
+        for (int i = lane + 64 * XR; i < nv; i += 64) put(m, i, xv[m][i]);
+      }
+    } else {
+      // four rows by two vectors a batch: eight loads in flight per lane; with
+      // two row groups each stages half of the rows
+#pragma unroll
+      for (int m0 = (MT / NRG) * rg; m0 < (MT / NRG) * (rg + 1); m0 += 4) {
+        if (m0 >= Mt) break;
+        for (int i0 = lane; i0 < nv; i0 += 128) {
+          u32x4 v[4][2];
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+              const int i = i0 + 64 * r;
+              v[m][r] = xv[m0 + m][i < nv ? i : 0];
+            }
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+              const int i = i0 + 64 * r;
+              if (m0 + m < Mt && i < nv) put(m0 + m, i, v[m][r]);
+            }
+        }
+      }
     }
-    wave_lds_order();
+    if constexpr (NRG > 1) {
+      __syncthreads();                           // the other row group's half of the rows
+    } else {
+      wave_lds_order();
+    }
 
     // the stream: int32 sums per group, fp32 across groups
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -363,6 +432,7 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
     float sc = 0.0f;
     int gi_next = 0, t_next = tb;                // next group entry and the step that opens it
     uint32_t T[Cfg::kRegTable ? (1 << B) / 4 : 1];
+    float ga = 0.0f, gb = 0.0f;                 // the open group's (a, b) (per-code carriers)
     const int ml = nl < Mt ? nl : 0;
     const int8_t* xa = xw + ml * xrow_bytes;
     for (int t0 = tb; t0 < te; t0 += PS) {
@@ -386,6 +456,9 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
                if constexpr (Cfg::kRegTable) {
 #pragma unroll
                  for (int d = 0; d < (1 << B) / 4; ++d) T[d] = ent[1 + d];
+               } else if constexpr (Cfg::kDirect) {
+                 ga = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ent[1] & 0xffffu)));
+                 gb = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ent[1] >> 16)));
                } else {
                  wave_lds_order();                // earlier reads of the old table stay ahead
                  build_lds_table<B>(tab_row, kb, ent[1]);
@@ -397,6 +470,8 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
                decode_w2(cb[u], T[0], car);
              } else if constexpr (Cfg::kRegTable) {
                decode_regs<B>(cb[u], T, car);
+             } else if constexpr (Cfg::kDirect) {
+               decode_direct<B>(cb[u], ga, gb, car);
              } else {
                decode_lds<B>(cb[u], tab_row, car);
              }
@@ -420,17 +495,19 @@ __global__ __launch_bounds__(256) void k_moe_a8(MoeA8Params p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kb + r) * 16 + nl] = acc[r];
     __syncthreads();
-    const int tt = threadIdx.x;
+    // thread tt of row group rg (tt / 256 = rg) sums that group's four partials
+    const int tt = threadIdx.x & 255;
     if (tt < Mt * 16) {
       const int m = tt >> 4, cc = tt & 15;
       if (n0 + cc < p.N) {
         int qp = pr[0];
 #pragma unroll
         for (int k = 1; k < MT; ++k) qp = m == k ? pr[k] : qp;
-        float v = red[(0 * 16 + m) * 16 + cc];
-        v += red[(1 * 16 + m) * 16 + cc];
-        v += red[(2 * 16 + m) * 16 + cc];
-        v += red[(3 * 16 + m) * 16 + cc];
+        const float* rr = red + rg * 4 * 16 * 16;
+        float v = rr[(0 * 16 + m) * 16 + cc];
+        v += rr[(1 * 16 + m) * 16 + cc];
+        v += rr[(2 * 16 + m) * 16 + cc];
+        v += rr[(3 * 16 + m) * 16 + cc];
         v *= p.xs[qp / p.topk];
         store_out(p.y, p.ybf16 != 0, static_cast<int64_t>(qp) * p.N + n0 + cc, v);
       }
@@ -472,6 +549,9 @@ bool moe_a8_supported(int64_t K, int bits, int group) {
     case 2: lds = a8_lds_bytes<2>(geo, 1); break;
     case 3: lds = a8_lds_bytes<3>(geo, 1); break;
     case 4: lds = a8_lds_bytes<4>(geo, 1); break;
+    case 5: lds = a8_lds_bytes<5>(geo, 1); break;
+    case 6: lds = a8_lds_bytes<6>(geo, 1); break;
+    case 7: lds = a8_lds_bytes<7>(geo, 1); break;
     default: lds = a8_lds_bytes<8>(geo, 1); break;
   }
   return lds <= 160 * 1024;
@@ -481,20 +561,29 @@ template <int B>
 hipError_t launch_gemv_a8_b(const MoeA8Params& p, hipStream_t st) {
   const A8Geom geo = a8_geom(p.K, p.group);
   const bool allin = geo.mpw <= A8Cfg<B>::kSlots;
-  // four rows per pass when the four activation slices fit, else one
-  int mt = p.dense_m <= 1 ? 1 : 4;
+  // Rows per pass: all 16 rows of the MFMA's activation side for more than
+  // four rows when their slices fit the LDS, else four, else one.
+  // 16-row passes take two 16-row groups per workgroup (eight waves) where both
+  // groups' tables fit: the 16 activation rows of a slice take most of the LDS,
+  // so one workgroup a compute unit, and 32 rows keep every tile in one round.
+  int mt = p.dense_m <= 1 ? 1 : (p.dense_m <= 4 ? 4 : 16);
+  int nrg = 1;
+  if (mt == 16 && a8_lds_bytes<B>(geo, 16, 2) <= 160 * 1024) nrg = 2;
+  if (mt == 16 && nrg == 1 && a8_lds_bytes<B>(geo, 16) > 160 * 1024) mt = 4;
   if (mt == 4 && a8_lds_bytes<B>(geo, 4) > 160 * 1024) mt = 1;
-  const size_t lds = a8_lds_bytes<B>(geo, mt);
+  const size_t lds = a8_lds_bytes<B>(geo, mt, nrg);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = mt == 1 ? (allin ? k_moe_a8<B, 1, true, true> : k_moe_a8<B, 1, false, true>)
-                      : (allin ? k_moe_a8<B, 4, true, true> : k_moe_a8<B, 4, false, true>);
+              : mt == 4 ? (allin ? k_moe_a8<B, 4, true, true> : k_moe_a8<B, 4, false, true>)
+              : nrg == 1 ? (allin ? k_moe_a8<B, 16, true, true> : k_moe_a8<B, 16, false, true>)
+                         : (allin ? k_moe_a8<B, 16, true, true, 2> : k_moe_a8<B, 16, false, true, 2>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  const int64_t tiles = (p.N + 15) / 16;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(256), lds, st, p);
+  const int64_t tiles = (p.N + 16 * nrg - 1) / (16 * nrg);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(256 * nrg), lds, st, p);
   return hipGetLastError();
 }
 

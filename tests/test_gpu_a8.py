@@ -107,6 +107,29 @@ def test_single_workload_a8():
     _check_a8(w, x)
 
 
+@pytest.mark.parametrize("bits,group,kind", [(2, 512, "ternary"), (4, 128, "uniform"), (8, 128, "uniform")])
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_a8_small_batch_full_shape(bits, group, kind, M):
+    """The small-batch A8 product at the gate_up expert shape (6144 x 7168), in
+    every launch configuration it takes there (one, four and sixteen rows a
+    pass): all rows against the oracle on the first and last 256 weight rows
+    and 64 spread ones."""
+    say(f"A8 small batch W{bits} G{group} gate_up 6144x7168 M={M}")
+    g = synth.make_generator(1700 + bits + M, DEV)
+    w = synth.make_weight(g, 6144, 7168, bits, group, kind, 0.02, DEV)
+    x = synth.activations(g, M, 7168, 0.005, 30.0, DEV)
+    cw = upload(w)
+    xq, sx = cq.act_quant_int8_per_token(x)
+    y = cq.cubic_gemm_a8(xq, sx, cw).cpu().numpy()
+    cols = np.unique(np.r_[0:256, 6144 - 256:6144, np.random.default_rng(M).integers(0, 6144, 64)])
+    codes, scales, shapes = np_weight(w)
+    xq_ref, sx_ref = oracle.act_quant(x_bits(x.cpu()))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    ref = oracle.gemm_a8(xq_ref, sx_ref, codes[cols], scales[cols], shapes[cols], bits, group)
+    err = row_rel_err(y[:, cols], ref)
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("bits,group", [(2, 128), (2, 256), (2, 512), (3, 128), (3, 256), (3, 512),
                                         (3, 1024), (4, 128), (5, 128), (6, 256), (7, 128), (8, 1024)])
 @pytest.mark.parametrize("M", [1, 4, 7, 16, 130, 300])
