@@ -3,6 +3,7 @@
 // stream. No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 
@@ -17,7 +18,12 @@ using namespace cubic;
 namespace {
 
 constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
-constexpr int64_t kGemvA8MaxM = 16;         // A8 rows taken by the routed kernel's organisation (passes of 4)
+// A8 rows taken by the routed kernel's organisation (passes of 16 rows): up to
+// 64 for 2- and 3-bit codes (the A8 tile kernel is faster beyond), 256 for
+// 4-bit codes, 128 for wider ones (measured on the expert shapes)
+constexpr int64_t gemv_a8_max_m(int bits) { return bits <= 3 ? 64 : (bits == 4 ? 256 : 128); }
+constexpr int64_t kSkinnyRows = 64;          // rows of one small-batch A16 pass
+constexpr int64_t kSkinnyPassMaxM = 256;     // A16 rows taken as passes of the small-batch kernel
 constexpr int64_t kGemvMaxM = 16;          // one MFMA activation tile
 constexpr int64_t kGemvMaxMW2 = 8;         // 2-bit codes: the small-batch kernel is faster above
 constexpr int64_t kInkMaxM = 4;            // single-kernel A16 path
@@ -190,6 +196,10 @@ int gemm_a16_impl(const uint16_t* x, bool xf16, int64_t M, const cubic_weight* w
   const bool use_gemv = M <= (w->bits == 2 ? kGemvMaxMW2 : kGemvMaxM) &&
                         gemv_supported(w->K, w->bits, w->group);
   const bool use_skinny = !use_gemv && skinny_supported(M, w->N, w->K, w->bits, w->group);
+  // up to kSkinnyPassMaxM rows: the small-batch kernel in passes of 64 rows
+  // (each pass streams the weight again; the tile kernels get too few tiles here)
+  const bool use_passes = !use_gemv && !use_skinny && M <= kSkinnyPassMaxM &&
+                          skinny_supported(kSkinnyRows, w->N, w->K, w->bits, w->group);
   if (use_gemv && w->bits > 2) {
     // 3- to 8-bit codes: the GEMV reads the caller's rows as they are (bf16:
     // against split bf16 levels; fp16: against fp16 levels)
@@ -214,6 +224,18 @@ int gemm_a16_impl(const uint16_t* x, bool xf16, int64_t M, const cubic_weight* w
   }
   TiledParams p{w->codes, w->scales, w->shapes, M, w->N, w->K, w->group, xa, xs, y, yb};
   if (use_skinny) return hip_status(launch_skinny_a16(p, w->bits, s));
+  if (use_passes) {
+    for (int64_t r0 = 0; r0 < M; r0 += kSkinnyRows) {
+      TiledParams q = p;
+      q.M = std::min(kSkinnyRows, M - r0);
+      q.xa = xa + r0 * w->K;
+      q.xs = xs ? xs + r0 : nullptr;
+      q.y = ybf16 ? reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(y) + r0 * w->N) : y + r0 * w->N;
+      const hipError_t e = launch_skinny_a16(q, w->bits, s);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    return CUBIC_OK;
+  }
   if (M >= kPrefillMinM && prefill_supported(M, w->N, w->K, w->bits, w->group))
     return hip_status(launch_prefill_a16(p, w->bits, s));
   return hip_status(launch_tiled_a16(p, w->bits, s));
@@ -241,9 +263,10 @@ int gemm_a8_impl(const int8_t* xq, const float* x_scale, int64_t M, const cubic_
   if ((M + 127) / 128 > 65535) return CUBIC_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->K == 0) return hip_status(launch_fill_zero(y, M * w->N, ybf16, s));
-  if (M <= kGemvA8MaxM && moe_a8_supported(w->K, w->bits, w->group) &&
+  if (M <= gemv_a8_max_m(w->bits) && moe_a8_supported(w->K, w->bits, w->group) &&
       cubic_code_bytes(w->N, w->K, w->bits) <= UINT32_MAX) {
-    // small M: the routed A8 kernel's organisation on one weight, no routing
+    // small M: the routed A8 kernel's organisation on one weight, no routing,
+    // in passes of 16 rows
     MoeA8Params q{};
     q.codes = w->codes;
     q.scales = w->scales;
@@ -300,11 +323,18 @@ CUBIC_API int cubic_gemm_a8_ex(const int8_t* xq, const float* x_scale, int64_t M
   return gemm_a8_impl(xq, x_scale, M, w, static_cast<float*>(y), y_dtype == CUBIC_DTYPE_BF16, stream);
 }
 
-constexpr int64_t kLinearA8MinM = 256;     // the measured crossover of 2- and 3-bit codes
+// The measured A16/A8 crossover of 2- and 3-bit codes on the expert shapes: A8
+// from 256 rows (its tile kernel), and in the 8..16-row window for long rows
+// (K >= 4096), where one 16-row A8 pass streams the weight once against the
+// A16 GEMV's one MFMA tile.
+constexpr int64_t kLinearA8MinM = 256;
+constexpr int64_t kLinearA8WindowLo = 8, kLinearA8WindowHi = 16, kLinearA8WindowMinK = 4096;
 
 CUBIC_API int cubic_linear_mode(int64_t M, int64_t N, int64_t K, int bits, int group) {
-  if ((bits == 2 || bits == 3) && M >= kLinearA8MinM && N > 0 && K > 0 && group > 0 &&
-      prefill_a8_supported(M, N, K, bits, group))
+  if (!(bits == 2 || bits == 3) || N <= 0 || K <= 0 || group <= 0) return CUBIC_MODE_A16;
+  if (M >= kLinearA8MinM && prefill_a8_supported(M, N, K, bits, group)) return CUBIC_MODE_A8;
+  if (M >= kLinearA8WindowLo && M <= kLinearA8WindowHi && K >= kLinearA8WindowMinK &&
+      moe_a8_supported(K, bits, group) && cubic_code_bytes(N, K, bits) <= UINT32_MAX)
     return CUBIC_MODE_A8;
   return CUBIC_MODE_A16;
 }

@@ -66,6 +66,13 @@ def test_linear_mode_rule_and_workspace():
     assert cq.cubic_linear_mode(256, 7168, 3072, 5, 128) == A16
     assert cq.cubic_linear_mode(4096, 256, 4096, 2, 2048) == A16     # group beyond the A8 kernel
     assert cq.cubic_linear_mode(0, 6144, 7168, 2, 512) == A16
+    # the small-batch window: 8..16 rows of long rows (K >= 4096), 2- and 3-bit codes
+    assert cq.cubic_linear_mode(8, 6144, 7168, 2, 512) == A8
+    assert cq.cubic_linear_mode(16, 6144, 7168, 3, 256) == A8
+    assert cq.cubic_linear_mode(7, 6144, 7168, 2, 512) == A16
+    assert cq.cubic_linear_mode(17, 6144, 7168, 2, 512) == A16
+    assert cq.cubic_linear_mode(12, 7168, 3072, 2, 512) == A16
+    assert cq.cubic_linear_mode(12, 6144, 7168, 4, 128) == A16
     # the larger of the A16 workspace and the A8 staging (xq, then x_scale, 256-aligned)
     assert cq.cubic_linear_workspace_bytes(1, 7168) == 7168 + 256
     assert cq.cubic_linear_workspace_bytes(4096, 7168) == max(

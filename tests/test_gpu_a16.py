@@ -61,7 +61,7 @@ def test_prefill_workload_full_sampled_rows():
 
 @pytest.mark.parametrize("bits,group", [(2, 512), (2, 128), (3, 128), (3, 256), (4, 128),
                                         (5, 256), (6, 128), (7, 128), (8, 256)])
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 9, 16, 17, 100])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 9, 16, 17, 65, 100, 256])
 def test_small_shapes_ragged(bits, group, M):
     # N not a multiple of 16 or of 128, K spanning several groups and waves
     say(f"A16 ragged bits={bits} G={group} M={M}")
@@ -73,7 +73,7 @@ def test_small_shapes_ragged(bits, group, M):
 
 
 @pytest.mark.parametrize("bits,group", [(5, 128), (6, 256), (7, 128), (8, 128), (8, 1024)])
-@pytest.mark.parametrize("M", [17, 32, 33, 64])
+@pytest.mark.parametrize("M", [17, 32, 33, 64, 130])
 def test_small_batch_wide_codes(bits, group, M):
     # 5- to 8-bit codes at 17..64 rows (the small-batch kernel: level tables up to
     # 6 bits, levels computed per code for 7 and 8 bits; one or two 32-row blocks);
@@ -86,13 +86,15 @@ def test_small_batch_wide_codes(bits, group, M):
 
 
 def test_small_batch_wide_codes_full_shape():
+    # 130 rows: three passes of the small-batch kernel (64, 64, 2 rows)
     for bits in (5, 8):
-        for M in (24, 64):
+        for M in (24, 64, 130):
             say(f"A16 small batch W{bits} G128 gate_up 6144x7168 M={M}")
             g = synth.make_generator(1600 + bits + M, DEV)
             w = synth.make_weight(g, 6144, 7168, bits, 128, "uniform", 0.02, DEV)
             x = synth.activations(g, M, 7168, 0.01, 50.0, DEV)
-            rows = np.unique(np.r_[0:3, M - 1, np.random.default_rng(M).integers(0, M, 4)])
+            rows = np.unique(np.r_[0:3, 63, 64, 127:M, np.random.default_rng(M).integers(0, M, 4)])
+            rows = rows[rows < M]
             _check_rows_cols(w, x, rows)
 
 

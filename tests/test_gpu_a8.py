@@ -132,7 +132,7 @@ def test_a8_small_batch_full_shape(bits, group, kind, M):
 
 @pytest.mark.parametrize("bits,group", [(2, 128), (2, 256), (2, 512), (3, 128), (3, 256), (3, 512),
                                         (3, 1024), (4, 128), (5, 128), (6, 256), (7, 128), (8, 1024)])
-@pytest.mark.parametrize("M", [1, 4, 7, 16, 130, 300])
+@pytest.mark.parametrize("M", [1, 4, 7, 16, 40, 130, 300])
 def test_a8_ragged(bits, group, M):
     say(f"A8 ragged bits={bits} G={group} M={M}")
     g = synth.make_generator(2000 + 10 * bits + M)

@@ -48,7 +48,7 @@ def _bf16_of(y32):
 # 2-bit codes the reordered rows), 33 and 64 the small-batch kernel (2- to 4-bit),
 # 300 the tiled kernel (or prefill where it applies), 17 with 5-bit codes the tiled.
 @pytest.mark.parametrize("bits,group", [(2, 512), (2, 128), (3, 128), (4, 128), (5, 256), (8, 128)])
-@pytest.mark.parametrize("M", [1, 4, 8, 16, 17, 33, 64, 300])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 17, 33, 64, 100, 300])
 def test_a16_fp16_activations(bits, group, M):
     say(f"A16 fp16 x bits={bits} G={group} M={M}")
     g = synth.make_generator(3000 + 10 * bits + M)
@@ -77,7 +77,7 @@ def test_prefill_fp16_activations(bits, group, M, N):
 
 
 @pytest.mark.parametrize("bits,group", [(2, 512), (3, 128), (4, 128), (6, 128)])
-@pytest.mark.parametrize("M", [1, 3, 8, 16, 40, 300])
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 40, 100, 300])
 def test_a16_bf16_outputs(bits, group, M):
     say(f"A16 bf16 out bits={bits} G={group} M={M}")
     g = synth.make_generator(3500 + 10 * bits + M)
@@ -114,7 +114,7 @@ def test_act_quant_fp16_bit_exact(M, K):
 
 
 @pytest.mark.parametrize("bits,group", [(2, 512), (3, 128), (3, 256)])
-@pytest.mark.parametrize("M", [1, 7, 300])
+@pytest.mark.parametrize("M", [1, 7, 40, 300])
 def test_a8_bf16_outputs(bits, group, M):
     say(f"A8 bf16 out bits={bits} G={group} M={M}")
     g = synth.make_generator(3700 + 10 * bits + M)

@@ -26,10 +26,11 @@ def test_a16_route_equals_gemm_a16(bits, group, M):
     assert torch.equal(cq.cubic_linear(x, cw), cq.cubic_gemm_a16(x, cw))
 
 
-@pytest.mark.parametrize("bits,group,M", [(3, 256, 300), (2, 512, 256), (3, 128, 513)])
-def test_a8_route_equals_quantiser_and_gemm_a8(bits, group, M):
-    say(f"linear A8 route bits={bits} G={group} M={M}")
-    N, K = 203, 1024
+@pytest.mark.parametrize("bits,group,M,K", [(3, 256, 300, 1024), (2, 512, 256, 1024), (3, 128, 513, 1024),
+                                            (2, 512, 12, 4096), (3, 256, 8, 4608)])
+def test_a8_route_equals_quantiser_and_gemm_a8(bits, group, M, K):
+    say(f"linear A8 route bits={bits} G={group} M={M} K={K}")
+    N = 203
     assert cq.cubic_linear_mode(M, N, K, bits, group) == cq.MODE_A8
     g = synth.make_generator(8200 + bits + M)
     w = synth.make_weight(g, N, K, bits, group, "ternary" if bits == 2 else "uniform", 0.02)
