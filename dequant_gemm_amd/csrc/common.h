@@ -312,6 +312,15 @@ __device__ __forceinline__ int row_prescale(float amax, float* back) {
   return 14 - e;
 }
 
+// 64-bit left shift of a register pair by a constant, as one v_lshlrev_b64
+// (the compiler otherwise splits a constant 64-bit shift into 32-bit ones).
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t v) {
+  uint64_t r;
+  asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(v));
+  return r;
+}
+
 // Orders this wave's earlier LDS writes before its later LDS reads. The LDS
 // executes one wave's instructions in order, so only the compiler must not
 // move memory accesses across this point; unlike a release fence it does not

@@ -13,6 +13,8 @@
 // fragments use the same order; slot_to_code() gives that order and the
 // activation staging code writes x in it.
 #pragma once
+#include <utility>
+
 #include "common.h"
 
 namespace cubic {
@@ -49,12 +51,19 @@ struct DecodeW2T {
   }
   // bit 2j+1 set iff field j of the word is 10 (code -2)
   __device__ static uint32_t extra_bits(uint32_t w) { return w & ~(w << 1) & 0xAAAAAAAAu; }
+  // r[i] and r[8 + i] come from one 64-bit shift of the pair w[1]:w[0]: the
+  // bits w[0] carries into w[1] land below bit 14 and are masked off.
   __device__ static void fast(const uint32_t* w, uint32_t* r) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r[8 * d + i] = (w[d] << (14 - 2 * i)) & 0xC000C000u;
-    }
+    const uint64_t v = (static_cast<uint64_t>(w[1]) << 32) | w[0];
+    auto one = [&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      const uint64_t t = shl64<14 - 2 * i>(v);
+      r[i] = static_cast<uint32_t>(t) & 0xC000C000u;
+      r[8 + i] = static_cast<uint32_t>(t >> 32) & 0xC000C000u;
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (one(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, 8>{});
   }
   // Fragments holding hi (rhi) and lo (rlo) at the halves whose field is 10
   // (code -2) and zero elsewhere; fast() contributes exactly 0 (-0.0) there.

@@ -122,33 +122,33 @@ __device__ __forceinline__ void load_dwords(const uint32_t* src, uint32_t* w) {
 
 // Accumulators of the streaming loop: the open group's MFMA partial (part, one
 // chain of MFMAs; several waves per SIMD hide their latency), the group-scaled
-// total (acc) and the current group's parameters. At a group boundary the
-// partial is scaled into acc and the group's first MFMA starts from zero
-// instead of a cleared register.
+// total (acc) and the current group's parameters. When a group opens, the
+// previous group's partial is scaled into acc and part is cleared; the macro
+// step that opens the next group is kept as a counter (no division per step).
 struct StreamState {
   f32x4 acc;
   f32x4 part;
-  bool fresh;                // the next MFMA opens a group: its C input is zero
   float gscale;
   uint32_t gab;
   int gcur;
+  int tnext;                 // the macro step at which the next group opens
   float ca, cb, cc;          // Horner coefficients of the group (direct-level decoders)
-  __device__ __forceinline__ void reset() {
+  // tb: the first macro step streamed (in order from there), g0 its group
+  __device__ __forceinline__ void reset(int tb, int g0) {
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
     part = f32x4{0.f, 0.f, 0.f, 0.f};
-    fresh = true;
     gscale = 0.0f;
     gab = 0u;
-    gcur = -1;
+    gcur = g0 - 1;
+    tnext = tb;
   }
   template <bool BF16>
   __device__ __forceinline__ void mac(const u32x4& a, const u32x4& b) {
-    part = mfma16<BF16>(a, b, fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : part);
-    fresh = false;
+    part = mfma16<BF16>(a, b, part);
   }
   // fold the open group's partial into acc
   __device__ __forceinline__ f32x4 total() const {
-    return fresh ? acc : acc + gscale * part;
+    return acc + gscale * part;
   }
 };
 
@@ -161,10 +161,11 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
                                            const u32x4 (*xa)[4], int t, int g0, int ml) {
   constexpr int B = Dec::kBits;
   const int kb = c.kb, nl = c.nl;
-  const int g = t / c.mpg;
-  if (g != st.gcur) {                    // wave-uniform
-    if (!st.fresh) st.acc += st.gscale * st.part;
-    st.fresh = true;
+  if (t == st.tnext) {                   // wave-uniform: a group opens
+    const int g = st.gcur + 1;
+    st.tnext = (g + 1) * c.mpg;
+    st.acc += st.gscale * st.part;       // the previous group (zero before the first)
+    st.part = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t* gp = c.gp_wave + (nl * c.gmax + (g - g0)) * 2;
     st.gscale = __uint_as_float(gp[0]) * Dec::kLevelUnit;
     st.gab = gp[1];
@@ -182,7 +183,12 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
   if constexpr (IsW2<Dec>::value) {
     uint32_t ex = 0;
 #pragma unroll
-    for (int d = 0; d < B * SPL; ++d) ex |= w[d] & ~(w[d] << 1);
+    for (int d = 0; d < B * SPL; d += 2) {
+      // w[d + 1]:w[d] shifted left by one as a pair; the bit carried into
+      // w[d + 1] lands on an even (masked) position
+      const uint64_t sv = shl64<1>((static_cast<uint64_t>(w[d + 1]) << 32) | w[d]);
+      ex |= (w[d] & ~static_cast<uint32_t>(sv)) | (w[d + 1] & ~static_cast<uint32_t>(sv >> 32));
+    }
     extra = __any((ex & 0xAAAAAAAAu) != 0u);
   }
 #pragma unroll
@@ -329,7 +335,7 @@ __device__ __forceinline__ f32x4 gemv_core(const CoreArgs& c, IssueX&& issue_x, 
   wave_lds_order();
 
   StreamState st;
-  st.reset();
+  st.reset(tb, g0);
   const int ml = nl < c.M ? nl : 0;
   for (int t0 = tb; t0 < te; t0 += P) {
     [&]<int... U>(std::integer_sequence<int, U...>) {

@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
 
     // stream the current unit; each slot is refilled with the next unit's step
     StreamState st;
-    st.reset();
+    st.reset(tb, g0);
     const int ml = nl < cur.M ? nl : 0;
     const uint32_t* crow_n = code_row(nxt);
     [&]<int... U>(std::integer_sequence<int, U...>) {
