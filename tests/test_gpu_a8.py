@@ -107,6 +107,20 @@ def test_single_workload_a8():
     _check_a8(w, x)
 
 
+@pytest.mark.parametrize("bits,group", [(2, 512), (3, 256), (5, 128), (8, 1024)])
+@pytest.mark.parametrize("M", [5, 16, 40])
+def test_a8_small_batch_long_rows(bits, group, M):
+    """K = 16384: sixteen activation rows of a K quarter no longer fit the LDS, so
+    the small-batch A8 kernel falls back to four-row passes; N = 75 leaves a
+    ragged last tile."""
+    say(f"A8 small batch long rows bits={bits} G={group} M={M}")
+    g = synth.make_generator(2600 + 10 * bits + M)
+    kind = "ternary" if bits == 2 else "uniform"
+    w = synth.make_weight(g, 75, 16384, bits, group, kind, 0.02)
+    x = synth.activations(g, M, 16384, 0.005, 30.0)
+    _check_a8(w, x)
+
+
 @pytest.mark.parametrize("bits,group,kind", [(2, 512, "ternary"), (4, 128, "uniform"), (8, 128, "uniform")])
 @pytest.mark.parametrize("M", [1, 5, 16])
 def test_a8_small_batch_full_shape(bits, group, kind, M):
