@@ -19,9 +19,9 @@ namespace {
 
 constexpr size_t kLdsLimit = 160 * 1024;   // LDS of one gfx950 compute unit
 // A8 rows taken by the routed kernel's organisation (passes of 16 rows): up to
-// 64 for 2- and 3-bit codes (the A8 tile kernel is faster beyond), 256 for
+// 32 for 2- and 3-bit codes (the A8 tile kernel is faster beyond), 256 for
 // 4-bit codes, 128 for wider ones (measured on the expert shapes)
-constexpr int64_t gemv_a8_max_m(int bits) { return bits <= 3 ? 64 : (bits == 4 ? 256 : 128); }
+constexpr int64_t gemv_a8_max_m(int bits) { return bits <= 3 ? 32 : (bits == 4 ? 256 : 128); }
 constexpr int64_t kSkinnyRows = 64;          // rows of one small-batch A16 pass
 constexpr int64_t kSkinnyPassMaxM = 256;     // A16 rows taken as passes of the small-batch kernel
 constexpr int64_t kGemvMaxM = 16;          // one MFMA activation tile
@@ -324,10 +324,10 @@ CUBIC_API int cubic_gemm_a8_ex(const int8_t* xq, const float* x_scale, int64_t M
 }
 
 // The measured A16/A8 crossover of 2- and 3-bit codes on the expert shapes: A8
-// from 256 rows (its tile kernel), and in the 8..16-row window for long rows
+// from 128 rows (its tile kernel), and in the 8..16-row window for long rows
 // (K >= 4096), where one 16-row A8 pass streams the weight once against the
 // A16 GEMV's one MFMA tile.
-constexpr int64_t kLinearA8MinM = 256;
+constexpr int64_t kLinearA8MinM = 128;
 constexpr int64_t kLinearA8WindowLo = 8, kLinearA8WindowHi = 16, kLinearA8WindowMinK = 4096;
 
 CUBIC_API int cubic_linear_mode(int64_t M, int64_t N, int64_t K, int bits, int group) {

@@ -40,7 +40,7 @@ namespace cubic {
 namespace {
 
 constexpr int A8N = 128;             // weight rows per tile
-constexpr int A8M = 256;             // activation rows per tile
+constexpr int A8M = 256;             // activation rows per tile (NB = 8 blocks of 32)
 constexpr int A8K = 128;             // K per step
 constexpr int kA8Threads = 256;
 constexpr int kA8Stages = 4;
@@ -49,11 +49,12 @@ constexpr uint32_t kA8RsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data form
 // Stage layout: activations [A8M][A8K] int8, then the code words of the tile's
 // A8N rows (A8K B / 8 bytes each, row-major), then group parameters (per wave
 // 512 bytes: 64 scales, 64 (a, b) words; lanes 32..63 repeat rows 0..31).
-constexpr size_t kA8XBytes = static_cast<size_t>(A8M) * A8K;
+// NB: 32-row activation blocks per tile (8: 256 rows; 2: 64 rows for small M).
+constexpr size_t a8_x_bytes(int NB) { return static_cast<size_t>(32 * NB) * A8K; }
 constexpr size_t a8_code_bytes(int B) { return static_cast<size_t>(A8N) * A8K * B / 8; }
 constexpr size_t kA8ParamBytes = 4 * 512;
-constexpr size_t a8_stage_bytes(int B) { return kA8XBytes + a8_code_bytes(B) + kA8ParamBytes; }
-constexpr size_t a8_lds_bytes(int B) { return kA8Stages * a8_stage_bytes(B); }
+constexpr size_t a8_stage_bytes(int B, int NB) { return a8_x_bytes(NB) + a8_code_bytes(B) + kA8ParamBytes; }
+constexpr size_t a8_lds_bytes(int B, int NB) { return kA8Stages * a8_stage_bytes(B, NB); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t a8_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
@@ -201,42 +202,51 @@ __device__ __forceinline__ int a8_slot(int r, int q) {
 }
 
 // SPG: steps per group when it is 1 or 2 (then known for each of the four
-// unrolled steps), or 0 for any group length (decided at run time).
-template <int B, int SPG>
+// unrolled steps), or 0 for any group length (decided at run time). NB: 32-row
+// activation blocks per tile (8, or 2 for small M). With gridDim.y = 2 the two
+// workgroups of a tile take the first and the second half of the groups and
+// add their results into y, which holds zeros before (fp32 only): the two
+// additions onto zero give the same sum in either order.
+template <int B, int SPG, int NB>
 __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   extern __shared__ __align__(16) unsigned char smem[];       // kA8Stages stages
   constexpr int DPR = A8K * B / 32;             // code dwords per row and step
-  constexpr size_t kStage = a8_stage_bytes(B);
-  constexpr size_t kCodeOff = kA8XBytes;
-  constexpr size_t kParamOff = kA8XBytes + a8_code_bytes(B);
+  constexpr int AM = 32 * NB;                   // activation rows per tile
+  constexpr size_t kStage = a8_stage_bytes(B, NB);
+  constexpr size_t kCodeOff = a8_x_bytes(NB);
+  constexpr size_t kParamOff = a8_x_bytes(NB) + a8_code_bytes(B);
+  static_assert(NB == 2 || NB == 4 || NB == 8, "even block counts keep the row-parity swizzle");
 
   const int tiles_n = static_cast<int>((p.N + A8N - 1) / A8N);
-  const int ntiles = tiles_n * static_cast<int>((p.M + A8M - 1) / A8M);
+  const int ntiles = tiles_n * static_cast<int>((p.M + AM - 1) / AM);
   int t = static_cast<int>(blockIdx.x);
   // consecutive workgroup ids go to different XCDs: give each XCD a contiguous
   // run of tiles (which share activation rows) when the count divides
   if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
-  const int64_t m0 = static_cast<int64_t>(t / tiles_n) * A8M;
+  const int64_t m0 = static_cast<int64_t>(t / tiles_n) * AM;
   const int64_t n0 = static_cast<int64_t>(t % tiles_n) * A8N;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, h = lane >> 5;
   const int gpr = static_cast<int>(p.K / p.group);
-  const int nsteps = static_cast<int>(p.K / A8K);
   const int spg = SPG != 0 ? SPG : p.group / A8K;
+  // this workgroup's steps [sb, se): whole groups, split gridDim.y ways
+  const int split = NB == 8 ? 1 : static_cast<int>(gridDim.y);   // 256-row tiles: never split
+  const int z = NB == 8 ? 0 : static_cast<int>(blockIdx.y);
+  const int sb = (z * gpr / split) * spg, se = ((z + 1) * gpr / split) * spg;
   const uint32_t row_bytes = static_cast<uint32_t>(p.K * B / 8);
   const int64_t nrow = n0 + 32 * wave + c;      // this lane's weight row
 
   // ---- the step's loads: global -> LDS stage ----
-  // activations: wave w fills slots 512 w + 64 i + lane (i = 0..7), 16 bytes
-  // each: row r = 64 w + 8 i + lane / 8, chunk (lane % 8) ^ (r % 8) ^ (i % 2)
-  // (the inverse of a8_slot), so the offset is one of two per-lane bases (by
-  // the parity of i) plus 8 i K. Rows past M read 0.
+  // activations: wave w fills slots 64 NB w + 64 i + lane (i < NB), 16 bytes
+  // each: row r = 8 NB w + 8 i + lane / 8, chunk (lane % 8) ^ (r % 8) ^ (i % 2)
+  // (the inverse of a8_slot; NB is even), so the offset is one of two per-lane
+  // bases (by the parity of i) plus 8 i K. Rows past M read 0.
   const __amdgpu_buffer_rsrc_t xrs = a8_rsrc(p.xa, static_cast<uint32_t>(p.M * p.K));
   uint32_t abase[2];
   {
-    const int64_t r = m0 + 64 * wave + (lane >> 3);
+    const int64_t r = m0 + 8 * NB * wave + (lane >> 3);
     const int q = (lane & 7) ^ ((lane >> 3) & 7);
     abase[0] = static_cast<uint32_t>(r * p.K + 16 * q);
     abase[1] = static_cast<uint32_t>(r * p.K + 16 * (q ^ 1));
@@ -257,29 +267,30 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   const __amdgpu_buffer_rsrc_t srs = a8_rsrc(p.scales, static_cast<uint32_t>(p.N * gpr * 4));
   const __amdgpu_buffer_rsrc_t brs = a8_rsrc(p.shapes, static_cast<uint32_t>(p.N * gpr * 4));
   const uint32_t poff = static_cast<uint32_t>(pc * gpr * 4);
-  constexpr int NV = 8 + NC + 2;                // loads per wave and step
-  static_assert(NV <= 16, "one code or parameter load per MFMA slot of a sub-step");
+  constexpr int NV = NB + NC + 2;               // loads per wave and step
+  static_assert(NC + 2 <= 8, "one code or parameter load per slot of a sub-step");
   static_assert(3 * NV < 64, "vmcnt holds at most 63");
   // Load i (0 .. NV - 1) of step s into a stage. The parameter slots of step
   // s hold the group after the one step s belongs to (read in that group's
-  // last step to prepare the next carriers). Past K, step 0 is loaded again
-  // into a stage nobody reads, so that the load count per step stays fixed.
+  // last step to prepare the next carriers). Past the workgroup's steps, its
+  // first step is loaded again into a stage nobody reads, so that the load
+  // count per step stays fixed.
   auto issue_load = [&](int s, int stage, int i) {
     unsigned char* st = smem + stage * kStage;
-    const int sv = s < nsteps ? s : 0;
-    if (i < 8) {
+    const int sv = s < se ? s : sb;
+    if (i < NB) {
       const uint32_t ko = static_cast<uint32_t>(8 * i) * static_cast<uint32_t>(p.K) +
                           static_cast<uint32_t>(sv) * A8K;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, st + wave * 8192 + i * 1024, 16, abase[i & 1] + ko,
-                                               0, 0, 0);
-    } else if (i < 8 + NC) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * (NC * wave + i - 8), 4,
-                                               coff[i - 8] + static_cast<uint32_t>(sv) * (4 * DPR),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, st + wave * (NB * 1024) + i * 1024, 16,
+                                               abase[i & 1] + ko, 0, 0, 0);
+    } else if (i < NB + NC) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, st + kCodeOff + 256 * (NC * wave + i - NB), 4,
+                                               coff[i - NB] + static_cast<uint32_t>(sv) * (4 * DPR),
                                                0, 0, 0);
     } else {
       int g = sv / spg + 1;
       g = g < gpr ? g : gpr - 1;
-      const bool ab = i == 8 + NC + 1;
+      const bool ab = i == NB + NC + 1;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ab ? brs : srs, st + kParamOff + 512 * wave + (ab ? 256 : 0),
                                                4, poff + 4u * static_cast<uint32_t>(g), 0, 0, 0);
     }
@@ -289,10 +300,10 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
     for (int i = 0; i < NV; ++i) issue_load(s, stage, i);
   };
 
-  i32x16 acc[8];                                // int32 sums of the open group
-  f32x16 accf[8];
+  i32x16 acc[NB];                               // int32 sums of the open group
+  f32x16 accf[NB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       acc[j][e] = 0;
@@ -303,15 +314,16 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   uint32_t t0 = 0u, t1 = 0u;                    // carriers of the group being decoded
   float sc = 0.0f;                              // s / 127 of the group in the int32 sums
   {
-    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b32(srs, poff, 0, 0);
-    const uint32_t ab = __builtin_amdgcn_raw_buffer_load_b32(brs, poff, 0, 0);
+    const uint32_t go = poff + 4u * static_cast<uint32_t>(sb / spg);   // the first group
+    const uint32_t sbits = __builtin_amdgcn_raw_buffer_load_b32(srs, go, 0, 0);
+    const uint32_t ab = __builtin_amdgcn_raw_buffer_load_b32(brs, go, 0, 0);
     CarrierBuild cb;
 #pragma unroll
-    for (int piece = 0; piece < 4; ++piece) carrier_piece<B>(cb, piece, ab, sb, t0, t1, sc);
+    for (int piece = 0; piece < 4; ++piece) carrier_piece<B>(cb, piece, ab, sbits, t0, t1, sc);
   }
-  issue_step(0, 0);
-  issue_step(1, 1);
-  issue_step(2, 2);
+  issue_step(sb, 0);
+  issue_step(sb + 1, 1);
+  issue_step(sb + 2, 2);
   __builtin_amdgcn_s_waitcnt(a8_wait_vm(2 * NV));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   // step 3: its activation loads here (they belong to the last sub-step of
   // step -1), its code and parameter loads in the first sub-step of step 0
 #pragma unroll
-  for (int i = 0; i < 8; ++i) issue_load(3, 3, i);
+  for (int i = 0; i < NB; ++i) issue_load(sb + 3, 3, i);
 
   uint32_t cw[2 * B];                           // this lane's 64 codes of the current step
   auto read_codes = [&](const unsigned char* st, uint32_t* w) {
@@ -335,11 +347,11 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   auto read_a = [&](const unsigned char* st, uint32_t xl, int ks, int j) {
     return *reinterpret_cast<const i32x4*>(st + (xl ^ (16u * ks)) + 4096 * j);
   };
-  i32x4 fa[8];
+  i32x4 fa[NB];
   i32x4 fb;
   read_codes(smem, cw);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) fa[j] = read_a(smem, xlane, 0, j);
+  for (int j = 0; j < NB; ++j) fa[j] = read_a(smem, xlane, 0, j);
   {
     uint32_t o[4];
 #pragma unroll
@@ -390,24 +402,27 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
       const uint32_t d1 = ks < 3 ? t1 : (last ? t1n : t1);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
+        // slot u: block u's MFMA (u < NB), then a share of the other work
         if constexpr (restart) {
-          // the finished group's sums of block u: out before the MFMA restarts
-          // them, into fp32 beside it (exact: |sum| < 2^24)
-          float f[16];
+          if (u < NB) {
+            // the finished group's sums of block u: out before the MFMA restarts
+            // them, into fp32 beside it (exact: |sum| < 2^24)
+            float f[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) f[e] = static_cast<float>(acc[u][e]);
-          hold16(f, fa[u]);
-          acc[u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[u], fb, i32x16{}, 0, 0, 0);
+            for (int e = 0; e < 16; ++e) f[e] = static_cast<float>(acc[u][e]);
+            hold16(f, fa[u]);
+            acc[u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[u], fb, i32x16{}, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float v = fmaf(f[e], sc_prev, accf[u][e]);
-            pin(v);
-            accf[u][e] = v;
+            for (int e = 0; e < 16; ++e) {
+              float v = fmaf(f[e], sc_prev, accf[u][e]);
+              pin(v);
+              accf[u][e] = v;
+            }
           }
         } else {
-          acc[u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[u], fb, acc[u], 0, 0, 0);
+          if (u < NB) acc[u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[u], fb, acc[u], 0, 0, 0);
         }
-        fa[u] = ks < 3 ? read_a(st, xl, ks + 1, u) : read_a(stn, xl, 0, u);
+        if (u < NB) fa[u] = ks < 3 ? read_a(st, xl, ks + 1, u) : read_a(stn, xl, 0, u);
         // decode of the next sub-step's fragment: quad piece u (sub-steps 0..2),
         // or from slot 1 on once the next step's codes are read (sub-step 3)
         if (ks < 3) {
@@ -420,8 +435,8 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
         // refill of the stage freed by the barrier of step s - 1 or s: the
         // activation loads of step s + 4 in the last sub-step, the code and
         // parameter loads of step s + 3 in the first (one load per slot)
-        if (ks == 3) issue_load(s + 4, ph, u);
-        if (ks == 0 && 8 + u < NV) issue_load(s + 3, (ph + 3) % 4, 8 + u);
+        if (ks == 3 && u < NB) issue_load(s + 4, ph, u);
+        if (ks == 0 && NB + u < NV) issue_load(s + 3, (ph + 3) % 4, NB + u);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ks == 2) {
@@ -454,19 +469,19 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
     }
     mg = last ? 0 : mg + 1;
   };
-  int s = 0;
-  for (; s + 3 < nsteps; s += 4) {
+  int s = sb;
+  for (; s + 3 < se; s += 4) {
     step(s, std::integral_constant<int, 0>{});
     step(s + 1, std::integral_constant<int, 1>{});
     step(s + 2, std::integral_constant<int, 2>{});
     step(s + 3, std::integral_constant<int, 3>{});
   }
-  if (s < nsteps) step(s, std::integral_constant<int, 0>{});
-  if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
-  if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
+  if (s < se) step(s, std::integral_constant<int, 0>{});
+  if (s + 1 < se) step(s + 1, std::integral_constant<int, 1>{});
+  if (s + 2 < se) step(s + 2, std::integral_constant<int, 2>{});
   // the last group's sums (its scale moved to sc_prev at its last step)
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) accf[j][e] = fmaf(static_cast<float>(acc[j][e]), sc_prev, accf[j][e]);
   __builtin_amdgcn_s_waitcnt(0);               // loads past K target stages nobody reads
@@ -481,12 +496,19 @@ __global__ __launch_bounds__(kA8Threads, 1) void k_prefill_a8(TiledParams p) {
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NB; ++j) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int ml = 32 * j + 8 * (e >> 2) + 4 * h + (e & 3);
       const int64_t m = m0 + ml;
-      if (m < p.M && nrow < p.N) store_out(p.y, p.ybf16 != 0, m * p.N + nrow, accf[j][e] * sxs[ml]);
+      if (m < p.M && nrow < p.N) {
+        const float v = accf[j][e] * sxs[ml];
+        if (split > 1) {
+          atomicAdd(p.y + m * p.N + nrow, v);
+        } else {
+          store_out(p.y, p.ybf16 != 0, m * p.N + nrow, v);
+        }
+      }
     }
   }
 }
@@ -506,26 +528,45 @@ bool prefill_a8_supported(int64_t M, int64_t N, int64_t K, int bits, int group) 
   return tiles <= INT32_MAX;
 }
 
-template <int B, int SPG>
-static hipError_t launch_prefill_a8_k(const TiledParams& p, hipStream_t st) {
-  auto kern = k_prefill_a8<B, SPG>;
-  constexpr size_t lds = a8_lds_bytes(B);
+template <int B, int SPG, int NB>
+static hipError_t launch_prefill_a8_k(const TiledParams& p, int split, hipStream_t st) {
+  auto kern = k_prefill_a8<B, SPG, NB>;
+  constexpr size_t lds = a8_lds_bytes(B, NB);
   static_assert(lds <= 160 * 1024, "one compute unit's LDS");
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  const int64_t tiles = ((p.M + A8M - 1) / A8M) * ((p.N + A8N - 1) / A8N);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(kA8Threads), lds, st, p);
+  const int64_t tiles = ((p.M + 32 * NB - 1) / (32 * NB)) * ((p.N + A8N - 1) / A8N);
+  if (split > 1) {
+    const hipError_t z = launch_fill_zero(p.y, p.M * p.N, false, st);   // the two halves add into y
+    if (z != hipSuccess) return z;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(split)), dim3(kA8Threads),
+                     lds, st, p);
   return hipGetLastError();
+}
+
+// Tiles of 256 activation rows while they fill the compute units; below that,
+// tiles of 64 rows, and the groups split between two workgroups per tile while
+// the 64-row tiles fill at most three quarters of the compute units (fp32
+// output only; measured on the expert shapes).
+template <int B, int SPG>
+static hipError_t launch_prefill_a8_s(const TiledParams& p, hipStream_t st) {
+  const int64_t cus = device_cu_count();
+  const int64_t tn = (p.N + A8N - 1) / A8N;
+  if (((p.M + 255) / 256) * tn >= cus) return launch_prefill_a8_k<B, SPG, 8>(p, 1, st);
+  const int64_t t2 = ((p.M + 63) / 64) * tn;
+  const int split = (4 * t2 <= 3 * cus && p.ybf16 == 0 && p.K / p.group >= 2) ? 2 : 1;
+  return launch_prefill_a8_k<B, SPG, 2>(p, split, st);
 }
 
 template <int B>
 static hipError_t launch_prefill_a8_b(const TiledParams& p, hipStream_t st) {
   const int spg = p.group / A8K;
-  if (spg == 1) return launch_prefill_a8_k<B, 1>(p, st);
-  if (spg == 2) return launch_prefill_a8_k<B, 2>(p, st);
-  return launch_prefill_a8_k<B, 0>(p, st);
+  if (spg == 1) return launch_prefill_a8_s<B, 1>(p, st);
+  if (spg == 2) return launch_prefill_a8_s<B, 2>(p, st);
+  return launch_prefill_a8_s<B, 0>(p, st);
 }
 
 hipError_t launch_prefill_a8(const TiledParams& p, int bits, hipStream_t st) {

@@ -212,7 +212,7 @@ int cubic_gemm_a8_ex(const int8_t* xq, const float* x_scale, int64_t M,
  * section and its kernel comparison: A16 serves decode-sized batches best, the
  * integer path once each decoded weight serves enough rows). The rule is
  * static and comes from the A16-vs-A8 sweep of this library on MI355X:
- * Dynamic A8 for 2- and 3-bit codes with M >= 256 (where its prefill kernel
+ * Dynamic A8 for 2- and 3-bit codes with M >= 128 (where its tile kernel
  * runs) or with 8 <= M <= 16 and K >= 4096 (one 16-row pass of its small-batch
  * kernel), A16 otherwise. The modes differ in numerics (A8 quantises the
  * activations); cubic_linear_mode tells which one a shape takes. It is a host

@@ -59,8 +59,8 @@ def test_linear_mode_rule_and_workspace():
     # Dynamic A8 for 2- and 3-bit codes from 256 rows on (the measured crossover), A16 otherwise
     A16, A8 = cq.MODE_A16, cq.MODE_A8
     assert cq.cubic_linear_mode(1, 6144, 7168, 2, 512) == A16
-    assert cq.cubic_linear_mode(255, 6144, 7168, 2, 512) == A16
-    assert cq.cubic_linear_mode(256, 6144, 7168, 2, 512) == A8
+    assert cq.cubic_linear_mode(127, 6144, 7168, 2, 512) == A16
+    assert cq.cubic_linear_mode(128, 6144, 7168, 2, 512) == A8
     assert cq.cubic_linear_mode(4096, 6144, 7168, 3, 256) == A8
     assert cq.cubic_linear_mode(4096, 6144, 7168, 4, 128) == A16
     assert cq.cubic_linear_mode(256, 7168, 3072, 5, 128) == A16

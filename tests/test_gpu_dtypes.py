@@ -124,7 +124,19 @@ def test_a8_bf16_outputs(bits, group, M):
     xq, sx = cq.act_quant_int8_per_token(x)
     y = cq.cubic_gemm_a8(xq, sx, cw)
     yb = cq.cubic_gemm_a8(xq, sx, cw, out_dtype=torch.bfloat16)
-    assert torch.equal(yb, _bf16_of(y))
+    if M <= 32:
+        assert torch.equal(yb, _bf16_of(y))
+    else:
+        # the tile kernel's fp32 result at these sizes adds two K halves (two
+        # workgroups per tile), the bf16 result rounds the unsplit sum: they
+        # may differ by the fp32 order, so one bf16 unit at most
+        yr = _bf16_of(y).float()
+        bound = torch.maximum(yb.float().abs(), yr.abs()) * 2.0 ** -7     # one bf16 unit
+        assert bool(((yb.float() - yr).abs() <= bound).all())
+        codes, scales, shapes = np_weight(w)
+        xq_ref, sx_ref = oracle.act_quant(x_bits(x))
+        ref = oracle.gemm_a8(xq_ref, sx_ref, codes, scales, shapes, bits, group)
+        assert row_rel_err(yb.float().cpu().numpy(), ref) <= TOL + 2.0 ** -8   # bf16 rounding on top
 
 
 def test_prefill_a8_workload_bf16_output_full():

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-@pytest.mark.parametrize("bits,group,M", [(3, 128, 100), (2, 512, 255), (4, 128, 300), (5, 128, 16)])
+@pytest.mark.parametrize("bits,group,M", [(3, 128, 100), (2, 512, 127), (4, 128, 300), (5, 128, 16)])
 def test_a16_route_equals_gemm_a16(bits, group, M):
     say(f"linear A16 route bits={bits} G={group} M={M}")
     N, K = 203, 1024
@@ -26,7 +26,7 @@ def test_a16_route_equals_gemm_a16(bits, group, M):
     assert torch.equal(cq.cubic_linear(x, cw), cq.cubic_gemm_a16(x, cw))
 
 
-@pytest.mark.parametrize("bits,group,M,K", [(3, 256, 300, 1024), (2, 512, 256, 1024), (3, 128, 513, 1024),
+@pytest.mark.parametrize("bits,group,M,K", [(3, 256, 300, 1024), (2, 512, 128, 1024), (3, 128, 513, 1024),
                                             (2, 512, 12, 4096), (3, 256, 8, 4608)])
 def test_a8_route_equals_quantiser_and_gemm_a8(bits, group, M, K):
     say(f"linear A8 route bits={bits} G={group} M={M} K={K}")
