@@ -216,18 +216,21 @@ __device__ __forceinline__ i32x4 mfma_i8(const u32x4& a, const u32x4& b, const i
 }
 
 // Geometry shared by the kernel and its launcher.
+// A step is 128 sub codes of a row: each lane takes sub 32-code chunks of it
+// (sub = 2 for 2-bit codes when K and the group are multiples of 256, so that a
+// lane's code load is 16 bytes).
 struct A8Geom {
-  int nstep;   // 128-code steps per row
+  int nstep;   // steps per row
   int mpw;     // steps reserved per wave
   int spg;     // steps per group
   int gmax;    // groups a wave can span
 };
 
-__host__ __device__ inline A8Geom a8_geom(int64_t K, int group) {
+__host__ __device__ inline A8Geom a8_geom(int64_t K, int group, int sub = 1) {
   A8Geom g;
-  g.nstep = static_cast<int>(K / 128);
+  g.nstep = static_cast<int>(K / (128 * sub));
   g.mpw = (g.nstep + 3) / 4;
-  g.spg = group / 128;
+  g.spg = group / (128 * sub);
   g.gmax = (g.mpw + g.spg - 1) / g.spg + 1;
   return g;
 }
@@ -235,12 +238,12 @@ __host__ __device__ inline A8Geom a8_geom(int64_t K, int group) {
 // nrg: 16-row groups per workgroup (four waves each); the groups share the
 // activation slices.
 template <int B>
-__host__ __device__ inline size_t a8_lds_bytes(const A8Geom& g, int mt, int nrg = 1) {
+__host__ __device__ inline size_t a8_lds_bytes(const A8Geom& g, int mt, int nrg = 1, int sub = 1) {
   const size_t w = static_cast<size_t>(4) * nrg;
   const size_t tab = (A8Cfg<B>::kRegTable || A8Cfg<B>::kDirect) ? 0 : w * 16 * (1 << B);
   return w * 16 * 16 * 4 +                                                      // partials
          w * 16 * g.gmax * A8Cfg<B>::kGpDwords * 4 +                            // group entries
-         tab + static_cast<size_t>(4) * mt * (g.mpw * 128 + 16);                // activations
+         tab + static_cast<size_t>(4) * mt * (g.mpw * 128 * sub + 16);          // activations
 }
 
 // One workgroup per (touched expert slot, 16-row tile); slots past the touched
@@ -249,10 +252,12 @@ __host__ __device__ inline size_t a8_lds_bytes(const A8Geom& g, int mt, int nrg 
 // row m of x and of y for pair m; no routing): one workgroup per tile of 16
 // NRG rows. With NRG = 2, waves 4..7 take the second 16 rows against the same
 // activation slices as waves 0..3 (the two groups stage half of the rows each).
-template <int B, int MT, bool ALLIN, bool DENSE = false, int NRG = 1>
+template <int B, int MT, bool ALLIN, bool DENSE = false, int NRG = 1, int SUB = 1>
 __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
   using Cfg = A8Cfg<B>;
-  constexpr int PS = Cfg::kSlots;
+  static_assert(SUB == 1 || B == 2, "16-byte code loads for 2-bit codes");
+  constexpr int PS = Cfg::kSlots / SUB;
+  constexpr int DW = B * SUB;                    // code dwords per lane and step
   constexpr int GPD = Cfg::kGpDwords;
   constexpr int TR = 16 * NRG;                   // weight rows per tile
   static_assert(NRG == 1 || (NRG == 2 && MT == 16), "two row groups share 16-row passes");
@@ -272,14 +277,14 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
   const int kq = wave & 3, rg = wave >> 2;       // K quarter, row group
   const int64_t n0 = t0n + 16 * rg;
   const int nl = lane & 15, kb = lane >> 4;
-  const A8Geom geo = a8_geom(p.K, p.group);
+  const A8Geom geo = a8_geom(p.K, p.group, SUB);
   const int tb = kq * geo.nstep / 4, te = (kq + 1) * geo.nstep / 4;
   const int g0 = tb / geo.spg;
   const int gn = te > tb ? (te - 1) / geo.spg - g0 + 1 : 0;
   const int gpr = static_cast<int>(p.K / p.group);
   // activation rows of a wave's slice, 16 bytes apart in bank position: the
   // fragment reads of 16 different rows then hit different banks
-  const int xrow_bytes = geo.mpw * 128 + 16;
+  const int xrow_bytes = geo.mpw * 128 * SUB + 16;
 
   float* red = reinterpret_cast<float*>(smem);
   unsigned char* q = smem + 4 * NRG * 16 * 16 * 4;
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
   const int64_t erow = static_cast<int64_t>(e) * p.N + nrow;
   // code loads: a wave-uniform base (the expert) plus a 32-bit per-lane offset
   const unsigned char* ebase = p.codes + e * p.code_bytes;
-  const uint32_t voff = static_cast<uint32_t>(nrow * (p.K * B / 8)) + static_cast<uint32_t>(kb * B * 4);
+  const uint32_t voff = static_cast<uint32_t>(nrow * (p.K * B / 8)) + static_cast<uint32_t>(kb * DW * 4);
 
   // Group parameters of the wave's range (entry gi = g - g0 of each row): the
   // raw (s, a|b) into LDS first, then each lane of a row turns every fourth
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
     }
   }
 
-  const int nv = (te - tb) * 8;                 // 16-byte activation vectors of the wave's slice
+  const int nv = (te - tb) * 8 * SUB;           // 16-byte activation vectors of the wave's slice
   for (int mt = 0; mt < cnt; mt += MT) {
     const int Mt = min(MT, cnt - mt);
     int pr[MT];
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
       xv[m] = reinterpret_cast<const u32x4*>(p.xq + static_cast<int64_t>(pr[m] / p.topk) * p.K +
-                                             static_cast<int64_t>(tb) * 128);
+                                             static_cast<int64_t>(tb) * 128 * SUB);
     // Up to four rows a pass: the first activation vectors of each row first
     // (unconditional, indices clamped), then the code stream. More rows copy
     // their activations after the code loads are issued.
@@ -345,13 +350,13 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
         xr[m][r] = xv[m][i < nv ? i : 0];
       }
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t cb[PS][B];
+    uint32_t cb[PS][DW];
     auto load_step = [&](auto u_c, int treq) {
       constexpr int u = decltype(u_c)::value;
       int t = treq < te ? treq : te - 1;
       t = t < 0 ? 0 : t;
-      const unsigned char* sb = ebase + static_cast<int64_t>(t) * (16 * B);   // uniform
-      load_chunk_dwords<B>(reinterpret_cast<const uint32_t*>(sb + voff), cb[u]);
+      const unsigned char* sb = ebase + static_cast<int64_t>(t) * (16 * DW);  // uniform
+      load_chunk_dwords<DW>(reinterpret_cast<const uint32_t*>(sb + voff), cb[u]);
     };
     [&]<int... U>(std::integer_sequence<int, U...>) {
       (load_step(std::integral_constant<int, U>{}, tb + U), ...);
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
            const int t = t0 + u;
            if (t < te) {
 #pragma unroll
-             for (int d = 0; d < B; ++d) asm volatile("" : "+v"(cb[u][d]));
+             for (int d = 0; d < DW; ++d) asm volatile("" : "+v"(cb[u][d]));
              if (t == t_next) {                   // wave-uniform: a group opens
                if (!fresh) {
 #pragma unroll
@@ -465,20 +470,24 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
                  wave_lds_order();
                }
              }
-             uint32_t car[8];
-             if constexpr (B == 2) {
-               decode_w2(cb[u], T[0], car);
-             } else if constexpr (Cfg::kRegTable) {
-               decode_regs<B>(cb[u], T, car);
-             } else if constexpr (Cfg::kDirect) {
-               decode_direct<B>(cb[u], ga, gb, car);
-             } else {
-               decode_lds<B>(cb[u], tab_row, car);
+#pragma unroll
+             for (int h = 0; h < SUB; ++h) {
+               // chunk h of the lane's SUB chunks: codes 32 (SUB kb + h) .. + 31 of the step
+               uint32_t car[8];
+               if constexpr (B == 2) {
+                 decode_w2(cb[u] + B * h, T[0], car);
+               } else if constexpr (Cfg::kRegTable) {
+                 decode_regs<B>(cb[u], T, car);
+               } else if constexpr (Cfg::kDirect) {
+                 decode_direct<B>(cb[u], ga, gb, car);
+               } else {
+                 decode_lds<B>(cb[u], tab_row, car);
+               }
+               const u32x4* xf = reinterpret_cast<const u32x4*>(xa + (((t - tb) * 4 + kb) * SUB + h) * 32);
+               isum = mfma_i8(xf[0], u32x4{car[0], car[1], car[2], car[3]}, fresh ? i32x4{0, 0, 0, 0} : isum);
+               isum = mfma_i8(xf[1], u32x4{car[4], car[5], car[6], car[7]}, isum);
+               fresh = false;
              }
-             const u32x4* xf = reinterpret_cast<const u32x4*>(xa + ((t - tb) * 4 + kb) * 32);
-             isum = mfma_i8(xf[0], u32x4{car[0], car[1], car[2], car[3]}, fresh ? i32x4{0, 0, 0, 0} : isum);
-             isum = mfma_i8(xf[1], u32x4{car[4], car[5], car[6], car[7]}, isum);
-             fresh = false;
            }
            if constexpr (!ALLIN) load_step(std::integral_constant<int, u>{}, t + PS);
            __builtin_amdgcn_sched_barrier(0);
@@ -516,18 +525,22 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
   }
 }
 
-template <int B>
-hipError_t launch_moe_a8_b(const MoeA8Params& p, int64_t blocks, int T, hipStream_t st) {
-  const A8Geom geo = a8_geom(p.K, p.group);
-  const bool allin = geo.mpw <= A8Cfg<B>::kSlots;
+// 2-bit codes take 16-byte code loads per lane (two 32-code chunks a step) when
+// K and the group are multiples of 256.
+inline bool a8_sub2(int bits, int64_t K, int group) { return bits == 2 && K % 256 == 0 && group % 256 == 0; }
+
+template <int B, int SUB>
+hipError_t launch_moe_a8_bs(const MoeA8Params& p, int64_t blocks, int T, hipStream_t st) {
+  const A8Geom geo = a8_geom(p.K, p.group, SUB);
+  const bool allin = geo.mpw <= A8Cfg<B>::kSlots / SUB;
   // One row per pass for one token (decode), four when several tokens are
   // routed and the slices fit; more pairs of an expert take more passes.
   int mt = T <= 1 ? 1 : 4;
-  if (mt == 4 && a8_lds_bytes<B>(geo, 4) > 80 * 1024) mt = 1;
-  const size_t lds = a8_lds_bytes<B>(geo, mt);
+  if (mt == 4 && a8_lds_bytes<B>(geo, 4, 1, SUB) > 80 * 1024) mt = 1;
+  const size_t lds = a8_lds_bytes<B>(geo, mt, 1, SUB);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  auto kern = mt == 1 ? (allin ? k_moe_a8<B, 1, true> : k_moe_a8<B, 1, false>)
-                      : (allin ? k_moe_a8<B, 4, true> : k_moe_a8<B, 4, false>);
+  auto kern = mt == 1 ? (allin ? k_moe_a8<B, 1, true, false, 1, SUB> : k_moe_a8<B, 1, false, false, 1, SUB>)
+                      : (allin ? k_moe_a8<B, 4, true, false, 1, SUB> : k_moe_a8<B, 4, false, false, 1, SUB>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -537,16 +550,25 @@ hipError_t launch_moe_a8_b(const MoeA8Params& p, int64_t blocks, int T, hipStrea
   return hipGetLastError();
 }
 
+template <int B>
+hipError_t launch_moe_a8_b(const MoeA8Params& p, int64_t blocks, int T, hipStream_t st) {
+  if constexpr (B == 2) {
+    if (a8_sub2(B, p.K, p.group)) return launch_moe_a8_bs<B, 2>(p, blocks, T, st);
+  }
+  return launch_moe_a8_bs<B, 1>(p, blocks, T, st);
+}
+
 }  // namespace
 
 bool moe_a8_supported(int64_t K, int bits, int group) {
   if (bits < 2 || bits > 8 || K < 0 || K > (int64_t{1} << 28)) return false;
   if (K % 128 != 0 || group % 128 != 0 || group > 1024 || (K > 0 && K % group != 0)) return false;
-  const A8Geom geo = a8_geom(K, group);
+  const int sub = a8_sub2(bits, K, group) ? 2 : 1;
+  const A8Geom geo = a8_geom(K, group, sub);
   if (geo.gmax > 4 * kA8GpRegs) return false;
   size_t lds = 0;
   switch (bits) {
-    case 2: lds = a8_lds_bytes<2>(geo, 1); break;
+    case 2: lds = a8_lds_bytes<2>(geo, 1, 1, sub); break;
     case 3: lds = a8_lds_bytes<3>(geo, 1); break;
     case 4: lds = a8_lds_bytes<4>(geo, 1); break;
     case 5: lds = a8_lds_bytes<5>(geo, 1); break;
@@ -557,10 +579,10 @@ bool moe_a8_supported(int64_t K, int bits, int group) {
   return lds <= 160 * 1024;
 }
 
-template <int B>
-hipError_t launch_gemv_a8_b(const MoeA8Params& p, hipStream_t st) {
-  const A8Geom geo = a8_geom(p.K, p.group);
-  const bool allin = geo.mpw <= A8Cfg<B>::kSlots;
+template <int B, int SUB>
+hipError_t launch_gemv_a8_bs(const MoeA8Params& p, hipStream_t st) {
+  const A8Geom geo = a8_geom(p.K, p.group, SUB);
+  const bool allin = geo.mpw <= A8Cfg<B>::kSlots / SUB;
   // Rows per pass: all 16 rows of the MFMA's activation side for more than
   // four rows when their slices fit the LDS, else four, else one.
   // 16-row passes take two 16-row groups per workgroup (eight waves) where both
@@ -568,15 +590,15 @@ hipError_t launch_gemv_a8_b(const MoeA8Params& p, hipStream_t st) {
   // so one workgroup a compute unit, and 32 rows keep every tile in one round.
   int mt = p.dense_m <= 1 ? 1 : (p.dense_m <= 4 ? 4 : 16);
   int nrg = 1;
-  if (mt == 16 && a8_lds_bytes<B>(geo, 16, 2) <= 160 * 1024) nrg = 2;
-  if (mt == 16 && nrg == 1 && a8_lds_bytes<B>(geo, 16) > 160 * 1024) mt = 4;
-  if (mt == 4 && a8_lds_bytes<B>(geo, 4) > 160 * 1024) mt = 1;
-  const size_t lds = a8_lds_bytes<B>(geo, mt, nrg);
+  if (mt == 16 && a8_lds_bytes<B>(geo, 16, 2, SUB) <= 160 * 1024) nrg = 2;
+  if (mt == 16 && nrg == 1 && a8_lds_bytes<B>(geo, 16, 1, SUB) > 160 * 1024) mt = 4;
+  if (mt == 4 && a8_lds_bytes<B>(geo, 4, 1, SUB) > 160 * 1024) mt = 1;
+  const size_t lds = a8_lds_bytes<B>(geo, mt, nrg, SUB);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  auto kern = mt == 1 ? (allin ? k_moe_a8<B, 1, true, true> : k_moe_a8<B, 1, false, true>)
-              : mt == 4 ? (allin ? k_moe_a8<B, 4, true, true> : k_moe_a8<B, 4, false, true>)
-              : nrg == 1 ? (allin ? k_moe_a8<B, 16, true, true> : k_moe_a8<B, 16, false, true>)
-                         : (allin ? k_moe_a8<B, 16, true, true, 2> : k_moe_a8<B, 16, false, true, 2>);
+  auto kern = mt == 1 ? (allin ? k_moe_a8<B, 1, true, true, 1, SUB> : k_moe_a8<B, 1, false, true, 1, SUB>)
+              : mt == 4 ? (allin ? k_moe_a8<B, 4, true, true, 1, SUB> : k_moe_a8<B, 4, false, true, 1, SUB>)
+              : nrg == 1 ? (allin ? k_moe_a8<B, 16, true, true, 1, SUB> : k_moe_a8<B, 16, false, true, 1, SUB>)
+                         : (allin ? k_moe_a8<B, 16, true, true, 2, SUB> : k_moe_a8<B, 16, false, true, 2, SUB>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -585,6 +607,14 @@ hipError_t launch_gemv_a8_b(const MoeA8Params& p, hipStream_t st) {
   const int64_t tiles = (p.N + 16 * nrg - 1) / (16 * nrg);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(256 * nrg), lds, st, p);
   return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_gemv_a8_b(const MoeA8Params& p, hipStream_t st) {
+  if constexpr (B == 2) {
+    if (a8_sub2(B, p.K, p.group)) return launch_gemv_a8_bs<B, 2>(p, st);
+  }
+  return launch_gemv_a8_bs<B, 1>(p, st);
 }
 
 hipError_t launch_gemv_a8(const MoeA8Params& p, int bits, hipStream_t st) {
