@@ -651,7 +651,7 @@ def decode_step_block(cq, synth, dev):
            "workload": "1 token x top-16 of 128 resident experts, gate_up 6144x7168 W2 G512, A16",
            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                        "kernel": "cubic_moe_grouped_gemm call: k_moe_route + k_moe_stream<DecodeW2>",
+                        "kernel": "cubic_moe_grouped_gemm call (one token: k_moe_stream<DecodeW2> reads the ids, no routing kernel)",
                         "avg_launch_us": round(ms * 1e3, 2),
                         "timing": "HIP events around graph replays of 40 launches over 8 disjoint "
                                   "expert sets"}}
@@ -663,7 +663,7 @@ def decode_step_block(cq, synth, dev):
     nb8 = topk * (N * H * bits // 8 + 8 * N * (H // group)) + H + 4 + topk * N * 4
     g8 = nb8 / ms8 / 1e6
     res["a8"] = {"GB/s": round(g8, 1), "us": round(ms8 * 1e3, 2), "bytes_per_launch": nb8,
-                 "kernel": "cubic_moe_grouped_gemm_a8 call: k_moe_route + k_moe_a8<2>",
+                 "kernel": "cubic_moe_grouped_gemm_a8 call (one token: k_moe_a8<2> reads the ids, no routing kernel)",
                  "frac_of_hbm_peak": round(g8 / HBM_PEAK_GBS, 4)}
     print(json.dumps({"decode_step_16x": res}), file=sys.stderr, flush=True)
     del pool

@@ -47,6 +47,14 @@ struct MoeGemvParams {
   const uint16_t* x;      // bf16 activations [T][K]
   float* y;               // [T*topk][N] fp32, or bf16 when ybf16
   int ybf16;
+  // Direct mode (one token): no routing kernel; pair q's expert is read from
+  // ids[q] by the product itself, invalid ids give zero rows, and the first
+  // workgroup writes their count to bad_count.
+  int direct;
+  int npairs;             // pairs (direct mode)
+  int E;                  // experts (direct mode)
+  const int32_t* ids;     // [npairs] (direct mode)
+  int32_t* bad_count;     // (direct mode)
 };
 
 // Routed experts in the Dynamic A8 mode: int8 activations with per-token scales.
@@ -65,6 +73,14 @@ struct MoeA8Params {
   float* y;               // [T*topk][N] fp32, or bf16 when ybf16
   int ybf16;
   int dense_m;            // launch_gemv_a8: activation rows of a plain product (no routing)
+  // Direct mode (one token): no routing kernel; the workgroups of pair q read
+  // its expert from ids[q], invalid ids give zero rows, and block 0 writes
+  // their count to bad_count.
+  int direct;
+  int npairs;             // pairs (direct mode, at most 64)
+  int E;                  // experts (direct mode)
+  const int32_t* ids;     // [npairs] (direct mode)
+  int32_t* bad_count;     // (direct mode)
 };
 
 int device_cu_count();   // compute units of the current device (0 if unknown)

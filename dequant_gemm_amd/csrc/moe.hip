@@ -276,11 +276,19 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
   constexpr int DW = B * SPL;
   constexpr int XB = 2;
   const unsigned tiles = static_cast<unsigned>((p.N + 15) / 16);
-  const unsigned items = static_cast<unsigned>(p.hdr[1]) * tiles;
+  // Direct mode (one token, no routing kernel): item it is pair it / tiles,
+  // whose expert erec[pair] holds (erec is the caller's id array then).
+  const unsigned items = static_cast<unsigned>(p.direct ? p.npairs : p.hdr[1]) * tiles;
+  const int lane = threadIdx.x & 63;
+  if (p.direct && blockIdx.x == 0 && threadIdx.x < 64) {
+    // the invalid-id count (npairs <= 64 in direct mode)
+    const int e = lane < p.npairs ? erec[lane] : 0;
+    const unsigned long long bad = __ballot(static_cast<unsigned>(e) >= static_cast<unsigned>(p.E));
+    if (lane == 0) *p.bad_count = __popcll(bad);
+  }
   // this workgroup's runs start at run * (blockIdx.x + j * gridDim.x)
   unsigned run_beg = run * blockIdx.x;
   if (run_beg >= items) return;
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nl = lane & 15, kb = lane >> 4;
   const GemvGeom geo = gemv_geom(p.K, p.group, SPL);
@@ -303,6 +311,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
   struct Unit {
     unsigned it;
     int mt, e, beg, cnt, M;
+    int bad;                 // direct mode: invalid id, the unit stores zeros
     int pr[MT];
     int64_t n0;
   };
@@ -311,6 +320,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
     u.it = it;
     u.mt = mt;
     u.e = rec[0]; u.beg = rec[1]; u.cnt = rec[2];
+    u.bad = p.direct ? rec[5] : 0;
     u.M = min(MT, u.cnt - mt);
     u.n0 = static_cast<int64_t>(it % tiles) * 16;
     // wave-uniform indices (readfirstlane) make these scalar loads, which do
@@ -326,6 +336,13 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
   };
   auto load_rec = [&](unsigned it) {
     const int a = __builtin_amdgcn_readfirstlane(static_cast<int>(it / tiles));
+    if (p.direct) {
+      // a record of one pair: expert (expert 0's codes stand in for an invalid
+      // id, whose rows are then stored as zeros), first position, one pair
+      const int e = erec[a];
+      const int ok = static_cast<unsigned>(e) < static_cast<unsigned>(p.E);
+      return i32x8{ok ? e : 0, a, 1, a, a, 1 - ok, 0, 0};
+    }
     return *reinterpret_cast<const i32x8*>(erec + 8 * a);
   };
   auto row_of = [&](const Unit& u) {
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
         v += red[(1 * 16 + m) * 16 + cc];
         v += red[(2 * 16 + m) * 16 + cc];
         v += red[(3 * 16 + m) * 16 + cc];
-        store_out(y, p.ybf16 != 0, static_cast<int64_t>(qp) * p.N + cur.n0 + cc, v);
+        store_out(y, p.ybf16 != 0, static_cast<int64_t>(qp) * p.N + cur.n0 + cc, cur.bad ? 0.0f : v);
       }
     }
     __syncthreads();                          // red is rewritten by the next unit
@@ -615,13 +632,35 @@ hipError_t launch_moe_route(const int32_t* ids, int P, int E, int64_t N, float* 
   return hipGetLastError();
 }
 
+// One token (its pairs all distinct rows of one activation row, at most 64)
+// on the streaming kernel: the product reads the ids itself, and no routing
+// kernel runs. Sets p's direct fields and returns true when this applies.
+static bool moe_set_direct(MoeGemvParams& p, const int32_t* ids, int T, int P, int E, int bits,
+                           int32_t* hdr) {
+  if (T != 1 || P < 1 || P > 64 || bits != 2 || p.group % 256 != 0) return false;
+  const GemvGeom geo = gemv_geom(p.K, p.group, 2);
+  if (!(geo.mpw <= 8 && geo.gmax <= 8)) return false;   // launch_moe_product_t's k_moe_stream cases
+  p.direct = 1;
+  p.npairs = P;
+  p.E = E;
+  p.ids = ids;
+  p.bad_count = hdr;
+  p.hdr = hdr;
+  p.erec = ids;
+  p.sorted = ids;
+  return true;
+}
+
 hipError_t launch_moe(const int32_t* ids, int T, int E, int topk, const MoeGemvParams& base,
                       int32_t* hdr, int32_t* erec, int32_t* sorted, int bits, bool xf16, hipStream_t st) {
   const int P = T * topk;
-  const hipError_t err = launch_moe_route(ids, P, E, base.N, base.y, base.ybf16, hdr, erec, sorted, st);
-  if (err != hipSuccess) return err;
   MoeGemvParams p = base;
   p.topk = topk;
+  p.direct = 0;
+  if (moe_set_direct(p, ids, T, P, E, bits, hdr))
+    return launch_moe_product(p, P, P, T, bits, xf16, st);
+  const hipError_t err = launch_moe_route(ids, P, E, base.N, base.y, base.ybf16, hdr, erec, sorted, st);
+  if (err != hipSuccess) return err;
   p.hdr = hdr; p.erec = erec; p.sorted = sorted;
   return launch_moe_product(p, P, E, T, bits, xf16, st);
 }
@@ -710,14 +749,31 @@ hipError_t launch_moe_mlp(const int32_t* ids, const float* topk_w, int T, int E,
                           hipStream_t st) {
   const int P = T * topk;
   const int64_t I = dn.K, H = dn.N;
-  hipError_t err = launch_moe(ids, T, E, topk, up, hdr, erec, sorted, up_bits, false, st);
-  if (err != hipSuccess) return err;
-  err = launch_moe_act(up.y, P, I, h, st);
-  if (err != hipSuccess) return err;
   MoeGemvParams p = dn;
   p.topk = 1;                                  // one activation row per pair
   p.x = h;
-  p.hdr = hdr; p.erec = erec; p.sorted = sorted;
+  p.direct = 0;
+  // The down product reuses the gate_up product's routing, unless it reads the
+  // ids itself; the routing kernel then runs only for a routed gate_up.
+  const bool dn_direct = moe_set_direct(p, ids, T, P, E, dn_bits, hdr);
+  hipError_t err;
+  if (dn_direct) {
+    err = launch_moe(ids, T, E, topk, up, hdr, erec, sorted, up_bits, false, st);
+  } else {
+    // the gate_up product must be routed too, so that the routing exists for down
+    err = launch_moe_route(ids, P, E, up.N, up.y, up.ybf16, hdr, erec, sorted, st);
+    if (err == hipSuccess) {
+      MoeGemvParams u = up;
+      u.topk = topk;
+      u.direct = 0;
+      u.hdr = hdr; u.erec = erec; u.sorted = sorted;
+      err = launch_moe_product(u, P, E, T, up_bits, false, st);
+    }
+  }
+  if (err != hipSuccess) return err;
+  err = launch_moe_act(up.y, P, I, h, st);
+  if (err != hipSuccess) return err;
+  if (!dn_direct) { p.hdr = hdr; p.erec = erec; p.sorted = sorted; }
   err = launch_moe_product(p, P, E, T, dn_bits, false, st);
   if (err != hipSuccess) return err;
   return launch_moe_combine(dn.y, ids, topk_w, T, topk, E, H, out, st);

@@ -268,9 +268,25 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
   if constexpr (DENSE) {
     rec = i32x8{0, 0, p.dense_m, 0, p.dense_m > 1 ? 1 : 0, 0, 0, 0};
   } else {
-    rec = *reinterpret_cast<const i32x8*>(p.erec + 8 * a);
+    if (p.direct) {
+      if (blockIdx.x == 0 && threadIdx.x < 64) {
+        // the invalid-id count (npairs <= 64 in direct mode)
+        const int l = threadIdx.x;
+        const int e = l < p.npairs ? p.ids[l] : 0;
+        const unsigned long long bad = __ballot(static_cast<unsigned>(e) >= static_cast<unsigned>(p.E));
+        if (l == 0) *p.bad_count = __popcll(bad);
+      }
+      // pair a alone: expert 0's codes stand in for an invalid id, whose rows
+      // are stored as zeros
+      const int e = p.ids[a];
+      const int ok = static_cast<unsigned>(e) < static_cast<unsigned>(p.E);
+      rec = i32x8{ok ? e : 0, static_cast<int>(a), 1, static_cast<int>(a), static_cast<int>(a), 1 - ok, 0, 0};
+    } else {
+      rec = *reinterpret_cast<const i32x8*>(p.erec + 8 * a);
+    }
   }
   if (rec[2] == 0) return;
+  const bool bad_pair = !DENSE && p.direct && rec[5] != 0;
   const int64_t t0n = static_cast<int64_t>(blockIdx.x - a * tiles) * TR;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(256 * NRG) void k_moe_a8(MoeA8Params p) {
         v += rr[(2 * 16 + m) * 16 + cc];
         v += rr[(3 * 16 + m) * 16 + cc];
         v *= p.xs[qp / p.topk];
-        store_out(p.y, p.ybf16 != 0, static_cast<int64_t>(qp) * p.N + n0 + cc, v);
+        store_out(p.y, p.ybf16 != 0, static_cast<int64_t>(qp) * p.N + n0 + cc, bad_pair ? 0.0f : v);
       }
     }
     if (mt + MT < cnt) __syncthreads();   // red and the activation slices are reused by the next pass
@@ -647,13 +663,28 @@ hipError_t launch_moe_a8_product(const MoeA8Params& p, int P, int E, int T, int 
   }
 }
 
+// One token (at most 64 pairs): the product reads the ids itself and no
+// routing kernel runs. Sets p's direct fields and returns true when this applies.
+static bool moe_a8_set_direct(MoeA8Params& p, const int32_t* ids, int T, int P, int E, int32_t* hdr) {
+  if (T != 1 || P < 1 || P > 64) return false;
+  p.direct = 1;
+  p.npairs = P;
+  p.E = E;
+  p.ids = ids;
+  p.bad_count = hdr;
+  p.hdr = hdr; p.erec = ids; p.sorted = ids;
+  return true;
+}
+
 hipError_t launch_moe_a8(const int32_t* ids, int T, int E, int topk, const MoeA8Params& base, int32_t* hdr,
                          int32_t* erec, int32_t* sorted, int bits, hipStream_t st) {
   const int P = T * topk;
-  hipError_t err = launch_moe_route(ids, P, E, base.N, base.y, base.ybf16, hdr, erec, sorted, st);
-  if (err != hipSuccess) return err;
   MoeA8Params p = base;
   p.topk = topk;
+  p.direct = 0;
+  if (moe_a8_set_direct(p, ids, T, P, E, hdr)) return launch_moe_a8_product(p, P, P, T, bits, st);
+  hipError_t err = launch_moe_route(ids, P, E, base.N, base.y, base.ybf16, hdr, erec, sorted, st);
+  if (err != hipSuccess) return err;
   p.hdr = hdr; p.erec = erec; p.sorted = sorted;
   return launch_moe_a8_product(p, P, E, T, bits, st);
 }
@@ -677,8 +708,15 @@ hipError_t launch_moe_mlp_a8(const uint16_t* x, const int32_t* ids, const float*
   MoeA8Params pd = dn;
   pd.topk = 1;                                 // one activation row per pair
   pd.xq = b.hq; pd.xs = b.hs; pd.y = b.y2; pd.ybf16 = 0;
-  pd.hdr = hdr; pd.erec = erec; pd.sorted = sorted;
-  err = launch_moe_a8_product(pd, P, E, T, dn_bits, st);
+  pd.direct = 0;
+  // one token: both products read the ids themselves (launch_moe_a8 took the
+  // same decision for gate_up); otherwise the gate_up product's routing
+  if (moe_a8_set_direct(pd, ids, T, P, E, hdr)) {
+    err = launch_moe_a8_product(pd, P, P, T, dn_bits, st);
+  } else {
+    pd.hdr = hdr; pd.erec = erec; pd.sorted = sorted;
+    err = launch_moe_a8_product(pd, P, E, T, dn_bits, st);
+  }
   if (err != hipSuccess) return err;
   return launch_moe_combine(b.y2, ids, topk_w, T, topk, E, dn.N, out, st);
 }
