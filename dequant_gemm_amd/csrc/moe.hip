@@ -372,16 +372,30 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
     for (int m = 0; m < MT; ++m)
       xv[m] = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(u.pr[m] / p.topk) * p.K + k0);
   };
-  auto code_row = [&](const Unit& u) {
-    const int64_t n = u.n0 + nl;
-    return reinterpret_cast<const uint32_t*>(p.codes + u.e * p.code_bytes +
-                                             (n < p.N ? n : p.N - 1) * row_bytes);
+  // A unit's code stream: a buffer resource on the tile's first row (wave-
+  // uniform), a per-lane offset (row in the tile, chunk) and a per-slot
+  // wave-uniform offset, so no per-slot address occupies vector registers.
+  static_assert(DW == 4, "one 16-byte code load per lane and macro step");
+  struct CodeSrc {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff;
   };
-  auto issue_slot = [&](auto u_c, const uint32_t* crow) {
+  auto code_src = [&](const Unit& u) {
+    const unsigned char* base = p.codes + u.e * p.code_bytes + u.n0 * row_bytes;
+    const int64_t n = u.n0 + nl;
+    const int64_t r = (n < p.N ? n : p.N - 1) - u.n0;   // rows past N repeat the last one
+    CodeSrc c;
+    c.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), static_cast<short>(0),
+                                             static_cast<int>(16 * row_bytes), static_cast<int>(0x00020000u));
+    c.voff = static_cast<uint32_t>(r * row_bytes) + static_cast<uint32_t>(kb * SPL * B * 4);
+    return c;
+  };
+  auto issue_slot = [&](auto u_c, const CodeSrc& src) {
     constexpr int u = decltype(u_c)::value;
     int t = tb + u < te ? tb + u : te - 1;     // slots past the wave's range repeat its last step
     t = t < 0 ? 0 : t;                         // (a wave without steps reads step 0, unused)
-    load_dwords<DW>(crow + (t * 4 * SPL + kb * SPL) * B, cb[u]);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src.rs, src.voff, t * (4 * SPL * B * 4), 0);
+    cb[u][0] = v.x; cb[u][1] = v.y; cb[u][2] = v.z; cb[u][3] = v.w;
   };
 
   // first unit: everything issued now
@@ -397,9 +411,9 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
   // waiting for them never waits for the code stream
   __builtin_amdgcn_sched_barrier(0);
   {
-    const uint32_t* crow = code_row(cur);
+    const CodeSrc src = code_src(cur);
     [&]<int... U>(std::integer_sequence<int, U...>) {
-      (issue_slot(std::integral_constant<int, U>{}, crow), ...);
+      (issue_slot(std::integral_constant<int, U>{}, src), ...);
     }(std::make_integer_sequence<int, PM>{});
   }
   bool xfresh = true;
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
     StreamState st;
     st.reset(tb, g0);
     const int ml = nl < cur.M ? nl : 0;
-    const uint32_t* crow_n = code_row(nxt);
+    const CodeSrc src_n = code_src(nxt);
     [&]<int... U>(std::integer_sequence<int, U...>) {
       (([&] {
          constexpr int u = U;
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(256, OCC) void k_moe_stream(MoeGemvParams p,
            for (int d = 0; d < DW; ++d) asm volatile("" : "+v"(cb[u][d]));
            step_macro<Dec, true, SPL>(c, st, cb[u], nullptr, t, g0, ml);
          }
-         issue_slot(std::integral_constant<int, u>{}, crow_n);
+         issue_slot(std::integral_constant<int, u>{}, src_n);
          __builtin_amdgcn_sched_barrier(0);
        }()),
        ...);
@@ -539,6 +553,11 @@ static hipError_t launch_moe_gemv_t(const MoeGemvParams& p, int64_t blocks, int 
   return hipGetLastError();
 }
 
+// Workgroups per compute unit of the one-row (decode) instance of k_moe_stream
+// (133 VGPRs a wave; four, at 128 VGPRs, measured slower: 54.5 against 51-52 us
+// for the 16-expert decode step).
+constexpr int kStreamOcc1 = 3;
+
 // The persistent kernel for 2-bit codes with groups of 256 or more: PM slots
 // cover a wave's macro steps, GPR registers its groups.
 template <int PM, int GPR, bool XF16>
@@ -554,7 +573,7 @@ static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, in
   if (mt == 2 && moe_lds_bytes<DecodeW2>(geo, 2) > 80 * 1024) mt = 1;
   const size_t lds = moe_lds_bytes<DecodeW2>(geo, mt);
   // several rows per pass need more registers: two workgroups per compute unit
-  auto kern = mt == 1 ? k_moe_stream<Dec, 2, PM, 1, GPR, 3, XF16>
+  auto kern = mt == 1 ? k_moe_stream<Dec, 2, PM, 1, GPR, kStreamOcc1, XF16>
                       : (mt == 2 ? k_moe_stream<Dec, 2, PM, 2, GPR, 2, XF16>
                                  : k_moe_stream<Dec, 2, PM, 4, GPR, 2, XF16>);
   if (lds > 64 * 1024) {
@@ -567,7 +586,7 @@ static hipError_t launch_moe_stream_t(const MoeGemvParams& p, int64_t blocks, in
   // longest run that keeps the busiest workgroup's item count (for the largest
   // possible item count) lowest.
   const int64_t cus = device_cu_count();
-  const int64_t occ = mt == 1 ? 3 : 2;
+  const int64_t occ = mt == 1 ? kStreamOcc1 : 2;
   const int64_t cap = (cus > 0 ? cus : 256) * occ;
   int64_t run = 1, best = INT64_MAX;
   for (int64_t r = 8; r >= 1; --r) {
