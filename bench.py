@@ -73,7 +73,7 @@ def parse():
 
 # Sources of the GEMV kernel the roofline line describes; the stored HBM traffic
 # figure is only reported while their hash matches the one it was measured on.
-GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "gemv.hip")
+GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "gemv.hip", "gemv_rows.hip")
 
 
 def gemv_source_hash():
@@ -429,7 +429,7 @@ def main():
                    "steps_per_graph": c, "algorithmic_bytes_per_step": bytes_up + bytes_dn},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gemv<DecodeW2> (gate_up 6144x7168, M=1)",
+                     "kernel": "k_gemv_rows<bf16, G=512, 2 wave-loads a wave> (gate_up 6144x7168, M=1)",
                      "avg_launch_us": round(up_avg_ms * 1e3, 3),
                      "timing": f"HIP events on the launch stream around graph replays of {2 * R} "
                                f"back-to-back gate_up launches over {R} rotating copies",
@@ -457,7 +457,10 @@ def floors(dev):
       16-expert decode step's 176 MB of codes in one launch (GEMV pattern, and
       contiguous with eight loads in flight per lane on 2688 and 768 workgroups);
     - one lane chasing a cyclic permutation of 2^27 uint32 (512 MB): the latency of
-      a dependent load that misses every cache."""
+      a dependent load that misses every cache;
+    - arrival probes over the gate_up codes: when a wave's first and last loads
+      arrive with the old GEMV's pattern (16 rows x 64 bytes per wave load) and
+      with whole rows per wave load."""
     import ctypes
 
     import numpy as np
@@ -493,6 +496,30 @@ def floors(dev):
         ms = _graph_time([(lambda b=b: call(b)) for b in bufs], 5, dev)
         res[name + "_us"] = round(ms * 1e3, 3)
         res[name + "_GB/s"] = round(nbytes / ms / 1e6, 1)
+    # When a wave's data arrives: each wave timestamps its start and the arrival
+    # of its first and last load (100 MHz clock); per launch the medians over
+    # waves, from the launch's earliest start; reported: the medians over 35
+    # launches (after 5), each launch on the next copy.
+    lib.floors_arrival.argtypes = [ctypes.c_int, vp, i64, vp, vp]
+    lib.floors_arrival.restype = ctypes.c_int
+    nw = 4 * ((rows + 11) // 12)
+    stamps = torch.empty(3 * nw, dtype=torch.int64, device=dev)
+    for kind, name in ((0, "arrival_gemv16_pattern"), (1, "arrival_whole_rows")):
+        first, last, span = [], [], []
+        for it in range(40):
+            ok(lib.floors_arrival(kind, bufs[it % len(bufs)].data_ptr(), rows, ctypes.c_void_p(stamps.data_ptr()),
+                                  st()))
+            torch.cuda.synchronize(dev)
+            if it < 5:
+                continue
+            t = stamps.view(nw, 3).cpu().numpy().astype(np.int64)
+            t0 = t[:, 0].min()
+            first.append(np.median(t[:, 1] - t0) * 0.01)
+            last.append(np.median(t[:, 2] - t0) * 0.01)
+            span.append((t[:, 2].max() - t0) * 0.01)
+        res[name + "_first_us"] = round(float(np.median(first)), 3)
+        res[name + "_last_us"] = round(float(np.median(last)), 3)
+        res[name + "_span_us"] = round(float(np.median(span)), 3)
     del bufs
     # the 16-expert decode step's code bytes in one launch: 16 x 6144 rows of
     # 1792 bytes (176 MB), three rotating copies (528 MB)

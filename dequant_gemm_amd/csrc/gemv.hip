@@ -265,6 +265,8 @@ bool gemv_supported(int64_t K, int bits, int group) {
 }
 
 hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, bool xf16, hipStream_t st) {
+  // one activation row of 2-bit codes: whole rows per wave load (gemv_rows.hip)
+  if (ink && gemv_rows_supported(p.M, p.N, p.K, bits, p.group)) return launch_gemv_rows(p, xf16, st);
   const bool spl2 = gemv_spl(bits, p.group) == 2;
   if (xf16) {
     // fp16 activations: 2-bit codes on the fp16 MFMA (x only permuted, by k_xprep for

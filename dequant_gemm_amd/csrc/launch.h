@@ -100,6 +100,10 @@ hipError_t launch_act_quant(const uint16_t* x, bool xf16, int64_t M, int64_t K, 
                             hipStream_t st);
 // xf16: the activations are fp16 (x, or xp with xback NULL on the multi-row path)
 hipError_t launch_gemv(const GemvParams& p, int bits, bool ink, bool xf16, hipStream_t st);
+// One activation row of 2-bit codes with groups of 256 or 512 and at most 16
+// groups per row: the whole-row streaming GEMV (gemv_rows.hip).
+bool gemv_rows_supported(int64_t M, int64_t N, int64_t K, int bits, int group);
+hipError_t launch_gemv_rows(const GemvParams& p, bool xf16, hipStream_t st);
 size_t gemv_ink_lds_bytes(int64_t M, int64_t K, int bits, int group);
 bool gemv_supported(int64_t K, int bits, int group);
 hipError_t launch_xprep(const uint16_t* x, int64_t M, int64_t K, bool w2_order, uint16_t* xp,
