@@ -23,45 +23,21 @@
 // element is one (row, group) partial: it is scaled by its group's fp32 scale
 // and the slots of a row are summed across the wave in a fixed order (DPP
 // within 16-lane rows, then the four row sums), so results are deterministic.
-#include "gemv_core.h"
 #include "launch.h"
+#include "rows.h"
 
 namespace cubic {
 namespace {
-
-constexpr uint32_t kRowsRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
-
-// Sum over the 64 lanes in a fixed order: within each 16-lane row by DPP
-// (quad swaps, then the half-row and row mirrors), then the four row sums.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = dpp_add<0xB1>(v);      // quad_perm [1, 0, 3, 2]
-  v = dpp_add<0x4E>(v);      // quad_perm [2, 3, 0, 1]
-  v = dpp_add<0x141>(v);     // row_half_mirror
-  v = dpp_add<0x140>(v);     // row_mirror
-  const int b = __builtin_bit_cast(int, v);
-  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
-         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
-}
 
 // XF16: fp16 activations (fp16 MFMA) instead of bf16. G: group size (256 or
 // 512). WL: wave-loads per wave, all issued up front.
 template <bool XF16, int G, int WL>
 __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams p, int S, int R, int L) {
   using Dec = DecodeW2T<XF16>;
-  constexpr int CL = G / 4;                // codes per lane and wave-load
-  constexpr int DWL = CL / 16;             // code dwords per lane and wave-load
-  constexpr int NSC = CL / 32;             // 32-code sub-chunks per lane
+  constexpr int DWL = G / 64;              // code dwords per lane and wave-load
+  constexpr int NSC = G / 128;             // 32-code sub-chunks per lane
   extern __shared__ __align__(16) unsigned char smem[];
-  // The activation row, with 16 bytes of padding after each group: the lanes of
-  // one 16-lane pass of a fragment read take the same offset in different
-  // groups, which the padding puts in different LDS banks.
-  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);   // the staged activation row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -72,19 +48,14 @@ __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams p, int S, int R, i
   const int gpr = static_cast<int>(p.K / G);
   const uint32_t row_bytes = static_cast<uint32_t>(p.K / 4);
 
-  // the activation row into LDS (issued first, so that waiting for it never
-  // waits for the code stream): thread t takes 32-value sub-chunk t (K <= 8192)
-  const int nsub = static_cast<int>(p.K / 32);
-  const u32x4* xg = reinterpret_cast<const u32x4*>(p.x) + 4 * (tid < nsub ? tid : 0);
-  u32x4 xv[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) xv[v] = xg[v];
+  rows::XStageRow xs;
+  xs.issue(p.x, p.K, tid);
 
   // codes and group parameters of this wave's WL wave-loads
   const __amdgpu_buffer_rsrc_t crs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.codes), static_cast<short>(0),
                                         static_cast<int>(static_cast<uint32_t>(p.N) * row_bytes),
-                                        static_cast<int>(kRowsRsrcWord3));
+                                        static_cast<int>(rows::kRsrcWord3));
   const int gw = static_cast<int>(blockIdx.x) * 4 + wave;
   uint32_t cw[WL][DWL];
   float gs[WL];
@@ -105,87 +76,19 @@ __global__ __launch_bounds__(256) void k_gemv_rows(GemvParams p, int S, int R, i
     gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi];
   }
 
-  // stored in the decoder's slot order: dword r of a sub-chunk holds the pair
-  // (x[n], x[n + 8]), n = 16 (r >> 3) + (r & 7) (DecodeW2T::slot_to_code)
-  if (tid < nsub) {
-    uint32_t nat[16], o[16];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      nat[4 * v] = xv[v].x; nat[4 * v + 1] = xv[v].y; nat[4 * v + 2] = xv[v].z; nat[4 * v + 3] = xv[v].w;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = 16 * (r >> 3) + (r & 7);
-      const uint32_t lo = nat[n >> 1], hi = nat[(n >> 1) + 4];
-      o[r] = (n & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    uint32_t* dst = xl + 16 * tid + 4 * (32 * tid / G);
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      *reinterpret_cast<u32x4*>(dst + 4 * v) = u32x4{o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]};
-  }
+  xs.store<G>(xl, p.K, tid);
   __syncthreads();
-
-  // this lane's activations: sub-chunk c of its quarter, four fragments
   u32x4 xa[NSC][4];
-  {
-    const int k0 = gi * G + kq * CL;       // the lane's first code along K
-    const uint32_t* xrow = xl + k0 / 2 + 4 * gi;   // (its group's padding)
-#pragma unroll
-    for (int c = 0; c < NSC; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xa[c][j] = *reinterpret_cast<const u32x4*>(xrow + 16 * c + 4 * j);
-  }
+  rows::load_lane_x<G>(xl, gi, kq, xa);
 
-  // the lane that holds diagonal element i of the MFMA output (register i % 4)
-  const bool diag = (lane >> 4) == (i >> 2);
 #pragma unroll
   for (int u = 0; u < WL; ++u) {
-    // two MFMA chains (even and odd sub-chunks), added at the end
-    f32x4 dc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int c = 0; c < NSC; ++c) {
-      uint32_t r[16];
-      Dec::fast(&cw[u][2 * c], r);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dc[c & 1] = mfma16<Dec::kBf16>(u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]}, xa[c][j], dc[c & 1]);
-    }
-    f32x4 d = dc[0] + dc[1];
-    // field value 10 (code -2, never written by a symmetric quantiser): its
-    // level -2 q(2) in units of s / 2 as hi + lo in the MFMA's 16-bit type
-    uint32_t ex = 0;
-#pragma unroll
-    for (int dd = 0; dd < DWL; ++dd) ex |= Dec::extra_bits(cw[u][dd]);
-    if (__any(active && ex != 0u)) {
-      const double a = f16_bits_to_f64(static_cast<uint16_t>(gab[u] & 0xffffu));
-      const double b = f16_bits_to_f64(static_cast<uint16_t>(gab[u] >> 16));
-      const float v = static_cast<float>(-2.0 * level_numerator(a, b, 2, 1));
-      uint32_t hi, lo;
-      if constexpr (Dec::kBf16) {
-        hi = bf16_rne_bits(v);
-        lo = bf16_rne_bits(v - __uint_as_float(hi << 16));
-      } else {
-        hi = f16_bits(v);
-        lo = f16_bits(v - static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi))));
-      }
-#pragma unroll
-      for (int c = 0; c < NSC; ++c) {
-        uint32_t rhi[16], rlo[16];
-        Dec::extra(&cw[u][2 * c], hi, lo, rhi, rlo);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          d = mfma16<Dec::kBf16>(u32x4{rhi[4 * j], rhi[4 * j + 1], rhi[4 * j + 2], rhi[4 * j + 3]}, xa[c][j], d);
-          d = mfma16<Dec::kBf16>(u32x4{rlo[4 * j], rlo[4 * j + 1], rlo[4 * j + 2], rlo[4 * j + 3]}, xa[c][j], d);
-        }
-      }
-    }
-    // scale each (row, group) partial; the slots of each row are summed over the wave
-    const float dv = (i & 3) == 0 ? d[0] : (i & 3) == 1 ? d[1] : (i & 3) == 2 ? d[2] : d[3];
-    const float part = (diag && active) ? dv * (gs[u] * Dec::kLevelUnit) : 0.0f;
+    const f32x4 d = rows::wave_load_dot<Dec, G>(cw[u], xa, gab[u], active);
+    // each (row, group) partial scaled; the slots of each row summed over the wave
+    const float part = rows::slot_partial<Dec>(d, lane, active, gs[u]);
     const int q0 = gw * WL + u;
     for (int rr = 0; rr < R; ++rr) {
-      const float tot = wave_sum(ri == rr ? part : 0.0f);
+      const float tot = rows::wave_sum(ri == rr ? part : 0.0f);
       const int64_t n = static_cast<int64_t>(q0) * R + rr;
       if (lane == 0 && q0 < L && n < p.N) store_out(p.y, p.ybf16 != 0, n, tot);
     }
@@ -196,7 +99,7 @@ template <bool XF16, int G>
 hipError_t launch_rows_g(const GemvParams& p, int S, int R, int L, int wl, hipStream_t st) {
   const int waves = (L + wl - 1) / wl;
   const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
-  const size_t lds = static_cast<size_t>(p.K) * 2 + 16 * static_cast<size_t>(p.K / G);   // K <= 8192
+  const size_t lds = rows::lds_bytes(p.K, G);   // K <= 8192
   switch (wl) {
     case 1: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1>), dim3(grid), dim3(256), lds, st, p, S, R, L); break;
     case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2>), dim3(grid), dim3(256), lds, st, p, S, R, L); break;
