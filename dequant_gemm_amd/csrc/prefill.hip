@@ -265,48 +265,6 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
     abrow[i] = reinterpret_cast<const uint32_t*>(p.shapes) + nc * gpr;
     coff[i] = static_cast<uint32_t>(n) * row_bytes + static_cast<uint32_t>(h * 4 * B);
   }
-  // Largest |s| of each row: the row's two lanes (h = 0, 1) take alternate
-  // groups, and all loads of a batch of 32 groups are issued before any is
-  // used (a dependent chain of loads here would cost one memory latency per
-  // group). Loads past the row go to an offset outside the buffer and read 0.
-  {
-    const __amdgpu_buffer_rsrc_t srs =
-        make_rsrc(p.scales, static_cast<uint32_t>(p.N * gpr * 4));
-    float smax[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) smax[i] = 0.0f;
-    for (int g0 = 0; g0 < gpr; g0 += 32) {
-      float v[NB][16];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int64_t n = n0 + 32 * NB * wave + 32 * i + c;
-        const int64_t nc = n < p.N ? n : p.N - 1;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int g = g0 + 2 * t + h;
-          const uint32_t off = g < gpr ? static_cast<uint32_t>((nc * gpr + g) * 4) : 0xFFFFFFF0u;
-          v[i][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int t = 0; t < 16; ++t) smax[i] = fmaxf(smax[i], fabsf(v[i][t]));
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const float m = fmaxf(smax[i], __shfl_xor(smax[i], 32, 64));
-      int e = 0;                                        // 2^e >= m
-      if (m > 0.0f && m <= 3.4e38f) e = ilogbf(m) + 1;
-      inv_rowscale[i] = ldexpf(1.0f, -e);
-      if (h == 0) colmul[32 * NB * wave + 32 * i + c] = ldexpf(1.0f, e);
-    }
-  }
-  {
-    const int64_t m = m0 + tid;
-    rowmul[tid] = m < p.M ? (p.xs ? p.xs[m] : 1.0f) : 0.0f;
-  }
-
   // ---- activation tile: global -> LDS, 16-byte slots, XOR swizzle ----
   // Slot (row r, chunk q) of a buffer holds the 8 fp16 x[m0 + r][k0 + 8 (q ^ sw(r))],
   // sw(r) = (r & 7) ^ ((r >> 3) & 1): rows are 128 bytes, so rows r and r + 8 of
@@ -383,6 +341,51 @@ __device__ __forceinline__ void prefill_tile(const TiledParams& p, int64_t m0, i
   issue_a(0, 0, 0, MB);
   issue_a(1, 1, 0, MB);
   issue_a(2, 2, 0, Q);
+  // The row scale scan below is issued after the pipeline fill above, so the two
+  // memory round trips of a tile's start overlap (the scan's values are used only
+  // by the level tables, after the wait below).
+  // Largest |s| of each row: the row's two lanes (h = 0, 1) take alternate
+  // groups, and all loads of a batch of 32 groups are issued before any is
+  // used (a dependent chain of loads here would cost one memory latency per
+  // group). Loads past the row go to an offset outside the buffer and read 0.
+  {
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(p.scales, static_cast<uint32_t>(p.N * gpr * 4));
+    float smax[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) smax[i] = 0.0f;
+    for (int g0 = 0; g0 < gpr; g0 += 32) {
+      float v[NB][16];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int64_t n = n0 + 32 * NB * wave + 32 * i + c;
+        const int64_t nc = n < p.N ? n : p.N - 1;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int g = g0 + 2 * t + h;
+          const uint32_t off = g < gpr ? static_cast<uint32_t>((nc * gpr + g) * 4) : 0xFFFFFFF0u;
+          v[i][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) smax[i] = fmaxf(smax[i], fabsf(v[i][t]));
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float m = fmaxf(smax[i], __shfl_xor(smax[i], 32, 64));
+      int e = 0;                                        // 2^e >= m
+      if (m > 0.0f && m <= 3.4e38f) e = ilogbf(m) + 1;
+      inv_rowscale[i] = ldexpf(1.0f, -e);
+      if (h == 0) colmul[32 * NB * wave + 32 * i + c] = ldexpf(1.0f, e);
+    }
+  }
+  {
+    const int64_t m = m0 + tid;
+    rowmul[tid] = m < p.M ? (p.xs ? p.xs[m] : 1.0f) : 0.0f;
+  }
+
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
