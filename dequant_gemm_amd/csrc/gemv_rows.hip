@@ -99,18 +99,20 @@ template <bool XF16, int G>
 hipError_t launch_rows_g(const GemvParams& p, int S, int R, int L, int wl, hipStream_t st) {
   const int waves = (L + wl - 1) / wl;
   const size_t lds = rows::lds_bytes(p.K, G);   // K <= 8192
-  // one wave-load a wave: workgroups of 8 waves (down 7168 x 3072: 4.84-4.94 us
-  // against 5.12-5.14 us with 4); more: 4 (gate_up: 7.10 against 7.32 us with 8)
+  // One wave-load a wave: workgroups of 8 waves (down 7168 x 3072: 4.84-4.94 us
+  // against 5.12-5.14 us with 4, 4.98-5.03 us with 14). More: 12 waves, one
+  // workgroup per compute unit, which the dispatcher starts sooner than three of
+  // 4 (gate_up: 7.04-7.06 us against 7.15-7.33 us with 4, 7.32 us with 8).
   if (wl == 1) {
     hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1, 8>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512), lds, st,
                        p, S, R, L);
     return hipGetLastError();
   }
-  const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
+  const unsigned grid = static_cast<unsigned>((waves + 11) / 12);
   switch (wl) {
-    case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 4>), dim3(grid), dim3(256), lds, st, p, S, R, L); break;
-    case 3: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 3, 4>), dim3(grid), dim3(256), lds, st, p, S, R, L); break;
-    default: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 4, 4>), dim3(grid), dim3(256), lds, st, p, S, R, L); break;
+    case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    case 3: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 3, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    default: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 4, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
   }
   return hipGetLastError();
 }

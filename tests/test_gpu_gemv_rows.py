@@ -1,8 +1,9 @@
 """GPU parity of the whole-row GEMV (one activation row, 2-bit codes, groups of
 256 or 512, at most 16 groups per row), against the float64 oracle at the
 products' bar (per-row 2e-3). The cases cover every number of rows per wave
-load (R = 16 / (K / G) from 1 to 8), ragged N (rows past N in the last wave
-load), raw random code bytes (every field value, so the code -2 path runs in
+load (R = 16 / (K / G) from 1 to 16), one to three wave loads per wave (the
+large-N cases take the 12-wave workgroups), ragged N (rows past N in the last
+wave load), raw random code bytes (every field value, so the code -2 path runs in
 many wave loads), fp16 activations and bf16 outputs (the fp32 sums rounded),
 and activation rows far outside the fp16 range."""
 import numpy as np
@@ -33,7 +34,8 @@ def _raw_weight(N, K, G, seed):
 
 
 @pytest.mark.parametrize("N,K,G", [(203, 7168, 512), (130, 3072, 512), (77, 8192, 512), (33, 512, 512),
-                                   (203, 4096, 256), (97, 768, 256), (64, 2048, 256), (1, 1024, 256)])
+                                   (203, 4096, 256), (97, 768, 256), (64, 2048, 256), (1, 1024, 256),
+                                   (10001, 4096, 256)])
 def test_rows_random_codes(N, K, G):
     say(f"GEMV rows N={N} K={K} G={G} (random code bytes)")
     cw, W = _raw_weight(N, K, G, seed=N + K + G)
@@ -46,7 +48,7 @@ def test_rows_random_codes(N, K, G):
     assert torch.equal(yb.float(), y.to(torch.bfloat16).float())
 
 
-@pytest.mark.parametrize("N,K,G", [(203, 7168, 512), (97, 768, 256)])
+@pytest.mark.parametrize("N,K,G", [(203, 7168, 512), (97, 768, 256), (6144, 7168, 512)])
 def test_rows_fp16_activations(N, K, G):
     say(f"GEMV rows fp16 x N={N} K={K} G={G}")
     cw, W = _raw_weight(N, K, G, seed=3 * N + K)
