@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -73,14 +74,21 @@ def parse():
 
 # Sources of the GEMV kernel the roofline line describes; the stored HBM traffic
 # figure is only reported while their hash matches the one it was measured on.
-GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "gemv.hip", "gemv_rows.hip")
+# The hash covers the code only: comments and blank lines are left out.
+GEMV_SOURCES = ("common.h", "decode.h", "gemv_core.h", "rows.h", "launch.h", "gemv.hip", "gemv_rows.hip")
+
+
+def _code_only(text):
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (ln.split("//", 1)[0].rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
 
 
 def gemv_source_hash():
     h = hashlib.sha256()
     for f in GEMV_SOURCES:
-        with open(os.path.join(ROOT, "dequant_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "dequant_gemm_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -429,7 +437,7 @@ def main():
                    "steps_per_graph": c, "algorithmic_bytes_per_step": bytes_up + bytes_dn},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gemv_rows<bf16, G=512, 2 wave-loads a wave, 12-wave workgroups> (gate_up 6144x7168, M=1)",
+                     "kernel": "k_gemv_rows<bf16, G=512, 2 wave-loads a wave, 12-wave workgroups, x staged first> (gate_up 6144x7168, M=1)",
                      "avg_launch_us": round(up_avg_ms * 1e3, 3),
                      "timing": f"HIP events on the launch stream around graph replays of {2 * R} "
                                f"back-to-back gate_up launches over {R} rotating copies",

@@ -31,7 +31,9 @@ namespace {
 
 // XF16: fp16 activations (fp16 MFMA) instead of bf16. G: group size (256 or
 // 512). WL: wave-loads per wave, all issued up front. NW: waves per workgroup.
-template <bool XF16, int G, int WL, int NW>
+// XFIRST: the waves that stage x wait for it before they issue their codes
+// (otherwise the codes are issued first and x is stored after).
+template <bool XF16, int G, int WL, int NW, bool XFIRST>
 __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int R, int L) {
   using Dec = DecodeW2T<XF16>;
   constexpr int DWL = G / 64;              // code dwords per lane and wave-load
@@ -48,8 +50,21 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
   const int gpr = static_cast<int>(p.K / G);
   const uint32_t row_bytes = static_cast<uint32_t>(p.K / 4);
 
+  // Staging x. Every workgroup reads the same row, so its loads hit the L2; but
+  // sent behind the code loads of the waves started before them, they were
+  // measured to come in behind those, and the barrier below then held every
+  // wave's decode until most of the compute unit's codes were in. With XFIRST
+  // the staging waves (the first of the workgroup) wait for x, one round trip,
+  // before they issue their codes, so all of x goes out before any code load.
   rows::XStageRow xs;
-  xs.issue(p.x, p.K, tid);
+  if constexpr (XFIRST) {
+    if (wave * 64 < static_cast<int>(p.K / 32)) {
+      xs.issue(p.x, p.K, tid);
+      xs.store<G>(xl, p.K, tid);
+    }
+  } else {
+    xs.issue(p.x, p.K, tid);
+  }
 
   // codes and group parameters of this wave's WL wave-loads
   const __amdgpu_buffer_rsrc_t crs =
@@ -76,7 +91,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
     gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi];
   }
 
-  xs.store<G>(xl, p.K, tid);
+  if constexpr (!XFIRST) xs.store<G>(xl, p.K, tid);
   __syncthreads();
   u32x4 xa[NSC][4];
   rows::load_lane_x<G>(xl, gi, kq, xa);
@@ -100,19 +115,22 @@ hipError_t launch_rows_g(const GemvParams& p, int S, int R, int L, int wl, hipSt
   const int waves = (L + wl - 1) / wl;
   const size_t lds = rows::lds_bytes(p.K, G);   // K <= 8192
   // One wave-load a wave: workgroups of 8 waves (down 7168 x 3072: 4.84-4.94 us
-  // against 5.12-5.14 us with 4, 4.98-5.03 us with 14). More: 12 waves, one
+  // against 5.12-5.14 us with 4, 4.98-5.03 us with 14), x stored after the codes
+  // are issued (4.92 against 5.05-5.14 us with x first). More: 12 waves, one
   // workgroup per compute unit, which the dispatcher starts sooner than three of
-  // 4 (gate_up: 7.04-7.06 us against 7.15-7.33 us with 4, 7.32 us with 8).
+  // 4 (gate_up: 7.04-7.06 us against 7.15-7.33 us with 4, 7.32 us with 8), x
+  // first (6.47 against 6.99 us; a workgroup of 12 code waves and 4 staging
+  // waves measured 7.3 us).
   if (wl == 1) {
-    hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1, 8>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512), lds, st,
-                       p, S, R, L);
+    hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1, 8, false>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512),
+                       lds, st, p, S, R, L);
     return hipGetLastError();
   }
   const unsigned grid = static_cast<unsigned>((waves + 11) / 12);
   switch (wl) {
-    case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
-    case 3: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 3, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
-    default: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 4, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 12, true>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    case 3: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 3, 12, true>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    default: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 4, 12, true>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
   }
   return hipGetLastError();
 }
