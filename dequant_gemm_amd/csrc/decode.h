@@ -51,13 +51,28 @@ struct DecodeW2T {
   }
   // bit 2j+1 set iff field j of the word is 10 (code -2)
   __device__ static uint32_t extra_bits(uint32_t w) { return w & ~(w << 1) & 0xAAAAAAAAu; }
+  // The OR of extra_bits over NW words (NW even): each pair w[d + 1]:w[d] is
+  // shifted as one 64-bit word; the bit w[d] carries into w[d + 1] lands at bit
+  // 0, which the mask clears.
+  template <int NW>
+  __device__ static uint32_t extra_bits_or(const uint32_t* w) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int d = 0; d < NW; d += 2) {
+      const uint64_t t = shl64<1>((static_cast<uint64_t>(w[d + 1]) << 32) | w[d]);
+      acc |= w[d] & ~static_cast<uint32_t>(t);
+      acc |= w[d + 1] & ~static_cast<uint32_t>(t >> 32);
+    }
+    return acc & 0xAAAAAAAAu;
+  }
   // r[i] and r[8 + i] come from one 64-bit shift of the pair w[1]:w[0]: the
   // bits w[0] carries into w[1] land below bit 14 and are masked off.
   __device__ static void fast(const uint32_t* w, uint32_t* r) {
     const uint64_t v = (static_cast<uint64_t>(w[1]) << 32) | w[0];
     auto one = [&](auto i_c) {
       constexpr int i = decltype(i_c)::value;
-      const uint64_t t = shl64<14 - 2 * i>(v);
+      uint64_t t = v;                        // i = 7: the fields are in place
+      if constexpr (i < 7) t = shl64<14 - 2 * i>(v);
       r[i] = static_cast<uint32_t>(t) & 0xC000C000u;
       r[8 + i] = static_cast<uint32_t>(t >> 32) & 0xC000C000u;
     };

@@ -234,7 +234,7 @@ __device__ __forceinline__ void step_macro(const CoreArgs& c, StreamState& st, c
     }
     if constexpr (IsW2<Dec>::value) {
       const uint32_t* wv = &w[h * B];
-      if (extra && __any((Dec::extra_bits(wv[0]) | Dec::extra_bits(wv[1])) != 0u)) {
+      if (extra && __any(Dec::template extra_bits_or<2>(wv) != 0u)) {
         // rare (wave-uniform): code -2 present; correct r and add the lo part
         const double a = f16_bits_to_f64(static_cast<uint16_t>(st.gab & 0xffffu));
         const double b = f16_bits_to_f64(static_cast<uint16_t>(st.gab >> 16));

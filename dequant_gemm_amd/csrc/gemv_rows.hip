@@ -29,6 +29,14 @@
 namespace cubic {
 namespace {
 
+// Zero, computed from v: an address that adds it is only formed once the load
+// that produced v has returned (the compiler waits for v before the asm).
+__device__ __forceinline__ uint32_t zero_after(uint32_t v) {
+  uint32_t z;
+  asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(v));
+  return z;
+}
+
 // XF16: fp16 activations (fp16 MFMA) instead of bf16. G: group size (256 or
 // 512). WL: wave-loads per wave, all issued up front. NW: waves per workgroup.
 // XFIRST: the waves that stage x wait for it before they issue their codes
@@ -72,23 +80,30 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
                                         static_cast<int>(static_cast<uint32_t>(p.N) * row_bytes),
                                         static_cast<int>(rows::kRsrcWord3));
   const int gw = static_cast<int>(blockIdx.x) * NW + wave;
+  // Wave-load u > 0 is issued only once the first data of wave-load u - 1 is in
+  // (its addresses take a zero computed from that data). The first wave-loads
+  // of all waves then come back from a less crowded memory system, and their
+  // decode overlaps the later loads: gate_up 6.32-6.43 us against 7.03-7.07 us
+  // with every load issued at once.
   uint32_t cw[WL][DWL];
   float gs[WL];
   uint32_t gab[WL];
+  uint32_t after = 0;
 #pragma unroll
   for (int u = 0; u < WL; ++u) {
+    if (u > 0) after = zero_after(cw[u - 1][0]);
     const int q0 = gw * WL + u;
     const int q = q0 < L ? q0 : L - 1;     // past the last wave-load: reload it, store nothing
     const int64_t n = static_cast<int64_t>(q) * R + ri;
     const int64_t nc = n < p.N ? n : p.N - 1;
-    const uint32_t off = static_cast<uint32_t>(nc) * row_bytes + static_cast<uint32_t>(gi * (G / 4) + kq * (G / 16));
+    const uint32_t off = static_cast<uint32_t>(nc) * row_bytes + static_cast<uint32_t>(gi * (G / 4) + kq * (G / 16)) + after;
 #pragma unroll
     for (int d = 0; d < DWL; d += 4) {
       const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(crs, off + 4 * d, 0, 0);
       cw[u][d] = w.x; cw[u][d + 1] = w.y; cw[u][d + 2] = w.z; cw[u][d + 3] = w.w;
     }
-    gs[u] = p.scales[nc * gpr + gi];
-    gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi];
+    gs[u] = p.scales[nc * gpr + gi + after];
+    gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi + after];
   }
 
   if constexpr (!XFIRST) xs.store<G>(xl, p.K, tid);

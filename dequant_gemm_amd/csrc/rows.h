@@ -105,9 +105,7 @@ __device__ __forceinline__ f32x4 wave_load_dot(const uint32_t* cw, const u32x4 (
   f32x4 d = dc[0] + dc[1];
   // field value 10 (code -2, never written by a symmetric quantiser): its level
   // -2 q(2) in units of s / 2 as hi + lo in the MFMA's 16-bit type
-  uint32_t ex = 0;
-#pragma unroll
-  for (int dd = 0; dd < DWL; ++dd) ex |= Dec::extra_bits(cw[dd]);
+  const uint32_t ex = Dec::template extra_bits_or<DWL>(cw);
   if (__any(active && ex != 0u)) {
     const double a = f16_bits_to_f64(static_cast<uint16_t>(gab & 0xffffu));
     const double b = f16_bits_to_f64(static_cast<uint16_t>(gab >> 16));
