@@ -39,9 +39,7 @@ __device__ __forceinline__ uint32_t zero_after(uint32_t v) {
 
 // XF16: fp16 activations (fp16 MFMA) instead of bf16. G: group size (256 or
 // 512). WL: wave-loads per wave, all issued up front. NW: waves per workgroup.
-// XFIRST: the waves that stage x wait for it before they issue their codes
-// (otherwise the codes are issued first and x is stored after).
-template <bool XF16, int G, int WL, int NW, bool XFIRST>
+template <bool XF16, int G, int WL, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int R, int L) {
   using Dec = DecodeW2T<XF16>;
   constexpr int DWL = G / 64;              // code dwords per lane and wave-load
@@ -61,17 +59,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
   // Staging x. Every workgroup reads the same row, so its loads hit the L2; but
   // sent behind the code loads of the waves started before them, they were
   // measured to come in behind those, and the barrier below then held every
-  // wave's decode until most of the compute unit's codes were in. With XFIRST
-  // the staging waves (the first of the workgroup) wait for x, one round trip,
-  // before they issue their codes, so all of x goes out before any code load.
-  rows::XStageRow xs;
-  if constexpr (XFIRST) {
-    if (wave * 64 < static_cast<int>(p.K / 32)) {
-      xs.issue(p.x, p.K, tid);
-      xs.store<G>(xl, p.K, tid);
-    }
-  } else {
+  // wave's decode until most of the compute unit's codes were in. So the
+  // staging waves (the first of the workgroup) wait for x, one round trip,
+  // before they issue their codes, and all of x goes out before any code load.
+  if (wave * 64 < static_cast<int>(p.K / 32)) {
+    rows::XStageRow xs;
     xs.issue(p.x, p.K, tid);
+    xs.store<G>(xl, p.K, tid);
   }
 
   // codes and group parameters of this wave's WL wave-loads
@@ -88,26 +82,35 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
   uint32_t cw[WL][DWL];
   float gs[WL];
   uint32_t gab[WL];
-  uint32_t after = 0;
+  // With one wave-load a wave there is nothing to stagger within a wave, so
+  // the upper half of the workgroup issues its codes after the barrier, once x
+  // is staged (down 7168 x 3072: 4.83-4.91 us against 4.94-4.97 us with every
+  // wave issuing at once; a quarter or three quarters late, or odd waves, did
+  // no better).
+  const bool late = WL == 1 && wave >= NW / 2;
+  auto issue = [&]() {
+    uint32_t after = 0;
 #pragma unroll
-  for (int u = 0; u < WL; ++u) {
-    if (u > 0) after = zero_after(cw[u - 1][0]);
-    const int q0 = gw * WL + u;
-    const int q = q0 < L ? q0 : L - 1;     // past the last wave-load: reload it, store nothing
-    const int64_t n = static_cast<int64_t>(q) * R + ri;
-    const int64_t nc = n < p.N ? n : p.N - 1;
-    const uint32_t off = static_cast<uint32_t>(nc) * row_bytes + static_cast<uint32_t>(gi * (G / 4) + kq * (G / 16)) + after;
+    for (int u = 0; u < WL; ++u) {
+      if (u > 0) after = zero_after(cw[u - 1][0]);
+      const int q0 = gw * WL + u;
+      const int q = q0 < L ? q0 : L - 1;     // past the last wave-load: reload it, store nothing
+      const int64_t n = static_cast<int64_t>(q) * R + ri;
+      const int64_t nc = n < p.N ? n : p.N - 1;
+      const uint32_t off = static_cast<uint32_t>(nc) * row_bytes + static_cast<uint32_t>(gi * (G / 4) + kq * (G / 16)) + after;
 #pragma unroll
-    for (int d = 0; d < DWL; d += 4) {
-      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(crs, off + 4 * d, 0, 0);
-      cw[u][d] = w.x; cw[u][d + 1] = w.y; cw[u][d + 2] = w.z; cw[u][d + 3] = w.w;
+      for (int d = 0; d < DWL; d += 4) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(crs, off + 4 * d, 0, 0);
+        cw[u][d] = w.x; cw[u][d + 1] = w.y; cw[u][d + 2] = w.z; cw[u][d + 3] = w.w;
+      }
+      gs[u] = p.scales[nc * gpr + gi + after];
+      gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi + after];
     }
-    gs[u] = p.scales[nc * gpr + gi + after];
-    gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi + after];
-  }
+  };
+  if (!late) issue();
 
-  if constexpr (!XFIRST) xs.store<G>(xl, p.K, tid);
   __syncthreads();
+  if (late) issue();
   u32x4 xa[NSC][4];
   rows::load_lane_x<G>(xl, gi, kq, xa);
 
@@ -130,22 +133,22 @@ hipError_t launch_rows_g(const GemvParams& p, int S, int R, int L, int wl, hipSt
   const int waves = (L + wl - 1) / wl;
   const size_t lds = rows::lds_bytes(p.K, G);   // K <= 8192
   // One wave-load a wave: workgroups of 8 waves (down 7168 x 3072: 4.84-4.94 us
-  // against 5.12-5.14 us with 4, 4.98-5.03 us with 14), x stored after the codes
-  // are issued (4.92 against 5.05-5.14 us with x first). More: 12 waves, one
-  // workgroup per compute unit, which the dispatcher starts sooner than three of
-  // 4 (gate_up: 7.04-7.06 us against 7.15-7.33 us with 4, 7.32 us with 8), x
-  // first (6.47 against 6.99 us; a workgroup of 12 code waves and 4 staging
-  // waves measured 7.3 us).
+  // against 5.12-5.14 us with 4, 4.98-5.03 us with 14), x first and half of
+  // the waves' codes after the barrier (x first alone: 5.05-5.14 us). More: 12
+  // waves, one workgroup per compute unit, which the dispatcher starts sooner
+  // than three of 4 (gate_up: 7.04-7.06 us against 7.15-7.33 us with 4, 7.32 us
+  // with 8); x first took gate_up from 6.99 to 6.47 us (a workgroup of 12 code
+  // waves and 4 staging waves measured 7.3 us).
   if (wl == 1) {
-    hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1, 8, false>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512),
+    hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1, 8>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512),
                        lds, st, p, S, R, L);
     return hipGetLastError();
   }
   const unsigned grid = static_cast<unsigned>((waves + 11) / 12);
   switch (wl) {
-    case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 12, true>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
-    case 3: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 3, 12, true>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
-    default: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 4, 12, true>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    case 2: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    case 3: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 3, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
+    default: hipLaunchKernelGGL((k_gemv_rows<XF16, G, 4, 12>), dim3(grid), dim3(768), lds, st, p, S, R, L); break;
   }
   return hipGetLastError();
 }
