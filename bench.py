@@ -437,7 +437,7 @@ def main():
                    "steps_per_graph": c, "algorithmic_bytes_per_step": bytes_up + bytes_dn},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gemv_rows<bf16, G=512, 2 wave-loads a wave, 12-wave workgroups, x staged first> (gate_up 6144x7168, M=1)",
+                     "kernel": "k_gemv_rows<bf16, G=512, 2 staggered wave-loads a wave, 12-wave workgroups, x staged first> (gate_up 6144x7168, M=1)",
                      "avg_launch_us": round(up_avg_ms * 1e3, 3),
                      "timing": f"HIP events on the launch stream around graph replays of {2 * R} "
                                f"back-to-back gate_up launches over {R} rotating copies",

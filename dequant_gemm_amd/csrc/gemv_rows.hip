@@ -74,24 +74,29 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
                                         static_cast<int>(static_cast<uint32_t>(p.N) * row_bytes),
                                         static_cast<int>(rows::kRsrcWord3));
   const int gw = static_cast<int>(blockIdx.x) * NW + wave;
-  // Wave-load u > 0 is issued only once the first data of wave-load u - 1 is in
-  // (its addresses take a zero computed from that data). The first wave-loads
-  // of all waves then come back from a less crowded memory system, and their
-  // decode overlaps the later loads: gate_up 6.32-6.43 us against 7.03-7.07 us
-  // with every load issued at once.
+  // Order of a wave. Wave-load 0 goes out before the barrier; the barrier
+  // then waits only for x and for every wave to have issued it (an earlier
+  // order, which also waited for each wave's first data before the barrier,
+  // measured gate_up 6.27-6.33 us against 5.71-5.76 us). After it, wave-load
+  // u > 0 goes out once the first data of wave-load u - 1 is in (its addresses
+  // take a zero computed from that data): the first wave-loads come back from
+  // a less crowded memory system and their decode overlaps the later ones
+  // (gate_up 6.32-6.43 us against 7.03-7.07 us with every load issued at once,
+  // both with the earlier barrier). Scheduling barriers keep the compiler from
+  // moving the decode of wave-load 0 ahead of the barrier.
   uint32_t cw[WL][DWL];
   float gs[WL];
   uint32_t gab[WL];
-  // With one wave-load a wave there is nothing to stagger within a wave, so
-  // the upper half of the workgroup issues its codes after the barrier, once x
-  // is staged (down 7168 x 3072: 4.83-4.91 us against 4.94-4.97 us with every
-  // wave issuing at once; a quarter or three quarters late, or odd waves, did
-  // no better).
+  // With one wave-load a wave (small N) there is nothing to stagger within a
+  // wave, so the upper half of the workgroup issues its codes after the
+  // barrier (down 7168 x 3072 run that way: 4.83-4.91 us against 4.94-4.97 us
+  // with every wave issuing at once).
   const bool late = WL == 1 && wave >= NW / 2;
-  auto issue = [&]() {
+  auto issue = [&](auto u0c, auto u1c) {
+    constexpr int U0 = decltype(u0c)::value, U1 = decltype(u1c)::value;
     uint32_t after = 0;
 #pragma unroll
-    for (int u = 0; u < WL; ++u) {
+    for (int u = U0; u < U1; ++u) {
       if (u > 0) after = zero_after(cw[u - 1][0]);
       const int q0 = gw * WL + u;
       const int q = q0 < L ? q0 : L - 1;     // past the last wave-load: reload it, store nothing
@@ -107,12 +112,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
       gab[u] = reinterpret_cast<const uint32_t*>(p.shapes)[nc * gpr + gi + after];
     }
   };
-  if (!late) issue();
+  if (!late) issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
 
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
-  if (late) issue();
+  __builtin_amdgcn_sched_barrier(0);
+  if (late) issue(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
   u32x4 xa[NSC][4];
   rows::load_lane_x<G>(xl, gi, kq, xa);
+  issue(std::integral_constant<int, 1>{}, std::integral_constant<int, WL>{});
+  __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
   for (int u = 0; u < WL; ++u) {
@@ -129,18 +138,22 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_rows(GemvParams p, int S, int 
 }
 
 template <bool XF16, int G>
-hipError_t launch_rows_g(const GemvParams& p, int S, int R, int L, int wl, hipStream_t st) {
+hipError_t launch_rows_g(const GemvParams& p, int S, int R, int L, int wl, int64_t cus, hipStream_t st) {
   const int waves = (L + wl - 1) / wl;
   const size_t lds = rows::lds_bytes(p.K, G);   // K <= 8192
-  // One wave-load a wave: workgroups of 8 waves (down 7168 x 3072: 4.84-4.94 us
-  // against 5.12-5.14 us with 4, 4.98-5.03 us with 14), x first and half of
-  // the waves' codes after the barrier (x first alone: 5.05-5.14 us). More: 12
-  // waves, one workgroup per compute unit, which the dispatcher starts sooner
-  // than three of 4 (gate_up: 7.04-7.06 us against 7.15-7.33 us with 4, 7.32 us
-  // with 8); x first took gate_up from 6.99 to 6.47 us (a workgroup of 12 code
-  // waves and 4 staging waves measured 7.3 us).
+  // Workgroups of 12 waves when that still fills every compute unit (one each,
+  // which the dispatcher starts sooner than three of 4: gate_up 7.04-7.06 us
+  // against 7.15-7.33 us with 4 and 7.32 us with 8, before the staggering);
+  // otherwise of 8 (down 7168 x 3072 with two wave-loads a wave: 4.66-4.70 us
+  // against 4.70-4.72 us with 7 and 5.07-5.08 us with 4). A workgroup of 12
+  // code waves and 4 waves that only stage x measured 7.3 us for gate_up.
   if (wl == 1) {
     hipLaunchKernelGGL((k_gemv_rows<XF16, G, 1, 8>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512),
+                       lds, st, p, S, R, L);
+    return hipGetLastError();
+  }
+  if (wl == 2 && waves < 12 * cus) {
+    hipLaunchKernelGGL((k_gemv_rows<XF16, G, 2, 8>), dim3(static_cast<unsigned>((waves + 7) / 8)), dim3(512),
                        lds, st, p, S, R, L);
     return hipGetLastError();
   }
@@ -167,18 +180,20 @@ hipError_t launch_gemv_rows(const GemvParams& p, bool xf16, hipStream_t st) {
   const int64_t L64 = (p.N + R - 1) / R;
   if (L64 > 0x3fffffff) return hipErrorInvalidValue;
   const int L = static_cast<int>(L64);
-  // Wave-loads per wave: one while that keeps at most 16 waves per CU, else as
-  // few as keep it there. Measured on the K3 shapes (graph replays, 50 rotating
-  // copies): down (3584 wave-loads) 5.16 us with one against 5.74 us with two;
-  // gate_up (6144) 7.25 us with two against 8.05 with one and 7.88 with three.
+  // Wave-loads per wave: as few as keep at most 16 waves per CU, but two
+  // (staggered) once there are at least two per CU. Measured on the K3 shapes
+  // (graph replays, 50 rotating copies): gate_up (6144 wave-loads) 5.71-5.76 us
+  // with two against 6.4-6.6 us with three in 8-wave workgroups; down (3584)
+  // 4.66-4.70 us with two against 4.76-4.85 us with one.
   const int64_t cus = device_cu_count() > 0 ? device_cu_count() : 256;
   int64_t wl = (L + cus * 16 - 1) / (cus * 16);
   wl = wl < 1 ? 1 : (wl > 4 ? 4 : wl);
+  if (wl == 1 && L >= 2 * cus) wl = 2;
   if (p.group == 512)
-    return xf16 ? launch_rows_g<true, 512>(p, S, R, L, static_cast<int>(wl), st)
-                : launch_rows_g<false, 512>(p, S, R, L, static_cast<int>(wl), st);
-  return xf16 ? launch_rows_g<true, 256>(p, S, R, L, static_cast<int>(wl), st)
-              : launch_rows_g<false, 256>(p, S, R, L, static_cast<int>(wl), st);
+    return xf16 ? launch_rows_g<true, 512>(p, S, R, L, static_cast<int>(wl), cus, st)
+                : launch_rows_g<false, 512>(p, S, R, L, static_cast<int>(wl), cus, st);
+  return xf16 ? launch_rows_g<true, 256>(p, S, R, L, static_cast<int>(wl), cus, st)
+              : launch_rows_g<false, 256>(p, S, R, L, static_cast<int>(wl), cus, st);
 }
 
 }  // namespace cubic

@@ -1,8 +1,8 @@
 """GPU parity of the whole-row GEMV (one activation row, 2-bit codes, groups of
 256 or 512, at most 16 groups per row), against the float64 oracle at the
 products' bar (per-row 2e-3). The cases cover every number of rows per wave
-load (R = 16 / (K / G) from 1 to 16), one to three wave loads per wave (the
-large-N cases take the 12-wave workgroups), ragged N (rows past N in the last
+load (R = 16 / (K / G) from 1 to 16), one to four wave loads per wave (8- and
+12-wave workgroups, staggered second and later wave loads), ragged N (rows past N in the last
 wave load), raw random code bytes (every field value, so the code -2 path runs in
 many wave loads), fp16 activations and bf16 outputs (the fp32 sums rounded),
 and activation rows far outside the fp16 range."""
@@ -35,7 +35,7 @@ def _raw_weight(N, K, G, seed):
 
 @pytest.mark.parametrize("N,K,G", [(203, 7168, 512), (130, 3072, 512), (77, 8192, 512), (33, 512, 512),
                                    (203, 4096, 256), (97, 768, 256), (64, 2048, 256), (1, 1024, 256),
-                                   (10001, 4096, 256)])
+                                   (10001, 4096, 256), (2001, 3072, 512), (13001, 4096, 256)])
 def test_rows_random_codes(N, K, G):
     say(f"GEMV rows N={N} K={K} G={G} (random code bytes)")
     cw, W = _raw_weight(N, K, G, seed=N + K + G)
